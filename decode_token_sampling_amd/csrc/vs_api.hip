@@ -1,0 +1,184 @@
+// C ABI of libvs.so: argument checks, workspace layout, kernel sequence.
+#include <stdint.h>
+
+#include "vs_device.h"
+#include "vs_kernels.h"
+
+namespace vsk {
+
+namespace {
+size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+}  // namespace
+
+WsLayout ws_layout(int B, int V) {
+  WsLayout L{};
+  L.B = B;
+  L.V = V;
+  L.ntile1 = (V + kSelTile - 1) / kSelTile;
+  L.wpr1 = (L.ntile1 + kSelWaves - 1) / kSelWaves;
+  L.ntile3 = (V + kGumTile - 1) / kGumTile;
+  const size_t tiles = static_cast<size_t>(B) * L.ntile1;
+  size_t off = 0;
+  L.meta = off;
+  off = align_up(off + tiles * sizeof(uint32_t));
+  L.cand = off;
+  off = align_up(off + tiles * kFastK * sizeof(uint64_t));
+  L.desc = off;
+  off = align_up(off + static_cast<size_t>(B) * sizeof(RowDesc));
+  L.gpart = off;
+  off = align_up(off + static_cast<size_t>(B) * L.ntile3 * sizeof(GPart));
+  L.lpart = off;
+  off = align_up(off + tiles * sizeof(LsePart));
+  L.rlse = off;
+  off = align_up(off + static_cast<size_t>(B) * sizeof(float2));
+  L.total = off;
+  return L;
+}
+
+}  // namespace vsk
+
+using vsk::WsLayout;
+
+namespace {
+
+// Per-thread stage profiling (vs_profile_begin / vs_profile_end).
+constexpr int kMaxProfiled = 4096;
+thread_local hipEvent_t* g_prof_ev = nullptr;
+thread_local int g_prof_cap = 0;
+thread_local int g_prof_n = 0;
+thread_local const char* g_prof_names[kMaxProfiled];
+
+// Runs one launch function, bracketed by profiling events when active.
+template <typename F>
+hipError_t stage(const char* name, hipStream_t st, F&& launch) {
+  const bool rec = g_prof_ev && 2 * g_prof_n + 1 < g_prof_cap && g_prof_n < kMaxProfiled;
+  if (rec && hipEventRecord(g_prof_ev[2 * g_prof_n], st) != hipSuccess) return hipErrorUnknown;
+  const hipError_t e = launch();
+  if (rec) {
+    if (hipEventRecord(g_prof_ev[2 * g_prof_n + 1], st) != hipSuccess) return hipErrorUnknown;
+    g_prof_names[g_prof_n++] = name;
+  }
+  return e;
+}
+
+bool sizes_ok(vs_dtype dt, int B, int V, int64_t ld) {
+  return (dt == VS_F32 || dt == VS_BF16) && B > 0 && V > 0 && V <= VS_MAX_V && ld >= V;
+}
+
+bool rows_aligned(const void* p, vs_dtype dt, int64_t ld) {
+  const int64_t es = (dt == VS_F32) ? 4 : 2;
+  return (reinterpret_cast<uintptr_t>(p) % 16 == 0) && ((ld * es) % 16 == 0);
+}
+
+}  // namespace
+
+extern "C" {
+
+vs_status vs_workspace_size(int B, int V, vs_dtype dt, size_t* bytes) {
+  if (!bytes || !sizes_ok(dt, B, V, V)) return VS_ERR_INVALID_ARGUMENT;
+  *bytes = vsk::ws_layout(B, V).total;
+  return VS_OK;
+}
+
+const char* vs_status_string(vs_status s) {
+  switch (s) {
+    case VS_OK: return "ok";
+    case VS_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case VS_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case VS_ERR_UNSUPPORTED: return "unsupported";
+    case VS_ERR_HIP: return "HIP launch failure";
+  }
+  return "unknown status";
+}
+
+vs_status vs_penalize(void* logits, vs_dtype dt, int B, int V, int64_t ld,
+                      const int32_t* prompt_ids, const int32_t* prompt_off,
+                      const int32_t* output_ids, const int32_t* output_off,
+                      const float* presence, const float* frequency,
+                      const float* repetition, int32_t* out_row_status,
+                      hipStream_t stream) {
+  if (!logits || !sizes_ok(dt, B, V, ld)) return VS_ERR_INVALID_ARGUMENT;
+  if ((prompt_ids == nullptr) != (prompt_off == nullptr)) return VS_ERR_INVALID_ARGUMENT;
+  if ((output_ids == nullptr) != (output_off == nullptr)) return VS_ERR_INVALID_ARGUMENT;
+  const hipError_t e = stage("penalize", stream, [&] {
+    return vsk::launch_penalize(logits, dt, B, V, ld, prompt_ids, prompt_off, output_ids,
+                                output_off, presence, frequency, repetition, out_row_status,
+                                stream);
+  });
+  return e == hipSuccess ? VS_OK : VS_ERR_HIP;
+}
+
+vs_status vs_sample(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
+                    const float* temperature, const int32_t* top_k,
+                    const float* top_p, const float* min_p,
+                    const uint64_t* seeds, uint32_t hints, int32_t* out_ids,
+                    int32_t* out_kept_count, uint32_t* out_kept_mask,
+                    int32_t* out_row_status, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  if (!logits || !out_ids || !ws || !sizes_ok(dt, B, V, ld)) return VS_ERR_INVALID_ARGUMENT;
+  if (hints & ~(VS_HINT_NO_FULLVOCAB | VS_HINT_ALL_GREEDY)) return VS_ERR_INVALID_ARGUMENT;
+  const WsLayout L = vsk::ws_layout(B, V);
+  if (ws_bytes < L.total) return VS_ERR_WORKSPACE_TOO_SMALL;
+  vsk::SampleArgs a{logits, dt, B, V, ld, rows_aligned(logits, dt, ld), temperature, top_k,
+                    top_p, min_p, seeds, hints, out_ids, out_kept_count, out_kept_mask,
+                    out_row_status};
+  char* w = static_cast<char*>(ws);
+  if (stage("select", stream, [&] { return vsk::launch_select(a, L, w, stream); }) != hipSuccess)
+    return VS_ERR_HIP;
+  if (stage("row", stream, [&] { return vsk::launch_row(a, L, w, stream); }) != hipSuccess)
+    return VS_ERR_HIP;
+  if (!(hints & (VS_HINT_NO_FULLVOCAB | VS_HINT_ALL_GREEDY))) {
+    if (stage("gumbel", stream, [&] { return vsk::launch_gumbel(a, L, w, stream); }) != hipSuccess)
+      return VS_ERR_HIP;
+  }
+  return VS_OK;
+}
+
+vs_status vs_logprobs(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
+                      const int32_t* token_ids, float* out_token_logprob, int k,
+                      int32_t* out_topk_ids, float* out_topk_logprobs,
+                      float* out_full, int64_t ld_out, int32_t* out_row_status,
+                      void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!logits || !ws || !sizes_ok(dt, B, V, ld)) return VS_ERR_INVALID_ARGUMENT;
+  if ((token_ids == nullptr) != (out_token_logprob == nullptr)) return VS_ERR_INVALID_ARGUMENT;
+  if (k < 0 || k > VS_LOGPROB_K_MAX || k > V) return VS_ERR_INVALID_ARGUMENT;
+  if (k > 0 && (!out_topk_ids || !out_topk_logprobs)) return VS_ERR_INVALID_ARGUMENT;
+  if (out_full && ld_out < V) return VS_ERR_INVALID_ARGUMENT;
+  const WsLayout L = vsk::ws_layout(B, V);
+  if (ws_bytes < L.total) return VS_ERR_WORKSPACE_TOO_SMALL;
+  vsk::LogprobArgs a{logits, dt, B, V, ld, rows_aligned(logits, dt, ld), token_ids,
+                     out_token_logprob, k, out_topk_ids, out_topk_logprobs, out_full, ld_out,
+                     out_row_status};
+  char* w = static_cast<char*>(ws);
+  if (stage("lse_select", stream, [&] { return vsk::launch_select_lse(a, L, w, stream); }) !=
+      hipSuccess)
+    return VS_ERR_HIP;
+  if (stage("lse_row", stream, [&] { return vsk::launch_lse_row(a, L, w, stream); }) != hipSuccess)
+    return VS_ERR_HIP;
+  if (out_full) {
+    if (stage("lse_full", stream, [&] { return vsk::launch_lse_full(a, L, w, stream); }) !=
+        hipSuccess)
+      return VS_ERR_HIP;
+  }
+  return VS_OK;
+}
+
+vs_status vs_profile_begin(hipEvent_t* events, int capacity) {
+  if (!events || capacity < 2) return VS_ERR_INVALID_ARGUMENT;
+  g_prof_ev = events;
+  g_prof_cap = capacity;
+  g_prof_n = 0;
+  return VS_OK;
+}
+
+int vs_profile_end(const char** names, int max_names) {
+  const int n = g_prof_n;
+  if (names)
+    for (int i = 0; i < n && i < max_names; ++i) names[i] = g_prof_names[i];
+  g_prof_ev = nullptr;
+  g_prof_cap = 0;
+  g_prof_n = 0;
+  return n;
+}
+
+}  // extern "C"

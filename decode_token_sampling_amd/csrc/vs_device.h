@@ -1,0 +1,390 @@
+// Device-side building blocks shared by the sampling kernels (gfx950, wave64).
+//
+// Numeric conventions (the same ones the C ABI documents):
+//  - order: larger value first, lower id first among equals; -0 equals +0;
+//  - ordered key of an fp32 value: a uint32 whose unsigned order is the float
+//    order (-0 canonicalised to +0), packed with the id as
+//    (key << 32) | ~id so that one uint64 comparison gives the full order;
+//  - relative weight e = exp(t) rounded to fp32 for t >= -87, else 0;
+//  - Gumbel uniforms from SplitMix64 keyed by (seed, row, id).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/vs.h"
+
+namespace vsk {
+
+constexpr int kWave = 64;
+constexpr int kFastK = 64;     // top-k handled by the per-tile fast path
+constexpr float kInf = __builtin_inff();
+
+// ---------------------------------------------------------------- keys
+__device__ __forceinline__ uint32_t f2key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;  // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key2f(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+__device__ __forceinline__ uint64_t pack(uint32_t key, int32_t id) {
+  return (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(id));
+}
+__device__ __forceinline__ uint32_t pkey(uint64_t p) { return static_cast<uint32_t>(p >> 32); }
+__device__ __forceinline__ int32_t pid(uint64_t p) {
+  return static_cast<int32_t>(~static_cast<uint32_t>(p));
+}
+constexpr uint32_t kKeyNegInf = 0x007fffffu;  // f2key(-inf)
+constexpr uint32_t kKeyPosInf = 0xff800000u;  // f2key(+inf)
+
+// ---------------------------------------------------------------- element access
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// 16-byte vector loads: elements per vector and unpacking to fp32.
+template <typename E>
+struct Epv;
+template <>
+struct Epv<float> {
+  static constexpr int n = 4;
+};
+template <>
+struct Epv<uint16_t> {
+  static constexpr int n = 8;
+};
+
+__device__ __forceinline__ void unpack16(const uint4& u, float* x, const float*) {
+  x[0] = __uint_as_float(u.x);
+  x[1] = __uint_as_float(u.y);
+  x[2] = __uint_as_float(u.z);
+  x[3] = __uint_as_float(u.w);
+}
+__device__ __forceinline__ void unpack16(const uint4& u, float* x, const uint16_t*) {
+  x[0] = __uint_as_float(u.x << 16);
+  x[1] = __uint_as_float(u.x & 0xffff0000u);
+  x[2] = __uint_as_float(u.y << 16);
+  x[3] = __uint_as_float(u.y & 0xffff0000u);
+  x[4] = __uint_as_float(u.z << 16);
+  x[5] = __uint_as_float(u.z & 0xffff0000u);
+  x[6] = __uint_as_float(u.w << 16);
+  x[7] = __uint_as_float(u.w & 0xffff0000u);
+}
+
+// ---------------------------------------------------------------- pinned exp
+// exp(t) rounded once to fp32 for t >= -87, 0 below. Evaluated in double:
+// Cody & Waite range reduction t = n*ln2 + r with ln2 split into a high part
+// (low 11 mantissa bits cleared, so n*hi is exact) and a low part, a degree-13
+// Taylor polynomial for e^r on |r| <= ln2/2 (truncation error < 5e-18), and an
+// exact scaling by 2^n. Its double result is within a few 1e-17 of e^t, so the
+// final fp32 rounding is the correctly rounded value; the oracle states this
+// function as libm's exp rounded to fp32 and the tests compare the two.
+__device__ __forceinline__ float pinned_exp(float tf) {
+  if (!(tf >= -87.0f)) return 0.0f;
+  const double t = static_cast<double>(tf);
+  const double n = rint(t * 1.4426950408889634);   // 1/ln2
+  const double hi = 0x1.62e42fefa3800p-1;           // ln2, low 11 bits cleared
+  const double lo = 0x1.ef35793c76730p-45;          // ln2 - hi
+  double r = __builtin_fma(-n, hi, t);
+  r = __builtin_fma(-n, lo, r);
+  double p = 1.0 / 6227020800.0;                    // 1/13!
+  p = __builtin_fma(p, r, 1.0 / 479001600.0);
+  p = __builtin_fma(p, r, 1.0 / 39916800.0);
+  p = __builtin_fma(p, r, 1.0 / 3628800.0);
+  p = __builtin_fma(p, r, 1.0 / 362880.0);
+  p = __builtin_fma(p, r, 1.0 / 40320.0);
+  p = __builtin_fma(p, r, 1.0 / 5040.0);
+  p = __builtin_fma(p, r, 1.0 / 720.0);
+  p = __builtin_fma(p, r, 1.0 / 120.0);
+  p = __builtin_fma(p, r, 1.0 / 24.0);
+  p = __builtin_fma(p, r, 1.0 / 6.0);
+  p = __builtin_fma(p, r, 0.5);
+  p = __builtin_fma(p, r, 1.0);
+  p = __builtin_fma(p, r, 1.0);
+  const int64_t ni = static_cast<int64_t>(n);
+  const double scale = __longlong_as_double((ni + 1023) << 52);
+  return static_cast<float>(p * scale);
+}
+
+// Fixed-point top-p mass of a relative weight e in [0,1]: floor(e * 2^31).
+__device__ __forceinline__ uint64_t mass_of(float e) {
+  return static_cast<uint64_t>(static_cast<uint32_t>(e * 2147483648.0f));
+}
+
+// ---------------------------------------------------------------- random stream
+// SplitMix64 (Steele, Lea, Flood 2014; Mix13 finaliser): output for state x.
+__device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
+  uint64_t z = x + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+__device__ __forceinline__ uint64_t row_stream(uint64_t seed, int row) {
+  return splitmix64(seed ^ (static_cast<uint64_t>(static_cast<uint32_t>(row)) << 32));
+}
+// Uniform strictly inside (0,1): 52 random bits plus one half, times 2^-52.
+__device__ __forceinline__ double uniform_of(uint64_t row_state, int id) {
+  const uint64_t b = splitmix64(row_state + static_cast<uint64_t>(static_cast<uint32_t>(id)));
+  return (static_cast<double>(b >> 12) + 0.5) * 0x1p-52;
+}
+// Gumbel-max score prob / q with q = -log(u) (exponential noise), in double.
+__device__ __forceinline__ double gumbel_score(float e, uint64_t row_state, int id) {
+  const double q = -log(uniform_of(row_state, id));
+  return static_cast<double>(e) / q;
+}
+
+// ---------------------------------------------------------------- row modes
+enum : int { kModeInvalid = 0, kModeGreedy = 1, kModeKFast = 2, kModeKSlow = 3, kModeFull = 4 };
+
+struct RowCfg {
+  int mode;
+  int status;
+  float T;
+  int k;      // effective top-k (0 = none)
+  float p;
+  float mp;
+  uint64_t seed;
+};
+
+__device__ __forceinline__ RowCfg load_cfg(int r, int V, const float* temperature,
+                                           const int32_t* top_k, const float* top_p,
+                                           const float* min_p, const uint64_t* seeds) {
+  RowCfg c;
+  c.T = temperature ? temperature[r] : 1.0f;
+  const int k = top_k ? top_k[r] : 0;
+  c.p = top_p ? top_p[r] : 1.0f;
+  c.mp = min_p ? min_p[r] : 0.0f;
+  c.seed = seeds ? seeds[r] : 0ull;
+  c.mode = kModeInvalid;
+  c.status = 0;
+  c.k = k;
+  const bool bad = !(c.T >= 0.0f && c.T <= 3.40282347e38f) || k < 0 ||
+                   !(c.p >= 0.0f && c.p <= 1.0f) || !(c.mp >= 0.0f && c.mp <= 1.0f);
+  if (bad) {
+    c.status = VS_ROW_BAD_PARAM;
+    return c;
+  }
+  if (c.T == 0.0f || k == 1 || c.p == 0.0f || c.mp == 1.0f) {
+    c.mode = kModeGreedy;
+    return c;
+  }
+  c.k = (k >= V) ? 0 : k;
+  if (c.k > VS_TOPK_MAX) {
+    c.status = VS_ROW_TOPK_UNSUPPORTED;
+    return c;
+  }
+  c.mode = (c.k == 0) ? kModeFull : (c.k <= kFastK ? kModeKFast : kModeKSlow);
+  return c;
+}
+
+// ---------------------------------------------------------------- workspace records
+// Per select tile: meta = count | flags, then up to kFastK packed candidates.
+constexpr uint32_t kMetaCountMask = 0xffu;
+constexpr uint32_t kMetaBadLogits = 0x100u;
+constexpr uint32_t kMetaOverflow = 0x200u;
+constexpr uint32_t kMetaHasFinite = 0x400u;  // some value of the tile is above -inf
+
+// Full-vocabulary rows: what K2 hands to the Gumbel kernels.
+enum : uint32_t { kFullSkip = 0, kFullNone = 1, kFullMinP = 2, kFullTopP = 3 };
+struct RowDesc {
+  uint32_t mode;
+  float m;         // max over the row of s = x / T
+  uint32_t tau;    // top-p: ordered key of the last kept value
+  int32_t id_cut;  // top-p: largest kept id among those whose key equals tau
+  int32_t kept;    // kept-set size as found by the cut (top-p)
+  uint32_t pad[3];
+};
+
+struct GPart {  // Gumbel partial result of one tile
+  double score;
+  int32_t id;
+  int32_t kept;
+};
+
+struct LsePart {  // log-sum-exp partial of one tile: max and sum of exp(x - max)
+  float m;
+  float s;
+};
+
+// ---------------------------------------------------------------- wave primitives
+__device__ __forceinline__ int lane() { return static_cast<int>(__lane_id()); }
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    T w = __shfl_xor(v, o);
+    v = (w > v) ? w : v;
+  }
+  return v;
+}
+template <typename T>
+__device__ __forceinline__ T wave_min(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    T w = __shfl_xor(v, o);
+    v = (w < v) ? w : v;
+  }
+  return v;
+}
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+// Number of set bits of a ballot below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t ballot) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(ballot >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(ballot), 0u));
+}
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Bitonic sort of one value per lane across the wave, larger first.
+template <typename T>
+__device__ __forceinline__ T wave_sort_desc(T v) {
+  const int l = lane();
+#pragma unroll
+  for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const T o = __shfl_xor(v, j);
+      const bool keep_max = (((l & k) == 0) == ((l & j) == 0));
+      v = keep_max ? (o > v ? o : v) : (o < v ? o : v);
+    }
+  }
+  return v;
+}
+// Given two descending lane-sorted sequences a and b, the 64 largest of their
+// union, descending (bitonic half-cleaner, then a bitonic merge).
+template <typename T>
+__device__ __forceinline__ T wave_merge_top_desc(T a, T b) {
+  const int l = lane();
+  const T br = __shfl(b, kWave - 1 - l);
+  T v = (a > br) ? a : br;
+#pragma unroll
+  for (int j = kWave >> 1; j > 0; j >>= 1) {
+    const T o = __shfl_xor(v, j);
+    v = ((l & j) == 0) ? (o > v ? o : v) : (o < v ? o : v);
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------- block primitives
+// All take a shared scratch array with at least (blockDim.x / 64) slots and
+// must be called by every thread of the block.
+template <typename T>
+__device__ __forceinline__ T block_max(T v, T* scratch) {
+  v = wave_max(v);
+  const int w = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  __syncthreads();
+  if (lane() == 0) scratch[w] = v;
+  __syncthreads();
+  v = scratch[0];
+  for (int i = 1; i < nw; ++i) v = (scratch[i] > v) ? scratch[i] : v;
+  __syncthreads();
+  return v;
+}
+template <typename T>
+__device__ __forceinline__ T block_min(T v, T* scratch) {
+  v = wave_min(v);
+  const int w = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  __syncthreads();
+  if (lane() == 0) scratch[w] = v;
+  __syncthreads();
+  v = scratch[0];
+  for (int i = 1; i < nw; ++i) v = (scratch[i] < v) ? scratch[i] : v;
+  __syncthreads();
+  return v;
+}
+template <typename T>
+__device__ __forceinline__ T block_sum(T v, T* scratch) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  __syncthreads();
+  if (lane() == 0) scratch[w] = v;
+  __syncthreads();
+  v = scratch[0];
+  for (int i = 1; i < nw; ++i) v += scratch[i];
+  __syncthreads();
+  return v;
+}
+// Inclusive prefix sum over the block in thread order; *total gets the block sum.
+template <typename T>
+__device__ __forceinline__ T block_scan_incl(T v, T* scratch, T* total) {
+  const int l = lane();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const T w = __shfl_up(v, o);
+    if (l >= o) v += w;
+  }
+  const int w = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  __syncthreads();
+  if (l == kWave - 1) scratch[w] = v;
+  __syncthreads();
+  T before = 0, all = 0;
+  for (int i = 0; i < nw; ++i) {
+    if (i < w) before += scratch[i];
+    all += scratch[i];
+  }
+  __syncthreads();
+  if (total) *total = all;
+  return v + before;
+}
+
+// Bitonic sort of n (a power of two) uint64 values in shared memory, larger first.
+__device__ __forceinline__ void block_sort_desc(uint64_t* buf, int n) {
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < (n >> 1); i += blockDim.x) {
+        const int lo = ((i / j) * 2 * j) + (i % j);
+        const int hi = lo + j;
+        const bool desc = ((lo & k) == 0);
+        const uint64_t a = buf[lo], b = buf[hi];
+        if (desc ? (a < b) : (a > b)) {
+          buf[lo] = b;
+          buf[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__device__ __forceinline__ int next_pow2(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+// XCD-aware placement: workgroups are dispatched round-robin over the 8 XCDs,
+// so workgroup L runs on XCD L % 8. Placing every tile of row r on XCD r % 8
+// keeps a row's re-reads in one L2. Returns false for padding workgroups.
+constexpr int kXcds = 8;
+__device__ __forceinline__ bool xcd_row_tile(int L, int B, int tiles_per_row, int* row, int* tile) {
+  const int x = L % kXcds;
+  const int q = L / kXcds;
+  const int a = q / tiles_per_row;
+  *tile = q - a * tiles_per_row;
+  *row = x + kXcds * a;
+  return *row < B;
+}
+__host__ __device__ inline int xcd_grid(int B, int tiles_per_row) {
+  return kXcds * ((B + kXcds - 1) / kXcds) * tiles_per_row;
+}
+
+}  // namespace vsk

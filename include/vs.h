@@ -1,0 +1,183 @@
+/*
+ * vs.h — batched decode-step token sampling on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libvs.so. Three calls make up one decode step over a row-major
+ * [B, ld] matrix of fp32 or bf16 logits (only columns [0, V) are read):
+ *
+ *   vs_penalize  presence / frequency / repetition penalties, in place
+ *   vs_sample    temperature, min-p, top-k, top-p, then a seeded Gumbel-max draw
+ *   vs_logprobs  log-softmax log-probabilities (given ids, top-k, full rows)
+ *
+ * Conventions shared by every call:
+ *  - All array arguments are DEVICE pointers unless stated otherwise; sizes and
+ *    scalars are host values. The caller owns every buffer. The library keeps no
+ *    pointer after a call returns, never allocates and never frees.
+ *  - Each call checks its host-visible arguments, enqueues kernels on `stream`
+ *    and returns without waiting. Outputs are valid once the stream reaches that
+ *    point; inputs must stay alive until then. No call synchronises, copies to
+ *    the host or allocates, so every call can be captured into a HIP graph.
+ *  - Host-detectable errors (NULL required pointer, B <= 0, V <= 0,
+ *    V > VS_MAX_V, ld < V, unknown dtype, bad k, workspace too small) return an
+ *    error status and enqueue nothing. A failed launch returns VS_ERR_HIP.
+ *  - Problems found on the device (per-row parameters, non-finite logits, token
+ *    ids out of range) are reported per row in `out_row_status` (bits VS_ROW_*)
+ *    when that pointer is not NULL; see each call for what such a row outputs.
+ *  - A workspace may serve one call at a time: two calls that overlap in time
+ *    (on different streams) need different workspaces.
+ *  - Logits rows are 16-byte aligned (base pointer and ld * element size) for the
+ *    fast load path; other layouts are accepted and take a slower path.
+ */
+#ifndef VS_H
+#define VS_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum vs_dtype { VS_F32 = 0, VS_BF16 = 1 } vs_dtype;
+
+typedef enum vs_status {
+  VS_OK = 0,
+  VS_ERR_INVALID_ARGUMENT = 1,
+  VS_ERR_WORKSPACE_TOO_SMALL = 2,
+  VS_ERR_UNSUPPORTED = 3,
+  VS_ERR_HIP = 4
+} vs_status;
+
+/* Per-row status bits (device-written int32 per row). */
+#define VS_ROW_BAD_PARAM 1        /* temperature < 0, NaN or inf; top_k < 0; top_p or min_p
+                                     outside [0,1]; repetition <= 0 or non-finite penalties;
+                                     logits / temperature overflowing to +inf */
+#define VS_ROW_BAD_LOGITS 2       /* a NaN or +inf logit in [0,V), or every logit is -inf */
+#define VS_ROW_BAD_TOKEN_ID 4     /* a history id (vs_penalize) or query id (vs_logprobs)
+                                     outside [0,V) */
+#define VS_ROW_TOPK_UNSUPPORTED 8 /* VS_TOPK_MAX < top_k < V */
+#define VS_ROW_HINT_VIOLATED 16   /* the row needs a stage the caller's hints switched off */
+
+/* vs_sample hints: promises by the caller that let the library skip kernels.
+ * A row that breaks a promise gets VS_ROW_HINT_VIOLATED and id -1 (it is never
+ * sampled wrongly). With hints = 0 every row is handled. */
+#define VS_HINT_NONE 0u
+#define VS_HINT_NO_FULLVOCAB 1u   /* no row samples over the full vocabulary: every row is
+                                     greedy or has 0 < top_k < V */
+#define VS_HINT_ALL_GREEDY 2u     /* every row is greedy */
+
+#define VS_MAX_V (1 << 21)        /* largest vocabulary */
+#define VS_TOPK_MAX 1024          /* largest top_k below V */
+#define VS_LOGPROB_K_MAX 64       /* largest top-k for vs_logprobs */
+
+/* Bytes of device workspace that vs_sample and vs_logprobs need for B rows of
+ * V logits of type dt. Returns VS_ERR_INVALID_ARGUMENT for bad sizes. */
+vs_status vs_workspace_size(int B, int V, vs_dtype dt, size_t* bytes);
+
+/* Static English text for a status code (host pointer, never NULL). */
+const char* vs_status_string(vs_status s);
+
+/*
+ * vs_penalize — occurrence penalties, in place.
+ *
+ * Defined by the TensorRT-LLM "Sampling" page (section "LLM API sampling
+ * behavior when using Torch Sampler", occurrence-penalty bullets). With c the
+ * number of times id j occurs in the row's prompt ids plus its output ids, every
+ * j with c > 0 becomes, each step one rounded fp32 operation:
+ *     y = x >= 0 ? x / repetition : x * repetition;  y = y - presence;
+ *     y = y - frequency * c
+ * bf16 logits are widened exactly, penalised in fp32 and rounded once to
+ * nearest-even. Ids with c = 0 are not touched.
+ *
+ *  logits      [B, ld] fp32 or bf16, modified in place
+ *  prompt_ids  int32 token ids, CSR by row: row r owns
+ *  prompt_off  prompt_ids[prompt_off[r] .. prompt_off[r+1]); prompt_off has B+1
+ *              entries. Both NULL: no prompt history.
+ *  output_ids, output_off: the generated tokens so far, same layout (or both NULL).
+ *  presence, frequency, repetition: [B] fp32 each; NULL means 0, 0 and 1.
+ *  out_row_status [B] int32 or NULL. A row with a bad parameter is left
+ *              unchanged (VS_ROW_BAD_PARAM); ids outside [0,V) are skipped
+ *              (VS_ROW_BAD_TOKEN_ID).
+ */
+vs_status vs_penalize(void* logits, vs_dtype dt, int B, int V, int64_t ld,
+                      const int32_t* prompt_ids, const int32_t* prompt_off,
+                      const int32_t* output_ids, const int32_t* output_off,
+                      const float* presence, const float* frequency,
+                      const float* repetition, int32_t* out_row_status,
+                      hipStream_t stream);
+
+/*
+ * vs_sample — one token per row.
+ *
+ * Truncation follows the TensorRT-LLM "Sampling" page (same section): greedy
+ * when temperature = 0, top_k = 1, top_p = 0 or min_p = 1; otherwise
+ * s = x / temperature (correctly rounded fp32), then min-p (keep relative
+ * weight >= min_p, applied first) and top-k (top_k = 0 or >= V: no top-k), then
+ * top-p on the survivors renormalised (shortest prefix reaching top_p of their
+ * mass). The draw follows vllm.cpp pull request #1997 ("The kernel (#1984)"):
+ * per kept id j a SplitMix64 uniform u(seed, row, j), q = -log(u) in double,
+ * score = prob / q, and the largest score wins with ties to the lowest id.
+ * Order everywhere is larger s first, lower id first among equals. Relative
+ * weights are e = exp(s - max s) rounded to fp32 (0 below -87); top-p masses are
+ * floor(e * 2^31) summed exactly; the top-p threshold is top_p * total in double.
+ *
+ *  logits       [B, ld] fp32 or bf16 (read only)
+ *  temperature  [B] fp32 or NULL (all 1)       top_k [B] int32 or NULL (all 0)
+ *  top_p        [B] fp32 or NULL (all 1)       min_p [B] fp32 or NULL (all 0)
+ *  seeds        [B] uint64 or NULL (all 0): the caller's per-row seed, advanced by
+ *               the caller once per sampled token
+ *  hints        VS_HINT_* promises (0 = none)
+ *  out_ids      [B] int32: the sampled id, -1 for a row with a nonzero status
+ *  out_kept_count [B] int32 or NULL: size of the kept set (1 for greedy)
+ *  out_kept_mask  [B, ceil(V/32)] uint32 or NULL: bit j%32 of word j/32 set for
+ *               every kept id (for tests; costs an extra write)
+ *  out_row_status [B] int32 or NULL
+ *  ws, ws_bytes  device workspace of at least vs_workspace_size() bytes
+ */
+vs_status vs_sample(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
+                    const float* temperature, const int32_t* top_k,
+                    const float* top_p, const float* min_p,
+                    const uint64_t* seeds, uint32_t hints, int32_t* out_ids,
+                    int32_t* out_kept_count, uint32_t* out_kept_mask,
+                    int32_t* out_row_status, void* ws, size_t ws_bytes,
+                    hipStream_t stream);
+
+/*
+ * vs_logprobs — log-softmax log-probabilities of the buffer given (temperature
+ * 1, no truncation), as the TT sampling README's LogProbsCalculator ("Key
+ * Components": numerically stable log-softmax via the max and the sum of
+ * exponentials) and the Tunix sampler page (greedy argmax plus a log-softmax)
+ * describe. Computed in fp32: lp_j = (x_j - max) - log(sum exp(x - max)).
+ *
+ *  token_ids, out_token_logprob: [B] each, or both NULL; lp of the given id.
+ *  k            0 <= k <= min(VS_LOGPROB_K_MAX, V)
+ *  out_topk_ids, out_topk_logprobs: [B, k] (NULL when k = 0): the k largest
+ *               logits, larger first and lower id first among equals.
+ *  out_full     [B, ld_out] fp32 or NULL: every lp of the row (ld_out >= V)
+ *  out_row_status [B] int32 or NULL. A row with bad logits gets NaN log-probs and
+ *               top-k ids -1; an id outside [0,V) gets NaN.
+ */
+vs_status vs_logprobs(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
+                      const int32_t* token_ids, float* out_token_logprob, int k,
+                      int32_t* out_topk_ids, float* out_topk_logprobs,
+                      float* out_full, int64_t ld_out, int32_t* out_row_status,
+                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Profiling aid (not part of the sampling step). While active on the calling
+ * host thread, every kernel stage that a vs_* call enqueues is bracketed by
+ * hipEventRecord(events[2i]) and hipEventRecord(events[2i+1]) on that call's
+ * stream, i = 0, 1, ... in enqueue order, until `capacity` events are used.
+ * `events` is a host array of events the caller created (hipEventCreate) and
+ * owns. Stage names: "select", "row", "gumbel", "lse_select", "lse_row",
+ * "lse_full", "penalize". vs_profile_end stops recording on this thread,
+ * copies up to max_names stage-name pointers (static strings) to `names` (may
+ * be NULL) and returns the number of stages recorded.
+ */
+vs_status vs_profile_begin(hipEvent_t* events, int capacity);
+int vs_profile_end(const char** names, int max_names);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VS_H */

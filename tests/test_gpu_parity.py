@@ -1,0 +1,323 @@
+"""GPU parity: the HIP library, called through the C ABI, against the CPU oracle.
+
+Bar: token ids, kept counts, kept sets and row status bit-exact (ids of rows
+whose two best Gumbel scores are within 1e-6 relative are exempt and counted);
+penalised logits bit-exact (0 ulp fp32, and the single rounding of bf16);
+log-probs within 1e-5 absolute.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import (LOGPROB_ATOL, compare_sample, dev, from_device, gpu_sample, host_pad,
+                    oracle_sample, params_from, random_params, to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decode_token_sampling_amd as vs
+    vs.load()
+    oracle.build(force=False)
+
+
+# ---------------------------------------------------------------- sampling grid
+# Widths around the 4096-id tile edges and the workload widths, several row
+# shapes (ties, flat rows, masked -inf ids) and parameters covering every path.
+WIDTHS = [1, 2, 7, 63, 64, 100, 1000, 4095, 4096, 4097, 8191, 12345, 32000, 70001]
+
+
+def _row_shapes(seed, B, V, dtype):
+    kinds = ["rank", "ties", "normal", "flat"]
+    x = np.concatenate([synth.random_rows(seed + i, (B + 3) // 4, V, dtype, kind=k)
+                        for i, k in enumerate(kinds)])[:B]
+    x = np.ascontiguousarray(x)
+    rng = np.random.default_rng(seed)
+    if V > 4:  # masked ids (-inf) on a few rows
+        neg = np.float32(-np.inf)
+        for r in range(0, B, 5):
+            cols = rng.choice(V, V // 3, replace=False)
+            if dtype == "bf16":
+                x[r, cols] = synth.f32_to_bf16_bits(np.array([neg]))[0]
+            else:
+                x[r, cols] = neg
+    return x
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", WIDTHS)
+def test_sample_grid(V, dtype):
+    B = 27
+    x = _row_shapes(1000 + V, B, V, dtype)
+    rng = np.random.default_rng(V)
+    w = random_params(rng, B, V)
+    g = gpu_sample(to_device(x), V, w)
+    o = oracle_sample(x, V, w)
+    compare_sample(g, o)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_sample_padded_and_unaligned_rows(dtype):
+    V = 5000
+    x = _row_shapes(77, 18, V, dtype)
+    w = random_params(np.random.default_rng(5), 18, V)
+    o = oracle_sample(x, V, w)
+    for ld in (V + 1, V + 8, V + 37):  # padding columns hold NaN: never read
+        g = gpu_sample(to_device(x, ld=ld), V, w)
+        compare_sample(g, o)
+
+
+def test_sample_seeds_change_draw_and_repeat():
+    V, B = 3000, 16
+    x = synth.random_rows(3, B, V, kind="flat")
+    w = dict(temperature=np.ones(B, np.float32), top_k=np.zeros(B, np.int32),
+             top_p=np.ones(B, np.float32), min_p=np.zeros(B, np.float32),
+             seeds=np.arange(B, dtype=np.uint64))
+    xd = to_device(x)
+    a = gpu_sample(xd, V, w)
+    b = gpu_sample(xd, V, w)
+    assert np.array_equal(a["ids"], b["ids"])
+    w2 = dict(w, seeds=np.arange(B, dtype=np.uint64) + 1000)
+    c = gpu_sample(xd, V, w2)
+    assert (a["ids"] != c["ids"]).sum() > B // 2
+    compare_sample(c, oracle_sample(x, V, w2))
+
+
+def test_sample_invalid_rows():
+    V, B = 300, 9
+    x = synth.random_rows(4, B, V)
+    x[1, 7] = np.nan
+    x[2, 299] = np.inf
+    x[3, :] = -np.inf
+    x[8, :] = 3e38
+    w = dict(temperature=np.array([1, 1, 1, 1, -1, np.nan, 1, 1, 1e-3], np.float32),
+             top_k=np.array([0, 0, 0, 0, 0, 0, -1, 0, 0], np.int32),
+             top_p=np.array([1, 1, 1, 1, 1, 1, 1, 1.5, 1], np.float32),
+             min_p=np.zeros(B, np.float32), seeds=np.zeros(B, np.uint64))
+    g = gpu_sample(to_device(x), V, w)
+    o = oracle_sample(x, V, w)
+    compare_sample(g, o)
+    assert g["status"].tolist() == [0, 2, 2, 2, 1, 1, 1, 1, 1]
+    assert (g["ids"][1:] == -1).all()
+
+
+def test_sample_topk_unsupported_and_k_at_least_v():
+    V, B = 3000, 3
+    x = synth.random_rows(6, B, V)
+    w = dict(temperature=np.ones(B, np.float32), top_k=np.array([1025, 3000, 5000], np.int32),
+             top_p=np.full(B, 0.9, np.float32), min_p=np.zeros(B, np.float32),
+             seeds=np.zeros(B, np.uint64))
+    g = gpu_sample(to_device(x), V, w)
+    compare_sample(g, oracle_sample(x, V, w))
+    assert g["status"].tolist() == [8, 0, 0]
+
+
+def test_sample_hints():
+    import decode_token_sampling_amd as vs
+    V, B = 9000, 12
+    x = synth.random_rows(8, B, V)
+    w = random_params(np.random.default_rng(1), B, V, kinds=["greedy", "kfast", "kslow", "topp"])
+    o = oracle_sample(x, V, w)
+    g = gpu_sample(to_device(x), V, w, hints=vs.HINT_NO_FULLVOCAB)
+    full = np.arange(B) % 4 == 3
+    assert (g["status"][full] == vs.ROW_HINT_VIOLATED).all() and (g["ids"][full] == -1).all()
+    compare_sample(g, o, rows=np.nonzero(~full)[0])
+    g = gpu_sample(to_device(x), V, w, hints=vs.HINT_ALL_GREEDY)
+    greedy = np.arange(B) % 4 == 0
+    assert (g["status"][~greedy] == vs.ROW_HINT_VIOLATED).all()
+    compare_sample(g, o, rows=np.nonzero(greedy)[0])
+
+
+def test_sample_heavy_ties_take_exact_path():
+    """Rows of a handful of distinct values: tile candidate lists overflow and
+    the exact row-level selection decides (ties to the lowest ids)."""
+    V, B = 20000, 12
+    x = (np.random.default_rng(2).integers(0, 3, (B, V)).astype(np.float32))
+    w = dict(temperature=np.ones(B, np.float32),
+             top_k=np.array([2, 20, 64, 65, 500, 1024, 0, 0, 0, 7, 33, 0], np.int32),
+             top_p=np.array([1, 1, 1, 1, 0.5, 0.9, 0.3, 0.01, 1, 0.7, 0.6, 0.999], np.float32),
+             min_p=np.array([0, 0, 0, 0, 0, 0, 0, 0, 0.5, 0, 0, 0.2], np.float32),
+             seeds=np.arange(B, dtype=np.uint64))
+    compare_sample(gpu_sample(to_device(x), V, w), oracle_sample(x, V, w))
+
+
+def test_sample_constant_rows_fallback_inside_bucket():
+    """Every id in one top-p bucket (> 8192 ids): the mass-weighted radix
+    select and tie cut inside the bucket decide."""
+    V, B = 50000, 4
+    x = np.zeros((B, V), np.float32)
+    x[1] = np.float32(0.25) * (np.arange(V) % 2)   # two values
+    x[2, ::7] = 1e-6
+    w = dict(temperature=np.ones(B, np.float32), top_k=np.zeros(B, np.int32),
+             top_p=np.array([0.37, 0.8, 0.5, 0.999], np.float32), min_p=np.zeros(B, np.float32),
+             seeds=np.arange(B, dtype=np.uint64))
+    compare_sample(gpu_sample(to_device(x), V, w), oracle_sample(x, V, w))
+
+
+# ---------------------------------------------------------------- penalties
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_penalize_parity(dtype):
+    import decode_token_sampling_amd as vs
+    rng = np.random.default_rng(11)
+    B, V = 24, 40000
+    x = synth.random_rows(12, B, V, dtype, kind="rank")
+    pl = rng.integers(0, 1500, B)
+    ol = rng.integers(0, 300, B)
+    pl[3] = 0
+    ol[4] = 0
+    pids, poff = synth._csr([synth.zipf_ids(rng, int(n), V) for n in pl])
+    oids, ooff = synth._csr([synth.zipf_ids(rng, int(n), V) for n in ol])
+    oids = oids.copy()
+    if len(oids) > 5:
+        oids[2] = -3            # bad ids are skipped and reported
+        oids[5] = V
+    pres = rng.uniform(-0.5, 1.0, B).astype(np.float32)
+    freq = rng.uniform(-0.2, 1.0, B).astype(np.float32)
+    rep = rng.uniform(0.7, 1.5, B).astype(np.float32)
+    rep[7] = 0.0                # bad parameter: row untouched
+    xd = to_device(x)
+    st = vs.penalize(xd, dev(pids, np.int32), dev(poff, np.int32), dev(oids, np.int32),
+                     dev(ooff, np.int32), dev(pres, np.float32), dev(freq, np.float32),
+                     dev(rep, np.float32)).cpu().numpy()
+    xo = x.copy()
+    so = oracle.penalize(xo, V, pids, poff, oids, ooff, pres, freq, rep)
+    assert np.array_equal(st, so)
+    got = from_device(xd, V)
+    assert np.array_equal(got.view(np.uint8), xo.view(np.uint8))
+
+
+def test_penalize_long_history_many_classes():
+    import decode_token_sampling_amd as vs
+    rng = np.random.default_rng(13)
+    B, V = 3, 300000
+    x = synth.random_rows(14, B, V)
+    lists = [rng.integers(0, V, 60000).astype(np.int32), np.arange(0, V, 7, dtype=np.int32),
+             np.zeros(5, np.int32)]
+    oids, ooff = synth._csr(lists)
+    rep = np.full(B, 1.3, np.float32)
+    freq = np.full(B, 0.01, np.float32)
+    xd = to_device(x)
+    vs.penalize(xd, output_ids=dev(oids, np.int32), output_off=dev(ooff, np.int32),
+                frequency=dev(freq, np.float32), repetition=dev(rep, np.float32))
+    xo = x.copy()
+    oracle.penalize(xo, V, None, None, oids, ooff, None, freq, rep)
+    assert np.array_equal(from_device(xd, V), xo)
+
+
+# ---------------------------------------------------------------- log-probs
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [1, 5, 64, 4097, 33333])
+def test_logprobs_parity(V, dtype):
+    import decode_token_sampling_amd as vs
+    B = 9
+    x = _row_shapes(50 + V, B, V, dtype)
+    rng = np.random.default_rng(V)
+    tok = rng.integers(0, V, B).astype(np.int32)
+    k = min(V, 20)
+    g = vs.logprobs(to_device(x), dev(tok, np.int32), k=k, full=True, V=V)
+    torch.cuda.synchronize()
+    o = oracle.logprobs(x, V, tok, k=k, full=True)
+    assert np.array_equal(g["status"].cpu().numpy(), o["status"])
+    assert np.allclose(g["token_lp"].cpu().numpy(), o["token_lp"], atol=LOGPROB_ATOL, rtol=0)
+    assert np.array_equal(g["topk_ids"].cpu().numpy(), o["topk_ids"])
+    assert np.allclose(g["topk_lp"].cpu().numpy(), o["topk_lp"], atol=LOGPROB_ATOL, rtol=0)
+    full = g["full"].cpu().numpy()
+    of = o["full"]
+    fin = np.isfinite(of)
+    assert np.array_equal(np.isfinite(full), fin) and np.array_equal(full[~fin], of[~fin])
+    assert np.abs(full[fin] - of[fin]).max() <= LOGPROB_ATOL
+
+
+def test_logprobs_ties_and_bad_rows():
+    import decode_token_sampling_amd as vs
+    V, B = 9000, 5
+    x = np.random.default_rng(3).integers(0, 2, (B, V)).astype(np.float32)
+    x[1, 5] = np.nan
+    x[2, :] = -np.inf
+    tok = np.array([0, 1, 2, V + 3, -1], np.int32)
+    g = vs.logprobs(to_device(x), dev(tok, np.int32), k=64, V=V)
+    torch.cuda.synchronize()
+    o = oracle.logprobs(x, V, tok, k=64)
+    assert np.array_equal(g["status"].cpu().numpy(), o["status"])
+    assert np.array_equal(g["topk_ids"].cpu().numpy(), o["topk_ids"])
+    gl, ol = g["token_lp"].cpu().numpy(), o["token_lp"]
+    assert np.array_equal(np.isnan(gl), np.isnan(ol))
+    ok = ~np.isnan(ol)
+    assert np.allclose(gl[ok], ol[ok], atol=LOGPROB_ATOL, rtol=0)
+
+
+# ---------------------------------------------------------------- the five workloads
+def _run_workload(name, sample_rows=None):
+    import decode_token_sampling_amd as vs
+    wl = synth.make(name)
+    xd = to_device(wl.logits)
+    x = wl.logits
+    if wl.has_penalties:
+        st = vs.penalize(xd, dev(wl.prompt_ids, np.int32), dev(wl.prompt_off, np.int32),
+                         dev(wl.output_ids, np.int32), dev(wl.output_off, np.int32),
+                         dev(wl.presence, np.float32), dev(wl.frequency, np.float32),
+                         dev(wl.repetition, np.float32)).cpu().numpy()
+        x = x.copy()
+        so = oracle.penalize(x, wl.V, wl.prompt_ids, wl.prompt_off, wl.output_ids, wl.output_off,
+                             wl.presence, wl.frequency, wl.repetition)
+        assert np.array_equal(st, so)
+        assert np.array_equal(from_device(xd, wl.V).view(np.uint8), x.view(np.uint8))
+    w = params_from(wl)
+    g = gpu_sample(xd, wl.V, w)
+    o = oracle_sample(x, wl.V, w, rows=sample_rows)
+    near = compare_sample(g, o, rows=sample_rows)
+    print(f"{name}: near-tie rows exempt from the id check: {near}")
+    return wl, xd, x, g
+
+
+def test_workload_w4x32000_f32():
+    import decode_token_sampling_amd as vs
+    wl, xd, x, g = _run_workload("w4x32000_f32")
+    lp = vs.logprobs(xd, dev(g["ids"], np.int32), k=0)
+    torch.cuda.synchronize()
+    o = oracle.logprobs(x, wl.V, g["ids"])
+    assert np.allclose(lp["token_lp"].cpu().numpy(), o["token_lp"], atol=LOGPROB_ATOL, rtol=0)
+
+
+def test_workload_w32x151936_bf16():
+    _run_workload("w32x151936_bf16")
+
+
+def test_workload_w256x248320_f32():
+    import decode_token_sampling_amd as vs
+    wl, xd, x, g = _run_workload("w256x248320_f32")
+    lp = vs.logprobs(xd, dev(g["ids"], np.int32), k=20)
+    torch.cuda.synchronize()
+    rows = np.arange(0, wl.B, 8)
+    o = oracle.logprobs(np.ascontiguousarray(x[rows]), wl.V, g["ids"][rows], k=20)
+    assert np.allclose(lp["token_lp"].cpu().numpy()[rows], o["token_lp"], atol=LOGPROB_ATOL, rtol=0)
+    assert np.array_equal(lp["topk_ids"].cpu().numpy()[rows], o["topk_ids"])
+    assert np.allclose(lp["topk_lp"].cpu().numpy()[rows], o["topk_lp"], atol=LOGPROB_ATOL, rtol=0)
+
+
+def test_workload_w1024x128256_f32():
+    import decode_token_sampling_amd as vs
+    wl = synth.make("w1024x128256_f32")
+    xd = to_device(wl.logits)
+    g = gpu_sample(xd, wl.V, params_from(wl), mask=False)
+    assert (g["status"] == 0).all()
+    assert np.array_equal(g["ids"], np.argmax(wl.logits, axis=1))  # greedy = first maximum
+    lp = vs.logprobs(xd, dev(g["ids"], np.int32), k=20, full=True)
+    torch.cuda.synchronize()
+    rows = np.arange(0, wl.B, 37)
+    o = oracle.logprobs(np.ascontiguousarray(wl.logits[rows]), wl.V, g["ids"][rows], k=20, full=True)
+    full = lp["full"][torch.from_numpy(rows).cuda()].cpu().numpy()
+    assert np.abs(full - o["full"]).max() <= LOGPROB_ATOL
+    assert np.array_equal(lp["topk_ids"].cpu().numpy()[rows], o["topk_ids"])
+    # every row: the log-probs sum to one
+    s = torch.logsumexp(lp["full"].double(), dim=1).cpu().numpy()
+    assert np.abs(s).max() < 1e-5
+
+
+def test_workload_w64x262144_bf16():
+    _run_workload("w64x262144_bf16")
