@@ -5,8 +5,8 @@
 
 A step is one pass of the whole sampling path over one batch of synthetic
 logits already resident in HBM: occurrence penalties when the workload has
-them, the draw (vs_sample) and the log-probabilities the workload asks for
-(vs_logprobs). Rotated copies of the inputs (together larger than the 256 MB
+them (vs_penalize), then the draw and the log-probabilities the workload asks
+for in one call (vs_sample_logprobs, one read of the logits). Rotated copies of the inputs (together larger than the 256 MB
 Infinity Cache) keep repeat reads from being served on chip. Prints one JSON
 line: rows/s for the whole step, the logits bandwidth it implies, the roofline
 of the dominant kernel (timed with HIP events on the stream it runs on) and
@@ -33,8 +33,8 @@ HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "w256x248320_f32"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {"select": "k_select.hip", "lse_select": "k_select.hip", "row": "k_row.hip",
-                  "lse_row": "k_row.hip", "gumbel": "k_gumbel.hip", "lse_full": "k_gumbel.hip",
-                  "penalize": "k_penalize.hip"}
+                  "lse_row": "k_row.hip", "row_full": "k_row.hip", "gumbel": "k_gumbel.hip",
+                  "lse_full": "k_gumbel.hip", "penalize": "k_penalize.hip"}
 
 
 class HipEvents:
@@ -122,24 +122,27 @@ def build_step(vs, torch, wl, copies, dev):
     kept = torch.empty(B, dtype=torch.int32, device=dev)
     st = torch.empty(B, dtype=torch.int32, device=dev)
     pst = torch.empty(B, dtype=torch.int32, device=dev)
-    lst = torch.empty(B, dtype=torch.int32, device=dev)
     full = torch.empty((B, V), dtype=torch.float32, device=dev) if wl.full_logprobs else None
     greedy = bool((wl.temperature == 0).all())
     hints = vs.HINT_ALL_GREEDY if greedy else (
         vs.HINT_NO_FULLVOCAB if bool(((wl.top_k > 0) & (wl.top_k < V)).all()) else 0)
     want_token_lp = not wl.full_logprobs
 
+    tlp = torch.empty(B, dtype=torch.float32, device=dev) if want_token_lp else None
+    tids = torch.empty((B, wl.logprob_k), dtype=torch.int32, device=dev) if wl.logprob_k else None
+    tlps = torch.empty((B, wl.logprob_k), dtype=torch.float32, device=dev) if wl.logprob_k else None
+
     def step(i):
         x = xs[i % copies]
         if pen is not None:
             vs.penalize(x, *pen, row_status=pst)
-        vs.sample(x, T, K, P, MP, S, hints=hints, ws=ws, out_ids=ids, kept=kept, row_status=st)
-        vs.logprobs(x, ids if want_token_lp else None, k=wl.logprob_k, ws=ws, out_full=full,
-                    row_status=lst)
+        vs.sample_logprobs(x, T, K, P, MP, S, hints=hints, k=wl.logprob_k,
+                           token_logprob=want_token_lp, ws=ws, out_ids=ids, kept=kept,
+                           row_status=st, out_token_lp=tlp, out_topk_ids=tids, out_topk_lp=tlps,
+                           out_full=full)
 
     parts = (["vs_penalize"] if pen is not None else []) + [
-        f"vs_sample(hints={hints})",
-        "vs_logprobs(" + ", ".join(p for p in [
+        f"vs_sample_logprobs(hints={hints}; " + ", ".join(p for p in [
             "sampled-id lp" if want_token_lp else "", f"top-{wl.logprob_k}" if wl.logprob_k else "",
             "full [B,V] write" if wl.full_logprobs else ""] if p) + ")"]
     outs = dict(ids=ids, kept=kept, status=st)

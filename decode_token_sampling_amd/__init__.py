@@ -21,7 +21,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "VsError", "load", "workspace_size", "workspace", "penalize", "sample",
-    "logprobs", "ROW_BAD_PARAM", "ROW_BAD_LOGITS", "ROW_BAD_TOKEN_ID", "ROW_TOPK_UNSUPPORTED",
+    "logprobs", "sample_logprobs", "ROW_BAD_PARAM", "ROW_BAD_LOGITS", "ROW_BAD_TOKEN_ID", "ROW_TOPK_UNSUPPORTED",
     "ROW_HINT_VIOLATED", "HINT_NONE", "HINT_NO_FULLVOCAB", "HINT_ALL_GREEDY", "MAX_V",
     "TOPK_MAX", "LOGPROB_K_MAX", "EXPORTED_SYMBOLS",
 ]
@@ -41,7 +41,7 @@ TOPK_MAX = 1024
 LOGPROB_K_MAX = 64
 
 EXPORTED_SYMBOLS = ("vs_workspace_size", "vs_status_string", "vs_penalize", "vs_sample",
-                    "vs_logprobs", "vs_profile_begin", "vs_profile_end")
+                    "vs_logprobs", "vs_sample_logprobs", "vs_profile_begin", "vs_profile_end")
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "workspace too small", 3: "unsupported",
            4: "HIP launch failure"}
@@ -70,10 +70,12 @@ def load() -> ctypes.CDLL:
     lib.vs_penalize.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, P, P, P, P]
     lib.vs_sample.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, u32, P, P, P, P, P, sz, P]
     lib.vs_logprobs.argtypes = [P, i32, i32, i32, i64, P, P, i32, P, P, P, i64, P, P, sz, P]
+    lib.vs_sample_logprobs.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, u32, P, P, P, P, P,
+                                       i32, P, P, P, i64, P, sz, P]
     lib.vs_profile_begin.argtypes = [P, i32]
     lib.vs_profile_end.argtypes = [ctypes.POINTER(ctypes.c_char_p), i32]
-    for f in ("vs_workspace_size", "vs_penalize", "vs_sample", "vs_logprobs", "vs_profile_begin",
-              "vs_profile_end"):
+    for f in ("vs_workspace_size", "vs_penalize", "vs_sample", "vs_logprobs",
+              "vs_sample_logprobs", "vs_profile_begin", "vs_profile_end"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -204,3 +206,50 @@ def logprobs(logits, token_ids=None, k=0, full=False, V=None, ws=None, out_full=
     if code:
         raise VsError("vs_logprobs", code)
     return dict(token_lp=tlp, topk_ids=tids, topk_lp=tlps, full=fo, status=st)
+
+
+def sample_logprobs(logits, temperature=None, top_k=None, top_p=None, min_p=None, seeds=None,
+                    hints=0, k=0, token_logprob=True, full=False, V=None, ws=None, out_ids=None,
+                    kept=None, mask=False, row_status=None, out_token_lp=None, out_topk_ids=None,
+                    out_topk_lp=None, out_full=None, stream=None) -> dict:
+    """vs_sample and the log-probs of the sampled ids (and top-k) in one pass over the
+    logits (vs_sample_logprobs). Returns dict(ids, kept, status, token_lp, topk_ids,
+    topk_lp, full[, mask])."""
+    B, V, ld = _logits_args(logits, V)
+    dev = logits.device
+    if ws is None:
+        ws = workspace(B, V, logits.dtype, dev)
+    ids = out_ids if out_ids is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    kc = kept if kept is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    st = row_status if row_status is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    tlp = out_token_lp
+    if token_logprob and tlp is None:
+        tlp = torch.empty(B, dtype=torch.float32, device=dev)
+    tids = out_topk_ids if out_topk_ids is not None else (
+        torch.empty((B, k), dtype=torch.int32, device=dev) if k > 0 else None)
+    tlps = out_topk_lp if out_topk_lp is not None else (
+        torch.empty((B, k), dtype=torch.float32, device=dev) if k > 0 else None)
+    fo = out_full
+    if full and fo is None:
+        fo = torch.empty((B, V), dtype=torch.float32, device=dev)
+    mk = None
+    if mask is True:
+        mk = torch.empty((B, (V + 31) // 32), dtype=torch.int32, device=dev)
+    elif isinstance(mask, torch.Tensor):
+        mk = mask
+    code = load().vs_sample_logprobs(
+        logits.data_ptr(), _dtype_code(logits), B, V, ld,
+        _ptr(temperature, torch.float32, B, "temperature"), _ptr(top_k, torch.int32, B, "top_k"),
+        _ptr(top_p, torch.float32, B, "top_p"), _ptr(min_p, torch.float32, B, "min_p"),
+        _ptr(seeds, torch.int64, B, "seeds"), int(hints), _ptr(ids, torch.int32, B, "out_ids"),
+        _ptr(kc, torch.int32, B, "kept"), _ptr(mk, torch.int32, name="mask"),
+        _ptr(st, torch.int32, B, "row_status"), _ptr(tlp, torch.float32, B, "token_lp"), int(k),
+        _ptr(tids, torch.int32, name="topk_ids"), _ptr(tlps, torch.float32, name="topk_lp"),
+        fo.data_ptr() if fo is not None else None, fo.stride(0) if fo is not None else 0,
+        _ptr(ws, torch.uint8, name="ws"), ws.numel(), _stream(stream))
+    if code:
+        raise VsError("vs_sample_logprobs", code)
+    out = dict(ids=ids, kept=kc, status=st, token_lp=tlp, topk_ids=tids, topk_lp=tlps, full=fo)
+    if mk is not None:
+        out["mask"] = mk
+    return out

@@ -6,9 +6,10 @@
 // (everything; e >= min_p; or for top-p "key > tau, or key == tau and
 // id <= id_cut"), and for kept ids forms score = e / -log(u(seed, row, id)).
 // Each tile keeps its best (score desc, id asc) and its kept count.
-// K4 (one workgroup per row) reduces the tiles: the sampled id and the kept
-// count. The argmax compares the true id, never thread or tile order, so the
-// result does not depend on the partition (vllm.cpp #1997, "The kernel").
+// K4 (one workgroup per row) reduces the tiles: the sampled id, the kept count
+// and, in the fused call, the sampled id's log-probability. The argmax compares
+// true ids, never thread or tile order, so the result does not depend on the
+// partition (vllm.cpp pull request #1997, "The kernel (#1984)").
 #include "vs_device.h"
 #include "vs_kernels.h"
 
@@ -18,28 +19,28 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kPerThread = kGumTile / kThreads;  // 16
 
+__device__ __forceinline__ bool full_row(uint32_t mode) {
+  return mode == kRowFullNone || mode == kRowFullMinP || mode == kRowFullTopP;
+}
+
 template <typename E>
-__global__ __launch_bounds__(kThreads) void k_gumbel_partial(
-    const E* __restrict__ logits, int B, int V, int64_t ld, bool aligned,
-    const float* __restrict__ temperature, const float* __restrict__ min_p,
-    const uint64_t* __restrict__ seeds, const RowDesc* __restrict__ desc, int ntile,
-    GPart* __restrict__ gpart, uint32_t* __restrict__ out_mask) {
+__global__ __launch_bounds__(kThreads) void k_gumbel_partial(Job j) {
   __shared__ double sd[kThreads / kWave];
   __shared__ int si[kThreads / kWave];
   int row, tile;
-  if (!xcd_row_tile(blockIdx.x, B, ntile, &row, &tile)) return;
-  const RowDesc d = desc[row];
-  if (d.mode == kFullSkip) return;  // uniform over the block
+  if (!xcd_row_tile(blockIdx.x, j.B, j.ntile3, &row, &tile)) return;
+  const RowDesc d = j.desc[row];
+  if (!full_row(d.mode)) return;  // uniform over the block
   constexpr int EPV = Epv<E>::n;
   constexpr int NV = kPerThread / EPV;
-  const float T = temperature ? temperature[row] : 1.0f;
-  const float mp = min_p ? min_p[row] : 0.0f;
-  const uint64_t rs = row_stream(seeds ? seeds[row] : 0ull, row);
-  const E* rowp = logits + static_cast<int64_t>(row) * ld;
+  const float T = j.T ? j.T[row] : 1.0f;
+  const float mp = j.mp ? j.mp[row] : 0.0f;
+  const uint64_t rs = row_stream(j.seeds ? j.seeds[row] : 0ull, row);
+  const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
   const int base = tile * kGumTile;
-  const bool vec = aligned && (base + kGumTile <= V);
-  const int mwords = (V + 31) / 32;
-  uint32_t* mask_row = out_mask ? out_mask + static_cast<size_t>(row) * mwords : nullptr;
+  const bool vec = j.aligned && (base + kGumTile <= j.V);
+  const int mwords = (j.V + 31) / 32;
+  uint32_t* mask_row = j.out_mask ? j.out_mask + static_cast<size_t>(row) * mwords : nullptr;
 
   double best = -1.0;
   int best_id = 0x7fffffff;
@@ -53,31 +54,31 @@ __global__ __launch_bounds__(kThreads) void k_gumbel_partial(
       unpack16(raw, x, rowp);
     } else {
 #pragma unroll
-      for (int c = 0; c < EPV; ++c) x[c] = (j0 + c < V) ? to_f32(rowp[j0 + c]) : -kInf;
+      for (int c = 0; c < EPV; ++c) x[c] = (j0 + c < j.V) ? to_f32(rowp[j0 + c]) : -kInf;
     }
     uint32_t bits = 0;
 #pragma unroll
     for (int c = 0; c < EPV; ++c) {
-      const int j = j0 + c;
-      if (j >= V) continue;
+      const int id = j0 + c;
+      if (id >= j.V) continue;
       const float s = (T == 1.0f) ? x[c] : x[c] / T;
       const float e = pinned_exp(s - d.m);
       bool keep;
-      if (d.mode == kFullNone) {
+      if (d.mode == kRowFullNone) {
         keep = true;
-      } else if (d.mode == kFullMinP) {
+      } else if (d.mode == kRowFullMinP) {
         keep = e >= mp;
       } else {
         const uint32_t key = f2key(s);
-        keep = key > d.tau || (key == d.tau && j <= d.id_cut);
+        keep = key > d.tau || (key == d.tau && id <= d.id_cut);
       }
       if (keep) {
         ++kept;
-        bits |= 1u << (j & 31);
-        const double sc = gumbel_score(e, rs, j);
-        if (sc > best || (sc == best && j < best_id)) {
+        bits |= 1u << (id & 31);
+        const double sc = gumbel_score(e, rs, id);
+        if (sc > best || (sc == best && id < best_id)) {
           best = sc;
-          best_id = j;
+          best_id = id;
         }
       }
     }
@@ -86,21 +87,20 @@ __global__ __launch_bounds__(kThreads) void k_gumbel_partial(
   const double bb = block_max(best, sd);
   const int bid = block_min(best == bb ? best_id : 0x7fffffff, si);
   const int bk = block_sum(kept, si);
-  if (threadIdx.x == 0) gpart[static_cast<size_t>(row) * ntile + tile] = GPart{bb, bid, bk};
+  if (threadIdx.x == 0) j.gpart[static_cast<size_t>(row) * j.ntile3 + tile] = GPart{bb, bid, bk};
 }
 
-__global__ __launch_bounds__(kThreads) void k_gumbel_final(
-    int B, int ntile, const RowDesc* __restrict__ desc, const GPart* __restrict__ gpart,
-    int32_t* __restrict__ out_ids, int32_t* __restrict__ out_kept) {
+template <typename E>
+__global__ __launch_bounds__(kThreads) void k_gumbel_final(Job j) {
   __shared__ double sd[kThreads / kWave];
   __shared__ int si[kThreads / kWave];
   const int row = blockIdx.x;
-  if (desc[row].mode == kFullSkip) return;
-  const GPart* g = gpart + static_cast<size_t>(row) * ntile;
+  if (!full_row(j.desc[row].mode)) return;
+  const GPart* g = j.gpart + static_cast<size_t>(row) * j.ntile3;
   double best = -1.0;
   int best_id = 0x7fffffff;
   int kept = 0;
-  for (int t = threadIdx.x; t < ntile; t += blockDim.x) {
+  for (int t = threadIdx.x; t < j.ntile3; t += blockDim.x) {
     const GPart p = g[t];
     kept += p.kept;
     if (p.kept && (p.score > best || (p.score == best && p.id < best_id))) {
@@ -112,26 +112,35 @@ __global__ __launch_bounds__(kThreads) void k_gumbel_final(
   const int bid = block_min(best == bb ? best_id : 0x7fffffff, si);
   const int bk = block_sum(kept, si);
   if (threadIdx.x == 0) {
-    out_ids[row] = bid;
-    if (out_kept) out_kept[row] = bk;
+    if (bid < 0 || bid >= j.V) {  // unreachable: the row maximum is always kept
+      j.out_ids[row] = -1;
+      if (j.out_kept) j.out_kept[row] = 0;
+      if (j.out_status) j.out_status[row] = VS_ROW_BAD_LOGITS;
+      if (j.tok_sampled) j.out_tok_lp[row] = __builtin_nanf("");
+      return;
+    }
+    j.out_ids[row] = bid;
+    if (j.out_kept) j.out_kept[row] = bk;
+    if (j.tok_sampled) {
+      const float2 ml = j.rlse[row];
+      const float x = to_f32(static_cast<const E*>(j.logits)[static_cast<int64_t>(row) * j.ld + bid]);
+      j.out_tok_lp[row] = (x - ml.x) - ml.y;
+    }
   }
 }
 
 // lp = (x - max) - log(sum exp(x - max)) for every id of the row.
 template <typename E>
-__global__ __launch_bounds__(kThreads) void k_lse_full(
-    const E* __restrict__ logits, int B, int V, int64_t ld, bool aligned,
-    const float2* __restrict__ rlse, int ntile, float* __restrict__ out, int64_t ld_out,
-    bool out_vec) {
+__global__ __launch_bounds__(kThreads) void k_lse_full(Job j, int ntile, bool out_vec) {
   int row, tile;
-  if (!xcd_row_tile(blockIdx.x, B, ntile, &row, &tile)) return;
+  if (!xcd_row_tile(blockIdx.x, j.B, ntile, &row, &tile)) return;
   constexpr int EPV = Epv<E>::n;
   constexpr int NV = kPerThread / EPV;
-  const float2 ml = rlse[row];
-  const E* rowp = logits + static_cast<int64_t>(row) * ld;
-  float* orow = out + static_cast<int64_t>(row) * ld_out;
+  const float2 ml = j.rlse[row];
+  const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
+  float* orow = j.out_full + static_cast<int64_t>(row) * j.ld_out;
   const int base = tile * kFullTile;
-  const bool vec = aligned && out_vec && (base + kFullTile <= V);
+  const bool vec = j.aligned && out_vec && (base + kFullTile <= j.V);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int j0 = base + (i * kThreads + static_cast<int>(threadIdx.x)) * EPV;
@@ -151,8 +160,8 @@ __global__ __launch_bounds__(kThreads) void k_lse_full(
     } else {
 #pragma unroll
       for (int c = 0; c < EPV; ++c) {
-        const int j = j0 + c;
-        if (j < V) orow[j] = (to_f32(rowp[j]) - ml.x) - ml.y;
+        const int id = j0 + c;
+        if (id < j.V) orow[id] = (to_f32(rowp[id]) - ml.x) - ml.y;
       }
     }
   }
@@ -160,38 +169,29 @@ __global__ __launch_bounds__(kThreads) void k_lse_full(
 
 }  // namespace
 
-hipError_t launch_gumbel(const SampleArgs& a, const WsLayout& L, char* ws, hipStream_t st) {
-  const auto* desc = reinterpret_cast<const RowDesc*>(ws + L.desc);
-  auto* gp = reinterpret_cast<GPart*>(ws + L.gpart);
-  const int grid = xcd_grid(a.B, L.ntile3);
-  if (a.dt == VS_F32)
-    hipLaunchKernelGGL(k_gumbel_partial<float>, dim3(grid), dim3(kThreads), 0, st,
-                       static_cast<const float*>(a.logits), a.B, a.V, a.ld, a.aligned,
-                       a.temperature, a.min_p, a.seeds, desc, L.ntile3, gp, a.out_mask);
+hipError_t launch_gumbel(const Job& j, hipStream_t st) {
+  const int grid = xcd_grid(j.B, j.ntile3);
+  if (j.dt == VS_F32)
+    hipLaunchKernelGGL(k_gumbel_partial<float>, dim3(grid), dim3(kThreads), 0, st, j);
   else
-    hipLaunchKernelGGL(k_gumbel_partial<uint16_t>, dim3(grid), dim3(kThreads), 0, st,
-                       static_cast<const uint16_t*>(a.logits), a.B, a.V, a.ld, a.aligned,
-                       a.temperature, a.min_p, a.seeds, desc, L.ntile3, gp, a.out_mask);
+    hipLaunchKernelGGL(k_gumbel_partial<uint16_t>, dim3(grid), dim3(kThreads), 0, st, j);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_gumbel_final, dim3(a.B), dim3(kThreads), 0, st, a.B, L.ntile3, desc, gp,
-                     a.out_ids, a.out_kept);
+  if (j.dt == VS_F32)
+    hipLaunchKernelGGL(k_gumbel_final<float>, dim3(j.B), dim3(kThreads), 0, st, j);
+  else
+    hipLaunchKernelGGL(k_gumbel_final<uint16_t>, dim3(j.B), dim3(kThreads), 0, st, j);
   return hipGetLastError();
 }
 
-hipError_t launch_lse_full(const LogprobArgs& a, const WsLayout& L, char* ws, hipStream_t st) {
-  const auto* rl = reinterpret_cast<const float2*>(ws + L.rlse);
-  const int ntile = (a.V + kFullTile - 1) / kFullTile;
-  const int grid = xcd_grid(a.B, ntile);
-  const bool out_vec = (reinterpret_cast<uintptr_t>(a.out_full) % 16 == 0) && (a.ld_out % 4 == 0);
-  if (a.dt == VS_F32)
-    hipLaunchKernelGGL(k_lse_full<float>, dim3(grid), dim3(kThreads), 0, st,
-                       static_cast<const float*>(a.logits), a.B, a.V, a.ld, a.aligned, rl, ntile,
-                       a.out_full, a.ld_out, out_vec);
+hipError_t launch_lse_full(const Job& j, hipStream_t st) {
+  const int ntile = (j.V + kFullTile - 1) / kFullTile;
+  const int grid = xcd_grid(j.B, ntile);
+  const bool out_vec = (reinterpret_cast<uintptr_t>(j.out_full) % 16 == 0) && (j.ld_out % 4 == 0);
+  if (j.dt == VS_F32)
+    hipLaunchKernelGGL(k_lse_full<float>, dim3(grid), dim3(kThreads), 0, st, j, ntile, out_vec);
   else
-    hipLaunchKernelGGL(k_lse_full<uint16_t>, dim3(grid), dim3(kThreads), 0, st,
-                       static_cast<const uint16_t*>(a.logits), a.B, a.V, a.ld, a.aligned, rl, ntile,
-                       a.out_full, a.ld_out, out_vec);
+    hipLaunchKernelGGL(k_lse_full<uint16_t>, dim3(grid), dim3(kThreads), 0, st, j, ntile, out_vec);
   return hipGetLastError();
 }
 

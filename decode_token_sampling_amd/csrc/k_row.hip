@@ -1,41 +1,53 @@
-// K2: one 1024-thread workgroup per row, after the streaming pass.
+// Row kernels, after the streaming pass.
 //
+// k_row_light (256 threads per row) finishes every row that does not need the
+// whole vocabulary:
 //  - greedy rows: the lowest id of the row maximum, from the tiles' argmaxes;
-//  - top-k rows (k <= 64): merge the tiles' sorted candidate lists, then
-//    truncate (min-p, top-p over the survivors) and draw among at most k ids;
-//  - larger k, or a tile whose candidates overflowed: an exact radix select of
-//    the k-th key over the whole row (three digit passes), a pass that finds the
-//    last kept id inside a tie group, and a gather of exactly k ids;
-//  - full-vocabulary rows: the row maximum m of s = x / T, and for top-p < 1 the
-//    cut: a histogram of fixed-point masses over buckets of (s - m) (128 per
-//    unit, monotone in s), the bucket where the cumulative mass reaches
-//    top_p * total, then the exact cut inside that bucket (gathered and sorted
-//    in LDS, or, if it holds more than 8192 ids, a mass-weighted radix select).
-//    The Gumbel kernels then draw over the kept set.
-// The log-softmax row kernel (vs_logprobs) shares the candidate merge and the
-// slow top-k path.
+//  - top-k rows (k <= 64): the exact top k of the union of the tiles' candidate
+//    lists (a radix select over packed (key, id) values), sorted, then min-p,
+//    top-p on fixed-point masses and the Gumbel-max draw in one wave;
+//  - top-k rows with k > 64, or whose tiles overflowed: an exact radix select
+//    of the k-th key over the row itself (three digit passes), the last kept
+//    id inside a tie group, and a gather of exactly k ids;
+//  - full-vocabulary rows: the row maximum m of s = x / T, handed on;
+//  - log-probabilities: log-sum-exp from the tile partials, the top-k log-probs
+//    from the candidate lists, and the log-prob of the sampled or given ids.
+// k_row_full (1024 threads per row) finds the top-p cut of full-vocabulary rows:
+// a histogram of fixed-point masses over 4096 buckets of (s - m) (128 per unit,
+// monotone in s), the bucket where the cumulative mass reaches top_p * total,
+// then the exact cut inside that bucket (gathered and sorted in LDS, or by a
+// mass-weighted radix select when the bucket holds more than 8192 ids).
 #include "vs_device.h"
 #include "vs_kernels.h"
 
 namespace vsk {
 namespace {
 
-constexpr int kRowThreads = 1024;
-constexpr int kBufCap = 8192;
+constexpr int kLightThreads = 256;
+constexpr int kFullThreads = 1024;
 constexpr int kBuckets = 4096;
 constexpr float kBucketsPerUnit = 128.0f;
+constexpr int kMaxTiles = (VS_MAX_V + kSelTile - 1) / kSelTile;
 
-struct RowShared {
-  uint64_t buf[kBufCap];   // gathered candidates (packed key, id)
-  uint64_t hw[kBuckets];   // histogram weights
-  uint32_t hc[kBuckets];   // histogram counts
+template <int kBuf, int kBins>
+struct RowSh {
+  static constexpr int kBufCap = kBuf;
+  static constexpr int kBinCap = kBins;
+  uint64_t buf[kBuf];
+  uint64_t hw[kBins];
+  uint32_t hc[kBins];
   uint64_t r64[16];
   double rd[16];
   int32_t ri[16];
+  float rf[16];
   int n;
+  uint32_t flags;
   uint64_t b64[4];
   int32_t b32[4];
+  int32_t toff[kMaxTiles + 1];  // per-tile offsets of a candidate union
 };
+using LightSh = RowSh<4096, 2048>;
+using FullSh = RowSh<8192, kBuckets>;
 
 __device__ __forceinline__ float scaled(float x, float T) { return (T == 1.0f) ? x : x / T; }
 
@@ -78,8 +90,8 @@ __device__ __forceinline__ void row_visit(const E* __restrict__ rowp, int V, boo
 // down (bin order = value order): the bin d with above < rem <= above + w[d],
 // where above is the weight of the bins higher than d. Returns d (or -1), with
 // the weight and count above it.
-__device__ __forceinline__ int hist_find_desc(RowShared& sh, int nb, uint64_t rem,
-                                              uint64_t* above_w, uint64_t* above_c) {
+template <class Sh>
+__device__ int hist_find_desc(Sh& sh, int nb, uint64_t rem, uint64_t* above_w, uint64_t* above_c) {
   const int G = (nb + blockDim.x - 1) / blockDim.x;
   uint64_t lw = 0, lc = 0;
   for (int g = 0; g < G; ++g) {
@@ -123,10 +135,11 @@ __device__ __forceinline__ int hist_find_desc(RowShared& sh, int nb, uint64_t re
 // element at which the cumulative weight, in the order (key desc, id asc),
 // first reaches rem. Three digit passes (11, 11, 10 bits). Outputs the weight
 // and count strictly above tau and the weight of one tau element.
-template <typename E, typename Pick>
+template <typename E, class Sh, typename Pick>
 __device__ void radix_select(const E* __restrict__ rowp, int V, bool aligned, float T, uint64_t rem,
-                             Pick pick, RowShared& sh, uint32_t* tau, uint64_t* w_above,
+                             Pick pick, Sh& sh, uint32_t* tau, uint64_t* w_above,
                              uint64_t* c_above, uint64_t* w_tau) {
+  static_assert(Sh::kBinCap >= 2048, "radix select needs 2048 bins");
   uint32_t prefix = 0, pmask = 0;
   uint64_t wa = 0, ca = 0;
   const int shifts[3] = {21, 10, 0};
@@ -169,9 +182,9 @@ __device__ void radix_select(const E* __restrict__ rowp, int V, bool aligned, fl
 
 // The id of the need-th (1-based) element, in increasing id order, whose key
 // equals tau and that `pick` accepts.
-template <typename E, typename Pick>
+template <typename E, class Sh, typename Pick>
 __device__ int32_t tie_cut(const E* __restrict__ rowp, int V, float T, uint32_t tau, uint64_t need,
-                           Pick pick, RowShared& sh) {
+                           Pick pick, Sh& sh) {
   constexpr int PER = 16;
   if (threadIdx.x == 0) sh.b32[1] = -1;
   __syncthreads();
@@ -215,57 +228,144 @@ __device__ int32_t tie_cut(const E* __restrict__ rowp, int V, float T, uint32_t 
   return r;
 }
 
-// Sort the first n entries of sh.buf (larger first); pads to a power of two.
-__device__ __forceinline__ void sort_buf(RowShared& sh, int n) {
+// Sort the first n entries of a (shared) array, larger first; pads to a power
+// of two no larger than cap.
+__device__ __forceinline__ void sort_desc(uint64_t* a, int n) {
   const int np = next_pow2(n < 2 ? 2 : n);
-  for (int i = n + threadIdx.x; i < np; i += blockDim.x) sh.buf[i] = 0ull;
+  for (int i = n + threadIdx.x; i < np; i += blockDim.x) a[i] = 0ull;
   __syncthreads();
-  block_sort_desc(sh.buf, np);
+  block_sort_desc(a, np);
 }
 
-// Merge the tiles' sorted top-k lists of one row into sh.buf, sorted; returns
-// min(k, total candidates), or -1 when a tile overflowed or too many survive.
-// Only entries >= P* can be in the row's top k, where P* is the largest k-th
-// entry of a full tile list (that tile alone has k entries >= P*).
-__device__ int merge_tiles(const uint32_t* __restrict__ mrow, const uint64_t* __restrict__ crow,
-                           int ntile, int k, RowShared& sh) {
-  uint64_t pl = 0;
-  int ovf = 0;
-  for (int t = threadIdx.x; t < ntile; t += blockDim.x) {
-    const uint32_t m = mrow[t];
-    if (m & kMetaOverflow) ovf = 1;
-    if (static_cast<int>(m & kMetaCountMask) == k) {
-      const uint64_t v = crow[static_cast<size_t>(t) * kFastK + k - 1];
-      pl = v > pl ? v : pl;
+// Exact k-th largest of n distinct packed values in shared memory: MSB-first
+// radix select with 8-bit digits. Stops early once the remaining rank equals
+// the size of the chosen bucket (the whole bucket is then selected and the
+// prefix alone is a valid threshold). Every value >= the result is selected,
+// exactly k of them (k <= n).
+template <class Sh>
+__device__ uint64_t block_kth_largest(const uint64_t* a, int n, int k, Sh& sh) {
+  uint64_t prefix = 0, pmask = 0;
+  int rem = k;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) sh.hc[i] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      const uint64_t v = a[i];
+      if ((v & pmask) == prefix) atomicAdd(&sh.hc[(v >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    const int G = (256 + blockDim.x - 1) / blockDim.x;
+    int lc = 0;
+    for (int g = 0; g < G; ++g) {
+      const int i = threadIdx.x * G + g;
+      if (i < 256) lc += static_cast<int>(sh.hc[255 - i]);
+    }
+    int tot;
+    int run = block_scan_incl(lc, sh.ri, &tot) - lc;
+    if (threadIdx.x == 0) sh.b32[0] = -1;
+    __syncthreads();
+    for (int g = 0; g < G; ++g) {
+      const int i = threadIdx.x * G + g;
+      if (i < 256) {
+        const int d = 255 - i;
+        const int c = static_cast<int>(sh.hc[d]);
+        if (run < rem && rem <= run + c) {
+          sh.b32[0] = d;
+          sh.b32[1] = run;
+          sh.b32[2] = c;
+        }
+        run += c;
+      }
+    }
+    __syncthreads();
+    const int d = sh.b32[0] < 0 ? 0 : sh.b32[0];
+    const int above = sh.b32[1], c = sh.b32[2];
+    __syncthreads();
+    rem -= above;
+    prefix |= static_cast<uint64_t>(d) << shift;
+    pmask |= 0xffull << shift;
+    if (c == rem) break;
+  }
+  return prefix;
+}
+
+// The exact top k (order: key desc, id asc) of the union of one candidate list
+// over the row's tiles, sorted into sh.buf[0..min(k, total)). Returns the
+// count, or -1 when a tile overflowed or the union does not fit.
+template <class Sh>
+__device__ int union_topk(const uint32_t* __restrict__ mrow, const uint64_t* __restrict__ crow,
+                          int ntile, int shift, uint32_t ovf_flag, int k, Sh& sh) {
+  // tile counts -> offsets (each thread owns consecutive tiles)
+  const int G = (ntile + blockDim.x - 1) / blockDim.x;
+  int lc = 0, ovf = 0;
+  for (int g = 0; g < G; ++g) {
+    const int t = threadIdx.x * G + g;
+    if (t < ntile) {
+      const uint32_t m = mrow[t];
+      if (m & ovf_flag) ovf = 1;
+      lc += static_cast<int>((m >> shift) & 0xffu);
     }
   }
   ovf = block_max(ovf, sh.ri);
   if (ovf) return -1;
-  const uint64_t pstar = block_max(pl, sh.r64);
-  if (threadIdx.x == 0) sh.n = 0;
-  __syncthreads();
-  for (int f = threadIdx.x; f < ntile * k; f += blockDim.x) {
-    const int t = f / k, i = f - t * k;
-    if (i < static_cast<int>(mrow[t] & kMetaCountMask)) {
-      const uint64_t v = crow[static_cast<size_t>(t) * kFastK + i];
-      if (v >= pstar) {
-        const int pos = atomicAdd(&sh.n, 1);
-        if (pos < kBufCap) sh.buf[pos] = v;
-      }
+  int n;
+  int off = block_scan_incl(lc, sh.ri, &n) - lc;
+  if (n > Sh::kBufCap) return -1;
+  for (int g = 0; g < G; ++g) {
+    const int t = threadIdx.x * G + g;
+    if (t < ntile) {
+      sh.toff[t] = off;
+      off += static_cast<int>((mrow[t] >> shift) & 0xffu);
     }
   }
+  if (threadIdx.x == 0) sh.toff[ntile] = n;
   __syncthreads();
-  const int n = sh.n;
+  // Copy the n valid entries with all threads: entry g lives in the tile t
+  // with toff[t] <= g < toff[t+1] (binary search in LDS). Four loads are issued
+  // before any is used so their latencies overlap.
+  constexpr int U = 4;
+  for (int g0 = threadIdx.x; g0 < n; g0 += U * blockDim.x) {
+    uint64_t v[U];
+    int dst[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int g = g0 + u * static_cast<int>(blockDim.x);
+      dst[u] = g;
+      if (g < n) {
+        int lo = 0, hi = ntile - 1;  // last t with toff[t] <= g
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (sh.toff[mid] <= g) lo = mid; else hi = mid - 1;
+        }
+        v[u] = crow[static_cast<size_t>(lo) * kSelCap + (g - sh.toff[lo])];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (dst[u] < n) sh.buf[dst[u]] = v[u];
+  }
   __syncthreads();
-  if (n > kBufCap) return -1;
-  sort_buf(sh, n);
-  return n < k ? n : k;
+  if (n > k) {
+    const uint64_t thr = block_kth_largest(sh.buf, n, k, sh);
+    uint64_t* tmp = sh.hw;  // at least 2048 slots
+    if (threadIdx.x == 0) sh.n = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      const uint64_t v = sh.buf[i];
+      if (v >= thr) tmp[atomicAdd(&sh.n, 1)] = v;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < k; i += blockDim.x) sh.buf[i] = tmp[i];
+    __syncthreads();
+    n = k;
+  }
+  sort_desc(sh.buf, n);
+  return n;
 }
 
-// Exact top-k of the row by radix select; leaves the k entries sorted in sh.buf.
-template <typename E>
-__device__ int slow_topk(const E* __restrict__ rowp, int V, bool aligned, float T, int k,
-                         RowShared& sh) {
+// Exact top k of s = x / T over the row data (k <= 1024); sorted into sh.buf.
+template <typename E, class Sh>
+__device__ int slow_topk(const E* __restrict__ rowp, int V, bool aligned, float T, int k, Sh& sh) {
   auto all = [](int, float, uint32_t, uint64_t* w) {
     *w = 1;
     return true;
@@ -281,49 +381,298 @@ __device__ int slow_topk(const E* __restrict__ rowp, int V, bool aligned, float 
     const uint32_t key = f2key(scaled(x, T));
     if (key > tau || (key == tau && j <= idc)) {
       const int pos = atomicAdd(&sh.n, 1);
-      if (pos < kBufCap) sh.buf[pos] = pack(key, j);
+      if (pos < Sh::kBufCap) sh.buf[pos] = pack(key, j);
     }
   });
   __syncthreads();
   int n = sh.n;
   __syncthreads();
   if (n > k) n = k;  // cannot happen: exactly k ids pass
-  sort_buf(sh, n);
+  sort_desc(sh.buf, n);
   return n;
 }
 
-// Truncate and draw over the n (<= blockDim) sorted candidates in sh.buf.
-// Returns the status (0, or VS_ROW_BAD_PARAM when x / T overflowed).
-__device__ int draw_sorted(RowShared& sh, int n, const RowCfg& c, int row, int32_t* id_out,
-                           int32_t* kept_out, uint32_t* mask_row) {
-  const int i = threadIdx.x;
-  const uint64_t top = sh.buf[0];
+// Truncate and draw over the n (<= 4 * blockDim) sorted candidates L. Returns
+// the status (0, or VS_ROW_BAD_PARAM when x / T overflowed to +inf).
+template <class Sh>
+__device__ int block_draw(const uint64_t* L, int n, const RowCfg& c, int row, int32_t* id_out,
+                          int32_t* kept_out, uint32_t* mask_row, Sh& sh) {
+  constexpr int PER = 4;
+  if (n <= 0) return VS_ROW_BAD_LOGITS;  // no candidate: never read an id from it
+  const uint64_t top = L[0];
+  if (pkey(top) == kKeyPosInf) return VS_ROW_BAD_PARAM;
+  const float m = key2f(pkey(top));
+  float e[PER];
+  bool in_s[PER], kept[PER];
+  uint64_t W[PER];
+  uint64_t lsum = 0;
+  for (int q = 0; q < PER; ++q) {
+    const int i = threadIdx.x * PER + q;
+    const bool has = i < n;
+    e[q] = has ? pinned_exp(key2f(pkey(L[i])) - m) : 0.0f;
+    in_s[q] = has && (e[q] >= c.mp);  // a prefix of the order: e is monotone in s
+    W[q] = in_s[q] ? mass_of(e[q]) : 0ull;
+    lsum += W[q];
+  }
+  if (c.p < 1.0f) {
+    uint64_t tw;
+    uint64_t run = block_scan_incl(lsum, sh.r64, &tw) - lsum;
+    const double thr = static_cast<double>(c.p) * static_cast<double>(tw);
+    int first = 0x7fffffff;
+    for (int q = 0; q < PER; ++q) {
+      run += W[q];
+      if (in_s[q] && static_cast<double>(run) >= thr && first == 0x7fffffff)
+        first = threadIdx.x * PER + q;
+    }
+    const int cut = block_min(first, sh.ri);
+    for (int q = 0; q < PER; ++q) kept[q] = in_s[q] && (static_cast<int>(threadIdx.x) * PER + q) <= cut;
+  } else {
+    for (int q = 0; q < PER; ++q) kept[q] = in_s[q];
+  }
+  const uint64_t rs = row_stream(c.seed, row);
+  double best = -1.0;
+  int best_id = 0x7fffffff, nk = 0;
+  for (int q = 0; q < PER; ++q) {
+    if (!kept[q]) continue;
+    const int i = threadIdx.x * PER + q;
+    const int id = pid(L[i]);
+    ++nk;
+    const double sc = gumbel_score(e[q], rs, id);
+    if (sc > best || (sc == best && id < best_id)) {
+      best = sc;
+      best_id = id;
+    }
+    if (mask_row) atomicOr(&mask_row[id >> 5], 1u << (id & 31));
+  }
+  const double bb = block_max(best, sh.rd);
+  const int win = block_min(best == bb ? best_id : 0x7fffffff, sh.ri);
+  const int total = block_sum(nk, sh.ri);
+  *id_out = win;
+  *kept_out = total;
+  return 0;
+}
+
+// The same over n <= 64 sorted candidates with one wave (no block barrier);
+// call from every lane of one wave.
+__device__ int wave_draw(const uint64_t* L, int n, const RowCfg& c, int row, int32_t* id_out,
+                         int32_t* kept_out, uint32_t* mask_row) {
+  const int i = lane();
+  if (n <= 0) return VS_ROW_BAD_LOGITS;  // no candidate: never read an id from it
+  const uint64_t top = L[0];
   if (pkey(top) == kKeyPosInf) return VS_ROW_BAD_PARAM;
   const float m = key2f(pkey(top));
   const bool has = i < n;
-  const uint64_t P = has ? sh.buf[i] : 0ull;
+  const uint64_t P = has ? L[i] : 0ull;
   const float e = has ? pinned_exp(key2f(pkey(P)) - m) : 0.0f;
-  const bool in_s = has && (e >= c.mp);  // a prefix of the order: e is monotone in s
+  const bool in_s = has && (e >= c.mp);
   bool kept = in_s;
   if (c.p < 1.0f) {
-    const uint64_t W = in_s ? mass_of(e) : 0ull;
-    uint64_t tw;
-    const uint64_t cum = block_scan_incl(W, sh.r64, &tw);
+    uint64_t cum = in_s ? mass_of(e) : 0ull;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const uint64_t w = __shfl_up(cum, o);
+      if (i >= o) cum += w;
+    }
+    const uint64_t tw = __shfl(cum, kWave - 1);
     const double thr = static_cast<double>(c.p) * static_cast<double>(tw);
-    const int first = (in_s && static_cast<double>(cum) >= thr) ? i : 0x7fffffff;
-    const int cut = block_min(first, sh.ri);
+    const uint64_t hit = __ballot(in_s && static_cast<double>(cum) >= thr);
+    const int cut = hit ? __ffsll(static_cast<unsigned long long>(hit)) - 1 : kWave;
     kept = in_s && i <= cut;
   }
-  const int nk = block_sum(kept ? 1 : 0, sh.ri);
-  const uint64_t rs = row_stream(c.seed, row);
   const int id = has ? pid(P) : 0x7fffffff;
-  const double score = kept ? gumbel_score(e, rs, id) : -1.0;
-  const double best = block_max(score, sh.rd);
-  const int win = block_min((kept && score == best) ? id : 0x7fffffff, sh.ri);
+  const double sc = kept ? gumbel_score(e, row_stream(c.seed, row), id) : -1.0;
+  const double best = wave_max(sc);
+  const int win = wave_min((kept && sc == best) ? id : 0x7fffffff);
   if (kept && mask_row) atomicOr(&mask_row[id >> 5], 1u << (id & 31));
   *id_out = win;
-  *kept_out = nk;
+  *kept_out = __popcll(__ballot(kept));
   return 0;
+}
+
+template <typename E>
+__device__ __forceinline__ float logit_at(const Job& j, int row, int id) {
+  return to_f32(static_cast<const E*>(j.logits)[static_cast<int64_t>(row) * j.ld + id]);
+}
+
+template <typename E>
+__global__ __launch_bounds__(kLightThreads) void k_row_light(Job j) {
+  __shared__ LightSh sh;
+  const int row = blockIdx.x;
+  const Plan pl = plan_row(j, row);
+  const RowCfg& c = pl.c;
+  const int ntile = j.ntile;
+  const uint32_t* mrow = j.meta + static_cast<size_t>(row) * ntile;
+  const uint64_t* crowA = j.candA + static_cast<size_t>(row) * ntile * kSelCap;
+  const uint64_t* crowB = j.candB + static_cast<size_t>(row) * ntile * kSelCap;
+  const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
+  const bool aligned = j.aligned;
+  const float nanv = __builtin_nanf("");
+
+  // flags over the tiles, and the row argmax when list A holds argmaxes
+  if (threadIdx.x == 0) sh.flags = 0u;
+  __syncthreads();
+  uint32_t fl = 0;
+  uint64_t top = 0;
+  for (int t = threadIdx.x; t < ntile; t += blockDim.x) {
+    const uint32_t m = mrow[t];
+    fl |= m;
+    if (pl.kA == 1 && (m & kMetaCountA)) {
+      const uint64_t v = crowA[static_cast<size_t>(t) * kSelCap];
+      top = v > top ? v : top;
+    }
+  }
+  if (fl) atomicOr(&sh.flags, fl & (kMetaBadLogits | kMetaHasFinite));
+  top = block_max(top, sh.r64);  // also orders the atomicOr above
+  const bool bad_logits = (sh.flags & kMetaBadLogits) || !(sh.flags & kMetaHasFinite);
+
+  // log-sum-exp from the tile partials
+  float M = -kInf, logS = nanv;
+  if (j.lse) {
+    const LsePart* lrow = j.lpart + static_cast<size_t>(row) * ntile;
+    float lm = -kInf;
+    for (int t = threadIdx.x; t < ntile; t += blockDim.x) lm = fmaxf(lm, lrow[t].m);
+    M = block_max(lm, sh.rf);
+    float ls = 0.0f;
+    if (M > -kInf) {
+      for (int t = threadIdx.x; t < ntile; t += blockDim.x) {
+        const LsePart pt = lrow[t];
+        if (pt.m > -kInf) ls += pt.s * __expf(pt.m - M);
+      }
+    }
+    logS = logf(block_sum(ls, sh.rf));
+    if (threadIdx.x == 0)
+      j.rlse[row] = bad_logits ? make_float2(nanv, nanv) : make_float2(M, logS);
+  }
+
+  // the draw
+  int sorted_shared = 0;  // entries of list A's exact top k left sorted in sh.buf
+  if (j.sample) {
+    const int mwords = (j.V + 31) / 32;
+    uint32_t* mask_row = j.out_mask ? j.out_mask + static_cast<size_t>(row) * mwords : nullptr;
+    if (mask_row) {
+      for (int i = threadIdx.x; i < mwords; i += blockDim.x) mask_row[i] = 0u;
+      __syncthreads();
+    }
+    int status = c.status | (bad_logits ? VS_ROW_BAD_LOGITS : 0);
+    if (pl.kA == 1 && top == 0ull) status |= VS_ROW_BAD_LOGITS;  // no argmax was found
+    if (status == 0) {
+      if ((j.hints & VS_HINT_ALL_GREEDY) && c.mode != kModeGreedy) status = VS_ROW_HINT_VIOLATED;
+      if ((j.hints & VS_HINT_NO_FULLVOCAB) && c.mode == kModeFull) status = VS_ROW_HINT_VIOLATED;
+    }
+    int32_t id = -1, kept = 0;
+    uint32_t next = kRowDone;
+    if (status == 0) {
+      if (c.mode == kModeGreedy) {
+        id = pid(top);
+        kept = 1;
+        if (mask_row && threadIdx.x == 0) atomicOr(&mask_row[id >> 5], 1u << (id & 31));
+      } else if (c.mode == kModeKFast || c.mode == kModeKSlow) {
+        int n = (pl.kA > 1) ? union_topk(mrow, crowA, ntile, 0, kMetaOverflowA, c.k, sh) : -1;
+        if (n < 0) n = slow_topk(rowp, j.V, aligned, c.T, c.k, sh);
+        if (c.T == 1.0f) sorted_shared = n;
+        if (n <= kWave) {
+          if (threadIdx.x < kWave) {
+            const int st = wave_draw(sh.buf, n, c, row, &id, &kept, mask_row);
+            if (threadIdx.x == 0) {
+              sh.b32[0] = st;
+              sh.b32[1] = id;
+              sh.b32[2] = kept;
+            }
+          }
+          __syncthreads();
+          status = sh.b32[0];
+          id = sh.b32[1];
+          kept = sh.b32[2];
+          __syncthreads();
+        } else {
+          status = block_draw(sh.buf, n, c, row, &id, &kept, mask_row, sh);
+        }
+      } else {  // full vocabulary: the cut and the draw come later
+        const float m = scaled(key2f(pkey(top)), c.T);
+        if (m == kInf) {
+          status = VS_ROW_BAD_PARAM;
+        } else {
+          next = kRowFull;
+          if (threadIdx.x == 0) j.desc[row].m = m;
+        }
+      }
+    }
+    if (status) {
+      id = -1;
+      kept = 0;
+      next = kRowDone;
+    }
+    if (threadIdx.x == 0) {
+      j.desc[row].mode = next;
+      if (next == kRowDone) {
+        if (id >= j.V) {  // unreachable: every id comes from a tile of [0, V)
+          id = -1;
+          kept = 0;
+          status = VS_ROW_BAD_LOGITS;
+        }
+        j.out_ids[row] = id;
+        if (j.out_kept) j.out_kept[row] = kept;
+        if (j.tok_sampled)
+          j.out_tok_lp[row] = (id < 0 || bad_logits) ? nanv : (logit_at<E>(j, row, id) - M) - logS;
+      }
+      if (j.out_status) j.out_status[row] = status;
+    }
+    if (status && mask_row) {  // a row that failed reports an empty kept set
+      __syncthreads();
+      for (int i = threadIdx.x; i < mwords; i += blockDim.x) mask_row[i] = 0u;
+    }
+    __syncthreads();
+  }
+
+  // top-k log-probabilities
+  if (j.lse && j.k_lp > 0) {
+    const int k = j.k_lp;
+    int32_t* ids = j.out_lp_ids + static_cast<size_t>(row) * k;
+    float* lps = j.out_lp + static_cast<size_t>(row) * k;
+    if (bad_logits) {
+      for (int i = threadIdx.x; i < k; i += blockDim.x) {
+        ids[i] = -1;
+        lps[i] = nanv;
+      }
+    } else {
+      int n;
+      const uint64_t* src = sh.buf;
+      if (pl.shared && pl.kA == 1) {  // k == 1 and list A holds the argmax
+        n = 1;
+        if (threadIdx.x == 0) sh.b64[2] = top;
+        __syncthreads();
+        src = &sh.b64[2];
+      } else if (pl.shared && sorted_shared >= k) {
+        n = sorted_shared;
+      } else {
+        n = pl.shared ? union_topk(mrow, crowA, ntile, 0, kMetaOverflowA, k, sh)
+                      : union_topk(mrow, crowB, ntile, kMetaCountBShift, kMetaOverflowB, k, sh);
+        if (n < 0) n = slow_topk(rowp, j.V, aligned, 1.0f, k, sh);
+      }
+      for (int i = threadIdx.x; i < k; i += blockDim.x) {
+        if (i < n) {
+          const uint64_t P = src[i];
+          ids[i] = pid(P);
+          lps[i] = (key2f(pkey(P)) - M) - logS;
+        } else {
+          ids[i] = -1;
+          lps[i] = nanv;
+        }
+      }
+    }
+  }
+
+  // log-probabilities of given ids (vs_logprobs)
+  if (j.lse && !j.sample && threadIdx.x == 0) {
+    int st = bad_logits ? VS_ROW_BAD_LOGITS : 0;
+    if (j.tok) {
+      const int tok = j.tok[row];
+      const bool badtok = tok < 0 || tok >= j.V;
+      if (badtok) st |= VS_ROW_BAD_TOKEN_ID;
+      j.out_tok_lp[row] = (bad_logits || badtok) ? nanv : (logit_at<E>(j, row, tok) - M) - logS;
+    }
+    if (j.out_lp_status) j.out_lp_status[row] = st;
+  }
 }
 
 // Per-element quantities of a full-vocabulary top-p row.
@@ -336,7 +685,7 @@ struct FullTerms {
     const uint64_t W = mass_of(e);
     if (W == 0) return false;
     *w = W;
-    int b = static_cast<int>(-t * kBucketsPerUnit);
+    const int b = static_cast<int>(-t * kBucketsPerUnit);
     *bucket = b < kBuckets - 1 ? b : kBuckets - 1;
     return true;
   }
@@ -344,7 +693,7 @@ struct FullTerms {
 
 template <typename E>
 __device__ void full_topp_cut(const E* __restrict__ rowp, int V, bool aligned, const RowCfg& c,
-                              float m, RowShared& sh, RowDesc* d) {
+                              float m, FullSh& sh, RowDesc* d) {
   const FullTerms ft{m, c.T, c.mp};
   for (int i = threadIdx.x; i < kBuckets; i += blockDim.x) {
     sh.hw[i] = 0;
@@ -363,13 +712,12 @@ __device__ void full_topp_cut(const E* __restrict__ rowp, int V, bool aligned, c
   uint64_t lt = 0;
   for (int i = threadIdx.x; i < kBuckets; i += blockDim.x) lt += sh.hw[i];
   const uint64_t total = block_sum(lt, sh.r64);
-  // The kept prefix is the shortest whose mass reaches thr; masses are integers,
-  // so "cum >= thr" is "cum >= ceil(thr)".
+  // The kept prefix is the shortest whose mass reaches thr; masses are
+  // integers, so "cum >= thr" is "cum >= ceil(thr)".
   const double thr = static_cast<double>(c.p) * static_cast<double>(total);
-  const uint64_t target = static_cast<uint64_t>(ceil(thr)) > 0 ? static_cast<uint64_t>(ceil(thr)) : 1;
-  // Bucket 0 holds the largest s: scan buckets upwards == values downwards.
-  // hist_find_desc scans bins from the top index down, so present the buckets
-  // reversed by swapping the arrays in place.
+  const uint64_t target = ceil(thr) >= 1.0 ? static_cast<uint64_t>(ceil(thr)) : 1ull;
+  // Bucket 0 holds the largest s; hist_find_desc scans from the highest index
+  // down, so present the buckets in reverse.
   for (int i = threadIdx.x; i < kBuckets / 2; i += blockDim.x) {
     const int o = kBuckets - 1 - i;
     const uint64_t tw = sh.hw[i];
@@ -394,25 +742,25 @@ __device__ void full_topp_cut(const E* __restrict__ rowp, int V, bool aligned, c
   uint32_t tau;
   int32_t idc;
   int32_t kept;
-  if (nb <= static_cast<uint32_t>(kBufCap)) {
+  if (nb <= static_cast<uint32_t>(FullSh::kBufCap)) {
     if (threadIdx.x == 0) sh.n = 0;
     __syncthreads();
-    row_visit(rowp, V, aligned, [&](int j, float x) {
+    row_visit(rowp, V, aligned, [&](int jj, float x) {
       const float s = scaled(x, c.T);
       uint64_t w;
       int b;
       if (ft.mass(s, &w, &b) && b == bstar) {
         const int pos = atomicAdd(&sh.n, 1);
-        if (pos < kBufCap) sh.buf[pos] = pack(f2key(s), j);
+        if (pos < FullSh::kBufCap) sh.buf[pos] = pack(f2key(s), jj);
       }
     });
     __syncthreads();
-    const int n = sh.n < kBufCap ? sh.n : kBufCap;
+    const int n = sh.n < FullSh::kBufCap ? sh.n : FullSh::kBufCap;
     __syncthreads();
-    sort_buf(sh, n);
+    sort_desc(sh.buf, n);
     // Cumulative mass inside the bucket, in order; the cut is the first index
     // where it reaches rem.
-    constexpr int PER = kBufCap / kRowThreads;
+    constexpr int PER = FullSh::kBufCap / kFullThreads;
     uint64_t loc[PER];
     uint64_t lsum = 0;
     for (int e = 0; e < PER; ++e) {
@@ -445,8 +793,7 @@ __device__ void full_topp_cut(const E* __restrict__ rowp, int V, bool aligned, c
     kept = static_cast<int32_t>(ac + ca + need);
   }
   if (threadIdx.x == 0) {
-    d->mode = kFullTopP;
-    d->m = m;
+    d->mode = kRowFullTopP;
     d->tau = tau;
     d->id_cut = idc;
     d->kept = kept;
@@ -454,199 +801,36 @@ __device__ void full_topp_cut(const E* __restrict__ rowp, int V, bool aligned, c
 }
 
 template <typename E>
-__global__ __launch_bounds__(kRowThreads) void k_row(
-    const E* __restrict__ logits, int B, int V, int64_t ld, bool aligned,
-    const float* __restrict__ temperature, const int32_t* __restrict__ top_k,
-    const float* __restrict__ top_p, const float* __restrict__ min_p,
-    const uint64_t* __restrict__ seeds, uint32_t hints, int ntile,
-    const uint32_t* __restrict__ meta, const uint64_t* __restrict__ cand,
-    RowDesc* __restrict__ desc, int32_t* __restrict__ out_ids, int32_t* __restrict__ out_kept,
-    uint32_t* __restrict__ out_mask, int32_t* __restrict__ out_status) {
-  __shared__ RowShared sh;
+__global__ __launch_bounds__(kFullThreads) void k_row_full(Job j) {
+  __shared__ FullSh sh;
   const int row = blockIdx.x;
-  const RowCfg c = load_cfg(row, V, temperature, top_k, top_p, min_p, seeds);
-  const uint32_t* mrow = meta + static_cast<size_t>(row) * ntile;
-  const uint64_t* crow = cand + static_cast<size_t>(row) * ntile * kFastK;
-  const E* rowp = logits + static_cast<int64_t>(row) * ld;
-  const int mwords = (V + 31) / 32;
-  uint32_t* mask_row = out_mask ? out_mask + static_cast<size_t>(row) * mwords : nullptr;
-
-  int bad = 0, finite = 0;
-  uint64_t top = 0;
-  for (int t = threadIdx.x; t < ntile; t += blockDim.x) {
-    const uint32_t m = mrow[t];
-    if (m & kMetaBadLogits) bad = 1;
-    if (m & kMetaHasFinite) finite = 1;
-    if (m & kMetaCountMask) {
-      const uint64_t v = crow[static_cast<size_t>(t) * kFastK];
-      top = v > top ? v : top;
-    }
+  RowDesc* d = j.desc + row;
+  if (d->mode != kRowFull) return;  // uniform over the block
+  const RowCfg c = load_cfg(row, j.V, j.T, j.k, j.p, j.mp, j.seeds);
+  const float m = d->m;
+  if (c.p < 1.0f) {
+    const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
+    full_topp_cut(rowp, j.V, j.aligned, c, m, sh, d);
+  } else if (threadIdx.x == 0) {
+    d->mode = (c.mp > 0.0f) ? kRowFullMinP : kRowFullNone;
   }
-  bad = block_max(bad, sh.ri);
-  finite = block_max(finite, sh.ri);
-  top = block_max(top, sh.r64);
-  if (mask_row) {
-    for (int i = threadIdx.x; i < mwords; i += blockDim.x) mask_row[i] = 0u;
-    __syncthreads();
-  }
-
-  int status = c.status;
-  if (bad || !finite) status |= VS_ROW_BAD_LOGITS;
-  if (status == 0) {
-    if ((hints & VS_HINT_ALL_GREEDY) && c.mode != kModeGreedy) status = VS_ROW_HINT_VIOLATED;
-    if ((hints & VS_HINT_NO_FULLVOCAB) && c.mode == kModeFull) status = VS_ROW_HINT_VIOLATED;
-  }
-  int32_t id = -1, kept = 0;
-  bool full = false;
-  RowDesc* d = desc + row;
-  if (status == 0) {
-    if (c.mode == kModeGreedy) {
-      id = pid(top);
-      kept = 1;
-      if (mask_row && threadIdx.x == 0) atomicOr(&mask_row[id >> 5], 1u << (id & 31));
-    } else if (c.mode == kModeKFast || c.mode == kModeKSlow) {
-      int n = (c.mode == kModeKFast) ? merge_tiles(mrow, crow, ntile, c.k, sh) : -1;
-      if (n < 0) n = slow_topk(rowp, V, aligned, c.T, c.k, sh);
-      status = draw_sorted(sh, n, c, row, &id, &kept, mask_row);
-    } else {  // full vocabulary
-      const float m = scaled(key2f(pkey(top)), c.T);
-      if (m == kInf) {
-        status = VS_ROW_BAD_PARAM;
-      } else {
-        full = true;
-        if (c.p < 1.0f) {
-          full_topp_cut(rowp, V, aligned, c, m, sh, d);
-        } else if (threadIdx.x == 0) {
-          d->mode = (c.mp > 0.0f) ? kFullMinP : kFullNone;
-          d->m = m;
-          d->tau = 0;
-          d->id_cut = 0;
-          d->kept = 0;
-        }
-      }
-    }
-  }
-  if (threadIdx.x == 0) {
-    if (!full) d->mode = kFullSkip;
-    if (status) {
-      id = -1;
-      kept = 0;
-    }
-    if (!full) {
-      out_ids[row] = id;
-      if (out_kept) out_kept[row] = kept;
-    }
-    if (out_status) out_status[row] = status;
-  }
-  if (status && mask_row) {  // a row that failed after setting bits reports an empty set
-    __syncthreads();
-    for (int i = threadIdx.x; i < mwords; i += blockDim.x) mask_row[i] = 0u;
-  }
-}
-
-template <typename E>
-__global__ __launch_bounds__(kRowThreads) void k_lse_row(
-    const E* __restrict__ logits, int B, int V, int64_t ld, bool aligned, int k,
-    const int32_t* __restrict__ token_ids, int ntile, const uint32_t* __restrict__ meta,
-    const uint64_t* __restrict__ cand, const LsePart* __restrict__ lpart,
-    float2* __restrict__ rlse, float* __restrict__ out_tok, int32_t* __restrict__ out_ids,
-    float* __restrict__ out_lp, int32_t* __restrict__ out_status) {
-  __shared__ RowShared sh;
-  const int row = blockIdx.x;
-  const uint32_t* mrow = meta + static_cast<size_t>(row) * ntile;
-  const uint64_t* crow = cand + static_cast<size_t>(row) * ntile * kFastK;
-  const LsePart* lrow = lpart + static_cast<size_t>(row) * ntile;
-  const E* rowp = logits + static_cast<int64_t>(row) * ld;
-
-  int bad = 0;
-  float M = -kInf;
-  for (int t = threadIdx.x; t < ntile; t += blockDim.x) {
-    if (mrow[t] & kMetaBadLogits) bad = 1;
-    M = fmaxf(M, lrow[t].m);
-  }
-  bad = block_max(bad, sh.ri);
-  M = block_max(M, reinterpret_cast<float*>(sh.rd));
-  float S = 0.0f;
-  if (M != -kInf) {
-    for (int t = threadIdx.x; t < ntile; t += blockDim.x) {
-      const LsePart p = lrow[t];
-      if (p.m != -kInf) S += p.s * __expf(p.m - M);
-    }
-  }
-  S = block_sum(S, reinterpret_cast<float*>(sh.rd));
-  int status = (bad || M == -kInf) ? VS_ROW_BAD_LOGITS : 0;
-  const float nanv = __builtin_nanf("");
-  const float logS = logf(S);
-  if (threadIdx.x == 0) {
-    rlse[row] = status ? make_float2(nanv, nanv) : make_float2(M, logS);
-  }
-  if (token_ids) {
-    const int tok = token_ids[row];
-    const bool badtok = tok < 0 || tok >= V;
-    if (badtok) status |= VS_ROW_BAD_TOKEN_ID;
-    if (threadIdx.x == 0)
-      out_tok[row] = (status & VS_ROW_BAD_LOGITS) || badtok ? nanv : (to_f32(rowp[tok]) - M) - logS;
-  }
-  if (k > 0) {
-    int32_t* ids = out_ids + static_cast<size_t>(row) * k;
-    float* lps = out_lp + static_cast<size_t>(row) * k;
-    if (status & VS_ROW_BAD_LOGITS) {
-      for (int i = threadIdx.x; i < k; i += blockDim.x) {
-        ids[i] = -1;
-        lps[i] = nanv;
-      }
-    } else {
-      int n = merge_tiles(mrow, crow, ntile, k, sh);
-      if (n < 0) n = slow_topk(rowp, V, aligned, 1.0f, k, sh);
-      for (int i = threadIdx.x; i < k; i += blockDim.x) {
-        if (i < n) {
-          const uint64_t P = sh.buf[i];
-          ids[i] = pid(P);
-          lps[i] = (key2f(pkey(P)) - M) - logS;
-        } else {
-          ids[i] = -1;
-          lps[i] = nanv;
-        }
-      }
-    }
-  }
-  if (threadIdx.x == 0 && out_status) out_status[row] = status;
 }
 
 }  // namespace
 
-hipError_t launch_row(const SampleArgs& a, const WsLayout& L, char* ws, hipStream_t st) {
-  const auto* meta = reinterpret_cast<const uint32_t*>(ws + L.meta);
-  const auto* cand = reinterpret_cast<const uint64_t*>(ws + L.cand);
-  auto* desc = reinterpret_cast<RowDesc*>(ws + L.desc);
-  if (a.dt == VS_F32)
-    hipLaunchKernelGGL(k_row<float>, dim3(a.B), dim3(kRowThreads), 0, st,
-                       static_cast<const float*>(a.logits), a.B, a.V, a.ld, a.aligned, a.temperature,
-                       a.top_k, a.top_p, a.min_p, a.seeds, a.hints, L.ntile1, meta, cand, desc,
-                       a.out_ids, a.out_kept, a.out_mask, a.out_status);
+hipError_t launch_row_light(const Job& j, hipStream_t st) {
+  if (j.dt == VS_F32)
+    hipLaunchKernelGGL(k_row_light<float>, dim3(j.B), dim3(kLightThreads), 0, st, j);
   else
-    hipLaunchKernelGGL(k_row<uint16_t>, dim3(a.B), dim3(kRowThreads), 0, st,
-                       static_cast<const uint16_t*>(a.logits), a.B, a.V, a.ld, a.aligned,
-                       a.temperature, a.top_k, a.top_p, a.min_p, a.seeds, a.hints, L.ntile1, meta,
-                       cand, desc, a.out_ids, a.out_kept, a.out_mask, a.out_status);
+    hipLaunchKernelGGL(k_row_light<uint16_t>, dim3(j.B), dim3(kLightThreads), 0, st, j);
   return hipGetLastError();
 }
 
-hipError_t launch_lse_row(const LogprobArgs& a, const WsLayout& L, char* ws, hipStream_t st) {
-  const auto* meta = reinterpret_cast<const uint32_t*>(ws + L.meta);
-  const auto* cand = reinterpret_cast<const uint64_t*>(ws + L.cand);
-  const auto* lp = reinterpret_cast<const LsePart*>(ws + L.lpart);
-  auto* rl = reinterpret_cast<float2*>(ws + L.rlse);
-  if (a.dt == VS_F32)
-    hipLaunchKernelGGL(k_lse_row<float>, dim3(a.B), dim3(kRowThreads), 0, st,
-                       static_cast<const float*>(a.logits), a.B, a.V, a.ld, a.aligned, a.k,
-                       a.token_ids, L.ntile1, meta, cand, lp, rl, a.out_token_lp, a.out_topk_ids,
-                       a.out_topk_lp, a.out_status);
+hipError_t launch_row_full(const Job& j, hipStream_t st) {
+  if (j.dt == VS_F32)
+    hipLaunchKernelGGL(k_row_full<float>, dim3(j.B), dim3(kFullThreads), 0, st, j);
   else
-    hipLaunchKernelGGL(k_lse_row<uint16_t>, dim3(a.B), dim3(kRowThreads), 0, st,
-                       static_cast<const uint16_t*>(a.logits), a.B, a.V, a.ld, a.aligned, a.k,
-                       a.token_ids, L.ntile1, meta, cand, lp, rl, a.out_token_lp, a.out_topk_ids,
-                       a.out_topk_lp, a.out_status);
+    hipLaunchKernelGGL(k_row_full<uint16_t>, dim3(j.B), dim3(kFullThreads), 0, st, j);
   return hipGetLastError();
 }
 

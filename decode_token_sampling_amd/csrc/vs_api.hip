@@ -12,17 +12,17 @@ size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 WsLayout ws_layout(int B, int V) {
   WsLayout L{};
-  L.B = B;
-  L.V = V;
-  L.ntile1 = (V + kSelTile - 1) / kSelTile;
-  L.wpr1 = (L.ntile1 + kSelWaves - 1) / kSelWaves;
+  L.ntile = (V + kSelTile - 1) / kSelTile;
+  L.wpr = (L.ntile + kSelWaves - 1) / kSelWaves;
   L.ntile3 = (V + kGumTile - 1) / kGumTile;
-  const size_t tiles = static_cast<size_t>(B) * L.ntile1;
+  const size_t tiles = static_cast<size_t>(B) * L.ntile;
   size_t off = 0;
   L.meta = off;
   off = align_up(off + tiles * sizeof(uint32_t));
-  L.cand = off;
-  off = align_up(off + tiles * kFastK * sizeof(uint64_t));
+  L.candA = off;
+  off = align_up(off + tiles * kSelCap * sizeof(uint64_t));
+  L.candB = off;
+  off = align_up(off + tiles * kSelCap * sizeof(uint64_t));
   L.desc = off;
   off = align_up(off + static_cast<size_t>(B) * sizeof(RowDesc));
   L.gpart = off;
@@ -33,6 +33,30 @@ WsLayout ws_layout(int B, int V) {
   off = align_up(off + static_cast<size_t>(B) * sizeof(float2));
   L.total = off;
   return L;
+}
+
+Job make_job(const void* logits, vs_dtype dt, int B, int V, int64_t ld, void* ws) {
+  const WsLayout L = ws_layout(B, V);
+  char* w = static_cast<char*>(ws);
+  Job j{};
+  j.logits = logits;
+  j.dt = dt;
+  j.B = B;
+  j.V = V;
+  j.ld = ld;
+  const int64_t es = (dt == VS_F32) ? 4 : 2;
+  j.aligned = (reinterpret_cast<uintptr_t>(logits) % 16 == 0) && ((ld * es) % 16 == 0);
+  j.ntile = L.ntile;
+  j.wpr = L.wpr;
+  j.ntile3 = L.ntile3;
+  j.meta = reinterpret_cast<uint32_t*>(w + L.meta);
+  j.candA = reinterpret_cast<uint64_t*>(w + L.candA);
+  j.candB = reinterpret_cast<uint64_t*>(w + L.candB);
+  j.desc = reinterpret_cast<RowDesc*>(w + L.desc);
+  j.gpart = reinterpret_cast<GPart*>(w + L.gpart);
+  j.lpart = reinterpret_cast<LsePart*>(w + L.lpart);
+  j.rlse = reinterpret_cast<float2*>(w + L.rlse);
+  return j;
 }
 
 }  // namespace vsk
@@ -63,11 +87,6 @@ hipError_t stage(const char* name, hipStream_t st, F&& launch) {
 
 bool sizes_ok(vs_dtype dt, int B, int V, int64_t ld) {
   return (dt == VS_F32 || dt == VS_BF16) && B > 0 && V > 0 && V <= VS_MAX_V && ld >= V;
-}
-
-bool rows_aligned(const void* p, vs_dtype dt, int64_t ld) {
-  const int64_t es = (dt == VS_F32) ? 4 : 2;
-  return (reinterpret_cast<uintptr_t>(p) % 16 == 0) && ((ld * es) % 16 == 0);
 }
 
 }  // namespace
@@ -115,20 +134,57 @@ vs_status vs_sample(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
                     int32_t* out_kept_count, uint32_t* out_kept_mask,
                     int32_t* out_row_status, void* ws, size_t ws_bytes,
                     hipStream_t stream) {
+  return vs_sample_logprobs(logits, dt, B, V, ld, temperature, top_k, top_p, min_p, seeds, hints,
+                            out_ids, out_kept_count, out_kept_mask, out_row_status, nullptr, 0,
+                            nullptr, nullptr, nullptr, 0, ws, ws_bytes, stream);
+}
+
+vs_status vs_sample_logprobs(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
+                             const float* temperature, const int32_t* top_k,
+                             const float* top_p, const float* min_p,
+                             const uint64_t* seeds, uint32_t hints, int32_t* out_ids,
+                             int32_t* out_kept_count, uint32_t* out_kept_mask,
+                             int32_t* out_row_status, float* out_token_logprob, int k,
+                             int32_t* out_topk_ids, float* out_topk_logprobs, float* out_full,
+                             int64_t ld_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!logits || !out_ids || !ws || !sizes_ok(dt, B, V, ld)) return VS_ERR_INVALID_ARGUMENT;
   if (hints & ~(VS_HINT_NO_FULLVOCAB | VS_HINT_ALL_GREEDY)) return VS_ERR_INVALID_ARGUMENT;
-  const WsLayout L = vsk::ws_layout(B, V);
-  if (ws_bytes < L.total) return VS_ERR_WORKSPACE_TOO_SMALL;
-  vsk::SampleArgs a{logits, dt, B, V, ld, rows_aligned(logits, dt, ld), temperature, top_k,
-                    top_p, min_p, seeds, hints, out_ids, out_kept_count, out_kept_mask,
-                    out_row_status};
-  char* w = static_cast<char*>(ws);
-  if (stage("select", stream, [&] { return vsk::launch_select(a, L, w, stream); }) != hipSuccess)
+  if (k < 0 || k > VS_LOGPROB_K_MAX || k > V) return VS_ERR_INVALID_ARGUMENT;
+  if (k > 0 && (!out_topk_ids || !out_topk_logprobs)) return VS_ERR_INVALID_ARGUMENT;
+  if (out_full && ld_out < V) return VS_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < vsk::ws_layout(B, V).total) return VS_ERR_WORKSPACE_TOO_SMALL;
+  vsk::Job j = vsk::make_job(logits, dt, B, V, ld, ws);
+  j.sample = 1;
+  j.T = temperature;
+  j.k = top_k;
+  j.p = top_p;
+  j.mp = min_p;
+  j.seeds = seeds;
+  j.hints = hints;
+  j.out_ids = out_ids;
+  j.out_kept = out_kept_count;
+  j.out_mask = out_kept_mask;
+  j.out_status = out_row_status;
+  j.lse = (out_token_logprob != nullptr || k > 0 || out_full != nullptr) ? 1 : 0;
+  j.k_lp = k;
+  j.tok_sampled = out_token_logprob != nullptr;
+  j.out_tok_lp = out_token_logprob;
+  j.out_lp_ids = out_topk_ids;
+  j.out_lp = out_topk_logprobs;
+  j.out_full = out_full;
+  j.ld_out = ld_out;
+  if (stage("select", stream, [&] { return vsk::launch_select(j, stream); }) != hipSuccess)
     return VS_ERR_HIP;
-  if (stage("row", stream, [&] { return vsk::launch_row(a, L, w, stream); }) != hipSuccess)
+  if (stage("row", stream, [&] { return vsk::launch_row_light(j, stream); }) != hipSuccess)
     return VS_ERR_HIP;
   if (!(hints & (VS_HINT_NO_FULLVOCAB | VS_HINT_ALL_GREEDY))) {
-    if (stage("gumbel", stream, [&] { return vsk::launch_gumbel(a, L, w, stream); }) != hipSuccess)
+    if (stage("row_full", stream, [&] { return vsk::launch_row_full(j, stream); }) != hipSuccess)
+      return VS_ERR_HIP;
+    if (stage("gumbel", stream, [&] { return vsk::launch_gumbel(j, stream); }) != hipSuccess)
+      return VS_ERR_HIP;
+  }
+  if (out_full) {
+    if (stage("lse_full", stream, [&] { return vsk::launch_lse_full(j, stream); }) != hipSuccess)
       return VS_ERR_HIP;
   }
   return VS_OK;
@@ -144,20 +200,23 @@ vs_status vs_logprobs(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
   if (k < 0 || k > VS_LOGPROB_K_MAX || k > V) return VS_ERR_INVALID_ARGUMENT;
   if (k > 0 && (!out_topk_ids || !out_topk_logprobs)) return VS_ERR_INVALID_ARGUMENT;
   if (out_full && ld_out < V) return VS_ERR_INVALID_ARGUMENT;
-  const WsLayout L = vsk::ws_layout(B, V);
-  if (ws_bytes < L.total) return VS_ERR_WORKSPACE_TOO_SMALL;
-  vsk::LogprobArgs a{logits, dt, B, V, ld, rows_aligned(logits, dt, ld), token_ids,
-                     out_token_logprob, k, out_topk_ids, out_topk_logprobs, out_full, ld_out,
-                     out_row_status};
-  char* w = static_cast<char*>(ws);
-  if (stage("lse_select", stream, [&] { return vsk::launch_select_lse(a, L, w, stream); }) !=
-      hipSuccess)
+  if (ws_bytes < vsk::ws_layout(B, V).total) return VS_ERR_WORKSPACE_TOO_SMALL;
+  vsk::Job j = vsk::make_job(logits, dt, B, V, ld, ws);
+  j.lse = 1;
+  j.k_lp = k;
+  j.tok = token_ids;
+  j.out_tok_lp = out_token_logprob;
+  j.out_lp_ids = out_topk_ids;
+  j.out_lp = out_topk_logprobs;
+  j.out_full = out_full;
+  j.ld_out = ld_out;
+  j.out_lp_status = out_row_status;
+  if (stage("lse_select", stream, [&] { return vsk::launch_select(j, stream); }) != hipSuccess)
     return VS_ERR_HIP;
-  if (stage("lse_row", stream, [&] { return vsk::launch_lse_row(a, L, w, stream); }) != hipSuccess)
+  if (stage("lse_row", stream, [&] { return vsk::launch_row_light(j, stream); }) != hipSuccess)
     return VS_ERR_HIP;
   if (out_full) {
-    if (stage("lse_full", stream, [&] { return vsk::launch_lse_full(a, L, w, stream); }) !=
-        hipSuccess)
+    if (stage("lse_full", stream, [&] { return vsk::launch_lse_full(j, stream); }) != hipSuccess)
       return VS_ERR_HIP;
   }
   return VS_OK;

@@ -189,14 +189,7 @@ __device__ __forceinline__ RowCfg load_cfg(int r, int V, const float* temperatur
 }
 
 // ---------------------------------------------------------------- workspace records
-// Per select tile: meta = count | flags, then up to kFastK packed candidates.
-constexpr uint32_t kMetaCountMask = 0xffu;
-constexpr uint32_t kMetaBadLogits = 0x100u;
-constexpr uint32_t kMetaOverflow = 0x200u;
-constexpr uint32_t kMetaHasFinite = 0x400u;  // some value of the tile is above -inf
-
-// Full-vocabulary rows: what K2 hands to the Gumbel kernels.
-enum : uint32_t { kFullSkip = 0, kFullNone = 1, kFullMinP = 2, kFullTopP = 3 };
+// Per-row record handed from the row kernel to the full-vocabulary kernels.
 struct RowDesc {
   uint32_t mode;
   float m;         // max over the row of s = x / T
@@ -252,6 +245,92 @@ __device__ __forceinline__ int lanes_below(uint64_t ballot) {
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   __builtin_amdgcn_wave_barrier();
+}
+
+// DPP lane movement within rows of 16 lanes (gfx9 encodings): quad_perm,
+// row_ror. Every lane has a valid source for these controls.
+constexpr int kDppXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppRor4 = 0x124;   // row_ror:4
+constexpr int kDppRor8 = 0x128;   // row_ror:8
+template <int kCtrl>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xF, 0xF, false);
+}
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(dpp_i32<kCtrl>(__float_as_int(v)));
+}
+__device__ __forceinline__ float readlane_f32(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+// Wave-wide max / sum of an fp32 (uniform result): all-reduce inside each row
+// of 16 lanes with DPP, then combine the four rows through scalar reads.
+// fmaxf ignores NaN. The summation order is fixed, so results are reproducible.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_f32<kDppXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppRor4>(v));
+  v = fmaxf(v, dpp_f32<kDppRor8>(v));
+  return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)),
+               fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f32<kDppXor1>(v);
+  v += dpp_f32<kDppXor2>(v);
+  v += dpp_f32<kDppRor4>(v);
+  v += dpp_f32<kDppRor8>(v);
+  return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
+}
+__device__ __forceinline__ int wave_min_dpp(int v) {
+  v = min(v, dpp_i32<kDppXor1>(v));
+  v = min(v, dpp_i32<kDppXor2>(v));
+  v = min(v, dpp_i32<kDppRor4>(v));
+  v = min(v, dpp_i32<kDppRor8>(v));
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// k-th largest (1-based, 1 <= k <= 64) of one uint32 per lane, every lane of
+// the wave active: MSB-first radix select on ballots (32 rounds of one vector
+// compare and scalar bit counts; no LDS traffic).
+__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t key, int k) {
+  uint64_t cand = ~0ull;
+  uint32_t prefix = 0;
+#pragma unroll
+  for (int b = 31; b >= 0; --b) {
+    const uint64_t ones = __ballot((key >> b) & 1u) & cand;
+    const int c = __popcll(ones);
+    if (c >= k) {
+      cand = ones;
+      prefix |= 1u << b;
+    } else {
+      k -= c;
+      cand &= ~ones;
+    }
+  }
+  return prefix;
+}
+// Same over two uint32 per lane (k <= 128).
+__device__ __forceinline__ uint32_t wave_kth_largest2(uint32_t ka, uint32_t kb, int k) {
+  uint64_t ca = ~0ull, cb = ~0ull;
+  uint32_t prefix = 0;
+#pragma unroll
+  for (int b = 31; b >= 0; --b) {
+    const uint64_t oa = __ballot((ka >> b) & 1u) & ca;
+    const uint64_t ob = __ballot((kb >> b) & 1u) & cb;
+    const int c = __popcll(oa) + __popcll(ob);
+    if (c >= k) {
+      ca = oa;
+      cb = ob;
+      prefix |= 1u << b;
+    } else {
+      k -= c;
+      ca &= ~oa;
+      cb &= ~ob;
+    }
+  }
+  return prefix;
 }
 
 // Bitonic sort of one value per lane across the wave, larger first.

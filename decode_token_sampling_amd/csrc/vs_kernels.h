@@ -1,70 +1,118 @@
-// Host-side launch interface between the C ABI and the kernels.
+// What one ABI call asks of the kernels, and the per-row plan all kernels
+// derive from it identically.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/vs.h"
+#include "vs_device.h"
 
 namespace vsk {
 
-// One select/log-sum-exp tile is one wave's 64 lanes x 64 values.
-constexpr int kSelTile = 4096;
+constexpr int kSelTile = 4096;    // one wave's tile in the streaming pass
 constexpr int kSelWaves = 4;      // tiles per 256-thread workgroup
+constexpr int kSelCap = 128;      // candidate slots per tile and list
 constexpr int kGumTile = 4096;    // Gumbel tile: 256 threads x 16 values
 constexpr int kFullTile = 4096;   // full log-softmax write tile
 
-struct WsLayout {
-  int B, V;
-  int ntile1;   // select tiles per row
-  int wpr1;     // select workgroups per row
-  int ntile3;   // Gumbel tiles per row
-  size_t meta, cand, desc, gpart, lpart, rlse, total;
+// Tile meta word.
+constexpr uint32_t kMetaCountA = 0xffu;
+constexpr int kMetaCountBShift = 8;
+constexpr uint32_t kMetaBadLogits = 1u << 16;
+constexpr uint32_t kMetaHasFinite = 1u << 17;
+constexpr uint32_t kMetaOverflowA = 1u << 18;
+constexpr uint32_t kMetaOverflowB = 1u << 19;
+
+// Row descriptor states (written for every row by the row kernel each call).
+enum : uint32_t {
+  kRowDone = 0,       // id final (or the row failed)
+  kRowFullNone = 1,   // full vocabulary, no truncation: Gumbel kernels draw
+  kRowFullMinP = 2,   // full vocabulary, min-p only
+  kRowFullTopP = 3,   // full vocabulary, top-p cut given by (tau, id_cut)
+  kRowFull = 4,       // full vocabulary, the cut still to be found (heavy kernel)
 };
 
-WsLayout ws_layout(int B, int V);
-
-struct SampleArgs {
+struct Job {
   const void* logits;
-  vs_dtype dt;
+  int dt;  // vs_dtype
   int B, V;
   int64_t ld;
-  bool aligned;
-  const float* temperature;
-  const int32_t* top_k;
-  const float* top_p;
-  const float* min_p;
+  int aligned;
+  // sampling
+  int sample;
+  const float* T;
+  const int32_t* k;
+  const float* p;
+  const float* mp;
   const uint64_t* seeds;
   uint32_t hints;
   int32_t* out_ids;
   int32_t* out_kept;
   uint32_t* out_mask;
   int32_t* out_status;
-};
-
-struct LogprobArgs {
-  const void* logits;
-  vs_dtype dt;
-  int B, V;
-  int64_t ld;
-  bool aligned;
-  const int32_t* token_ids;
-  float* out_token_lp;
-  int k;
-  int32_t* out_topk_ids;
-  float* out_topk_lp;
+  // log-probabilities
+  int lse;                 // log-sum-exp wanted
+  int k_lp;                // top-k log-probs (0..64)
+  const int32_t* tok;      // ids whose log-prob is wanted (vs_logprobs), or NULL
+  int tok_sampled;         // the log-prob of the sampled id is wanted (fused call)
+  float* out_tok_lp;
+  int32_t* out_lp_ids;
+  float* out_lp;
   float* out_full;
   int64_t ld_out;
-  int32_t* out_status;
+  int32_t* out_lp_status;  // vs_logprobs status
+  // workspace
+  int ntile, wpr, ntile3;
+  uint32_t* meta;
+  uint64_t* candA;
+  uint64_t* candB;
+  LsePart* lpart;
+  float2* rlse;
+  RowDesc* desc;
+  GPart* gpart;
 };
 
-hipError_t launch_select(const SampleArgs& a, const WsLayout& L, char* ws, hipStream_t st);
-hipError_t launch_select_lse(const LogprobArgs& a, const WsLayout& L, char* ws, hipStream_t st);
-hipError_t launch_row(const SampleArgs& a, const WsLayout& L, char* ws, hipStream_t st);
-hipError_t launch_gumbel(const SampleArgs& a, const WsLayout& L, char* ws, hipStream_t st);
-hipError_t launch_lse_row(const LogprobArgs& a, const WsLayout& L, char* ws, hipStream_t st);
-hipError_t launch_lse_full(const LogprobArgs& a, const WsLayout& L, char* ws, hipStream_t st);
+struct Plan {
+  RowCfg c;
+  int kA;       // list A: 1 = argmax of x, 2..64 = top-k of s = x / TA, 0 = none
+  float TA;
+  int kB;       // list B: top-k of x for log-probs, when list A cannot serve
+  bool shared;  // the log-prob top-k comes from list A
+};
+
+__device__ __forceinline__ Plan plan_row(const Job& j, int row) {
+  Plan pl;
+  pl.kB = 0;
+  pl.shared = true;
+  if (j.sample) {
+    pl.c = load_cfg(row, j.V, j.T, j.k, j.p, j.mp, j.seeds);
+    const bool fast = pl.c.mode == kModeKFast && !(j.hints & VS_HINT_ALL_GREEDY);
+    pl.kA = fast ? pl.c.k : 1;
+    pl.TA = fast ? pl.c.T : 1.0f;
+    if (j.lse && j.k_lp > 0) {
+      pl.shared = (pl.kA == 1) ? (j.k_lp == 1) : (pl.TA == 1.0f && j.k_lp <= pl.kA);
+      pl.kB = pl.shared ? 0 : j.k_lp;
+    }
+  } else {
+    pl.c = RowCfg{kModeInvalid, 0, 1.0f, 0, 1.0f, 0.0f, 0ull};
+    pl.kA = j.k_lp;
+    pl.TA = 1.0f;
+  }
+  return pl;
+}
+
+struct WsLayout {
+  int ntile, wpr, ntile3;
+  size_t meta, candA, candB, desc, gpart, lpart, rlse, total;
+};
+WsLayout ws_layout(int B, int V);
+
+hipError_t launch_select(const Job& j, hipStream_t st);
+hipError_t launch_row_light(const Job& j, hipStream_t st);
+hipError_t launch_row_full(const Job& j, hipStream_t st);
+hipError_t launch_gumbel(const Job& j, hipStream_t st);
+hipError_t launch_lse_full(const Job& j, hipStream_t st);
 hipError_t launch_penalize(void* logits, vs_dtype dt, int B, int V, int64_t ld,
                            const int32_t* prompt_ids, const int32_t* prompt_off,
                            const int32_t* output_ids, const int32_t* output_off,

@@ -7,6 +7,7 @@
  *   vs_penalize  presence / frequency / repetition penalties, in place
  *   vs_sample    temperature, min-p, top-k, top-p, then a seeded Gumbel-max draw
  *   vs_logprobs  log-softmax log-probabilities (given ids, top-k, full rows)
+ *   vs_sample_logprobs  the last two fused: the logits are read once
  *
  * Conventions shared by every call:
  *  - All array arguments are DEVICE pointers unless stated otherwise; sizes and
@@ -143,6 +144,27 @@ vs_status vs_sample(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
                     hipStream_t stream);
 
 /*
+ * vs_sample_logprobs — vs_sample and the log-probabilities of the same logits
+ * in one pass over them: the result equals vs_sample followed by vs_logprobs
+ * with token_ids = out_ids (a row whose id is -1 gets a NaN log-prob), but the
+ * logits are read once (the streaming pass also forms the log-sum-exp partials
+ * and the top-k candidates of the raw logits).
+ *
+ *  out_token_logprob [B] fp32 or NULL: log-prob of the sampled id
+ *  k, out_topk_ids, out_topk_logprobs, out_full, ld_out: as in vs_logprobs
+ *  other arguments and out_row_status: as in vs_sample (the status of the draw;
+ *  a row with bad logits also gets NaN log-probs and top-k ids -1)
+ */
+vs_status vs_sample_logprobs(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
+                             const float* temperature, const int32_t* top_k,
+                             const float* top_p, const float* min_p,
+                             const uint64_t* seeds, uint32_t hints, int32_t* out_ids,
+                             int32_t* out_kept_count, uint32_t* out_kept_mask,
+                             int32_t* out_row_status, float* out_token_logprob, int k,
+                             int32_t* out_topk_ids, float* out_topk_logprobs, float* out_full,
+                             int64_t ld_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * vs_logprobs — log-softmax log-probabilities of the buffer given (temperature
  * 1, no truncation), as the TT sampling README's LogProbsCalculator ("Key
  * Components": numerically stable log-softmax via the max and the sum of
@@ -169,8 +191,8 @@ vs_status vs_logprobs(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
  * hipEventRecord(events[2i]) and hipEventRecord(events[2i+1]) on that call's
  * stream, i = 0, 1, ... in enqueue order, until `capacity` events are used.
  * `events` is a host array of events the caller created (hipEventCreate) and
- * owns. Stage names: "select", "row", "gumbel", "lse_select", "lse_row",
- * "lse_full", "penalize". vs_profile_end stops recording on this thread,
+ * owns. Stage names: "select", "row", "row_full", "gumbel", "lse_select",
+ * "lse_row", "lse_full", "penalize". vs_profile_end stops recording on this thread,
  * copies up to max_names stage-name pointers (static strings) to `names` (may
  * be NULL) and returns the number of stages recorded.
  */

@@ -18,8 +18,8 @@ def _declared():
 
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["vs_workspace_size", "vs_status_string", "vs_penalize",
-                                  "vs_sample", "vs_logprobs", "vs_profile_begin",
-                                  "vs_profile_end"])
+                                  "vs_sample", "vs_logprobs", "vs_sample_logprobs",
+                                  "vs_profile_begin", "vs_profile_end"])
 
 
 def test_library_exports_every_declared_symbol():

@@ -321,3 +321,84 @@ def test_workload_w1024x128256_f32():
 
 def test_workload_w64x262144_bf16():
     _run_workload("w64x262144_bf16")
+
+
+# ---------------------------------------------------------------- fused draw + log-probs
+def _check_fused_logprobs(x, V, out, k):
+    ids = out["ids"].cpu().numpy()
+    o = oracle.logprobs(x, V, ids, k=k)
+    tlp = out["token_lp"].cpu().numpy()
+    ok = ~np.isnan(o["token_lp"])
+    assert np.array_equal(np.isnan(tlp), ~ok)
+    assert np.allclose(tlp[ok], o["token_lp"][ok], atol=LOGPROB_ATOL, rtol=0)
+    if k:
+        assert np.array_equal(out["topk_ids"].cpu().numpy(), o["topk_ids"])
+        gl, ol = out["topk_lp"].cpu().numpy(), o["topk_lp"]
+        assert np.array_equal(np.isnan(gl), np.isnan(ol))
+        fin = ~np.isnan(ol)
+        assert np.allclose(gl[fin], ol[fin], atol=LOGPROB_ATOL, rtol=0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [7, 4097, 32000, 70001])
+@pytest.mark.parametrize("k", [0, 1, 5, 64])
+def test_sample_logprobs_fused(V, dtype, k):
+    import decode_token_sampling_amd as vs
+    B = 27
+    k = min(k, V)
+    x = _row_shapes(2000 + V, B, V, dtype)
+    x[3, 1] = np.nan if dtype == "f32" else 0x7FC0   # a bad row
+    w = random_params(np.random.default_rng(V + k), B, V)
+    out = vs.sample_logprobs(to_device(x), dev(w["temperature"], np.float32),
+                             dev(w["top_k"], np.int32), dev(w["top_p"], np.float32),
+                             dev(w["min_p"], np.float32),
+                             dev(np.asarray(w["seeds"], np.uint64).view(np.int64), np.int64),
+                             k=k, mask=True, V=V)
+    torch.cuda.synchronize()
+    from parity import mask_bits
+    g = dict(ids=out["ids"].cpu().numpy(), kept=out["kept"].cpu().numpy(),
+             status=out["status"].cpu().numpy(), mask=mask_bits(out["mask"], V))
+    compare_sample(g, oracle_sample(x, V, w))
+    _check_fused_logprobs(x, V, out, k)
+
+
+def test_fused_equals_separate_calls():
+    import decode_token_sampling_amd as vs
+    V, B = 50000, 24
+    x = _row_shapes(31, B, V, "f32")
+    w = random_params(np.random.default_rng(4), B, V)
+    args = [dev(w["temperature"], np.float32), dev(w["top_k"], np.int32), dev(w["top_p"], np.float32),
+            dev(w["min_p"], np.float32), dev(np.asarray(w["seeds"], np.uint64).view(np.int64), np.int64)]
+    xd = to_device(x)
+    f = vs.sample_logprobs(xd, *args, k=20, full=True)
+    s = vs.sample(xd, *args)
+    l = vs.logprobs(xd, s["ids"], k=20, full=True)
+    torch.cuda.synchronize()
+    assert torch.equal(f["ids"], s["ids"]) and torch.equal(f["kept"], s["kept"])
+    assert torch.equal(f["status"], s["status"])
+    good = s["ids"] >= 0
+    assert torch.equal(f["token_lp"][good], l["token_lp"][good])
+    assert torch.equal(f["topk_ids"], l["topk_ids"]) and torch.equal(f["topk_lp"], l["topk_lp"])
+    assert torch.equal(f["full"], l["full"])
+
+
+def test_workload_fused_w256x248320_f32():
+    import decode_token_sampling_amd as vs
+    wl = synth.make("w256x248320_f32")
+    x = wl.logits
+    w = params_from(wl)
+    out = vs.sample_logprobs(to_device(x), dev(w["temperature"], np.float32),
+                             dev(w["top_k"], np.int32), dev(w["top_p"], np.float32),
+                             dev(w["min_p"], np.float32),
+                             dev(np.asarray(w["seeds"], np.uint64).view(np.int64), np.int64),
+                             hints=vs.HINT_NO_FULLVOCAB, k=20, mask=True)
+    torch.cuda.synchronize()
+    from parity import mask_bits
+    g = dict(ids=out["ids"].cpu().numpy(), kept=out["kept"].cpu().numpy(),
+             status=out["status"].cpu().numpy(), mask=mask_bits(out["mask"], wl.V))
+    near = compare_sample(g, oracle_sample(x, wl.V, w))
+    print(f"near-tie rows: {near}")
+    rows = np.arange(0, wl.B, 4)
+    sub = {kk: (v[torch.from_numpy(rows).cuda()] if isinstance(v, torch.Tensor) else v)
+           for kk, v in out.items()}
+    _check_fused_logprobs(np.ascontiguousarray(x[rows]), wl.V, sub, 20)
