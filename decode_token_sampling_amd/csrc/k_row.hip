@@ -291,26 +291,33 @@ __device__ uint64_t block_kth_largest(const uint64_t* a, int n, int k, Sh& sh) {
 
 // The exact top k (order: key desc, id asc) of the union of one candidate list
 // over the row's tiles, sorted into sh.buf[0..min(k, total)). Returns the
-// count, or -1 when a tile overflowed or the union does not fit.
+// count, or -1 when a tile overflowed or the union does not fit. Only entries
+// whose key reaches P* = the largest per-tile exact k-th key are gathered: that
+// tile alone holds k values >= P*, so no entry below it is in the row's top k.
 template <class Sh>
 __device__ int union_topk(const uint32_t* __restrict__ mrow, const uint64_t* __restrict__ crow,
-                          int ntile, int shift, uint32_t ovf_flag, int k, Sh& sh) {
-  // tile counts -> offsets (each thread owns consecutive tiles)
+                          const uint32_t* __restrict__ kth_row, int ntile, int shift,
+                          uint32_t ovf_flag, int k, Sh& sh) {
+  // tile counts -> offsets (each thread owns consecutive tiles), and P*
   const int G = (ntile + blockDim.x - 1) / blockDim.x;
   int lc = 0, ovf = 0;
+  uint32_t lp = 0;
   for (int g = 0; g < G; ++g) {
     const int t = threadIdx.x * G + g;
     if (t < ntile) {
       const uint32_t m = mrow[t];
       if (m & ovf_flag) ovf = 1;
       lc += static_cast<int>((m >> shift) & 0xffu);
+      const uint32_t kt = kth_row[t];
+      lp = kt > lp ? kt : lp;
     }
   }
   ovf = block_max(ovf, sh.ri);
   if (ovf) return -1;
-  int n;
-  int off = block_scan_incl(lc, sh.ri, &n) - lc;
-  if (n > Sh::kBufCap) return -1;
+  const uint64_t pstar = static_cast<uint64_t>(block_max(lp, reinterpret_cast<uint32_t*>(sh.ri)))
+                         << 32;
+  int total;
+  int off = block_scan_incl(lc, sh.ri, &total) - lc;
   for (int g = 0; g < G; ++g) {
     const int t = threadIdx.x * G + g;
     if (t < ntile) {
@@ -318,20 +325,22 @@ __device__ int union_topk(const uint32_t* __restrict__ mrow, const uint64_t* __r
       off += static_cast<int>((mrow[t] >> shift) & 0xffu);
     }
   }
-  if (threadIdx.x == 0) sh.toff[ntile] = n;
+  if (threadIdx.x == 0) {
+    sh.toff[ntile] = total;
+    sh.n = 0;
+  }
   __syncthreads();
-  // Copy the n valid entries with all threads: entry g lives in the tile t
-  // with toff[t] <= g < toff[t+1] (binary search in LDS). Four loads are issued
+  // Read the valid entries with all threads: entry g lives in the tile t with
+  // toff[t] <= g < toff[t+1] (binary search in LDS). Four loads are issued
   // before any is used so their latencies overlap.
   constexpr int U = 4;
-  for (int g0 = threadIdx.x; g0 < n; g0 += U * blockDim.x) {
+  for (int g0 = threadIdx.x; g0 < total; g0 += U * blockDim.x) {
     uint64_t v[U];
-    int dst[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int g = g0 + u * static_cast<int>(blockDim.x);
-      dst[u] = g;
-      if (g < n) {
+      v[u] = 0ull;
+      if (g < total) {
         int lo = 0, hi = ntile - 1;  // last t with toff[t] <= g
         while (lo < hi) {
           const int mid = (lo + hi + 1) >> 1;
@@ -341,11 +350,18 @@ __device__ int union_topk(const uint32_t* __restrict__ mrow, const uint64_t* __r
       }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (dst[u] < n) sh.buf[dst[u]] = v[u];
+    for (int u = 0; u < U; ++u) {
+      if (v[u] >= pstar && v[u] != 0ull) {
+        const int pos = atomicAdd(&sh.n, 1);
+        if (pos < Sh::kBufCap) sh.buf[pos] = v[u];
+      }
+    }
   }
   __syncthreads();
-  if (n > k) {
+  int n = sh.n;
+  __syncthreads();
+  if (n > Sh::kBufCap) return -1;
+  if (n > 256 && n > k) {
     const uint64_t thr = block_kth_largest(sh.buf, n, k, sh);
     uint64_t* tmp = sh.hw;  // at least 2048 slots
     if (threadIdx.x == 0) sh.n = 0;
@@ -360,7 +376,7 @@ __device__ int union_topk(const uint32_t* __restrict__ mrow, const uint64_t* __r
     n = k;
   }
   sort_desc(sh.buf, n);
-  return n;
+  return n < k ? n : k;
 }
 
 // Exact top k of s = x / T over the row data (k <= 1024); sorted into sh.buf.
@@ -504,6 +520,8 @@ __global__ __launch_bounds__(kLightThreads) void k_row_light(Job j) {
   const uint32_t* mrow = j.meta + static_cast<size_t>(row) * ntile;
   const uint64_t* crowA = j.candA + static_cast<size_t>(row) * ntile * kSelCap;
   const uint64_t* crowB = j.candB + static_cast<size_t>(row) * ntile * kSelCap;
+  const uint32_t* kthA = j.kthA + static_cast<size_t>(row) * ntile;
+  const uint32_t* kthB = j.kthB + static_cast<size_t>(row) * ntile;
   const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
   const bool aligned = j.aligned;
   const float nanv = __builtin_nanf("");
@@ -567,7 +585,7 @@ __global__ __launch_bounds__(kLightThreads) void k_row_light(Job j) {
         kept = 1;
         if (mask_row && threadIdx.x == 0) atomicOr(&mask_row[id >> 5], 1u << (id & 31));
       } else if (c.mode == kModeKFast || c.mode == kModeKSlow) {
-        int n = (pl.kA > 1) ? union_topk(mrow, crowA, ntile, 0, kMetaOverflowA, c.k, sh) : -1;
+        int n = (pl.kA > 1) ? union_topk(mrow, crowA, kthA, ntile, 0, kMetaOverflowA, c.k, sh) : -1;
         if (n < 0) n = slow_topk(rowp, j.V, aligned, c.T, c.k, sh);
         if (c.T == 1.0f) sorted_shared = n;
         if (n <= kWave) {
@@ -645,8 +663,9 @@ __global__ __launch_bounds__(kLightThreads) void k_row_light(Job j) {
       } else if (pl.shared && sorted_shared >= k) {
         n = sorted_shared;
       } else {
-        n = pl.shared ? union_topk(mrow, crowA, ntile, 0, kMetaOverflowA, k, sh)
-                      : union_topk(mrow, crowB, ntile, kMetaCountBShift, kMetaOverflowB, k, sh);
+        n = pl.shared
+                ? union_topk(mrow, crowA, kthA, ntile, 0, kMetaOverflowA, k, sh)
+                : union_topk(mrow, crowB, kthB, ntile, kMetaCountBShift, kMetaOverflowB, k, sh);
         if (n < 0) n = slow_topk(rowp, j.V, aligned, 1.0f, k, sh);
       }
       for (int i = threadIdx.x; i < k; i += blockDim.x) {

@@ -33,15 +33,19 @@ __device__ __forceinline__ int elem_index(int tile_base, int q) {
 
 template <typename E>
 __device__ __forceinline__ void load_tile(const E* __restrict__ rowp, int tile_base, int V,
-                                          bool vec, float (&v)[kVals]) {
+                                          bool vec, bool stream, float (&v)[kVals]) {
   constexpr int EPV = Epv<E>::n;
   constexpr int NV = kVals / EPV;
   const int l = lane();
   if (vec) {
     uint4 raw[NV];
+    if (stream) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
-      raw[i] = *reinterpret_cast<const uint4*>(rowp + tile_base + (i * kWave + l) * EPV);
+      for (int i = 0; i < NV; ++i) raw[i] = load16_stream(rowp + tile_base + (i * kWave + l) * EPV);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) raw[i] = load16(rowp + tile_base + (i * kWave + l) * EPV);
+    }
 #pragma unroll
     for (int i = 0; i < NV; ++i) unpack16(raw[i], &v[i * EPV], rowp);
   } else {
@@ -80,12 +84,50 @@ __device__ __forceinline__ uint64_t tile_argmax(const float (&v)[kVals], float M
   return 0ull;
 }
 
+// Stages in LDS (sk: keys, si: ids; one region per wave) every value of the
+// tile that reaches the threshold: v >= pre, and for T != 1 also
+// key(v / T) >= sig_key. Returns the count (only the first kSelCap are stored).
+template <typename E, bool kVec, bool kT1>
+__device__ __forceinline__ int extract(const float (&v)[kVals], int tile_base, int V, float pre,
+                                       uint32_t sig_key, float T, uint32_t* __restrict__ sk,
+                                       int32_t* __restrict__ si) {
+  int n = 0;
+#pragma unroll
+  for (int q = 0; q < kVals; ++q) {
+    bool p = v[q] >= pre;
+    if (!kVec) p = p && elem_index<E>(tile_base, q) < V;
+    uint64_t bal = __builtin_amdgcn_ballot_w64(p);
+    if (bal) {  // uniform: taken only when some lane has a candidate here
+      uint32_t key = f2key(v[q]);
+      if (!kT1) {
+        if (p) {
+          key = f2key(v[q] / T);
+          p = key >= sig_key;
+        }
+        bal = __builtin_amdgcn_ballot_w64(p);
+      }
+      if (p) {
+        const int pos = n + lanes_below(bal);
+        if (pos < kSelCap) {
+          sk[pos] = key;
+          si[pos] = elem_index<E>(tile_base, q);
+        }
+      }
+      n += __popcll(bal);
+    }
+  }
+  return n;
+}
+
 // Writes a superset of the tile's top-k (2 <= k <= 64) of s = x / T (T > 0) to
-// out and returns its size, or -1 when more than kSelCap values qualify.
+// out and returns its size, or -1 when more than kSelCap values qualify. The
+// exact k-th largest key of the tile (0 when the tile holds fewer than k
+// values) goes to *kth: at least k values of the row reach it.
 template <typename E>
 __device__ __forceinline__ int tile_topk(const float (&v)[kVals], float lmax, int tile_base,
                                          int V, bool vec, int k, float T,
-                                         uint64_t* __restrict__ out) {
+                                         uint64_t* __restrict__ out, uint32_t* __restrict__ sk,
+                                         int32_t* __restrict__ si, uint32_t* kth) {
   uint32_t tau_key;
   if (k <= 32) {
     tau_key = wave_kth_largest(f2key(lmax), k);
@@ -103,47 +145,44 @@ __device__ __forceinline__ int tile_topk(const float (&v)[kVals], float lmax, in
     tau_key = wave_kth_largest2(f2key(lmax), f2key(b), k);
   }
   const float tau = key2f(tau_key);
-  const bool t1 = (T == 1.0f);
-  float pre = tau;             // prefilter on x
-  uint32_t sig_key = tau_key;  // exact filter on the key of s = x / T
-  if (!t1) {
-    sig_key = f2key(tau / T);
+  int n;
+  if (T == 1.0f) {
+    n = vec ? extract<E, true, true>(v, tile_base, V, tau, tau_key, T, sk, si)
+            : extract<E, false, true>(v, tile_base, V, tau, tau_key, T, sk, si);
+  } else {
+    const uint32_t sig_key = f2key(tau / T);
     // fl(x/T) >= fl(tau/T) implies x >= tau - 2^-22 |tau| - T 2^-149 (both
     // quotients round to the same float, so they differ by at most one ulp of
     // it); the bound used is looser still and rounded down.
     const double lb = static_cast<double>(tau) -
                       __builtin_ldexp(fabs(static_cast<double>(tau)), -21) -
                       static_cast<double>(T) * 0x1p-148;
-    pre = static_cast<float>(lb);
+    float pre = static_cast<float>(lb);
     if (static_cast<double>(pre) > lb) pre = nextafterf(pre, -kInf);
+    n = vec ? extract<E, true, false>(v, tile_base, V, pre, sig_key, T, sk, si)
+            : extract<E, false, false>(v, tile_base, V, pre, sig_key, T, sk, si);
   }
-  int n = 0;
-#pragma unroll
-  for (int q = 0; q < kVals; ++q) {
-    const int idx = elem_index<E>(tile_base, q);
-    bool pred = (v[q] >= pre) && (vec || idx < V);
-    uint64_t bal = __ballot(pred);
-    if (bal) {
-      uint32_t key = f2key(v[q]);
-      if (!t1) {
-        if (pred) {
-          key = f2key(v[q] / T);
-          pred = key >= sig_key;
-        }
-        bal = __ballot(pred);
-      }
-      if (pred) {
-        const int pos = n + lanes_below(bal);
-        if (pos < kSelCap) out[pos] = pack(key, idx);
-      }
-      n += __popcll(bal);
-    }
+  if (n > kSelCap) return -1;
+  wave_lds_wait();
+  // one coalesced write of the staged candidates, and the exact k-th key
+  const int l = lane();
+  const uint32_t ka = l < n ? sk[l] : 0u;
+  if (l < n) out[l] = pack(ka, si[l]);
+  if (n > kWave) {
+    const uint32_t kb = l + kWave < n ? sk[l + kWave] : 0u;
+    if (l + kWave < n) out[l + kWave] = pack(kb, si[l + kWave]);
+    *kth = wave_kth_largest2(ka, kb, k);
+  } else {
+    *kth = (n >= k) ? wave_kth_largest(ka, k) : 0u;
   }
-  return n > kSelCap ? -1 : n;
+  wave_lds_wait();
+  return n;
 }
 
 template <typename E>
 __global__ __launch_bounds__(256) void k_select(Job j) {
+  __shared__ uint32_t stage_key[kSelWaves][kSelCap];
+  __shared__ int32_t stage_id[kSelWaves][kSelCap];
   int row, wg;
   if (!xcd_row_tile(blockIdx.x, j.B, j.wpr, &row, &wg)) return;
   const int w = threadIdx.x / kWave;
@@ -155,8 +194,12 @@ __global__ __launch_bounds__(256) void k_select(Job j) {
   const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
   const int tile_base = tile * kSelTile;
   const bool vec = j.aligned && (tile_base + kSelTile <= j.V);
+  // Rows finished from this pass alone are read once: stream them past the
+  // caches. Rows whose logits are read again later keep the normal policy.
+  const bool stream = !j.out_full && j.sample &&
+                      (pl.c.mode == kModeGreedy || pl.c.mode == kModeKFast);
   float v[kVals];
-  load_tile<E>(rowp, tile_base, j.V, vec, v);
+  load_tile<E>(rowp, tile_base, j.V, vec, stream, v);
 
   float lmax = -kInf;
   bool bad = false;
@@ -183,23 +226,30 @@ __global__ __launch_bounds__(256) void k_select(Job j) {
   uint64_t* outA = j.candA + slot * kSelCap;
   if (pl.kA == 1) {
     const uint64_t best = tile_argmax<E>(v, M, tile_base, j.V, vec);
-    if (best) {
-      meta |= 1u;
-      if (l == 0) outA[0] = best;
+    if (best) meta |= 1u;
+    if (l == 0) {
+      if (best) outA[0] = best;
+      j.kthA[slot] = pkey(best);  // the tile maximum: its 1st-largest key
     }
   } else if (pl.kA > 1) {
-    const int n = tile_topk<E>(v, lmax, tile_base, j.V, vec, pl.kA, pl.TA, outA);
+    uint32_t kth = 0;
+    const int n = tile_topk<E>(v, lmax, tile_base, j.V, vec, pl.kA, pl.TA, outA, stage_key[w],
+                               stage_id[w], &kth);
     meta |= (n < 0) ? kMetaOverflowA : static_cast<uint32_t>(n);
+    if (l == 0) j.kthA[slot] = kth;
   }
   if (pl.kB > 1) {
+    uint32_t kth = 0;
     const int n = tile_topk<E>(v, lmax, tile_base, j.V, vec, pl.kB, 1.0f,
-                               j.candB + slot * kSelCap);
+                               j.candB + slot * kSelCap, stage_key[w], stage_id[w], &kth);
     meta |= (n < 0) ? kMetaOverflowB : (static_cast<uint32_t>(n) << kMetaCountBShift);
+    if (l == 0) j.kthB[slot] = kth;
   } else if (pl.kB == 1) {
     const uint64_t best = tile_argmax<E>(v, M, tile_base, j.V, vec);
-    if (best) {
-      meta |= 1u << kMetaCountBShift;
-      if (l == 0) j.candB[slot * kSelCap] = best;
+    if (best) meta |= 1u << kMetaCountBShift;
+    if (l == 0) {
+      if (best) j.candB[slot * kSelCap] = best;
+      j.kthB[slot] = pkey(best);
     }
   }
   if (l == 0) j.meta[slot] = meta;

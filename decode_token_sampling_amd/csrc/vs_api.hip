@@ -23,6 +23,10 @@ WsLayout ws_layout(int B, int V) {
   off = align_up(off + tiles * kSelCap * sizeof(uint64_t));
   L.candB = off;
   off = align_up(off + tiles * kSelCap * sizeof(uint64_t));
+  L.kthA = off;
+  off = align_up(off + tiles * sizeof(uint32_t));
+  L.kthB = off;
+  off = align_up(off + tiles * sizeof(uint32_t));
   L.desc = off;
   off = align_up(off + static_cast<size_t>(B) * sizeof(RowDesc));
   L.gpart = off;
@@ -52,6 +56,8 @@ Job make_job(const void* logits, vs_dtype dt, int B, int V, int64_t ld, void* ws
   j.meta = reinterpret_cast<uint32_t*>(w + L.meta);
   j.candA = reinterpret_cast<uint64_t*>(w + L.candA);
   j.candB = reinterpret_cast<uint64_t*>(w + L.candB);
+  j.kthA = reinterpret_cast<uint32_t*>(w + L.kthA);
+  j.kthB = reinterpret_cast<uint32_t*>(w + L.kthB);
   j.desc = reinterpret_cast<RowDesc*>(w + L.desc);
   j.gpart = reinterpret_cast<GPart*>(w + L.gpart);
   j.lpart = reinterpret_cast<LsePart*>(w + L.lpart);

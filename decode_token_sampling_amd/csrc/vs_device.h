@@ -82,6 +82,17 @@ __device__ __forceinline__ void unpack16(const uint4& u, float* x, const uint16_
   x[7] = __uint_as_float(u.w & 0xffff0000u);
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16(const void* p) {
+  const u32x4 t = *reinterpret_cast<const u32x4*>(p);
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+// Streaming read hint (non-temporal): data read once need not stay in L2.
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 // ---------------------------------------------------------------- pinned exp
 // exp(t) rounded once to fp32 for t >= -87, 0 below. Evaluated in double:
 // Cody & Waite range reduction t = n*ln2 + r with ln2 split into a high part
@@ -245,6 +256,15 @@ __device__ __forceinline__ int lanes_below(uint64_t ballot) {
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   __builtin_amdgcn_wave_barrier();
+}
+// Cross-lane exchange through LDS inside one wave: wait for this wave's LDS
+// operations only (lgkmcnt(0); vector-memory and export counters left at their
+// maxima, gfx9 encoding) and keep the compiler from moving memory operations
+// across. Outstanding global stores are not waited for.
+__device__ __forceinline__ void wave_lds_wait() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_wave_barrier();
+  __asm__ volatile("" ::: "memory");
 }
 
 // DPP lane movement within rows of 16 lanes (gfx9 encodings): quad_perm,

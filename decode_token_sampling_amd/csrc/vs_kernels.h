@@ -67,6 +67,8 @@ struct Job {
   uint32_t* meta;
   uint64_t* candA;
   uint64_t* candB;
+  uint32_t* kthA;   // per tile: exact k-th key of list A's candidates (0: fewer than k)
+  uint32_t* kthB;
   LsePart* lpart;
   float2* rlse;
   RowDesc* desc;
@@ -104,7 +106,7 @@ __device__ __forceinline__ Plan plan_row(const Job& j, int row) {
 
 struct WsLayout {
   int ntile, wpr, ntile3;
-  size_t meta, candA, candB, desc, gpart, lpart, rlse, total;
+  size_t meta, candA, candB, kthA, kthB, desc, gpart, lpart, rlse, total;
 };
 WsLayout ws_layout(int B, int V);
 
