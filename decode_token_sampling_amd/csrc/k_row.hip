@@ -27,7 +27,7 @@ constexpr int kLightThreads = 256;
 constexpr int kFullThreads = 1024;
 constexpr int kBuckets = 4096;
 constexpr float kBucketsPerUnit = 128.0f;
-constexpr int kMaxTiles = (VS_MAX_V + kSelTile - 1) / kSelTile;
+constexpr int kMaxSegs = (VS_MAX_V + kSegMin - 1) / kSegMin;
 
 template <int kBuf, int kBins>
 struct RowSh {
@@ -44,7 +44,7 @@ struct RowSh {
   uint32_t flags;
   uint64_t b64[4];
   int32_t b32[4];
-  int32_t toff[kMaxTiles + 1];  // per-tile offsets of a candidate union
+  int32_t toff[kMaxSegs + 1];  // per-segment offsets of a candidate union
 };
 using LightSh = RowSh<4096, 2048>;
 using FullSh = RowSh<8192, kBuckets>;
@@ -516,7 +516,7 @@ __global__ __launch_bounds__(kLightThreads) void k_row_light(Job j) {
   const int row = blockIdx.x;
   const Plan pl = plan_row(j, row);
   const RowCfg& c = pl.c;
-  const int ntile = j.ntile;
+  const int ntile = j.nseg;  // candidate lists and partials come per segment
   const uint32_t* mrow = j.meta + static_cast<size_t>(row) * ntile;
   const uint64_t* crowA = j.candA + static_cast<size_t>(row) * ntile * kSelCap;
   const uint64_t* crowB = j.candB + static_cast<size_t>(row) * ntile * kSelCap;

@@ -8,14 +8,29 @@ namespace vsk {
 
 namespace {
 size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  constexpr int kMaxDev = 64;
+  static int cache[kMaxDev] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
+  int n = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    __atomic_store_n(&cache[dev], n, __ATOMIC_RELAXED);
+  }
+  return n;
+}
 }  // namespace
 
 WsLayout ws_layout(int B, int V) {
   WsLayout L{};
   L.ntile = (V + kSelTile - 1) / kSelTile;
-  L.wpr = (L.ntile + kSelWaves - 1) / kSelWaves;
+  const int nslot = (V + kSegMin - 1) / kSegMin;  // segment slots per row
   L.ntile3 = (V + kGumTile - 1) / kGumTile;
-  const size_t tiles = static_cast<size_t>(B) * L.ntile;
+  const size_t tiles = static_cast<size_t>(B) * nslot;
   size_t off = 0;
   L.meta = off;
   off = align_up(off + tiles * sizeof(uint32_t));
@@ -51,8 +66,16 @@ Job make_job(const void* logits, vs_dtype dt, int B, int V, int64_t ld, void* ws
   const int64_t es = (dt == VS_F32) ? 4 : 2;
   j.aligned = (reinterpret_cast<uintptr_t>(logits) % 16 == 0) && ((ld * es) % 16 == 0);
   j.ntile = L.ntile;
-  j.wpr = L.wpr;
   j.ntile3 = L.ntile3;
+  // Streaming-pass geometry: enough segments per row that the batch gives
+  // every compute unit a workgroup, each segment read by up to 16 waves.
+  const int cus = device_cus();
+  const int nslot = (V + kSegMin - 1) / kSegMin;
+  int S = (cus + B - 1) / B;
+  S = S < 1 ? 1 : (S > nslot ? nslot : S);
+  j.tps = (L.ntile + S - 1) / S;
+  j.nseg = (L.ntile + j.tps - 1) / j.tps;
+  j.nwave = j.tps < kSelMaxWaves ? j.tps : kSelMaxWaves;
   j.meta = reinterpret_cast<uint32_t*>(w + L.meta);
   j.candA = reinterpret_cast<uint64_t*>(w + L.candA);
   j.candB = reinterpret_cast<uint64_t*>(w + L.candB);

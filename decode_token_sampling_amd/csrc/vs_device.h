@@ -332,6 +332,35 @@ __device__ __forceinline__ uint32_t wave_kth_largest(uint32_t key, int k) {
   return prefix;
 }
 // Same over two uint32 per lane (k <= 128).
+// The k-th largest of the 64 * N keys held N per lane (1 <= k <= 64 * N),
+// MSB-first with one ballot per key slot and bit.
+template <int N>
+__device__ __forceinline__ uint32_t wave_kth_largest_n(const uint32_t (&key)[N], int k) {
+  uint64_t cand[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) cand[i] = ~0ull;
+  uint32_t prefix = 0;
+#pragma unroll
+  for (int b = 31; b >= 0; --b) {
+    uint64_t ones[N];
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      ones[i] = __ballot((key[i] >> b) & 1u) & cand[i];
+      c += __popcll(ones[i]);
+    }
+    if (c >= k) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) cand[i] = ones[i];
+      prefix |= 1u << b;
+    } else {
+      k -= c;
+#pragma unroll
+      for (int i = 0; i < N; ++i) cand[i] &= ~ones[i];
+    }
+  }
+  return prefix;
+}
 __device__ __forceinline__ uint32_t wave_kth_largest2(uint32_t ka, uint32_t kb, int k) {
   uint64_t ca = ~0ull, cb = ~0ull;
   uint32_t prefix = 0;

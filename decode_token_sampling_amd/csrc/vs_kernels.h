@@ -10,13 +10,15 @@
 
 namespace vsk {
 
-constexpr int kSelTile = 4096;    // one wave's tile in the streaming pass
-constexpr int kSelWaves = 4;      // tiles per 256-thread workgroup
-constexpr int kSelCap = 128;      // candidate slots per tile and list
+constexpr int kSelTile = 2048;    // one wave's tile in the streaming pass
+constexpr int kSegMin = 4096;     // values per segment, at least (bounds the segment count)
+constexpr int kSelMaxWaves = 16;  // waves per streaming-pass workgroup, at most
+constexpr int kSelCap = 128;      // candidate slots per segment and list
 constexpr int kGumTile = 4096;    // Gumbel tile: 256 threads x 16 values
 constexpr int kFullTile = 4096;   // full log-softmax write tile
 
-// Tile meta word.
+// Segment meta word (a segment is the run of tiles of one row that one
+// streaming-pass workgroup reads).
 constexpr uint32_t kMetaCountA = 0xffu;
 constexpr int kMetaCountBShift = 8;
 constexpr uint32_t kMetaBadLogits = 1u << 16;
@@ -62,12 +64,16 @@ struct Job {
   float* out_full;
   int64_t ld_out;
   int32_t* out_lp_status;  // vs_logprobs status
-  // workspace
-  int ntile, wpr, ntile3;
+  // workspace; streaming-pass geometry
+  int ntile;  // tiles per row
+  int nseg;   // segments per row (<= ceil(V / kSegMin), the workspace's slots per row)
+  int tps;    // tiles per segment
+  int nwave;  // waves per streaming-pass workgroup
+  int ntile3;
   uint32_t* meta;
   uint64_t* candA;
   uint64_t* candB;
-  uint32_t* kthA;   // per tile: exact k-th key of list A's candidates (0: fewer than k)
+  uint32_t* kthA;   // per segment: exact k-th key of list A's candidates (0: fewer than k)
   uint32_t* kthB;
   LsePart* lpart;
   float2* rlse;
@@ -105,7 +111,7 @@ __device__ __forceinline__ Plan plan_row(const Job& j, int row) {
 }
 
 struct WsLayout {
-  int ntile, wpr, ntile3;
+  int ntile, ntile3;
   size_t meta, candA, candB, kthA, kthB, desc, gpart, lpart, rlse, total;
 };
 WsLayout ws_layout(int B, int V);
