@@ -468,43 +468,6 @@ __device__ int block_draw(const uint64_t* L, int n, const RowCfg& c, int row, in
   return 0;
 }
 
-// The same over n <= 64 sorted candidates with one wave (no block barrier);
-// call from every lane of one wave.
-__device__ int wave_draw(const uint64_t* L, int n, const RowCfg& c, int row, int32_t* id_out,
-                         int32_t* kept_out, uint32_t* mask_row) {
-  const int i = lane();
-  if (n <= 0) return VS_ROW_BAD_LOGITS;  // no candidate: never read an id from it
-  const uint64_t top = L[0];
-  if (pkey(top) == kKeyPosInf) return VS_ROW_BAD_PARAM;
-  const float m = key2f(pkey(top));
-  const bool has = i < n;
-  const uint64_t P = has ? L[i] : 0ull;
-  const float e = has ? pinned_exp(key2f(pkey(P)) - m) : 0.0f;
-  const bool in_s = has && (e >= c.mp);
-  bool kept = in_s;
-  if (c.p < 1.0f) {
-    uint64_t cum = in_s ? mass_of(e) : 0ull;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const uint64_t w = __shfl_up(cum, o);
-      if (i >= o) cum += w;
-    }
-    const uint64_t tw = __shfl(cum, kWave - 1);
-    const double thr = static_cast<double>(c.p) * static_cast<double>(tw);
-    const uint64_t hit = __ballot(in_s && static_cast<double>(cum) >= thr);
-    const int cut = hit ? __ffsll(static_cast<unsigned long long>(hit)) - 1 : kWave;
-    kept = in_s && i <= cut;
-  }
-  const int id = has ? pid(P) : 0x7fffffff;
-  const double sc = kept ? gumbel_score(e, row_stream(c.seed, row), id) : -1.0;
-  const double best = wave_max(sc);
-  const int win = wave_min((kept && sc == best) ? id : 0x7fffffff);
-  if (kept && mask_row) atomicOr(&mask_row[id >> 5], 1u << (id & 31));
-  *id_out = win;
-  *kept_out = __popcll(__ballot(kept));
-  return 0;
-}
-
 template <typename E>
 __device__ __forceinline__ float logit_at(const Job& j, int row, int id) {
   return to_f32(static_cast<const E*>(j.logits)[static_cast<int64_t>(row) * j.ld + id]);
@@ -514,6 +477,7 @@ template <typename E>
 __global__ __launch_bounds__(kLightThreads) void k_row_light(Job j) {
   __shared__ LightSh sh;
   const int row = blockIdx.x;
+  if (j.nseg == 1 && (j.meta[row] & kMetaFinal)) return;  // finished by the streaming pass
   const Plan pl = plan_row(j, row);
   const RowCfg& c = pl.c;
   const int ntile = j.nseg;  // candidate lists and partials come per segment

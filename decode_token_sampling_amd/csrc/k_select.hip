@@ -30,14 +30,17 @@ namespace vsk {
 namespace {
 
 constexpr int kVals = kSelTile / kWave;  // values per lane and tile (32)
-constexpr int kGroup = 8;         // values per group (a lane's maxima are kept per group)
+constexpr int kGroup = 4;         // values per group (a lane's maxima are kept per group)
 constexpr int kGroups = kVals / kGroup;
+static_assert(kGroup == 4 && kGroups == 8, "the group switch in extract() is written for 8 x 4");
 
-constexpr int kPoolN = 3;         // pool slots per lane
-constexpr int kPool = kWave * kPoolN;
-constexpr int kCompactAt = 96;    // compact a pool once it holds more than this
-constexpr int kMergeCap = 1024;   // merged candidates per segment and list
+constexpr int kPoolCap = 512;     // candidates per segment and list (the shared pool)
+constexpr int kCheck = 64;        // the pool's bound is recomputed every kCheck entries
+static_assert(kPoolCap % 16 == 0, "rank_counts reads the pool in batches of up to 16");
 constexpr float kL2E = 1.44269504088896340736f;
+// s_waitcnt operand for "vector memory count 0", other counters left at their
+// maxima (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 template <typename E>
 __device__ __forceinline__ int elem_index(int tile_base, int q) {
@@ -53,16 +56,18 @@ struct Raw {
 
 // kStream: non-temporal loads (a compile-time choice, so that the hint cannot
 // be merged away with the ordinary load of the same address).
-// The 16-byte loads of the tile at base; stride 0 makes every load read the
-// 16 bytes at base (a placeholder load that keeps the load count fixed).
+// The 16-byte loads of the tile at base; stride 0 makes each load read 16
+// bytes of the first tile in every lane (a placeholder load that keeps the
+// load count fixed).
 template <typename E, bool kStream>
 __device__ __forceinline__ void load_raw(const E* __restrict__ base, int stride, Raw<E>& raw) {
   constexpr int EPV = Epv<E>::n;
-  const int l = lane();
+  // one lane address, the loads at fixed offsets from it (a placeholder reads
+  // the same 16 bytes in every lane, at each load's offset)
+  const E* p = base + lane() * EPV * stride;
 #pragma unroll
   for (int i = 0; i < Raw<E>::n; ++i) {
-    const E* p = base + (i * kWave + l) * EPV * stride;
-    raw.r[i] = kStream ? load16_stream(p) : load16(p);
+    raw.r[i] = kStream ? load16_stream(p + i * kWave * EPV) : load16(p + i * kWave * EPV);
   }
 }
 
@@ -111,49 +116,6 @@ __device__ __forceinline__ uint64_t tile_argmax(const float (&v)[kVals], float M
   return 0ull;
 }
 
-// Appends to the pool (keys sk, ids si, room free slots) every value of the
-// tile that reaches the threshold: v >= pre, and for T != 1 also
-// key(v / T) >= thr. g holds each lane's maxima of its 8 groups of 8 values;
-// a group no lane's maximum of which reaches pre is skipped whole. Returns the
-// count (only the first `room` are stored).
-template <typename E, bool kVec, bool kT1>
-__device__ __forceinline__ int extract(const float (&v)[kVals], const float (&g)[kGroups],
-                                       int tile_base, int V, float pre, uint32_t thr, float T,
-                                       uint32_t* __restrict__ sk, int32_t* __restrict__ si,
-                                       int room) {
-  int n = 0;
-#pragma unroll
-  for (int gi = 0; gi < kGroups; ++gi) {
-    if (__builtin_amdgcn_ballot_w64(g[gi] >= pre) == 0ull) continue;  // uniform
-#pragma unroll
-    for (int u = 0; u < kGroup; ++u) {
-      const int q = gi * kGroup + u;
-      bool p = v[q] >= pre;
-      if (!kVec) p = p && elem_index<E>(tile_base, q) < V;
-      uint64_t bal = __builtin_amdgcn_ballot_w64(p);
-      if (bal) {  // uniform: taken only when some lane has a candidate here
-        uint32_t key = f2key(v[q]);
-        if (!kT1) {
-          if (p) {
-            key = f2key(v[q] / T);
-            p = key >= thr;
-          }
-          bal = __builtin_amdgcn_ballot_w64(p);
-        }
-        if (p) {
-          const int pos = n + lanes_below(bal);
-          if (pos < room) {
-            sk[pos] = key;
-            si[pos] = elem_index<E>(tile_base, q);
-          }
-        }
-        n += __popcll(bal);
-      }
-    }
-  }
-  return n;
-}
-
 // The smallest float pre such that key(fl(x / T)) >= thr implies x >= pre:
 // fl(x / T) >= s forces x / T >= pred(s), so x >= T * pred(s) (exact in
 // double), rounded down to float.
@@ -170,13 +132,10 @@ __device__ __forceinline__ float prefilter(uint32_t thr, float T) {
 // k > 32), as a key of s = x / T: at least k values of the tile reach it.
 __device__ __forceinline__ uint32_t tile_bound(const float (&v)[kVals], float lmax, int k,
                                                float T) {
-  uint32_t tk;
-  if (k <= 32) {
-    tk = wave_kth_largest(f2key(lmax), k);
-  } else {
+  float b = -kInf;
+  if (k > 32) {
     // the lane's second largest value: the largest value below the lane
     // maximum, or the maximum itself when it occurs twice
-    float b = -kInf;
     int nmax = 0;
 #pragma unroll
     for (int q = 0; q < kVals; ++q) {
@@ -184,161 +143,291 @@ __device__ __forceinline__ uint32_t tile_bound(const float (&v)[kVals], float lm
       nmax += (v[q] == lmax) ? 1 : 0;
     }
     if (nmax > 1) b = lmax;
-    tk = wave_kth_largest2(f2key(lmax), f2key(b), k);
   }
+  const uint32_t tk = (k <= 32) ? wave_kth_largest(f2key(lmax), k)
+                                : wave_kth_largest2(f2key(lmax), f2key(b), k);
   return (T == 1.0f) ? tk : f2key(key2f(tk) / T);
 }
 
-// One wave's candidate pool for one list.
-struct Pool {
-  uint32_t* key;  // kPool slots in LDS; slot i lives with lane i % 64
-  int32_t* id;
-  uint32_t* shared_thr;  // the workgroup's bound (LDS, only grows)
-  int k;
-  float T;
-  int n;         // entries held
-  uint32_t thr;  // this wave's bound: a lower bound on the segment's k-th key
-  bool ovf;
-};
+// The values of the tile that reach a list's threshold: v >= pre (pre =
+// prefilter(thr, T)), and for T != 1 also key(v / T) >= thr. g holds each
+// lane's maxima of its groups of 4 values; only groups whose maximum reaches
+// pre in some lane are visited, by a loop over them that copies the group's
+// values out with a uniform switch (so the code for one value exists 4 times,
+// not 32). kWrite = false counts them; kWrite = true writes them, packed, to
+// out[0..count) (the count pass gives the space).
+template <typename E, bool kWrite>
+__device__ __forceinline__ int extract(const float (&v)[kVals], const float (&g)[kGroups],
+                                       uint32_t active, int tile_base, int V, bool vec,
+                                       uint32_t thr, float pre, float T,
+                                       uint64_t* __restrict__ out) {
+  constexpr int EPV = Epv<E>::n;
+  const bool t1 = T == 1.0f;
+  const int l = lane();
+  int n = 0;
+  while (active) {  // uniform
+    const int gi = __builtin_ctz(active);
+    active &= active - 1u;
+    float x[kGroup];
+    switch (gi) {
+#define VS_GROUP_CASE(G)                                          \
+  case G:                                                         \
+    x[0] = v[G * kGroup + 0];                                     \
+    x[1] = v[G * kGroup + 1];                                     \
+    x[2] = v[G * kGroup + 2];                                     \
+    x[3] = v[G * kGroup + 3];                                     \
+    break;
+      VS_GROUP_CASE(0)
+      VS_GROUP_CASE(1)
+      VS_GROUP_CASE(2)
+      VS_GROUP_CASE(3)
+      VS_GROUP_CASE(4)
+      VS_GROUP_CASE(5)
+      VS_GROUP_CASE(6)
+      default:
+        x[0] = v[7 * kGroup + 0];
+        x[1] = v[7 * kGroup + 1];
+        x[2] = v[7 * kGroup + 2];
+        x[3] = v[7 * kGroup + 3];
+        break;
+#undef VS_GROUP_CASE
+    }
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) {
+      // value q = gi * 4 + u of the lane: vector q / EPV, component q % EPV
+      const int q = gi * kGroup + u;
+      const int id = tile_base + ((q / EPV) * kWave + l) * EPV + (q % EPV);
+      bool p = x[u] >= pre && (vec || id < V);
+      uint64_t bal = __builtin_amdgcn_ballot_w64(p);
+      if (bal) {  // uniform: taken only when some lane has a candidate here
+        uint32_t key = f2key(x[u]);
+        if (!t1) {
+          if (p) {
+            key = f2key(x[u] / T);
+            p = key >= thr;
+          }
+          bal = __builtin_amdgcn_ballot_w64(p);
+        }
+        if (kWrite && p) out[n + lanes_below(bal)] = pack(key, id);
+        n += __popcll(bal);
+      }
+    }
+  }
+  return n;
+}
 
 __device__ __forceinline__ uint32_t lds_load_relaxed(uint32_t* p) {
   return __builtin_amdgcn_readfirstlane(
       __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
 }
 
-// Drops the pool entries below max(floor, exact k-th largest pool key).
-__device__ __forceinline__ void pool_compact(Pool& P, uint32_t floor) {
+// Adds to r[i] the number of the first n pool entries larger than e[i]. The
+// pool is read kBatch entries at a time, all lanes reading the same words, so
+// that the reads overlap instead of each waiting on the one before; entries
+// from n on count as 0. n <= kPoolCap, a multiple of kBatch.
+template <int R, int kBatch>
+__device__ __forceinline__ void rank_counts(const uint64_t* pool, int n, const uint64_t (&e)[R],
+                                            int (&r)[R]) {
+  for (int m0 = 0; m0 < n; m0 += kBatch) {  // uniform
+    uint64_t o[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) o[u] = pool[m0 + u];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const uint64_t x = (m0 + u < n) ? o[u] : 0ull;
+#pragma unroll
+      for (int i = 0; i < R; ++i) r[i] += (x > e[i]) ? 1 : 0;
+    }
+  }
+}
+
+// The k-th largest key among the n packed entries of an LDS pool, with one
+// wave: each entry's rank is the number of larger entries, and the entry of
+// rank k - 1 holds the key. Entries still being written read as 0 (below every
+// value), which can only lower the result: it stays a valid bound. 0 when the
+// pool has fewer than k entries.
+__device__ __forceinline__ uint32_t pool_kth(const uint64_t* pool, int n, int k) {
+  constexpr int R = 2;  // entries per lane and pass (the passes cover 128 entries each)
   const int l = lane();
-  uint32_t k3[kPoolN];
-  int32_t i3[kPoolN];
+  uint32_t best = 0u;
+  for (int c0 = 0; c0 < n; c0 += R * kWave) {  // uniform
+    uint64_t e[R];
+    int r[R];
 #pragma unroll
-  for (int s = 0; s < kPoolN; ++s) {
-    const int slot = s * kWave + l;
-    k3[s] = slot < P.n ? P.key[slot] : 0u;
-    i3[s] = slot < P.n ? P.id[slot] : 0;
-  }
-  uint32_t cut = floor;
-  if (P.n >= P.k) {
-    const uint32_t kth = wave_kth_largest_n<kPoolN>(k3, P.k);
-    cut = kth > cut ? kth : cut;
-  }
-  wave_lds_wait();
-  int base = 0;
+    for (int i = 0; i < R; ++i) {
+      const int at = c0 + i * kWave + l;
+      e[i] = at < n ? pool[at] : 0ull;
+      r[i] = 0;
+    }
+    rank_counts<R, 8>(pool, n, e, r);
 #pragma unroll
-  for (int s = 0; s < kPoolN; ++s) {
-    const bool keep = (s * kWave + l) < P.n && k3[s] >= cut;
-    const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
-    if (keep) {
-      const int pos = base + lanes_below(bal);
-      P.key[pos] = k3[s];
-      P.id[pos] = i3[s];
-    }
-    base += __popcll(bal);
+    for (int i = 0; i < R; ++i)
+      if (r[i] == k - 1 && e[i] != 0ull) best = pkey(e[i]);
   }
-  P.n = base;
-  P.thr = cut > P.thr ? cut : P.thr;
-  wave_lds_wait();
+  return wave_max_u32_dpp(best);
 }
 
-template <typename E, bool kVec>
-__device__ __forceinline__ int extract_any(const float (&v)[kVals], const float (&g)[kGroups],
-                                           float lmax, int tile_base, int V, uint32_t thr,
-                                           const Pool& P) {
-  const float pre = prefilter(thr, P.T);
-  if (__builtin_amdgcn_ballot_w64(lmax >= pre) == 0ull) return 0;  // nothing in the tile
-  if (P.T == 1.0f)
-    return extract<E, kVec, true>(v, g, tile_base, V, pre, thr, P.T, P.key + P.n, P.id + P.n,
-                                  kPool - P.n);
-  return extract<E, kVec, false>(v, g, tile_base, V, pre, thr, P.T, P.key + P.n, P.id + P.n,
-                                 kPool - P.n);
-}
-
-// Adds one tile to the pool.
-template <typename E>
-__device__ __forceinline__ void pool_tile(const float (&v)[kVals], const float (&g)[kGroups],
-                                          float lmax, int tile_base, int V, bool vec, Pool& P) {
-  if (P.ovf) return;
-  const uint32_t sh = lds_load_relaxed(P.shared_thr);
-  uint32_t thr = P.thr > sh ? P.thr : sh;
-  bool publish = false;
-  if (thr == 0u) {  // no bound yet
-    thr = tile_bound(v, lmax, P.k, P.T);
-    publish = true;
-  }
-  int n = vec ? extract_any<E, true>(v, g, lmax, tile_base, V, thr, P)
-              : extract_any<E, false>(v, g, lmax, tile_base, V, thr, P);
-  if (P.n + n > kPool) {
-    // Too many: raise the bound with this tile's own and the pool's k-th.
-    uint32_t t2 = publish ? thr : tile_bound(v, lmax, P.k, P.T);
-    t2 = t2 > thr ? t2 : thr;
-    pool_compact(P, t2);
-    t2 = P.thr > t2 ? P.thr : t2;
-    n = vec ? extract_any<E, true>(v, g, lmax, tile_base, V, t2, P)
-            : extract_any<E, false>(v, g, lmax, tile_base, V, t2, P);
-    if (P.n + n > kPool) {
-      P.ovf = true;
-      return;
-    }
-    thr = t2;
-    publish = true;
-  }
-  P.n += n;
-  P.thr = thr > P.thr ? thr : P.thr;
-  if (P.n > kCompactAt && P.n >= P.k) {
-    pool_compact(P, P.thr);
-    publish = true;
-  }
-  if (publish && lane() == 0) atomicMax(P.shared_thr, P.thr);
-}
-
-// Workgroup LDS, laid out at run time for W waves.
-struct Layout {
-  static constexpr int kPoolBytes = kPool * 8;  // keys and ids
-  int W;
-  __device__ __forceinline__ uint32_t* pool_key(char* base, int w, int list) const {
-    return reinterpret_cast<uint32_t*>(base + (w * 2 + list) * kPoolBytes);
-  }
-  __device__ __forceinline__ int32_t* pool_id(char* base, int w, int list) const {
-    return reinterpret_cast<int32_t*>(base + (w * 2 + list) * kPoolBytes + kPool * 4);
-  }
-  __device__ __forceinline__ uint64_t* merge(char* base) const {
-    return reinterpret_cast<uint64_t*>(base + W * 2 * kPoolBytes);
+// A wave's view of one top-k list.
+struct List {
+  int li;        // 0: list A, 1: list B
+  int k;
+  float T;
+  uint32_t thr;  // the bound this wave uses (a lower bound on the segment's k-th key)
+  float pre;     // prefilter(thr, T): values of x below it cannot reach thr
+  __device__ __forceinline__ void set_thr(uint32_t t) {
+    thr = t;
+    pre = prefilter(t, T);
   }
 };
 
+
 struct SegSh {
+  uint64_t pool[2][kPoolCap];  // each list's candidates (packed), appended by all waves
+  int next_tile;  // the segment's next unclaimed tile (claimed by whole waves)
   uint32_t thr[2];
-  int merge_n;
+  int merge_n[2];
   int ovf[2];
+  uint32_t kth_key[2];
   uint32_t flags;
   uint32_t hist[256];
   uint32_t prefix;
   int krem;
-  int out_n;
+  int out_n[2];
   float wm[16];
   float ws[16];
   uint64_t best[2][16];
+  uint64_t top[2][kSelCap];  // each list's segment candidates
+  uint64_t srt[2][kWave];    // a list's 64 best, sorted (finishing a row)
+  float segM, segS;          // the segment's log-sum-exp partial
+  uint64_t seg_best[2];      // the segment's argmax for argmax lists
 };
 
-__host__ __device__ inline size_t dyn_lds_bytes(int W) {
-  return static_cast<size_t>(W) * 2 * Layout::kPoolBytes + kMergeCap * sizeof(uint64_t);
+
+// Finishes list `li`: writes the segment's candidates (every value whose key
+// reaches the segment's exact k-th largest key) and that key, and leaves the
+// 64 best sorted in sh.srt. Each pool entry's rank (the number of larger
+// entries; packed values are distinct) is counted against all the others,
+// every thread reading the same LDS word at a time: the rank is the sorted
+// position, and the entry of rank k - 1 holds the k-th key. Returns the count,
+// or -1 on overflow. Called by the whole block after the streaming loop.
+__device__ int merge_list(SegSh& sh, int li, int k, uint64_t* __restrict__ out,
+                          uint32_t* kth_out) {
+  uint64_t* keep = sh.top[li];
+  const uint64_t* pool = sh.pool[li];
+  const int l = lane();
+  const int n = sh.merge_n[li];
+  if (sh.ovf[li] || n > kPoolCap) return -1;
+  for (int i0 = 0; i0 < n; i0 += blockDim.x) {
+    if (i0 + static_cast<int>(threadIdx.x / kWave) * kWave < n) {  // waves with an entry
+      const int i = i0 + static_cast<int>(threadIdx.x);
+      const uint64_t e[1] = {i < n ? pool[i] : 0ull};
+      int r[1] = {0};
+      rank_counts<1, 16>(pool, n, e, r);
+      if (i < n && r[0] < kWave) sh.srt[li][r[0]] = e[0];
+      if (i < n && r[0] == k - 1) sh.kth_key[li] = pkey(e[0]);
+    }
+  }
+  __syncthreads();
+  const uint32_t kth = (n >= k) ? sh.kth_key[li] : 0u;
+  // every entry reaching kth goes out (order is irrelevant to the reader)
+  for (int i0 = 0; i0 < n; i0 += blockDim.x) {
+    const int i = i0 + static_cast<int>(threadIdx.x);
+    const uint64_t e = i < n ? pool[i] : 0ull;
+    const bool take = i < n && pkey(e) >= kth;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(take);
+    int b0 = 0;
+    if (l == 0 && bal) b0 = atomicAdd(&sh.out_n[li], __popcll(bal));
+    b0 = __shfl(b0, 0);
+    if (take) {
+      const int pos = b0 + lanes_below(bal);
+      if (pos < kSelCap) {
+        out[pos] = e;
+        keep[pos] = e;
+      }
+    }
+  }
+  __syncthreads();
+  const int c = sh.out_n[li];
+  if (threadIdx.x == 0) *kth_out = kth;
+  return c > kSelCap ? -1 : c;
 }
 
-// Exact k-th largest key of n (<= kMergeCap) packed entries, with the whole
-// block: four 8-bit digit passes over LDS histograms.
-__device__ uint32_t block_kth_key(const uint64_t* a, int n, int k, SegSh& sh) {
+// Per-lane maxima of the 4-value groups and of the lane, NaN-propagating: a
+// lane maximum is NaN or +inf exactly when the lane holds a NaN or a +inf,
+// which make the row invalid.
+__device__ __forceinline__ void tile_maxima(const float (&v)[kVals], float (&g)[kGroups],
+                                            float& lmax) {
+#pragma unroll
+  for (int gi = 0; gi < kGroups; ++gi) {
+    float m = v[gi * kGroup];
+#pragma unroll
+    for (int u = 1; u < kGroup; ++u) m = __builtin_elementwise_maximum(m, v[gi * kGroup + u]);
+    g[gi] = m;
+  }
+  lmax = g[0];
+#pragma unroll
+  for (int gi = 1; gi < kGroups; ++gi) lmax = __builtin_elementwise_maximum(lmax, g[gi]);
+}
+
+// Adds one tile's candidates to the list's shared pool (in LDS). The count
+// pass reserves space with one atomic add; the write pass fills it. Each time
+// the pool grows past a multiple of kCheck entries, the wave that crossed it
+// recomputes the exact k-th largest key of the pool and raises the shared
+// bound: the pool holds every value seen so far that reached the bound in
+// force, so that key is the running k-th largest value of the segment.
+template <typename E>
+__device__ __forceinline__ void list_tile(const float (&v)[kVals], const float (&g)[kGroups],
+                                          float lmax, int tile_base, int V, bool vec, List& L,
+                                          SegSh& sh, uint64_t* pool) {
+  // no value of the tile reaches this wave's bound: nothing to do (no LDS)
+  if (L.thr != 0u && __builtin_amdgcn_ballot_w64(lmax >= L.pre) == 0ull) return;
+  const uint32_t shv = lds_load_relaxed(&sh.thr[L.li]);
+  if (shv > L.thr) {  // another wave raised the bound
+    L.set_thr(shv);
+    if (__builtin_amdgcn_ballot_w64(lmax >= L.pre) == 0ull) return;
+  }
+  if (L.thr == 0u) {  // no bound yet: this tile's own k-th lane maximum
+    L.set_thr(tile_bound(v, lmax, L.k, L.T));
+    if (lane() == 0) atomicMax(&sh.thr[L.li], L.thr);
+  }
+  uint32_t active = 0;
+#pragma unroll
+  for (int gi = 0; gi < kGroups; ++gi)
+    if (__builtin_amdgcn_ballot_w64(g[gi] >= L.pre) != 0ull) active |= 1u << gi;
+  if (!active) return;
+  const int n = extract<E, false>(v, g, active, tile_base, V, vec, L.thr, L.pre, L.T, nullptr);
+  if (n == 0) return;
+  int base = 0;
+  if (lane() == 0) base = atomicAdd(&sh.merge_n[L.li], n);
+  base = __shfl(base, 0);
+  if (base + n > kPoolCap) {  // the pool is full: the row is selected the slow way
+    if (lane() == 0) sh.ovf[L.li] = 1;
+    return;
+  }
+  extract<E, true>(v, g, active, tile_base, V, vec, L.thr, L.pre, L.T, pool + base);
+  if ((base + n) / kCheck > base / kCheck) {
+    const uint32_t nb = pool_kth(pool, base + n, L.k);
+    if (nb > L.thr) {
+      L.set_thr(nb);
+      if (lane() == 0) atomicMax(&sh.thr[L.li], nb);
+    }
+  }
+}
+
+// A lower bound on the k-th largest of the block's keys, one per thread
+// (1 <= k <= blockDim): the top 16 bits of that key, found by two 8-bit digit
+// passes over an LDS histogram (at least k keys reach the result). Called by
+// the whole block.
+__device__ uint32_t block_kth_u32(uint32_t key, int k, SegSh& sh) {
   uint32_t prefix = 0;
-  for (int d = 3; d >= 0; --d) {
+  for (int d = 3; d >= 2; --d) {
+    __syncthreads();  // the previous pass's readers are done with sh
     for (int i = threadIdx.x; i < 256; i += blockDim.x) sh.hist[i] = 0u;
     __syncthreads();
     const uint32_t hmask = (d == 3) ? 0u : (0xffffffffu << (8 * (d + 1)));
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-      const uint32_t key = pkey(a[i]);
-      if ((key & hmask) == prefix) atomicAdd(&sh.hist[(key >> (8 * d)) & 0xffu], 1u);
-    }
+    if ((key & hmask) == prefix) atomicAdd(&sh.hist[(key >> (8 * d)) & 0xffu], 1u);
     __syncthreads();
     if (threadIdx.x < kWave) {
-      // bins scanned from the top: lane l owns bins 255-4l .. 252-4l
       uint32_t c[4];
       uint32_t lsum = 0;
 #pragma unroll
@@ -373,116 +462,150 @@ __device__ uint32_t block_kth_key(const uint64_t* a, int n, int k, SegSh& sh) {
     __syncthreads();
     prefix = sh.prefix;
     k = sh.krem;
-    __syncthreads();
   }
+  __syncthreads();
   return prefix;
 }
 
-// Merges list `li` of the W pools: writes the segment's candidates (every
-// value whose key reaches the segment's exact k-th largest key) and that key.
-// Returns the count, or -1 on overflow. Called by the whole block.
-__device__ int merge_list(char* dyn, const Layout& lay, SegSh& sh, int li, int k,
-                          const uint32_t* pkey_, const int32_t* pid_, int pn, bool povf,
-                          uint64_t* __restrict__ out, uint32_t* kth_out) {
-  const int w = threadIdx.x / kWave;
+// Finishes a row from its segment results with one wave: the same outputs the
+// row kernel writes (draw, kept count, status, log-sum-exp, the log-probs of
+// the sampled or given id and the top-k log-probs).
+template <typename E>
+__device__ __forceinline__ void finish_row(const Job& j, int row, const Plan& pl, SegSh& sh,
+                                           uint32_t flags, int nA, int nB) {
   const int l = lane();
-  uint64_t* mb = lay.merge(dyn);
-  __syncthreads();  // every thread is done with the previous merge's counters
-  if (threadIdx.x == 0) {
-    sh.merge_n = 0;
-    sh.out_n = 0;
-  }
-  __syncthreads();
-  const uint32_t thr = sh.thr[li];
-  if (!povf) {
-#pragma unroll
-    for (int s = 0; s < kPoolN; ++s) {
-      const int slot = s * kWave + l;
-      const uint32_t key = slot < pn ? pkey_[slot] : 0u;
-      const bool take = slot < pn && key >= thr;
-      const uint64_t bal = __builtin_amdgcn_ballot_w64(take);
-      int b0 = 0;
-      if (l == 0 && bal) b0 = atomicAdd(&sh.merge_n, __popcll(bal));
-      b0 = __shfl(b0, 0);
-      if (take) {
-        const int pos = b0 + lanes_below(bal);
-        if (pos < kMergeCap) mb[pos] = pack(key, pid_[slot]);
+  const float nanv = __builtin_nanf("");
+  const RowCfg& c = pl.c;
+  const bool bad_logits = (flags & kMetaBadLogits) || !(flags & kMetaHasFinite);
+  const float M = sh.segM;
+  const float logS = j.lse ? logf(sh.segS) : nanv;
+  const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
+  if (j.lse && l == 0)
+    j.rlse[row] = bad_logits ? make_float2(nanv, nanv) : make_float2(M, logS);
+  if (j.sample) {
+    int status = c.status | (bad_logits ? VS_ROW_BAD_LOGITS : 0);
+    if (pl.kA == 1 && sh.seg_best[0] == 0ull) status |= VS_ROW_BAD_LOGITS;
+    if (status == 0 && (j.hints & VS_HINT_ALL_GREEDY) && c.mode != kModeGreedy)
+      status = VS_ROW_HINT_VIOLATED;
+    int32_t id = -1, kept = 0;
+    if (status == 0) {
+      if (c.mode == kModeGreedy) {
+        id = pid(sh.seg_best[0]);
+        kept = 1;
+      } else {  // top-k <= 64
+        status = wave_draw(sh.srt[0], nA < pl.kA ? nA : pl.kA, c, row, &id, &kept, nullptr);
       }
     }
-  } else if (l == 0) {
-    sh.ovf[li] = 1;
-  }
-  __syncthreads();
-  const int n = sh.merge_n;
-  if (sh.ovf[li] || n > kMergeCap) return -1;
-  uint32_t kth = 0;
-  if (n >= k) {
-    if (n <= kPool) {
-      if (w == 0) {
-        uint32_t k3[kPoolN];
-#pragma unroll
-        for (int s = 0; s < kPoolN; ++s) {
-          const int slot = s * kWave + l;
-          k3[s] = slot < n ? pkey(mb[slot]) : 0u;
+    if (status || id < 0 || id >= j.V) {
+      if (!status) status = VS_ROW_BAD_LOGITS;  // unreachable: ids come from the row
+      id = -1;
+      kept = 0;
+    }
+    // the sampled id's logit: its key when the list holds keys of x itself
+    float x_id = nanv;
+    bool x_known = false;
+    if (id >= 0) {
+      if (c.mode == kModeGreedy) {
+        x_id = key2f(pkey(sh.seg_best[0]));
+        x_known = true;
+      } else if (pl.TA == 1.0f) {
+        const uint64_t P = sh.srt[0][l];
+        const uint64_t hit = __ballot(l < nA && P != 0ull && pid(P) == id);
+        if (hit) {
+          x_id = key2f(pkey(__shfl(P, __ffsll(static_cast<unsigned long long>(hit)) - 1)));
+          x_known = true;
         }
-        const uint32_t t = wave_kth_largest_n<kPoolN>(k3, k);
-        if (l == 0) sh.prefix = t;
       }
-      __syncthreads();
-      kth = sh.prefix;
-      __syncthreads();
-    } else {
-      kth = block_kth_key(mb, n, k, sh);
+    }
+    if (l == 0) {
+      j.desc[row].mode = kRowDone;
+      j.out_ids[row] = id;
+      if (j.out_kept) j.out_kept[row] = kept;
+      if (j.out_status) j.out_status[row] = status;
+      if (j.tok_sampled) {
+        if (id >= 0 && !x_known) x_id = to_f32(rowp[id]);
+        j.out_tok_lp[row] = (id < 0 || bad_logits) ? nanv : (x_id - M) - logS;
+      }
     }
   }
-  // every entry reaching kth goes out (order is irrelevant to the reader)
-  for (int i0 = 0; i0 < n; i0 += blockDim.x) {
-    const int i = i0 + static_cast<int>(threadIdx.x);
-    const uint64_t e = i < n ? mb[i] : 0ull;
-    const bool take = i < n && pkey(e) >= kth;
-    const uint64_t bal = __builtin_amdgcn_ballot_w64(take);
-    int b0 = 0;
-    if (l == 0 && bal) b0 = atomicAdd(&sh.out_n, __popcll(bal));
-    b0 = __shfl(b0, 0);
-    if (take) {
-      const int pos = b0 + lanes_below(bal);
-      if (pos < kSelCap) out[pos] = e;
+  // top-k log-probabilities
+  if (j.lse && j.k_lp > 0) {
+    const int k = j.k_lp;
+    int32_t* ids = j.out_lp_ids + static_cast<size_t>(row) * k;
+    float* lps = j.out_lp + static_cast<size_t>(row) * k;
+    uint64_t P = 0ull;
+    int n = 0;
+    if (!bad_logits) {
+      if (pl.shared && pl.kA == 1) {  // k == 1: the argmax of list A
+        n = 1;
+        P = sh.seg_best[0];
+      } else if (pl.shared) {
+        n = nA;
+        P = sh.srt[0][l];
+      } else if (pl.kB == 1) {
+        n = 1;
+        P = sh.seg_best[1];
+      } else {
+        n = nB;
+        P = sh.srt[1][l];
+      }
+    }
+    if (l < k) {
+      const bool has = l < n && P != 0ull;
+      ids[l] = has ? pid(P) : -1;
+      lps[l] = has ? (key2f(pkey(P)) - M) - logS : nanv;
     }
   }
-  __syncthreads();
-  const int c = sh.out_n;
-  if (threadIdx.x == 0) *kth_out = kth;
-  return c > kSelCap ? -1 : c;
+  // log-probabilities of given ids (vs_logprobs)
+  if (j.lse && !j.sample && l == 0) {
+    int st = bad_logits ? VS_ROW_BAD_LOGITS : 0;
+    if (j.tok) {
+      const int tok = j.tok[row];
+      const bool badtok = tok < 0 || tok >= j.V;
+      if (badtok) st |= VS_ROW_BAD_TOKEN_ID;
+      j.out_tok_lp[row] = (bad_logits || badtok) ? nanv : (to_f32(rowp[tok]) - M) - logS;
+    }
+    if (j.out_lp_status) j.out_lp_status[row] = st;
+  }
 }
 
 template <typename E, bool kStream>
 __global__ __launch_bounds__(1024) void k_select(Job j) {
-  extern __shared__ __align__(16) char dyn[];
   __shared__ SegSh sh;
   int row, seg;
   if (!xcd_row_tile(blockIdx.x, j.B, j.nseg, &row, &seg)) return;  // uniform per block
   const int W = blockDim.x / kWave;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int l = lane();
-  const Layout lay{W};
   const Plan pl = plan_row(j, row);
   const int t_begin = seg * j.tps;
   const int t_end = min(t_begin + j.tps, j.ntile);
 
   if (threadIdx.x == 0) {
+    sh.next_tile = t_begin + W;  // the first W tiles go to the waves in order
     sh.thr[0] = sh.thr[1] = 0u;
     sh.ovf[0] = sh.ovf[1] = 0;
+    sh.merge_n[0] = sh.merge_n[1] = 0;
+    sh.out_n[0] = sh.out_n[1] = 0;
+    sh.kth_key[0] = sh.kth_key[1] = 0u;
     sh.flags = 0u;
   }
+  // empty pool slots read as 0, below every candidate
+  for (int i = threadIdx.x; i < 2 * kPoolCap; i += blockDim.x) (&sh.pool[0][0])[i] = 0ull;
   __syncthreads();
 
-  Pool PA{lay.pool_key(dyn, w, 0), lay.pool_id(dyn, w, 0), &sh.thr[0], pl.kA, pl.TA, 0, 0u, false};
-  Pool PB{lay.pool_key(dyn, w, 1), lay.pool_id(dyn, w, 1), &sh.thr[1], pl.kB, 1.0f, 0, 0u, false};
+  List LA{0, pl.kA, pl.TA, 0u, -kInf};
+  List LB{1, pl.kB, 1.0f, 0u, -kInf};
   const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
 
-  float Mw = -kInf, Sw = 0.0f;  // this wave's log-sum-exp partial
+  // log-sum-exp state per lane: running maximum lm, its shift lc = fl(lm
+  // log2 e) (-inf while lm is), and the sum ls of 2^(x log2 e - lc); in
+  // "huge" mode (a maximum of 2^120 or more seen by the wave) ls is the sum of
+  // exp(x - lm) instead
+  float lm = -kInf, lc = -kInf, ls = 0.0f;
+  bool huge = false;
   uint64_t bestA = 0ull, bestB = 0ull;
-  bool bad = false, fin = false;
+  bool bad_l = false, fin_l = false;
   // Each wave walks its tiles with the next tile's loads in flight while the
   // current one is processed: two register buffers used in turn, and a load
   // issued for every step (of the row's first 16 bytes when there is no next
@@ -494,101 +617,143 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
     const bool real = tt < t_end && full_tile(tt);  // else a placeholder load
     load_raw<E, kStream>(rowp + (real ? tt * kSelTile : 0), real ? 1 : 0, X);
   };
-  auto step = [&](const float (&v)[kVals], int tt, bool vec) __attribute__((always_inline)) {
+  auto step = [&](const float (&v)[kVals], const float (&g)[kGroups], float lmax, int tt,
+                  bool vec) __attribute__((always_inline)) {
     const int tile_base = tt * kSelTile;
-    // NaN-propagating maximum: a lane maximum is NaN or +inf exactly when the
-    // lane holds a NaN or a +inf, which make the row invalid.
-    float g[kGroups];
-#pragma unroll
-    for (int gi = 0; gi < kGroups; ++gi) {
-      float m = v[gi * kGroup];
-#pragma unroll
-      for (int u = 1; u < kGroup; ++u) m = __builtin_elementwise_maximum(m, v[gi * kGroup + u]);
-      g[gi] = m;
-    }
-    float lmax = g[0];
-#pragma unroll
-    for (int gi = 1; gi < kGroups; ++gi) lmax = __builtin_elementwise_maximum(lmax, g[gi]);
-    bad = bad || (__ballot(!(lmax < kInf)) != 0ull);
-    const float M = wave_max_dpp(lmax);
-    fin = fin || M > -kInf;
+    bad_l = bad_l || !(lmax < kInf);
+    fin_l = fin_l || lmax > -kInf;
 
-    if (j.lse && M > -kInf) {
-      // sum of 2^(x log2 e - c) with c = fl(M log2 e) (one fma and one exp2 per
-      // value), then times 2^-r with r = M log2 e - c exactly: the sum of
-      // exp(x - M) up to the rounding of each term
-      float sl = 0.0f;
-      float corr;
-      if (fabsf(M) < 0x1p100f) {
-        const float c = M * kL2E;
-        const float r = fmaf(M, kL2E, -c);
-        float s2[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // independent partial sums
-#pragma unroll
-        for (int q = 0; q < kVals; ++q) s2[q & 3] += __builtin_amdgcn_exp2f(fmaf(v[q], kL2E, -c));
-        sl = (s2[0] + s2[1]) + (s2[2] + s2[3]);
-        corr = __builtin_amdgcn_exp2f(-r);
-      } else {
-#pragma unroll
-        for (int q = 0; q < kVals; ++q) sl += __expf(v[q] - M);
-        corr = 1.0f;
+    if (j.lse) {
+      // Each lane keeps sum 2^(x log2 e - c) over its values, c = fl(m log2 e)
+      // for its running maximum m (one fma and one exp2 per value); a new
+      // maximum rescales the sum by 2^(c_old - c_new). The wave and the
+      // workgroup combine the lanes once, at the end.
+      if (!huge && __ballot(fabsf(lmax) >= 0x1p120f && fabsf(lmax) < kInf) != 0ull) {
+        // a maximum too large for c: from here on sums of exp(x - m)
+        huge = true;
+        if (lm > -kInf) ls *= __builtin_amdgcn_exp2f(-fmaf(lm, kL2E, -lc));
       }
-      const float st = wave_sum_dpp(sl) * corr;
-      if (M > Mw) {
-        Sw = (Mw > -kInf ? Sw * __expf(Mw - M) : 0.0f) + st;
-        Mw = M;
+      const float mn = fmaxf(lm, lmax);  // (a NaN lmax leaves m: the row is invalid anyway)
+      if (!huge) {
+        const float cn = mn * kL2E;
+        ls *= (mn > -kInf) ? __builtin_amdgcn_exp2f(lc - cn) : 1.0f;
+        const float cu = (mn > -kInf) ? cn : 0.0f;  // all -inf so far: terms of 0
+        float s2[4] = {0.0f, 0.0f, 0.0f, 0.0f};    // independent partial sums
+#pragma unroll
+        for (int q = 0; q < kVals; ++q) s2[q & 3] += __builtin_amdgcn_exp2f(fmaf(v[q], kL2E, -cu));
+        ls += (s2[0] + s2[1]) + (s2[2] + s2[3]);
+        lc = cn;
       } else {
-        Sw += st * __expf(M - Mw);
+        const float mu = (mn > -kInf) ? mn : 0.0f;
+        ls *= (mn > -kInf && lm > -kInf) ? __expf(lm - mn) : 1.0f;
+        float s1 = 0.0f;
+#pragma unroll
+        for (int q = 0; q < kVals; ++q) s1 += __expf(v[q] - mu);
+        ls += s1;
       }
+      lm = mn;
     }
 
     if (pl.kA == 1 || pl.kB == 1) {
+      const float M = wave_max_dpp(lmax);
       const uint64_t best = tile_argmax<E>(v, M, tile_base, j.V, vec);
       if (pl.kA == 1) bestA = best > bestA ? best : bestA;
       if (pl.kB == 1) bestB = best > bestB ? best : bestB;
     }
-    if (pl.kA > 1) pool_tile<E>(v, g, lmax, tile_base, j.V, vec, PA);
-    if (pl.kB > 1) pool_tile<E>(v, g, lmax, tile_base, j.V, vec, PB);
+    if (pl.kA > 1) list_tile<E>(v, g, lmax, tile_base, j.V, vec, LA, sh, sh.pool[0]);
+    if (pl.kB > 1) list_tile<E>(v, g, lmax, tile_base, j.V, vec, LB, sh, sh.pool[1]);
   };
-  int t = t_begin + w;
-  if (j.aligned && j.V >= kSelTile) {  // full tiles exist: row element 0 starts one
-    const int tf_end = min(t_end, j.V / kSelTile);  // this segment's full tiles end here
-    Raw<E> A, Bf;
-    issue(A, t);
-    while (t < tf_end) {
-      issue(Bf, t + W);
-      {
-        float v[kVals];
-        unpack_raw<E>(A, rowp, v);
-        step(v, t, true);
-      }
-      t += W;
-      if (t >= tf_end) break;
-      issue(A, t + W);
-      {
-        float v[kVals];
-        unpack_raw<E>(Bf, rowp, v);
-        step(v, t, true);
-      }
-      t += W;
+  const bool pf = j.aligned && j.V >= kSelTile;  // full tiles exist: element 0 starts one
+  const int tf_end = pf ? min(t_end, j.V / kSelTile) : t_begin;  // this segment's full tiles
+  // Tiles go to waves as they need them (a wave that is ahead takes more): the
+  // first round gives wave w tile t_begin + w, later ones come from an LDS
+  // counter. Claims increase, so at most one wave draws the row's partial last
+  // tile (the only tile in [tf_end, t_end)).
+  auto claim = [&]() __attribute__((always_inline)) {
+    int c = 0;
+    if (l == 0) c = atomicAdd(&sh.next_tile, 1);
+    return __shfl(c, 0);
+  };
+  const int t0 = t_begin + w;
+  int ta = t0;
+  int tb = pf ? claim() : t_end;
+  Raw<E> A, Bf;
+  if (pf) {
+    issue(A, ta);
+    issue(Bf, tb);
+  }
+  // First round: the maxima of every wave's first tile, if it is a full one.
+  // The k-th largest lane maximum over the workgroup bounds each list's k-th
+  // key from below (k distinct values reach it) and is the pools' starting
+  // bound. (A key of 0 stands for no value; a bound of 0 means no bound yet.)
+  {
+    uint32_t key0 = 0u;
+    if (t0 < tf_end) {
+      float v[kVals], g[kGroups], lmax;
+      unpack_raw<E>(A, rowp, v);
+      tile_maxima(v, g, lmax);
+      key0 = f2key(lmax);
+    } else if (pf) {
+      // the placeholder loads finish here, so that no path reaches the loop
+      // below with the buffers' loads outstanding
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    }
+    // (a bound of 0 means fewer than k lanes held data: no bound yet)
+    if (pl.kA > 1) {
+      const uint32_t tk = block_kth_u32(key0, pl.kA, sh);
+      LA.set_thr((pl.TA == 1.0f || tk == 0u) ? tk : f2key(key2f(tk) / pl.TA));
+    }
+    if (pl.kB > 1) LB.set_thr(block_kth_u32(key0, pl.kB, sh));
+    if (threadIdx.x == 0) {
+      atomicMax(&sh.thr[0], LA.thr);
+      atomicMax(&sh.thr[1], LB.thr);
     }
   }
-  // the tiles left: the row's last, partial tile, or all of them when the row
-  // is not 16-byte aligned
-  for (; t < t_end; t += W) {
-    float v[kVals];
-    load_tail<E>(rowp, t * kSelTile, j.V, v);
-    step(v, t, false);
+  if (pf) {
+    // Two buffers in turn: process one, then refill it with a newly claimed
+    // tile while the other one's loads are in flight. The buffer processed is
+    // always the one holding the smaller tile index.
+    while (ta < tf_end) {
+      {
+        float v[kVals], g[kGroups], lmax;
+        unpack_raw<E>(A, rowp, v);
+        tile_maxima(v, g, lmax);
+        step(v, g, lmax, ta, true);
+      }
+      ta = claim();
+      issue(A, ta);
+      if (tb >= tf_end) break;
+      {
+        float v[kVals], g[kGroups], lmax;
+        unpack_raw<E>(Bf, rowp, v);
+        tile_maxima(v, g, lmax);
+        step(v, g, lmax, tb, true);
+      }
+      tb = claim();
+      issue(Bf, tb);
+    }
+  }
+  // Element loads: the row's partial last tile, if this wave drew it, or every
+  // tile of a row that is not 16-byte aligned or is shorter than a tile (then
+  // the waves take them in turn).
+  int tt = pf ? ((ta >= tf_end && ta < t_end) ? ta : ((tb >= tf_end && tb < t_end) ? tb : t_end))
+              : t0;
+  for (; tt < t_end; tt = pf ? t_end : tt + W) {
+    float v[kVals], g[kGroups], lmax;
+    load_tail<E>(rowp, tt * kSelTile, j.V, v);
+    tile_maxima(v, g, lmax);
+    step(v, g, lmax, tt, false);
   }
 
-  // Shrink each pool to its exact top k (and ties) and share the bound.
-  if (pl.kA > 1 && !PA.ovf && PA.n > PA.k) {
-    pool_compact(PA, PA.thr);
-    if (l == 0) atomicMax(PA.shared_thr, PA.thr);
+  // this wave's log-sum-exp partial (Mw, Sw): Sw = sum of exp(x - Mw)
+  float Mw = -kInf, Sw = 0.0f;
+  if (j.lse) {
+    const float s_l = (!huge && lm > -kInf) ? ls * __builtin_amdgcn_exp2f(-fmaf(lm, kL2E, -lc)) : ls;
+    Mw = wave_max_dpp(lm);
+    Sw = wave_sum_dpp((lm > -kInf && Mw > -kInf) ? s_l * __expf(lm - Mw) : 0.0f);
   }
-  if (pl.kB > 1 && !PB.ovf && PB.n > PB.k) {
-    pool_compact(PB, PB.thr);
-    if (l == 0) atomicMax(PB.shared_thr, PB.thr);
-  }
+  const bool bad = __ballot(bad_l) != 0ull;
+  const bool fin = __ballot(fin_l) != 0ull;
   if (l == 0) {
     sh.wm[w] = Mw;
     sh.ws[w] = Sw;
@@ -603,47 +768,58 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
   const size_t slot = static_cast<size_t>(row) * j.nseg + seg;
   uint32_t meta = sh.flags;
   if (pl.kA > 1) {
-    const int n = merge_list(dyn, lay, sh, 0, pl.kA, PA.key, PA.id, PA.n, PA.ovf,
-                             j.candA + slot * kSelCap, &j.kthA[slot]);
+    const int n = merge_list(sh, 0, pl.kA, j.candA + slot * kSelCap, &j.kthA[slot]);
     meta |= (n < 0) ? kMetaOverflowA : static_cast<uint32_t>(n);
   }
   if (pl.kB > 1) {
-    const int n = merge_list(dyn, lay, sh, 1, pl.kB, PB.key, PB.id, PB.n, PB.ovf,
-                             j.candB + slot * kSelCap, &j.kthB[slot]);
+    const int n = merge_list(sh, 1, pl.kB, j.candB + slot * kSelCap, &j.kthB[slot]);
     meta |= (n < 0) ? kMetaOverflowB : (static_cast<uint32_t>(n) << kMetaCountBShift);
   }
-  if (threadIdx.x == 0) {
-    float M = -kInf;
-    uint64_t bA = 0ull, bB = 0ull;
-    for (int i = 0; i < W; ++i) {
-      M = fmaxf(M, sh.wm[i]);
-      bA = sh.best[0][i] > bA ? sh.best[0][i] : bA;
-      bB = sh.best[1][i] > bB ? sh.best[1][i] : bB;
-    }
-    if (j.lse) {
-      float S = 0.0f;
-      if (M > -kInf) {
-        for (int i = 0; i < W; ++i)
-          if (sh.wm[i] > -kInf) S += sh.ws[i] * __expf(sh.wm[i] - M);
+  if (w == 0) {  // the segment totals, across wave 0's lanes
+    const float mi = l < W ? sh.wm[l] : -kInf;
+    const float M = wave_max_dpp(mi);
+    const float S = wave_sum_dpp((j.lse && mi > -kInf) ? sh.ws[l] * __expf(mi - M) : 0.0f);
+    const uint64_t bA = wave_max(l < W ? sh.best[0][l] : 0ull);
+    const uint64_t bB = wave_max(l < W ? sh.best[1][l] : 0ull);
+    if (l == 0) {
+      if (j.lse) j.lpart[slot] = LsePart{M, S};
+      sh.segM = M;
+      sh.segS = S;
+      sh.seg_best[0] = bA;
+      sh.seg_best[1] = bB;
+      if (pl.kA == 1) {
+        if (bA) {
+          meta |= 1u;
+          j.candA[slot * kSelCap] = bA;
+        }
+        j.kthA[slot] = pkey(bA);  // the segment maximum: its 1st-largest key
       }
-      j.lpart[slot] = LsePart{M, S};
-    }
-    if (pl.kA == 1) {
-      if (bA) {
-        meta |= 1u;
-        j.candA[slot * kSelCap] = bA;
+      if (pl.kB == 1) {
+        if (bB) {
+          meta |= 1u << kMetaCountBShift;
+          j.candB[slot * kSelCap] = bB;
+        }
+        j.kthB[slot] = pkey(bB);
       }
-      j.kthA[slot] = pkey(bA);  // the segment maximum: its 1st-largest key
     }
-    if (pl.kB == 1) {
-      if (bB) {
-        meta |= 1u << kMetaCountBShift;
-        j.candB[slot * kSelCap] = bB;
-      }
-      j.kthB[slot] = pkey(bB);
-    }
-    j.meta[slot] = meta;
+    meta = __shfl(meta, 0);
   }
+  // A row read whole by this workgroup whose draw needs nothing beyond its
+  // candidates (greedy, top-k <= 64, or rows that fail their checks; no kept
+  // mask asked for) is finished here; the row kernel then skips it.
+  const bool finish = j.nseg == 1 && !j.out_mask &&
+                      !(meta & (kMetaOverflowA | kMetaOverflowB)) &&
+                      (!j.sample || pl.c.mode == kModeGreedy || pl.c.mode == kModeKFast ||
+                       pl.c.mode == kModeInvalid);
+  if (finish) {
+    __syncthreads();  // the segment totals above
+    if (w == 0) {
+      const int nA = (pl.kA > 1) ? static_cast<int>(meta & kMetaCountA) : 0;
+      const int nB = (pl.kB > 1) ? static_cast<int>((meta >> kMetaCountBShift) & 0xffu) : 0;
+      finish_row<E>(j, row, pl, sh, meta, nA, nB);
+    }
+  }
+  if (threadIdx.x == 0) j.meta[slot] = meta | (finish ? kMetaFinal : 0u);
 }
 
 }  // namespace
@@ -651,7 +827,7 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
 hipError_t launch_select(const Job& j, hipStream_t st) {
   const int grid = xcd_grid(j.B, j.nseg);
   const dim3 block(kWave * j.nwave);
-  const size_t lds = dyn_lds_bytes(j.nwave);
+  const size_t lds = 0;
   // Logits read once (no later kernel reads them again: no full log-softmax
   // output, and no full-vocabulary rows) stream past the caches.
   const bool stream = !j.out_full &&

@@ -284,9 +284,19 @@ __device__ __forceinline__ float dpp_f32(float v) {
 __device__ __forceinline__ float readlane_f32(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
-// Wave-wide max / sum of an fp32 (uniform result): all-reduce inside each row
-// of 16 lanes with DPP, then combine the four rows through scalar reads.
-// fmaxf ignores NaN. The summation order is fixed, so results are reproducible.
+// Wave-wide max of a u32, max / sum of an fp32 (uniform result): all-reduce
+// inside each row of 16 lanes with DPP, then combine the four rows through
+// scalar reads. fmaxf ignores NaN. The summation order is fixed, so results are
+// reproducible.
+__device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
+  v = max(v, static_cast<uint32_t>(dpp_i32<kDppXor1>(static_cast<int>(v))));
+  v = max(v, static_cast<uint32_t>(dpp_i32<kDppXor2>(static_cast<int>(v))));
+  v = max(v, static_cast<uint32_t>(dpp_i32<kDppRor4>(static_cast<int>(v))));
+  v = max(v, static_cast<uint32_t>(dpp_i32<kDppRor8>(static_cast<int>(v))));
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
+}
 __device__ __forceinline__ float wave_max_dpp(float v) {
   v = fmaxf(v, dpp_f32<kDppXor1>(v));
   v = fmaxf(v, dpp_f32<kDppXor2>(v));
@@ -317,7 +327,7 @@ __device__ __forceinline__ int wave_min_dpp(int v) {
 __device__ __forceinline__ uint32_t wave_kth_largest(uint32_t key, int k) {
   uint64_t cand = ~0ull;
   uint32_t prefix = 0;
-#pragma unroll
+#pragma unroll 4
   for (int b = 31; b >= 0; --b) {
     const uint64_t ones = __ballot((key >> b) & 1u) & cand;
     const int c = __popcll(ones);
@@ -340,7 +350,7 @@ __device__ __forceinline__ uint32_t wave_kth_largest_n(const uint32_t (&key)[N],
 #pragma unroll
   for (int i = 0; i < N; ++i) cand[i] = ~0ull;
   uint32_t prefix = 0;
-#pragma unroll
+#pragma unroll 4
   for (int b = 31; b >= 0; --b) {
     uint64_t ones[N];
     int c = 0;
@@ -364,7 +374,7 @@ __device__ __forceinline__ uint32_t wave_kth_largest_n(const uint32_t (&key)[N],
 __device__ __forceinline__ uint32_t wave_kth_largest2(uint32_t ka, uint32_t kb, int k) {
   uint64_t ca = ~0ull, cb = ~0ull;
   uint32_t prefix = 0;
-#pragma unroll
+#pragma unroll 4
   for (int b = 31; b >= 0; --b) {
     const uint64_t oa = __ballot((ka >> b) & 1u) & ca;
     const uint64_t ob = __ballot((kb >> b) & 1u) & cb;
@@ -410,6 +420,47 @@ __device__ __forceinline__ T wave_merge_top_desc(T a, T b) {
     v = ((l & j) == 0) ? (o > v ? o : v) : (o < v ? o : v);
   }
   return v;
+}
+
+// Truncation and the draw over the n <= 64 sorted candidates L (packed, key of
+// s = x / T) with one wave, no block barrier; call from every lane of one wave.
+// min-p keeps e = E(s - m) >= min_p; top-p keeps the shortest prefix whose
+// fixed-point mass reaches p times the kept mass; the draw is the Gumbel-max
+// argmax of e / -log(u) over the kept set, ties to the lowest id. Returns the
+// status (VS_ROW_BAD_LOGITS for an empty list, VS_ROW_BAD_PARAM when s = +inf).
+__device__ inline int wave_draw(const uint64_t* L, int n, const RowCfg& c, int row,
+                                int32_t* id_out, int32_t* kept_out, uint32_t* mask_row) {
+  const int i = lane();
+  if (n <= 0) return VS_ROW_BAD_LOGITS;  // no candidate: never read an id from it
+  const uint64_t top = L[0];
+  if (pkey(top) == kKeyPosInf) return VS_ROW_BAD_PARAM;
+  const float m = key2f(pkey(top));
+  const bool has = i < n;
+  const uint64_t P = has ? L[i] : 0ull;
+  const float e = has ? pinned_exp(key2f(pkey(P)) - m) : 0.0f;
+  const bool in_s = has && (e >= c.mp);
+  bool kept = in_s;
+  if (c.p < 1.0f) {
+    uint64_t cum = in_s ? mass_of(e) : 0ull;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const uint64_t w = __shfl_up(cum, o);
+      if (i >= o) cum += w;
+    }
+    const uint64_t tw = __shfl(cum, kWave - 1);
+    const double thr = static_cast<double>(c.p) * static_cast<double>(tw);
+    const uint64_t hit = __ballot(in_s && static_cast<double>(cum) >= thr);
+    const int cut = hit ? __ffsll(static_cast<unsigned long long>(hit)) - 1 : kWave;
+    kept = in_s && i <= cut;
+  }
+  const int id = has ? pid(P) : 0x7fffffff;
+  const double sc = kept ? gumbel_score(e, row_stream(c.seed, row), id) : -1.0;
+  const double best = wave_max(sc);
+  const int win = wave_min((kept && sc == best) ? id : 0x7fffffff);
+  if (kept && mask_row) atomicOr(&mask_row[id >> 5], 1u << (id & 31));
+  *id_out = win;
+  *kept_out = __popcll(__ballot(kept));
+  return 0;
 }
 
 // ---------------------------------------------------------------- block primitives

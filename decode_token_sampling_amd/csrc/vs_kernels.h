@@ -25,6 +25,7 @@ constexpr uint32_t kMetaBadLogits = 1u << 16;
 constexpr uint32_t kMetaHasFinite = 1u << 17;
 constexpr uint32_t kMetaOverflowA = 1u << 18;
 constexpr uint32_t kMetaOverflowB = 1u << 19;
+constexpr uint32_t kMetaFinal = 1u << 20;  // the streaming pass finished the row itself
 
 // Row descriptor states (written for every row by the row kernel each call).
 enum : uint32_t {
