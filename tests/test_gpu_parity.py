@@ -402,3 +402,94 @@ def test_workload_fused_w256x248320_f32():
     sub = {kk: (v[torch.from_numpy(rows).cuda()] if isinstance(v, torch.Tensor) else v)
            for kk, v in out.items()}
     _check_fused_logprobs(np.ascontiguousarray(x[rows]), wl.V, sub, 20)
+
+
+# ---------------------------------------------------------------- rows finished by the streaming pass
+# With at least one row per compute unit every row gets a workgroup of its
+# own, which also finishes the row (draw, log-probs) when no kept mask is asked
+# for; rows that need the row kernels (top-k > 64, full vocabulary, ties that
+# overflow the candidate pool) still go there. These tests run such batches
+# without a mask, against the oracle and against the row-kernel path (the
+# same call with a mask).
+FIN_B = 320
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [7, 2048, 4097, 70001])
+def test_finish_in_stream_sample(V, dtype):
+    x = _row_shapes(3000 + V, FIN_B, V, dtype)
+    w = random_params(np.random.default_rng(V + 7), FIN_B, V)
+    xd = to_device(x)
+    g = gpu_sample(xd, V, w, mask=False)
+    compare_sample(g, oracle_sample(x, V, w, mask=False))
+    gm = gpu_sample(xd, V, w, mask=True)
+    for key in ("ids", "kept", "status"):
+        assert np.array_equal(g[key], gm[key]), key
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [4097, 32000])
+@pytest.mark.parametrize("k", [0, 1, 5, 20, 64])
+def test_finish_in_stream_fused(V, dtype, k):
+    import decode_token_sampling_amd as vs
+    x = _row_shapes(4000 + V, FIN_B, V, dtype)
+    x[3, 1] = np.nan if dtype == "f32" else 0x7FC0   # a bad row
+    w = random_params(np.random.default_rng(V + 3 * k), FIN_B, V)
+    out = vs.sample_logprobs(to_device(x), dev(w["temperature"], np.float32),
+                             dev(w["top_k"], np.int32), dev(w["top_p"], np.float32),
+                             dev(w["min_p"], np.float32),
+                             dev(np.asarray(w["seeds"], np.uint64).view(np.int64), np.int64),
+                             k=k, V=V)
+    torch.cuda.synchronize()
+    g = dict(ids=out["ids"].cpu().numpy(), kept=out["kept"].cpu().numpy(),
+             status=out["status"].cpu().numpy())
+    compare_sample(g, oracle_sample(x, V, w, mask=False))
+    _check_fused_logprobs(x, V, out, k)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("k", [0, 1, 20, 64])
+def test_finish_in_stream_logprobs(dtype, k):
+    import decode_token_sampling_amd as vs
+    V = 33333
+    x = _row_shapes(5000 + k, FIN_B, V, dtype)
+    x[7, 3] = np.nan if dtype == "f32" else 0x7FC0
+    tok = np.random.default_rng(k).integers(0, V, FIN_B).astype(np.int32)
+    tok[5], tok[6] = -1, V  # bad ids
+    g = vs.logprobs(to_device(x), dev(tok, np.int32), k=k, V=V)
+    torch.cuda.synchronize()
+    o = oracle.logprobs(x, V, tok, k=k)
+    assert np.array_equal(g["status"].cpu().numpy(), o["status"])
+    gl, ol = g["token_lp"].cpu().numpy(), o["token_lp"]
+    assert np.array_equal(np.isnan(gl), np.isnan(ol))
+    ok = ~np.isnan(ol)
+    assert np.allclose(gl[ok], ol[ok], atol=LOGPROB_ATOL, rtol=0)
+    if k:
+        assert np.array_equal(g["topk_ids"].cpu().numpy(), o["topk_ids"])
+        gk, ok_ = g["topk_lp"].cpu().numpy(), o["topk_lp"]
+        assert np.array_equal(np.isnan(gk), np.isnan(ok_))
+        fin = ~np.isnan(ok_)
+        assert np.allclose(gk[fin], ok_[fin], atol=LOGPROB_ATOL, rtol=0)
+
+
+def test_finish_in_stream_workload_w256x248320_f32():
+    """The benchmarked call (no mask, hints, top-20 log-probs) against the oracle."""
+    import decode_token_sampling_amd as vs
+    wl = synth.make("w256x248320_f32")
+    x = wl.logits
+    w = params_from(wl)
+    out = vs.sample_logprobs(to_device(x), dev(w["temperature"], np.float32),
+                             dev(w["top_k"], np.int32), dev(w["top_p"], np.float32),
+                             dev(w["min_p"], np.float32),
+                             dev(np.asarray(w["seeds"], np.uint64).view(np.int64), np.int64),
+                             hints=vs.HINT_NO_FULLVOCAB, k=20)
+    torch.cuda.synchronize()
+    g = dict(ids=out["ids"].cpu().numpy(), kept=out["kept"].cpu().numpy(),
+             status=out["status"].cpu().numpy())
+    near = compare_sample(g, oracle_sample(x, wl.V, w, mask=False))
+    print(f"near-tie rows: {near}")
+    rows = np.arange(0, wl.B, 4)
+    o = oracle.logprobs(np.ascontiguousarray(x[rows]), wl.V, g["ids"][rows], k=20)
+    assert np.allclose(out["token_lp"].cpu().numpy()[rows], o["token_lp"], atol=LOGPROB_ATOL, rtol=0)
+    assert np.array_equal(out["topk_ids"].cpu().numpy()[rows], o["topk_ids"])
+    assert np.allclose(out["topk_lp"].cpu().numpy()[rows], o["topk_lp"], atol=LOGPROB_ATOL, rtol=0)
