@@ -145,17 +145,18 @@ __global__ __launch_bounds__(kThreads) void k_lse_full(Job j, int ntile, bool ou
   for (int i = 0; i < NV; ++i) {
     const int j0 = base + (i * kThreads + static_cast<int>(threadIdx.x)) * EPV;
     if (vec) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(rowp + j0);
+      // read once, written once: both streamed past the caches
+      const uint4 raw = load16_stream(rowp + j0);
       float x[EPV];
       unpack16(raw, x, rowp);
 #pragma unroll
       for (int c = 0; c < EPV; c += 4) {
-        float4 o;
+        f32x4 o;
         o.x = (x[c] - ml.x) - ml.y;
         o.y = (x[c + 1] - ml.x) - ml.y;
         o.z = (x[c + 2] - ml.x) - ml.y;
         o.w = (x[c + 3] - ml.x) - ml.y;
-        *reinterpret_cast<float4*>(orow + j0 + c) = o;
+        __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(orow + j0 + c));
       }
     } else {
 #pragma unroll

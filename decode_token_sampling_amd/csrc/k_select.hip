@@ -8,7 +8,8 @@
 //  - the flags (NaN or +inf seen, some value above -inf), from a
 //    NaN-propagating maximum;
 //  - in log-probability mode the log-sum-exp partial (max, sum of exp(x - max));
-//  - for a list that wants the argmax of x: the tile argmax with its lowest id;
+//  - for a list that wants the argmax of x: each lane's best value and its
+//    first id;
 //  - for a list that wants the top k (2 <= k <= 64) of s = x / T: a pool of
 //    candidates in LDS. Values are taken into the pool only if their key
 //    reaches the best lower bound known for the segment's k-th largest key:
@@ -87,33 +88,6 @@ __device__ __forceinline__ void load_tail(const E* __restrict__ rowp, int tile_b
     const int idx = elem_index<E>(tile_base, q);
     v[q] = (idx < V) ? to_f32(rowp[idx]) : -kInf;
   }
-}
-
-// Argmax of the tile with its lowest id: the wave max M, then a scan in id
-// order (vector index ascending; within it lane, then component) that stops
-// at the first value equal to M. Returns the packed candidate, 0 if none.
-template <typename E>
-__device__ __forceinline__ uint64_t tile_argmax(const float (&v)[kVals], float M, int tile_base,
-                                                int V, bool vec) {
-  constexpr int EPV = Epv<E>::n;
-  constexpr int NV = kVals / EPV;
-  if (!(M >= -kInf)) return 0ull;  // only NaN in this tile
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    int cfirst = EPV;
-#pragma unroll
-    for (int c = EPV - 1; c >= 0; --c) {
-      const int idx = tile_base + (i * kWave + lane()) * EPV + c;
-      if (v[i * EPV + c] == M && (vec || idx < V)) cfirst = c;
-    }
-    const uint64_t bal = __ballot(cfirst < EPV);
-    if (bal) {
-      const int l0 = __ffsll(static_cast<unsigned long long>(bal)) - 1;
-      const int c0 = __builtin_amdgcn_readlane(cfirst, l0);
-      return pack(f2key(M), tile_base + (i * kWave + l0) * EPV + c0);
-    }
-  }
-  return 0ull;
 }
 
 // The smallest float pre such that key(fl(x / T)) >= thr implies x >= pre:
@@ -604,7 +578,10 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
   // exp(x - lm) instead
   float lm = -kInf, lc = -kInf, ls = 0.0f;
   bool huge = false;
-  uint64_t bestA = 0ull, bestB = 0ull;
+  // argmax lists: each lane's best value of x so far (ordered key) and the
+  // lowest id holding it
+  uint32_t arg_key = 0u;
+  int32_t arg_id = -1;
   bool bad_l = false, fin_l = false;
   // Each wave walks its tiles with the next tile's loads in flight while the
   // current one is processed: two register buffers used in turn, and a load
@@ -655,10 +632,22 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
     }
 
     if (pl.kA == 1 || pl.kB == 1) {
-      const float M = wave_max_dpp(lmax);
-      const uint64_t best = tile_argmax<E>(v, M, tile_base, j.V, vec);
-      if (pl.kA == 1) bestA = best > bestA ? best : bestA;
-      if (pl.kB == 1) bestB = best > bestB ? best : bestB;
+      // a lane whose maximum beats its best so far finds the first position
+      // of that maximum (ids grow with q in a lane and with the tiles a wave
+      // takes, so the earliest one is the lowest id); rare after a few tiles
+      const uint32_t lk = f2key(lmax);
+      if (__builtin_amdgcn_ballot_w64(lk > arg_key) != 0ull) {
+        if (lk > arg_key) {
+          int first = kVals;
+#pragma unroll
+          for (int q = kVals - 1; q >= 0; --q)
+            if (v[q] == lmax && (vec || elem_index<E>(tile_base, q) < j.V)) first = q;
+          if (first < kVals) {
+            arg_key = lk;
+            arg_id = elem_index<E>(tile_base, first);
+          }
+        }
+      }
     }
     if (pl.kA > 1) list_tile<E>(v, g, lmax, tile_base, j.V, vec, LA, sh, sh.pool[0]);
     if (pl.kB > 1) list_tile<E>(v, g, lmax, tile_base, j.V, vec, LB, sh, sh.pool[1]);
@@ -754,11 +743,13 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
   }
   const bool bad = __ballot(bad_l) != 0ull;
   const bool fin = __ballot(fin_l) != 0ull;
+  uint64_t best = 0ull;
+  if (pl.kA == 1 || pl.kB == 1) best = wave_max(arg_id >= 0 ? pack(arg_key, arg_id) : 0ull);
   if (l == 0) {
     sh.wm[w] = Mw;
     sh.ws[w] = Sw;
-    sh.best[0][w] = bestA;
-    sh.best[1][w] = bestB;
+    sh.best[0][w] = pl.kA == 1 ? best : 0ull;
+    sh.best[1][w] = pl.kB == 1 ? best : 0ull;
     uint32_t f = bad ? kMetaBadLogits : 0u;
     if (fin) f |= kMetaHasFinite;
     if (f) atomicOr(&sh.flags, f);
@@ -829,9 +820,13 @@ hipError_t launch_select(const Job& j, hipStream_t st) {
   const dim3 block(kWave * j.nwave);
   const size_t lds = 0;
   // Logits read once (no later kernel reads them again: no full log-softmax
-  // output, and no full-vocabulary rows) stream past the caches.
-  const bool stream = !j.out_full &&
-                      (!j.sample || (j.hints & (VS_HINT_NO_FULLVOCAB | VS_HINT_ALL_GREEDY)));
+  // output, and no full-vocabulary rows) stream past the caches, and so do
+  // logits too large for the last-level cache to keep for a second reader
+  // (more than half of its 256 MB).
+  const int64_t bytes = static_cast<int64_t>(j.B) * j.V * (j.dt == VS_F32 ? 4 : 2);
+  const bool stream = bytes > (int64_t{128} << 20) ||
+                      (!j.out_full &&
+                       (!j.sample || (j.hints & (VS_HINT_NO_FULLVOCAB | VS_HINT_ALL_GREEDY))));
   if (j.dt == VS_F32) {
     if (stream)
       hipLaunchKernelGGL((k_select<float, true>), dim3(grid), block, lds, st, j);

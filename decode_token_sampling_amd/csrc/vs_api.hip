@@ -68,14 +68,20 @@ Job make_job(const void* logits, vs_dtype dt, int B, int V, int64_t ld, void* ws
   j.ntile = L.ntile;
   j.ntile3 = L.ntile3;
   // Streaming-pass geometry: enough segments per row that the batch gives
-  // every compute unit a workgroup, each segment read by up to 16 waves.
+  // every compute unit a workgroup, each segment read by up to 16 waves. When
+  // the batch alone holds more rows than compute units, workgroups shrink
+  // (down to 4 waves) so that several share a compute unit and one row's
+  // closing steps overlap other rows' streaming.
   const int cus = device_cus();
   const int nslot = (V + kSegMin - 1) / kSegMin;
   int S = (cus + B - 1) / B;
   S = S < 1 ? 1 : (S > nslot ? nslot : S);
   j.tps = (L.ntile + S - 1) / S;
   j.nseg = (L.ntile + j.tps - 1) / j.tps;
-  j.nwave = j.tps < kSelMaxWaves ? j.tps : kSelMaxWaves;
+  int wmax = kSelMaxWaves;
+  while (wmax > 4 && static_cast<int64_t>(B) * wmax > static_cast<int64_t>(cus) * kSelMaxWaves)
+    wmax >>= 1;
+  j.nwave = j.tps < wmax ? j.tps : wmax;
   j.meta = reinterpret_cast<uint32_t*>(w + L.meta);
   j.candA = reinterpret_cast<uint64_t*>(w + L.candA);
   j.candB = reinterpret_cast<uint64_t*>(w + L.candB);

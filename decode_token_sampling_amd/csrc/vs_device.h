@@ -83,6 +83,7 @@ __device__ __forceinline__ void unpack16(const uint4& u, float* x, const uint16_
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load16(const void* p) {
   const u32x4 t = *reinterpret_cast<const u32x4*>(p);
   return make_uint4(t.x, t.y, t.z, t.w);
