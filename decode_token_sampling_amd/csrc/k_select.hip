@@ -272,26 +272,27 @@ struct SegSh {
   uint64_t best[2][16];
   uint64_t top[2][kSelCap];  // each list's segment candidates
   uint64_t srt[2][kWave];    // a list's 64 best, sorted (finishing a row)
-  float segM, segS;          // the segment's log-sum-exp partial
-  uint64_t seg_best[2];      // the segment's argmax for argmax lists
 };
 
 
-// Finishes list `li`: writes the segment's candidates (every value whose key
-// reaches the segment's exact k-th largest key) and that key, and leaves the
-// 64 best sorted in sh.srt. Each pool entry's rank (the number of larger
-// entries; packed values are distinct) is counted against all the others,
-// every thread reading the same LDS word at a time: the rank is the sorted
-// position, and the entry of rank k - 1 holds the k-th key. Returns the count,
-// or -1 on overflow. Called by the whole block after the streaming loop.
-__device__ int merge_list(SegSh& sh, int li, int k, uint64_t* __restrict__ out,
-                          uint32_t* kth_out) {
-  uint64_t* keep = sh.top[li];
-  const uint64_t* pool = sh.pool[li];
+// Finishes list `li` in LDS: leaves the 64 best entries sorted in sh.srt and,
+// when `out` is set, gathers in sh.top every entry whose key reaches the
+// segment's exact k-th largest key (*kth, 0 with fewer than k entries). Each
+// pool entry's rank (the number of larger entries; packed values are
+// distinct) is counted against all the others, every thread reading the same
+// LDS word at a time: the rank is the sorted position, and the entry of rank
+// k - 1 holds the k-th key. Returns the number gathered (without `out`: the
+// number of sorted entries the list needs, min(n, k)), or -1 on overflow.
+// Called by the whole block (NT threads) after the streaming loop; nothing
+// here touches global memory, so no wait on the memory system is taken.
+__device__ __forceinline__ int merge_list(SegSh& sh, int li, int k, int NT, bool out,
+                                          uint32_t* kth) {
   const int l = lane();
   const int n = sh.merge_n[li];
+  *kth = 0u;
   if (sh.ovf[li] || n > kPoolCap) return -1;
-  for (int i0 = 0; i0 < n; i0 += blockDim.x) {
+  const uint64_t* pool = sh.pool[li];
+  for (int i0 = 0; i0 < n; i0 += NT) {
     if (i0 + static_cast<int>(threadIdx.x / kWave) * kWave < n) {  // waves with an entry
       const int i = i0 + static_cast<int>(threadIdx.x);
       const uint64_t e[1] = {i < n ? pool[i] : 0ull};
@@ -302,27 +303,25 @@ __device__ int merge_list(SegSh& sh, int li, int k, uint64_t* __restrict__ out,
     }
   }
   __syncthreads();
-  const uint32_t kth = (n >= k) ? sh.kth_key[li] : 0u;
-  // every entry reaching kth goes out (order is irrelevant to the reader)
-  for (int i0 = 0; i0 < n; i0 += blockDim.x) {
+  if (!out) return n < k ? n : k;
+  const uint32_t kt = (n >= k) ? sh.kth_key[li] : 0u;
+  uint64_t* keep = sh.top[li];
+  for (int i0 = 0; i0 < n; i0 += NT) {
     const int i = i0 + static_cast<int>(threadIdx.x);
     const uint64_t e = i < n ? pool[i] : 0ull;
-    const bool take = i < n && pkey(e) >= kth;
+    const bool take = i < n && pkey(e) >= kt;
     const uint64_t bal = __builtin_amdgcn_ballot_w64(take);
     int b0 = 0;
     if (l == 0 && bal) b0 = atomicAdd(&sh.out_n[li], __popcll(bal));
     b0 = __shfl(b0, 0);
     if (take) {
       const int pos = b0 + lanes_below(bal);
-      if (pos < kSelCap) {
-        out[pos] = e;
-        keep[pos] = e;
-      }
+      if (pos < kSelCap) keep[pos] = e;
     }
   }
   __syncthreads();
   const int c = sh.out_n[li];
-  if (threadIdx.x == 0) *kth_out = kth;
+  *kth = kt;
   return c > kSelCap ? -1 : c;
 }
 
@@ -391,12 +390,13 @@ __device__ __forceinline__ void list_tile(const float (&v)[kVals], const float (
 // A lower bound on the k-th largest of the block's keys, one per thread
 // (1 <= k <= blockDim): the top 16 bits of that key, found by two 8-bit digit
 // passes over an LDS histogram (at least k keys reach the result). Called by
-// the whole block.
-__device__ uint32_t block_kth_u32(uint32_t key, int k, SegSh& sh) {
+// the whole block (NT threads); inline, so that the loads in flight around it
+// are not waited for.
+__device__ __forceinline__ uint32_t block_kth_u32(uint32_t key, int k, int NT, SegSh& sh) {
   uint32_t prefix = 0;
   for (int d = 3; d >= 2; --d) {
     __syncthreads();  // the previous pass's readers are done with sh
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) sh.hist[i] = 0u;
+    for (int i = threadIdx.x; i < 256; i += NT) sh.hist[i] = 0u;
     __syncthreads();
     const uint32_t hmask = (d == 3) ? 0u : (0xffffffffu << (8 * (d + 1)));
     if ((key & hmask) == prefix) atomicAdd(&sh.hist[(key >> (8 * d)) & 0xffu], 1u);
@@ -443,28 +443,32 @@ __device__ uint32_t block_kth_u32(uint32_t key, int k, SegSh& sh) {
 
 // Finishes a row from its segment results with one wave: the same outputs the
 // row kernel writes (draw, kept count, status, log-sum-exp, the log-probs of
-// the sampled or given id and the top-k log-probs).
+// the sampled or given id and the top-k log-probs). (M, S) is the row's
+// log-sum-exp partial and bA, bB its argmax for argmax lists. Every load comes
+// before the first store: a load issued after stores waits for them too.
 template <typename E>
 __device__ __forceinline__ void finish_row(const Job& j, int row, const Plan& pl, SegSh& sh,
-                                           uint32_t flags, int nA, int nB) {
+                                           uint32_t flags, int nA, int nB, float M, float S,
+                                           uint64_t bA, uint64_t bB) {
   const int l = lane();
   const float nanv = __builtin_nanf("");
   const RowCfg& c = pl.c;
   const bool bad_logits = (flags & kMetaBadLogits) || !(flags & kMetaHasFinite);
-  const float M = sh.segM;
-  const float logS = j.lse ? logf(sh.segS) : nanv;
+  const float logS = j.lse ? logf(S) : nanv;
   const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
-  if (j.lse && l == 0)
-    j.rlse[row] = bad_logits ? make_float2(nanv, nanv) : make_float2(M, logS);
+
+  // the draw
+  int status = 0;
+  int32_t id = -1, kept = 0;
+  float x_id = nanv;
   if (j.sample) {
-    int status = c.status | (bad_logits ? VS_ROW_BAD_LOGITS : 0);
-    if (pl.kA == 1 && sh.seg_best[0] == 0ull) status |= VS_ROW_BAD_LOGITS;
+    status = c.status | (bad_logits ? VS_ROW_BAD_LOGITS : 0);
+    if (pl.kA == 1 && bA == 0ull) status |= VS_ROW_BAD_LOGITS;
     if (status == 0 && (j.hints & VS_HINT_ALL_GREEDY) && c.mode != kModeGreedy)
       status = VS_ROW_HINT_VIOLATED;
-    int32_t id = -1, kept = 0;
     if (status == 0) {
       if (c.mode == kModeGreedy) {
-        id = pid(sh.seg_best[0]);
+        id = pid(bA);
         kept = 1;
       } else {  // top-k <= 64
         status = wave_draw(sh.srt[0], nA < pl.kA ? nA : pl.kA, c, row, &id, &kept, nullptr);
@@ -476,11 +480,10 @@ __device__ __forceinline__ void finish_row(const Job& j, int row, const Plan& pl
       kept = 0;
     }
     // the sampled id's logit: its key when the list holds keys of x itself
-    float x_id = nanv;
     bool x_known = false;
     if (id >= 0) {
       if (c.mode == kModeGreedy) {
-        x_id = key2f(pkey(sh.seg_best[0]));
+        x_id = key2f(pkey(bA));
         x_known = true;
       } else if (pl.TA == 1.0f) {
         const uint64_t P = sh.srt[0][l];
@@ -491,55 +494,56 @@ __device__ __forceinline__ void finish_row(const Job& j, int row, const Plan& pl
         }
       }
     }
-    if (l == 0) {
+    if (j.tok_sampled && id >= 0 && !x_known) x_id = to_f32(rowp[id]);
+  }
+  // the given id (vs_logprobs)
+  int lp_st = bad_logits ? VS_ROW_BAD_LOGITS : 0;
+  float x_tok = nanv;
+  if (j.lse && !j.sample && j.tok) {
+    const int tok = j.tok[row];
+    if (tok < 0 || tok >= j.V)
+      lp_st |= VS_ROW_BAD_TOKEN_ID;
+    else if (!bad_logits)
+      x_tok = to_f32(rowp[tok]);
+  }
+  // the top-k log-probabilities' source
+  uint64_t P = 0ull;
+  int n = 0;
+  if (j.lse && j.k_lp > 0 && !bad_logits) {
+    if (pl.shared && pl.kA == 1) {  // k == 1: the argmax of list A
+      n = 1;
+      P = bA;
+    } else if (pl.shared) {
+      n = nA;
+      P = sh.srt[0][l];
+    } else if (pl.kB == 1) {
+      n = 1;
+      P = bB;
+    } else {
+      n = nB;
+      P = sh.srt[1][l];
+    }
+  }
+
+  // stores
+  if (l == 0) {
+    if (j.lse) j.rlse[row] = bad_logits ? make_float2(nanv, nanv) : make_float2(M, logS);
+    if (j.sample) {
       j.desc[row].mode = kRowDone;
       j.out_ids[row] = id;
       if (j.out_kept) j.out_kept[row] = kept;
       if (j.out_status) j.out_status[row] = status;
-      if (j.tok_sampled) {
-        if (id >= 0 && !x_known) x_id = to_f32(rowp[id]);
-        j.out_tok_lp[row] = (id < 0 || bad_logits) ? nanv : (x_id - M) - logS;
-      }
+      if (j.tok_sampled) j.out_tok_lp[row] = (id < 0 || bad_logits) ? nanv : (x_id - M) - logS;
+    } else if (j.lse) {
+      if (j.tok) j.out_tok_lp[row] = (lp_st != 0) ? nanv : (x_tok - M) - logS;
+      if (j.out_lp_status) j.out_lp_status[row] = lp_st;
     }
   }
-  // top-k log-probabilities
-  if (j.lse && j.k_lp > 0) {
+  if (j.lse && j.k_lp > 0 && l < j.k_lp) {
     const int k = j.k_lp;
-    int32_t* ids = j.out_lp_ids + static_cast<size_t>(row) * k;
-    float* lps = j.out_lp + static_cast<size_t>(row) * k;
-    uint64_t P = 0ull;
-    int n = 0;
-    if (!bad_logits) {
-      if (pl.shared && pl.kA == 1) {  // k == 1: the argmax of list A
-        n = 1;
-        P = sh.seg_best[0];
-      } else if (pl.shared) {
-        n = nA;
-        P = sh.srt[0][l];
-      } else if (pl.kB == 1) {
-        n = 1;
-        P = sh.seg_best[1];
-      } else {
-        n = nB;
-        P = sh.srt[1][l];
-      }
-    }
-    if (l < k) {
-      const bool has = l < n && P != 0ull;
-      ids[l] = has ? pid(P) : -1;
-      lps[l] = has ? (key2f(pkey(P)) - M) - logS : nanv;
-    }
-  }
-  // log-probabilities of given ids (vs_logprobs)
-  if (j.lse && !j.sample && l == 0) {
-    int st = bad_logits ? VS_ROW_BAD_LOGITS : 0;
-    if (j.tok) {
-      const int tok = j.tok[row];
-      const bool badtok = tok < 0 || tok >= j.V;
-      if (badtok) st |= VS_ROW_BAD_TOKEN_ID;
-      j.out_tok_lp[row] = (bad_logits || badtok) ? nanv : (to_f32(rowp[tok]) - M) - logS;
-    }
-    if (j.out_lp_status) j.out_lp_status[row] = st;
+    const bool has = l < n && P != 0ull;
+    j.out_lp_ids[static_cast<size_t>(row) * k + l] = has ? pid(P) : -1;
+    j.out_lp[static_cast<size_t>(row) * k + l] = has ? (key2f(pkey(P)) - M) - logS : nanv;
   }
 }
 
@@ -548,7 +552,9 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
   __shared__ SegSh sh;
   int row, seg;
   if (!xcd_row_tile(blockIdx.x, j.B, j.nseg, &row, &seg)) return;  // uniform per block
-  const int W = blockDim.x / kWave;
+  // the block size as a kernel argument: reading blockDim costs a memory load
+  const int W = j.nwave;
+  const int NT = W * kWave;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int l = lane();
   const Plan pl = plan_row(j, row);
@@ -565,7 +571,7 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
     sh.flags = 0u;
   }
   // empty pool slots read as 0, below every candidate
-  for (int i = threadIdx.x; i < 2 * kPoolCap; i += blockDim.x) (&sh.pool[0][0])[i] = 0ull;
+  for (int i = threadIdx.x; i < 2 * kPoolCap; i += NT) (&sh.pool[0][0])[i] = 0ull;
   __syncthreads();
 
   List LA{0, pl.kA, pl.TA, 0u, -kInf};
@@ -689,10 +695,10 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
     }
     // (a bound of 0 means fewer than k lanes held data: no bound yet)
     if (pl.kA > 1) {
-      const uint32_t tk = block_kth_u32(key0, pl.kA, sh);
+      const uint32_t tk = block_kth_u32(key0, pl.kA, NT, sh);
       LA.set_thr((pl.TA == 1.0f || tk == 0u) ? tk : f2key(key2f(tk) / pl.TA));
     }
-    if (pl.kB > 1) LB.set_thr(block_kth_u32(key0, pl.kB, sh));
+    if (pl.kB > 1) LB.set_thr(block_kth_u32(key0, pl.kB, NT, sh));
     if (threadIdx.x == 0) {
       atomicMax(&sh.thr[0], LA.thr);
       atomicMax(&sh.thr[1], LB.thr);
@@ -757,14 +763,25 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
   __syncthreads();
 
   const size_t slot = static_cast<size_t>(row) * j.nseg + seg;
+  // A row read whole by this workgroup whose draw needs nothing beyond its
+  // candidates (greedy, top-k <= 64, or rows that fail their checks; no kept
+  // mask asked for) is finished here, from LDS; the row kernel then skips it.
+  // Other segments hand their lists and partials on through the workspace.
+  const bool pool_ovf = (pl.kA > 1 && (sh.ovf[0] || sh.merge_n[0] > kPoolCap)) ||
+                        (pl.kB > 1 && (sh.ovf[1] || sh.merge_n[1] > kPoolCap));
+  const bool finish = j.nseg == 1 && !j.out_mask && !pool_ovf &&
+                      (!j.sample || pl.c.mode == kModeGreedy || pl.c.mode == kModeKFast ||
+                       pl.c.mode == kModeInvalid);
   uint32_t meta = sh.flags;
+  uint32_t kthA = 0u, kthB = 0u;
+  int nA = 0, nB = 0;
   if (pl.kA > 1) {
-    const int n = merge_list(sh, 0, pl.kA, j.candA + slot * kSelCap, &j.kthA[slot]);
-    meta |= (n < 0) ? kMetaOverflowA : static_cast<uint32_t>(n);
+    nA = merge_list(sh, 0, pl.kA, NT, !finish, &kthA);
+    meta |= (nA < 0) ? kMetaOverflowA : static_cast<uint32_t>(nA);
   }
   if (pl.kB > 1) {
-    const int n = merge_list(sh, 1, pl.kB, j.candB + slot * kSelCap, &j.kthB[slot]);
-    meta |= (n < 0) ? kMetaOverflowB : (static_cast<uint32_t>(n) << kMetaCountBShift);
+    nB = merge_list(sh, 1, pl.kB, NT, !finish, &kthB);
+    meta |= (nB < 0) ? kMetaOverflowB : (static_cast<uint32_t>(nB) << kMetaCountBShift);
   }
   if (w == 0) {  // the segment totals, across wave 0's lanes
     const float mi = l < W ? sh.wm[l] : -kInf;
@@ -772,45 +789,31 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
     const float S = wave_sum_dpp((j.lse && mi > -kInf) ? sh.ws[l] * __expf(mi - M) : 0.0f);
     const uint64_t bA = wave_max(l < W ? sh.best[0][l] : 0ull);
     const uint64_t bB = wave_max(l < W ? sh.best[1][l] : 0ull);
-    if (l == 0) {
+    if (pl.kA == 1 && bA) meta |= 1u;
+    if (pl.kB == 1 && bB) meta |= 1u << kMetaCountBShift;
+    if (finish) {
+      finish_row<E>(j, row, pl, sh, meta, nA, nB, M, S, bA, bB);
+    } else if (l == 0) {
       if (j.lse) j.lpart[slot] = LsePart{M, S};
-      sh.segM = M;
-      sh.segS = S;
-      sh.seg_best[0] = bA;
-      sh.seg_best[1] = bB;
       if (pl.kA == 1) {
-        if (bA) {
-          meta |= 1u;
-          j.candA[slot * kSelCap] = bA;
-        }
+        if (bA) j.candA[slot * kSelCap] = bA;
         j.kthA[slot] = pkey(bA);  // the segment maximum: its 1st-largest key
       }
       if (pl.kB == 1) {
-        if (bB) {
-          meta |= 1u << kMetaCountBShift;
-          j.candB[slot * kSelCap] = bB;
-        }
+        if (bB) j.candB[slot * kSelCap] = bB;
         j.kthB[slot] = pkey(bB);
       }
     }
-    meta = __shfl(meta, 0);
+    if (l == 0) j.meta[slot] = meta | (finish ? kMetaFinal : 0u);
   }
-  // A row read whole by this workgroup whose draw needs nothing beyond its
-  // candidates (greedy, top-k <= 64, or rows that fail their checks; no kept
-  // mask asked for) is finished here; the row kernel then skips it.
-  const bool finish = j.nseg == 1 && !j.out_mask &&
-                      !(meta & (kMetaOverflowA | kMetaOverflowB)) &&
-                      (!j.sample || pl.c.mode == kModeGreedy || pl.c.mode == kModeKFast ||
-                       pl.c.mode == kModeInvalid);
-  if (finish) {
-    __syncthreads();  // the segment totals above
-    if (w == 0) {
-      const int nA = (pl.kA > 1) ? static_cast<int>(meta & kMetaCountA) : 0;
-      const int nB = (pl.kB > 1) ? static_cast<int>((meta >> kMetaCountBShift) & 0xffu) : 0;
-      finish_row<E>(j, row, pl, sh, meta, nA, nB);
+  if (!finish) {  // the lists' candidates, for the row kernel
+    for (int i = threadIdx.x; i < nA; i += NT) j.candA[slot * kSelCap + i] = sh.top[0][i];
+    for (int i = threadIdx.x; i < nB; i += NT) j.candB[slot * kSelCap + i] = sh.top[1][i];
+    if (threadIdx.x == 0) {
+      if (pl.kA > 1) j.kthA[slot] = kthA;
+      if (pl.kB > 1) j.kthB[slot] = kthB;
     }
   }
-  if (threadIdx.x == 0) j.meta[slot] = meta | (finish ? kMetaFinal : 0u);
 }
 
 }  // namespace
