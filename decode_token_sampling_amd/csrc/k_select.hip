@@ -272,35 +272,52 @@ struct SegSh {
   uint64_t best[2][16];
   uint64_t top[2][kSelCap];  // each list's segment candidates
   uint64_t srt[2][kWave];    // a list's 64 best, sorted (finishing a row)
+  uint32_t rank[2][kPoolCap];  // each pool entry's rank, summed over the waves' slices
 };
 
 
 // Finishes list `li` in LDS: leaves the 64 best entries sorted in sh.srt and,
 // when `out` is set, gathers in sh.top every entry whose key reaches the
-// segment's exact k-th largest key (*kth, 0 with fewer than k entries). Each
-// pool entry's rank (the number of larger entries; packed values are
-// distinct) is counted against all the others, every thread reading the same
-// LDS word at a time: the rank is the sorted position, and the entry of rank
-// k - 1 holds the k-th key. Returns the number gathered (without `out`: the
-// number of sorted entries the list needs, min(n, k)), or -1 on overflow.
-// Called by the whole block (NT threads) after the streaming loop; nothing
-// here touches global memory, so no wait on the memory system is taken.
-__device__ __forceinline__ int merge_list(SegSh& sh, int li, int k, int NT, bool out,
+// segment's exact k-th largest key (*kth, 0 with fewer than k entries). An
+// entry's rank is the number of larger entries (packed values are distinct),
+// so it is the entry's sorted position, and the entry of rank k - 1 holds the
+// k-th key. Every wave counts one slice of the pool against all entries and
+// adds its counts to sh.rank (zero at the start), so the count is spread over
+// the block. Returns the number gathered (without `out`: the number of sorted
+// entries the list needs, min(n, k)), or -1 on overflow. Called by the whole
+// block (W waves) after the streaming loop; nothing here touches global
+// memory, so no wait on the memory system is taken.
+__device__ __forceinline__ int merge_list(SegSh& sh, int li, int k, int W, bool out,
                                           uint32_t* kth) {
   const int l = lane();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int NT = W * kWave;
   const int n = sh.merge_n[li];
   *kth = 0u;
   if (sh.ovf[li] || n > kPoolCap) return -1;
   const uint64_t* pool = sh.pool[li];
-  for (int i0 = 0; i0 < n; i0 += NT) {
-    if (i0 + static_cast<int>(threadIdx.x / kWave) * kWave < n) {  // waves with an entry
-      const int i = i0 + static_cast<int>(threadIdx.x);
-      const uint64_t e[1] = {i < n ? pool[i] : 0ull};
-      int r[1] = {0};
-      rank_counts<1, 16>(pool, n, e, r);
-      if (i < n && r[0] < kWave) sh.srt[li][r[0]] = e[0];
-      if (i < n && r[0] == k - 1) sh.kth_key[li] = pkey(e[0]);
+  uint32_t* rank = sh.rank[li];
+  const int C = (n + W - 1) / W;  // slice length
+  const int c0 = w * C;
+  const int c1 = min(n, c0 + C);
+  for (int i0 = 0; i0 < n && c0 < c1; i0 += kWave) {  // uniform
+    const int i = i0 + l;
+    const uint64_t e = i < n ? pool[i] : ~0ull;
+    int cnt = 0;
+    for (int m0 = c0; m0 < c1; m0 += 8) {  // uniform; 8 reads in flight
+      uint64_t o[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) o[u] = (m0 + u < c1) ? pool[m0 + u] : 0ull;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) cnt += (o[u] > e) ? 1 : 0;
     }
+    if (i < n && cnt) atomicAdd(&rank[i], static_cast<uint32_t>(cnt));
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += NT) {
+    const int r = static_cast<int>(rank[i]);
+    if (r < kWave) sh.srt[li][r] = pool[i];
+    if (r == k - 1) sh.kth_key[li] = pkey(pool[i]);
   }
   __syncthreads();
   if (!out) return n < k ? n : k;
@@ -570,8 +587,11 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
     sh.kth_key[0] = sh.kth_key[1] = 0u;
     sh.flags = 0u;
   }
-  // empty pool slots read as 0, below every candidate
-  for (int i = threadIdx.x; i < 2 * kPoolCap; i += NT) (&sh.pool[0][0])[i] = 0ull;
+  // empty pool slots read as 0, below every candidate; ranks start at 0
+  for (int i = threadIdx.x; i < 2 * kPoolCap; i += NT) {
+    (&sh.pool[0][0])[i] = 0ull;
+    (&sh.rank[0][0])[i] = 0u;
+  }
   __syncthreads();
 
   List LA{0, pl.kA, pl.TA, 0u, -kInf};
@@ -750,7 +770,7 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
   const bool bad = __ballot(bad_l) != 0ull;
   const bool fin = __ballot(fin_l) != 0ull;
   uint64_t best = 0ull;
-  if (pl.kA == 1 || pl.kB == 1) best = wave_max(arg_id >= 0 ? pack(arg_key, arg_id) : 0ull);
+  if (pl.kA == 1 || pl.kB == 1) best = wave_max_u64_dpp(arg_id >= 0 ? pack(arg_key, arg_id) : 0ull);
   if (l == 0) {
     sh.wm[w] = Mw;
     sh.ws[w] = Sw;
@@ -776,19 +796,19 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
   uint32_t kthA = 0u, kthB = 0u;
   int nA = 0, nB = 0;
   if (pl.kA > 1) {
-    nA = merge_list(sh, 0, pl.kA, NT, !finish, &kthA);
+    nA = merge_list(sh, 0, pl.kA, W, !finish, &kthA);
     meta |= (nA < 0) ? kMetaOverflowA : static_cast<uint32_t>(nA);
   }
   if (pl.kB > 1) {
-    nB = merge_list(sh, 1, pl.kB, NT, !finish, &kthB);
+    nB = merge_list(sh, 1, pl.kB, W, !finish, &kthB);
     meta |= (nB < 0) ? kMetaOverflowB : (static_cast<uint32_t>(nB) << kMetaCountBShift);
   }
   if (w == 0) {  // the segment totals, across wave 0's lanes
     const float mi = l < W ? sh.wm[l] : -kInf;
     const float M = wave_max_dpp(mi);
     const float S = wave_sum_dpp((j.lse && mi > -kInf) ? sh.ws[l] * __expf(mi - M) : 0.0f);
-    const uint64_t bA = wave_max(l < W ? sh.best[0][l] : 0ull);
-    const uint64_t bB = wave_max(l < W ? sh.best[1][l] : 0ull);
+    const uint64_t bA = wave_max_u64_dpp(l < W ? sh.best[0][l] : 0ull);
+    const uint64_t bB = wave_max_u64_dpp(l < W ? sh.best[1][l] : 0ull);
     if (pl.kA == 1 && bA) meta |= 1u;
     if (pl.kB == 1 && bB) meta |= 1u << kMetaCountBShift;
     if (finish) {

@@ -298,6 +298,32 @@ __device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
   const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
   return max(max(a, b), max(c, d));
 }
+template <int kCtrl>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = static_cast<uint32_t>(dpp_i32<kCtrl>(static_cast<int>(static_cast<uint32_t>(v))));
+  const uint32_t hi = static_cast<uint32_t>(dpp_i32<kCtrl>(static_cast<int>(static_cast<uint32_t>(v >> 32))));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), l);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), l);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+// Wave-wide max of a u64 (every lane active).
+__device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v) {
+  uint64_t o = dpp_u64<kDppXor1>(v);
+  v = o > v ? o : v;
+  o = dpp_u64<kDppXor2>(v);
+  v = o > v ? o : v;
+  o = dpp_u64<kDppRor4>(v);
+  v = o > v ? o : v;
+  o = dpp_u64<kDppRor8>(v);
+  v = o > v ? o : v;
+  const uint64_t a = readlane_u64(v, 0), b = readlane_u64(v, 16);
+  const uint64_t c = readlane_u64(v, 32), d = readlane_u64(v, 48);
+  const uint64_t ab = a > b ? a : b, cd = c > d ? c : d;
+  return ab > cd ? ab : cd;
+}
 __device__ __forceinline__ float wave_max_dpp(float v) {
   v = fmaxf(v, dpp_f32<kDppXor1>(v));
   v = fmaxf(v, dpp_f32<kDppXor2>(v));
@@ -429,6 +455,7 @@ __device__ __forceinline__ T wave_merge_top_desc(T a, T b) {
 // fixed-point mass reaches p times the kept mass; the draw is the Gumbel-max
 // argmax of e / -log(u) over the kept set, ties to the lowest id. Returns the
 // status (VS_ROW_BAD_LOGITS for an empty list, VS_ROW_BAD_PARAM when s = +inf).
+// Called by a whole wave, every lane active.
 __device__ inline int wave_draw(const uint64_t* L, int n, const RowCfg& c, int row,
                                 int32_t* id_out, int32_t* kept_out, uint32_t* mask_row) {
   const int i = lane();
@@ -440,6 +467,10 @@ __device__ inline int wave_draw(const uint64_t* L, int n, const RowCfg& c, int r
   const uint64_t P = has ? L[i] : 0ull;
   const float e = has ? pinned_exp(key2f(pkey(P)) - m) : 0.0f;
   const bool in_s = has && (e >= c.mp);
+  const int id = has ? pid(P) : 0x7fffffff;
+  // every candidate's score, computed before the cut is known so that the two
+  // overlap; nonnegative, so its bits order as integers
+  const double sc = has ? gumbel_score(e, row_stream(c.seed, row), id) : 0.0;
   bool kept = in_s;
   if (c.p < 1.0f) {
     uint64_t cum = in_s ? mass_of(e) : 0ull;
@@ -454,10 +485,9 @@ __device__ inline int wave_draw(const uint64_t* L, int n, const RowCfg& c, int r
     const int cut = hit ? __ffsll(static_cast<unsigned long long>(hit)) - 1 : kWave;
     kept = in_s && i <= cut;
   }
-  const int id = has ? pid(P) : 0x7fffffff;
-  const double sc = kept ? gumbel_score(e, row_stream(c.seed, row), id) : -1.0;
-  const double best = wave_max(sc);
-  const int win = wave_min((kept && sc == best) ? id : 0x7fffffff);
+  const uint64_t sb = kept ? static_cast<uint64_t>(__double_as_longlong(sc)) : 0ull;
+  const uint64_t best = wave_max_u64_dpp(sb);
+  const int win = wave_min_dpp((kept && sb == best) ? id : 0x7fffffff);
   if (kept && mask_row) atomicOr(&mask_row[id >> 5], 1u << (id & 31));
   *id_out = win;
   *kept_out = __popcll(__ballot(kept));
