@@ -540,6 +540,8 @@ __global__ __launch_bounds__(kLightThreads) void k_row_light(Job j) {
     if (status == 0) {
       if ((j.hints & VS_HINT_ALL_GREEDY) && c.mode != kModeGreedy) status = VS_ROW_HINT_VIOLATED;
       if ((j.hints & VS_HINT_NO_FULLVOCAB) && c.mode == kModeFull) status = VS_ROW_HINT_VIOLATED;
+      if ((j.hints & VS_HINT_SMALL_TOPK) && c.mode != kModeGreedy && c.mode != kModeKFast)
+        status = VS_ROW_HINT_VIOLATED;
     }
     int32_t id = -1, kept = 0;
     uint32_t next = kRowDone;

@@ -92,8 +92,10 @@ __device__ __forceinline__ void load_tail(const E* __restrict__ rowp, int tile_b
 
 // The smallest float pre such that key(fl(x / T)) >= thr implies x >= pre:
 // fl(x / T) >= s forces x / T >= pred(s), so x >= T * pred(s) (exact in
-// double), rounded down to float.
+// double), rounded down to float. Keys at or below key(-inf) stand for -inf
+// or for negative NaNs: every value passes.
 __device__ __forceinline__ float prefilter(uint32_t thr, float T) {
+  if (thr <= kKeyNegInf) return -kInf;
   const float s = key2f(thr);
   if (T == 1.0f) return s;
   const double y = static_cast<double>(T) * static_cast<double>(nextafterf(s, -kInf));
@@ -273,6 +275,7 @@ struct SegSh {
   uint64_t top[2][kSelCap];  // each list's segment candidates
   uint64_t srt[2][kWave];    // a list's 64 best, sorted (finishing a row)
   uint32_t rank[2][kPoolCap];  // each pool entry's rank, summed over the waves' slices
+  uint64_t stage[kSelMaxWaves][kWave];  // per-wave staging of a list rescan
 };
 
 
@@ -458,6 +461,96 @@ __device__ __forceinline__ uint32_t block_kth_u32(uint32_t key, int k, int NT, S
   return prefix;
 }
 
+// The exact 64 best entries of one list (packed keys of s = x / T with their
+// ids) over the whole row, for a row whose candidate pool overflowed. Each
+// wave rescans its slices of the row (64 lanes x one 16-byte vector: 256 fp32
+// or 512 bf16 values, every W-th slice) keeping its 64 best entries sorted
+// across its lanes, lane 0 the best. A slice contributes at most its own 64
+// best: when more than 64 of its entries beat the wave's 64th best, they are
+// cut to the keys above the slice's exact 64th largest key plus, of the keys
+// equal to it, the lowest ids (larger packed values) up to 64 in all. The
+// survivors are compacted through the wave's LDS stage, sorted and merged in.
+// The waves' lists then merge pairwise through LDS, and the block's 64 best
+// land in srt. Packed entries are distinct, so the result depends on no
+// order. Small slices keep the code and its registers small: the path is
+// rare. Called by the whole block (W waves, every lane active).
+template <typename E>
+__device__ __forceinline__ void rescan_list(const E* __restrict__ rowp, int V, bool aligned,
+                                            float T, int W, uint64_t (*stage)[kWave],
+                                            uint64_t* srt) {
+  constexpr int EPV = Epv<E>::n;
+  constexpr int kSlice = kWave * EPV;
+  const int l = lane();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int nslice = (V + kSlice - 1) / kSlice;
+  uint64_t top = 0ull;   // this wave's 64 best, descending across lanes
+  uint64_t tmin = 0ull;  // its 64th best: entries must beat it
+  for (int t = w; t < nslice; t += W) {
+    const int id0 = t * kSlice + l * EPV;  // this lane's first id; ids follow the lane, then u
+    float v[EPV];
+    if (aligned && (t + 1) * kSlice <= V) {
+      unpack16(load16(rowp + id0), v, rowp);
+    } else {
+#pragma unroll
+      for (int u = 0; u < EPV; ++u) v[u] = (id0 + u < V) ? to_f32(rowp[id0 + u]) : -kInf;
+    }
+    uint32_t key[EPV];
+    int cnt = 0;
+#pragma unroll
+    for (int u = 0; u < EPV; ++u) {
+      key[u] = (id0 + u < V) ? f2key((T == 1.0f) ? v[u] : v[u] / T) : 0u;
+      cnt += (key[u] != 0u && pack(key[u], id0 + u) > tmin) ? 1 : 0;
+    }
+    cnt = wave_sum_dpp_i32(cnt);
+    if (cnt == 0) continue;
+    uint32_t kt = 0u;  // with more than 64 entries: the slice's 64th largest key
+    int need = kWave;  // entries equal to kt still wanted, lowest ids first
+    if (cnt > kWave) {
+      // the largest t with at least 64 keys >= t, one bit at a time
+      for (int b = 31; b >= 0; --b) {
+        const uint32_t c = kt | (1u << b);
+        int ge = 0;
+#pragma unroll
+        for (int u = 0; u < EPV; ++u) ge += key[u] >= c ? 1 : 0;
+        if (wave_sum_dpp_i32(ge) >= kWave) kt = c;
+      }
+      int gt = 0;
+#pragma unroll
+      for (int u = 0; u < EPV; ++u) gt += key[u] > kt ? 1 : 0;
+      need = kWave - wave_sum_dpp_i32(gt);
+    }
+    // rank of a key equal to kt among those of the slice, in id order: ties in
+    // lower lanes, then in this lane before it
+    int rank = 0;
+#pragma unroll
+    for (int u = 0; u < EPV; ++u) rank += lanes_below(__ballot(key[u] != 0u && key[u] == kt));
+    int n = 0;  // entries staged (uniform)
+#pragma unroll
+    for (int u = 0; u < EPV; ++u) {
+      const bool tie = key[u] != 0u && key[u] == kt;
+      const bool sel = key[u] != 0u && (key[u] > kt || (tie && rank < need)) &&
+                       pack(key[u], id0 + u) > tmin;
+      rank += tie ? 1 : 0;
+      const uint64_t bs = __ballot(sel);
+      if (sel) stage[w][n + lanes_below(bs)] = pack(key[u], id0 + u);
+      n += __popcll(bs);
+    }
+    wave_lds_sync();
+    const uint64_t b = l < n ? stage[w][l] : 0ull;
+    top = wave_merge_top_desc(top, wave_sort_desc(b));
+    tmin = __shfl(top, kWave - 1);
+    wave_lds_sync();
+  }
+  for (int h = 1; h < W; h <<= 1) {
+    __syncthreads();
+    if ((w & (2 * h - 1)) == h) stage[w][l] = top;
+    __syncthreads();
+    if ((w & (2 * h - 1)) == 0 && w + h < W) top = wave_merge_top_desc(top, stage[w + h][l]);
+  }
+  if (w == 0) srt[l] = top;
+  __syncthreads();
+}
+
 // Finishes a row from its segment results with one wave: the same outputs the
 // row kernel writes (draw, kept count, status, log-sum-exp, the log-probs of
 // the sampled or given id and the top-k log-probs). (M, S) is the row's
@@ -481,8 +574,11 @@ __device__ __forceinline__ void finish_row(const Job& j, int row, const Plan& pl
   if (j.sample) {
     status = c.status | (bad_logits ? VS_ROW_BAD_LOGITS : 0);
     if (pl.kA == 1 && bA == 0ull) status |= VS_ROW_BAD_LOGITS;
-    if (status == 0 && (j.hints & VS_HINT_ALL_GREEDY) && c.mode != kModeGreedy)
-      status = VS_ROW_HINT_VIOLATED;
+    if (status == 0) {
+      if ((j.hints & VS_HINT_ALL_GREEDY) && c.mode != kModeGreedy) status = VS_ROW_HINT_VIOLATED;
+      if ((j.hints & VS_HINT_SMALL_TOPK) && c.mode != kModeGreedy && c.mode != kModeKFast)
+        status = VS_ROW_HINT_VIOLATED;
+    }
     if (status == 0) {
       if (c.mode == kModeGreedy) {
         id = pid(bA);
@@ -714,11 +810,19 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
     // (a bound of 0 means fewer than k lanes held data: no bound yet)
+    // The 16-bit prefix can fall below key(-inf), into keys of negative NaNs,
+    // when the k-th lane maximum is -inf: key(-inf) is then the bound (only a
+    // NaN, which fails the row anyway, lies below it).
     if (pl.kA > 1) {
-      const uint32_t tk = block_kth_u32(key0, pl.kA, NT, sh);
+      uint32_t tk = block_kth_u32(key0, pl.kA, NT, sh);
+      if (tk != 0u && tk < kKeyNegInf) tk = kKeyNegInf;
       LA.set_thr((pl.TA == 1.0f || tk == 0u) ? tk : f2key(key2f(tk) / pl.TA));
     }
-    if (pl.kB > 1) LB.set_thr(block_kth_u32(key0, pl.kB, NT, sh));
+    if (pl.kB > 1) {
+      uint32_t tk = block_kth_u32(key0, pl.kB, NT, sh);
+      if (tk != 0u && tk < kKeyNegInf) tk = kKeyNegInf;
+      LB.set_thr(tk);
+    }
     if (threadIdx.x == 0) {
       atomicMax(&sh.thr[0], LA.thr);
       atomicMax(&sh.thr[1], LB.thr);
@@ -784,25 +888,33 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
 
   const size_t slot = static_cast<size_t>(row) * j.nseg + seg;
   // A row read whole by this workgroup whose draw needs nothing beyond its
-  // candidates (greedy, top-k <= 64, or rows that fail their checks; no kept
-  // mask asked for) is finished here, from LDS; the row kernel then skips it.
-  // Other segments hand their lists and partials on through the workspace.
-  const bool pool_ovf = (pl.kA > 1 && (sh.ovf[0] || sh.merge_n[0] > kPoolCap)) ||
-                        (pl.kB > 1 && (sh.ovf[1] || sh.merge_n[1] > kPoolCap));
-  const bool finish = j.nseg == 1 && !j.out_mask && !pool_ovf &&
-                      (!j.sample || pl.c.mode == kModeGreedy || pl.c.mode == kModeKFast ||
-                       pl.c.mode == kModeInvalid);
+  // candidates (greedy, top-k <= 64, or rows that fail their checks, and every
+  // row when the caller's hints promise that; no kept mask asked for) is
+  // finished here, from LDS; the row kernel then skips it, or is not launched.
+  // A list whose pool overflowed is then rebuilt by a rescan of the row. Other
+  // segments hand their lists and partials on through the workspace.
+  const bool hinted = (j.hints & (VS_HINT_SMALL_TOPK | VS_HINT_ALL_GREEDY)) != 0u;
+  const bool finish = j.nseg == 1 && !j.out_mask &&
+                      (!j.sample || hinted || pl.c.mode == kModeGreedy ||
+                       pl.c.mode == kModeKFast || pl.c.mode == kModeInvalid);
   uint32_t meta = sh.flags;
   uint32_t kthA = 0u, kthB = 0u;
   int nA = 0, nB = 0;
-  if (pl.kA > 1) {
-    nA = merge_list(sh, 0, pl.kA, W, !finish, &kthA);
-    meta |= (nA < 0) ? kMetaOverflowA : static_cast<uint32_t>(nA);
+  const bool rsA = finish && pl.kA > 1 && (sh.ovf[0] || sh.merge_n[0] > kPoolCap);
+  const bool rsB = finish && pl.kB > 1 && (sh.ovf[1] || sh.merge_n[1] > kPoolCap);
+  if (pl.kA > 1 && !rsA) nA = merge_list(sh, 0, pl.kA, W, !finish, &kthA);
+  if (pl.kB > 1 && !rsB) nB = merge_list(sh, 1, pl.kB, W, !finish, &kthB);
+  if (rsA || rsB) {  // rare: one copy of the rescan serves both lists
+#pragma unroll 1
+    for (int li = 0; li < 2; ++li) {
+      if (li == 0 ? rsA : rsB)
+        rescan_list<E>(rowp, j.V, j.aligned, li == 0 ? pl.TA : 1.0f, W, sh.stage, sh.srt[li]);
+    }
+    if (rsA) nA = pl.kA;
+    if (rsB) nB = pl.kB;
   }
-  if (pl.kB > 1) {
-    nB = merge_list(sh, 1, pl.kB, W, !finish, &kthB);
-    meta |= (nB < 0) ? kMetaOverflowB : (static_cast<uint32_t>(nB) << kMetaCountBShift);
-  }
+  if (pl.kA > 1) meta |= (nA < 0) ? kMetaOverflowA : static_cast<uint32_t>(nA);
+  if (pl.kB > 1) meta |= (nB < 0) ? kMetaOverflowB : (static_cast<uint32_t>(nB) << kMetaCountBShift);
   if (w == 0) {  // the segment totals, across wave 0's lanes
     const float mi = l < W ? sh.wm[l] : -kInf;
     const float M = wave_max_dpp(mi);
@@ -849,7 +961,8 @@ hipError_t launch_select(const Job& j, hipStream_t st) {
   const int64_t bytes = static_cast<int64_t>(j.B) * j.V * (j.dt == VS_F32 ? 4 : 2);
   const bool stream = bytes > (int64_t{128} << 20) ||
                       (!j.out_full &&
-                       (!j.sample || (j.hints & (VS_HINT_NO_FULLVOCAB | VS_HINT_ALL_GREEDY))));
+                       (!j.sample || (j.hints & (VS_HINT_NO_FULLVOCAB | VS_HINT_ALL_GREEDY |
+                                                 VS_HINT_SMALL_TOPK))));
   if (j.dt == VS_F32) {
     if (stream)
       hipLaunchKernelGGL((k_select<float, true>), dim3(grid), block, lds, st, j);

@@ -183,7 +183,8 @@ vs_status vs_sample_logprobs(const void* logits, vs_dtype dt, int B, int V, int6
                              int32_t* out_topk_ids, float* out_topk_logprobs, float* out_full,
                              int64_t ld_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!logits || !out_ids || !ws || !sizes_ok(dt, B, V, ld)) return VS_ERR_INVALID_ARGUMENT;
-  if (hints & ~(VS_HINT_NO_FULLVOCAB | VS_HINT_ALL_GREEDY)) return VS_ERR_INVALID_ARGUMENT;
+  if (hints & ~(VS_HINT_NO_FULLVOCAB | VS_HINT_ALL_GREEDY | VS_HINT_SMALL_TOPK))
+    return VS_ERR_INVALID_ARGUMENT;
   if (k < 0 || k > VS_LOGPROB_K_MAX || k > V) return VS_ERR_INVALID_ARGUMENT;
   if (k > 0 && (!out_topk_ids || !out_topk_logprobs)) return VS_ERR_INVALID_ARGUMENT;
   if (out_full && ld_out < V) return VS_ERR_INVALID_ARGUMENT;
@@ -210,9 +211,15 @@ vs_status vs_sample_logprobs(const void* logits, vs_dtype dt, int B, int V, int6
   j.ld_out = ld_out;
   if (stage("select", stream, [&] { return vsk::launch_select(j, stream); }) != hipSuccess)
     return VS_ERR_HIP;
-  if (stage("row", stream, [&] { return vsk::launch_row_light(j, stream); }) != hipSuccess)
+  // With one segment per row, no kept mask and hints that rule out every row
+  // the streaming pass cannot finish (top-k above 64, full vocabulary), the
+  // streaming pass finishes every row and the row kernel has nothing to do.
+  const bool select_finishes =
+      j.nseg == 1 && !out_kept_mask && (hints & (VS_HINT_SMALL_TOPK | VS_HINT_ALL_GREEDY));
+  if (!select_finishes &&
+      stage("row", stream, [&] { return vsk::launch_row_light(j, stream); }) != hipSuccess)
     return VS_ERR_HIP;
-  if (!(hints & (VS_HINT_NO_FULLVOCAB | VS_HINT_ALL_GREEDY))) {
+  if (!(hints & (VS_HINT_NO_FULLVOCAB | VS_HINT_ALL_GREEDY | VS_HINT_SMALL_TOPK))) {
     if (stage("row_full", stream, [&] { return vsk::launch_row_full(j, stream); }) != hipSuccess)
       return VS_ERR_HIP;
     if (stage("gumbel", stream, [&] { return vsk::launch_gumbel(j, stream); }) != hipSuccess)
@@ -248,7 +255,9 @@ vs_status vs_logprobs(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
   j.out_lp_status = out_row_status;
   if (stage("lse_select", stream, [&] { return vsk::launch_select(j, stream); }) != hipSuccess)
     return VS_ERR_HIP;
-  if (stage("lse_row", stream, [&] { return vsk::launch_row_light(j, stream); }) != hipSuccess)
+  // with one segment per row the streaming pass finishes every row
+  if (j.nseg > 1 &&
+      stage("lse_row", stream, [&] { return vsk::launch_row_light(j, stream); }) != hipSuccess)
     return VS_ERR_HIP;
   if (out_full) {
     if (stage("lse_full", stream, [&] { return vsk::launch_lse_full(j, stream); }) != hipSuccess)

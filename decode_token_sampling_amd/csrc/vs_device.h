@@ -339,6 +339,14 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   v += dpp_f32<kDppRor8>(v);
   return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
 }
+__device__ __forceinline__ int wave_sum_dpp_i32(int v) {
+  v += dpp_i32<kDppXor1>(v);
+  v += dpp_i32<kDppXor2>(v);
+  v += dpp_i32<kDppRor4>(v);
+  v += dpp_i32<kDppRor8>(v);
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
 __device__ __forceinline__ int wave_min_dpp(int v) {
   v = min(v, dpp_i32<kDppXor1>(v));
   v = min(v, dpp_i32<kDppXor2>(v));

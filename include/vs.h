@@ -66,6 +66,8 @@ typedef enum vs_status {
 #define VS_HINT_NO_FULLVOCAB 1u   /* no row samples over the full vocabulary: every row is
                                      greedy or has 0 < top_k < V */
 #define VS_HINT_ALL_GREEDY 2u     /* every row is greedy */
+#define VS_HINT_SMALL_TOPK 4u     /* every row is greedy or has 1 < top_k <= 64 (and
+                                     top_k < V): no full-vocabulary row, no larger top-k */
 
 #define VS_MAX_V (1 << 21)        /* largest vocabulary */
 #define VS_TOPK_MAX 1024          /* largest top_k below V */

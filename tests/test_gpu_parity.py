@@ -493,3 +493,137 @@ def test_finish_in_stream_workload_w256x248320_f32():
     assert np.allclose(out["token_lp"].cpu().numpy()[rows], o["token_lp"], atol=LOGPROB_ATOL, rtol=0)
     assert np.array_equal(out["topk_ids"].cpu().numpy()[rows], o["topk_ids"])
     assert np.allclose(out["topk_lp"].cpu().numpy()[rows], o["topk_lp"], atol=LOGPROB_ATOL, rtol=0)
+
+
+# ---------------------------------------------------------------- pool overflow: the rescan
+# Rows that overflow the streaming pass's candidate pool: ascending or
+# descending values (the running bound trails every new value), constant rows
+# and a handful of levels (ties at the k-th value), a few finite values among
+# -inf (fewer than k finite ids). A row finished by the streaming pass then
+# rebuilds its lists by a rescan of the row; with a kept mask the row kernel's
+# exact path does it instead. Both must equal the oracle.
+def _overflow_rows(seed, B, V, dtype):
+    rng = np.random.default_rng(seed)
+    x = np.empty((B, V), np.float32)
+    for r in range(B):
+        kind = r % 6
+        if kind == 0:
+            x[r] = np.linspace(-6, 6, V, dtype=np.float32)
+        elif kind == 1:
+            x[r] = np.linspace(6, -6, V, dtype=np.float32)
+        elif kind == 2:
+            x[r] = np.float32(0.5)
+        elif kind == 3:
+            x[r] = -np.inf
+            n = int(rng.integers(1, 12))
+            x[r, rng.choice(V, min(n, V), replace=False)] = rng.normal(size=min(n, V))
+        elif kind == 4:
+            x[r] = rng.integers(0, 4, V).astype(np.float32)
+        else:
+            x[r] = rng.normal(size=V).astype(np.float32)
+    return synth.f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+def _small_topk_params(rng, B):
+    """Greedy rows and rows with 1 < top_k <= 64, some with top-p and min-p."""
+    T = rng.choice(np.array([1.0, 0.7, 1.3], np.float32), B).astype(np.float32)
+    k = rng.choice(np.array([2, 5, 20, 64], np.int32), B).astype(np.int32)
+    p = np.where(rng.random(B) < 0.5, np.float32(1.0), rng.uniform(0.2, 0.99, B)).astype(np.float32)
+    mp = np.where(rng.random(B) < 0.25, np.float32(0.05), np.float32(0)).astype(np.float32)
+    T[::7] = 0.0  # greedy rows
+    return dict(temperature=T, top_k=k, top_p=p, min_p=mp,
+                seeds=rng.integers(0, 2**63, B, dtype=np.int64).astype(np.uint64))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [4097, 8192, 70001, 70004])
+def test_finish_in_stream_overflow_rescan(V, dtype):
+    import decode_token_sampling_amd as vs
+    x = _overflow_rows(6000 + V, FIN_B, V, dtype)
+    w = _small_topk_params(np.random.default_rng(V), FIN_B)
+    xd = to_device(x)
+    o = oracle_sample(x, V, w, mask=False)
+    for hints in (vs.HINT_SMALL_TOPK, 0):  # without the row kernel, and with it launched
+        compare_sample(gpu_sample(xd, V, w, hints=hints, mask=False), o)
+    g = gpu_sample(xd, V, w, mask=True)  # the row kernel's exact path
+    compare_sample(g, oracle_sample(x, V, w, mask=True))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [12344, 12345])
+@pytest.mark.parametrize("k", [1, 20, 64])
+def test_finish_in_stream_overflow_fused(dtype, V, k):
+    import decode_token_sampling_amd as vs
+    x = _overflow_rows(7000 + k, FIN_B, V, dtype)
+    w = _small_topk_params(np.random.default_rng(k), FIN_B)
+    out = vs.sample_logprobs(to_device(x), dev(w["temperature"], np.float32),
+                             dev(w["top_k"], np.int32), dev(w["top_p"], np.float32),
+                             dev(w["min_p"], np.float32),
+                             dev(np.asarray(w["seeds"], np.uint64).view(np.int64), np.int64),
+                             hints=vs.HINT_SMALL_TOPK, k=k, V=V)
+    torch.cuda.synchronize()
+    g = dict(ids=out["ids"].cpu().numpy(), kept=out["kept"].cpu().numpy(),
+             status=out["status"].cpu().numpy())
+    compare_sample(g, oracle_sample(x, V, w, mask=False))
+    _check_fused_logprobs(x, V, out, k)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("k", [20, 64])
+def test_finish_in_stream_overflow_logprobs(dtype, k):
+    import decode_token_sampling_amd as vs
+    V = 9000
+    x = _overflow_rows(8000 + k, FIN_B, V, dtype)
+    tok = np.random.default_rng(k).integers(0, V, FIN_B).astype(np.int32)
+    g = vs.logprobs(to_device(x), dev(tok, np.int32), k=k, V=V)
+    torch.cuda.synchronize()
+    o = oracle.logprobs(x, V, tok, k=k)
+    assert np.array_equal(g["status"].cpu().numpy(), o["status"])
+    gl, ol = g["token_lp"].cpu().numpy(), o["token_lp"]
+    assert np.array_equal(np.isnan(gl), np.isnan(ol))
+    fin = ~np.isnan(ol)
+    assert np.allclose(gl[fin], ol[fin], atol=LOGPROB_ATOL, rtol=0)
+    assert np.array_equal(g["topk_ids"].cpu().numpy(), o["topk_ids"])
+    gk, ok_ = g["topk_lp"].cpu().numpy(), o["topk_lp"]
+    assert np.array_equal(np.isnan(gk), np.isnan(ok_))
+    fin = ~np.isnan(ok_)
+    assert np.allclose(gk[fin], ok_[fin], atol=LOGPROB_ATOL, rtol=0)
+
+
+@pytest.mark.parametrize("B", [12, FIN_B])
+def test_sample_hint_small_topk(B):
+    """Rows that break the small top-k promise (full vocabulary, top-k above
+    64) report it and draw nothing; the others match the oracle, whether the
+    streaming pass finishes every row (one segment per row) or not."""
+    import decode_token_sampling_amd as vs
+    V = 9000
+    x = synth.random_rows(9 + B, B, V)
+    w = random_params(np.random.default_rng(B), B, V, kinds=["greedy", "kfast", "kslow", "topp"])
+    o = oracle_sample(x, V, w, mask=False)
+    g = gpu_sample(to_device(x), V, w, hints=vs.HINT_SMALL_TOPK, mask=False)
+    bad = (np.arange(B) % 4 == 2) | (np.arange(B) % 4 == 3)
+    assert (g["status"][bad] == vs.ROW_HINT_VIOLATED).all() and (g["ids"][bad] == -1).all()
+    assert (g["kept"][bad] == 0).all()
+    compare_sample(g, o, rows=np.nonzero(~bad)[0])
+
+
+def test_finish_in_stream_workload_small_topk_hint():
+    """The benchmarked call with the small top-k promise (no row kernel)."""
+    import decode_token_sampling_amd as vs
+    wl = synth.make("w256x248320_f32")
+    x = wl.logits
+    w = params_from(wl)
+    out = vs.sample_logprobs(to_device(x), dev(w["temperature"], np.float32),
+                             dev(w["top_k"], np.int32), dev(w["top_p"], np.float32),
+                             dev(w["min_p"], np.float32),
+                             dev(np.asarray(w["seeds"], np.uint64).view(np.int64), np.int64),
+                             hints=vs.HINT_SMALL_TOPK, k=20)
+    torch.cuda.synchronize()
+    g = dict(ids=out["ids"].cpu().numpy(), kept=out["kept"].cpu().numpy(),
+             status=out["status"].cpu().numpy())
+    compare_sample(g, oracle_sample(x, wl.V, w, mask=False))
+    rows = np.arange(1, wl.B, 4)
+    o = oracle.logprobs(np.ascontiguousarray(x[rows]), wl.V, g["ids"][rows], k=20)
+    assert np.allclose(out["token_lp"].cpu().numpy()[rows], o["token_lp"], atol=LOGPROB_ATOL, rtol=0)
+    assert np.array_equal(out["topk_ids"].cpu().numpy()[rows], o["topk_ids"])
+    assert np.allclose(out["topk_lp"].cpu().numpy()[rows], o["topk_lp"], atol=LOGPROB_ATOL, rtol=0)
