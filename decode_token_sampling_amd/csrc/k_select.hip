@@ -33,7 +33,7 @@ namespace {
 constexpr int kVals = kSelTile / kWave;  // values per lane and tile (32)
 constexpr int kGroup = 4;         // values per group (a lane's maxima are kept per group)
 constexpr int kGroups = kVals / kGroup;
-static_assert(kGroup == 4 && kGroups == 8, "the group switch in extract() is written for 8 x 4");
+static_assert(kGroup == 4 && kGroups == 8, "extract() visits 8 groups of 4 values");
 
 constexpr int kPoolCap = 512;     // candidates per segment and list (the shared pool)
 constexpr int kCheck = 64;        // the pool's bound is recomputed every kCheck entries
@@ -125,76 +125,79 @@ __device__ __forceinline__ uint32_t tile_bound(const float (&v)[kVals], float lm
   return (T == 1.0f) ? tk : f2key(key2f(tk) / T);
 }
 
-// The values of the tile that reach a list's threshold: v >= pre (pre =
-// prefilter(thr, T)), and for T != 1 also key(v / T) >= thr. g holds each
-// lane's maxima of its groups of 4 values; only groups whose maximum reaches
-// pre in some lane are visited, by a loop over them that copies the group's
-// values out with a uniform switch (so the code for one value exists 4 times,
-// not 32). kWrite = false counts them; kWrite = true writes them, packed, to
-// out[0..count) (the count pass gives the space).
-template <typename E, bool kWrite>
-__device__ __forceinline__ int extract(const float (&v)[kVals], const float (&g)[kGroups],
-                                       uint32_t active, int tile_base, int V, bool vec,
-                                       uint32_t thr, float pre, float T,
-                                       uint64_t* __restrict__ out) {
+// Appends to the list's shared pool the values of group gi (values 4 gi ..
+// 4 gi + 3 of every lane) that reach its threshold: v >= pre (pre =
+// prefilter(thr, T)), and for T != 1 also key(v / T) >= thr. The group
+// reserves its space in the pool with one atomic add and writes its entries
+// packed. Returns -1 when the pool is full (the caller then flags the
+// overflow), else 1 when the reservation crossed a multiple of kCheck entries
+// (*end: the pool size after it), else 0.
+template <typename E, int gi>
+__device__ __forceinline__ int extract_group(const float (&v)[kVals], int tile_base, int V,
+                                             bool vec, uint32_t thr, float pre, float T,
+                                             int* pool_n, uint64_t* __restrict__ pool, int* end) {
   constexpr int EPV = Epv<E>::n;
-  const bool t1 = T == 1.0f;
   const int l = lane();
-  int n = 0;
-  while (active) {  // uniform
-    const int gi = __builtin_ctz(active);
-    active &= active - 1u;
-    float x[kGroup];
-    switch (gi) {
-#define VS_GROUP_CASE(G)                                          \
-  case G:                                                         \
-    x[0] = v[G * kGroup + 0];                                     \
-    x[1] = v[G * kGroup + 1];                                     \
-    x[2] = v[G * kGroup + 2];                                     \
-    x[3] = v[G * kGroup + 3];                                     \
-    break;
-      VS_GROUP_CASE(0)
-      VS_GROUP_CASE(1)
-      VS_GROUP_CASE(2)
-      VS_GROUP_CASE(3)
-      VS_GROUP_CASE(4)
-      VS_GROUP_CASE(5)
-      VS_GROUP_CASE(6)
-      default:
-        x[0] = v[7 * kGroup + 0];
-        x[1] = v[7 * kGroup + 1];
-        x[2] = v[7 * kGroup + 2];
-        x[3] = v[7 * kGroup + 3];
-        break;
-#undef VS_GROUP_CASE
-    }
+  bool p[kGroup];
+  uint32_t key[kGroup];
+  uint64_t bal[kGroup];
+  int cnt = 0;
 #pragma unroll
-    for (int u = 0; u < kGroup; ++u) {
-      // value q = gi * 4 + u of the lane: vector q / EPV, component q % EPV
-      const int q = gi * kGroup + u;
-      const int id = tile_base + ((q / EPV) * kWave + l) * EPV + (q % EPV);
-      bool p = x[u] >= pre && (vec || id < V);
-      uint64_t bal = __builtin_amdgcn_ballot_w64(p);
-      if (bal) {  // uniform: taken only when some lane has a candidate here
-        uint32_t key = f2key(x[u]);
-        if (!t1) {
-          if (p) {
-            key = f2key(x[u] / T);
-            p = key >= thr;
-          }
-          bal = __builtin_amdgcn_ballot_w64(p);
-        }
-        if (kWrite && p) out[n + lanes_below(bal)] = pack(key, id);
-        n += __popcll(bal);
-      }
+  for (int u = 0; u < kGroup; ++u) {
+    // value q = gi * 4 + u of the lane: vector q / EPV, component q % EPV
+    constexpr int q0 = gi * kGroup;
+    const int q = q0 + u;
+    const int id = tile_base + ((q / EPV) * kWave + l) * EPV + (q % EPV);
+    const float x = v[q];
+    p[u] = x >= pre && (vec || id < V);
+    key[u] = f2key(x);
+    if (T != 1.0f && p[u]) {
+      key[u] = f2key(x / T);
+      p[u] = key[u] >= thr;
     }
+    bal[u] = __builtin_amdgcn_ballot_w64(p[u]);
+    cnt += __popcll(bal[u]);
   }
-  return n;
+  if (cnt == 0) return 0;
+  int base = 0;
+  if (l == 0) base = atomicAdd(pool_n, cnt);
+  base = __builtin_amdgcn_readfirstlane(base);
+  if (base + cnt > kPoolCap) return -1;
+  const int crossed = (base + cnt) / kCheck > base / kCheck ? 1 : 0;
+  if (crossed) *end = base + cnt;
+#pragma unroll
+  for (int u = 0; u < kGroup; ++u) {
+    const int q = gi * kGroup + u;
+    const int id = tile_base + ((q / EPV) * kWave + l) * EPV + (q % EPV);
+    if (p[u]) pool[base + lanes_below(bal[u])] = pack(key[u], id);
+    base += __popcll(bal[u]);
+  }
+  return crossed;
 }
 
-__device__ __forceinline__ uint32_t lds_load_relaxed(uint32_t* p) {
-  return __builtin_amdgcn_readfirstlane(
-      __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+// The active groups of the tile (a bit per group whose maximum reaches the
+// prefilter in some lane), each through extract_group. Same result codes.
+template <typename E>
+__device__ __forceinline__ int extract(const float (&v)[kVals], uint32_t active, int tile_base,
+                                       int V, bool vec, uint32_t thr, float pre, float T,
+                                       int* pool_n, uint64_t* __restrict__ pool, int* end) {
+  int crossed = 0;
+#define VS_GROUP(G)                                                                         \
+  if (active & (1u << G)) {                                                                 \
+    const int r = extract_group<E, G>(v, tile_base, V, vec, thr, pre, T, pool_n, pool, end); \
+    if (r < 0) return -1;                                                                   \
+    crossed |= r;                                                                           \
+  }
+  VS_GROUP(0)
+  VS_GROUP(1)
+  VS_GROUP(2)
+  VS_GROUP(3)
+  VS_GROUP(4)
+  VS_GROUP(5)
+  VS_GROUP(6)
+  VS_GROUP(7)
+#undef VS_GROUP
+  return crossed;
 }
 
 // Adds to r[i] the number of the first n pool entries larger than e[i]. The
@@ -274,6 +277,9 @@ struct SegSh {
   uint64_t best[2][16];
   uint64_t top[2][kSelCap];  // each list's segment candidates
   uint64_t srt[2][kWave];    // a list's 64 best, sorted (finishing a row)
+  double srt_q[kWave];       // -log(u) of list A's sorted entries, for the draw
+  float tot_m, tot_s;        // the segment's log-sum-exp partial
+  uint64_t tot_b[2];         // the segment's argmax per argmax list
   uint32_t rank[2][kPoolCap];  // each pool entry's rank, summed over the waves' slices
   uint64_t stage[kSelMaxWaves][kWave];  // per-wave staging of a list rescan
 };
@@ -286,12 +292,13 @@ struct SegSh {
 // so it is the entry's sorted position, and the entry of rank k - 1 holds the
 // k-th key. Every wave counts one slice of the pool against all entries and
 // adds its counts to sh.rank (zero at the start), so the count is spread over
-// the block. Returns the number gathered (without `out`: the number of sorted
+// the block. For the first qk sorted entries the draw's -log(u) (random stream
+// state qstate) goes to sh.srt_q. Returns the number gathered (without `out`: the number of sorted
 // entries the list needs, min(n, k)), or -1 on overflow. Called by the whole
 // block (W waves) after the streaming loop; nothing here touches global
 // memory, so no wait on the memory system is taken.
 __device__ __forceinline__ int merge_list(SegSh& sh, int li, int k, int W, bool out,
-                                          uint32_t* kth) {
+                                          uint32_t* kth, int qk, uint64_t qstate) {
   const int l = lane();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int NT = W * kWave;
@@ -300,17 +307,20 @@ __device__ __forceinline__ int merge_list(SegSh& sh, int li, int k, int W, bool 
   if (sh.ovf[li] || n > kPoolCap) return -1;
   const uint64_t* pool = sh.pool[li];
   uint32_t* rank = sh.rank[li];
-  const int C = (n + W - 1) / W;  // slice length
+  // slices of a multiple of 8 entries (clamped to the pool, whose unused
+  // entries read as 0 and count as smaller than every entry), read 8 at a
+  // time with no condition, so that the reads overlap
+  const int C = (((n + W - 1) / W) + 7) & ~7;
   const int c0 = w * C;
-  const int c1 = min(n, c0 + C);
-  for (int i0 = 0; i0 < n && c0 < c1; i0 += kWave) {  // uniform
+  const int c1 = min(c0 + C, kPoolCap);
+  for (int i0 = 0; i0 < n && c0 < n; i0 += kWave) {  // uniform
     const int i = i0 + l;
-    const uint64_t e = i < n ? pool[i] : ~0ull;
+    const uint64_t e = pool[i < kPoolCap ? i : kPoolCap - 1];
     int cnt = 0;
-    for (int m0 = c0; m0 < c1; m0 += 8) {  // uniform; 8 reads in flight
+    for (int m0 = c0; m0 < c1; m0 += 8) {  // uniform
       uint64_t o[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) o[u] = (m0 + u < c1) ? pool[m0 + u] : 0ull;
+      for (int u = 0; u < 8; ++u) o[u] = pool[m0 + u];
 #pragma unroll
       for (int u = 0; u < 8; ++u) cnt += (o[u] > e) ? 1 : 0;
     }
@@ -319,8 +329,13 @@ __device__ __forceinline__ int merge_list(SegSh& sh, int li, int k, int W, bool 
   __syncthreads();
   for (int i = threadIdx.x; i < n; i += NT) {
     const int r = static_cast<int>(rank[i]);
-    if (r < kWave) sh.srt[li][r] = pool[i];
-    if (r == k - 1) sh.kth_key[li] = pkey(pool[i]);
+    const uint64_t e = pool[i];
+    if (r < kWave) {
+      sh.srt[li][r] = e;
+      // the draw's exponential noise, computed here by many threads at once
+      if (r < qk) sh.srt_q[r] = -log(uniform_of(qstate, pid(e)));
+    }
+    if (r == k - 1) sh.kth_key[li] = pkey(e);
   }
   __syncthreads();
   if (!out) return n < k ? n : k;
@@ -362,23 +377,21 @@ __device__ __forceinline__ void tile_maxima(const float (&v)[kVals], float (&g)[
   for (int gi = 1; gi < kGroups; ++gi) lmax = __builtin_elementwise_maximum(lmax, g[gi]);
 }
 
-// Adds one tile's candidates to the list's shared pool (in LDS). The count
-// pass reserves space with one atomic add; the write pass fills it. Each time
-// the pool grows past a multiple of kCheck entries, the wave that crossed it
-// recomputes the exact k-th largest key of the pool and raises the shared
-// bound: the pool holds every value seen so far that reached the bound in
-// force, so that key is the running k-th largest value of the segment.
+// Adds one tile's candidates to the list's shared pool (in LDS). shv is the
+// workgroup's shared bound, read from LDS when the tile's processing began (a
+// stale value is still a valid bound). Each time the pool grows past a
+// multiple of kCheck entries, the wave that crossed it recomputes the exact
+// k-th largest key of the pool and raises the shared bound: the pool holds
+// every value seen so far that reached the bound in force, so that key is the
+// running k-th largest value of the segment.
 template <typename E>
 __device__ __forceinline__ void list_tile(const float (&v)[kVals], const float (&g)[kGroups],
                                           float lmax, int tile_base, int V, bool vec, List& L,
-                                          SegSh& sh, uint64_t* pool) {
+                                          uint32_t shv, SegSh& sh, uint64_t* pool) {
+  shv = __builtin_amdgcn_readfirstlane(shv);
+  if (shv > L.thr) L.set_thr(shv);  // another wave raised the bound
   // no value of the tile reaches this wave's bound: nothing to do (no LDS)
   if (L.thr != 0u && __builtin_amdgcn_ballot_w64(lmax >= L.pre) == 0ull) return;
-  const uint32_t shv = lds_load_relaxed(&sh.thr[L.li]);
-  if (shv > L.thr) {  // another wave raised the bound
-    L.set_thr(shv);
-    if (__builtin_amdgcn_ballot_w64(lmax >= L.pre) == 0ull) return;
-  }
   if (L.thr == 0u) {  // no bound yet: this tile's own k-th lane maximum
     L.set_thr(tile_bound(v, lmax, L.k, L.T));
     if (lane() == 0) atomicMax(&sh.thr[L.li], L.thr);
@@ -388,18 +401,15 @@ __device__ __forceinline__ void list_tile(const float (&v)[kVals], const float (
   for (int gi = 0; gi < kGroups; ++gi)
     if (__builtin_amdgcn_ballot_w64(g[gi] >= L.pre) != 0ull) active |= 1u << gi;
   if (!active) return;
-  const int n = extract<E, false>(v, g, active, tile_base, V, vec, L.thr, L.pre, L.T, nullptr);
-  if (n == 0) return;
-  int base = 0;
-  if (lane() == 0) base = atomicAdd(&sh.merge_n[L.li], n);
-  base = __shfl(base, 0);
-  if (base + n > kPoolCap) {  // the pool is full: the row is selected the slow way
+  int end = 0;
+  const int r = extract<E>(v, active, tile_base, V, vec, L.thr, L.pre, L.T, &sh.merge_n[L.li],
+                           pool, &end);
+  if (r < 0) {  // the pool is full: the row is selected the slow way
     if (lane() == 0) sh.ovf[L.li] = 1;
     return;
   }
-  extract<E, true>(v, g, active, tile_base, V, vec, L.thr, L.pre, L.T, pool + base);
-  if ((base + n) / kCheck > base / kCheck) {
-    const uint32_t nb = pool_kth(pool, base + n, L.k);
+  if (r > 0) {
+    const uint32_t nb = pool_kth(pool, end, L.k);
     if (nb > L.thr) {
       L.set_thr(nb);
       if (lane() == 0) atomicMax(&sh.thr[L.li], nb);
@@ -551,15 +561,17 @@ __device__ __forceinline__ void rescan_list(const E* __restrict__ rowp, int V, b
   __syncthreads();
 }
 
-// Finishes a row from its segment results with one wave: the same outputs the
-// row kernel writes (draw, kept count, status, log-sum-exp, the log-probs of
-// the sampled or given id and the top-k log-probs). (M, S) is the row's
-// log-sum-exp partial and bA, bB its argmax for argmax lists. Every load comes
-// before the first store: a load issued after stores waits for them too.
+// Finishes a row from its segment results: the same outputs the row kernel
+// writes. A wave with role bit 1 writes the draw, kept count, status,
+// log-sum-exp and the log-prob of the sampled or given id; one with role bit
+// 2 writes the top-k log-probs (two waves can share the work). (M, S) is the
+// row's log-sum-exp partial and bA, bB its argmax for argmax lists; q, when
+// given, holds -log(u) for list A's sorted entries. Every load comes before
+// the first store: a load issued after stores waits for them too.
 template <typename E>
 __device__ __forceinline__ void finish_row(const Job& j, int row, const Plan& pl, SegSh& sh,
                                            uint32_t flags, int nA, int nB, float M, float S,
-                                           uint64_t bA, uint64_t bB) {
+                                           uint64_t bA, uint64_t bB, int role, const double* q) {
   const int l = lane();
   const float nanv = __builtin_nanf("");
   const RowCfg& c = pl.c;
@@ -571,7 +583,7 @@ __device__ __forceinline__ void finish_row(const Job& j, int row, const Plan& pl
   int status = 0;
   int32_t id = -1, kept = 0;
   float x_id = nanv;
-  if (j.sample) {
+  if ((role & 1) && j.sample) {
     status = c.status | (bad_logits ? VS_ROW_BAD_LOGITS : 0);
     if (pl.kA == 1 && bA == 0ull) status |= VS_ROW_BAD_LOGITS;
     if (status == 0) {
@@ -584,7 +596,7 @@ __device__ __forceinline__ void finish_row(const Job& j, int row, const Plan& pl
         id = pid(bA);
         kept = 1;
       } else {  // top-k <= 64
-        status = wave_draw(sh.srt[0], nA < pl.kA ? nA : pl.kA, c, row, &id, &kept, nullptr);
+        status = wave_draw(sh.srt[0], nA < pl.kA ? nA : pl.kA, c, row, &id, &kept, nullptr, q);
       }
     }
     if (status || id < 0 || id >= j.V) {
@@ -602,7 +614,7 @@ __device__ __forceinline__ void finish_row(const Job& j, int row, const Plan& pl
         const uint64_t P = sh.srt[0][l];
         const uint64_t hit = __ballot(l < nA && P != 0ull && pid(P) == id);
         if (hit) {
-          x_id = key2f(pkey(__shfl(P, __ffsll(static_cast<unsigned long long>(hit)) - 1)));
+          x_id = key2f(pkey(readlane_u64(P, __ffsll(static_cast<unsigned long long>(hit)) - 1)));
           x_known = true;
         }
       }
@@ -612,7 +624,7 @@ __device__ __forceinline__ void finish_row(const Job& j, int row, const Plan& pl
   // the given id (vs_logprobs)
   int lp_st = bad_logits ? VS_ROW_BAD_LOGITS : 0;
   float x_tok = nanv;
-  if (j.lse && !j.sample && j.tok) {
+  if ((role & 1) && j.lse && !j.sample && j.tok) {
     const int tok = j.tok[row];
     if (tok < 0 || tok >= j.V)
       lp_st |= VS_ROW_BAD_TOKEN_ID;
@@ -622,7 +634,7 @@ __device__ __forceinline__ void finish_row(const Job& j, int row, const Plan& pl
   // the top-k log-probabilities' source
   uint64_t P = 0ull;
   int n = 0;
-  if (j.lse && j.k_lp > 0 && !bad_logits) {
+  if ((role & 2) && j.lse && j.k_lp > 0 && !bad_logits) {
     if (pl.shared && pl.kA == 1) {  // k == 1: the argmax of list A
       n = 1;
       P = bA;
@@ -639,7 +651,7 @@ __device__ __forceinline__ void finish_row(const Job& j, int row, const Plan& pl
   }
 
   // stores
-  if (l == 0) {
+  if ((role & 1) && l == 0) {
     if (j.lse) j.rlse[row] = bad_logits ? make_float2(nanv, nanv) : make_float2(M, logS);
     if (j.sample) {
       j.desc[row].mode = kRowDone;
@@ -652,7 +664,7 @@ __device__ __forceinline__ void finish_row(const Job& j, int row, const Plan& pl
       if (j.out_lp_status) j.out_lp_status[row] = lp_st;
     }
   }
-  if (j.lse && j.k_lp > 0 && l < j.k_lp) {
+  if ((role & 2) && j.lse && j.k_lp > 0 && l < j.k_lp) {
     const int k = j.k_lp;
     const bool has = l < n && P != 0ull;
     j.out_lp_ids[static_cast<size_t>(row) * k + l] = has ? pid(P) : -1;
@@ -719,6 +731,11 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
   auto step = [&](const float (&v)[kVals], const float (&g)[kGroups], float lmax, int tt,
                   bool vec) __attribute__((always_inline)) {
     const int tile_base = tt * kSelTile;
+    // the shared bounds, read now so that the LDS latency hides behind the work below
+    const uint32_t shvA =
+        pl.kA > 1 ? __hip_atomic_load(&sh.thr[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) : 0u;
+    const uint32_t shvB =
+        pl.kB > 1 ? __hip_atomic_load(&sh.thr[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) : 0u;
     bad_l = bad_l || !(lmax < kInf);
     fin_l = fin_l || lmax > -kInf;
 
@@ -771,8 +788,8 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
         }
       }
     }
-    if (pl.kA > 1) list_tile<E>(v, g, lmax, tile_base, j.V, vec, LA, sh, sh.pool[0]);
-    if (pl.kB > 1) list_tile<E>(v, g, lmax, tile_base, j.V, vec, LB, sh, sh.pool[1]);
+    if (pl.kA > 1) list_tile<E>(v, g, lmax, tile_base, j.V, vec, LA, shvA, sh, sh.pool[0]);
+    if (pl.kB > 1) list_tile<E>(v, g, lmax, tile_base, j.V, vec, LB, shvB, sh, sh.pool[1]);
   };
   const bool pf = j.aligned && j.V >= kSelTile;  // full tiles exist: element 0 starts one
   const int tf_end = pf ? min(t_end, j.V / kSelTile) : t_begin;  // this segment's full tiles
@@ -783,7 +800,7 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
   auto claim = [&]() __attribute__((always_inline)) {
     int c = 0;
     if (l == 0) c = atomicAdd(&sh.next_tile, 1);
-    return __shfl(c, 0);
+    return __builtin_amdgcn_readfirstlane(c);
   };
   const int t0 = t_begin + w;
   int ta = t0;
@@ -900,10 +917,28 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
   uint32_t meta = sh.flags;
   uint32_t kthA = 0u, kthB = 0u;
   int nA = 0, nB = 0;
+  // the segment totals, by the last wave while the others start the merge
+  if (w == W - 1) {
+    const float mi = l < W ? sh.wm[l] : -kInf;
+    const float M = wave_max_dpp(mi);
+    const float S = wave_sum_dpp((j.lse && mi > -kInf) ? sh.ws[l] * __expf(mi - M) : 0.0f);
+    uint64_t bA = 0ull, bB = 0ull;
+    if (pl.kA == 1) bA = wave_max_u64_dpp(l < W ? sh.best[0][l] : 0ull);
+    if (pl.kB == 1) bB = wave_max_u64_dpp(l < W ? sh.best[1][l] : 0ull);
+    if (l == 0) {
+      sh.tot_m = M;
+      sh.tot_s = S;
+      sh.tot_b[0] = bA;
+      sh.tot_b[1] = bB;
+    }
+  }
   const bool rsA = finish && pl.kA > 1 && (sh.ovf[0] || sh.merge_n[0] > kPoolCap);
   const bool rsB = finish && pl.kB > 1 && (sh.ovf[1] || sh.merge_n[1] > kPoolCap);
-  if (pl.kA > 1 && !rsA) nA = merge_list(sh, 0, pl.kA, W, !finish, &kthA);
-  if (pl.kB > 1 && !rsB) nB = merge_list(sh, 1, pl.kB, W, !finish, &kthB);
+  // list A of a finished sampling row feeds the draw: its noise comes with the merge
+  const int qk = (finish && j.sample && pl.kA > 1 && !rsA) ? pl.kA : 0;
+  const uint64_t qstate = qk ? row_stream(pl.c.seed, row) : 0ull;
+  if (pl.kA > 1 && !rsA) nA = merge_list(sh, 0, pl.kA, W, !finish, &kthA, qk, qstate);
+  if (pl.kB > 1 && !rsB) nB = merge_list(sh, 1, pl.kB, W, !finish, &kthB, 0, 0ull);
   if (rsA || rsB) {  // rare: one copy of the rescan serves both lists
 #pragma unroll 1
     for (int li = 0; li < 2; ++li) {
@@ -913,31 +948,32 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
     if (rsA) nA = pl.kA;
     if (rsB) nB = pl.kB;
   }
+  __syncthreads();  // the totals (and the merged lists) are visible to every wave
   if (pl.kA > 1) meta |= (nA < 0) ? kMetaOverflowA : static_cast<uint32_t>(nA);
   if (pl.kB > 1) meta |= (nB < 0) ? kMetaOverflowB : (static_cast<uint32_t>(nB) << kMetaCountBShift);
-  if (w == 0) {  // the segment totals, across wave 0's lanes
-    const float mi = l < W ? sh.wm[l] : -kInf;
-    const float M = wave_max_dpp(mi);
-    const float S = wave_sum_dpp((j.lse && mi > -kInf) ? sh.ws[l] * __expf(mi - M) : 0.0f);
-    const uint64_t bA = wave_max_u64_dpp(l < W ? sh.best[0][l] : 0ull);
-    const uint64_t bB = wave_max_u64_dpp(l < W ? sh.best[1][l] : 0ull);
-    if (pl.kA == 1 && bA) meta |= 1u;
-    if (pl.kB == 1 && bB) meta |= 1u << kMetaCountBShift;
-    if (finish) {
-      finish_row<E>(j, row, pl, sh, meta, nA, nB, M, S, bA, bB);
-    } else if (l == 0) {
-      if (j.lse) j.lpart[slot] = LsePart{M, S};
-      if (pl.kA == 1) {
-        if (bA) j.candA[slot * kSelCap] = bA;
-        j.kthA[slot] = pkey(bA);  // the segment maximum: its 1st-largest key
-      }
-      if (pl.kB == 1) {
-        if (bB) j.candB[slot * kSelCap] = bB;
-        j.kthB[slot] = pkey(bB);
-      }
+  const float M = sh.tot_m, S = sh.tot_s;
+  const uint64_t bA = sh.tot_b[0], bB = sh.tot_b[1];
+  if (pl.kA == 1 && bA) meta |= 1u;
+  if (pl.kB == 1 && bB) meta |= 1u << kMetaCountBShift;
+  if (finish) {
+    // wave 0 draws and writes the row's scalars while wave 1 writes the top-k
+    // log-probs (one wave does both in a one-wave workgroup)
+    const int wl = W > 1 ? 1 : 0;
+    if (w == 0 || w == wl)
+      finish_row<E>(j, row, pl, sh, meta, nA, nB, M, S, bA, bB, (w == 0 ? 1 : 0) | (w == wl ? 2 : 0),
+                    qk ? sh.srt_q : nullptr);
+  } else if (w == 0 && l == 0) {
+    if (j.lse) j.lpart[slot] = LsePart{M, S};
+    if (pl.kA == 1) {
+      if (bA) j.candA[slot * kSelCap] = bA;
+      j.kthA[slot] = pkey(bA);  // the segment maximum: its 1st-largest key
     }
-    if (l == 0) j.meta[slot] = meta | (finish ? kMetaFinal : 0u);
+    if (pl.kB == 1) {
+      if (bB) j.candB[slot * kSelCap] = bB;
+      j.kthB[slot] = pkey(bB);
+    }
   }
+  if (w == 0 && l == 0) j.meta[slot] = meta | (finish ? kMetaFinal : 0u);
   if (!finish) {  // the lists' candidates, for the row kernel
     for (int i = threadIdx.x; i < nA; i += NT) j.candA[slot * kSelCap + i] = sh.top[0][i];
     for (int i = threadIdx.x; i < nB; i += NT) j.candB[slot * kSelCap + i] = sh.top[1][i];

@@ -356,6 +356,25 @@ __device__ __forceinline__ int wave_min_dpp(int v) {
              min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 
+// Inclusive prefix sum of a u32 over the 64 lanes in lane order (every lane
+// active; the caller keeps the sums below 2^32). Within each row of 16 lanes:
+// the shifts by 1, 2 and 3 of the inputs give 4-lane window sums, then the
+// shifts by 4 (banks 1-3) and by 8 (banks 2-3) of the running sums complete
+// the row; the row broadcasts of lane 15 (into rows 1 and 3) and of lane 31
+// (into rows 2 and 3) carry the totals across rows (gfx9 DPP encodings).
+__device__ __forceinline__ uint32_t wave_scan_incl_u32(uint32_t v) {
+  const int x0 = static_cast<int>(v);
+  int x = x0;
+  x += __builtin_amdgcn_update_dpp(0, x0, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x0, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x0, 0x113, 0xF, 0xF, false);  // row_shr:3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xE, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xC, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31
+  return static_cast<uint32_t>(x);
+}
+
 // k-th largest (1-based, 1 <= k <= 64) of one uint32 per lane, every lane of
 // the wave active: MSB-first radix select on ballots (32 rounds of one vector
 // compare and scalar bit counts; no LDS traffic).
@@ -461,11 +480,13 @@ __device__ __forceinline__ T wave_merge_top_desc(T a, T b) {
 // s = x / T) with one wave, no block barrier; call from every lane of one wave.
 // min-p keeps e = E(s - m) >= min_p; top-p keeps the shortest prefix whose
 // fixed-point mass reaches p times the kept mass; the draw is the Gumbel-max
-// argmax of e / -log(u) over the kept set, ties to the lowest id. Returns the
-// status (VS_ROW_BAD_LOGITS for an empty list, VS_ROW_BAD_PARAM when s = +inf).
-// Called by a whole wave, every lane active.
+// argmax of e / -log(u) over the kept set, ties to the lowest id. q, when
+// given, holds -log(u) of the candidates (the same values this function would
+// compute). Returns the status (VS_ROW_BAD_LOGITS for an empty list,
+// VS_ROW_BAD_PARAM when s = +inf). Called by a whole wave, every lane active.
 __device__ inline int wave_draw(const uint64_t* L, int n, const RowCfg& c, int row,
-                                int32_t* id_out, int32_t* kept_out, uint32_t* mask_row) {
+                                int32_t* id_out, int32_t* kept_out, uint32_t* mask_row,
+                                const double* q = nullptr) {
   const int i = lane();
   if (n <= 0) return VS_ROW_BAD_LOGITS;  // no candidate: never read an id from it
   const uint64_t top = L[0];
@@ -478,16 +499,17 @@ __device__ inline int wave_draw(const uint64_t* L, int n, const RowCfg& c, int r
   const int id = has ? pid(P) : 0x7fffffff;
   // every candidate's score, computed before the cut is known so that the two
   // overlap; nonnegative, so its bits order as integers
-  const double sc = has ? gumbel_score(e, row_stream(c.seed, row), id) : 0.0;
+  double sc = 0.0;
+  if (has) sc = q ? static_cast<double>(e) / q[i] : gumbel_score(e, row_stream(c.seed, row), id);
   bool kept = in_s;
   if (c.p < 1.0f) {
-    uint64_t cum = in_s ? mass_of(e) : 0ull;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const uint64_t w = __shfl_up(cum, o);
-      if (i >= o) cum += w;
-    }
-    const uint64_t tw = __shfl(cum, kWave - 1);
+    // fixed-point masses (< 2^31 + 1) scanned as 16-bit halves, whose sums
+    // over 64 lanes fit in 32 bits
+    const uint32_t w = in_s ? static_cast<uint32_t>(mass_of(e)) : 0u;
+    const uint32_t lo = wave_scan_incl_u32(w & 0xffffu);
+    const uint32_t hi = wave_scan_incl_u32(w >> 16);
+    const uint64_t cum = (static_cast<uint64_t>(hi) << 16) + lo;
+    const uint64_t tw = readlane_u64(cum, kWave - 1);
     const double thr = static_cast<double>(c.p) * static_cast<double>(tw);
     const uint64_t hit = __ballot(in_s && static_cast<double>(cum) >= thr);
     const int cut = hit ? __ffsll(static_cast<unsigned long long>(hit)) - 1 : kWave;
