@@ -276,8 +276,8 @@ struct SegSh {
   float ws[16];
   uint64_t best[2][16];
   uint64_t top[2][kSelCap];  // each list's segment candidates
-  uint64_t srt[2][kWave];    // a list's 64 best, sorted (finishing a row)
-  double srt_q[kWave];       // -log(u) of list A's sorted entries, for the draw
+  uint64_t srt[2][kWave];    // a list's 64 best, sorted (segments handed on; rescans)
+  double q[kPoolCap];        // list A's pool: -log(u) of the entries reaching the bound
   float tot_m, tot_s;        // the segment's log-sum-exp partial
   uint64_t tot_b[2];         // the segment's argmax per argmax list
   uint32_t rank[2][kPoolCap];  // each pool entry's rank, summed over the waves' slices
@@ -292,13 +292,12 @@ struct SegSh {
 // so it is the entry's sorted position, and the entry of rank k - 1 holds the
 // k-th key. Every wave counts one slice of the pool against all entries and
 // adds its counts to sh.rank (zero at the start), so the count is spread over
-// the block. For the first qk sorted entries the draw's -log(u) (random stream
-// state qstate) goes to sh.srt_q. Returns the number gathered (without `out`: the number of sorted
+// the block. Returns the number gathered (without `out`: the number of sorted
 // entries the list needs, min(n, k)), or -1 on overflow. Called by the whole
 // block (W waves) after the streaming loop; nothing here touches global
 // memory, so no wait on the memory system is taken.
 __device__ __forceinline__ int merge_list(SegSh& sh, int li, int k, int W, bool out,
-                                          uint32_t* kth, int qk, uint64_t qstate) {
+                                          uint32_t* kth) {
   const int l = lane();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int NT = W * kWave;
@@ -330,11 +329,7 @@ __device__ __forceinline__ int merge_list(SegSh& sh, int li, int k, int W, bool 
   for (int i = threadIdx.x; i < n; i += NT) {
     const int r = static_cast<int>(rank[i]);
     const uint64_t e = pool[i];
-    if (r < kWave) {
-      sh.srt[li][r] = e;
-      // the draw's exponential noise, computed here by many threads at once
-      if (r < qk) sh.srt_q[r] = -log(uniform_of(qstate, pid(e)));
-    }
+    if (r < kWave) sh.srt[li][r] = e;
     if (r == k - 1) sh.kth_key[li] = pkey(e);
   }
   __syncthreads();
@@ -561,17 +556,76 @@ __device__ __forceinline__ void rescan_list(const E* __restrict__ rowp, int V, b
   __syncthreads();
 }
 
-// Finishes a row from its segment results: the same outputs the row kernel
-// writes. A wave with role bit 1 writes the draw, kept count, status,
-// log-sum-exp and the log-prob of the sampled or given id; one with role bit
-// 2 writes the top-k log-probs (two waves can share the work). (M, S) is the
-// row's log-sum-exp partial and bA, bB its argmax for argmax lists; q, when
-// given, holds -log(u) for list A's sorted entries. Every load comes before
-// the first store: a load issued after stores waits for them too.
+// A pool entry with its pool position i in the low bits, ordered as the entry:
+// the key, then 0x1fffff - id (ids are below 2^21), then i (11 bits).
+constexpr int kTagBits = 11;
+static_assert(kPoolCap <= (1 << kTagBits), "pool positions fit the tag");
+__device__ __forceinline__ uint64_t tag_entry(uint64_t e, int i) {
+  const uint32_t rid = 0x1fffffu - static_cast<uint32_t>(pid(e));
+  return (static_cast<uint64_t>(pkey(e)) << 32) | (static_cast<uint64_t>(rid) << kTagBits) |
+         static_cast<uint32_t>(i);
+}
+__device__ __forceinline__ uint64_t untag_entry(uint64_t t) {
+  if (t == 0ull) return 0ull;
+  const int32_t id = static_cast<int32_t>(0x1fffffu - ((static_cast<uint32_t>(t) >> kTagBits) & 0x1fffffu));
+  return pack(static_cast<uint32_t>(t >> 32), id);
+}
+__device__ __forceinline__ int tag_pos(uint64_t t) {
+  return static_cast<int>(static_cast<uint32_t>(t) & ((1u << kTagBits) - 1u));
+}
+
+// The best entries of a list's pool (n entries, unused slots 0) whose key
+// reaches the bound thr, sorted descending across the lanes of one wave (lane
+// i the i-th; 0 past the end), as tagged entries (tag_entry) when kTag; *cnt
+// gets how many reach thr. Every entry of the row's top k reaches a valid
+// bound, and every value that reaches the final bound entered the pool, so the
+// result starts with the row's top k. Usually at most 64 entries reach it:
+// they are compacted through the wave's LDS stage and sorted in registers.
+// Otherwise the pool's chunks are sorted and merged one by one. Called by a
+// whole wave, every lane active.
+template <bool kTag>
+__device__ __forceinline__ uint64_t wave_top_of_pool(const uint64_t* pool, int n, uint32_t thr,
+                                                     uint64_t* stage, int* cnt) {
+  const int l = lane();
+  int total = 0;
+  for (int c0 = 0; c0 < n; c0 += kWave) {  // uniform
+    const int i = c0 + l;
+    uint64_t e = i < n ? pool[i] : 0ull;
+    const bool keep = e != 0ull && pkey(e) >= thr;
+    if (kTag && keep) e = tag_entry(e, i);
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+    const int at = total + lanes_below(bal);
+    if (keep && at < kWave) stage[at] = e;
+    total += __popcll(bal);
+  }
+  *cnt = total;
+  if (total <= kWave) {
+    wave_lds_wait();
+    return wave_sort_u64<true>(l < total ? stage[l] : 0ull);
+  }
+  uint64_t top = 0ull;
+  for (int c0 = 0; c0 < n; c0 += kWave) {  // uniform
+    const int i = c0 + l;
+    uint64_t e = i < n ? pool[i] : 0ull;
+    if (e == 0ull || pkey(e) < thr) e = 0ull;
+    if (kTag && e != 0ull) e = tag_entry(e, i);
+    if (__builtin_amdgcn_ballot_w64(e != 0ull) == 0ull) continue;
+    top = wave_merge_top_u64(top, wave_sort_u64<false>(e));
+  }
+  return top;
+}
+
+// Finishes a row with one wave: the same outputs the row kernel writes (draw,
+// kept count, status, log-sum-exp, the log-probs of the sampled or given id and
+// the top-k log-probs). LA and LB hold the lists' best entries sorted across
+// the lanes (lane i the i-th, nA and nB of them); (M, S) is the row's
+// log-sum-exp partial and bA, bB its argmax for argmax lists; qA, when given,
+// holds -log(u) of list A's entries by lane. Every load comes before the first
+// store: a load issued after stores waits for them too.
 template <typename E>
-__device__ __forceinline__ void finish_row(const Job& j, int row, const Plan& pl, SegSh& sh,
-                                           uint32_t flags, int nA, int nB, float M, float S,
-                                           uint64_t bA, uint64_t bB, int role, const double* q) {
+__device__ __forceinline__ void finish_row(const Job& j, int row, const Plan& pl, uint32_t flags,
+                                           uint64_t LA, int nA, uint64_t LB, int nB, float M,
+                                           float S, uint64_t bA, uint64_t bB, const double* qA) {
   const int l = lane();
   const float nanv = __builtin_nanf("");
   const RowCfg& c = pl.c;
@@ -583,7 +637,7 @@ __device__ __forceinline__ void finish_row(const Job& j, int row, const Plan& pl
   int status = 0;
   int32_t id = -1, kept = 0;
   float x_id = nanv;
-  if ((role & 1) && j.sample) {
+  if (j.sample) {
     status = c.status | (bad_logits ? VS_ROW_BAD_LOGITS : 0);
     if (pl.kA == 1 && bA == 0ull) status |= VS_ROW_BAD_LOGITS;
     if (status == 0) {
@@ -596,7 +650,7 @@ __device__ __forceinline__ void finish_row(const Job& j, int row, const Plan& pl
         id = pid(bA);
         kept = 1;
       } else {  // top-k <= 64
-        status = wave_draw(sh.srt[0], nA < pl.kA ? nA : pl.kA, c, row, &id, &kept, nullptr, q);
+        status = wave_draw_lanes(LA, nA < pl.kA ? nA : pl.kA, c, row, &id, &kept, nullptr, qA);
       }
     }
     if (status || id < 0 || id >= j.V) {
@@ -611,10 +665,9 @@ __device__ __forceinline__ void finish_row(const Job& j, int row, const Plan& pl
         x_id = key2f(pkey(bA));
         x_known = true;
       } else if (pl.TA == 1.0f) {
-        const uint64_t P = sh.srt[0][l];
-        const uint64_t hit = __ballot(l < nA && P != 0ull && pid(P) == id);
+        const uint64_t hit = __ballot(l < nA && LA != 0ull && pid(LA) == id);
         if (hit) {
-          x_id = key2f(pkey(readlane_u64(P, __ffsll(static_cast<unsigned long long>(hit)) - 1)));
+          x_id = key2f(pkey(readlane_u64(LA, __ffsll(static_cast<unsigned long long>(hit)) - 1)));
           x_known = true;
         }
       }
@@ -624,7 +677,7 @@ __device__ __forceinline__ void finish_row(const Job& j, int row, const Plan& pl
   // the given id (vs_logprobs)
   int lp_st = bad_logits ? VS_ROW_BAD_LOGITS : 0;
   float x_tok = nanv;
-  if ((role & 1) && j.lse && !j.sample && j.tok) {
+  if (j.lse && !j.sample && j.tok) {
     const int tok = j.tok[row];
     if (tok < 0 || tok >= j.V)
       lp_st |= VS_ROW_BAD_TOKEN_ID;
@@ -634,24 +687,24 @@ __device__ __forceinline__ void finish_row(const Job& j, int row, const Plan& pl
   // the top-k log-probabilities' source
   uint64_t P = 0ull;
   int n = 0;
-  if ((role & 2) && j.lse && j.k_lp > 0 && !bad_logits) {
+  if (j.lse && j.k_lp > 0 && !bad_logits) {
     if (pl.shared && pl.kA == 1) {  // k == 1: the argmax of list A
       n = 1;
       P = bA;
     } else if (pl.shared) {
       n = nA;
-      P = sh.srt[0][l];
+      P = LA;
     } else if (pl.kB == 1) {
       n = 1;
       P = bB;
     } else {
       n = nB;
-      P = sh.srt[1][l];
+      P = LB;
     }
   }
 
   // stores
-  if ((role & 1) && l == 0) {
+  if (l == 0) {
     if (j.lse) j.rlse[row] = bad_logits ? make_float2(nanv, nanv) : make_float2(M, logS);
     if (j.sample) {
       j.desc[row].mode = kRowDone;
@@ -664,7 +717,7 @@ __device__ __forceinline__ void finish_row(const Job& j, int row, const Plan& pl
       if (j.out_lp_status) j.out_lp_status[row] = lp_st;
     }
   }
-  if ((role & 2) && j.lse && j.k_lp > 0 && l < j.k_lp) {
+  if (j.lse && j.k_lp > 0 && l < j.k_lp) {
     const int k = j.k_lp;
     const bool has = l < n && P != 0ull;
     j.out_lp_ids[static_cast<size_t>(row) * k + l] = has ? pid(P) : -1;
@@ -915,6 +968,86 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
                       (!j.sample || hinted || pl.c.mode == kModeGreedy ||
                        pl.c.mode == kModeKFast || pl.c.mode == kModeInvalid);
   uint32_t meta = sh.flags;
+  if (finish) {
+    // A list whose pool overflowed is rebuilt by a rescan of the row (every
+    // wave). Then the waves split the closing work: wave 0 sorts each list's
+    // best entries in registers; wave 1 reduces the row totals; the others
+    // compute the draw's exponential noise of list A's entries that reach the
+    // final bound, by pool position. After one barrier wave 0 draws and writes
+    // the row; the other waves are done.
+    const bool rsA = pl.kA > 1 && (sh.ovf[0] || sh.merge_n[0] > kPoolCap);
+    const bool rsB = pl.kB > 1 && (sh.ovf[1] || sh.merge_n[1] > kPoolCap);
+    if (rsA || rsB) {  // rare: one copy of the rescan serves both lists
+#pragma unroll 1
+      for (int li = 0; li < 2; ++li) {
+        if (li == 0 ? rsA : rsB)
+          rescan_list<E>(rowp, j.V, j.aligned, li == 0 ? pl.TA : 1.0f, W, sh.stage, sh.srt[li]);
+      }
+    }
+    const bool noise = j.sample && pl.kA > 1 && !rsA && W > 2;  // the table is filled
+    const int wt = W > 1 ? 1 : 0;                               // the wave reducing the totals
+    uint64_t LA = 0ull, LB = 0ull;
+    int nA = 0, nB = 0;
+    if (w == 0) {
+      if (pl.kA > 1) {
+        int cnt = pl.kA;
+        if (rsA)
+          LA = sh.srt[0][l];
+        else if (noise)
+          LA = wave_top_of_pool<true>(sh.pool[0], sh.merge_n[0], sh.thr[0], sh.stage[0], &cnt);
+        else
+          LA = wave_top_of_pool<false>(sh.pool[0], sh.merge_n[0], sh.thr[0], sh.stage[0], &cnt);
+        nA = cnt < pl.kA ? cnt : pl.kA;
+      }
+      if (pl.kB > 1) {
+        int cnt = pl.kB;
+        LB = rsB ? sh.srt[1][l]
+                 : wave_top_of_pool<false>(sh.pool[1], sh.merge_n[1], sh.thr[1], sh.stage[1], &cnt);
+        nB = cnt < pl.kB ? cnt : pl.kB;
+      }
+    }
+    if (w == wt) {
+      const float mi = l < W ? sh.wm[l] : -kInf;
+      const float M = wave_max_dpp(mi);
+      const float S = wave_sum_dpp((j.lse && mi > -kInf) ? sh.ws[l] * __expf(mi - M) : 0.0f);
+      const uint64_t bA = (pl.kA == 1) ? wave_max_u64_dpp(l < W ? sh.best[0][l] : 0ull) : 0ull;
+      const uint64_t bB = (pl.kB == 1) ? wave_max_u64_dpp(l < W ? sh.best[1][l] : 0ull) : 0ull;
+      if (l == 0) {
+        sh.tot_m = M;
+        sh.tot_s = S;
+        sh.tot_b[0] = bA;
+        sh.tot_b[1] = bB;
+      }
+    }
+    if (noise && w >= 2) {
+      const uint64_t rs = row_stream(pl.c.seed, row);
+      const uint32_t thr = sh.thr[0];
+      const int n = sh.merge_n[0];
+      for (int i = (w - 2) * kWave + l; i < n; i += (W - 2) * kWave) {
+        const uint64_t e = sh.pool[0][i];
+        if (pkey(e) >= thr) sh.q[i] = -log(uniform_of(rs, pid(e)));
+      }
+    }
+    __syncthreads();
+    if (w != 0) return;
+    double q = 1.0;
+    if (noise) {
+      q = (LA != 0ull) ? sh.q[tag_pos(LA)] : 1.0;
+      LA = untag_entry(LA);
+    }
+    const float M = sh.tot_m, S = sh.tot_s;
+    const uint64_t bA = sh.tot_b[0], bB = sh.tot_b[1];
+    if (pl.kA > 1) meta |= static_cast<uint32_t>(nA);
+    if (pl.kB > 1) meta |= static_cast<uint32_t>(nB) << kMetaCountBShift;
+    if (pl.kA == 1 && bA) meta |= 1u;
+    if (pl.kB == 1 && bB) meta |= 1u << kMetaCountBShift;
+    sh.stage[0][l] = __double_as_longlong(q);  // the noise by lane, for the draw
+    wave_lds_wait();
+    finish_row<E>(j, row, pl, meta, LA, nA, LB, nB, M, S, bA, bB,
+                  noise ? reinterpret_cast<const double*>(sh.stage[0]) : nullptr);
+    if (l == 0) j.meta[slot] = meta | kMetaFinal;
+    return;
+  }
   uint32_t kthA = 0u, kthB = 0u;
   int nA = 0, nB = 0;
   // the segment totals, by the last wave while the others start the merge
@@ -932,37 +1065,16 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
       sh.tot_b[1] = bB;
     }
   }
-  const bool rsA = finish && pl.kA > 1 && (sh.ovf[0] || sh.merge_n[0] > kPoolCap);
-  const bool rsB = finish && pl.kB > 1 && (sh.ovf[1] || sh.merge_n[1] > kPoolCap);
-  // list A of a finished sampling row feeds the draw: its noise comes with the merge
-  const int qk = (finish && j.sample && pl.kA > 1 && !rsA) ? pl.kA : 0;
-  const uint64_t qstate = qk ? row_stream(pl.c.seed, row) : 0ull;
-  if (pl.kA > 1 && !rsA) nA = merge_list(sh, 0, pl.kA, W, !finish, &kthA, qk, qstate);
-  if (pl.kB > 1 && !rsB) nB = merge_list(sh, 1, pl.kB, W, !finish, &kthB, 0, 0ull);
-  if (rsA || rsB) {  // rare: one copy of the rescan serves both lists
-#pragma unroll 1
-    for (int li = 0; li < 2; ++li) {
-      if (li == 0 ? rsA : rsB)
-        rescan_list<E>(rowp, j.V, j.aligned, li == 0 ? pl.TA : 1.0f, W, sh.stage, sh.srt[li]);
-    }
-    if (rsA) nA = pl.kA;
-    if (rsB) nB = pl.kB;
-  }
-  __syncthreads();  // the totals (and the merged lists) are visible to every wave
+  if (pl.kA > 1) nA = merge_list(sh, 0, pl.kA, W, true, &kthA);
+  if (pl.kB > 1) nB = merge_list(sh, 1, pl.kB, W, true, &kthB);
+  __syncthreads();  // the totals are visible to every wave
   if (pl.kA > 1) meta |= (nA < 0) ? kMetaOverflowA : static_cast<uint32_t>(nA);
   if (pl.kB > 1) meta |= (nB < 0) ? kMetaOverflowB : (static_cast<uint32_t>(nB) << kMetaCountBShift);
   const float M = sh.tot_m, S = sh.tot_s;
   const uint64_t bA = sh.tot_b[0], bB = sh.tot_b[1];
   if (pl.kA == 1 && bA) meta |= 1u;
   if (pl.kB == 1 && bB) meta |= 1u << kMetaCountBShift;
-  if (finish) {
-    // wave 0 draws and writes the row's scalars while wave 1 writes the top-k
-    // log-probs (one wave does both in a one-wave workgroup)
-    const int wl = W > 1 ? 1 : 0;
-    if (w == 0 || w == wl)
-      finish_row<E>(j, row, pl, sh, meta, nA, nB, M, S, bA, bB, (w == 0 ? 1 : 0) | (w == wl ? 2 : 0),
-                    qk ? sh.srt_q : nullptr);
-  } else if (w == 0 && l == 0) {
+  if (w == 0 && l == 0) {
     if (j.lse) j.lpart[slot] = LsePart{M, S};
     if (pl.kA == 1) {
       if (bA) j.candA[slot * kSelCap] = bA;
@@ -972,15 +1084,14 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
       if (bB) j.candB[slot * kSelCap] = bB;
       j.kthB[slot] = pkey(bB);
     }
+    j.meta[slot] = meta;
   }
-  if (w == 0 && l == 0) j.meta[slot] = meta | (finish ? kMetaFinal : 0u);
-  if (!finish) {  // the lists' candidates, for the row kernel
-    for (int i = threadIdx.x; i < nA; i += NT) j.candA[slot * kSelCap + i] = sh.top[0][i];
-    for (int i = threadIdx.x; i < nB; i += NT) j.candB[slot * kSelCap + i] = sh.top[1][i];
-    if (threadIdx.x == 0) {
-      if (pl.kA > 1) j.kthA[slot] = kthA;
-      if (pl.kB > 1) j.kthB[slot] = kthB;
-    }
+  // the lists' candidates, for the row kernel
+  for (int i = threadIdx.x; i < nA; i += NT) j.candA[slot * kSelCap + i] = sh.top[0][i];
+  for (int i = threadIdx.x; i < nB; i += NT) j.candB[slot * kSelCap + i] = sh.top[1][i];
+  if (threadIdx.x == 0) {
+    if (pl.kA > 1) j.kthA[slot] = kthA;
+    if (pl.kB > 1) j.kthB[slot] = kthB;
   }
 }
 

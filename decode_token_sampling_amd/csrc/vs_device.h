@@ -375,6 +375,87 @@ __device__ __forceinline__ uint32_t wave_scan_incl_u32(uint32_t v) {
   return static_cast<uint32_t>(x);
 }
 
+// The value of lane (this lane XOR J) for J = 1, 2, 4, 8, 16, 32, every lane
+// active: DPP quad permutations for 1 and 2, row shifts into alternate banks
+// for 4, a row rotation by 8, and the gfx950 row-pair and half-wave swaps for
+// 16 and 32 (a copy of the value in both operands, so each lane finds its
+// partner in one of the two results).
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t x) {
+  const int v = static_cast<int>(x);
+  if constexpr (J == 1) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
+  } else if constexpr (J == 2) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
+  } else if constexpr (J == 4) {
+    const int t = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0x5, false);  // row_shl:4, banks 0, 2
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(t, v, 0x114, 0xF, 0xA, false));  // row_shr:4
+  } else if constexpr (J == 8) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false));  // row_ror:8
+  } else if constexpr (J == 16) {
+    const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane() & 16) ? a[0] : a[1];
+  } else {
+    static_assert(J == 32, "lane_xor_u32: J in {1, 2, 4, 8, 16, 32}");
+    const auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane() & 32) ? a[0] : a[1];
+  }
+}
+template <int J>
+__device__ __forceinline__ uint64_t lane_xor_u64(uint64_t x) {
+  const uint32_t lo = lane_xor_u32<J>(static_cast<uint32_t>(x));
+  const uint32_t hi = lane_xor_u32<J>(static_cast<uint32_t>(x >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+// One compare-exchange step of a bitonic network over the 64 lanes (block
+// size K, partner distance J); kDesc: the finished sequence is descending.
+template <int K, int J, bool kDesc>
+__device__ __forceinline__ uint64_t bitonic_step(uint64_t v) {
+  const int l = lane();
+  const uint64_t o = lane_xor_u64<J>(v);
+  const bool keep_max = (((l & K) == 0) == ((l & J) == 0)) == kDesc;
+  return keep_max ? (o > v ? o : v) : (o < v ? o : v);
+}
+// Sorts one u64 per lane across the wave in registers (lane 0 first).
+template <bool kDesc>
+__device__ __forceinline__ uint64_t wave_sort_u64(uint64_t v) {
+  v = bitonic_step<2, 1, kDesc>(v);
+  v = bitonic_step<4, 2, kDesc>(v);
+  v = bitonic_step<4, 1, kDesc>(v);
+  v = bitonic_step<8, 4, kDesc>(v);
+  v = bitonic_step<8, 2, kDesc>(v);
+  v = bitonic_step<8, 1, kDesc>(v);
+  v = bitonic_step<16, 8, kDesc>(v);
+  v = bitonic_step<16, 4, kDesc>(v);
+  v = bitonic_step<16, 2, kDesc>(v);
+  v = bitonic_step<16, 1, kDesc>(v);
+  v = bitonic_step<32, 16, kDesc>(v);
+  v = bitonic_step<32, 8, kDesc>(v);
+  v = bitonic_step<32, 4, kDesc>(v);
+  v = bitonic_step<32, 2, kDesc>(v);
+  v = bitonic_step<32, 1, kDesc>(v);
+  v = bitonic_step<64, 32, kDesc>(v);
+  v = bitonic_step<64, 16, kDesc>(v);
+  v = bitonic_step<64, 8, kDesc>(v);
+  v = bitonic_step<64, 4, kDesc>(v);
+  v = bitonic_step<64, 2, kDesc>(v);
+  v = bitonic_step<64, 1, kDesc>(v);
+  return v;
+}
+// The 64 largest of a (descending across the lanes) and b (ascending),
+// descending: the lane-wise maxima form a bitonic sequence holding them,
+// which the last six steps sort.
+__device__ __forceinline__ uint64_t wave_merge_top_u64(uint64_t a_desc, uint64_t b_asc) {
+  uint64_t v = a_desc > b_asc ? a_desc : b_asc;
+  v = bitonic_step<64, 32, true>(v);
+  v = bitonic_step<64, 16, true>(v);
+  v = bitonic_step<64, 8, true>(v);
+  v = bitonic_step<64, 4, true>(v);
+  v = bitonic_step<64, 2, true>(v);
+  v = bitonic_step<64, 1, true>(v);
+  return v;
+}
+
 // k-th largest (1-based, 1 <= k <= 64) of one uint32 per lane, every lane of
 // the wave active: MSB-first radix select on ballots (32 rounds of one vector
 // compare and scalar bit counts; no LDS traffic).
@@ -480,20 +561,21 @@ __device__ __forceinline__ T wave_merge_top_desc(T a, T b) {
 // s = x / T) with one wave, no block barrier; call from every lane of one wave.
 // min-p keeps e = E(s - m) >= min_p; top-p keeps the shortest prefix whose
 // fixed-point mass reaches p times the kept mass; the draw is the Gumbel-max
-// argmax of e / -log(u) over the kept set, ties to the lowest id. q, when
-// given, holds -log(u) of the candidates (the same values this function would
-// compute). Returns the status (VS_ROW_BAD_LOGITS for an empty list,
-// VS_ROW_BAD_PARAM when s = +inf). Called by a whole wave, every lane active.
-__device__ inline int wave_draw(const uint64_t* L, int n, const RowCfg& c, int row,
-                                int32_t* id_out, int32_t* kept_out, uint32_t* mask_row,
-                                const double* q = nullptr) {
+// argmax of e / -log(u) over the kept set, ties to the lowest id. Lane i holds
+// the i-th candidate P (the list in registers); q, when given, holds -log(u)
+// of the candidates (the same values this function would compute). Returns
+// the status (VS_ROW_BAD_LOGITS for an empty list, VS_ROW_BAD_PARAM when s =
+// +inf). Called by a whole wave, every lane active.
+__device__ inline int wave_draw_lanes(uint64_t P, int n, const RowCfg& c, int row,
+                                      int32_t* id_out, int32_t* kept_out, uint32_t* mask_row,
+                                      const double* q) {
   const int i = lane();
   if (n <= 0) return VS_ROW_BAD_LOGITS;  // no candidate: never read an id from it
-  const uint64_t top = L[0];
+  const uint64_t top = readlane_u64(P, 0);
   if (pkey(top) == kKeyPosInf) return VS_ROW_BAD_PARAM;
   const float m = key2f(pkey(top));
   const bool has = i < n;
-  const uint64_t P = has ? L[i] : 0ull;
+  if (!has) P = 0ull;
   const float e = has ? pinned_exp(key2f(pkey(P)) - m) : 0.0f;
   const bool in_s = has && (e >= c.mp);
   const int id = has ? pid(P) : 0x7fffffff;
@@ -522,6 +604,14 @@ __device__ inline int wave_draw(const uint64_t* L, int n, const RowCfg& c, int r
   *id_out = win;
   *kept_out = __popcll(__ballot(kept));
   return 0;
+}
+// The same with the sorted candidates in memory (LDS).
+__device__ inline int wave_draw(const uint64_t* L, int n, const RowCfg& c, int row,
+                                int32_t* id_out, int32_t* kept_out, uint32_t* mask_row,
+                                const double* q = nullptr) {
+  const int i = lane();
+  const uint64_t P = (i < n) ? L[i] : 0ull;
+  return wave_draw_lanes(P, n, c, row, id_out, kept_out, mask_row, q);
 }
 
 // ---------------------------------------------------------------- block primitives
