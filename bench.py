@@ -290,10 +290,11 @@ def main():
     hip.destroy(pev)
     stage_avg = {k: float(np.mean(v)) for k, v in stage_ms.items()}
 
-    # Dominant kernel: the streaming pass of the draw (one read of the logits),
-    # or the full log-softmax write when the workload asks for it.
-    dom = "lse_full" if wl.full_logprobs else "select"
-    dom_bytes = logit_bytes + (wl.B * wl.V * 4 if dom == "lse_full" else 0)
+    # Dominant kernel: the streaming pass (one read of the logits, plus the
+    # full log-softmax write when the workload asks for it and the pass writes
+    # it itself), or the separate full log-softmax write when one ran.
+    dom = "lse_full" if (wl.full_logprobs and "lse_full" in stage_avg) else "select"
+    dom_bytes = logit_bytes + (wl.B * wl.V * 4 if wl.full_logprobs else 0)
     dom_ms = stage_avg[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     side = 0

@@ -24,6 +24,10 @@
 // with that key; the row kernel merges the segments. A segment whose candidates
 // do not fit sets an overflow flag and the row kernel selects exactly from the
 // row itself.
+// A segment that is a whole row finishes the row itself when its draw needs
+// nothing beyond its candidates (see the closing steps below), and when it
+// finishes every row of a call that asks for the full log-softmax, its waves
+// then write the row's log-probabilities, reading the row a second time.
 #include "vs_device.h"
 #include "vs_kernels.h"
 
@@ -33,7 +37,7 @@ namespace {
 constexpr int kVals = kSelTile / kWave;  // values per lane and tile (32)
 constexpr int kGroup = 4;         // values per group (a lane's maxima are kept per group)
 constexpr int kGroups = kVals / kGroup;
-static_assert(kGroup == 4 && kGroups == 8, "extract() visits 8 groups of 4 values");
+static_assert(kGroup == 4 && kVals % kGroup == 0 && kGroups <= 32, "groups of 4 values, a bit each");
 
 constexpr int kPoolCap = 512;     // candidates per segment and list (the shared pool)
 constexpr int kCheck = 64;        // the pool's bound is recomputed every kCheck entries
@@ -175,29 +179,24 @@ __device__ __forceinline__ int extract_group(const float (&v)[kVals], int tile_b
   return crossed;
 }
 
-// The active groups of the tile (a bit per group whose maximum reaches the
-// prefilter in some lane), each through extract_group. Same result codes.
-template <typename E>
+// The active groups of the tile from group G on (a bit per group whose
+// maximum reaches the prefilter in some lane), each through extract_group.
+// Same result codes.
+template <typename E, int G = 0>
 __device__ __forceinline__ int extract(const float (&v)[kVals], uint32_t active, int tile_base,
                                        int V, bool vec, uint32_t thr, float pre, float T,
                                        int* pool_n, uint64_t* __restrict__ pool, int* end) {
-  int crossed = 0;
-#define VS_GROUP(G)                                                                         \
-  if (active & (1u << G)) {                                                                 \
-    const int r = extract_group<E, G>(v, tile_base, V, vec, thr, pre, T, pool_n, pool, end); \
-    if (r < 0) return -1;                                                                   \
-    crossed |= r;                                                                           \
+  if constexpr (G == kGroups) {
+    return 0;
+  } else {
+    int crossed = 0;
+    if (active & (1u << G)) {
+      crossed = extract_group<E, G>(v, tile_base, V, vec, thr, pre, T, pool_n, pool, end);
+      if (crossed < 0) return -1;
+    }
+    const int rest = extract<E, G + 1>(v, active, tile_base, V, vec, thr, pre, T, pool_n, pool, end);
+    return rest < 0 ? -1 : (crossed | rest);
   }
-  VS_GROUP(0)
-  VS_GROUP(1)
-  VS_GROUP(2)
-  VS_GROUP(3)
-  VS_GROUP(4)
-  VS_GROUP(5)
-  VS_GROUP(6)
-  VS_GROUP(7)
-#undef VS_GROUP
-  return crossed;
 }
 
 // Adds to r[i] the number of the first n pool entries larger than e[i]. The
@@ -263,6 +262,7 @@ struct List {
 struct SegSh {
   uint64_t pool[2][kPoolCap];  // each list's candidates (packed), appended by all waves
   int next_tile;  // the segment's next unclaimed tile (claimed by whole waves)
+  int next_out;   // the next tile of the full log-softmax write
   uint32_t thr[2];
   int merge_n[2];
   int ovf[2];
@@ -615,6 +615,53 @@ __device__ __forceinline__ uint64_t wave_top_of_pool(const uint64_t* pool, int n
   return top;
 }
 
+// Writes the row's full log-softmax, lp = (x - M) - logS for every id (NaN
+// throughout for a row that failed its checks), with the formula and inputs of
+// the separate write pass. Whole waves claim 2048-id tiles from an LDS counter
+// as they arrive; a tile is read with 16-byte loads (a second read of the row
+// this workgroup has just streamed, mostly served by the caches) and written
+// with non-temporal 16-byte stores, or element by element at the row's end
+// and for unaligned rows or outputs.
+template <typename E, bool kStream>
+__device__ __forceinline__ void write_full_row(const Job& j, const E* __restrict__ rowp,
+                                               float* __restrict__ orow, int t_end, float M,
+                                               float logS, int* next) {
+  constexpr int EPV = Epv<E>::n;
+  const int l = lane();
+  for (;;) {
+    int t = 0;
+    if (l == 0) t = atomicAdd(next, 1);
+    t = __builtin_amdgcn_readfirstlane(t);
+    if (t >= t_end) break;
+    const int base = t * kSelTile;
+    if (j.aligned && j.full_vec && base + kSelTile <= j.V) {  // uniform
+      Raw<E> X;
+      load_raw<E, kStream>(rowp + base, 1, X);
+#pragma unroll
+      for (int i = 0; i < Raw<E>::n; ++i) {
+        float x[EPV];
+        unpack16(X.r[i], x, rowp);
+        const int j0 = base + (i * kWave + l) * EPV;
+#pragma unroll
+        for (int c = 0; c < EPV; c += 4) {
+          f32x4 o;
+          o.x = (x[c] - M) - logS;
+          o.y = (x[c + 1] - M) - logS;
+          o.z = (x[c + 2] - M) - logS;
+          o.w = (x[c + 3] - M) - logS;
+          __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(orow + j0 + c));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < kVals; ++q) {
+        const int id = elem_index<E>(base, q);
+        if (id < j.V) orow[id] = (to_f32(rowp[id]) - M) - logS;
+      }
+    }
+  }
+}
+
 // Finishes a row with one wave: the same outputs the row kernel writes (draw,
 // kept count, status, log-sum-exp, the log-probs of the sampled or given id and
 // the top-k log-probs). LA and LB hold the lists' best entries sorted across
@@ -747,6 +794,7 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
     sh.out_n[0] = sh.out_n[1] = 0;
     sh.kth_key[0] = sh.kth_key[1] = 0u;
     sh.flags = 0u;
+    sh.next_out = t_begin;
   }
   // empty pool slots read as 0, below every candidate; ranks start at 0
   for (int i = threadIdx.x; i < 2 * kPoolCap; i += NT) {
@@ -1029,23 +1077,32 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
       }
     }
     __syncthreads();
-    if (w != 0) return;
-    double q = 1.0;
-    if (noise) {
-      q = (LA != 0ull) ? sh.q[tag_pos(LA)] : 1.0;
-      LA = untag_entry(LA);
+    if (w == 0) {
+      double q = 1.0;
+      if (noise) {
+        q = (LA != 0ull) ? sh.q[tag_pos(LA)] : 1.0;
+        LA = untag_entry(LA);
+      }
+      const float M = sh.tot_m, S = sh.tot_s;
+      const uint64_t bA = sh.tot_b[0], bB = sh.tot_b[1];
+      if (pl.kA > 1) meta |= static_cast<uint32_t>(nA);
+      if (pl.kB > 1) meta |= static_cast<uint32_t>(nB) << kMetaCountBShift;
+      if (pl.kA == 1 && bA) meta |= 1u;
+      if (pl.kB == 1 && bB) meta |= 1u << kMetaCountBShift;
+      sh.stage[0][l] = __double_as_longlong(q);  // the noise by lane, for the draw
+      wave_lds_wait();
+      finish_row<E>(j, row, pl, meta, LA, nA, LB, nB, M, S, bA, bB,
+                    noise ? reinterpret_cast<const double*>(sh.stage[0]) : nullptr);
+      if (l == 0) j.meta[slot] = meta | kMetaFinal;
     }
-    const float M = sh.tot_m, S = sh.tot_s;
-    const uint64_t bA = sh.tot_b[0], bB = sh.tot_b[1];
-    if (pl.kA > 1) meta |= static_cast<uint32_t>(nA);
-    if (pl.kB > 1) meta |= static_cast<uint32_t>(nB) << kMetaCountBShift;
-    if (pl.kA == 1 && bA) meta |= 1u;
-    if (pl.kB == 1 && bB) meta |= 1u << kMetaCountBShift;
-    sh.stage[0][l] = __double_as_longlong(q);  // the noise by lane, for the draw
-    wave_lds_wait();
-    finish_row<E>(j, row, pl, meta, LA, nA, LB, nB, M, S, bA, bB,
-                  noise ? reinterpret_cast<const double*>(sh.stage[0]) : nullptr);
-    if (l == 0) j.meta[slot] = meta | kMetaFinal;
+    if (j.full_in_select) {  // every wave, wave 0 once the row's outputs are written
+      const bool bad = (meta & kMetaBadLogits) || !(meta & kMetaHasFinite);
+      const float nanv = __builtin_nanf("");
+      const float M = bad ? nanv : sh.tot_m;
+      const float logS = bad ? nanv : logf(sh.tot_s);
+      write_full_row<E, true>(j, rowp, j.out_full + static_cast<int64_t>(row) * j.ld_out, t_end, M,
+                              logS, &sh.next_out);
+    }
     return;
   }
   uint32_t kthA = 0u, kthB = 0u;
@@ -1106,10 +1163,14 @@ hipError_t launch_select(const Job& j, hipStream_t st) {
   // logits too large for the last-level cache to keep for a second reader
   // (more than half of its 256 MB).
   const int64_t bytes = static_cast<int64_t>(j.B) * j.V * (j.dt == VS_F32 ? 4 : 2);
-  const bool stream = bytes > (int64_t{128} << 20) ||
-                      (!j.out_full &&
-                       (!j.sample || (j.hints & (VS_HINT_NO_FULLVOCAB | VS_HINT_ALL_GREEDY |
-                                                 VS_HINT_SMALL_TOPK))));
+  // When the pass also writes the full log-softmax it reads each row a second
+  // time right away: the first read then goes through the caches (measured
+  // faster overall than streaming it past them).
+  const bool stream = !j.full_in_select &&
+                      (bytes > (int64_t{128} << 20) ||
+                       (!j.out_full &&
+                        (!j.sample || (j.hints & (VS_HINT_NO_FULLVOCAB | VS_HINT_ALL_GREEDY |
+                                                  VS_HINT_SMALL_TOPK)))));
   if (j.dt == VS_F32) {
     if (stream)
       hipLaunchKernelGGL((k_select<float, true>), dim3(grid), block, lds, st, j);

@@ -120,6 +120,11 @@ hipError_t stage(const char* name, hipStream_t st, F&& launch) {
   return e;
 }
 
+// Full log-softmax rows that take 16-byte stores.
+int full_vec(const float* out_full, int64_t ld_out) {
+  return (out_full && reinterpret_cast<uintptr_t>(out_full) % 16 == 0 && ld_out % 4 == 0) ? 1 : 0;
+}
+
 bool sizes_ok(vs_dtype dt, int B, int V, int64_t ld) {
   return (dt == VS_F32 || dt == VS_BF16) && B > 0 && V > 0 && V <= VS_MAX_V && ld >= V;
 }
@@ -209,13 +214,16 @@ vs_status vs_sample_logprobs(const void* logits, vs_dtype dt, int B, int V, int6
   j.out_lp = out_topk_logprobs;
   j.out_full = out_full;
   j.ld_out = ld_out;
-  if (stage("select", stream, [&] { return vsk::launch_select(j, stream); }) != hipSuccess)
-    return VS_ERR_HIP;
   // With one segment per row, no kept mask and hints that rule out every row
   // the streaming pass cannot finish (top-k above 64, full vocabulary), the
-  // streaming pass finishes every row and the row kernel has nothing to do.
+  // streaming pass finishes every row and the row kernel has nothing to do;
+  // it then also writes the full log-softmax, right after reading each row.
   const bool select_finishes =
       j.nseg == 1 && !out_kept_mask && (hints & (VS_HINT_SMALL_TOPK | VS_HINT_ALL_GREEDY));
+  j.full_in_select = (out_full && select_finishes) ? 1 : 0;
+  j.full_vec = full_vec(out_full, ld_out);
+  if (stage("select", stream, [&] { return vsk::launch_select(j, stream); }) != hipSuccess)
+    return VS_ERR_HIP;
   if (!select_finishes &&
       stage("row", stream, [&] { return vsk::launch_row_light(j, stream); }) != hipSuccess)
     return VS_ERR_HIP;
@@ -225,7 +233,7 @@ vs_status vs_sample_logprobs(const void* logits, vs_dtype dt, int B, int V, int6
     if (stage("gumbel", stream, [&] { return vsk::launch_gumbel(j, stream); }) != hipSuccess)
       return VS_ERR_HIP;
   }
-  if (out_full) {
+  if (out_full && !j.full_in_select) {
     if (stage("lse_full", stream, [&] { return vsk::launch_lse_full(j, stream); }) != hipSuccess)
       return VS_ERR_HIP;
   }
@@ -253,13 +261,16 @@ vs_status vs_logprobs(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
   j.out_full = out_full;
   j.ld_out = ld_out;
   j.out_lp_status = out_row_status;
+  // with one segment per row the streaming pass finishes every row (and then
+  // writes the full log-softmax itself)
+  j.full_in_select = (out_full && j.nseg == 1) ? 1 : 0;
+  j.full_vec = full_vec(out_full, ld_out);
   if (stage("lse_select", stream, [&] { return vsk::launch_select(j, stream); }) != hipSuccess)
     return VS_ERR_HIP;
-  // with one segment per row the streaming pass finishes every row
   if (j.nseg > 1 &&
       stage("lse_row", stream, [&] { return vsk::launch_row_light(j, stream); }) != hipSuccess)
     return VS_ERR_HIP;
-  if (out_full) {
+  if (out_full && !j.full_in_select) {
     if (stage("lse_full", stream, [&] { return vsk::launch_lse_full(j, stream); }) != hipSuccess)
       return VS_ERR_HIP;
   }

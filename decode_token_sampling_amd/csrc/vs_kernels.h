@@ -65,6 +65,8 @@ struct Job {
   float* out_full;
   int64_t ld_out;
   int32_t* out_lp_status;  // vs_logprobs status
+  int full_in_select;      // the streaming pass writes out_full itself (it finishes every row)
+  int full_vec;            // out_full rows take 16-byte stores
   // workspace; streaming-pass geometry
   int ntile;  // tiles per row
   int nseg;   // segments per row (<= ceil(V / kSegMin), the workspace's slots per row)

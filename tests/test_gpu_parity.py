@@ -448,6 +448,48 @@ def test_finish_in_stream_fused(V, dtype, k):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [4097, 32000])
+def test_finish_in_stream_full_logsoftmax(V, dtype):
+    """Rows the streaming pass finishes (greedy and small top-k rows, promised
+    by the hint): the pass writes the full log-softmax itself. It agrees with
+    the separate write pass that runs when a kept mask sends the rows to the
+    row kernel (to the log-prob tolerance: the waves' log-sum-exp partials are
+    summed in the order their dynamically claimed tiles give, so the last bit
+    of log S can differ from call to call) and with the oracle; a bad row is
+    NaN throughout."""
+    import decode_token_sampling_amd as vs
+    x = _row_shapes(7000 + V, FIN_B, V, dtype)
+    x[3, 1] = np.nan if dtype == "f32" else 0x7FC0
+    rng = np.random.default_rng(V + 11)
+    T = rng.uniform(0.5, 1.5, FIN_B).astype(np.float32)
+    T[::5] = 0.0
+    top_k = rng.integers(2, 65, FIN_B).astype(np.int32)
+    top_p = rng.uniform(0.5, 1.0, FIN_B).astype(np.float32)
+    seeds = np.arange(99, 99 + FIN_B, dtype=np.uint64)
+    args = [dev(T, np.float32), dev(top_k, np.int32), dev(top_p, np.float32),
+            dev(np.zeros(FIN_B, np.float32), np.float32), dev(seeds.view(np.int64), np.int64)]
+    xd = to_device(x)
+    f = vs.sample_logprobs(xd, *args, hints=vs.HINT_SMALL_TOPK, k=20, full=True, V=V)
+    r = vs.sample_logprobs(xd, *args, k=20, full=True, mask=True, V=V)
+    torch.cuda.synchronize()
+    assert torch.equal(f["ids"], r["ids"]) and torch.equal(f["status"], r["status"])
+    ff, rf = f["full"], r["full"]
+    assert torch.equal(torch.isnan(ff), torch.isnan(rf)) and bool(torch.isnan(ff[3]).all())
+    inf = torch.isinf(ff)
+    assert torch.equal(inf, torch.isinf(rf)) and torch.equal(ff[inf], rf[inf])
+    fin = torch.isfinite(ff)
+    assert torch.equal(fin, torch.isfinite(rf))
+    assert (ff[fin] - rf[fin]).abs().max().item() <= LOGPROB_ATOL
+    rows = np.array([0, 1, 3, 100, FIN_B - 1])
+    o = oracle.logprobs(np.ascontiguousarray(x[rows]), V, f["ids"].cpu().numpy()[rows], k=20,
+                        full=True)
+    got = f["full"][torch.from_numpy(rows).cuda()].cpu().numpy()
+    fin = np.isfinite(o["full"])
+    assert np.array_equal(np.isfinite(got), fin)
+    assert np.abs(got[fin] - o["full"][fin]).max() <= LOGPROB_ATOL
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("k", [0, 1, 20, 64])
 def test_finish_in_stream_logprobs(dtype, k):
     import decode_token_sampling_amd as vs
