@@ -33,6 +33,7 @@ HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "w256x248320_f32"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {"select": "k_select.hip", "lse_select": "k_select.hip", "row": "k_row.hip",
+                  "full_prep": "k_full.hip",
                   "lse_row": "k_row.hip", "row_full": "k_row.hip", "gumbel": "k_gumbel.hip",
                   "lse_full": "k_gumbel.hip", "penalize": "k_penalize.hip"}
 

@@ -1,11 +1,20 @@
 // K3/K4: the Gumbel-max draw over full-vocabulary kept sets, and the full
 // log-softmax write of vs_logprobs.
 //
-// K3 (grid: rows x 4096-id tiles, all tiles of a row on one XCD): for every id
-// of the tile it recomputes s = x / T and e = exp(s - m), tests membership
-// (everything; e >= min_p; or for top-p "key > tau, or key == tau and
-// id <= id_cut"), and for kept ids forms score = e / -log(u(seed, row, id)).
-// Each tile keeps its best (score desc, id asc) and its kept count.
+// K3 (grid: rows x runs of gseg 4096-id tiles, all of a row on one XCD; each
+// run reports in its first tile's record, the others empty): for every id
+// of the tile it recomputes s = x / T, tests membership (everything; e >=
+// min_p; or for top-p "key > tau, or key == tau and id <= id_cut"), and for
+// kept ids forms score = e / -log(u(seed, row, id)) with e = E(s - m). Each
+// tile keeps its best (score desc, id asc) and its kept count. A thread skips
+// the logarithm and the division for an id that provably scores below its
+// best so far: -log u > 1 - u for u < 1, so 1 - u >= e / best (with margins
+// for the rounding of both sides) means e / -log u < best; e <= 1 gives a
+// first test before e itself is computed. Any kept id's score bounds the
+// row's maximum from below, so after each tile the waves of a workgroup share
+// their bests through LDS (plain stores and loads: a stale value is only a
+// looser bound). Skipped ids cannot be the argmax, so the result is the exact
+// one.
 // K4 (one workgroup per row) reduces the tiles: the sampled id, the kept count
 // and, in the fused call, the sampled id's log-probability. The argmax compares
 // true ids, never thread or tile order, so the result does not depend on the
@@ -27,8 +36,10 @@ template <typename E>
 __global__ __launch_bounds__(kThreads) void k_gumbel_partial(Job j) {
   __shared__ double sd[kThreads / kWave];
   __shared__ int si[kThreads / kWave];
-  int row, tile;
-  if (!xcd_row_tile(blockIdx.x, j.B, j.ntile3, &row, &tile)) return;
+  __shared__ uint64_t swb[kThreads / kWave];  // each wave's best score bits so far
+  int row, run;
+  const int nrun = (j.ntile3 + j.gseg - 1) / j.gseg;
+  if (!xcd_row_tile(blockIdx.x, j.B, nrun, &row, &run)) return;
   const RowDesc d = j.desc[row];
   if (!full_row(d.mode)) return;  // uniform over the block
   constexpr int EPV = Epv<E>::n;
@@ -37,57 +48,90 @@ __global__ __launch_bounds__(kThreads) void k_gumbel_partial(Job j) {
   const float mp = j.mp ? j.mp[row] : 0.0f;
   const uint64_t rs = row_stream(j.seeds ? j.seeds[row] : 0ull, row);
   const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
-  const int base = tile * kGumTile;
-  const bool vec = j.aligned && (base + kGumTile <= j.V);
   const int mwords = (j.V + 31) / 32;
   uint32_t* mask_row = j.out_mask ? j.out_mask + static_cast<size_t>(row) * mwords : nullptr;
+  const int t0 = run * j.gseg;
+  const int t1 = min(j.ntile3, t0 + j.gseg);
+  const int wv = static_cast<int>(threadIdx.x) / kWave;
+  if (lane() == 0) swb[wv] = 0ull;
+  __syncthreads();
 
   double best = -1.0;
   int best_id = 0x7fffffff;
+  // (1 + 2^-40) / (the largest kept id's score known here): an id whose 1 - u
+  // reaches lim * e scores below it (infinite, so that no id is skipped,
+  // until a score is known)
+  double lim = __builtin_inf();
   int kept = 0;
+  for (int tile = t0; tile < t1; ++tile) {
+    const int base = tile * kGumTile;
+    const bool vec = j.aligned && (base + kGumTile <= j.V);
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int j0 = base + (i * kThreads + static_cast<int>(threadIdx.x)) * EPV;
-    float x[EPV];
-    if (vec) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(rowp + j0);
-      unpack16(raw, x, rowp);
-    } else {
-#pragma unroll
-      for (int c = 0; c < EPV; ++c) x[c] = (j0 + c < j.V) ? to_f32(rowp[j0 + c]) : -kInf;
-    }
-    uint32_t bits = 0;
-#pragma unroll
-    for (int c = 0; c < EPV; ++c) {
-      const int id = j0 + c;
-      if (id >= j.V) continue;
-      const float s = (T == 1.0f) ? x[c] : x[c] / T;
-      const float e = pinned_exp(s - d.m);
-      bool keep;
-      if (d.mode == kRowFullNone) {
-        keep = true;
-      } else if (d.mode == kRowFullMinP) {
-        keep = e >= mp;
+    for (int i = 0; i < NV; ++i) {
+      const int j0 = base + (i * kThreads + static_cast<int>(threadIdx.x)) * EPV;
+      float x[EPV];
+      if (vec) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(rowp + j0);
+        unpack16(raw, x, rowp);
       } else {
-        const uint32_t key = f2key(s);
-        keep = key > d.tau || (key == d.tau && id <= d.id_cut);
+#pragma unroll
+        for (int c = 0; c < EPV; ++c) x[c] = (j0 + c < j.V) ? to_f32(rowp[j0 + c]) : -kInf;
       }
-      if (keep) {
-        ++kept;
-        bits |= 1u << (id & 31);
-        const double sc = gumbel_score(e, rs, id);
-        if (sc > best || (sc == best && id < best_id)) {
-          best = sc;
-          best_id = id;
+      uint32_t bits = 0;
+#pragma unroll
+      for (int c = 0; c < EPV; ++c) {
+        const int id = j0 + c;
+        if (id >= j.V) continue;
+        const float s = (T == 1.0f) ? x[c] : x[c] / T;
+        float e = -1.0f;  // E(s - m), once computed
+        bool keep;
+        if (d.mode == kRowFullNone) {
+          keep = true;
+        } else if (d.mode == kRowFullMinP) {
+          e = pinned_exp(s - d.m);
+          keep = e >= mp;
+        } else {
+          const uint32_t key = f2key(s);
+          keep = key > d.tau || (key == d.tau && id <= d.id_cut);
+        }
+        if (keep) {
+          ++kept;
+          bits |= 1u << (id & 31);
+          const double u = uniform_of(rs, id);
+          const double one_u = (1.0 - u) * (1.0 - 0x1p-50);  // rounded down past any rounding error
+          if (one_u >= lim) continue;                        // e <= 1: below the bound
+          if (e < 0.0f) e = pinned_exp(s - d.m);
+          if (one_u >= lim * static_cast<double>(e)) continue;  // below the bound
+          const double sc = static_cast<double>(e) / -log(u);   // as gumbel_score
+          if (sc > best || (sc == best && id < best_id)) {
+            best = sc;
+            best_id = id;
+            lim = fmin(lim, (1.0 + 0x1p-40) / best);
+          }
         }
       }
+      if (mask_row && bits) atomicOr(&mask_row[j0 >> 5], bits);
     }
-    if (mask_row && bits) atomicOr(&mask_row[j0 >> 5], bits);
+    // this wave's best into its slot, then the workgroup's (scores are
+    // nonnegative: their bits order as integers)
+    uint64_t wb = wave_max_u64_dpp(best >= 0.0 ? static_cast<uint64_t>(__double_as_longlong(best)) : 0ull);
+    if (lane() == 0) __hip_atomic_store(&swb[wv], wb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+#pragma unroll
+    for (int w = 0; w < kThreads / kWave; ++w) {
+      const uint64_t o = __hip_atomic_load(&swb[w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      wb = o > wb ? o : wb;
+    }
+    const double sbest = __longlong_as_double(static_cast<long long>(wb));
+    if (sbest > 0.0) lim = fmin(lim, (1.0 + 0x1p-40) / sbest);
   }
   const double bb = block_max(best, sd);
   const int bid = block_min(best == bb ? best_id : 0x7fffffff, si);
   const int bk = block_sum(kept, si);
-  if (threadIdx.x == 0) j.gpart[static_cast<size_t>(row) * j.ntile3 + tile] = GPart{bb, bid, bk};
+  if (threadIdx.x == 0) {
+    GPart* g = j.gpart + static_cast<size_t>(row) * j.ntile3;
+    g[t0] = GPart{bb, bid, bk};
+    for (int t = t0 + 1; t < t1; ++t) g[t] = GPart{-1.0, 0x7fffffff, 0};
+  }
 }
 
 template <typename E>
@@ -171,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void k_lse_full(Job j, int ntile, bool ou
 }  // namespace
 
 hipError_t launch_gumbel(const Job& j, hipStream_t st) {
-  const int grid = xcd_grid(j.B, j.ntile3);
+  const int grid = xcd_grid(j.B, (j.ntile3 + j.gseg - 1) / j.gseg);
   if (j.dt == VS_F32)
     hipLaunchKernelGGL(k_gumbel_partial<float>, dim3(grid), dim3(kThreads), 0, st, j);
   else

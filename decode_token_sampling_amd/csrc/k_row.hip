@@ -25,8 +25,7 @@ namespace {
 
 constexpr int kLightThreads = 256;
 constexpr int kFullThreads = 1024;
-constexpr int kBuckets = 4096;
-constexpr float kBucketsPerUnit = 128.0f;
+constexpr int kBuckets = kFullBuckets;
 constexpr int kMaxSegs = (VS_MAX_V + kSegMin - 1) / kSegMin;
 
 template <int kBuf, int kBins>
@@ -47,7 +46,7 @@ struct RowSh {
   int32_t toff[kMaxSegs + 1];  // per-segment offsets of a candidate union
 };
 using LightSh = RowSh<4096, 2048>;
-using FullSh = RowSh<8192, kBuckets>;
+using FullSh = RowSh<kFullListCap, kBuckets>;
 
 __device__ __forceinline__ float scaled(float x, float T) { return (T == 1.0f) ? x : x / T; }
 
@@ -578,6 +577,15 @@ __global__ __launch_bounds__(kLightThreads) void k_row_light(Job j) {
         } else {
           next = kRowFull;
           if (threadIdx.x == 0) j.desc[row].m = m;
+          if (c.p < 1.0f) {  // the histogram and gather passes accumulate from zero
+            uint64_t* hw = j.fhw + static_cast<size_t>(row) * kFullBuckets;
+            uint32_t* hc = j.fhc + static_cast<size_t>(row) * kFullBuckets;
+            for (int i = threadIdx.x; i < kFullBuckets; i += blockDim.x) {
+              hw[i] = 0ull;
+              hc[i] = 0u;
+            }
+            if (threadIdx.x == 0) j.fcnt[row] = 0u;
+          }
         }
       }
     }
@@ -660,26 +668,10 @@ __global__ __launch_bounds__(kLightThreads) void k_row_light(Job j) {
   }
 }
 
-// Per-element quantities of a full-vocabulary top-p row.
-struct FullTerms {
-  float m, T, mp;
-  __device__ __forceinline__ bool mass(float s, uint64_t* w, int* bucket) const {
-    const float t = s - m;
-    const float e = pinned_exp(t);
-    if (!(e >= mp)) return false;
-    const uint64_t W = mass_of(e);
-    if (W == 0) return false;
-    *w = W;
-    const int b = static_cast<int>(-t * kBucketsPerUnit);
-    *bucket = b < kBuckets - 1 ? b : kBuckets - 1;
-    return true;
-  }
-};
-
 template <typename E>
 __device__ void full_topp_cut(const E* __restrict__ rowp, int V, bool aligned, const RowCfg& c,
                               float m, FullSh& sh, RowDesc* d) {
-  const FullTerms ft{m, c.T, c.mp};
+  const FullTerms ft{m, c.mp};
   for (int i = threadIdx.x; i < kBuckets; i += blockDim.x) {
     sh.hw[i] = 0;
     sh.hc[i] = 0;
@@ -785,6 +777,104 @@ __device__ void full_topp_cut(const E* __restrict__ rowp, int V, bool aligned, c
   }
 }
 
+// The top-p cut from the ids of the cut bucket, gathered by the parallel
+// passes: the first entry, in the order (key desc, id asc), at which the mass
+// inside the bucket reaches the remainder. No sort: an MSB-first radix select
+// on the packed values (whose descending order is that order) with 8-bit
+// digits, each round adding the masses of the entries still in play per digit
+// and keeping the digit where the running mass crosses the remainder. The
+// leading bits that every entry shares are skipped; a round that leaves one
+// entry ends the search. False when the gather did not hold the whole bucket;
+// the row then takes the one-workgroup path.
+__device__ bool full_cut_from_list(const Job& j, int row, const RowCfg& c, float m, FullSh& sh,
+                                   RowDesc* d) {
+  const FullCut fc = j.fcut[row];
+  const uint32_t got = j.fcnt[row];
+  if (fc.bucket < 0 || got != fc.count || got > static_cast<uint32_t>(FullSh::kBufCap) || got == 0)
+    return false;  // uniform
+  const int n = static_cast<int>(got);
+  const uint64_t* lst = j.flist + static_cast<size_t>(row) * kFullListCap;
+  uint64_t lo = ~0ull, hi = 0ull;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const uint64_t v = lst[i];
+    sh.buf[i] = v;
+    lo = v < lo ? v : lo;
+    hi = v > hi ? v : hi;
+  }
+  lo = block_min(lo, sh.r64);
+  hi = block_max(hi, sh.r64);
+  const FullTerms ft{m, c.mp};
+  uint64_t rem = fc.rem;  // mass still needed, counted from the top of the bucket
+  int rank = 0;           // entries above the digit group in play
+  uint64_t cutv = hi;
+  if (lo != hi) {
+    int shift = ((63 - __clzll(lo ^ hi)) / 8) * 8;
+    uint64_t pmask = (shift + 8 >= 64) ? 0ull : (~0ull << (shift + 8));
+    uint64_t prefix = hi & pmask;
+    for (;;) {  // every condition below is uniform over the block
+      for (int i = threadIdx.x; i < 256; i += blockDim.x) {
+        sh.hw[i] = 0ull;
+        sh.hc[i] = 0u;
+      }
+      if (threadIdx.x == 0) sh.b32[0] = -1;
+      __syncthreads();
+      for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const uint64_t v = sh.buf[i];
+        if ((v & pmask) == prefix) {
+          uint64_t w;
+          int b;
+          if (!ft.mass(key2f(pkey(v)), &w, &b)) w = 0;
+          const int dg = static_cast<int>((v >> shift) & 255u);
+          atomicAdd(reinterpret_cast<unsigned long long*>(&sh.hw[dg]), static_cast<unsigned long long>(w));
+          atomicAdd(&sh.hc[dg], 1u);
+        }
+      }
+      __syncthreads();
+      // thread t < 256 holds digit 255 - t (largest digits first)
+      const int t = static_cast<int>(threadIdx.x);
+      const uint64_t w = t < 256 ? sh.hw[255 - t] : 0ull;
+      const int cn = t < 256 ? static_cast<int>(sh.hc[255 - t]) : 0;
+      uint64_t tw;
+      int tc;
+      const uint64_t wb = block_scan_incl(w, sh.r64, &tw) - w;
+      const int cb = block_scan_incl(cn, sh.ri, &tc) - cn;
+      if (t < 256 && cn > 0 && wb < rem && rem <= wb + w) {
+        sh.b32[0] = 255 - t;
+        sh.b32[1] = cb;
+        sh.b32[2] = cn;
+        sh.b64[0] = wb;
+      }
+      __syncthreads();
+      const int dg = sh.b32[0];
+      const int above = sh.b32[1], cnt = sh.b32[2];
+      const uint64_t wabove = sh.b64[0];
+      __syncthreads();
+      if (dg < 0) return false;  // the list's masses fall short of the remainder
+      rem -= wabove;
+      rank += above;
+      prefix |= static_cast<uint64_t>(dg) << shift;
+      pmask |= 0xffull << shift;
+      if (cnt == 1) {
+        for (int i = threadIdx.x; i < n; i += blockDim.x)
+          if ((sh.buf[i] & pmask) == prefix) sh.b64[1] = sh.buf[i];
+        __syncthreads();
+        cutv = sh.b64[1];
+        __syncthreads();
+        break;
+      }
+      if (shift == 0) return false;  // distinct entries: unreachable
+      shift -= 8;
+    }
+  }
+  if (threadIdx.x == 0) {
+    d->mode = kRowFullTopP;
+    d->tau = pkey(cutv);
+    d->id_cut = pid(cutv);
+    d->kept = static_cast<int32_t>(fc.above_c) + rank + 1;
+  }
+  return true;
+}
+
 template <typename E>
 __global__ __launch_bounds__(kFullThreads) void k_row_full(Job j) {
   __shared__ FullSh sh;
@@ -794,8 +884,10 @@ __global__ __launch_bounds__(kFullThreads) void k_row_full(Job j) {
   const RowCfg c = load_cfg(row, j.V, j.T, j.k, j.p, j.mp, j.seeds);
   const float m = d->m;
   if (c.p < 1.0f) {
-    const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
-    full_topp_cut(rowp, j.V, j.aligned, c, m, sh, d);
+    if (!full_cut_from_list(j, row, c, m, sh, d)) {
+      const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
+      full_topp_cut(rowp, j.V, j.aligned, c, m, sh, d);
+    }
   } else if (threadIdx.x == 0) {
     d->mode = (c.mp > 0.0f) ? kRowFullMinP : kRowFullNone;
   }

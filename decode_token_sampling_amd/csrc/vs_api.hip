@@ -50,6 +50,16 @@ WsLayout ws_layout(int B, int V) {
   off = align_up(off + tiles * sizeof(LsePart));
   L.rlse = off;
   off = align_up(off + static_cast<size_t>(B) * sizeof(float2));
+  L.fhw = off;
+  off = align_up(off + static_cast<size_t>(B) * kFullBuckets * sizeof(uint64_t));
+  L.fhc = off;
+  off = align_up(off + static_cast<size_t>(B) * kFullBuckets * sizeof(uint32_t));
+  L.flist = off;
+  off = align_up(off + static_cast<size_t>(B) * kFullListCap * sizeof(uint64_t));
+  L.fcnt = off;
+  off = align_up(off + static_cast<size_t>(B) * sizeof(uint32_t));
+  L.fcut = off;
+  off = align_up(off + static_cast<size_t>(B) * sizeof(FullCut));
   L.total = off;
   return L;
 }
@@ -91,6 +101,29 @@ Job make_job(const void* logits, vs_dtype dt, int B, int V, int64_t ld, void* ws
   j.gpart = reinterpret_cast<GPart*>(w + L.gpart);
   j.lpart = reinterpret_cast<LsePart*>(w + L.lpart);
   j.rlse = reinterpret_cast<float2*>(w + L.rlse);
+  j.fhw = reinterpret_cast<uint64_t*>(w + L.fhw);
+  j.fhc = reinterpret_cast<uint32_t*>(w + L.fhc);
+  j.flist = reinterpret_cast<uint64_t*>(w + L.flist);
+  j.fcnt = reinterpret_cast<uint32_t*>(w + L.fcnt);
+  j.fcut = reinterpret_cast<FullCut*>(w + L.fcut);
+  // Gumbel pass of full-vocabulary rows: up to 8 tiles per workgroup (the
+  // pruning bound tightens along them) while the grid keeps about 512
+  // workgroups.
+  {
+    const int64_t t = static_cast<int64_t>(B) * L.ntile3 / 512;
+    j.gseg = t < 1 ? 1 : (t > 8 ? 8 : static_cast<int>(t));
+  }
+  // Histogram and gather passes of full-vocabulary rows: enough segments per
+  // row that the batch gives every compute unit about four workgroups, each at
+  // least kFullSegMin ids (a multiple of 8, so segments start 16-byte aligned).
+  {
+    const int smax = (V + kFullSegMin - 1) / kFullSegMin;
+    int fs = (4 * cus + B - 1) / B;
+    fs = fs < 1 ? 1 : (fs > smax ? smax : fs);
+    const int len = ((V + fs - 1) / fs + 7) & ~7;
+    j.fseg_len = len;
+    j.fseg = (V + len - 1) / len;
+  }
   return j;
 }
 
@@ -228,6 +261,8 @@ vs_status vs_sample_logprobs(const void* logits, vs_dtype dt, int B, int V, int6
       stage("row", stream, [&] { return vsk::launch_row_light(j, stream); }) != hipSuccess)
     return VS_ERR_HIP;
   if (!(hints & (VS_HINT_NO_FULLVOCAB | VS_HINT_ALL_GREEDY | VS_HINT_SMALL_TOPK))) {
+    if (stage("full_prep", stream, [&] { return vsk::launch_full_prep(j, stream); }) != hipSuccess)
+      return VS_ERR_HIP;
     if (stage("row_full", stream, [&] { return vsk::launch_row_full(j, stream); }) != hipSuccess)
       return VS_ERR_HIP;
     if (stage("gumbel", stream, [&] { return vsk::launch_gumbel(j, stream); }) != hipSuccess)

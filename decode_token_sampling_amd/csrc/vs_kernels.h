@@ -16,6 +16,13 @@ constexpr int kSelMaxWaves = 16;  // waves per streaming-pass workgroup, at most
 constexpr int kSelCap = 128;      // candidate slots per segment and list
 constexpr int kGumTile = 4096;    // Gumbel tile: 256 threads x 16 values
 constexpr int kFullTile = 4096;   // full log-softmax write tile
+// Full-vocabulary top-p: fixed-point masses histogrammed over buckets of
+// t = s - m (kFullPerUnit buckets per unit, bucket 0 holding the largest s),
+// and the ids of the bucket holding the cut gathered into a list per row.
+constexpr int kFullBuckets = 4096;
+constexpr float kFullPerUnit = 128.0f;
+constexpr int kFullListCap = 8192;
+constexpr int kFullSegMin = 4096;  // ids per segment of the histogram and gather passes, at least
 
 // Segment meta word (a segment is the run of tiles of one row that one
 // streaming-pass workgroup reads).
@@ -34,6 +41,37 @@ enum : uint32_t {
   kRowFullMinP = 2,   // full vocabulary, min-p only
   kRowFullTopP = 3,   // full vocabulary, top-p cut given by (tau, id_cut)
   kRowFull = 4,       // full vocabulary, the cut still to be found (heavy kernel)
+};
+
+// The top-p cut of a full-vocabulary row, found from its mass histogram.
+struct FullCut {
+  int32_t bucket;     // the bucket holding the cut (-1: not found)
+  uint32_t count;     // ids in that bucket
+  uint64_t rem;       // mass still needed inside it (>= 1)
+  uint64_t above_c;   // ids in the buckets above it
+  uint64_t pad;
+};
+
+// Per-id terms of a full-vocabulary row: the relative weight e = E(s - m),
+// the fixed-point mass W and the bucket of t = s - m; false for ids outside
+// the kept candidates (e < min_p, or zero mass). The one definition every
+// full-vocabulary kernel uses.
+struct FullTerms {
+  float m, mp;
+  __device__ __forceinline__ bool mass(float s, uint64_t* w, int* bucket) const {
+    const float t = s - m;
+    const float e = pinned_exp(t);
+    if (!(e >= mp)) return false;
+    const uint64_t W = mass_of(e);
+    if (W == 0) return false;
+    *w = W;
+    *bucket = bucket_of(t);
+    return true;
+  }
+  __device__ __forceinline__ static int bucket_of(float t) {
+    const int b = static_cast<int>(-t * kFullPerUnit);
+    return b < kFullBuckets - 1 ? b : kFullBuckets - 1;
+  }
 };
 
 struct Job {
@@ -65,6 +103,14 @@ struct Job {
   float* out_full;
   int64_t ld_out;
   int32_t* out_lp_status;  // vs_logprobs status
+  // full-vocabulary top-p (per row): mass histogram, the cut bucket's ids
+  uint64_t* fhw;       // [B][kFullBuckets] masses
+  uint32_t* fhc;       // [B][kFullBuckets] counts
+  uint64_t* flist;     // [B][kFullListCap] packed (key, id) of the cut bucket
+  uint32_t* fcnt;      // [B] entries appended to flist (may exceed the capacity)
+  FullCut* fcut;       // [B] the cut bucket and the mass needed inside it
+  int fseg;            // segments per row of the histogram and gather passes
+  int fseg_len;        // ids per segment (a multiple of 8)
   int full_in_select;      // the streaming pass writes out_full itself (it finishes every row)
   int full_vec;            // out_full rows take 16-byte stores
   // workspace; streaming-pass geometry
@@ -73,6 +119,7 @@ struct Job {
   int tps;    // tiles per segment
   int nwave;  // waves per streaming-pass workgroup
   int ntile3;
+  int gseg;  // Gumbel-pass tiles per workgroup
   uint32_t* meta;
   uint64_t* candA;
   uint64_t* candB;
@@ -115,13 +162,14 @@ __device__ __forceinline__ Plan plan_row(const Job& j, int row) {
 
 struct WsLayout {
   int ntile, ntile3;
-  size_t meta, candA, candB, kthA, kthB, desc, gpart, lpart, rlse, total;
+  size_t meta, candA, candB, kthA, kthB, desc, gpart, lpart, rlse, fhw, fhc, flist, fcnt, fcut, total;
 };
 WsLayout ws_layout(int B, int V);
 
 hipError_t launch_select(const Job& j, hipStream_t st);
 hipError_t launch_row_light(const Job& j, hipStream_t st);
 hipError_t launch_row_full(const Job& j, hipStream_t st);
+hipError_t launch_full_prep(const Job& j, hipStream_t st);
 hipError_t launch_gumbel(const Job& j, hipStream_t st);
 hipError_t launch_lse_full(const Job& j, hipStream_t st);
 hipError_t launch_penalize(void* logits, vs_dtype dt, int B, int V, int64_t ld,
