@@ -78,7 +78,7 @@ class HipEvents:
 def kernel_hash(stage: str) -> str:
     src = os.path.join(ROOT, "decode_token_sampling_amd", "csrc")
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[stage], "vs_device.h"):
+    for f in (KERNEL_SOURCES[stage], "vs_device.h", "vs_kernels.h"):
         with open(os.path.join(src, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
