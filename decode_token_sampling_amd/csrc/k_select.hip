@@ -40,7 +40,7 @@ constexpr int kGroups = kVals / kGroup;
 static_assert(kGroup == 4 && kVals % kGroup == 0 && kGroups <= 32, "groups of 4 values, a bit each");
 
 constexpr int kPoolCap = 512;     // candidates per segment and list (the shared pool)
-constexpr int kCheck = 64;        // the pool's bound is recomputed every kCheck entries
+constexpr int kCheck = 32;        // the pool's bound is recomputed every kCheck entries
 static_assert(kPoolCap % 16 == 0, "rank_counts reads the pool in batches of up to 16");
 constexpr float kL2E = 1.44269504088896340736f;
 // s_waitcnt operand for "vector memory count 0", other counters left at their
