@@ -10,11 +10,11 @@
 // the logarithm and the division for an id that provably scores below its
 // best so far: -log u > 1 - u for u < 1, so 1 - u >= e / best (with margins
 // for the rounding of both sides) means e / -log u < best; e <= 1 gives a
-// first test before e itself is computed. Any kept id's score bounds the
-// row's maximum from below, so after each tile the waves of a workgroup share
-// their bests through LDS (plain stores and loads: a stale value is only a
-// looser bound). Skipped ids cannot be the argmax, so the result is the exact
-// one.
+// first test before e itself is computed, a hardware-exponential upper bound
+// on e a second one. Any kept id's score bounds the row's maximum from below,
+// so after each tile the waves of a workgroup share their bests through LDS
+// (plain stores and loads: a stale value is only a looser bound). Skipped ids
+// cannot be the argmax, so the result is the exact one.
 // K4 (one workgroup per row) reduces the tiles: the sampled id, the kept count
 // and, in the fused call, the sampled id's log-probability. The argmax compares
 // true ids, never thread or tile order, so the result does not depend on the
@@ -27,6 +27,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kPerThread = kGumTile / kThreads;  // 16
+constexpr float kLog2E = 1.44269504088896340736f;
 
 __device__ __forceinline__ bool full_row(uint32_t mode) {
   return mode == kRowFullNone || mode == kRowFullMinP || mode == kRowFullTopP;
@@ -100,7 +101,15 @@ __global__ __launch_bounds__(kThreads) void k_gumbel_partial(Job j) {
           const double u = uniform_of(rs, id);
           const double one_u = (1.0 - u) * (1.0 - 0x1p-50);  // rounded down past any rounding error
           if (one_u >= lim) continue;                        // e <= 1: below the bound
-          if (e < 0.0f) e = pinned_exp(s - d.m);
+          if (e < 0.0f) {
+            // an upper bound on e from the hardware exponential first: for
+            // s - m >= -87 the fp32 constant and product move the exponent by
+            // at most 9e-6 (2^x by 6.3e-6 relative), the instruction adds
+            // about 1 ulp, and 2^-16 covers both; below -87 e is 0
+            const float eub = __builtin_amdgcn_exp2f((s - d.m) * kLog2E) * (1.0f + 0x1p-16f);
+            if (one_u >= lim * static_cast<double>(eub)) continue;  // below the bound
+            e = pinned_exp(s - d.m);
+          }
           if (one_u >= lim * static_cast<double>(e)) continue;  // below the bound
           const double sc = static_cast<double>(e) / -log(u);   // as gumbel_score
           if (sc > best || (sc == best && id < best_id)) {
