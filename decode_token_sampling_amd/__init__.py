@@ -41,8 +41,9 @@ MAX_V = 1 << 21
 TOPK_MAX = 1024
 LOGPROB_K_MAX = 64
 
-EXPORTED_SYMBOLS = ("vs_workspace_size", "vs_status_string", "vs_penalize", "vs_sample",
-                    "vs_logprobs", "vs_sample_logprobs", "vs_profile_begin", "vs_profile_end")
+EXPORTED_SYMBOLS = ("vs_workspace_size", "vs_status_string", "vs_penalize", "vs_penalize_ex",
+                    "vs_sample", "vs_logprobs", "vs_sample_logprobs", "vs_profile_begin",
+                    "vs_profile_end")
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "workspace too small", 3: "unsupported",
            4: "HIP launch failure"}
@@ -69,13 +70,14 @@ def load() -> ctypes.CDLL:
     lib.vs_status_string.argtypes = [i32]
     lib.vs_status_string.restype = ctypes.c_char_p
     lib.vs_penalize.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, P, P, P, P]
+    lib.vs_penalize_ex.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, P, P, P, P, P]
     lib.vs_sample.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, u32, P, P, P, P, P, sz, P]
     lib.vs_logprobs.argtypes = [P, i32, i32, i32, i64, P, P, i32, P, P, P, i64, P, P, sz, P]
     lib.vs_sample_logprobs.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, u32, P, P, P, P, P,
                                        i32, P, P, P, i64, P, sz, P]
     lib.vs_profile_begin.argtypes = [P, i32]
     lib.vs_profile_end.argtypes = [ctypes.POINTER(ctypes.c_char_p), i32]
-    for f in ("vs_workspace_size", "vs_penalize", "vs_sample", "vs_logprobs",
+    for f in ("vs_workspace_size", "vs_penalize", "vs_penalize_ex", "vs_sample", "vs_logprobs",
               "vs_sample_logprobs", "vs_profile_begin", "vs_profile_end"):
         getattr(lib, f).restype = i32
     _lib = lib
@@ -134,20 +136,25 @@ def workspace(B: int, V: int, dtype: torch.dtype = torch.float32, device=None) -
 
 def penalize(logits, prompt_ids=None, prompt_off=None, output_ids=None, output_off=None,
              presence=None, frequency=None, repetition=None, V=None, row_status=None,
-             stream=None) -> torch.Tensor:
-    """Occurrence penalties in place (vs_penalize). Returns the per-row status tensor."""
+             stream=None, prompt_ignore=None) -> torch.Tensor:
+    """Occurrence penalties in place (vs_penalize, or vs_penalize_ex with a per-row
+    prompt_ignore_length tensor). Returns the per-row status tensor."""
     B, V, ld = _logits_args(logits, V)
     st = row_status if row_status is not None else torch.empty(B, dtype=torch.int32,
                                                                 device=logits.device)
-    code = load().vs_penalize(
-        logits.data_ptr(), _dtype_code(logits), B, V, ld,
-        _ptr(prompt_ids, torch.int32, name="prompt_ids"), _ptr(prompt_off, torch.int32, B + 1, "prompt_off"),
-        _ptr(output_ids, torch.int32, name="output_ids"), _ptr(output_off, torch.int32, B + 1, "output_off"),
-        _ptr(presence, torch.float32, B, "presence"), _ptr(frequency, torch.float32, B, "frequency"),
-        _ptr(repetition, torch.float32, B, "repetition"), _ptr(st, torch.int32, B, "row_status"),
-        _stream(stream))
+    args = [logits.data_ptr(), _dtype_code(logits), B, V, ld,
+            _ptr(prompt_ids, torch.int32, name="prompt_ids"), _ptr(prompt_off, torch.int32, B + 1, "prompt_off"),
+            _ptr(output_ids, torch.int32, name="output_ids"), _ptr(output_off, torch.int32, B + 1, "output_off"),
+            _ptr(presence, torch.float32, B, "presence"), _ptr(frequency, torch.float32, B, "frequency"),
+            _ptr(repetition, torch.float32, B, "repetition")]
+    tail = [_ptr(st, torch.int32, B, "row_status"), _stream(stream)]
+    if prompt_ignore is None:
+        name, code = "vs_penalize", load().vs_penalize(*args, *tail)
+    else:
+        name = "vs_penalize_ex"
+        code = load().vs_penalize_ex(*args, _ptr(prompt_ignore, torch.int32, B, "prompt_ignore"), *tail)
     if code:
-        raise VsError("vs_penalize", code)
+        raise VsError(name, code)
     return st
 
 

@@ -5,7 +5,11 @@
 // slots of id and count) and then rewrites each distinct id's logit once:
 // repetition (divide a non-negative logit, multiply a negative one), presence,
 // frequency times the count, each a separately rounded fp32 operation
-// (TensorRT-LLM "Sampling", occurrence-penalty bullets). A history with more
+// (TensorRT-LLM "Sampling", occurrence-penalty bullets). With a prompt ignore
+// length n (the prompt_ignore_length bullet), the first n prompt ids still put
+// their id in the table, so that the repetition step applies, but add nothing
+// to its count; presence and frequency apply to ids whose count is positive.
+// Without one every id in the table has a positive count. A history with more
 // distinct ids than the table holds is processed in hash classes: the ids
 // whose hash falls in one class are counted and applied together, and a class
 // that still overflows is split in two; no id is ever applied twice.
@@ -44,7 +48,7 @@ __global__ __launch_bounds__(kThreads) void k_penalize(
     const int32_t* __restrict__ poff, const int32_t* __restrict__ oids,
     const int32_t* __restrict__ ooff, const float* __restrict__ presence,
     const float* __restrict__ frequency, const float* __restrict__ repetition,
-    int32_t* __restrict__ out_status) {
+    const int32_t* __restrict__ pignore, int32_t* __restrict__ out_status) {
   __shared__ uint32_t keys[kSlots];
   __shared__ uint32_t counts[kSlots];
   __shared__ int s_overflow, s_badid;
@@ -63,6 +67,8 @@ __global__ __launch_bounds__(kThreads) void k_penalize(
   const int o0 = (oids && ooff) ? ooff[row] : 0;
   const int lo = (oids && ooff) ? ooff[row + 1] - o0 : 0;
   const int L = lp + lo;
+  // the prompt ids [0, nign) count for repetition only (clamped to the prompt)
+  const int nign = pignore ? min(max(pignore[row], 0), lp) : 0;
   E* rowp = logits + static_cast<int64_t>(row) * ld;
 
   auto hist_id = [&](int i) -> int32_t { return i < lp ? pids[p0 + i] : oids[o0 + (i - lp)]; };
@@ -119,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void k_penalize(
       while (true) {
         const uint32_t prev = atomicCAS(&keys[slot], kEmpty, u);
         if (prev == kEmpty || prev == u) {
-          atomicAdd(&counts[slot], 1u);
+          if (i >= nign) atomicAdd(&counts[slot], 1u);
           break;
         }
         slot = (slot + 1) & (kSlots - 1);
@@ -145,13 +151,15 @@ __global__ __launch_bounds__(kThreads) void k_penalize(
     for (int i = threadIdx.x; i < kSlots; i += blockDim.x) {
       const uint32_t id = keys[i];
       if (id == kEmpty) continue;
-      const float c = static_cast<float>(counts[i]);
+      const uint32_t n = counts[i];
       E* p = rowp + id;
       const float x = to_f32(*p);
       float y = (x >= 0.0f) ? x / rep : x * rep;
-      y = y - pres;
-      const float fc = freq * c;
-      y = y - fc;
+      if (n > 0u) {
+        y = y - pres;
+        const float fc = freq * static_cast<float>(n);
+        y = y - fc;
+      }
       store_penalised<E>(p, y);
     }
   }
@@ -165,15 +173,16 @@ hipError_t launch_penalize(void* logits, vs_dtype dt, int B, int V, int64_t ld,
                            const int32_t* prompt_ids, const int32_t* prompt_off,
                            const int32_t* output_ids, const int32_t* output_off,
                            const float* presence, const float* frequency,
-                           const float* repetition, int32_t* out_status, hipStream_t st) {
+                           const float* repetition, const int32_t* prompt_ignore,
+                           int32_t* out_status, hipStream_t st) {
   if (dt == VS_F32)
     hipLaunchKernelGGL(k_penalize<float>, dim3(B), dim3(kThreads), 0, st,
                        static_cast<float*>(logits), B, V, ld, prompt_ids, prompt_off, output_ids,
-                       output_off, presence, frequency, repetition, out_status);
+                       output_off, presence, frequency, repetition, prompt_ignore, out_status);
   else
     hipLaunchKernelGGL(k_penalize<uint16_t>, dim3(B), dim3(kThreads), 0, st,
                        static_cast<uint16_t*>(logits), B, V, ld, prompt_ids, prompt_off, output_ids,
-                       output_off, presence, frequency, repetition, out_status);
+                       output_off, presence, frequency, repetition, prompt_ignore, out_status);
   return hipGetLastError();
 }
 

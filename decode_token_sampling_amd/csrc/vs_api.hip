@@ -183,21 +183,31 @@ const char* vs_status_string(vs_status s) {
   return "unknown status";
 }
 
+vs_status vs_penalize_ex(void* logits, vs_dtype dt, int B, int V, int64_t ld,
+                         const int32_t* prompt_ids, const int32_t* prompt_off,
+                         const int32_t* output_ids, const int32_t* output_off,
+                         const float* presence, const float* frequency,
+                         const float* repetition, const int32_t* prompt_ignore_len,
+                         int32_t* out_row_status, hipStream_t stream) {
+  if (!logits || !sizes_ok(dt, B, V, ld)) return VS_ERR_INVALID_ARGUMENT;
+  if ((prompt_ids == nullptr) != (prompt_off == nullptr)) return VS_ERR_INVALID_ARGUMENT;
+  if ((output_ids == nullptr) != (output_off == nullptr)) return VS_ERR_INVALID_ARGUMENT;
+  const hipError_t e = stage("penalize", stream, [&] {
+    return vsk::launch_penalize(logits, dt, B, V, ld, prompt_ids, prompt_off, output_ids,
+                                output_off, presence, frequency, repetition, prompt_ignore_len,
+                                out_row_status, stream);
+  });
+  return e == hipSuccess ? VS_OK : VS_ERR_HIP;
+}
+
 vs_status vs_penalize(void* logits, vs_dtype dt, int B, int V, int64_t ld,
                       const int32_t* prompt_ids, const int32_t* prompt_off,
                       const int32_t* output_ids, const int32_t* output_off,
                       const float* presence, const float* frequency,
                       const float* repetition, int32_t* out_row_status,
                       hipStream_t stream) {
-  if (!logits || !sizes_ok(dt, B, V, ld)) return VS_ERR_INVALID_ARGUMENT;
-  if ((prompt_ids == nullptr) != (prompt_off == nullptr)) return VS_ERR_INVALID_ARGUMENT;
-  if ((output_ids == nullptr) != (output_off == nullptr)) return VS_ERR_INVALID_ARGUMENT;
-  const hipError_t e = stage("penalize", stream, [&] {
-    return vsk::launch_penalize(logits, dt, B, V, ld, prompt_ids, prompt_off, output_ids,
-                                output_off, presence, frequency, repetition, out_row_status,
-                                stream);
-  });
-  return e == hipSuccess ? VS_OK : VS_ERR_HIP;
+  return vs_penalize_ex(logits, dt, B, V, ld, prompt_ids, prompt_off, output_ids, output_off,
+                        presence, frequency, repetition, nullptr, out_row_status, stream);
 }
 
 vs_status vs_sample(const void* logits, vs_dtype dt, int B, int V, int64_t ld,

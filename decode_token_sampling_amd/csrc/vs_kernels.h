@@ -176,6 +176,7 @@ hipError_t launch_penalize(void* logits, vs_dtype dt, int B, int V, int64_t ld,
                            const int32_t* prompt_ids, const int32_t* prompt_off,
                            const int32_t* output_ids, const int32_t* output_off,
                            const float* presence, const float* frequency,
-                           const float* repetition, int32_t* out_status, hipStream_t st);
+                           const float* repetition, const int32_t* prompt_ignore,
+                           int32_t* out_status, hipStream_t st);
 
 }  // namespace vsk

@@ -110,6 +110,27 @@ vs_status vs_penalize(void* logits, vs_dtype dt, int B, int V, int64_t ld,
                       hipStream_t stream);
 
 /*
+ * vs_penalize_ex — vs_penalize with a prompt ignore length per row.
+ *
+ * The TensorRT-LLM "Sampling" page's prompt_ignore_length bullet: the first n
+ * prompt ids of a row, n = prompt_ignore_len[r] clamped to [0, the row's prompt
+ * length], are left out of the presence and frequency counts and still count
+ * for the repetition penalty. So an id that occurs only there gets the
+ * repetition step alone; values <= 0 change nothing; a value at or past the
+ * prompt length counts presence and frequency over the output ids only.
+ *
+ *  prompt_ignore_len [B] int32 device pointer, or NULL (every n = 0: exactly
+ *              vs_penalize). Every other argument, and the errors, as
+ *              vs_penalize.
+ */
+vs_status vs_penalize_ex(void* logits, vs_dtype dt, int B, int V, int64_t ld,
+                         const int32_t* prompt_ids, const int32_t* prompt_off,
+                         const int32_t* output_ids, const int32_t* output_off,
+                         const float* presence, const float* frequency,
+                         const float* repetition, const int32_t* prompt_ignore_len,
+                         int32_t* out_row_status, hipStream_t stream);
+
+/*
  * vs_sample — one token per row.
  *
  * Truncation follows the TensorRT-LLM "Sampling" page (same section): greedy

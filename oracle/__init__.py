@@ -47,7 +47,7 @@ def _load():
         lib = ctypes.CDLL(LIB_PATH)
         P = ctypes.c_void_p
         i32, i64, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_float
-        lib.oracle_penalize.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, P, P, P]
+        lib.oracle_penalize.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, P, P, P, P]
         lib.oracle_sample.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_sample_row.argtypes = [P, i32, i32, i32, i64, i32, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_logprobs.argtypes = [P, i32, i32, i32, i64, P, P, i32, P, P, P, P]
@@ -85,14 +85,16 @@ def _as(a, dt):
 
 
 def penalize(logits, V, prompt_ids=None, prompt_off=None, output_ids=None,
-             output_off=None, presence=None, frequency=None, repetition=None):
-    """Apply occurrence penalties in place on a [B, ld] array; returns row status."""
+             output_off=None, presence=None, frequency=None, repetition=None,
+             prompt_ignore=None):
+    """Apply occurrence penalties in place on a [B, ld] array; returns row status.
+    prompt_ignore: per-row prompt_ignore_length (None: 0)."""
     lib = _load()
     B, ld = logits.shape
     st = np.zeros(B, np.int32)
     args = [_as(prompt_ids, np.int32), _as(prompt_off, np.int32), _as(output_ids, np.int32),
             _as(output_off, np.int32), _as(presence, np.float32), _as(frequency, np.float32),
-            _as(repetition, np.float32)]
+            _as(repetition, np.float32), _as(prompt_ignore, np.int32)]
     lib.oracle_penalize(_ptr(logits), _dtype_code(logits), B, V, ld, *[_ptr(a) for a in args],
                         _ptr(st))
     return st

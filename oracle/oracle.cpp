@@ -257,8 +257,10 @@ int oracle_penalize(void* logits, int dtype, int B, int V, int64_t ld,
                     const int32_t* prompt_ids, const int32_t* prompt_off,
                     const int32_t* output_ids, const int32_t* output_off,
                     const float* presence, const float* frequency,
-                    const float* repetition, int32_t* row_status) {
-  std::vector<int> count(V);
+                    const float* repetition, const int32_t* prompt_ignore,
+                    int32_t* row_status) {
+  std::vector<int> count(V);   // every occurrence: the repetition penalty
+  std::vector<int> pcount(V);  // occurrences past the ignored prompt prefix
   for (int r = 0; r < B; ++r) {
     int status = 0;
     const float pres = presence ? presence[r] : 0.0f;
@@ -270,8 +272,11 @@ int oracle_penalize(void* logits, int dtype, int B, int V, int64_t ld,
     if (bad) status |= kRowBadParam;
 
     // c = occurrences in the prompt plus occurrences in the generated output.
+    // The first n prompt ids (prompt_ignore_length, clamped to [0, prompt
+    // length]) count for repetition only.
     std::fill(count.begin(), count.end(), 0);
-    auto add = [&](const int32_t* ids, const int32_t* off) {
+    std::fill(pcount.begin(), pcount.end(), 0);
+    auto add = [&](const int32_t* ids, const int32_t* off, int32_t skip) {
       if (!ids || !off) return;
       for (int32_t i = off[r]; i < off[r + 1]; ++i) {
         const int32_t t = ids[i];
@@ -280,10 +285,12 @@ int oracle_penalize(void* logits, int dtype, int B, int V, int64_t ld,
           continue;
         }
         ++count[t];
+        if (i - off[r] >= skip) ++pcount[t];
       }
     };
-    add(prompt_ids, prompt_off);
-    add(output_ids, output_off);
+    const int32_t ign = prompt_ignore ? prompt_ignore[r] : 0;
+    add(prompt_ids, prompt_off, ign > 0 ? ign : 0);
+    add(output_ids, output_off, 0);
 
     if (!bad) {
       const int64_t base = static_cast<int64_t>(r) * ld;
@@ -294,9 +301,11 @@ int oracle_penalize(void* logits, int dtype, int B, int V, int64_t ld,
         // then presence; then frequency times the count. Each step is one
         // rounded fp32 operation, no fused multiply-add.
         float y = (x >= 0.0f) ? x / rep : x * rep;
-        y = y - pres;
-        const float fc = freq * static_cast<float>(count[j]);
-        y = y - fc;
+        if (pcount[j] > 0) {
+          y = y - pres;
+          const float fc = freq * static_cast<float>(pcount[j]);
+          y = y - fc;
+        }
         store_logit(logits, dtype, base + j, y);
       }
     }

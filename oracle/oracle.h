@@ -33,11 +33,16 @@ extern "C" {
 
 /* dtype: 0 = fp32, 1 = bf16 (stored as raw uint16). ld = row stride in elements. */
 
+/* prompt_ignore: [B] int32 or NULL (TensorRT-LLM "Sampling" page, the
+ * prompt_ignore_length bullet): the first n prompt ids of row r, n =
+ * clamp(prompt_ignore[r], 0, prompt length), count for the repetition penalty
+ * but not for presence and frequency. */
 int oracle_penalize(void* logits, int dtype, int B, int V, int64_t ld,
                     const int32_t* prompt_ids, const int32_t* prompt_off,
                     const int32_t* output_ids, const int32_t* output_off,
                     const float* presence, const float* frequency,
-                    const float* repetition, int32_t* row_status);
+                    const float* repetition, const int32_t* prompt_ignore,
+                    int32_t* row_status);
 
 /* out_kept_mask: B*V bytes or NULL; out_top2: B*2 doubles (best and second-best
  * Gumbel score, -1 where fewer than two kept ids) or NULL. */

@@ -18,7 +18,7 @@ def _declared():
 
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["vs_workspace_size", "vs_status_string", "vs_penalize",
-                                  "vs_sample", "vs_logprobs", "vs_sample_logprobs",
+                                  "vs_penalize_ex", "vs_sample", "vs_logprobs", "vs_sample_logprobs",
                                   "vs_profile_begin", "vs_profile_end"])
 
 
@@ -43,6 +43,7 @@ def test_host_checks_without_gpu():
     assert lib.vs_sample(None, 0, 4, 10, 10, *([None] * 5), 0, None, None, None, None,
                          None, 0, None) == 1
     assert lib.vs_penalize(None, 0, 4, 10, 10, *([None] * 9)) == 1
+    assert lib.vs_penalize_ex(None, 0, 4, 10, 10, *([None] * 10)) == 1
     assert lib.vs_logprobs(None, 0, 4, 10, 10, None, None, 0, None, None, None, 0, None,
                            None, 0, None) == 1
     dummy = ctypes.c_void_p(16)  # never dereferenced: the checks fail first

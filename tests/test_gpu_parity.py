@@ -191,6 +191,59 @@ def test_penalize_parity(dtype):
     assert np.array_equal(got.view(np.uint8), xo.view(np.uint8))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_penalize_prompt_ignore_parity(dtype):
+    """vs_penalize_ex: per-row prompt_ignore_length of 0, negative, inside the
+    prompt, the whole prompt and past it, on rows with and without a prompt."""
+    import decode_token_sampling_amd as vs
+    rng = np.random.default_rng(17)
+    B, V = 24, 40000
+    x = synth.random_rows(18, B, V, dtype, kind="rank")
+    pl = rng.integers(0, 1500, B)
+    ol = rng.integers(0, 300, B)
+    pl[3] = 0
+    ol[4] = 0
+    pids, poff = synth._csr([synth.zipf_ids(rng, int(n), V) for n in pl])
+    oids, ooff = synth._csr([synth.zipf_ids(rng, int(n), V) for n in ol])
+    ign = np.array([rng.integers(0, n + 1) if n else 0 for n in pl], np.int32)
+    ign[0], ign[1], ign[2], ign[5] = 0, -7, int(pl[2]), int(pl[5]) + 100
+    pres = rng.uniform(-0.5, 1.0, B).astype(np.float32)
+    freq = rng.uniform(-0.2, 1.0, B).astype(np.float32)
+    rep = rng.uniform(0.7, 1.5, B).astype(np.float32)
+    xd = to_device(x)
+    st = vs.penalize(xd, dev(pids, np.int32), dev(poff, np.int32), dev(oids, np.int32),
+                     dev(ooff, np.int32), dev(pres, np.float32), dev(freq, np.float32),
+                     dev(rep, np.float32), prompt_ignore=dev(ign, np.int32)).cpu().numpy()
+    xo = x.copy()
+    so = oracle.penalize(xo, V, pids, poff, oids, ooff, pres, freq, rep, prompt_ignore=ign)
+    assert np.array_equal(st, so)
+    assert np.array_equal(from_device(xd, V).view(np.uint8), xo.view(np.uint8))
+
+
+def test_penalize_prompt_ignore_many_classes():
+    """A prompt long enough for several hash classes: the ignored prefix is
+    decided by history position in every class pass."""
+    import decode_token_sampling_amd as vs
+    rng = np.random.default_rng(19)
+    B, V = 2, 300000
+    x = synth.random_rows(20, B, V)
+    plists = [rng.integers(0, V, 60000).astype(np.int32), np.arange(0, V, 5, dtype=np.int32)]
+    olists = [rng.integers(0, V, 500).astype(np.int32), np.arange(0, V, 11, dtype=np.int32)]
+    pids, poff = synth._csr(plists)
+    oids, ooff = synth._csr(olists)
+    ign = np.array([31000, 20000], np.int32)
+    pres = np.full(B, 0.25, np.float32)
+    freq = np.full(B, 0.01, np.float32)
+    rep = np.full(B, 1.3, np.float32)
+    xd = to_device(x)
+    vs.penalize(xd, dev(pids, np.int32), dev(poff, np.int32), dev(oids, np.int32),
+                dev(ooff, np.int32), dev(pres, np.float32), dev(freq, np.float32),
+                dev(rep, np.float32), prompt_ignore=dev(ign, np.int32))
+    xo = x.copy()
+    oracle.penalize(xo, V, pids, poff, oids, ooff, pres, freq, rep, prompt_ignore=ign)
+    assert np.array_equal(from_device(xd, V), xo)
+
+
 def test_penalize_long_history_many_classes():
     import decode_token_sampling_amd as vs
     rng = np.random.default_rng(13)

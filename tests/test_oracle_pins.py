@@ -127,6 +127,54 @@ def test_penalty_hand_case(orc):
     assert x[0].tolist() == g["expected"]
 
 
+def test_penalty_prompt_ignore_hand_case(orc):
+    """prompt_ignore_length on a hand-derived case; 0, negative and past-the-prompt
+    values behave as the page says (no effect, no effect, clamped)."""
+    g = _golden("penalties_ignore_hand.json")
+    pids, poff = _pen_csr([g["prompt_ids"]])
+    oids, ooff = _pen_csr([g["output_ids"]])
+    par = [np.array([g[k]], np.float32) for k in ("presence", "frequency", "repetition")]
+    for n, key in [(g["prompt_ignore"], "expected"), (0, "expected_no_ignore"), (-5, "expected_no_ignore")]:
+        x = np.array([g["logits"]], np.float32)
+        st = orc.penalize(x, g["V"], pids, poff, oids, ooff, *par, prompt_ignore=np.array([n], np.int32))
+        assert st[0] == 0
+        assert x[0].tolist() == g[key], n
+
+
+def test_penalty_prompt_ignore_properties(orc):
+    """N past the prompt equals N = prompt length (every prompt id counts for
+    repetition only); N = 0 equals no argument; an id seen only in the ignored
+    prefix gets the repetition step alone."""
+    rng = np.random.default_rng(11)
+    B, V = 6, 300
+    plist = [rng.integers(0, V, rng.integers(0, 40)).tolist() for _ in range(B)]
+    olist = [rng.integers(0, V, rng.integers(0, 20)).tolist() for _ in range(B)]
+    pids, poff = _pen_csr(plist)
+    oids, ooff = _pen_csr(olist)
+    par = [rng.uniform(-1, 1, B).astype(np.float32), rng.uniform(-1, 1, B).astype(np.float32),
+           rng.uniform(0.5, 2, B).astype(np.float32)]
+    base = rng.normal(0, 3, (B, V)).astype(np.float32)
+    lens = np.diff(poff)
+
+    def run(ign):
+        x = base.copy()
+        orc.penalize(x, V, pids, poff, oids, ooff, *par, prompt_ignore=ign)
+        return x
+    assert np.array_equal(run(None).view(np.uint32), run(np.zeros(B, np.int32)).view(np.uint32))
+    assert np.array_equal(run(lens.astype(np.int32)).view(np.uint32),
+                          run((lens + 7).astype(np.int32)).view(np.uint32))
+    full = run(lens.astype(np.int32))
+    for r in range(B):
+        only_prompt = set(plist[r]) - set(olist[r])
+        rep = par[2][r]
+        for j in only_prompt:
+            x = base[r, j]
+            want = np.float32(x / rep) if x >= 0 else np.float32(x * rep)
+            assert full[r, j] == want
+        for j in set(range(V)) - set(plist[r]) - set(olist[r]):
+            assert full[r, j] == base[r, j]
+
+
 def test_penalty_neutral_is_identity_and_unseen_untouched(orc):
     for dt in ("f32", "bf16"):
         x = synth.random_rows(5, 3, 500, dt)
