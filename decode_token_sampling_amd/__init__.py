@@ -42,8 +42,8 @@ TOPK_MAX = 1024
 LOGPROB_K_MAX = 64
 
 EXPORTED_SYMBOLS = ("vs_workspace_size", "vs_status_string", "vs_penalize", "vs_penalize_ex",
-                    "vs_sample", "vs_logprobs", "vs_sample_logprobs", "vs_profile_begin",
-                    "vs_profile_end")
+                    "vs_sample", "vs_logprobs", "vs_sample_logprobs", "vs_topp_decay",
+                    "vs_seed_advance", "vs_profile_begin", "vs_profile_end")
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "workspace too small", 3: "unsupported",
            4: "HIP launch failure"}
@@ -71,13 +71,16 @@ def load() -> ctypes.CDLL:
     lib.vs_status_string.restype = ctypes.c_char_p
     lib.vs_penalize.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, P, P, P, P]
     lib.vs_penalize_ex.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, P, P, P, P, P]
+    lib.vs_topp_decay.argtypes = [i32, P, P, P, P, P, P, P, P]
+    lib.vs_seed_advance.argtypes = [i32, P, P, P]
     lib.vs_sample.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, u32, P, P, P, P, P, sz, P]
     lib.vs_logprobs.argtypes = [P, i32, i32, i32, i64, P, P, i32, P, P, P, i64, P, P, sz, P]
     lib.vs_sample_logprobs.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, u32, P, P, P, P, P,
                                        i32, P, P, P, i64, P, sz, P]
     lib.vs_profile_begin.argtypes = [P, i32]
     lib.vs_profile_end.argtypes = [ctypes.POINTER(ctypes.c_char_p), i32]
-    for f in ("vs_workspace_size", "vs_penalize", "vs_penalize_ex", "vs_sample", "vs_logprobs",
+    for f in ("vs_workspace_size", "vs_penalize", "vs_penalize_ex", "vs_topp_decay",
+              "vs_seed_advance", "vs_sample", "vs_logprobs",
               "vs_sample_logprobs", "vs_profile_begin", "vs_profile_end"):
         getattr(lib, f).restype = i32
     _lib = lib
@@ -156,6 +159,33 @@ def penalize(logits, prompt_ids=None, prompt_off=None, output_ids=None, output_o
     if code:
         raise VsError(name, code)
     return st
+
+
+def topp_decay(top_p, top_p_init, decay, sampled_ids, top_p_min=None, reset_ids=None,
+               row_status=None, stream=None) -> torch.Tensor:
+    """Top-p decay after one sampled token, in place on the fp32 state tensor
+    top_p (vs_topp_decay). Returns the per-row status tensor."""
+    B = top_p.shape[0]
+    st = row_status if row_status is not None else torch.empty(B, dtype=torch.int32,
+                                                                device=top_p.device)
+    code = load().vs_topp_decay(
+        B, _ptr(top_p, torch.float32, B, "top_p"), _ptr(top_p_init, torch.float32, B, "top_p_init"),
+        _ptr(decay, torch.float32, B, "decay"), _ptr(top_p_min, torch.float32, B, "top_p_min"),
+        _ptr(reset_ids, torch.int32, B, "reset_ids"), _ptr(sampled_ids, torch.int32, B, "sampled_ids"),
+        _ptr(st, torch.int32, B, "row_status"), _stream(stream))
+    if code:
+        raise VsError("vs_topp_decay", code)
+    return st
+
+
+def seed_advance(seeds, sampled_ids=None, stream=None) -> None:
+    """One new seed per row per sampled token, in place on the int64 (uint64
+    bits) seed tensor (vs_seed_advance)."""
+    B = seeds.shape[0]
+    code = load().vs_seed_advance(B, _ptr(seeds, torch.int64, B, "seeds"),
+                                  _ptr(sampled_ids, torch.int32, B, "sampled_ids"), _stream(stream))
+    if code:
+        raise VsError("vs_seed_advance", code)
 
 
 def sample(logits, temperature=None, top_k=None, top_p=None, min_p=None, seeds=None, hints=0,

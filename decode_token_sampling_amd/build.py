@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libvs.so")
-SOURCES = ["vs_api.hip", "k_select.hip", "k_row.hip", "k_full.hip", "k_gumbel.hip",
+SOURCES = ["vs_api.hip", "k_select.hip", "k_row.hip", "k_full.hip", "k_state.hip", "k_gumbel.hip",
            "k_penalize.hip"]
 ARCH = os.environ.get("VS_OFFLOAD_ARCH", "gfx950")
 

@@ -210,6 +210,25 @@ vs_status vs_penalize(void* logits, vs_dtype dt, int B, int V, int64_t ld,
                         presence, frequency, repetition, nullptr, out_row_status, stream);
 }
 
+vs_status vs_topp_decay(int B, float* top_p, const float* top_p_init, const float* decay,
+                        const float* top_p_min, const int32_t* reset_ids,
+                        const int32_t* sampled_ids, int32_t* out_row_status, hipStream_t stream) {
+  if (B <= 0 || !top_p || !top_p_init || !decay || !sampled_ids) return VS_ERR_INVALID_ARGUMENT;
+  const hipError_t e = stage("topp_decay", stream, [&] {
+    return vsk::launch_topp_decay(B, top_p, top_p_init, decay, top_p_min, reset_ids, sampled_ids,
+                                  out_row_status, stream);
+  });
+  return e == hipSuccess ? VS_OK : VS_ERR_HIP;
+}
+
+vs_status vs_seed_advance(int B, uint64_t* seeds, const int32_t* sampled_ids, hipStream_t stream) {
+  if (B <= 0 || !seeds) return VS_ERR_INVALID_ARGUMENT;
+  const hipError_t e = stage("seed_advance", stream, [&] {
+    return vsk::launch_seed_advance(B, seeds, sampled_ids, stream);
+  });
+  return e == hipSuccess ? VS_OK : VS_ERR_HIP;
+}
+
 vs_status vs_sample(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
                     const float* temperature, const int32_t* top_k,
                     const float* top_p, const float* min_p,

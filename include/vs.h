@@ -131,6 +131,47 @@ vs_status vs_penalize_ex(void* logits, vs_dtype dt, int B, int V, int64_t ld,
                          int32_t* out_row_status, hipStream_t stream);
 
 /*
+ * vs_topp_decay — the effective top-p after one sampled token, in place.
+ *
+ * The TensorRT-LLM "Sampling" page's Top-P decay bullets: after every sampled
+ * token the effective top_p is multiplied by top_p_decay (one rounded fp32
+ * product), bounded from below by top_p_min, and reset to the initial top_p
+ * when the token top_p_reset_ids is sampled. With top_p = 1 and an active
+ * decay the state starts from 1. The caller passes the state as vs_sample's
+ * top_p on the next step; a greedy row ignores it there (greedy takes
+ * precedence).
+ *
+ *  top_p        [B] fp32, the state, updated in place (device).
+ *  top_p_init   [B] fp32 in [0, 1]; decay [B] fp32 in (0, 1].
+ *  top_p_min    [B] fp32 in (0, 1], or NULL (1e-6 for every row).
+ *  reset_ids    [B] int32, -1 for none, or NULL (none).
+ *  sampled_ids  [B] int32, the step's ids; a row with a negative id (nothing
+ *               sampled) keeps its state.
+ *  out_row_status [B] int32 or NULL: VS_ROW_BAD_PARAM for a parameter out of
+ *               range (also a reset id below -1); that row keeps its state.
+ * Errors: VS_ERR_INVALID_ARGUMENT for B <= 0 or a required NULL pointer.
+ */
+vs_status vs_topp_decay(int B, float* top_p, const float* top_p_init, const float* decay,
+                        const float* top_p_min, const int32_t* reset_ids,
+                        const int32_t* sampled_ids, int32_t* out_row_status, hipStream_t stream);
+
+/*
+ * vs_seed_advance — one new seed per row per sampled token, in place.
+ *
+ * The TT sampling README's seed contract asks for new seed values exactly once
+ * per sampled token; the Tunix sampler folds the decoding step into its key.
+ * Here seeds[r] += 0x9E3779B97F4A7C15 (mod 2^64), the SplitMix64 increment,
+ * so successive seeds are that generator's successive states and each step's
+ * draw (keyed by seed, row and id) is a fresh stream.
+ *
+ *  seeds        [B] uint64, device, updated in place.
+ *  sampled_ids  [B] int32 or NULL: only rows with an id >= 0 advance (NULL:
+ *               every row).
+ * Errors: VS_ERR_INVALID_ARGUMENT for B <= 0 or seeds NULL.
+ */
+vs_status vs_seed_advance(int B, uint64_t* seeds, const int32_t* sampled_ids, hipStream_t stream);
+
+/*
  * vs_sample — one token per row.
  *
  * Truncation follows the TensorRT-LLM "Sampling" page (same section): greedy

@@ -51,6 +51,8 @@ def _load():
         lib.oracle_sample.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_sample_row.argtypes = [P, i32, i32, i32, i64, i32, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_logprobs.argtypes = [P, i32, i32, i32, i64, P, P, i32, P, P, P, P]
+        lib.oracle_topp_decay.argtypes = [i32, P, P, P, P, P, P, P]
+        lib.oracle_seed_advance.argtypes = [i32, P, P]
         lib.oracle_exp_pinned.argtypes = [f32]
         lib.oracle_exp_pinned.restype = f32
         lib.oracle_splitmix64.argtypes = [ctypes.c_uint64]
@@ -144,6 +146,24 @@ def logprobs(logits, V, token_ids=None, k=0, full=False):
     lib.oracle_logprobs(_ptr(logits), _dtype_code(logits), B, V, ld, _ptr(tok), _ptr(tlp), k,
                         _ptr(tids), _ptr(tlps), _ptr(fullo), _ptr(st))
     return dict(token_lp=tlp, topk_ids=tids, topk_lp=tlps, full=fullo, status=st)
+
+
+def topp_decay(top_p, top_p_init, decay, sampled, top_p_min=None, reset_ids=None):
+    """Top-p decay after one sampled token, in place on the fp32 array top_p;
+    returns row status."""
+    lib = _load()
+    B = len(top_p)
+    st = np.zeros(B, np.int32)
+    args = [_as(top_p_init, np.float32), _as(decay, np.float32), _as(top_p_min, np.float32),
+            _as(reset_ids, np.int32), _as(sampled, np.int32)]
+    lib.oracle_topp_decay(B, _ptr(top_p), *[_ptr(a) for a in args], _ptr(st))
+    return st
+
+
+def seed_advance(seeds, sampled=None):
+    """One new seed per row per sampled token, in place on the uint64 array seeds."""
+    lib = _load()
+    lib.oracle_seed_advance(len(seeds), _ptr(seeds), _ptr(_as(sampled, np.int32)))
 
 
 def exp_pinned(t: float) -> float:

@@ -314,6 +314,36 @@ int oracle_penalize(void* logits, int dtype, int B, int V, int64_t ld,
   return 0;
 }
 
+int oracle_topp_decay(int B, float* top_p, const float* top_p_init, const float* decay,
+                      const float* top_p_min, const int32_t* reset_ids,
+                      const int32_t* sampled, int32_t* row_status) {
+  for (int r = 0; r < B; ++r) {
+    const float d = decay[r];
+    const float lo = top_p_min ? top_p_min[r] : 1e-6f;
+    const float p0 = top_p_init[r];
+    const int32_t reset = reset_ids ? reset_ids[r] : -1;
+    // the page rejects a decay or floor outside (0, 1] and a negative reset
+    // id other than the "no reset id" value -1
+    const bool bad = !(d > 0.0f && d <= 1.0f) || !(lo > 0.0f && lo <= 1.0f) ||
+                     !(p0 >= 0.0f && p0 <= 1.0f) || reset < -1;
+    if (row_status) row_status[r] = bad ? kRowBadParam : 0;
+    if (bad || sampled[r] < 0) continue;  // no token was sampled: nothing decays
+    if (reset >= 0 && sampled[r] == reset) {
+      top_p[r] = p0;  // the reset id was sampled: back to the initial top_p
+    } else {
+      const float p = top_p[r] * d;  // one rounded fp32 product
+      top_p[r] = p > lo ? p : lo;    // bounded from below
+    }
+  }
+  return 0;
+}
+
+int oracle_seed_advance(int B, uint64_t* seeds, const int32_t* sampled) {
+  for (int r = 0; r < B; ++r)
+    if (!sampled || sampled[r] >= 0) seeds[r] += 0x9E3779B97F4A7C15ull;
+  return 0;
+}
+
 int oracle_sample_row(const void* logits, int dtype, int B, int V, int64_t ld,
                       int r, const float* temperature, const int32_t* top_k,
                       const float* top_p, const float* min_p,

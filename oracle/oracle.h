@@ -67,6 +67,22 @@ int oracle_logprobs(const void* logits, int dtype, int B, int V, int64_t ld,
                     int32_t* out_topk_ids, double* out_topk_lp,
                     double* out_full, int32_t* row_status);
 
+/* Top-p decay after one sampled token (TensorRT-LLM "Sampling" page, the
+ * Top-P decay bullets). Row r with sampled[r] >= 0: top_p[r] = top_p_init[r]
+ * when reset_ids[r] >= 0 and sampled[r] == reset_ids[r], else
+ * max(top_p[r] * decay[r] rounded to fp32, top_p_min[r]). top_p_min NULL:
+ * 1e-6 for every row; reset_ids NULL: no reset id. decay or top_p_min outside
+ * (0, 1], top_p_init outside [0, 1] or a reset id below -1: row unchanged,
+ * status 1 (bad parameter). */
+int oracle_topp_decay(int B, float* top_p, const float* top_p_init, const float* decay,
+                      const float* top_p_min, const int32_t* reset_ids,
+                      const int32_t* sampled, int32_t* row_status);
+
+/* One new seed per row per sampled token: seeds[r] += 0x9E3779B97F4A7C15
+ * (mod 2^64), the SplitMix64 increment, for rows with sampled[r] >= 0 (every
+ * row when sampled is NULL). */
+int oracle_seed_advance(int B, uint64_t* seeds, const int32_t* sampled);
+
 /* Building blocks exposed for the pin tests. */
 float oracle_exp_pinned(float t);
 uint64_t oracle_splitmix64(uint64_t x);

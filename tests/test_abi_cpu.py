@@ -19,6 +19,7 @@ def _declared():
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["vs_workspace_size", "vs_status_string", "vs_penalize",
                                   "vs_penalize_ex", "vs_sample", "vs_logprobs", "vs_sample_logprobs",
+                                  "vs_topp_decay", "vs_seed_advance",
                                   "vs_profile_begin", "vs_profile_end"])
 
 
@@ -44,6 +45,9 @@ def test_host_checks_without_gpu():
                          None, 0, None) == 1
     assert lib.vs_penalize(None, 0, 4, 10, 10, *([None] * 9)) == 1
     assert lib.vs_penalize_ex(None, 0, 4, 10, 10, *([None] * 10)) == 1
+    assert lib.vs_topp_decay(0, *([None] * 8)) == 1
+    assert lib.vs_topp_decay(4, None, *([None] * 7)) == 1
+    assert lib.vs_seed_advance(4, None, None, None) == 1
     assert lib.vs_logprobs(None, 0, 4, 10, 10, None, None, 0, None, None, None, 0, None,
                            None, 0, None) == 1
     dummy = ctypes.c_void_p(16)  # never dereferenced: the checks fail first

@@ -31,6 +31,53 @@ def test_splitmix64_known_answers(orc):
         assert orc.splitmix64((n * gamma) % 2**64) == int(want, 16)
 
 
+def test_seed_advance_walks_the_splitmix64_states(orc):
+    """Advancing a seed of 0 n times gives the generator's state n * gamma, so its
+    mixed value is the published output n + 1; rows without a sampled token
+    keep their seed."""
+    g = _golden("splitmix64_known_answers.json")
+    seeds = np.zeros(2, np.uint64)
+    for n, want in enumerate(g["state0_outputs"]):
+        assert orc.splitmix64(int(seeds[0])) == int(want, 16)
+        orc.seed_advance(seeds, np.array([5, -1], np.int32))
+    assert int(seeds[1]) == 0
+    s = np.array([2**64 - 1], np.uint64)
+    orc.seed_advance(s)
+    assert int(s[0]) == (2**64 - 1 + 0x9E3779B97F4A7C15) % 2**64
+
+
+def test_topp_decay_hand_sequence(orc):
+    g = _golden("topp_decay_hand.json")
+    p = np.array([g["top_p_init"]], np.float32)
+    got = []
+    for t in g["tokens"]:
+        st = orc.topp_decay(p, [g["top_p_init"]], [g["decay"]], np.array([t], np.int32),
+                            top_p_min=[g["top_p_min"]], reset_ids=[g["reset_id"]])
+        assert st[0] == 0
+        got.append(float(p[0]))
+    assert got == [float(np.float32(v)) for v in g["expected"]]
+
+
+def test_topp_decay_defaults_and_rejections(orc):
+    # an initial top_p of 1 with an active decay: the first token already decays it
+    p = np.array([1.0], np.float32)
+    orc.topp_decay(p, [1.0], [0.75], np.array([0], np.int32))
+    assert p[0] == np.float32(0.75)
+    # the default floor is 1e-6 and no reset id matches by default
+    p = np.array([0.5], np.float32)
+    for _ in range(60):
+        orc.topp_decay(p, [0.5], [0.5], np.array([0], np.int32))
+    assert p[0] == np.float32(1e-6)
+    # out-of-range parameters: the row is rejected and unchanged
+    bad = [dict(decay=0.0), dict(decay=1.5), dict(top_p_min=0.0), dict(top_p_min=2.0),
+           dict(reset=-2), dict(init=1.5)]
+    for b in bad:
+        p = np.array([0.3], np.float32)
+        st = orc.topp_decay(p, [b.get("init", 0.3)], [b.get("decay", 0.5)], np.array([4], np.int32),
+                            top_p_min=[b.get("top_p_min", 0.1)], reset_ids=[b.get("reset", -1)])
+        assert st[0] == 1 and p[0] == np.float32(0.3), b
+
+
 def test_uniform_range_and_distribution(orc):
     u = np.array([orc.uniform(s, r, j) for s in (0, 1234, 2**63 + 5) for r in range(8)
                   for j in range(0, 4000, 3)])
