@@ -159,6 +159,22 @@ def test_sample_constant_rows_fallback_inside_bucket():
     compare_sample(gpu_sample(to_device(x), V, w), oracle_sample(x, V, w))
 
 
+def test_full_topp_gather_overflows_lds_but_fits_list():
+    """A cut bucket of 3000 tied ids inside one gather segment: the segment's
+    LDS staging (2048 ids) overflows into direct appends while the row's list
+    (<= 8192) still feeds the radix-select cut; ties go to the lowest ids."""
+    V, B = 32768, 3
+    x = np.full((B, V), -4.0, np.float32)
+    x[0, :3000] = 2.0                      # one segment holds the whole bucket
+    x[1, 100:3100] = 2.0
+    x[1, 5] = 2.5                          # a larger id above the bucket
+    x[2, 4096:7096] = 1.0                  # the bucket in the second segment
+    w = dict(temperature=np.ones(B, np.float32), top_k=np.zeros(B, np.int32),
+             top_p=np.array([0.5, 0.7, 0.3], np.float32), min_p=np.zeros(B, np.float32),
+             seeds=np.arange(B, dtype=np.uint64))
+    compare_sample(gpu_sample(to_device(x), V, w), oracle_sample(x, V, w))
+
+
 # ---------------------------------------------------------------- penalties
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_penalize_parity(dtype):
