@@ -302,6 +302,41 @@ def test_logprobs_parity(V, dtype):
     assert np.abs(full[fin] - of[fin]).max() <= LOGPROB_ATOL
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_maximum_vocabulary(dtype):
+    """V = 2^21, the largest vocabulary the library takes: every row mode for
+    the draw (ids, kept sets, status) and the log-probs (sampled-id, top-20,
+    full row) against the oracle."""
+    import decode_token_sampling_amd as vs
+    V, B = 1 << 21, 9
+    x = _row_shapes(77, B, V, dtype)
+    rng = np.random.default_rng(78)
+    w = random_params(rng, B, V)
+    xd = to_device(x)
+    compare_sample(gpu_sample(xd, V, w), oracle_sample(x, V, w))
+    tok = rng.integers(0, V, B).astype(np.int32)
+    g = vs.logprobs(xd, dev(tok, np.int32), k=20, full=True, V=V)
+    torch.cuda.synchronize()
+    o = oracle.logprobs(x, V, tok, k=20, full=True)
+    assert np.array_equal(g["status"].cpu().numpy(), o["status"])
+    assert np.allclose(g["token_lp"].cpu().numpy(), o["token_lp"], atol=LOGPROB_ATOL, rtol=0)
+    assert np.array_equal(g["topk_ids"].cpu().numpy(), o["topk_ids"])
+    assert np.allclose(g["topk_lp"].cpu().numpy(), o["topk_lp"], atol=LOGPROB_ATOL, rtol=0)
+    full = g["full"].cpu().numpy()
+    of = o["full"]
+    fin = np.isfinite(of)
+    assert np.array_equal(np.isfinite(full), fin) and np.array_equal(full[~fin], of[~fin])
+    assert np.abs(full[fin] - of[fin]).max() <= LOGPROB_ATOL
+
+
+def test_large_batch_short_rows():
+    """2048 rows of 1000 ids: more rows than compute units, every row mode."""
+    V, B = 1000, 2048
+    x = _row_shapes(79, B, V, "f32")
+    w = random_params(np.random.default_rng(80), B, V)
+    compare_sample(gpu_sample(to_device(x), V, w), oracle_sample(x, V, w))
+
+
 def test_logprobs_ties_and_bad_rows():
     import decode_token_sampling_amd as vs
     V, B = 9000, 5
