@@ -25,6 +25,7 @@ namespace {
 
 constexpr int kLightThreads = 256;
 constexpr int kFullThreads = 1024;
+constexpr int kWaveCutMax = 1024;  // longest gathered list that one wave selects in
 constexpr int kBuckets = kFullBuckets;
 constexpr int kMaxSegs = (VS_MAX_V + kSegMin - 1) / kSegMin;
 
@@ -784,28 +785,116 @@ __device__ void full_topp_cut(const E* __restrict__ rowp, int V, bool aligned, c
 // digits, each round adding the masses of the entries still in play per digit
 // and keeping the digit where the running mass crosses the remainder. The
 // leading bits that every entry shares are skipped; a round that leaves one
-// entry ends the search. False when the gather did not hold the whole bucket;
-// the row then takes the one-workgroup path.
-__device__ bool full_cut_from_list(const Job& j, int row, const RowCfg& c, float m, FullSh& sh,
-                                   RowDesc* d) {
-  const FullCut fc = j.fcut[row];
-  const uint32_t got = j.fcnt[row];
-  if (fc.bucket < 0 || got != fc.count || got > static_cast<uint32_t>(FullSh::kBufCap) || got == 0)
-    return false;  // uniform
-  const int n = static_cast<int>(got);
-  const uint64_t* lst = j.flist + static_cast<size_t>(row) * kFullListCap;
-  uint64_t lo = ~0ull, hi = 0ull;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const uint64_t v = lst[i];
-    sh.buf[i] = v;
-    lo = v < lo ? v : lo;
-    hi = v > hi ? v : hi;
-  }
-  lo = block_min(lo, sh.r64);
-  hi = block_max(hi, sh.r64);
-  const FullTerms ft{m, c.mp};
+// entry ends the search. The workgroup loads the list into sh.buf and each
+// entry's mass into mw (a mass is at most 2^31) with one barrier; then one
+// wave runs the rounds with wave syncs only. lo and hi: the smallest and
+// largest entry. Returns false when the masses fall short of the remainder
+// (not expected: the list holds the whole bucket); the result is the same in
+// every lane.
+__device__ bool wave_cut_from_list(const FullCut& fc, int n, uint64_t lo, uint64_t hi,
+                                   const uint32_t* mw, FullSh& sh, RowDesc* d) {
+  const int l = lane();
   uint64_t rem = fc.rem;  // mass still needed, counted from the top of the bucket
   int rank = 0;           // entries above the digit group in play
+  uint64_t cutv = hi;
+  if (lo != hi) {
+    int shift = ((63 - __clzll(lo ^ hi)) / 8) * 8;
+    uint64_t pmask = (shift + 8 >= 64) ? 0ull : (~0ull << (shift + 8));
+    uint64_t prefix = hi & pmask;
+    for (;;) {  // every condition below is uniform over the wave
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sh.hw[l * 4 + e] = 0ull;
+        sh.hc[l * 4 + e] = 0u;
+      }
+      wave_lds_sync();
+      for (int i = l; i < n; i += kWave) {
+        const uint64_t v = sh.buf[i];
+        if ((v & pmask) == prefix) {
+          const int dg = static_cast<int>((v >> shift) & 255u);
+          atomicAdd(reinterpret_cast<unsigned long long*>(&sh.hw[dg]),
+                    static_cast<unsigned long long>(mw[i]));
+          atomicAdd(&sh.hc[dg], 1u);
+        }
+      }
+      wave_lds_sync();
+      // lane t holds digits 255 - 4t .. 252 - 4t (largest first)
+      uint64_t w4[4];
+      int c4[4];
+      uint64_t lw = 0;
+      int lc = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w4[e] = sh.hw[255 - 4 * l - e];
+        c4[e] = static_cast<int>(sh.hc[255 - 4 * l - e]);
+        lw += w4[e];
+        lc += c4[e];
+      }
+      uint64_t iw = lw;
+      int ic = lc;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const uint64_t tw = __shfl_up(iw, o);
+        const int tc = __shfl_up(ic, o);
+        if (l >= o) {
+          iw += tw;
+          ic += tc;
+        }
+      }
+      uint64_t wb = iw - lw;  // mass of the digits above this lane's
+      int cb = ic - lc;
+      int dg = -1, above = 0, cnt = 0;
+      uint64_t wabove = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (dg < 0 && c4[e] > 0 && wb < rem && rem <= wb + w4[e]) {
+          dg = 255 - 4 * l - e;
+          above = cb;
+          cnt = c4[e];
+          wabove = wb;
+        }
+        wb += w4[e];
+        cb += c4[e];
+      }
+      const uint64_t hit = __ballot(dg >= 0);
+      if (hit == 0ull) return false;  // the list's masses fall short of the remainder
+      const int src = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+      dg = __shfl(dg, src);
+      above = __shfl(above, src);
+      cnt = __shfl(cnt, src);
+      wabove = __shfl(wabove, src);
+      rem -= wabove;
+      rank += above;
+      prefix |= static_cast<uint64_t>(dg) << shift;
+      pmask |= 0xffull << shift;
+      if (cnt == 1) {
+        uint64_t f = 0ull;
+        for (int i = l; i < n; i += kWave)
+          if ((sh.buf[i] & pmask) == prefix) f = sh.buf[i];
+        cutv = wave_max(f);  // the one entry with that prefix
+        break;
+      }
+      if (shift == 0) return false;  // distinct entries: unreachable
+      shift -= 8;
+      wave_lds_sync();  // the bins are cleared again only after every lane has read them
+    }
+  }
+  if (l == 0) {
+    d->mode = kRowFullTopP;
+    d->tau = pkey(cutv);
+    d->id_cut = pid(cutv);
+    d->kept = static_cast<int32_t>(fc.above_c) + rank + 1;
+  }
+  return true;
+}
+
+// The same select over the whole workgroup, for long lists (each round's
+// counting spread over every wave, at the price of a few barriers a round).
+// Called by every thread; the result is the same in every thread.
+__device__ bool block_cut_from_list(const FullCut& fc, int n, uint64_t lo, uint64_t hi,
+                                    const uint32_t* mw, FullSh& sh, RowDesc* d) {
+  uint64_t rem = fc.rem;
+  int rank = 0;
   uint64_t cutv = hi;
   if (lo != hi) {
     int shift = ((63 - __clzll(lo ^ hi)) / 8) * 8;
@@ -821,11 +910,9 @@ __device__ bool full_cut_from_list(const Job& j, int row, const RowCfg& c, float
       for (int i = threadIdx.x; i < n; i += blockDim.x) {
         const uint64_t v = sh.buf[i];
         if ((v & pmask) == prefix) {
-          uint64_t w;
-          int b;
-          if (!ft.mass(key2f(pkey(v)), &w, &b)) w = 0;
           const int dg = static_cast<int>((v >> shift) & 255u);
-          atomicAdd(reinterpret_cast<unsigned long long*>(&sh.hw[dg]), static_cast<unsigned long long>(w));
+          atomicAdd(reinterpret_cast<unsigned long long*>(&sh.hw[dg]),
+                    static_cast<unsigned long long>(mw[i]));
           atomicAdd(&sh.hc[dg], 1u);
         }
       }
@@ -884,10 +971,46 @@ __global__ __launch_bounds__(kFullThreads) void k_row_full(Job j) {
   const RowCfg c = load_cfg(row, j.V, j.T, j.k, j.p, j.mp, j.seeds);
   const float m = d->m;
   if (c.p < 1.0f) {
-    if (!full_cut_from_list(j, row, c, m, sh, d)) {
-      const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
-      full_topp_cut(rowp, j.V, j.aligned, c, m, sh, d);
+    // the gathered list, when it holds the whole cut bucket: its masses once,
+    // then the select by wave 0 alone (the others wait at one barrier), or by
+    // the whole workgroup for a long list
+    const FullCut fc = j.fcut[row];
+    const uint32_t got = j.fcnt[row];
+    const bool listed = fc.bucket >= 0 && got == fc.count && got > 0u &&
+                        got <= static_cast<uint32_t>(FullSh::kBufCap);  // uniform
+    if (listed) {
+      __shared__ int s_done;
+      __shared__ uint32_t mw[kFullListCap];
+      const int n = static_cast<int>(got);
+      const uint64_t* lst = j.flist + static_cast<size_t>(row) * kFullListCap;
+      const FullTerms ft{m, c.mp};
+      uint64_t lo = ~0ull, hi = 0ull;
+      for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const uint64_t v = lst[i];
+        uint64_t w;
+        int b;
+        if (!ft.mass(key2f(pkey(v)), &w, &b)) w = 0;
+        sh.buf[i] = v;
+        mw[i] = static_cast<uint32_t>(w);
+        lo = v < lo ? v : lo;
+        hi = v > hi ? v : hi;
+      }
+      lo = block_min(lo, sh.r64);  // (its barriers also publish buf and mw)
+      hi = block_max(hi, sh.r64);
+      if (n > kWaveCutMax) {
+        if (block_cut_from_list(fc, n, lo, hi, mw, sh, d)) return;  // uniform
+      } else {
+        if (threadIdx.x < kWave) {
+          const bool ok = wave_cut_from_list(fc, n, lo, hi, mw, sh, d);
+          if (threadIdx.x == 0) s_done = ok ? 1 : 0;
+        }
+        __syncthreads();
+        if (s_done) return;  // uniform; else (a list short of the remainder) the full path
+      }
+      __syncthreads();
     }
+    const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
+    full_topp_cut(rowp, j.V, j.aligned, c, m, sh, d);
   } else if (threadIdx.x == 0) {
     d->mode = (c.mp > 0.0f) ? kRowFullMinP : kRowFullNone;
   }
