@@ -18,6 +18,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libvs.so")
+# a test aid with the device exponential alone (never linked into libvs.so)
+SELFTEST_LIB = os.path.join(HERE, "libvs_selftest.so")
+SELFTEST_SOURCES = ["selftest.hip"]
 SOURCES = ["vs_api.hip", "k_select.hip", "k_row.hip", "k_full.hip", "k_state.hip", "k_gumbel.hip",
            "k_penalize.hip"]
 ARCH = os.environ.get("VS_OFFLOAD_ARCH", "gfx950")
@@ -45,18 +48,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + SELFTEST_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], SELFTEST_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {SELFTEST_LIB}")
     return LIB
 
 

@@ -62,6 +62,9 @@ def _load():
         lib.oracle_f32_to_bf16.argtypes = [f32]
         lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
         lib.oracle_exp_scan.argtypes = [f32, f32, ctypes.POINTER(ctypes.c_double)]
+        lib.oracle_exp_compare.argtypes = [ctypes.c_uint32, ctypes.c_uint32, P,
+                                           ctypes.POINTER(ctypes.c_uint32)]
+        lib.oracle_exp_compare.restype = ctypes.c_long
         lib.oracle_exp_scan.restype = ctypes.c_long
         _lib = lib
     return _lib
@@ -180,6 +183,16 @@ def uniform(seed: int, row: int, idx: int) -> float:
 
 def f32_to_bf16(f: float) -> int:
     return _load().oracle_f32_to_bf16(float(f))
+
+
+def exp_compare(lo_bits: int, got: np.ndarray):
+    """Number of got[i] (fp32) whose bits differ from E(float bits lo_bits + i),
+    and the first such i (len(got) if none)."""
+    lib = _load()
+    got = np.ascontiguousarray(got, np.float32)
+    first = ctypes.c_uint32(0)
+    bad = lib.oracle_exp_compare(lo_bits, len(got), _ptr(got), ctypes.byref(first))
+    return int(bad), int(first.value)
 
 
 def exp_scan(lo: float, hi: float):

@@ -314,6 +314,26 @@ int oracle_penalize(void* logits, int dtype, int B, int V, int64_t ld,
   return 0;
 }
 
+long oracle_exp_compare(uint32_t lo_bits, uint32_t n, const float* got, uint32_t* first_bad) {
+  long bad = 0;
+  uint32_t first = n;
+  for (uint32_t i = 0; i < n; ++i) {
+    uint32_t b = lo_bits + i;
+    float t;
+    std::memcpy(&t, &b, sizeof t);
+    const float want = oracle_exp_pinned(t);
+    uint32_t wb, gb;
+    std::memcpy(&wb, &want, sizeof wb);
+    std::memcpy(&gb, &got[i], sizeof gb);
+    if (wb != gb) {
+      if (first == n) first = i;
+      ++bad;
+    }
+  }
+  if (first_bad) *first_bad = first;
+  return bad;
+}
+
 int oracle_topp_decay(int B, float* top_p, const float* top_p_init, const float* decay,
                       const float* top_p_min, const int32_t* reset_ids,
                       const int32_t* sampled, int32_t* row_status) {

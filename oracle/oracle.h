@@ -88,6 +88,10 @@ float oracle_exp_pinned(float t);
 uint64_t oracle_splitmix64(uint64_t x);
 double oracle_uniform(uint64_t seed, int row, int id);
 uint16_t oracle_f32_to_bf16(float f);
+/* got[i] against E(the float with bits lo_bits + i), i < n: returns the number
+ * of results whose bits differ; *first_bad (if not NULL) receives the first
+ * such i, or n. */
+long oracle_exp_compare(uint32_t lo_bits, uint32_t n, const float* got, uint32_t* first_bad);
 /* Exhaustive checks of the pinned exp over every float in [lo, hi] (lo <= hi <= 0):
  * returns the number of monotonicity violations; *max_ulp receives the largest
  * error in fp32 ulps against libm's double exp rounded to float. */

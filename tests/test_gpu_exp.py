@@ -1,0 +1,56 @@
+"""The kernels' device exponential E against the oracle's on every fp32 input
+it can receive, t in [-87, 0] (about 1.1e9 values), bit for bit. E decides
+the min-p and top-p sets, so one disagreement could change a kept set.
+The device side comes from libvs_selftest.so, a test aid built from the same
+device header as libvs.so."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "decode_token_sampling_amd", "libvs_selftest.so")
+NEG_ZERO = 0x80000000          # -0.0
+NEG_87 = 0xC2AE0000            # -87.0; every float in between is negative with larger bits
+CHUNK = 1 << 26
+
+
+@pytest.fixture(scope="module")
+def selftest():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    if not os.path.exists(LIB):
+        raise RuntimeError(f"{LIB} is missing: build it with `python -m decode_token_sampling_amd.build`")
+    lib = ctypes.CDLL(LIB)
+    lib.vs_selftest_exp.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.vs_selftest_exp.restype = ctypes.c_int
+    oracle.build(force=False)
+    return lib
+
+
+def test_device_exp_matches_oracle_everywhere(selftest):
+    assert np.uint32(NEG_87).view(np.float32) == np.float32(-87.0)
+    out = torch.empty(CHUNK, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    total = NEG_87 - NEG_ZERO + 1
+    bad, checked = 0, 0
+    lo = NEG_ZERO
+    while lo <= NEG_87:
+        n = min(CHUNK, NEG_87 - lo + 1)
+        assert selftest.vs_selftest_exp(lo, n, out.data_ptr(), stream) == 0
+        got = out[:n].cpu().numpy()
+        b, first = oracle.exp_compare(lo, got)
+        if b:
+            t = np.uint32(lo + first).view(np.float32)
+            print(f"first disagreement at t = {t!r}: device {got[first]!r}", flush=True)
+        bad += b
+        checked += n
+        lo += n
+    assert checked == total
+    assert bad == 0, f"{bad} inputs disagree"
