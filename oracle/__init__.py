@@ -39,34 +39,38 @@ def build(force: bool = True) -> str:
     return LIB_PATH
 
 
+def _configure(lib):
+    """Argument and result types of the library's entry points."""
+    P = ctypes.c_void_p
+    i32, i64, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    lib.oracle_penalize.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, P, P, P, P]
+    lib.oracle_sample.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, P, P, P, P, P]
+    lib.oracle_sample_row.argtypes = [P, i32, i32, i32, i64, i32, P, P, P, P, P, P, P, P, P, P]
+    lib.oracle_logprobs.argtypes = [P, i32, i32, i32, i64, P, P, i32, P, P, P, P]
+    lib.oracle_topp_decay.argtypes = [i32, P, P, P, P, P, P, P]
+    lib.oracle_seed_advance.argtypes = [i32, P, P]
+    lib.oracle_exp_pinned.argtypes = [f32]
+    lib.oracle_exp_pinned.restype = f32
+    lib.oracle_splitmix64.argtypes = [ctypes.c_uint64]
+    lib.oracle_splitmix64.restype = ctypes.c_uint64
+    lib.oracle_uniform.argtypes = [ctypes.c_uint64, i32, i32]
+    lib.oracle_uniform.restype = ctypes.c_double
+    lib.oracle_f32_to_bf16.argtypes = [f32]
+    lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_exp_scan.argtypes = [f32, f32, ctypes.POINTER(ctypes.c_double)]
+    lib.oracle_exp_scan.restype = ctypes.c_long
+    lib.oracle_exp_compare.argtypes = [ctypes.c_uint32, ctypes.c_uint32, P,
+                                       ctypes.POINTER(ctypes.c_uint32)]
+    lib.oracle_exp_compare.restype = ctypes.c_long
+    return lib
+
+
 def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             build()
-        lib = ctypes.CDLL(LIB_PATH)
-        P = ctypes.c_void_p
-        i32, i64, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_float
-        lib.oracle_penalize.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, P, P, P, P]
-        lib.oracle_sample.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, P, P, P, P, P]
-        lib.oracle_sample_row.argtypes = [P, i32, i32, i32, i64, i32, P, P, P, P, P, P, P, P, P, P]
-        lib.oracle_logprobs.argtypes = [P, i32, i32, i32, i64, P, P, i32, P, P, P, P]
-        lib.oracle_topp_decay.argtypes = [i32, P, P, P, P, P, P, P]
-        lib.oracle_seed_advance.argtypes = [i32, P, P]
-        lib.oracle_exp_pinned.argtypes = [f32]
-        lib.oracle_exp_pinned.restype = f32
-        lib.oracle_splitmix64.argtypes = [ctypes.c_uint64]
-        lib.oracle_splitmix64.restype = ctypes.c_uint64
-        lib.oracle_uniform.argtypes = [ctypes.c_uint64, i32, i32]
-        lib.oracle_uniform.restype = ctypes.c_double
-        lib.oracle_f32_to_bf16.argtypes = [f32]
-        lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
-        lib.oracle_exp_scan.argtypes = [f32, f32, ctypes.POINTER(ctypes.c_double)]
-        lib.oracle_exp_compare.argtypes = [ctypes.c_uint32, ctypes.c_uint32, P,
-                                           ctypes.POINTER(ctypes.c_uint32)]
-        lib.oracle_exp_compare.restype = ctypes.c_long
-        lib.oracle_exp_scan.restype = ctypes.c_long
-        _lib = lib
+        _lib = _configure(ctypes.CDLL(LIB_PATH))
     return _lib
 
 
