@@ -297,6 +297,13 @@ def main():
     dom = "lse_full" if (wl.full_logprobs and "lse_full" in stage_avg) else "select"
     dom_bytes = logit_bytes + (wl.B * wl.V * 4 if wl.full_logprobs else 0)
     dom_ms = stage_avg[dom]
+    duration_source = "per-stage HIP events (eager steps)"
+    if set(stage_ms) == {dom} and len(stage_ms[dom]) == nprof:
+        # the step is this one launch: its average duration is the timed
+        # region's (HIP events around the graph replays on the kernel's
+        # stream, including the gap between consecutive launches)
+        dom_ms = ms_per_step
+        duration_source = "timed region, one launch per step (HIP events)"
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     side = 0
     if wl.has_penalties:
@@ -327,7 +334,8 @@ def main():
         "stages_ms": stage_avg,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "algorithmic_bytes_per_launch": dom_bytes,
+                     "algorithmic_bytes_per_launch": dom_bytes, "launch_ms": dom_ms,
+                     "duration_source": duration_source,
                      "traffic": load_traffic(wl.name, dom)},
     }
     if not args.no_cpu:
