@@ -911,16 +911,24 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
     issue(A, ta);
     issue(Bf, tb);
   }
-  // First round: the maxima of every wave's first tile, if it is a full one.
-  // The k-th largest lane maximum over the workgroup bounds each list's k-th
-  // key from below (k distinct values reach it) and is the pools' starting
-  // bound. (A key of 0 stands for no value; a bound of 0 means no bound yet.)
+  // First round: the maxima of every wave's first two tiles (both buffers),
+  // where they are full ones. The k-th largest lane maximum over the
+  // workgroup bounds each list's k-th key from below (k distinct values reach
+  // it) and is the pools' starting bound; two tiles make it tighter, which
+  // saves more extraction later than the wait for the second one costs. (A
+  // key of 0 stands for no value; a bound of 0 means no bound yet.)
   {
     uint32_t key0 = 0u;
     if (t0 < tf_end) {
       float v[kVals], g[kGroups], lmax;
       unpack_raw<E>(A, rowp, v);
       tile_maxima(v, g, lmax);
+      if (tb < tf_end) {  // the second buffer's tile too (uniform per wave)
+        float v2[kVals], g2[kGroups], lmax2;
+        unpack_raw<E>(Bf, rowp, v2);
+        tile_maxima(v2, g2, lmax2);
+        lmax = __builtin_elementwise_maximum(lmax, lmax2);
+      }
       key0 = f2key(lmax);
     } else if (pf) {
       // the placeholder loads finish here, so that no path reaches the loop
