@@ -43,7 +43,7 @@ LOGPROB_K_MAX = 64
 
 EXPORTED_SYMBOLS = ("vs_workspace_size", "vs_status_string", "vs_penalize", "vs_penalize_ex",
                     "vs_sample", "vs_logprobs", "vs_sample_logprobs", "vs_topp_decay",
-                    "vs_seed_advance", "vs_profile_begin", "vs_profile_end")
+                    "vs_seed_advance", "vs_slot_remap", "vs_profile_begin", "vs_profile_end")
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "workspace too small", 3: "unsupported",
            4: "HIP launch failure"}
@@ -73,6 +73,7 @@ def load() -> ctypes.CDLL:
     lib.vs_penalize_ex.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, P, P, P, P, P]
     lib.vs_topp_decay.argtypes = [i32, P, P, P, P, P, P, P, P]
     lib.vs_seed_advance.argtypes = [i32, P, P, P]
+    lib.vs_slot_remap.argtypes = [i32, i32, P, P, P, i32, P, P]
     lib.vs_sample.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, u32, P, P, P, P, P, sz, P]
     lib.vs_logprobs.argtypes = [P, i32, i32, i32, i64, P, P, i32, P, P, P, i64, P, P, sz, P]
     lib.vs_sample_logprobs.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, u32, P, P, P, P, P,
@@ -80,7 +81,7 @@ def load() -> ctypes.CDLL:
     lib.vs_profile_begin.argtypes = [P, i32]
     lib.vs_profile_end.argtypes = [ctypes.POINTER(ctypes.c_char_p), i32]
     for f in ("vs_workspace_size", "vs_penalize", "vs_penalize_ex", "vs_topp_decay",
-              "vs_seed_advance", "vs_sample", "vs_logprobs",
+              "vs_seed_advance", "vs_slot_remap", "vs_sample", "vs_logprobs",
               "vs_sample_logprobs", "vs_profile_begin", "vs_profile_end"):
         getattr(lib, f).restype = i32
     _lib = lib
@@ -186,6 +187,23 @@ def seed_advance(seeds, sampled_ids=None, stream=None) -> None:
                                   _ptr(sampled_ids, torch.int32, B, "sampled_ids"), _stream(stream))
     if code:
         raise VsError("vs_seed_advance", code)
+
+
+def slot_remap(slot_remap, src, dst, row_status=None, stream=None) -> torch.Tensor:
+    """New slot i takes src[slot_remap[i]] into dst[i] (vs_slot_remap); src and dst
+    are 4- or 8-byte per-row tensors. Returns the per-row status tensor."""
+    B, B_src = slot_remap.shape[0], src.shape[0]
+    if src.element_size() != dst.element_size() or src.element_size() not in (4, 8):
+        raise TypeError("src and dst must hold 4- or 8-byte elements of one size")
+    st = row_status if row_status is not None else torch.empty(B, dtype=torch.int32,
+                                                                device=dst.device)
+    code = load().vs_slot_remap(B, B_src, _ptr(slot_remap, torch.int32, B, "slot_remap"),
+                                _ptr(src, src.dtype, B_src, "src"), _ptr(dst, dst.dtype, B, "dst"),
+                                src.element_size(), _ptr(st, torch.int32, B, "row_status"),
+                                _stream(stream))
+    if code:
+        raise VsError("vs_slot_remap", code)
+    return st
 
 
 def sample(logits, temperature=None, top_k=None, top_p=None, min_p=None, seeds=None, hints=0,

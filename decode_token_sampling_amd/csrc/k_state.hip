@@ -9,6 +9,10 @@
 // README's seed contract; the Tunix sampler folds the decoding step into the
 // key): the seed moves by the SplitMix64 increment, so successive seeds are
 // the generator's successive states.
+//
+// Slot remap (the TT sampling README's decode update contract): new slot i
+// takes the state of old slot slot_remap[i]; a gather from one array into
+// another, 4- or 8-byte elements.
 #include "vs_device.h"
 #include "vs_kernels.h"
 
@@ -52,7 +56,32 @@ __global__ __launch_bounds__(kThreads) void k_seed_advance(int B, uint64_t* __re
   if (!sampled || sampled[r] >= 0) seeds[r] += 0x9E3779B97F4A7C15ull;
 }
 
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_slot_remap(int B, int B_src,
+                                                         const int32_t* __restrict__ remap,
+                                                         const T* __restrict__ src,
+                                                         T* __restrict__ dst,
+                                                         int32_t* __restrict__ out_status) {
+  const int r = blockIdx.x * kThreads + static_cast<int>(threadIdx.x);
+  if (r >= B) return;
+  const int32_t j = remap[r];
+  if (out_status) out_status[r] = (j >= B_src) ? VS_ROW_BAD_PARAM : 0;
+  if (j >= 0 && j < B_src) dst[r] = src[j];  // a negative entry: a new request, left as it is
+}
+
 }  // namespace
+
+hipError_t launch_slot_remap(int B, int B_src, const int32_t* remap, const void* src, void* dst,
+                             int elem_bytes, int32_t* out_status, hipStream_t st) {
+  const dim3 grid((B + kThreads - 1) / kThreads);
+  if (elem_bytes == 4)
+    hipLaunchKernelGGL(k_slot_remap<uint32_t>, grid, dim3(kThreads), 0, st, B, B_src, remap,
+                       static_cast<const uint32_t*>(src), static_cast<uint32_t*>(dst), out_status);
+  else
+    hipLaunchKernelGGL(k_slot_remap<uint64_t>, grid, dim3(kThreads), 0, st, B, B_src, remap,
+                       static_cast<const uint64_t*>(src), static_cast<uint64_t*>(dst), out_status);
+  return hipGetLastError();
+}
 
 hipError_t launch_topp_decay(int B, float* top_p, const float* top_p_init, const float* decay,
                              const float* top_p_min, const int32_t* reset_ids,

@@ -221,6 +221,17 @@ vs_status vs_topp_decay(int B, float* top_p, const float* top_p_init, const floa
   return e == hipSuccess ? VS_OK : VS_ERR_HIP;
 }
 
+vs_status vs_slot_remap(int B, int B_src, const int32_t* slot_remap, const void* src, void* dst,
+                        int elem_bytes, int32_t* out_row_status, hipStream_t stream) {
+  if (B <= 0 || B_src <= 0 || !slot_remap || !src || !dst || src == dst ||
+      (elem_bytes != 4 && elem_bytes != 8))
+    return VS_ERR_INVALID_ARGUMENT;
+  const hipError_t e = stage("slot_remap", stream, [&] {
+    return vsk::launch_slot_remap(B, B_src, slot_remap, src, dst, elem_bytes, out_row_status, stream);
+  });
+  return e == hipSuccess ? VS_OK : VS_ERR_HIP;
+}
+
 vs_status vs_seed_advance(int B, uint64_t* seeds, const int32_t* sampled_ids, hipStream_t stream) {
   if (B <= 0 || !seeds) return VS_ERR_INVALID_ARGUMENT;
   const hipError_t e = stage("seed_advance", stream, [&] {

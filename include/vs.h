@@ -172,6 +172,27 @@ vs_status vs_topp_decay(int B, float* top_p, const float* top_p_init, const floa
 vs_status vs_seed_advance(int B, uint64_t* seeds, const int32_t* sampled_ids, hipStream_t stream);
 
 /*
+ * vs_slot_remap — per-row state follows its request to a new batch slot.
+ *
+ * The TT sampling README's decode update contract: slot_remap[i] = j means
+ * new slot i takes the state of the continuing request from old slot j,
+ * applied once per decode that carries the remap (the caller's duty). Here
+ * one per-row array at a time (seeds, the top-p decay state, parameters):
+ * dst[i] = src[slot_remap[i]] for 0 <= slot_remap[i] < B_src. A negative
+ * entry leaves dst[i] as it is (a new request, which the caller initialises);
+ * an entry >= B_src leaves it too and reports VS_ROW_BAD_PARAM.
+ *
+ *  slot_remap  [B] int32, device.
+ *  src         [B_src] elements of elem_bytes (4 or 8), device.
+ *  dst         [B] elements, device, not src (the old state is read whole).
+ *  out_row_status [B] int32 or NULL.
+ * Errors: VS_ERR_INVALID_ARGUMENT for B or B_src <= 0, a NULL pointer, src ==
+ * dst, or elem_bytes other than 4 and 8.
+ */
+vs_status vs_slot_remap(int B, int B_src, const int32_t* slot_remap, const void* src, void* dst,
+                        int elem_bytes, int32_t* out_row_status, hipStream_t stream);
+
+/*
  * vs_sample — one token per row.
  *
  * Truncation follows the TensorRT-LLM "Sampling" page (same section): greedy

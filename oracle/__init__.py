@@ -49,6 +49,7 @@ def _configure(lib):
     lib.oracle_logprobs.argtypes = [P, i32, i32, i32, i64, P, P, i32, P, P, P, P]
     lib.oracle_topp_decay.argtypes = [i32, P, P, P, P, P, P, P]
     lib.oracle_seed_advance.argtypes = [i32, P, P]
+    lib.oracle_slot_remap.argtypes = [i32, i32, P, P, P, i32, P]
     lib.oracle_exp_pinned.argtypes = [f32]
     lib.oracle_exp_pinned.restype = f32
     lib.oracle_splitmix64.argtypes = [ctypes.c_uint64]
@@ -171,6 +172,17 @@ def seed_advance(seeds, sampled=None):
     """One new seed per row per sampled token, in place on the uint64 array seeds."""
     lib = _load()
     lib.oracle_seed_advance(len(seeds), _ptr(seeds), _ptr(_as(sampled, np.int32)))
+
+
+def slot_remap(remap, src, dst):
+    """dst[i] = src[remap[i]] in place on dst (4- or 8-byte elements); returns row status."""
+    lib = _load()
+    remap = _as(remap, np.int32)
+    assert src.dtype == dst.dtype and src.itemsize in (4, 8) and dst.flags["C_CONTIGUOUS"]
+    st = np.zeros(len(remap), np.int32)
+    lib.oracle_slot_remap(len(remap), len(src), _ptr(remap), _ptr(np.ascontiguousarray(src)),
+                          _ptr(dst), src.itemsize, _ptr(st))
+    return st
 
 
 def exp_pinned(t: float) -> float:

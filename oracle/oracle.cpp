@@ -334,6 +334,18 @@ long oracle_exp_compare(uint32_t lo_bits, uint32_t n, const float* got, uint32_t
   return bad;
 }
 
+int oracle_slot_remap(int B, int B_src, const int32_t* remap, const void* src, void* dst,
+                      int elem_bytes, int32_t* row_status) {
+  for (int i = 0; i < B; ++i) {
+    const int32_t j = remap[i];  // new slot i continues the request of old slot j
+    if (row_status) row_status[i] = (j >= B_src) ? kRowBadParam : 0;
+    if (j < 0 || j >= B_src) continue;
+    std::memcpy(static_cast<char*>(dst) + static_cast<int64_t>(i) * elem_bytes,
+                static_cast<const char*>(src) + static_cast<int64_t>(j) * elem_bytes, elem_bytes);
+  }
+  return 0;
+}
+
 int oracle_topp_decay(int B, float* top_p, const float* top_p_init, const float* decay,
                       const float* top_p_min, const int32_t* reset_ids,
                       const int32_t* sampled, int32_t* row_status) {

@@ -83,6 +83,12 @@ int oracle_topp_decay(int B, float* top_p, const float* top_p_init, const float*
  * row when sampled is NULL). */
 int oracle_seed_advance(int B, uint64_t* seeds, const int32_t* sampled);
 
+/* Slot remap: dst[i] = src[remap[i]] (elements of elem_bytes, 4 or 8) for
+ * 0 <= remap[i] < B_src; a negative entry leaves dst[i]; an entry >= B_src
+ * leaves it and sets status 1. */
+int oracle_slot_remap(int B, int B_src, const int32_t* remap, const void* src, void* dst,
+                      int elem_bytes, int32_t* row_status);
+
 /* Building blocks exposed for the pin tests. */
 float oracle_exp_pinned(float t);
 uint64_t oracle_splitmix64(uint64_t x);

@@ -19,7 +19,7 @@ def _declared():
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["vs_workspace_size", "vs_status_string", "vs_penalize",
                                   "vs_penalize_ex", "vs_sample", "vs_logprobs", "vs_sample_logprobs",
-                                  "vs_topp_decay", "vs_seed_advance",
+                                  "vs_topp_decay", "vs_seed_advance", "vs_slot_remap",
                                   "vs_profile_begin", "vs_profile_end"])
 
 
@@ -48,6 +48,10 @@ def test_host_checks_without_gpu():
     assert lib.vs_topp_decay(0, *([None] * 8)) == 1
     assert lib.vs_topp_decay(4, None, *([None] * 7)) == 1
     assert lib.vs_seed_advance(4, None, None, None) == 1
+    assert lib.vs_slot_remap(4, 4, None, None, None, 4, None, None) == 1
+    p16, p32 = ctypes.c_void_p(16), ctypes.c_void_p(32)  # never dereferenced
+    assert lib.vs_slot_remap(4, 4, p16, p16, p16, 4, None, None) == 1   # src == dst
+    assert lib.vs_slot_remap(4, 4, p16, p16, p32, 2, None, None) == 1   # 2-byte elements
     assert lib.vs_logprobs(None, 0, 4, 10, 10, None, None, 0, None, None, None, 0, None,
                            None, 0, None) == 1
     dummy = ctypes.c_void_p(16)  # never dereferenced: the checks fail first

@@ -105,3 +105,21 @@ def test_decode_loop_with_state():
         oracle.topp_decay(state, p0, decay, g["ids"], top_p_min=floor, reset_ids=reset)
         oracle.seed_advance(seeds, g["ids"])
     assert near <= 2
+
+
+def test_slot_remap_parity():
+    import decode_token_sampling_amd as vs
+    rng = np.random.default_rng(25)
+    for B, B_src, dt in [(300, 300, np.uint64), (257, 400, np.float32), (64, 10, np.int32)]:
+        remap = rng.integers(-1, B_src + 2, B).astype(np.int32)
+        src = rng.integers(0, 2**31, B_src).astype(dt) if dt != np.float32 else rng.random(B_src).astype(dt)
+        dst = np.zeros(B, dt) + dt(3)
+        tdt = {np.uint64: torch.int64, np.float32: torch.float32, np.int32: torch.int32}[dt]
+        sv = torch.from_numpy(src.view(np.int64) if dt == np.uint64 else src).cuda()
+        dv = torch.from_numpy(dst.view(np.int64) if dt == np.uint64 else dst.copy()).cuda()
+        st = vs.slot_remap(dev(remap, np.int32), sv, dv).cpu().numpy()
+        so = oracle.slot_remap(remap, src, dst)
+        assert np.array_equal(st, so)
+        got = dv.cpu().numpy()
+        assert np.array_equal(got.view(np.uint8), dst.view(np.uint8)), (B, B_src, dt)
+        assert sv.dtype == tdt

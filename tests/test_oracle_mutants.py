@@ -42,6 +42,10 @@ MUTANTS = {
     "seed_step_of_one": ("seeds[r] += 0x9E3779B97F4A7C15ull;", "seeds[r] += 1ull;"),
     "logsoftmax_sign": ("auto lp = [&](int j) { return (z[j] - M) - logS; };",
                         "auto lp = [&](int j) { return (z[j] - M) + logS; };"),
+    "slot_remap_scatters": ("    std::memcpy(static_cast<char*>(dst) + static_cast<int64_t>(i) * elem_bytes,\n"
+                            "                static_cast<const char*>(src) + static_cast<int64_t>(j) * elem_bytes, elem_bytes);",
+                            "    std::memcpy(static_cast<char*>(dst) + static_cast<int64_t>(j) * elem_bytes,\n"
+                            "                static_cast<const char*>(src) + static_cast<int64_t>(i) * elem_bytes, elem_bytes);"),
     "logprob_ties_to_highest_id": ("        if (z[a] != z[b]) return z[a] > z[b];\n        return a < b;",
                                    "        if (z[a] != z[b]) return z[a] > z[b];\n        return a > b;"),
 }

@@ -46,6 +46,18 @@ def test_seed_advance_walks_the_splitmix64_states(orc):
     assert int(s[0]) == (2**64 - 1 + 0x9E3779B97F4A7C15) % 2**64
 
 
+def test_slot_remap_hand_case(orc):
+    g = _golden("slot_remap_hand.json")
+    src = np.array(g["old"], np.uint64)
+    dst = np.array(g["dst_before"], np.uint64)
+    st = orc.slot_remap(np.array(g["remap"], np.int32), src, dst)
+    assert dst.tolist() == g["expected"] and st.tolist() == [0, 0, 0, 0]
+    # an entry past the old batch is reported and leaves the slot
+    d2 = np.full(3, 7, np.float32)
+    st = orc.slot_remap(np.array([1, 5, 0], np.int32), np.array([0.5, 0.25], np.float32), d2)
+    assert d2.tolist() == [0.25, 7.0, 0.5] and st.tolist() == [0, 1, 0]
+
+
 def test_topp_decay_hand_sequence(orc):
     g = _golden("topp_decay_hand.json")
     p = np.array([g["top_p_init"]], np.float32)
