@@ -624,8 +624,8 @@ __device__ __forceinline__ uint64_t wave_top_of_pool(const uint64_t* pool, int n
 // and for unaligned rows or outputs.
 template <typename E, bool kStream>
 __device__ __forceinline__ void write_full_row(const Job& j, const E* __restrict__ rowp,
-                                               float* __restrict__ orow, int t_end, float M,
-                                               float logS, int* next) {
+                                               float* __restrict__ orow, int t_begin, int t_end,
+                                               float M, float logS, int* next) {
   constexpr int EPV = Epv<E>::n;
   const int l = lane();
   for (;;) {
@@ -633,6 +633,9 @@ __device__ __forceinline__ void write_full_row(const Job& j, const E* __restrict
     if (l == 0) t = atomicAdd(next, 1);
     t = __builtin_amdgcn_readfirstlane(t);
     if (t >= t_end) break;
+    // last tiles first: the streaming pass read them last, so more of them
+    // are still in the caches
+    t = t_end - 1 - (t - t_begin);
     const int base = t * kSelTile;
     if (j.aligned && j.full_vec && base + kSelTile <= j.V) {  // uniform
       Raw<E> X;
@@ -1108,7 +1111,7 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
       const float nanv = __builtin_nanf("");
       const float M = bad ? nanv : sh.tot_m;
       const float logS = bad ? nanv : logf(sh.tot_s);
-      write_full_row<E, true>(j, rowp, j.out_full + static_cast<int64_t>(row) * j.ld_out, t_end, M,
+      write_full_row<E, true>(j, rowp, j.out_full + static_cast<int64_t>(row) * j.ld_out, t_begin, t_end, M,
                               logS, &sh.next_out);
     }
     return;
