@@ -163,7 +163,12 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
   }
   __syncthreads();
   const int bstar = s_bucket;
-  if (bstar < 0) return;  // uniform; unreachable (the row maximum has mass 2^31)
+  if (bstar < 0) {  // uniform; unreachable (the row maximum has mass 2^31)
+    // no stale record from an earlier call may stand: the cut kernel then
+    // takes its one-workgroup path
+    if (seg == 0 && threadIdx.x == 0) j.fcut[row].bucket = -1;
+    return;
+  }
   if (seg == 0 && threadIdx.x == 0)
     j.fcut[row] = FullCut{bstar, ghc[bstar], target - s_above_w, s_above_c, 0ull};
 
