@@ -42,7 +42,7 @@ TOPK_MAX = 1024
 LOGPROB_K_MAX = 64
 
 EXPORTED_SYMBOLS = ("vs_workspace_size", "vs_status_string", "vs_penalize", "vs_penalize_ex",
-                    "vs_sample", "vs_logprobs", "vs_sample_logprobs", "vs_topp_decay",
+                    "vs_sample", "vs_logprobs", "vs_logprobs_ex", "vs_sample_logprobs", "vs_topp_decay",
                     "vs_seed_advance", "vs_slot_remap", "vs_profile_begin", "vs_profile_end")
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "workspace too small", 3: "unsupported",
@@ -76,12 +76,13 @@ def load() -> ctypes.CDLL:
     lib.vs_slot_remap.argtypes = [i32, i32, P, P, P, i32, P, P]
     lib.vs_sample.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, u32, P, P, P, P, P, sz, P]
     lib.vs_logprobs.argtypes = [P, i32, i32, i32, i64, P, P, i32, P, P, P, i64, P, P, sz, P]
+    lib.vs_logprobs_ex.argtypes = [P, i32, i32, i32, i64, P, P, P, i32, P, P, P, i64, P, P, sz, P]
     lib.vs_sample_logprobs.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, u32, P, P, P, P, P,
                                        i32, P, P, P, i64, P, sz, P]
     lib.vs_profile_begin.argtypes = [P, i32]
     lib.vs_profile_end.argtypes = [ctypes.POINTER(ctypes.c_char_p), i32]
     for f in ("vs_workspace_size", "vs_penalize", "vs_penalize_ex", "vs_topp_decay",
-              "vs_seed_advance", "vs_slot_remap", "vs_sample", "vs_logprobs",
+              "vs_seed_advance", "vs_slot_remap", "vs_sample", "vs_logprobs", "vs_logprobs_ex",
               "vs_sample_logprobs", "vs_profile_begin", "vs_profile_end"):
         getattr(lib, f).restype = i32
     _lib = lib
@@ -239,8 +240,9 @@ def sample(logits, temperature=None, top_k=None, top_p=None, min_p=None, seeds=N
 
 
 def logprobs(logits, token_ids=None, k=0, full=False, V=None, ws=None, out_full=None,
-             row_status=None, stream=None) -> dict:
-    """Log-softmax log-probs (vs_logprobs). Returns dict(token_lp, topk_ids, topk_lp, full, status)."""
+             row_status=None, stream=None, temperature=None) -> dict:
+    """Log-softmax log-probs (vs_logprobs; vs_logprobs_ex at a per-row temperature when
+    one is given). Returns dict(token_lp, topk_ids, topk_lp, full, status)."""
     B, V, ld = _logits_args(logits, V)
     dev = logits.device
     if ws is None:
@@ -253,14 +255,18 @@ def logprobs(logits, token_ids=None, k=0, full=False, V=None, ws=None, out_full=
         fo = torch.empty((B, V), dtype=torch.float32, device=dev)
     ld_out = fo.stride(0) if fo is not None else 0
     st = row_status if row_status is not None else torch.empty(B, dtype=torch.int32, device=dev)
-    code = load().vs_logprobs(
-        logits.data_ptr(), _dtype_code(logits), B, V, ld,
-        _ptr(token_ids, torch.int32, B, "token_ids"), _ptr(tlp, torch.float32, B, "token_lp"),
-        int(k), _ptr(tids, torch.int32, name="topk_ids"), _ptr(tlps, torch.float32, name="topk_lp"),
-        fo.data_ptr() if fo is not None else None, ld_out, _ptr(st, torch.int32, B, "row_status"),
-        _ptr(ws, torch.uint8, name="ws"), ws.numel(), _stream(stream))
+    head = [logits.data_ptr(), _dtype_code(logits), B, V, ld]
+    tail = [_ptr(token_ids, torch.int32, B, "token_ids"), _ptr(tlp, torch.float32, B, "token_lp"),
+            int(k), _ptr(tids, torch.int32, name="topk_ids"), _ptr(tlps, torch.float32, name="topk_lp"),
+            fo.data_ptr() if fo is not None else None, ld_out, _ptr(st, torch.int32, B, "row_status"),
+            _ptr(ws, torch.uint8, name="ws"), ws.numel(), _stream(stream)]
+    if temperature is None:
+        name, code = "vs_logprobs", load().vs_logprobs(*head, *tail)
+    else:
+        name = "vs_logprobs_ex"
+        code = load().vs_logprobs_ex(*head, _ptr(temperature, torch.float32, B, "temperature"), *tail)
     if code:
-        raise VsError("vs_logprobs", code)
+        raise VsError(name, code)
     return dict(token_lp=tlp, topk_ids=tids, topk_lp=tlps, full=fo, status=st)
 
 

@@ -183,13 +183,14 @@ __global__ __launch_bounds__(kThreads) void k_gumbel_final(Job j) {
 }
 
 // lp = (x - max) - log(sum exp(x - max)) for every id of the row.
-template <typename E>
+template <typename E, bool kScaled>
 __global__ __launch_bounds__(kThreads) void k_lse_full(Job j, int ntile, bool out_vec) {
   int row, tile;
   if (!xcd_row_tile(blockIdx.x, j.B, ntile, &row, &tile)) return;
   constexpr int EPV = Epv<E>::n;
   constexpr int NV = kPerThread / EPV;
   const float2 ml = j.rlse[row];
+  const float Tl = kScaled ? lse_T(j, row) : 1.0f;  // the log-prob temperature (1: none)
   const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
   float* orow = j.out_full + static_cast<int64_t>(row) * j.ld_out;
   const int base = tile * kFullTile;
@@ -202,6 +203,10 @@ __global__ __launch_bounds__(kThreads) void k_lse_full(Job j, int ntile, bool ou
       const uint4 raw = load16_stream(rowp + j0);
       float x[EPV];
       unpack16(raw, x, rowp);
+      if (Tl != 1.0f) {  // uniform
+#pragma unroll
+        for (int c = 0; c < EPV; ++c) x[c] = x[c] / Tl;
+      }
 #pragma unroll
       for (int c = 0; c < EPV; c += 4) {
         f32x4 o;
@@ -215,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void k_lse_full(Job j, int ntile, bool ou
 #pragma unroll
       for (int c = 0; c < EPV; ++c) {
         const int id = j0 + c;
-        if (id < j.V) orow[id] = (to_f32(rowp[id]) - ml.x) - ml.y;
+        if (id < j.V) orow[id] = (lse_scaled(to_f32(rowp[id]), Tl) - ml.x) - ml.y;
       }
     }
   }
@@ -242,10 +247,16 @@ hipError_t launch_lse_full(const Job& j, hipStream_t st) {
   const int ntile = (j.V + kFullTile - 1) / kFullTile;
   const int grid = xcd_grid(j.B, ntile);
   const bool out_vec = (reinterpret_cast<uintptr_t>(j.out_full) % 16 == 0) && (j.ld_out % 4 == 0);
-  if (j.dt == VS_F32)
-    hipLaunchKernelGGL(k_lse_full<float>, dim3(grid), dim3(kThreads), 0, st, j, ntile, out_vec);
+  const bool scaled = j.lpT != nullptr && !j.sample;  // the log-prob temperature's instances
+  const dim3 g(grid), b(kThreads);
+  if (j.dt == VS_F32 && scaled)
+    hipLaunchKernelGGL((k_lse_full<float, true>), g, b, 0, st, j, ntile, out_vec);
+  else if (j.dt == VS_F32)
+    hipLaunchKernelGGL((k_lse_full<float, false>), g, b, 0, st, j, ntile, out_vec);
+  else if (scaled)
+    hipLaunchKernelGGL((k_lse_full<uint16_t, true>), g, b, 0, st, j, ntile, out_vec);
   else
-    hipLaunchKernelGGL(k_lse_full<uint16_t>, dim3(grid), dim3(kThreads), 0, st, j, ntile, out_vec);
+    hipLaunchKernelGGL((k_lse_full<uint16_t, false>), g, b, 0, st, j, ntile, out_vec);
   return hipGetLastError();
 }
 

@@ -641,7 +641,7 @@ __global__ __launch_bounds__(kLightThreads) void k_row_light(Job j) {
         n = pl.shared
                 ? union_topk(mrow, crowA, kthA, ntile, 0, kMetaOverflowA, k, sh)
                 : union_topk(mrow, crowB, kthB, ntile, kMetaCountBShift, kMetaOverflowB, k, sh);
-        if (n < 0) n = slow_topk(rowp, j.V, aligned, 1.0f, k, sh);
+        if (n < 0) n = slow_topk(rowp, j.V, aligned, lse_T(j, row), k, sh);
       }
       for (int i = threadIdx.x; i < k; i += blockDim.x) {
         if (i < n) {
@@ -663,7 +663,9 @@ __global__ __launch_bounds__(kLightThreads) void k_row_light(Job j) {
       const int tok = j.tok[row];
       const bool badtok = tok < 0 || tok >= j.V;
       if (badtok) st |= VS_ROW_BAD_TOKEN_ID;
-      j.out_tok_lp[row] = (bad_logits || badtok) ? nanv : (logit_at<E>(j, row, tok) - M) - logS;
+      j.out_tok_lp[row] = (bad_logits || badtok)
+                              ? nanv
+                              : (lse_scaled(logit_at<E>(j, row, tok), lse_T(j, row)) - M) - logS;
     }
     if (j.out_lp_status) j.out_lp_status[row] = st;
   }

@@ -76,21 +76,27 @@ __device__ __forceinline__ void load_raw(const E* __restrict__ base, int stride,
   }
 }
 
+// Tl: the log-prob temperature of the row (1: the values as they are).
 template <typename E>
-__device__ __forceinline__ void unpack_raw(const Raw<E>& raw, const E* rowp, float (&v)[kVals]) {
+__device__ __forceinline__ void unpack_raw(const Raw<E>& raw, const E* rowp, float (&v)[kVals],
+                                           float Tl) {
   constexpr int EPV = Epv<E>::n;
 #pragma unroll
   for (int i = 0; i < Raw<E>::n; ++i) unpack16(raw.r[i], &v[i * EPV], rowp);
+  if (Tl != 1.0f) {  // uniform
+#pragma unroll
+    for (int q = 0; q < kVals; ++q) v[q] = v[q] / Tl;
+  }
 }
 
 // A tile that ends past V: element loads, -inf beyond V.
 template <typename E>
 __device__ __forceinline__ void load_tail(const E* __restrict__ rowp, int tile_base, int V,
-                                          float (&v)[kVals]) {
+                                          float (&v)[kVals], float Tl) {
 #pragma unroll
   for (int q = 0; q < kVals; ++q) {
     const int idx = elem_index<E>(tile_base, q);
-    v[q] = (idx < V) ? to_f32(rowp[idx]) : -kInf;
+    v[q] = (idx < V) ? lse_scaled(to_f32(rowp[idx]), Tl) : -kInf;
   }
 }
 
@@ -625,7 +631,7 @@ __device__ __forceinline__ uint64_t wave_top_of_pool(const uint64_t* pool, int n
 template <typename E, bool kStream>
 __device__ __forceinline__ void write_full_row(const Job& j, const E* __restrict__ rowp,
                                                float* __restrict__ orow, int t_begin, int t_end,
-                                               float M, float logS, int* next) {
+                                               float M, float logS, float Tl, int* next) {
   constexpr int EPV = Epv<E>::n;
   const int l = lane();
   for (;;) {
@@ -644,6 +650,10 @@ __device__ __forceinline__ void write_full_row(const Job& j, const E* __restrict
       for (int i = 0; i < Raw<E>::n; ++i) {
         float x[EPV];
         unpack16(X.r[i], x, rowp);
+        if (Tl != 1.0f) {  // uniform
+#pragma unroll
+          for (int c = 0; c < EPV; ++c) x[c] = x[c] / Tl;
+        }
         const int j0 = base + (i * kWave + l) * EPV;
 #pragma unroll
         for (int c = 0; c < EPV; c += 4) {
@@ -659,7 +669,7 @@ __device__ __forceinline__ void write_full_row(const Job& j, const E* __restrict
 #pragma unroll
       for (int q = 0; q < kVals; ++q) {
         const int id = elem_index<E>(base, q);
-        if (id < j.V) orow[id] = (to_f32(rowp[id]) - M) - logS;
+        if (id < j.V) orow[id] = (lse_scaled(to_f32(rowp[id]), Tl) - M) - logS;
       }
     }
   }
@@ -732,7 +742,7 @@ __device__ __forceinline__ void finish_row(const Job& j, int row, const Plan& pl
     if (tok < 0 || tok >= j.V)
       lp_st |= VS_ROW_BAD_TOKEN_ID;
     else if (!bad_logits)
-      x_tok = to_f32(rowp[tok]);
+      x_tok = lse_scaled(to_f32(rowp[tok]), lse_T(j, row));
   }
   // the top-k log-probabilities' source
   uint64_t P = 0ull;
@@ -775,7 +785,7 @@ __device__ __forceinline__ void finish_row(const Job& j, int row, const Plan& pl
   }
 }
 
-template <typename E, bool kStream>
+template <typename E, bool kStream, bool kScaled>
 __global__ __launch_bounds__(1024) void k_select(Job j) {
   __shared__ SegSh sh;
   int row, seg;
@@ -786,6 +796,10 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int l = lane();
   const Plan pl = plan_row(j, row);
+  // the log-prob temperature (kScaled: vs_logprobs_ex; 1 otherwise, known at
+  // compile time): every value is read as x / Tl, so the log-sum-exp, the
+  // lists and the writes see s
+  const float Tl = kScaled ? lse_T(j, row) : 1.0f;
   const int t_begin = seg * j.tps;
   const int t_end = min(t_begin + j.tps, j.ntile);
 
@@ -924,11 +938,11 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
     uint32_t key0 = 0u;
     if (t0 < tf_end) {
       float v[kVals], g[kGroups], lmax;
-      unpack_raw<E>(A, rowp, v);
+      unpack_raw<E>(A, rowp, v, Tl);
       tile_maxima(v, g, lmax);
       if (tb < tf_end) {  // the second buffer's tile too (uniform per wave)
         float v2[kVals], g2[kGroups], lmax2;
-        unpack_raw<E>(Bf, rowp, v2);
+        unpack_raw<E>(Bf, rowp, v2, Tl);
         tile_maxima(v2, g2, lmax2);
         lmax = __builtin_elementwise_maximum(lmax, lmax2);
       }
@@ -964,7 +978,7 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
     while (ta < tf_end) {
       {
         float v[kVals], g[kGroups], lmax;
-        unpack_raw<E>(A, rowp, v);
+        unpack_raw<E>(A, rowp, v, Tl);
         tile_maxima(v, g, lmax);
         step(v, g, lmax, ta, true);
       }
@@ -973,7 +987,7 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
       if (tb >= tf_end) break;
       {
         float v[kVals], g[kGroups], lmax;
-        unpack_raw<E>(Bf, rowp, v);
+        unpack_raw<E>(Bf, rowp, v, Tl);
         tile_maxima(v, g, lmax);
         step(v, g, lmax, tb, true);
       }
@@ -988,7 +1002,7 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
               : t0;
   for (; tt < t_end; tt = pf ? t_end : tt + W) {
     float v[kVals], g[kGroups], lmax;
-    load_tail<E>(rowp, tt * kSelTile, j.V, v);
+    load_tail<E>(rowp, tt * kSelTile, j.V, v, Tl);
     tile_maxima(v, g, lmax);
     step(v, g, lmax, tt, false);
   }
@@ -1040,7 +1054,10 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
 #pragma unroll 1
       for (int li = 0; li < 2; ++li) {
         if (li == 0 ? rsA : rsB)
-          rescan_list<E>(rowp, j.V, j.aligned, li == 0 ? pl.TA : 1.0f, W, sh.stage, sh.srt[li]);
+          // (Tl is 1 in a sampling call and TA is 1 in a log-prob call: the
+          // product is the one of them that applies, exactly)
+          rescan_list<E>(rowp, j.V, j.aligned, (li == 0 ? pl.TA : 1.0f) * Tl, W, sh.stage,
+                         sh.srt[li]);
       }
     }
     const bool noise = j.sample && pl.kA > 1 && !rsA && W > 2;  // the table is filled
@@ -1112,7 +1129,7 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
       const float M = bad ? nanv : sh.tot_m;
       const float logS = bad ? nanv : logf(sh.tot_s);
       write_full_row<E, true>(j, rowp, j.out_full + static_cast<int64_t>(row) * j.ld_out, t_begin, t_end, M,
-                              logS, &sh.next_out);
+                              logS, Tl, &sh.next_out);
     }
     return;
   }
@@ -1182,16 +1199,26 @@ hipError_t launch_select(const Job& j, hipStream_t st) {
                        (!j.out_full &&
                         (!j.sample || (j.hints & (VS_HINT_NO_FULLVOCAB | VS_HINT_ALL_GREEDY |
                                                   VS_HINT_SMALL_TOPK)))));
+  // (instances with the log-prob temperature only for calls that pass one)
+  const bool scaled = j.lpT != nullptr && !j.sample;
   if (j.dt == VS_F32) {
-    if (stream)
-      hipLaunchKernelGGL((k_select<float, true>), dim3(grid), block, lds, st, j);
+    if (scaled && stream)
+      hipLaunchKernelGGL((k_select<float, true, true>), dim3(grid), block, lds, st, j);
+    else if (scaled)
+      hipLaunchKernelGGL((k_select<float, false, true>), dim3(grid), block, lds, st, j);
+    else if (stream)
+      hipLaunchKernelGGL((k_select<float, true, false>), dim3(grid), block, lds, st, j);
     else
-      hipLaunchKernelGGL((k_select<float, false>), dim3(grid), block, lds, st, j);
+      hipLaunchKernelGGL((k_select<float, false, false>), dim3(grid), block, lds, st, j);
   } else {
-    if (stream)
-      hipLaunchKernelGGL((k_select<uint16_t, true>), dim3(grid), block, lds, st, j);
+    if (scaled && stream)
+      hipLaunchKernelGGL((k_select<uint16_t, true, true>), dim3(grid), block, lds, st, j);
+    else if (scaled)
+      hipLaunchKernelGGL((k_select<uint16_t, false, true>), dim3(grid), block, lds, st, j);
+    else if (stream)
+      hipLaunchKernelGGL((k_select<uint16_t, true, false>), dim3(grid), block, lds, st, j);
     else
-      hipLaunchKernelGGL((k_select<uint16_t, false>), dim3(grid), block, lds, st, j);
+      hipLaunchKernelGGL((k_select<uint16_t, false, false>), dim3(grid), block, lds, st, j);
   }
   return hipGetLastError();
 }

@@ -329,6 +329,17 @@ vs_status vs_logprobs(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
                       int32_t* out_topk_ids, float* out_topk_logprobs,
                       float* out_full, int64_t ld_out, int32_t* out_row_status,
                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  return vs_logprobs_ex(logits, dt, B, V, ld, nullptr, token_ids, out_token_logprob, k,
+                        out_topk_ids, out_topk_logprobs, out_full, ld_out, out_row_status, ws,
+                        ws_bytes, stream);
+}
+
+vs_status vs_logprobs_ex(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
+                         const float* temperature, const int32_t* token_ids,
+                         float* out_token_logprob, int k, int32_t* out_topk_ids,
+                         float* out_topk_logprobs, float* out_full, int64_t ld_out,
+                         int32_t* out_row_status, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
   if (!logits || !ws || !sizes_ok(dt, B, V, ld)) return VS_ERR_INVALID_ARGUMENT;
   if ((token_ids == nullptr) != (out_token_logprob == nullptr)) return VS_ERR_INVALID_ARGUMENT;
   if (k < 0 || k > VS_LOGPROB_K_MAX || k > V) return VS_ERR_INVALID_ARGUMENT;
@@ -345,6 +356,7 @@ vs_status vs_logprobs(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
   j.out_full = out_full;
   j.ld_out = ld_out;
   j.out_lp_status = out_row_status;
+  j.lpT = temperature;
   // with one segment per row the streaming pass finishes every row (and then
   // writes the full log-softmax itself)
   j.full_in_select = (out_full && j.nseg == 1) ? 1 : 0;

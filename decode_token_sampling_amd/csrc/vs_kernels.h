@@ -103,6 +103,7 @@ struct Job {
   float* out_full;
   int64_t ld_out;
   int32_t* out_lp_status;  // vs_logprobs status
+  const float* lpT;        // [B] temperature of the log-probs (vs_logprobs_ex), or NULL
   // full-vocabulary top-p (per row): mass histogram, the cut bucket's ids
   uint64_t* fhw;       // [B][kFullBuckets] masses
   uint32_t* fhc;       // [B][kFullBuckets] counts
@@ -159,6 +160,17 @@ __device__ __forceinline__ Plan plan_row(const Job& j, int row) {
   }
   return pl;
 }
+
+// The temperature the log-probs of a row are taken at: vs_logprobs_ex's per-row
+// temperature when it is positive and finite, else 1 (never in a sampling
+// call). Every read of the logits in the log-prob path divides by it, so that
+// the log-softmax is that of s = x / T rounded to fp32.
+__device__ __forceinline__ float lse_T(const Job& j, int row) {
+  if (!j.lpT || j.sample) return 1.0f;
+  const float t = j.lpT[row];
+  return (t > 0.0f && t <= 3.40282347e38f) ? t : 1.0f;
+}
+__device__ __forceinline__ float lse_scaled(float x, float T) { return T == 1.0f ? x : x / T; }
 
 struct WsLayout {
   int ntile, ntile3;

@@ -271,6 +271,25 @@ vs_status vs_logprobs(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
                       void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * vs_logprobs_ex — vs_logprobs at a temperature per row ("processed"
+ * log-probs): the log-softmax of s = x / T, with s rounded to fp32 as the
+ * sampling step forms it (the TensorRT-LLM page: temperature divides the
+ * logits; the Tunix sampler divides by the temperature before its softmax).
+ * lp_j = (s_j - max s) - log(sum exp(s - max s)); the top-k are the k largest
+ * s. A row whose T is not positive and finite takes T = 1; a row where x / T
+ * overflows to +inf is a row with bad logits.
+ *
+ *  temperature [B] fp32, device, or NULL (exactly vs_logprobs). Every other
+ *              argument, and the errors, as vs_logprobs.
+ */
+vs_status vs_logprobs_ex(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
+                         const float* temperature, const int32_t* token_ids,
+                         float* out_token_logprob, int k, int32_t* out_topk_ids,
+                         float* out_topk_logprobs, float* out_full, int64_t ld_out,
+                         int32_t* out_row_status, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/*
  * Profiling aid (not part of the sampling step). While active on the calling
  * host thread, every kernel stage that a vs_* call enqueues is bracketed by
  * hipEventRecord(events[2i]) and hipEventRecord(events[2i+1]) on that call's

@@ -47,6 +47,7 @@ def _configure(lib):
     lib.oracle_sample.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, P, P, P, P, P]
     lib.oracle_sample_row.argtypes = [P, i32, i32, i32, i64, i32, P, P, P, P, P, P, P, P, P, P]
     lib.oracle_logprobs.argtypes = [P, i32, i32, i32, i64, P, P, i32, P, P, P, P]
+    lib.oracle_logprobs_t.argtypes = [P, i32, i32, i32, i64, P, P, P, i32, P, P, P, P]
     lib.oracle_topp_decay.argtypes = [i32, P, P, P, P, P, P, P]
     lib.oracle_seed_advance.argtypes = [i32, P, P]
     lib.oracle_slot_remap.argtypes = [i32, i32, P, P, P, i32, P]
@@ -141,8 +142,9 @@ def sample(logits, V, temperature, top_k, top_p, min_p, seeds, want_mask=False, 
     return out
 
 
-def logprobs(logits, V, token_ids=None, k=0, full=False):
-    """Log-softmax log-probs in fp64. Returns dict(token_lp, topk_ids, topk_lp, full, status)."""
+def logprobs(logits, V, token_ids=None, k=0, full=False, temperature=None):
+    """Log-softmax log-probs in fp64 (of x / T per row when temperature is given).
+    Returns dict(token_lp, topk_ids, topk_lp, full, status)."""
     lib = _load()
     B, ld = logits.shape
     tok = _as(token_ids, np.int32)
@@ -151,8 +153,9 @@ def logprobs(logits, V, token_ids=None, k=0, full=False):
     tlps = np.zeros((B, max(k, 0)), np.float64)
     fullo = np.zeros((B, V), np.float64) if full else None
     st = np.zeros(B, np.int32)
-    lib.oracle_logprobs(_ptr(logits), _dtype_code(logits), B, V, ld, _ptr(tok), _ptr(tlp), k,
-                        _ptr(tids), _ptr(tlps), _ptr(fullo), _ptr(st))
+    Tv = _as(temperature, np.float32)
+    lib.oracle_logprobs_t(_ptr(logits), _dtype_code(logits), B, V, ld, _ptr(Tv), _ptr(tok),
+                          _ptr(tlp), k, _ptr(tids), _ptr(tlps), _ptr(fullo), _ptr(st))
     return dict(token_lp=tlp, topk_ids=tids, topk_lp=tlps, full=fullo, status=st)
 
 

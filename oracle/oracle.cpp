@@ -410,13 +410,34 @@ int oracle_logprobs(const void* logits, int dtype, int B, int V, int64_t ld,
                     const int32_t* token_ids, double* out_token_lp, int k,
                     int32_t* out_topk_ids, double* out_topk_lp,
                     double* out_full, int32_t* row_status) {
+  return oracle_logprobs_t(logits, dtype, B, V, ld, nullptr, token_ids, out_token_lp, k,
+                           out_topk_ids, out_topk_lp, out_full, row_status);
+}
+
+int oracle_logprobs_t(const void* logits, int dtype, int B, int V, int64_t ld,
+                      const float* temperature, const int32_t* token_ids, double* out_token_lp,
+                      int k, int32_t* out_topk_ids, double* out_topk_lp, double* out_full,
+                      int32_t* row_status) {
   const double nan = std::numeric_limits<double>::quiet_NaN();
   std::vector<double> z(V);
   std::vector<int> order(V);
   for (int r = 0; r < B; ++r) {
     const int64_t base = static_cast<int64_t>(r) * ld;
     int status = 0;
-    if (row_logits_bad(logits, dtype, base, V)) status |= kRowBadLogits;
+    // The log-probs are those of s = x / T, one rounded fp32 division as the
+    // sampling step forms s; a temperature that is not positive and finite
+    // means T = 1. The row checks apply to s (x / T may overflow).
+    float T = temperature ? temperature[r] : 1.0f;
+    if (!(T > 0.0f && T <= std::numeric_limits<float>::max())) T = 1.0f;
+    bool all_neg_inf = true, bad = false;
+    for (int j = 0; j < V; ++j) {
+      const float x = load_logit(logits, dtype, base + j);
+      const float s = (T == 1.0f) ? x : x / T;
+      if (std::isnan(s) || s == std::numeric_limits<float>::infinity()) bad = true;
+      if (s != -std::numeric_limits<float>::infinity()) all_neg_inf = false;
+      z[j] = static_cast<double>(s);
+    }
+    if (bad || all_neg_inf) status |= kRowBadLogits;
     if (token_ids && (token_ids[r] < 0 || token_ids[r] >= V)) status |= kRowBadTokenId;
     if (row_status) row_status[r] = status;
     if (status & kRowBadLogits) {
@@ -431,7 +452,6 @@ int oracle_logprobs(const void* logits, int dtype, int B, int V, int64_t ld,
     }
     // Numerically stable log-softmax: subtract the row max, sum the
     // exponentials, subtract the log of the sum.
-    for (int j = 0; j < V; ++j) z[j] = static_cast<double>(load_logit(logits, dtype, base + j));
     double M = z[0];
     for (int j = 1; j < V; ++j) M = std::max(M, z[j]);
     double S = 0.0;

@@ -61,6 +61,13 @@ int oracle_sample_row(const void* logits, int dtype, int B, int V, int64_t ld,
                       int32_t* out_kept_count, uint8_t* out_kept_mask,
                       double* out_top2, int32_t* row_status);
 
+/* The same at a temperature per row: the log-softmax of s = x / T (fp32
+ * division); temperature NULL, or a T that is not positive and finite, means
+ * T = 1. */
+int oracle_logprobs_t(const void* logits, int dtype, int B, int V, int64_t ld,
+                      const float* temperature, const int32_t* token_ids, double* out_token_lp,
+                      int k, int32_t* out_topk_ids, double* out_topk_lp, double* out_full,
+                      int32_t* row_status);
 /* token_ids/out_token_lp may be NULL; out_full (B*V doubles) may be NULL. */
 int oracle_logprobs(const void* logits, int dtype, int B, int V, int64_t ld,
                     const int32_t* token_ids, double* out_token_lp, int k,

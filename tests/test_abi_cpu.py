@@ -18,7 +18,8 @@ def _declared():
 
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["vs_workspace_size", "vs_status_string", "vs_penalize",
-                                  "vs_penalize_ex", "vs_sample", "vs_logprobs", "vs_sample_logprobs",
+                                  "vs_penalize_ex", "vs_sample", "vs_logprobs", "vs_logprobs_ex",
+                                  "vs_sample_logprobs",
                                   "vs_topp_decay", "vs_seed_advance", "vs_slot_remap",
                                   "vs_profile_begin", "vs_profile_end"])
 
@@ -54,6 +55,8 @@ def test_host_checks_without_gpu():
     assert lib.vs_slot_remap(4, 4, p16, p16, p32, 2, None, None) == 1   # 2-byte elements
     assert lib.vs_logprobs(None, 0, 4, 10, 10, None, None, 0, None, None, None, 0, None,
                            None, 0, None) == 1
+    assert lib.vs_logprobs_ex(None, 0, 4, 10, 10, None, None, None, 0, None, None, None, 0,
+                              None, None, 0, None) == 1
     dummy = ctypes.c_void_p(16)  # never dereferenced: the checks fail first
     assert lib.vs_sample(dummy, 0, 4, 10, 9, *([None] * 5), 0, dummy, None, None, None,
                          dummy, 1 << 30, None) == 1          # ld < V

@@ -337,6 +337,46 @@ def test_large_batch_short_rows():
     compare_sample(gpu_sample(to_device(x), V, w), oracle_sample(x, V, w))
 
 
+def _temperatures(rng, B):
+    T = rng.choice([1.0, 0.5, 0.7, 1.3, 2.5], B).astype(np.float32)
+    T[0], T[1 % B], T[2 % B] = 0.0, -1.0, np.nan
+    if B > 3:
+        T[3] = np.inf
+    return T
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V,B", [(64, 9), (4097, 9), (33333, 9), (70001, 9), (9000, 320), (40000, 320)])
+def test_logprobs_at_temperature(V, B, dtype):
+    """vs_logprobs_ex: the log-softmax of x / T per row (T not positive and
+    finite: 1) against the oracle; 9 rows take several segments each (the row
+    kernel merges them), 320 rows one segment each (the streaming pass finishes
+    them and writes the full row itself)."""
+    import decode_token_sampling_amd as vs
+    x = _row_shapes(90 + V, B, V, dtype)
+    rng = np.random.default_rng(V + B)
+    T = _temperatures(rng, B)
+    if dtype == "f32" and B > 5:
+        x[5, 7] = np.float32(3e38)   # x / T overflows on a row with T < 1
+        T[5] = np.float32(0.5)
+    tok = rng.integers(0, V, B).astype(np.int32)
+    k = min(V, 20)
+    g = vs.logprobs(to_device(x), dev(tok, np.int32), k=k, full=True, V=V, temperature=dev(T, np.float32))
+    torch.cuda.synchronize()
+    o = oracle.logprobs(x, V, tok, k=k, full=True, temperature=T)
+    assert np.array_equal(g["status"].cpu().numpy(), o["status"])
+    assert np.allclose(g["token_lp"].cpu().numpy(), o["token_lp"], atol=LOGPROB_ATOL, rtol=0,
+                       equal_nan=True)
+    assert np.array_equal(g["topk_ids"].cpu().numpy(), o["topk_ids"])
+    assert np.allclose(g["topk_lp"].cpu().numpy(), o["topk_lp"], atol=LOGPROB_ATOL, rtol=0,
+                       equal_nan=True)
+    full, of = g["full"].cpu().numpy(), o["full"]
+    finf = np.isfinite(of)
+    assert np.array_equal(np.isfinite(full), finf)
+    assert np.array_equal(np.isnan(full), np.isnan(of))
+    assert np.abs(full[finf] - of[finf]).max() <= LOGPROB_ATOL
+
+
 def test_logprobs_ties_and_bad_rows():
     import decode_token_sampling_amd as vs
     V, B = 9000, 5

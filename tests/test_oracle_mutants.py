@@ -46,6 +46,8 @@ MUTANTS = {
                             "                static_cast<const char*>(src) + static_cast<int64_t>(j) * elem_bytes, elem_bytes);",
                             "    std::memcpy(static_cast<char*>(dst) + static_cast<int64_t>(j) * elem_bytes,\n"
                             "                static_cast<const char*>(src) + static_cast<int64_t>(i) * elem_bytes, elem_bytes);"),
+    "logprob_temperature_multiplies": ("const float s = (T == 1.0f) ? x : x / T;",
+                                       "const float s = (T == 1.0f) ? x : x * T;"),
     "logprob_ties_to_highest_id": ("        if (z[a] != z[b]) return z[a] > z[b];\n        return a < b;",
                                    "        if (z[a] != z[b]) return z[a] > z[b];\n        return a > b;"),
 }

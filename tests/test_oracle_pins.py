@@ -504,6 +504,35 @@ def test_logsoftmax_normalised_and_topk_brute(orc):
     assert out["token_lp"][0] == -np.inf and out["topk_ids"][0].tolist() == [2, 0, 1]
 
 
+def test_logsoftmax_at_temperature(orc):
+    """Processed log-probs (vs_logprobs_ex): T = 1, T <= 0 and NaN give the plain
+    log-softmax bit for bit; logits doubled at T = 2 give exactly the plain
+    result (2x / 2 = x in fp32); a two-level row matches its closed form; an
+    overflow of x / T makes the row invalid."""
+    rng = np.random.default_rng(41)
+    B, V = 5, 700
+    x = (rng.normal(0, 3, (B, V))).astype(np.float32)
+    plain = orc.logprobs(x, V, k=7, full=True)
+    for T in (1.0, 0.0, -2.0, float("nan")):
+        got = orc.logprobs(x, V, k=7, full=True, temperature=np.full(B, T, np.float32))
+        assert np.array_equal(got["full"], plain["full"]) and np.array_equal(got["topk_ids"], plain["topk_ids"]), T
+    doubled = orc.logprobs(2 * x, V, k=7, full=True, temperature=np.full(B, 2.0, np.float32))
+    assert np.array_equal(doubled["full"], plain["full"])
+    assert np.array_equal(doubled["topk_ids"], plain["topk_ids"])
+    # two levels a (n1 ids) and b (n2 ids): lp_a = -log(n1 + n2 exp((b - a) / T))
+    a, b, n1, T = 3.0, 1.0, 4, 0.5
+    row = np.full((1, V), b, np.float32)
+    row[0, :n1] = a
+    o = orc.logprobs(row, V, full=True, temperature=np.array([T], np.float32))
+    want_a = -np.log(n1 + (V - n1) * np.exp((b - a) / T))
+    assert abs(o["full"][0, 0] - want_a) < 1e-12
+    assert abs(o["full"][0, -1] - (want_a + (b - a) / T)) < 1e-12
+    big = np.full((1, V), 1.0, np.float32)
+    big[0, 3] = 3e38
+    o = orc.logprobs(big, V, k=1, temperature=np.array([1e-3], np.float32))
+    assert o["status"][0] == 2 and o["topk_ids"][0, 0] == -1
+
+
 def test_logsoftmax_bad_rows(orc):
     x = np.array([[0.0, np.nan], [-np.inf, -np.inf], [1.0, 2.0]], np.float32)
     out = orc.logprobs(x, 2, np.array([0, 0, 5], np.int32), k=1)
