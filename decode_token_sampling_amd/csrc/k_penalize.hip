@@ -1,8 +1,9 @@
 // vs_penalize: occurrence penalties in place, one 1024-thread workgroup per row.
 //
 // The history of a row is its prompt ids followed by its output ids (CSR). The
-// workgroup counts occurrences in an LDS open-addressing hash table (16384
-// slots of id and count) and then rewrites each distinct id's logit once:
+// workgroup counts occurrences in an LDS open-addressing hash table (of
+// 2^10..2^14 slots of id and count, by the history's length) and then
+// rewrites each distinct id's logit once:
 // repetition (divide a non-negative logit, multiply a negative one), presence,
 // frequency times the count, each a separately rounded fp32 operation
 // (TensorRT-LLM "Sampling", occurrence-penalty bullets). With a prompt ignore
@@ -25,8 +26,9 @@ constexpr int kSlots = 1 << kSlotsLog2;
 constexpr uint32_t kEmpty = 0xffffffffu;
 
 __device__ __forceinline__ uint32_t class_hash(uint32_t id) { return id * 0x9E3779B1u; }
-__device__ __forceinline__ uint32_t slot_hash(uint32_t id) {
-  return (id * 0x2545F491u) >> (32 - kSlotsLog2);
+// Slot of an id in a table of 2^lgs slots: the top lgs bits of its hash.
+__device__ __forceinline__ uint32_t slot_hash(uint32_t id, int lgs) {
+  return (id * 0x2545F491u) >> (32 - lgs);
 }
 // Class of an id among Q = 2^lq classes: the top lq bits of its hash.
 __device__ __forceinline__ uint32_t id_class(uint32_t id, int lq) {
@@ -67,6 +69,12 @@ __global__ __launch_bounds__(kThreads) void k_penalize(
   const int o0 = (oids && ooff) ? ooff[row] : 0;
   const int lo = (oids && ooff) ? ooff[row + 1] - o0 : 0;
   const int L = lp + lo;
+  // The table in use: the smallest power of two of at least twice the
+  // history, between 2^10 and kSlots slots (clearing and scanning it is most
+  // of the work for short histories).
+  int lgs = 10;
+  while ((1 << lgs) < 2 * L && lgs < kSlotsLog2) ++lgs;
+  const int S = 1 << lgs;
   // the prompt ids [0, nign) count for repetition only (clamped to the prompt)
   const int nign = pignore ? min(max(pignore[row], 0), lp) : 0;
   E* rowp = logits + static_cast<int64_t>(row) * ld;
@@ -79,7 +87,7 @@ __global__ __launch_bounds__(kThreads) void k_penalize(
     if (!bad && L > 0) {
       // start with enough classes for about half a table of ids each
       int lq = 0;
-      while ((static_cast<int64_t>(kSlots / 2) << lq) < L && lq < 31) ++lq;
+      while ((static_cast<int64_t>(S / 2) << lq) < L && lq < 31) ++lq;
       // push every class of that level (in reverse so class 0 pops first);
       // at most 64 entries: lq <= 5 is enough for 2^19 history ids per row, and
       // longer histories are split further on overflow.
@@ -105,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void k_penalize(
     if (top == 0) break;
     const int lq = s_stack_lq[top - 1];
     const uint32_t q = s_stack_q[top - 1];
-    for (int i = threadIdx.x; i < kSlots; i += blockDim.x) {
+    for (int i = threadIdx.x; i < S; i += blockDim.x) {
       keys[i] = kEmpty;
       counts[i] = 0u;
     }
@@ -120,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void k_penalize(
       if (id < 0 || id >= V) continue;
       const uint32_t u = static_cast<uint32_t>(id);
       if (id_class(u, lq) != q) continue;
-      uint32_t slot = slot_hash(u);
+      uint32_t slot = slot_hash(u, lgs);
       int probes = 0;
       while (true) {
         const uint32_t prev = atomicCAS(&keys[slot], kEmpty, u);
@@ -128,8 +136,8 @@ __global__ __launch_bounds__(kThreads) void k_penalize(
           if (i >= nign) atomicAdd(&counts[slot], 1u);
           break;
         }
-        slot = (slot + 1) & (kSlots - 1);
-        if (++probes >= kSlots) {
+        slot = (slot + 1) & static_cast<uint32_t>(S - 1);
+        if (++probes >= S) {
           s_overflow = 1;
           break;
         }
@@ -148,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void k_penalize(
       }
       continue;
     }
-    for (int i = threadIdx.x; i < kSlots; i += blockDim.x) {
+    for (int i = threadIdx.x; i < S; i += blockDim.x) {
       const uint32_t id = keys[i];
       if (id == kEmpty) continue;
       const uint32_t n = counts[i];
