@@ -580,12 +580,12 @@ __global__ __launch_bounds__(kLightThreads) void k_row_light(Job j) {
           if (threadIdx.x == 0) j.desc[row].m = m;
           if (c.p < 1.0f) {  // the histogram and gather passes accumulate from zero
             uint64_t* hw = j.fhw + static_cast<size_t>(row) * kFullBuckets;
-            uint32_t* hc = j.fhc + static_cast<size_t>(row) * kFullBuckets;
-            for (int i = threadIdx.x; i < kFullBuckets; i += blockDim.x) {
-              hw[i] = 0ull;
-              hc[i] = 0u;
+            for (int i = threadIdx.x; i < kFullBuckets; i += blockDim.x) hw[i] = 0ull;
+            if (threadIdx.x == 0) {
+              j.fcnt[row] = 0u;
+              j.fcut[row].count = 0u;
+              j.fcut[row].above_c = 0ull;
             }
-            if (threadIdx.x == 0) j.fcnt[row] = 0u;
           }
         }
       }

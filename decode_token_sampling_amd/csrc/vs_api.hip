@@ -52,8 +52,6 @@ WsLayout ws_layout(int B, int V) {
   off = align_up(off + static_cast<size_t>(B) * sizeof(float2));
   L.fhw = off;
   off = align_up(off + static_cast<size_t>(B) * kFullBuckets * sizeof(uint64_t));
-  L.fhc = off;
-  off = align_up(off + static_cast<size_t>(B) * kFullBuckets * sizeof(uint32_t));
   L.flist = off;
   off = align_up(off + static_cast<size_t>(B) * kFullListCap * sizeof(uint64_t));
   L.fcnt = off;
@@ -102,7 +100,6 @@ Job make_job(const void* logits, vs_dtype dt, int B, int V, int64_t ld, void* ws
   j.lpart = reinterpret_cast<LsePart*>(w + L.lpart);
   j.rlse = reinterpret_cast<float2*>(w + L.rlse);
   j.fhw = reinterpret_cast<uint64_t*>(w + L.fhw);
-  j.fhc = reinterpret_cast<uint32_t*>(w + L.fhc);
   j.flist = reinterpret_cast<uint64_t*>(w + L.flist);
   j.fcnt = reinterpret_cast<uint32_t*>(w + L.fcnt);
   j.fcut = reinterpret_cast<FullCut*>(w + L.fcut);
@@ -113,12 +110,14 @@ Job make_job(const void* logits, vs_dtype dt, int B, int V, int64_t ld, void* ws
     const int64_t t = static_cast<int64_t>(B) * L.ntile3 / 512;
     j.gseg = t < 1 ? 1 : (t > 8 ? 8 : static_cast<int>(t));
   }
-  // Histogram and gather passes of full-vocabulary rows: enough segments per
-  // row that the batch gives every compute unit about four workgroups, each at
-  // least kFullSegMin ids (a multiple of 8, so segments start 16-byte aligned).
+  // Histogram and gather passes of full-vocabulary rows (1024-thread
+  // workgroups): enough segments per row that the batch gives every compute
+  // unit about one workgroup, each at least kFullSegMin ids (a multiple of 8,
+  // so segments start 16-byte aligned). Fewer, longer segments mean fewer
+  // flushes of per-segment histograms into the row's.
   {
     const int smax = (V + kFullSegMin - 1) / kFullSegMin;
-    int fs = (4 * cus + B - 1) / B;
+    int fs = (cus + B - 1) / B;
     fs = fs < 1 ? 1 : (fs > smax ? smax : fs);
     const int len = ((V + fs - 1) / fs + 7) & ~7;
     j.fseg_len = len;

@@ -44,6 +44,9 @@ enum : uint32_t {
 };
 
 // The top-p cut of a full-vocabulary row, found from its mass histogram.
+// bucket and rem come from the first segment's gather workgroup; count and
+// above_c are sums over all of the row's gather workgroups (zeroed by the row
+// kernel with the histogram).
 struct FullCut {
   int32_t bucket;     // the bucket holding the cut (-1: not found)
   uint32_t count;     // ids in that bucket
@@ -106,7 +109,6 @@ struct Job {
   const float* lpT;        // [B] temperature of the log-probs (vs_logprobs_ex), or NULL
   // full-vocabulary top-p (per row): mass histogram, the cut bucket's ids
   uint64_t* fhw;       // [B][kFullBuckets] masses
-  uint32_t* fhc;       // [B][kFullBuckets] counts
   uint64_t* flist;     // [B][kFullListCap] packed (key, id) of the cut bucket
   uint32_t* fcnt;      // [B] entries appended to flist (may exceed the capacity)
   FullCut* fcut;       // [B] the cut bucket and the mass needed inside it
@@ -174,7 +176,7 @@ __device__ __forceinline__ float lse_scaled(float x, float T) { return T == 1.0f
 
 struct WsLayout {
   int ntile, ntile3;
-  size_t meta, candA, candB, kthA, kthB, desc, gpart, lpart, rlse, fhw, fhc, flist, fcnt, fcut, total;
+  size_t meta, candA, candB, kthA, kthB, desc, gpart, lpart, rlse, fhw, flist, fcnt, fcut, total;
 };
 WsLayout ws_layout(int B, int V);
 
