@@ -17,6 +17,8 @@
 //    ids above are counted from their bucket alone, with no exponential.
 // The cut kernel then sorts the list and finds the exact cut; a bucket larger
 // than the list goes to its one-workgroup path.
+#include <type_traits>
+
 #include "vs_device.h"
 #include "vs_kernels.h"
 
@@ -26,8 +28,6 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kPer = kFullBuckets / kThreads;  // buckets per thread (4)
 constexpr int kGatherBuf = 2048;  // ids a gather workgroup collects in LDS before one global append
-
-__device__ __forceinline__ float scaled_of(float x, float T) { return (T == 1.0f) ? x : x / T; }
 
 // A full-vocabulary row whose top-p cut is still to be found.
 __device__ __forceinline__ bool topp_row(const Job& j, int row, RowCfg* c, float* m) {
@@ -41,16 +41,16 @@ __device__ __forceinline__ bool topp_row(const Job& j, int row, RowCfg* c, float
 // Reads the ids [lo, hi) of a row with the whole block: 16-byte loads when
 // the row is aligned (lo is a multiple of 8, so the segment starts on a
 // 16-byte boundary), elements otherwise and at the end. start() issues the
-// loads of the first kFirst vectors of each thread, so that they are in
-// flight while the workgroup does its set-up; visit() then calls f(id, x)
-// for every id, all lanes of a wave together in the vector loops.
-template <typename E, int kFirst>  // kFirst: vectors per thread loaded by start()
+// loads of each thread's first U vectors, so that they are in flight while
+// the workgroup does its set-up; visit() then calls f(id, x) for every id,
+// all lanes of a wave together in the vector loop, with the next U vectors'
+// loads issued before the current ones are used.
+template <typename E, int U>
 struct SegReader {
   static constexpr int EPV = Epv<E>::n;
-  static constexpr int U = 4;       // vectors per thread in flight after that
   const E* rowp;
   int lo, hi, nvec;
-  uint4 raw[kFirst];
+  uint4 raw[U];
 
   __device__ __forceinline__ void start(const E* __restrict__ r, int l, int h, bool aligned) {
     rowp = r;
@@ -59,7 +59,7 @@ struct SegReader {
     nvec = aligned ? (h - l) / EPV : 0;
     const E* base = rowp + lo;
 #pragma unroll
-    for (int u = 0; u < kFirst; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int i = static_cast<int>(threadIdx.x) + u * kThreads;
       if (i < nvec) raw[u] = load16(base + i * EPV);
     }
@@ -68,40 +68,35 @@ struct SegReader {
   template <typename F>
   __device__ __forceinline__ void visit(F&& f) {
     const E* base = rowp + lo;
-    const int st = kThreads;
-#pragma unroll
-    for (int u = 0; u < kFirst; ++u) {
-      const int i = static_cast<int>(threadIdx.x) + u * st;
-      if (i < nvec) {
-        float x[EPV];
-        unpack16(raw[u], x, rowp);
-#pragma unroll
-        for (int c = 0; c < EPV; ++c) f(lo + i * EPV + c, x[c]);
-      }
-    }
-    int i = static_cast<int>(threadIdx.x) + kFirst * st;
-    for (; i + (U - 1) * st < nvec; i += U * st) {
-      uint4 r[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) r[u] = load16(base + (i + u * st) * EPV);
+    for (int i0 = static_cast<int>(threadIdx.x); i0 < nvec; i0 += U * kThreads) {
+      uint4 nxt[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        float x[EPV];
-        unpack16(r[u], x, rowp);
-#pragma unroll
-        for (int c = 0; c < EPV; ++c) f(lo + (i + u * st) * EPV + c, x[c]);
+        const int i = i0 + (U + u) * kThreads;
+        if (i < nvec) nxt[u] = load16(base + i * EPV);
       }
-    }
-    for (; i < nvec; i += st) {
-      float x[EPV];
-      unpack16(load16(base + i * EPV), x, rowp);
 #pragma unroll
-      for (int c = 0; c < EPV; ++c) f(lo + i * EPV + c, x[c]);
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * kThreads;
+        if (i < nvec) {
+          float x[EPV];
+          unpack16(raw[u], x, rowp);
+#pragma unroll
+          for (int c = 0; c < EPV; ++c) f(lo + i * EPV + c, x[c]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) raw[u] = nxt[u];
     }
     for (int q = lo + nvec * EPV + static_cast<int>(threadIdx.x); q < hi; q += kThreads)
       f(q, to_f32(rowp[q]));
   }
 };
+
+// s = x / T, with the division left out (x / 1 is x) for rows at T = 1: the
+// callers branch once per workgroup on kDiv.
+template <bool kDiv>
+__device__ __forceinline__ float scaled_by(float x, float T) { return kDiv ? x / T : x; }
 
 template <typename E>
 __global__ __launch_bounds__(kThreads) void k_full_hist(Job j) {
@@ -119,12 +114,18 @@ __global__ __launch_bounds__(kThreads) void k_full_hist(Job j) {
   for (int i = threadIdx.x; i < kFullBuckets; i += kThreads) hw[i] = 0ull;
   __syncthreads();
   const FullTerms ft{m, c.mp};
-  rd.visit([&](int, float x) {
-    uint64_t w;
-    int b;
-    if (ft.mass(scaled_of(x, c.T), &w, &b))
-      atomicAdd(reinterpret_cast<unsigned long long*>(&hw[b]), static_cast<unsigned long long>(w));
-  });
+  auto pass = [&](auto div) {
+    rd.visit([&](int, float x) {
+      uint64_t w;
+      int b;
+      if (ft.mass(scaled_by<decltype(div)::value>(x, c.T), &w, &b))
+        atomicAdd(reinterpret_cast<unsigned long long*>(&hw[b]), static_cast<unsigned long long>(w));
+    });
+  };
+  if (c.T == 1.0f)  // uniform
+    pass(std::false_type{});
+  else
+    pass(std::true_type{});
   __syncthreads();
   uint64_t* ghw = j.fhw + static_cast<size_t>(row) * kFullBuckets;
   for (int b = threadIdx.x; b < kFullBuckets; b += kThreads) {
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
   const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
   const int lo = seg * j.fseg_len;
   const int hi = min(j.V, lo + j.fseg_len);
-  SegReader<E, 2> rd;
+  SegReader<E, 4> rd;
   rd.start(rowp, lo, hi, j.aligned != 0);
   const uint64_t* ghw = j.fhw + static_cast<size_t>(row) * kFullBuckets;
 
@@ -203,39 +204,45 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
   uint64_t* lst = j.flist + static_cast<size_t>(row) * kFullListCap;
   uint32_t* cnt = j.fcnt + row;
   uint32_t n_above = 0, n_hit = 0;
-  rd.visit([&](int id, float x) {
-    const float s = scaled_of(x, c.T);
-    const float t = s - m;
-    const int b = (t == t) ? FullTerms::bucket_of(t) : kFullBuckets;  // the bucket alone, no exponential
-    n_above += b < bstar ? 1u : 0u;
-    bool hit = b == bstar;
-    if (hit) {
-      uint64_t wt;
-      int bb;
-      hit = ft.mass(s, &wt, &bb);  // the histogram's membership (e >= min_p, mass > 0)
-    }
-    n_hit += hit ? 1u : 0u;
-    const uint64_t bal = __ballot(hit);
-    if (bal) {
-      const int first = __ffsll(static_cast<unsigned long long>(bal)) - 1;
-      const uint32_t nb = static_cast<uint32_t>(__popcll(bal));
-      uint32_t at = 0;
-      if (lane() == first) at = atomicAdd(&s_n, nb);
-      at = __builtin_amdgcn_readlane(at, first);
-      if (at + nb <= static_cast<uint32_t>(kGatherBuf)) {  // uniform
-        if (hit) sbuf[at + lanes_below(bal)] = pack(f2key(s), id);
-      } else {
-        uint32_t base = 0;
-        if (lane() == first) {
-          atomicMin(&s_lim, at);
-          base = atomicAdd(cnt, nb);
-        }
-        base = __builtin_amdgcn_readlane(base, first);
-        const uint32_t pos = base + static_cast<uint32_t>(lanes_below(bal));
-        if (hit && pos < static_cast<uint32_t>(kFullListCap)) lst[pos] = pack(f2key(s), id);
+  auto pass = [&](auto div) {
+    rd.visit([&](int id, float x) {
+      const float s = scaled_by<decltype(div)::value>(x, c.T);
+      const float t = s - m;
+      const int b = (t == t) ? FullTerms::bucket_of(t) : kFullBuckets;  // the bucket alone, no exponential
+      n_above += b < bstar ? 1u : 0u;
+      bool hit = b == bstar;
+      if (hit) {
+        uint64_t wt;
+        int bb;
+        hit = ft.mass(s, &wt, &bb);  // the histogram's membership (e >= min_p, mass > 0)
       }
-    }
-  });
+      n_hit += hit ? 1u : 0u;
+      const uint64_t bal = __ballot(hit);
+      if (bal) {
+        const int first = __ffsll(static_cast<unsigned long long>(bal)) - 1;
+        const uint32_t nb = static_cast<uint32_t>(__popcll(bal));
+        uint32_t at = 0;
+        if (lane() == first) at = atomicAdd(&s_n, nb);
+        at = __builtin_amdgcn_readlane(at, first);
+        if (at + nb <= static_cast<uint32_t>(kGatherBuf)) {  // uniform
+          if (hit) sbuf[at + lanes_below(bal)] = pack(f2key(s), id);
+        } else {
+          uint32_t base = 0;
+          if (lane() == first) {
+            atomicMin(&s_lim, at);
+            base = atomicAdd(cnt, nb);
+          }
+          base = __builtin_amdgcn_readlane(base, first);
+          const uint32_t pos = base + static_cast<uint32_t>(lanes_below(bal));
+          if (hit && pos < static_cast<uint32_t>(kFullListCap)) lst[pos] = pack(f2key(s), id);
+        }
+      }
+    });
+  };
+  if (c.T == 1.0f)  // uniform
+    pass(std::false_type{});
+  else
+    pass(std::true_type{});
   // this workgroup's counts into the row's record (block_sum's barriers also
   // complete the LDS appends)
   n_above = block_sum(n_above, sc);

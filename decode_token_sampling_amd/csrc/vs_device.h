@@ -102,31 +102,49 @@ __device__ __forceinline__ uint4 load16_stream(const void* p) {
 // exact scaling by 2^n. Its double result is within a few 1e-17 of e^t, so the
 // final fp32 rounding is the correctly rounded value; the oracle states this
 // function as libm's exp rounded to fp32 and the tests compare the two.
+//
+// c + a * b in double with the constant c read from scalar registers: one
+// VALU instruction per step. (Left to itself the compiler copies each 64-bit
+// constant into a vector register first, since the VOP3 form cannot take a
+// 64-bit literal; that doubles the instruction count of the polynomial.)
+// Only the named constant operand goes to scalar registers: every other
+// operand is a per-lane value.
+__device__ __forceinline__ double fma_k(double a, double b, double c) {
+  double d;
+  asm("v_fma_f64 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "s"(c));
+  return d;
+}
+// c - n * k with the constant k from scalar registers.
+__device__ __forceinline__ double fnma_k(double n, double k, double c) {
+  double d;
+  asm("v_fma_f64 %0, -%1, %2, %3" : "=v"(d) : "v"(n), "s"(k), "v"(c));
+  return d;
+}
 __device__ __forceinline__ float pinned_exp(float tf) {
   if (!(tf >= -87.0f)) return 0.0f;
   const double t = static_cast<double>(tf);
   const double n = rint(t * 1.4426950408889634);   // 1/ln2
   const double hi = 0x1.62e42fefa3800p-1;           // ln2, low 11 bits cleared
   const double lo = 0x1.ef35793c76730p-45;          // ln2 - hi
-  double r = __builtin_fma(-n, hi, t);
-  r = __builtin_fma(-n, lo, r);
+  double r = fnma_k(n, hi, t);
+  r = fnma_k(n, lo, r);
   double p = 1.0 / 6227020800.0;                    // 1/13!
-  p = __builtin_fma(p, r, 1.0 / 479001600.0);
-  p = __builtin_fma(p, r, 1.0 / 39916800.0);
-  p = __builtin_fma(p, r, 1.0 / 3628800.0);
-  p = __builtin_fma(p, r, 1.0 / 362880.0);
-  p = __builtin_fma(p, r, 1.0 / 40320.0);
-  p = __builtin_fma(p, r, 1.0 / 5040.0);
-  p = __builtin_fma(p, r, 1.0 / 720.0);
-  p = __builtin_fma(p, r, 1.0 / 120.0);
-  p = __builtin_fma(p, r, 1.0 / 24.0);
-  p = __builtin_fma(p, r, 1.0 / 6.0);
-  p = __builtin_fma(p, r, 0.5);
-  p = __builtin_fma(p, r, 1.0);
-  p = __builtin_fma(p, r, 1.0);
-  const int64_t ni = static_cast<int64_t>(n);
-  const double scale = __longlong_as_double((ni + 1023) << 52);
-  return static_cast<float>(p * scale);
+  p = fma_k(p, r, 1.0 / 479001600.0);
+  p = fma_k(p, r, 1.0 / 39916800.0);
+  p = fma_k(p, r, 1.0 / 3628800.0);
+  p = fma_k(p, r, 1.0 / 362880.0);
+  p = fma_k(p, r, 1.0 / 40320.0);
+  p = fma_k(p, r, 1.0 / 5040.0);
+  p = fma_k(p, r, 1.0 / 720.0);
+  p = fma_k(p, r, 1.0 / 120.0);
+  p = fma_k(p, r, 1.0 / 24.0);
+  p = fma_k(p, r, 1.0 / 6.0);
+  p = fma_k(p, r, 0.5);
+  p = fma_k(p, r, 1.0);
+  p = fma_k(p, r, 1.0);
+  // n is an integer in [-126, 128] for every t that gets here and is not
+  // above the fp32 overflow threshold; p * 2^n is exact in double
+  return static_cast<float>(ldexp(p, static_cast<int>(n)));
 }
 
 // Fixed-point top-p mass of a relative weight e in [0,1]: floor(e * 2^31).
