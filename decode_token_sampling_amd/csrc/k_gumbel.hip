@@ -10,15 +10,21 @@
 // the logarithm and the division for an id that provably scores below its
 // best so far: -log u > 1 - u for u < 1, so 1 - u >= e / best (with margins
 // for the rounding of both sides) means e / -log u < best; e <= 1 gives a
-// first test before e itself is computed, a hardware-exponential upper bound
-// on e a second one. Any kept id's score bounds the row's maximum from below,
-// so after each tile the waves of a workgroup share their bests through LDS
-// (plain stores and loads: a stale value is only a looser bound). Skipped ids
-// cannot be the argmax, so the result is the exact one.
+// first test before e itself is computed (an integer compare of the id's
+// random word with a threshold derived from the bound, no floating point),
+// a hardware-exponential upper bound on e a second one. Any kept id's score
+// bounds the row's maximum from below, so each workgroup first scores one id
+// per thread and shares the best (one barrier), and after each tile its waves
+// share their bests again through LDS (plain stores and loads: a stale value
+// is only a looser bound). Skipped ids cannot be the argmax, so the result is
+// the exact one. The next tile's loads are issued before the current tile is
+// scored, and rows at T = 1 take a copy of the loop without the division.
 // K4 (one workgroup per row) reduces the tiles: the sampled id, the kept count
 // and, in the fused call, the sampled id's log-probability. The argmax compares
 // true ids, never thread or tile order, so the result does not depend on the
 // partition (vllm.cpp pull request #1997, "The kernel (#1984)").
+#include <type_traits>
+
 #include "vs_device.h"
 #include "vs_kernels.h"
 
@@ -31,6 +37,18 @@ constexpr float kLog2E = 1.44269504088896340736f;
 
 __device__ __forceinline__ bool full_row(uint32_t mode) {
   return mode == kRowFullNone || mode == kRowFullMinP || mode == kRowFullTopP;
+}
+
+// The random words b below which an id cannot beat the score bound lim:
+// with u = ((b >> 12) + 1/2) 2^-52, every b < skip_below(lim) has
+// 1 - u >= lim (1 + 2^-45) + 2^-52, so (1 - u)(1 - 2^-50) rounded stays
+// >= lim and the id scores below the best (0: no b, while lim >= 1).
+__device__ __forceinline__ uint64_t skip_below(double lim) {
+  if (!(lim < 1.0)) return 0ull;
+  // (1 - lim (1 + 2^-45)) 2^52 - 2, whose rounding errors stay below 1.5
+  const double v = (1.0 - lim * (1.0 + 0x1p-45)) * 0x1p52 - 2.0;
+  if (!(v > 0.0)) return 0ull;
+  return static_cast<uint64_t>(v) << 12;  // floor(v) < 2^52
 }
 
 template <typename E>
@@ -54,85 +72,177 @@ __global__ __launch_bounds__(kThreads) void k_gumbel_partial(Job j) {
   const int t0 = run * j.gseg;
   const int t1 = min(j.ntile3, t0 + j.gseg);
   const int wv = static_cast<int>(threadIdx.x) / kWave;
-  if (lane() == 0) swb[wv] = 0ull;
-  __syncthreads();
 
   double best = -1.0;
   int best_id = 0x7fffffff;
   // (1 + 2^-40) / (the largest kept id's score known here): an id whose 1 - u
   // reaches lim * e scores below it (infinite, so that no id is skipped,
-  // until a score is known)
+  // until a score is known); skip: the random words that reach it for any e
   double lim = __builtin_inf();
+  uint64_t skip = 0ull;
   int kept = 0;
-  for (int tile = t0; tile < t1; ++tile) {
-    const int base = tile * kGumTile;
-    const bool vec = j.aligned && (base + kGumTile <= j.V);
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int j0 = base + (i * kThreads + static_cast<int>(threadIdx.x)) * EPV;
-      float x[EPV];
-      if (vec) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(rowp + j0);
-        unpack16(raw, x, rowp);
-      } else {
-#pragma unroll
-        for (int c = 0; c < EPV; ++c) x[c] = (j0 + c < j.V) ? to_f32(rowp[j0 + c]) : -kInf;
-      }
-      uint32_t bits = 0;
+
+  // the 16-byte vectors of a tile this thread reads, when the tile is whole
+  // and the row aligned
+  const auto vec_of = [&](int tile) { return j.aligned && (tile + 1) * kGumTile <= j.V; };
+  const auto first_id = [&](int tile, int i) {
+    return tile * kGumTile + (i * kThreads + static_cast<int>(threadIdx.x)) * EPV;
+  };
+
+  // The draw's score of a kept id whose random word b passed the integer
+  // test, unless a finer bound test shows it cannot beat the best; e < 0:
+  // E(s - m) not computed yet.
+  const auto score = [&](int id, float s, float e, uint64_t b) {
+    const double u = uniform_of_bits(b);
+    const double one_u = (1.0 - u) * (1.0 - 0x1p-50);  // rounded down past any rounding error
+    if (one_u >= lim) return;                          // e <= 1: below the bound
+    if (e < 0.0f) {
+      // an upper bound on e from the hardware exponential first: for
+      // s - m >= -87 the fp32 constant and product move the exponent by
+      // at most 9e-6 (2^x by 6.3e-6 relative), the instruction adds
+      // about 1 ulp, and 2^-16 covers both; below -87 e is 0
+      const float eub = __builtin_amdgcn_exp2f((s - d.m) * kLog2E) * (1.0f + 0x1p-16f);
+      if (one_u >= lim * static_cast<double>(eub)) return;  // below the bound
+      e = pinned_exp(s - d.m);
+    }
+    if (one_u >= lim * static_cast<double>(e)) return;  // below the bound
+    const double sc = static_cast<double>(e) / -log(u);  // as gumbel_score
+    if (sc > best || (sc == best && id < best_id)) {
+      best = sc;
+      best_id = id;
+      lim = fmin(lim, (1.0 + 0x1p-40) / best);
+      skip = skip_below(lim);
+    }
+  };
+
+  // Membership of the ids v[c] = s of ids j0 + c (c < n, n <= EPV) as a bit
+  // mask; e[c] gets E(s - m) where membership needed it, else -1.
+  const auto members = [&](int j0, int n, const float* v, float* e) {
+    uint32_t km = 0;
+    if (d.mode == kRowFullMinP) {  // uniform
 #pragma unroll
       for (int c = 0; c < EPV; ++c) {
-        const int id = j0 + c;
-        if (id >= j.V) continue;
-        const float s = (T == 1.0f) ? x[c] : x[c] / T;
-        float e = -1.0f;  // E(s - m), once computed
-        bool keep;
-        if (d.mode == kRowFullNone) {
-          keep = true;
-        } else if (d.mode == kRowFullMinP) {
-          e = pinned_exp(s - d.m);
-          keep = e >= mp;
-        } else {
-          const uint32_t key = f2key(s);
-          keep = key > d.tau || (key == d.tau && id <= d.id_cut);
-        }
-        if (keep) {
-          ++kept;
-          bits |= 1u << (id & 31);
-          const double u = uniform_of(rs, id);
-          const double one_u = (1.0 - u) * (1.0 - 0x1p-50);  // rounded down past any rounding error
-          if (one_u >= lim) continue;                        // e <= 1: below the bound
-          if (e < 0.0f) {
-            // an upper bound on e from the hardware exponential first: for
-            // s - m >= -87 the fp32 constant and product move the exponent by
-            // at most 9e-6 (2^x by 6.3e-6 relative), the instruction adds
-            // about 1 ulp, and 2^-16 covers both; below -87 e is 0
-            const float eub = __builtin_amdgcn_exp2f((s - d.m) * kLog2E) * (1.0f + 0x1p-16f);
-            if (one_u >= lim * static_cast<double>(eub)) continue;  // below the bound
-            e = pinned_exp(s - d.m);
-          }
-          if (one_u >= lim * static_cast<double>(e)) continue;  // below the bound
-          const double sc = static_cast<double>(e) / -log(u);   // as gumbel_score
-          if (sc > best || (sc == best && id < best_id)) {
-            best = sc;
-            best_id = id;
-            lim = fmin(lim, (1.0 + 0x1p-40) / best);
-          }
-        }
+        e[c] = pinned_exp(v[c] - d.m);
+        km |= (c < n && e[c] >= mp) ? 1u << c : 0u;
       }
-      if (mask_row && bits) atomicOr(&mask_row[j0 >> 5], bits);
+    } else if (d.mode == kRowFullNone) {  // uniform
+#pragma unroll
+      for (int c = 0; c < EPV; ++c) {
+        e[c] = -1.0f;
+        km |= c < n ? 1u << c : 0u;
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < EPV; ++c) {
+        e[c] = -1.0f;
+        const uint32_t key = f2key(v[c]);
+        km |= (c < n && (key > d.tau || (key == d.tau && j0 + c <= d.id_cut))) ? 1u << c : 0u;
+      }
     }
-    // this wave's best into its slot, then the workgroup's (scores are
-    // nonnegative: their bits order as integers)
+    return km;
+  };
+
+  // the workgroup's best so far into every thread's bound (scores are
+  // nonnegative: their bits order as integers)
+  const auto share = [&](bool barrier) {
     uint64_t wb = wave_max_u64_dpp(best >= 0.0 ? static_cast<uint64_t>(__double_as_longlong(best)) : 0ull);
+    if (barrier) __syncthreads();
     if (lane() == 0) __hip_atomic_store(&swb[wv], wb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (barrier) __syncthreads();
 #pragma unroll
     for (int w = 0; w < kThreads / kWave; ++w) {
       const uint64_t o = __hip_atomic_load(&swb[w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       wb = o > wb ? o : wb;
     }
     const double sbest = __longlong_as_double(static_cast<long long>(wb));
-    if (sbest > 0.0) lim = fmin(lim, (1.0 + 0x1p-40) / sbest);
-  }
+    if (sbest > 0.0 && (1.0 + 0x1p-40) / sbest < lim) {
+      lim = (1.0 + 0x1p-40) / sbest;
+      skip = skip_below(lim);
+    }
+  };
+
+  const auto run_tiles = [&](auto div) {
+    constexpr bool kDiv = decltype(div)::value;
+    const auto scaled = [&](float x) { return kDiv ? x / T : x; };
+    uint4 cur[NV];
+    if (vec_of(t0)) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) cur[i] = *reinterpret_cast<const uint4*>(rowp + first_id(t0, i));
+    }
+    // First one id per thread, the first of its first vector: the workgroup
+    // then starts from the best of up to 256 scores rather than each thread
+    // from its own. (The id is scored again, and counted, with its tile.)
+    {
+      const int id = first_id(t0, 0);
+      float v[EPV], e[EPV];
+#pragma unroll
+      for (int c = 0; c < EPV; ++c) v[c] = -kInf;
+      if (id < j.V) {
+        if (vec_of(t0)) {
+          float x[EPV];
+          unpack16(cur[0], x, rowp);
+          v[0] = scaled(x[0]);
+        } else {
+          v[0] = scaled(to_f32(rowp[id]));
+        }
+      }
+      const uint32_t km = members(id, id < j.V ? 1 : 0, v, e);
+      if (km & 1u) {
+        const uint64_t b = random_bits(rs, id);
+        if (b >= skip) score(id, v[0], e[0], b);
+      }
+      share(true);
+    }
+    for (int tile = t0; tile < t1; ++tile) {
+      const bool vec = vec_of(tile);
+      uint4 nxt[NV];
+      if (tile + 1 < t1 && vec_of(tile + 1)) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) nxt[i] = *reinterpret_cast<const uint4*>(rowp + first_id(tile + 1, i));
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int j0 = first_id(tile, i);
+        const int n = min(EPV, max(0, j.V - j0));
+        float v[EPV], e[EPV];
+        if (vec) {
+          unpack16(cur[i], v, rowp);
+        } else {
+#pragma unroll
+          for (int c = 0; c < EPV; ++c) v[c] = (c < n) ? to_f32(rowp[j0 + c]) : -kInf;
+        }
+#pragma unroll
+        for (int c = 0; c < EPV; ++c) v[c] = scaled(v[c]);
+        const uint32_t km = members(j0, n, v, e);
+        kept += __popc(km);
+        // EPV divides 32: the vector's ids share one mask word
+        if (mask_row && km) atomicOr(&mask_row[j0 >> 5], km << (j0 & 31));
+        if (__ballot(km != 0u)) {  // uniform: some lane keeps an id here
+          // every kept id's random word, then the integer bound test
+          uint64_t bw[EPV];
+          uint32_t need = 0;
+#pragma unroll
+          for (int c = 0; c < EPV; ++c) {
+            bw[c] = random_bits(rs, j0 + c);
+            need |= ((km >> c) & 1u) && bw[c] >= skip ? 1u << c : 0u;
+          }
+          if (__ballot(need != 0u)) {  // rare once a bound is known
+#pragma unroll
+            for (int c = 0; c < EPV; ++c)
+              if ((need >> c) & 1u) score(j0 + c, v[c], e[c], bw[c]);
+          }
+        }
+      }
+      share(false);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) cur[i] = nxt[i];
+    }
+  };
+  if (T == 1.0f)  // uniform; x / 1 is x
+    run_tiles(std::false_type{});
+  else
+    run_tiles(std::true_type{});
+
   const double bb = block_max(best, sd);
   const int bid = block_min(best == bb ? best_id : 0x7fffffff, si);
   const int bk = block_sum(kept, si);

@@ -163,10 +163,16 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
 __device__ __forceinline__ uint64_t row_stream(uint64_t seed, int row) {
   return splitmix64(seed ^ (static_cast<uint64_t>(static_cast<uint32_t>(row)) << 32));
 }
-// Uniform strictly inside (0,1): 52 random bits plus one half, times 2^-52.
-__device__ __forceinline__ double uniform_of(uint64_t row_state, int id) {
-  const uint64_t b = splitmix64(row_state + static_cast<uint64_t>(static_cast<uint32_t>(id)));
+// The random word of an id, and the uniform strictly inside (0,1) made from
+// it: its top 52 bits plus one half, times 2^-52.
+__device__ __forceinline__ uint64_t random_bits(uint64_t row_state, int id) {
+  return splitmix64(row_state + static_cast<uint64_t>(static_cast<uint32_t>(id)));
+}
+__device__ __forceinline__ double uniform_of_bits(uint64_t b) {
   return (static_cast<double>(b >> 12) + 0.5) * 0x1p-52;
+}
+__device__ __forceinline__ double uniform_of(uint64_t row_state, int id) {
+  return uniform_of_bits(random_bits(row_state, id));
 }
 // Gumbel-max score prob / q with q = -log(u) (exponential noise), in double.
 __device__ __forceinline__ double gumbel_score(float e, uint64_t row_state, int id) {
