@@ -42,9 +42,10 @@ __device__ __forceinline__ bool topp_row(const Job& j, int row, RowCfg* c, float
 // the row is aligned (lo is a multiple of 8, so the segment starts on a
 // 16-byte boundary), elements otherwise and at the end. start() issues the
 // loads of each thread's first U vectors, so that they are in flight while
-// the workgroup does its set-up; visit() then calls f(id, x) for every id,
-// all lanes of a wave together in the vector loop, with the next U vectors'
-// loads issued before the current ones are used.
+// the workgroup does its set-up; visit() then calls f(id0, x, n) for every
+// vector (x[c] the value of id id0 + c, c < n; the rest -inf), all lanes of
+// a wave together in the vector loop, with the next U vectors' loads issued
+// before the current ones are used.
 template <typename E, int U>
 struct SegReader {
   static constexpr int EPV = Epv<E>::n;
@@ -81,15 +82,19 @@ struct SegReader {
         if (i < nvec) {
           float x[EPV];
           unpack16(raw[u], x, rowp);
-#pragma unroll
-          for (int c = 0; c < EPV; ++c) f(lo + i * EPV + c, x[c]);
+          f(lo + i * EPV, x, EPV);
         }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) raw[u] = nxt[u];
     }
-    for (int q = lo + nvec * EPV + static_cast<int>(threadIdx.x); q < hi; q += kThreads)
-      f(q, to_f32(rowp[q]));
+    for (int q = lo + nvec * EPV + static_cast<int>(threadIdx.x); q < hi; q += kThreads) {
+      float x[EPV];
+#pragma unroll
+      for (int c = 0; c < EPV; ++c) x[c] = -kInf;
+      x[0] = to_f32(rowp[q]);
+      f(q, x, 1);
+    }
   }
 };
 
@@ -114,12 +119,17 @@ __global__ __launch_bounds__(kThreads) void k_full_hist(Job j) {
   for (int i = threadIdx.x; i < kFullBuckets; i += kThreads) hw[i] = 0ull;
   __syncthreads();
   const FullTerms ft{m, c.mp};
+  // one LDS atomic per member id (non-members, e.g. below min-p, skip it:
+  // adding 0 at one shared address would serialize the wave's lanes)
   auto pass = [&](auto div) {
-    rd.visit([&](int, float x) {
-      uint64_t w;
-      int b;
-      if (ft.mass(scaled_by<decltype(div)::value>(x, c.T), &w, &b))
-        atomicAdd(reinterpret_cast<unsigned long long*>(&hw[b]), static_cast<unsigned long long>(w));
+    rd.visit([&](int, const float* x, int n) {
+#pragma unroll
+      for (int q = 0; q < SegReader<E, 4>::EPV; ++q) {
+        uint64_t w;
+        int b;
+        if (ft.mass(scaled_by<decltype(div)::value>(x[q], c.T), &w, &b) && q < n)
+          atomicAdd(reinterpret_cast<unsigned long long*>(&hw[b]), static_cast<unsigned long long>(w));
+      }
     });
   };
   if (c.T == 1.0f)  // uniform
@@ -204,37 +214,49 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
   uint64_t* lst = j.flist + static_cast<size_t>(row) * kFullListCap;
   uint32_t* cnt = j.fcnt + row;
   uint32_t n_above = 0, n_hit = 0;
+  constexpr int EPV = SegReader<E, 4>::EPV;
   auto pass = [&](auto div) {
-    rd.visit([&](int id, float x) {
-      const float s = scaled_by<decltype(div)::value>(x, c.T);
-      const float t = s - m;
-      const int b = (t == t) ? FullTerms::bucket_of(t) : kFullBuckets;  // the bucket alone, no exponential
-      n_above += b < bstar ? 1u : 0u;
-      bool hit = b == bstar;
-      if (hit) {
-        uint64_t wt;
-        int bb;
-        hit = ft.mass(s, &wt, &bb);  // the histogram's membership (e >= min_p, mass > 0)
+    rd.visit([&](int id0, const float* x, int n) {
+      float sv[EPV];
+      uint32_t hm = 0;  // ids in the cut bucket (the bucket alone, no exponential)
+#pragma unroll
+      for (int q = 0; q < EPV; ++q) {
+        sv[q] = scaled_by<decltype(div)::value>(x[q], c.T);
+        const float t = sv[q] - m;
+        const int b = (t == t && q < n) ? FullTerms::bucket_of(t) : kFullBuckets;
+        n_above += b < bstar ? 1u : 0u;
+        hm |= b == bstar ? 1u << q : 0u;
       }
-      n_hit += hit ? 1u : 0u;
-      const uint64_t bal = __ballot(hit);
-      if (bal) {
-        const int first = __ffsll(static_cast<unsigned long long>(bal)) - 1;
-        const uint32_t nb = static_cast<uint32_t>(__popcll(bal));
-        uint32_t at = 0;
-        if (lane() == first) at = atomicAdd(&s_n, nb);
-        at = __builtin_amdgcn_readlane(at, first);
-        if (at + nb <= static_cast<uint32_t>(kGatherBuf)) {  // uniform
-          if (hit) sbuf[at + lanes_below(bal)] = pack(f2key(s), id);
-        } else {
-          uint32_t base = 0;
-          if (lane() == first) {
-            atomicMin(&s_lim, at);
-            base = atomicAdd(cnt, nb);
+      if (__ballot(hm != 0u)) {  // uniform; few vectors hold cut-bucket ids
+#pragma unroll
+        for (int q = 0; q < EPV; ++q) {
+          bool hit = (hm >> q) & 1u;
+          if (hit) {
+            uint64_t wt;
+            int bb;
+            hit = ft.mass(sv[q], &wt, &bb);  // the histogram's membership (e >= min_p, mass > 0)
           }
-          base = __builtin_amdgcn_readlane(base, first);
-          const uint32_t pos = base + static_cast<uint32_t>(lanes_below(bal));
-          if (hit && pos < static_cast<uint32_t>(kFullListCap)) lst[pos] = pack(f2key(s), id);
+          n_hit += hit ? 1u : 0u;
+          const uint64_t bal = __ballot(hit);
+          if (bal) {
+            const int first = __ffsll(static_cast<unsigned long long>(bal)) - 1;
+            const uint32_t nb = static_cast<uint32_t>(__popcll(bal));
+            uint32_t at = 0;
+            if (lane() == first) at = atomicAdd(&s_n, nb);
+            at = __builtin_amdgcn_readlane(at, first);
+            if (at + nb <= static_cast<uint32_t>(kGatherBuf)) {  // uniform
+              if (hit) sbuf[at + lanes_below(bal)] = pack(f2key(sv[q]), id0 + q);
+            } else {
+              uint32_t base = 0;
+              if (lane() == first) {
+                atomicMin(&s_lim, at);
+                base = atomicAdd(cnt, nb);
+              }
+              base = __builtin_amdgcn_readlane(base, first);
+              const uint32_t pos = base + static_cast<uint32_t>(lanes_below(bal));
+              if (hit && pos < static_cast<uint32_t>(kFullListCap)) lst[pos] = pack(f2key(sv[q]), id0 + q);
+            }
+          }
         }
       }
     });

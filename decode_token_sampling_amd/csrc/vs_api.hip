@@ -104,10 +104,10 @@ Job make_job(const void* logits, vs_dtype dt, int B, int V, int64_t ld, void* ws
   j.fcnt = reinterpret_cast<uint32_t*>(w + L.fcnt);
   j.fcut = reinterpret_cast<FullCut*>(w + L.fcut);
   // Gumbel pass of full-vocabulary rows: up to 8 tiles per workgroup (the
-  // pruning bound tightens along them) while the grid keeps about 512
-  // workgroups.
+  // pruning bound tightens along them) while the grid keeps about 1024
+  // workgroups (four waves per SIMD to hide the loads' latency).
   {
-    const int64_t t = static_cast<int64_t>(B) * L.ntile3 / 512;
+    const int64_t t = static_cast<int64_t>(B) * L.ntile3 / 1024;
     j.gseg = t < 1 ? 1 : (t > 8 ? 8 : static_cast<int>(t));
   }
   // Histogram and gather passes of full-vocabulary rows (1024-thread
