@@ -25,7 +25,7 @@ namespace {
 
 constexpr int kLightThreads = 256;
 constexpr int kFullThreads = 1024;
-constexpr int kWaveCutMax = 1024;  // longest gathered list that one wave selects in
+constexpr int kSortCutMax = kFullThreads;  // longest gathered list cut by the sort (one entry per thread)
 constexpr int kBuckets = kFullBuckets;
 constexpr int kMaxSegs = (VS_MAX_V + kSegMin - 1) / kSegMin;
 
@@ -782,109 +782,55 @@ __device__ void full_topp_cut(const E* __restrict__ rowp, int V, bool aligned, c
 
 // The top-p cut from the ids of the cut bucket, gathered by the parallel
 // passes: the first entry, in the order (key desc, id asc), at which the mass
-// inside the bucket reaches the remainder. No sort: an MSB-first radix select
-// on the packed values (whose descending order is that order) with 8-bit
-// digits, each round adding the masses of the entries still in play per digit
-// and keeping the digit where the running mass crosses the remainder. The
-// leading bits that every entry shares are skipped; a round that leaves one
-// entry ends the search. The workgroup loads the list into sh.buf and each
-// entry's mass into mw (a mass is at most 2^31) with one barrier; then one
-// wave runs the rounds with wave syncs only. lo and hi: the smallest and
-// largest entry. Returns false when the masses fall short of the remainder
-// (not expected: the list holds the whole bucket); the result is the same in
-// every lane.
-__device__ bool wave_cut_from_list(const FullCut& fc, int n, uint64_t lo, uint64_t hi,
-                                   const uint32_t* mw, FullSh& sh, RowDesc* d) {
-  const int l = lane();
-  uint64_t rem = fc.rem;  // mass still needed, counted from the top of the bucket
-  int rank = 0;           // entries above the digit group in play
-  uint64_t cutv = hi;
-  if (lo != hi) {
-    int shift = ((63 - __clzll(lo ^ hi)) / 8) * 8;
-    uint64_t pmask = (shift + 8 >= 64) ? 0ull : (~0ull << (shift + 8));
-    uint64_t prefix = hi & pmask;
-    for (;;) {  // every condition below is uniform over the wave
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sh.hw[l * 4 + e] = 0ull;
-        sh.hc[l * 4 + e] = 0u;
+// inside the bucket reaches the remainder. For a list of at most one entry
+// per thread: a bitonic sort of the packed values (whose descending order is
+// that order), exchanges within a wave through lane shuffles and across
+// waves through LDS, then a prefix sum of the masses in sorted order; the
+// cut is the first entry whose running mass reaches the remainder. Called by
+// every thread with its entry (v = 0, w = 0 past the list: below every
+// packed value, which holds ~id in its low half); returns false when the
+// masses fall short of the remainder (not expected: the list holds the whole
+// bucket). The result is the same in every thread.
+__device__ bool sort_cut_from_list(const FullCut& fc, int n, uint64_t v, uint32_t w, uint32_t* mw,
+                                   FullSh& sh, RowDesc* d) {
+  const int t = static_cast<int>(threadIdx.x);
+  // only the first P entries (P the power of two >= n) need sorting: every
+  // entry past them is padding, and so is every sorted entry past n
+  const int P = n <= 1 ? 1 : 1 << (32 - __clz(n - 1));
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      uint64_t ov;
+      uint32_t ow;
+      if (jj >= kWave) {  // uniform
+        __syncthreads();  // every read of the previous exchange is done
+        sh.buf[t] = v;
+        mw[t] = w;
+        __syncthreads();
+        ov = sh.buf[t ^ jj];
+        ow = mw[t ^ jj];
+      } else {
+        ov = __shfl_xor(v, jj);
+        ow = __shfl_xor(w, jj);
       }
-      wave_lds_sync();
-      for (int i = l; i < n; i += kWave) {
-        const uint64_t v = sh.buf[i];
-        if ((v & pmask) == prefix) {
-          const int dg = static_cast<int>((v >> shift) & 255u);
-          atomicAdd(reinterpret_cast<unsigned long long*>(&sh.hw[dg]),
-                    static_cast<unsigned long long>(mw[i]));
-          atomicAdd(&sh.hc[dg], 1u);
-        }
+      // runs of k entries alternate descending / ascending; the lower
+      // index of each pair keeps the larger entry of a descending run
+      const bool desc = (t & k) == 0;
+      const bool lower = (t & jj) == 0;
+      if (lower == desc ? ov > v : ov < v) {
+        v = ov;
+        w = ow;
       }
-      wave_lds_sync();
-      // lane t holds digits 255 - 4t .. 252 - 4t (largest first)
-      uint64_t w4[4];
-      int c4[4];
-      uint64_t lw = 0;
-      int lc = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        w4[e] = sh.hw[255 - 4 * l - e];
-        c4[e] = static_cast<int>(sh.hc[255 - 4 * l - e]);
-        lw += w4[e];
-        lc += c4[e];
-      }
-      uint64_t iw = lw;
-      int ic = lc;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const uint64_t tw = __shfl_up(iw, o);
-        const int tc = __shfl_up(ic, o);
-        if (l >= o) {
-          iw += tw;
-          ic += tc;
-        }
-      }
-      uint64_t wb = iw - lw;  // mass of the digits above this lane's
-      int cb = ic - lc;
-      int dg = -1, above = 0, cnt = 0;
-      uint64_t wabove = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (dg < 0 && c4[e] > 0 && wb < rem && rem <= wb + w4[e]) {
-          dg = 255 - 4 * l - e;
-          above = cb;
-          cnt = c4[e];
-          wabove = wb;
-        }
-        wb += w4[e];
-        cb += c4[e];
-      }
-      const uint64_t hit = __ballot(dg >= 0);
-      if (hit == 0ull) return false;  // the list's masses fall short of the remainder
-      const int src = __ffsll(static_cast<unsigned long long>(hit)) - 1;
-      dg = __shfl(dg, src);
-      above = __shfl(above, src);
-      cnt = __shfl(cnt, src);
-      wabove = __shfl(wabove, src);
-      rem -= wabove;
-      rank += above;
-      prefix |= static_cast<uint64_t>(dg) << shift;
-      pmask |= 0xffull << shift;
-      if (cnt == 1) {
-        uint64_t f = 0ull;
-        for (int i = l; i < n; i += kWave)
-          if ((sh.buf[i] & pmask) == prefix) f = sh.buf[i];
-        cutv = wave_max(f);  // the one entry with that prefix
-        break;
-      }
-      if (shift == 0) return false;  // distinct entries: unreachable
-      shift -= 8;
-      wave_lds_sync();  // the bins are cleared again only after every lane has read them
     }
   }
-  if (l == 0) {
+  // thread t holds the entry of rank t
+  uint64_t total;
+  const uint64_t cum = block_scan_incl(static_cast<uint64_t>(w), sh.r64, &total);
+  const int rank = block_sum(cum < fc.rem ? 1 : 0, sh.ri);  // the running mass is nondecreasing
+  if (rank >= n) return false;  // uniform: the list's masses fall short of the remainder
+  if (t == rank) {
     d->mode = kRowFullTopP;
-    d->tau = pkey(cutv);
-    d->id_cut = pid(cutv);
+    d->tau = pkey(v);
+    d->id_cut = pid(v);
     d->kept = static_cast<int32_t>(fc.above_c) + rank + 1;
   }
   return true;
@@ -973,43 +919,45 @@ __global__ __launch_bounds__(kFullThreads) void k_row_full(Job j) {
   const RowCfg c = load_cfg(row, j.V, j.T, j.k, j.p, j.mp, j.seeds);
   const float m = d->m;
   if (c.p < 1.0f) {
-    // the gathered list, when it holds the whole cut bucket: its masses once,
-    // then the select by wave 0 alone (the others wait at one barrier), or by
-    // the whole workgroup for a long list
+    // the gathered list, when it holds the whole cut bucket: a short list
+    // (one entry per thread) sorted and cut by the whole workgroup, a longer
+    // one loaded with its masses into LDS for the workgroup's radix select
     const FullCut fc = j.fcut[row];
     const uint32_t got = j.fcnt[row];
     const bool listed = fc.bucket >= 0 && got == fc.count && got > 0u &&
                         got <= static_cast<uint32_t>(FullSh::kBufCap);  // uniform
     if (listed) {
-      __shared__ int s_done;
       __shared__ uint32_t mw[kFullListCap];
       const int n = static_cast<int>(got);
       const uint64_t* lst = j.flist + static_cast<size_t>(row) * kFullListCap;
       const FullTerms ft{m, c.mp};
-      uint64_t lo = ~0ull, hi = 0ull;
-      for (int i = threadIdx.x; i < n; i += blockDim.x) {
-        const uint64_t v = lst[i];
-        uint64_t w;
-        int b;
-        if (!ft.mass(key2f(pkey(v)), &w, &b)) w = 0;
-        sh.buf[i] = v;
-        mw[i] = static_cast<uint32_t>(w);
-        lo = v < lo ? v : lo;
-        hi = v > hi ? v : hi;
-      }
-      lo = block_min(lo, sh.r64);  // (its barriers also publish buf and mw)
-      hi = block_max(hi, sh.r64);
-      if (n > kWaveCutMax) {
-        if (block_cut_from_list(fc, n, lo, hi, mw, sh, d)) return;  // uniform
-      } else {
-        if (threadIdx.x < kWave) {
-          const bool ok = wave_cut_from_list(fc, n, lo, hi, mw, sh, d);
-          if (threadIdx.x == 0) s_done = ok ? 1 : 0;
+      if (n <= kSortCutMax) {  // uniform
+        uint64_t v = 0ull;
+        uint32_t w = 0u;
+        if (static_cast<int>(threadIdx.x) < n) {
+          v = lst[threadIdx.x];
+          uint64_t wt;
+          int b;
+          w = ft.mass(key2f(pkey(v)), &wt, &b) ? static_cast<uint32_t>(wt) : 0u;
         }
-        __syncthreads();
-        if (s_done) return;  // uniform; else (a list short of the remainder) the full path
+        if (sort_cut_from_list(fc, n, v, w, mw, sh, d)) return;  // uniform
+      } else {
+        uint64_t lo = ~0ull, hi = 0ull;
+        for (int i = threadIdx.x; i < n; i += blockDim.x) {
+          const uint64_t v = lst[i];
+          uint64_t w;
+          int b;
+          if (!ft.mass(key2f(pkey(v)), &w, &b)) w = 0;
+          sh.buf[i] = v;
+          mw[i] = static_cast<uint32_t>(w);
+          lo = v < lo ? v : lo;
+          hi = v > hi ? v : hi;
+        }
+        lo = block_min(lo, sh.r64);  // (its barriers also publish buf and mw)
+        hi = block_max(hi, sh.r64);
+        if (block_cut_from_list(fc, n, lo, hi, mw, sh, d)) return;  // uniform
       }
-      __syncthreads();
+      __syncthreads();  // else (a list short of the remainder) the full path
     }
     const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
     full_topp_cut(rowp, j.V, j.aligned, c, m, sh, d);
