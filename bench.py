@@ -125,16 +125,7 @@ def build_step(vs, torch, wl, copies, dev):
     pst = torch.empty(B, dtype=torch.int32, device=dev)
     full = torch.empty((B, V), dtype=torch.float32, device=dev) if wl.full_logprobs else None
     # the promises a serving engine derives from its batch's parameters
-    greedy_rows = ((wl.temperature == 0) | (wl.top_k == 1) | (wl.top_p == 0) | (wl.min_p == 1))
-    small_k = (wl.top_k > 1) & (wl.top_k <= 64) & (wl.top_k < V)
-    if bool(greedy_rows.all()):
-        hints = vs.HINT_ALL_GREEDY
-    elif bool((greedy_rows | small_k).all()):
-        hints = vs.HINT_SMALL_TOPK
-    elif bool((greedy_rows | ((wl.top_k > 0) & (wl.top_k < V))).all()):
-        hints = vs.HINT_NO_FULLVOCAB
-    else:
-        hints = 0
+    hints = vs.hints_for(wl.temperature, wl.top_k, wl.top_p, wl.min_p, V)
     want_token_lp = not wl.full_logprobs
 
     tlp = torch.empty(B, dtype=torch.float32, device=dev) if want_token_lp else None

@@ -23,7 +23,7 @@ __all__ = [
     "LIB_PATH", "VsError", "load", "workspace_size", "workspace", "penalize", "sample",
     "logprobs", "sample_logprobs", "ROW_BAD_PARAM", "ROW_BAD_LOGITS", "ROW_BAD_TOKEN_ID", "ROW_TOPK_UNSUPPORTED",
     "ROW_HINT_VIOLATED", "HINT_NONE", "HINT_NO_FULLVOCAB", "HINT_ALL_GREEDY", "HINT_SMALL_TOPK", "MAX_V",
-    "TOPK_MAX", "LOGPROB_K_MAX", "EXPORTED_SYMBOLS",
+    "TOPK_MAX", "LOGPROB_K_MAX", "EXPORTED_SYMBOLS", "hints_for",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvs.so")
@@ -87,6 +87,30 @@ def load() -> ctypes.CDLL:
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
+
+
+def hints_for(temperature, top_k, top_p, min_p, V: int) -> int:
+    """The strongest VS_HINT_* promise that a batch's parameters (host arrays,
+    one entry per row; None means the call's default for every row) support:
+    every row greedy; every row greedy or 1 < top_k <= 64; every row greedy or
+    0 < top_k < V; else none. Host bookkeeping only: it reads no logits."""
+    import numpy as np
+
+    def arr(a, default, dt):
+        return np.full(1, default, dt) if a is None else np.asarray(a, dt)
+
+    T = arr(temperature, 1.0, np.float32)
+    k = arr(top_k, 0, np.int64)
+    p = arr(top_p, 1.0, np.float32)
+    mp = arr(min_p, 0.0, np.float32)
+    greedy = (T == 0) | (k == 1) | (p == 0) | (mp == 1)
+    if bool(greedy.all()):
+        return HINT_ALL_GREEDY
+    if bool((greedy | ((k > 1) & (k <= 64) & (k < V))).all()):
+        return HINT_SMALL_TOPK
+    if bool((greedy | ((k > 0) & (k < V))).all()):
+        return HINT_NO_FULLVOCAB
+    return HINT_NONE
 
 
 def _dtype_code(t: torch.Tensor) -> int:

@@ -100,6 +100,8 @@ __global__ __launch_bounds__(kThreads) void k_penalize(
       }
     }
   }
+  // the flag is cleared before any wave can set it
+  __syncthreads();
   // ids outside [0, V) are skipped and reported
   for (int i = threadIdx.x; i < L; i += blockDim.x) {
     const int32_t id = hist_id(i);

@@ -29,7 +29,8 @@ def _lib():
 # ---------------------------------------------------------------- sampling grid
 # Widths around the 4096-id tile edges and the workload widths, several row
 # shapes (ties, flat rows, masked -inf ids) and parameters covering every path.
-WIDTHS = [1, 2, 7, 63, 64, 100, 1000, 4095, 4096, 4097, 8191, 12345, 32000, 70001]
+WIDTHS = [1, 2, 7, 63, 64, 100, 1000, 4095, 4096, 4097, 8191, 12345, 32000, 70001, 151936,
+          248320]
 
 
 def _row_shapes(seed, B, V, dtype):
@@ -49,16 +50,17 @@ def _row_shapes(seed, B, V, dtype):
     return x
 
 
+@pytest.mark.parametrize("seed", range(4))
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("V", WIDTHS)
-def test_sample_grid(V, dtype):
+def test_sample_grid(V, dtype, seed):
     B = 27
-    x = _row_shapes(1000 + V, B, V, dtype)
-    rng = np.random.default_rng(V)
+    x = _row_shapes(1000 + V + 7919 * seed, B, V, dtype)
+    rng = np.random.default_rng(V + 104729 * seed)
     w = random_params(rng, B, V)
     g = gpu_sample(to_device(x), V, w)
     o = oracle_sample(x, V, w)
-    compare_sample(g, o)
+    assert compare_sample(g, o) <= 1
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -260,6 +262,33 @@ def test_penalize_prompt_ignore_many_classes():
     assert np.array_equal(from_device(xd, V), xo)
 
 
+def test_penalize_bad_id_in_every_wave():
+    """Thread i of the penalty workgroup reads history ids i, i + 1024, ...;
+    row r holds its one bad id at position 64 r + 5, which wave r reads. The
+    row status reports it whichever wave finds it, and the valid ids are
+    still applied."""
+    import decode_token_sampling_amd as vs
+    rng = np.random.default_rng(23)
+    B, V = 16, 5000
+    x = synth.random_rows(24, B, V, kind="rank")
+    lists = []
+    for r in range(B):
+        ids = rng.integers(0, V, 1100).astype(np.int32)
+        ids[64 * r + 5] = -1 if r % 2 else V
+        lists.append(ids)
+    oids, ooff = synth._csr(lists)
+    rep = np.full(B, 1.25, np.float32)
+    pres = np.full(B, 0.5, np.float32)
+    xd = to_device(x)
+    st = vs.penalize(xd, output_ids=dev(oids, np.int32), output_off=dev(ooff, np.int32),
+                     presence=dev(pres, np.float32), repetition=dev(rep, np.float32)).cpu().numpy()
+    xo = x.copy()
+    so = oracle.penalize(xo, V, None, None, oids, ooff, pres, None, rep)
+    assert (so == vs.ROW_BAD_TOKEN_ID).all()
+    assert np.array_equal(st, so), st
+    assert np.array_equal(from_device(xd, V), xo)
+
+
 def test_penalize_long_history_many_classes():
     import decode_token_sampling_amd as vs
     rng = np.random.default_rng(13)
@@ -395,78 +424,6 @@ def test_logprobs_ties_and_bad_rows():
     assert np.allclose(gl[ok], ol[ok], atol=LOGPROB_ATOL, rtol=0)
 
 
-# ---------------------------------------------------------------- the five workloads
-def _run_workload(name, sample_rows=None):
-    import decode_token_sampling_amd as vs
-    wl = synth.make(name)
-    xd = to_device(wl.logits)
-    x = wl.logits
-    if wl.has_penalties:
-        st = vs.penalize(xd, dev(wl.prompt_ids, np.int32), dev(wl.prompt_off, np.int32),
-                         dev(wl.output_ids, np.int32), dev(wl.output_off, np.int32),
-                         dev(wl.presence, np.float32), dev(wl.frequency, np.float32),
-                         dev(wl.repetition, np.float32)).cpu().numpy()
-        x = x.copy()
-        so = oracle.penalize(x, wl.V, wl.prompt_ids, wl.prompt_off, wl.output_ids, wl.output_off,
-                             wl.presence, wl.frequency, wl.repetition)
-        assert np.array_equal(st, so)
-        assert np.array_equal(from_device(xd, wl.V).view(np.uint8), x.view(np.uint8))
-    w = params_from(wl)
-    g = gpu_sample(xd, wl.V, w)
-    o = oracle_sample(x, wl.V, w, rows=sample_rows)
-    near = compare_sample(g, o, rows=sample_rows)
-    print(f"{name}: near-tie rows exempt from the id check: {near}")
-    return wl, xd, x, g
-
-
-def test_workload_w4x32000_f32():
-    import decode_token_sampling_amd as vs
-    wl, xd, x, g = _run_workload("w4x32000_f32")
-    lp = vs.logprobs(xd, dev(g["ids"], np.int32), k=0)
-    torch.cuda.synchronize()
-    o = oracle.logprobs(x, wl.V, g["ids"])
-    assert np.allclose(lp["token_lp"].cpu().numpy(), o["token_lp"], atol=LOGPROB_ATOL, rtol=0)
-
-
-def test_workload_w32x151936_bf16():
-    _run_workload("w32x151936_bf16")
-
-
-def test_workload_w256x248320_f32():
-    import decode_token_sampling_amd as vs
-    wl, xd, x, g = _run_workload("w256x248320_f32")
-    lp = vs.logprobs(xd, dev(g["ids"], np.int32), k=20)
-    torch.cuda.synchronize()
-    rows = np.arange(0, wl.B, 8)
-    o = oracle.logprobs(np.ascontiguousarray(x[rows]), wl.V, g["ids"][rows], k=20)
-    assert np.allclose(lp["token_lp"].cpu().numpy()[rows], o["token_lp"], atol=LOGPROB_ATOL, rtol=0)
-    assert np.array_equal(lp["topk_ids"].cpu().numpy()[rows], o["topk_ids"])
-    assert np.allclose(lp["topk_lp"].cpu().numpy()[rows], o["topk_lp"], atol=LOGPROB_ATOL, rtol=0)
-
-
-def test_workload_w1024x128256_f32():
-    import decode_token_sampling_amd as vs
-    wl = synth.make("w1024x128256_f32")
-    xd = to_device(wl.logits)
-    g = gpu_sample(xd, wl.V, params_from(wl), mask=False)
-    assert (g["status"] == 0).all()
-    assert np.array_equal(g["ids"], np.argmax(wl.logits, axis=1))  # greedy = first maximum
-    lp = vs.logprobs(xd, dev(g["ids"], np.int32), k=20, full=True)
-    torch.cuda.synchronize()
-    rows = np.arange(0, wl.B, 37)
-    o = oracle.logprobs(np.ascontiguousarray(wl.logits[rows]), wl.V, g["ids"][rows], k=20, full=True)
-    full = lp["full"][torch.from_numpy(rows).cuda()].cpu().numpy()
-    assert np.abs(full - o["full"]).max() <= LOGPROB_ATOL
-    assert np.array_equal(lp["topk_ids"].cpu().numpy()[rows], o["topk_ids"])
-    # every row: the log-probs sum to one
-    s = torch.logsumexp(lp["full"].double(), dim=1).cpu().numpy()
-    assert np.abs(s).max() < 1e-5
-
-
-def test_workload_w64x262144_bf16():
-    _run_workload("w64x262144_bf16")
-
-
 # ---------------------------------------------------------------- fused draw + log-probs
 def _check_fused_logprobs(x, V, out, k):
     ids = out["ids"].cpu().numpy()
@@ -524,28 +481,6 @@ def test_fused_equals_separate_calls():
     assert torch.equal(f["token_lp"][good], l["token_lp"][good])
     assert torch.equal(f["topk_ids"], l["topk_ids"]) and torch.equal(f["topk_lp"], l["topk_lp"])
     assert torch.equal(f["full"], l["full"])
-
-
-def test_workload_fused_w256x248320_f32():
-    import decode_token_sampling_amd as vs
-    wl = synth.make("w256x248320_f32")
-    x = wl.logits
-    w = params_from(wl)
-    out = vs.sample_logprobs(to_device(x), dev(w["temperature"], np.float32),
-                             dev(w["top_k"], np.int32), dev(w["top_p"], np.float32),
-                             dev(w["min_p"], np.float32),
-                             dev(np.asarray(w["seeds"], np.uint64).view(np.int64), np.int64),
-                             hints=vs.HINT_NO_FULLVOCAB, k=20, mask=True)
-    torch.cuda.synchronize()
-    from parity import mask_bits
-    g = dict(ids=out["ids"].cpu().numpy(), kept=out["kept"].cpu().numpy(),
-             status=out["status"].cpu().numpy(), mask=mask_bits(out["mask"], wl.V))
-    near = compare_sample(g, oracle_sample(x, wl.V, w))
-    print(f"near-tie rows: {near}")
-    rows = np.arange(0, wl.B, 4)
-    sub = {kk: (v[torch.from_numpy(rows).cuda()] if isinstance(v, torch.Tensor) else v)
-           for kk, v in out.items()}
-    _check_fused_logprobs(np.ascontiguousarray(x[rows]), wl.V, sub, 20)
 
 
 # ---------------------------------------------------------------- rows finished by the streaming pass
@@ -658,29 +593,6 @@ def test_finish_in_stream_logprobs(dtype, k):
         assert np.allclose(gk[fin], ok_[fin], atol=LOGPROB_ATOL, rtol=0)
 
 
-def test_finish_in_stream_workload_w256x248320_f32():
-    """The benchmarked call (no mask, hints, top-20 log-probs) against the oracle."""
-    import decode_token_sampling_amd as vs
-    wl = synth.make("w256x248320_f32")
-    x = wl.logits
-    w = params_from(wl)
-    out = vs.sample_logprobs(to_device(x), dev(w["temperature"], np.float32),
-                             dev(w["top_k"], np.int32), dev(w["top_p"], np.float32),
-                             dev(w["min_p"], np.float32),
-                             dev(np.asarray(w["seeds"], np.uint64).view(np.int64), np.int64),
-                             hints=vs.HINT_NO_FULLVOCAB, k=20)
-    torch.cuda.synchronize()
-    g = dict(ids=out["ids"].cpu().numpy(), kept=out["kept"].cpu().numpy(),
-             status=out["status"].cpu().numpy())
-    near = compare_sample(g, oracle_sample(x, wl.V, w, mask=False))
-    print(f"near-tie rows: {near}")
-    rows = np.arange(0, wl.B, 4)
-    o = oracle.logprobs(np.ascontiguousarray(x[rows]), wl.V, g["ids"][rows], k=20)
-    assert np.allclose(out["token_lp"].cpu().numpy()[rows], o["token_lp"], atol=LOGPROB_ATOL, rtol=0)
-    assert np.array_equal(out["topk_ids"].cpu().numpy()[rows], o["topk_ids"])
-    assert np.allclose(out["topk_lp"].cpu().numpy()[rows], o["topk_lp"], atol=LOGPROB_ATOL, rtol=0)
-
-
 # ---------------------------------------------------------------- pool overflow: the rescan
 # Rows that overflow the streaming pass's candidate pool: ascending or
 # descending values (the running bound trails every new value), constant rows
@@ -791,25 +703,3 @@ def test_sample_hint_small_topk(B):
     assert (g["status"][bad] == vs.ROW_HINT_VIOLATED).all() and (g["ids"][bad] == -1).all()
     assert (g["kept"][bad] == 0).all()
     compare_sample(g, o, rows=np.nonzero(~bad)[0])
-
-
-def test_finish_in_stream_workload_small_topk_hint():
-    """The benchmarked call with the small top-k promise (no row kernel)."""
-    import decode_token_sampling_amd as vs
-    wl = synth.make("w256x248320_f32")
-    x = wl.logits
-    w = params_from(wl)
-    out = vs.sample_logprobs(to_device(x), dev(w["temperature"], np.float32),
-                             dev(w["top_k"], np.int32), dev(w["top_p"], np.float32),
-                             dev(w["min_p"], np.float32),
-                             dev(np.asarray(w["seeds"], np.uint64).view(np.int64), np.int64),
-                             hints=vs.HINT_SMALL_TOPK, k=20)
-    torch.cuda.synchronize()
-    g = dict(ids=out["ids"].cpu().numpy(), kept=out["kept"].cpu().numpy(),
-             status=out["status"].cpu().numpy())
-    compare_sample(g, oracle_sample(x, wl.V, w, mask=False))
-    rows = np.arange(1, wl.B, 4)
-    o = oracle.logprobs(np.ascontiguousarray(x[rows]), wl.V, g["ids"][rows], k=20)
-    assert np.allclose(out["token_lp"].cpu().numpy()[rows], o["token_lp"], atol=LOGPROB_ATOL, rtol=0)
-    assert np.array_equal(out["topk_ids"].cpu().numpy()[rows], o["topk_ids"])
-    assert np.allclose(out["topk_lp"].cpu().numpy()[rows], o["topk_lp"], atol=LOGPROB_ATOL, rtol=0)

@@ -48,6 +48,8 @@ MUTANTS = {
                             "                static_cast<const char*>(src) + static_cast<int64_t>(i) * elem_bytes, elem_bytes);"),
     "logprob_temperature_multiplies": ("const float s = (T == 1.0f) ? x : x / T;",
                                        "const float s = (T == 1.0f) ? x : x * T;"),
+    "top2_second_not_demoted": ("      g2 = g1;\n      g1 = score;", "      g1 = score;"),
+    "top2_second_from_best_only": ("    } else if (score > g2) {", "    } else if (score > g1) {"),
     "logprob_ties_to_highest_id": ("        if (z[a] != z[b]) return z[a] > z[b];\n        return a < b;",
                                    "        if (z[a] != z[b]) return z[a] > z[b];\n        return a > b;"),
 }

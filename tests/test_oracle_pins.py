@@ -423,7 +423,7 @@ def test_pipeline_invariants_random_rows(orc):
 def test_gumbel_frequencies_follow_renormalised_softmax(orc):
     """The distribution check (vllm.cpp #1997, 'Red before green': the large-N
     empirical frequency case owns the score formula prob / q)."""
-    V, N = 8, 40000
+    V, N = 8, 100000
     probs = np.array([8, 7, 6, 5, 4, 3, 2, 1], np.float64)
     probs /= probs.sum()
     row = np.log(probs).astype(np.float32)
@@ -443,6 +443,44 @@ def test_gumbel_frequencies_follow_renormalised_softmax(orc):
         exp_c = q[keep] * N
         chi2 = ((counts[keep] - exp_c) ** 2 / exp_c).sum()
         assert chi2 < 30, (k, p, counts, exp_c)      # <= 7 dof, far beyond the 99.99% point
+
+
+def test_gumbel_top_two_scores_brute_force(orc):
+    """The two best Gumbel scores the oracle reports (they decide which rows are
+    near-ties, exempt from the id comparison) against a brute force over the
+    kept set: every kept id's score e / (-log u) from the pinned exponential and
+    uniform, sorted by numpy. The drawn id is the lowest id of the best score
+    (vllm.cpp #1997, 'The kernel (#1984)': score = prob / q, argmax with ties to
+    the lowest index); a row of one kept id reports no scores (-1, -1)."""
+    rng = np.random.default_rng(41)
+    B, V = 60, 48
+    x = np.concatenate([synth.random_rows(42, 20, V, kind="rank"),
+                        synth.random_rows(43, 20, V, kind="normal"),
+                        synth.random_rows(44, 20, V, kind="flat")])
+    T = rng.choice([1.0, 0.5, 1.7], B).astype(np.float32)
+    k = rng.choice([0, 2, 3, 10, 30], B).astype(np.int32)
+    p = rng.choice([1.0, 0.9, 0.5, 0.05], B).astype(np.float32)
+    mp = rng.choice([0.0, 0.0, 0.1], B).astype(np.float32)
+    seeds = rng.integers(0, 2**63, B, dtype=np.int64).astype(np.uint64)
+    out = orc.sample(x, V, T, k, p, mp, seeds, want_mask=True)
+    seen_two = 0
+    for r in range(B):
+        kept = np.nonzero(out["mask"][r])[0]
+        assert len(kept) == out["kept"][r] >= 1
+        if len(kept) == 1:
+            assert out["ids"][r] == kept[0]
+            assert out["top2"][r].tolist() == [-1.0, -1.0]
+            continue
+        s = (x[r] / T[r]).astype(np.float32)
+        m = s.max()
+        sc = np.array([orc.exp_pinned(np.float32(s[j] - m)) / -math.log(orc.uniform(int(seeds[r]), r, int(j)))
+                       for j in kept])
+        order = np.lexsort((kept, -sc))            # best score first, lower id first
+        assert out["ids"][r] == kept[order[0]]
+        assert out["top2"][r, 0] == sc[order[0]]
+        assert out["top2"][r, 1] == sc[order[1]]
+        seen_two += 1
+    assert seen_two >= B // 2
 
 
 # ---------------------------------------------------------------- status rows
