@@ -1,7 +1,8 @@
-// A test aid, built into its own library (libvs_selftest.so), never linked into
-// libvs.so: it evaluates the sampling kernels' device exponential E on a range
-// of fp32 bit patterns so that tests can compare it with the oracle on every
-// input the method can produce.
+// Test and measurement aids, built into their own library (libvs_selftest.so),
+// never linked into libvs.so: the sampling kernels' device exponential E on a
+// range of fp32 bit patterns (so that tests can compare it with the oracle on
+// every input the method can produce), and reference kernels for the
+// benchmark (below).
 #include <hip/hip_runtime.h>
 
 #include "vs_device.h"
@@ -37,23 +38,17 @@ namespace {
 constexpr int kReadThreads = 1024;  // 16 waves, as the streaming pass uses per row
 constexpr int kReadUnroll = 8;      // 16-byte loads in flight per lane
 
-__device__ __forceinline__ uint4 ld16(const uint4* p, int nt) {
-  if (nt) {
-    uint4 v;
-    v.x = __builtin_nontemporal_load(&p->x);
-    v.y = __builtin_nontemporal_load(&p->y);
-    v.z = __builtin_nontemporal_load(&p->z);
-    v.w = __builtin_nontemporal_load(&p->w);
-    return v;
-  }
-  return *p;
+template <bool NT>
+__device__ __forceinline__ uint4 ld16(const uint4* p) {
+  return NT ? vsk::load16_stream(p) : vsk::load16(p);
 }
 
 // One workgroup per row: the row's row_bytes / 16 vectors read by 1024
 // threads, kReadUnroll loads issued before any is used; the bits are folded
 // with max so that no load can be dropped.
+template <bool NT>
 __global__ __launch_bounds__(kReadThreads) void k_read_rows(const char* __restrict__ base,
-                                                           int64_t ld_bytes, int64_t nvec, int nt,
+                                                           int64_t ld_bytes, int64_t nvec,
                                                            uint32_t* __restrict__ out) {
   const uint4* p = reinterpret_cast<const uint4*>(base + static_cast<int64_t>(blockIdx.x) * ld_bytes);
   uint32_t acc = 0;
@@ -61,12 +56,12 @@ __global__ __launch_bounds__(kReadThreads) void k_read_rows(const char* __restri
   for (; i + (kReadUnroll - 1) * kReadThreads < nvec; i += kReadUnroll * kReadThreads) {
     uint4 v[kReadUnroll];
 #pragma unroll
-    for (int u = 0; u < kReadUnroll; ++u) v[u] = ld16(p + i + u * kReadThreads, nt);
+    for (int u = 0; u < kReadUnroll; ++u) v[u] = ld16<NT>(p + i + u * kReadThreads);
 #pragma unroll
     for (int u = 0; u < kReadUnroll; ++u) acc = max(acc, max(max(v[u].x, v[u].y), max(v[u].z, v[u].w)));
   }
   for (; i < nvec; i += kReadThreads) {
-    const uint4 v = ld16(p + i, nt);
+    const uint4 v = ld16<NT>(p + i);
     acc = max(acc, max(max(v.x, v.y), max(v.z, v.w)));
   }
   __shared__ uint32_t s[kReadThreads / 64];
@@ -114,8 +109,12 @@ extern "C" int vs_selftest_read_rows(const void* base, int B, int64_t row_bytes,
   if (!base || !out || B <= 0 || row_bytes <= 0 || row_bytes % 16 || ld_bytes % 16 ||
       ld_bytes < row_bytes || reinterpret_cast<uintptr_t>(base) % 16)
     return static_cast<int>(hipErrorInvalidValue);
-  hipLaunchKernelGGL(k_read_rows, dim3(B), dim3(kReadThreads), 0, stream,
-                     static_cast<const char*>(base), ld_bytes, row_bytes / 16, nt, out);
+  if (nt)
+    hipLaunchKernelGGL(k_read_rows<true>, dim3(B), dim3(kReadThreads), 0, stream,
+                       static_cast<const char*>(base), ld_bytes, row_bytes / 16, out);
+  else
+    hipLaunchKernelGGL(k_read_rows<false>, dim3(B), dim3(kReadThreads), 0, stream,
+                       static_cast<const char*>(base), ld_bytes, row_bytes / 16, out);
   return static_cast<int>(hipGetLastError());
 }
 
