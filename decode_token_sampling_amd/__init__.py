@@ -23,7 +23,8 @@ __all__ = [
     "LIB_PATH", "VsError", "load", "workspace_size", "workspace", "penalize", "sample",
     "logprobs", "sample_logprobs", "ROW_BAD_PARAM", "ROW_BAD_LOGITS", "ROW_BAD_TOKEN_ID", "ROW_TOPK_UNSUPPORTED",
     "ROW_HINT_VIOLATED", "HINT_NONE", "HINT_NO_FULLVOCAB", "HINT_ALL_GREEDY", "HINT_SMALL_TOPK", "MAX_V",
-    "TOPK_MAX", "LOGPROB_K_MAX", "EXPORTED_SYMBOLS", "hints_for",
+    "TOPK_MAX", "LOGPROB_K_MAX", "EXPORTED_SYMBOLS", "hints_for", "sample_logprobs_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvs.so")
@@ -40,10 +41,12 @@ HINT_SMALL_TOPK = 4
 MAX_V = 1 << 21
 TOPK_MAX = 1024
 LOGPROB_K_MAX = 64
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTED_SYMBOLS = ("vs_workspace_size", "vs_status_string", "vs_penalize", "vs_penalize_ex",
                     "vs_sample", "vs_logprobs", "vs_logprobs_ex", "vs_sample_logprobs", "vs_topp_decay",
-                    "vs_seed_advance", "vs_slot_remap", "vs_profile_begin", "vs_profile_end")
+                    "vs_seed_advance", "vs_slot_remap", "vs_profile_begin", "vs_profile_end",
+                    "vs_sample_logprobs_noalloc")
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "workspace too small", 3: "unsupported",
            4: "HIP launch failure"}
@@ -79,11 +82,14 @@ def load() -> ctypes.CDLL:
     lib.vs_logprobs_ex.argtypes = [P, i32, i32, i32, i64, P, P, P, i32, P, P, P, i64, P, P, sz, P]
     lib.vs_sample_logprobs.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, u32, P, P, P, P, P,
                                        i32, P, P, P, i64, P, sz, P]
+    lib.vs_sample_logprobs_noalloc.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, u32, P, P, P,
+                                               P, P, i32, P, P, P, i64, P]
     lib.vs_profile_begin.argtypes = [P, i32]
     lib.vs_profile_end.argtypes = [ctypes.POINTER(ctypes.c_char_p), i32]
     for f in ("vs_workspace_size", "vs_penalize", "vs_penalize_ex", "vs_topp_decay",
               "vs_seed_advance", "vs_slot_remap", "vs_sample", "vs_logprobs", "vs_logprobs_ex",
-              "vs_sample_logprobs", "vs_profile_begin", "vs_profile_end"):
+              "vs_sample_logprobs", "vs_sample_logprobs_noalloc", "vs_profile_begin",
+              "vs_profile_end"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -301,9 +307,31 @@ def sample_logprobs(logits, temperature=None, top_k=None, top_p=None, min_p=None
     """vs_sample and the log-probs of the sampled ids (and top-k) in one pass over the
     logits (vs_sample_logprobs). Returns dict(ids, kept, status, token_lp, topk_ids,
     topk_lp, full[, mask])."""
+    return _sample_logprobs(False, logits, temperature, top_k, top_p, min_p, seeds, hints, k,
+                            token_logprob, full, V, ws, out_ids, kept, mask, row_status,
+                            out_token_lp, out_topk_ids, out_topk_lp, out_full, stream)
+
+
+def sample_logprobs_noalloc(logits, temperature=None, top_k=None, top_p=None, min_p=None,
+                            seeds=None, hints=0, k=0, token_logprob=True, full=False, V=None,
+                            out_ids=None, kept=None, mask=False, row_status=None,
+                            out_token_lp=None, out_topk_ids=None, out_topk_lp=None,
+                            out_full=None, stream=None) -> dict:
+    """sample_logprobs through vs_sample_logprobs_noalloc: no workspace, the
+    library's per-device scratch instead (the library allocates nothing; calls
+    on one device must not overlap). Outputs the caller does not pass are
+    still allocated here, by torch."""
+    return _sample_logprobs(True, logits, temperature, top_k, top_p, min_p, seeds, hints, k,
+                            token_logprob, full, V, None, out_ids, kept, mask, row_status,
+                            out_token_lp, out_topk_ids, out_topk_lp, out_full, stream)
+
+
+def _sample_logprobs(noalloc, logits, temperature, top_k, top_p, min_p, seeds, hints, k,
+                     token_logprob, full, V, ws, out_ids, kept, mask, row_status, out_token_lp,
+                     out_topk_ids, out_topk_lp, out_full, stream) -> dict:
     B, V, ld = _logits_args(logits, V)
     dev = logits.device
-    if ws is None:
+    if ws is None and not noalloc:
         ws = workspace(B, V, logits.dtype, dev)
     ids = out_ids if out_ids is not None else torch.empty(B, dtype=torch.int32, device=dev)
     kc = kept if kept is not None else torch.empty(B, dtype=torch.int32, device=dev)
@@ -323,18 +351,23 @@ def sample_logprobs(logits, temperature=None, top_k=None, top_p=None, min_p=None
         mk = torch.empty((B, (V + 31) // 32), dtype=torch.int32, device=dev)
     elif isinstance(mask, torch.Tensor):
         mk = mask
-    code = load().vs_sample_logprobs(
-        logits.data_ptr(), _dtype_code(logits), B, V, ld,
-        _ptr(temperature, torch.float32, B, "temperature"), _ptr(top_k, torch.int32, B, "top_k"),
-        _ptr(top_p, torch.float32, B, "top_p"), _ptr(min_p, torch.float32, B, "min_p"),
-        _ptr(seeds, torch.int64, B, "seeds"), int(hints), _ptr(ids, torch.int32, B, "out_ids"),
-        _ptr(kc, torch.int32, B, "kept"), _ptr(mk, torch.int32, name="mask"),
-        _ptr(st, torch.int32, B, "row_status"), _ptr(tlp, torch.float32, B, "token_lp"), int(k),
-        _ptr(tids, torch.int32, name="topk_ids"), _ptr(tlps, torch.float32, name="topk_lp"),
-        fo.data_ptr() if fo is not None else None, fo.stride(0) if fo is not None else 0,
-        _ptr(ws, torch.uint8, name="ws"), ws.numel(), _stream(stream))
+    args = [logits.data_ptr(), _dtype_code(logits), B, V, ld,
+            _ptr(temperature, torch.float32, B, "temperature"), _ptr(top_k, torch.int32, B, "top_k"),
+            _ptr(top_p, torch.float32, B, "top_p"), _ptr(min_p, torch.float32, B, "min_p"),
+            _ptr(seeds, torch.int64, B, "seeds"), int(hints), _ptr(ids, torch.int32, B, "out_ids"),
+            _ptr(kc, torch.int32, B, "kept"), _ptr(mk, torch.int32, name="mask"),
+            _ptr(st, torch.int32, B, "row_status"), _ptr(tlp, torch.float32, B, "token_lp"), int(k),
+            _ptr(tids, torch.int32, name="topk_ids"), _ptr(tlps, torch.float32, name="topk_lp"),
+            fo.data_ptr() if fo is not None else None, fo.stride(0) if fo is not None else 0]
+    if noalloc:
+        name = "vs_sample_logprobs_noalloc"
+        code = load().vs_sample_logprobs_noalloc(*args, _stream(stream))
+    else:
+        name = "vs_sample_logprobs"
+        code = load().vs_sample_logprobs(*args, _ptr(ws, torch.uint8, name="ws"), ws.numel(),
+                                         _stream(stream))
     if code:
-        raise VsError("vs_sample_logprobs", code)
+        raise VsError(name, code)
     out = dict(ids=ids, kept=kc, status=st, token_lp=tlp, topk_ids=tids, topk_lp=tlps, full=fo)
     if mk is not None:
         out["mask"] = mk

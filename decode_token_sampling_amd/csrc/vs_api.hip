@@ -1,6 +1,8 @@
 // C ABI of libvs.so: argument checks, workspace layout, kernel sequence.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "vs_device.h"
 #include "vs_kernels.h"
 
@@ -25,10 +27,9 @@ int device_cus() {
 }
 }  // namespace
 
-WsLayout ws_layout(int B, int V) {
+WsLayout ws_layout(int B, int V, int nslot) {
   WsLayout L{};
   L.ntile = (V + kSelTile - 1) / kSelTile;
-  const int nslot = (V + kSegMin - 1) / kSegMin;  // segment slots per row
   L.ntile3 = (V + kGumTile - 1) / kGumTile;
   const size_t tiles = static_cast<size_t>(B) * nslot;
   size_t off = 0;
@@ -62,8 +63,20 @@ WsLayout ws_layout(int B, int V) {
   return L;
 }
 
-Job make_job(const void* logits, vs_dtype dt, int B, int V, int64_t ld, void* ws) {
-  const WsLayout L = ws_layout(B, V);
+int stream_segments(int B, int V) {
+  const int cus = device_cus();
+  const int nslot = ws_slots_any(V);
+  int S = (cus + B - 1) / B;
+  S = S < 1 ? 1 : (S > nslot ? nslot : S);
+  const int ntile = (V + kSelTile - 1) / kSelTile;
+  const int tps = (ntile + S - 1) / S;
+  return (ntile + tps - 1) / tps;
+}
+
+// nslot: the workspace's segment slots per row (ws_slots_any(V) for a
+// caller's workspace, the device's segment count for the library's scratch).
+Job make_job(const void* logits, vs_dtype dt, int B, int V, int64_t ld, void* ws, int nslot) {
+  const WsLayout L = ws_layout(B, V, nslot);
   char* w = static_cast<char*>(ws);
   Job j{};
   j.logits = logits;
@@ -81,9 +94,8 @@ Job make_job(const void* logits, vs_dtype dt, int B, int V, int64_t ld, void* ws
   // (down to 4 waves) so that several share a compute unit and one row's
   // closing steps overlap other rows' streaming.
   const int cus = device_cus();
-  const int nslot = (V + kSegMin - 1) / kSegMin;
   int S = (cus + B - 1) / B;
-  S = S < 1 ? 1 : (S > nslot ? nslot : S);
+  S = S < 1 ? 1 : (S > ws_slots_any(V) ? ws_slots_any(V) : S);
   j.tps = (L.ntile + S - 1) / S;
   j.nseg = (L.ntile + j.tps - 1) / j.tps;
   int wmax = kSelMaxWaves;
@@ -175,7 +187,7 @@ extern "C" {
 
 vs_status vs_workspace_size(int B, int V, vs_dtype dt, size_t* bytes) {
   if (!bytes || !sizes_ok(dt, B, V, V)) return VS_ERR_INVALID_ARGUMENT;
-  *bytes = vsk::ws_layout(B, V).total;
+  *bytes = vsk::ws_layout(B, V, vsk::ws_slots_any(V)).total;
   return VS_OK;
 }
 
@@ -259,22 +271,29 @@ vs_status vs_sample(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
                             nullptr, nullptr, nullptr, 0, ws, ws_bytes, stream);
 }
 
-vs_status vs_sample_logprobs(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
-                             const float* temperature, const int32_t* top_k,
-                             const float* top_p, const float* min_p,
-                             const uint64_t* seeds, uint32_t hints, int32_t* out_ids,
-                             int32_t* out_kept_count, uint32_t* out_kept_mask,
-                             int32_t* out_row_status, float* out_token_logprob, int k,
-                             int32_t* out_topk_ids, float* out_topk_logprobs, float* out_full,
-                             int64_t ld_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// vs_sample_logprobs on a workspace laid out with nslot segment slots per row
+// (ws may be NULL only to check the arguments: then nothing is enqueued).
+vs_status sample_logprobs_impl(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
+                               const float* temperature, const int32_t* top_k,
+                               const float* top_p, const float* min_p,
+                               const uint64_t* seeds, uint32_t hints, int32_t* out_ids,
+                               int32_t* out_kept_count, uint32_t* out_kept_mask,
+                               int32_t* out_row_status, float* out_token_logprob, int k,
+                               int32_t* out_topk_ids, float* out_topk_logprobs, float* out_full,
+                               int64_t ld_out, void* ws, size_t ws_bytes, int nslot,
+                               hipStream_t stream) {
   if (!logits || !out_ids || !ws || !sizes_ok(dt, B, V, ld)) return VS_ERR_INVALID_ARGUMENT;
   if (hints & ~(VS_HINT_NO_FULLVOCAB | VS_HINT_ALL_GREEDY | VS_HINT_SMALL_TOPK))
     return VS_ERR_INVALID_ARGUMENT;
   if (k < 0 || k > VS_LOGPROB_K_MAX || k > V) return VS_ERR_INVALID_ARGUMENT;
   if (k > 0 && (!out_topk_ids || !out_topk_logprobs)) return VS_ERR_INVALID_ARGUMENT;
   if (out_full && ld_out < V) return VS_ERR_INVALID_ARGUMENT;
-  if (ws_bytes < vsk::ws_layout(B, V).total) return VS_ERR_WORKSPACE_TOO_SMALL;
-  vsk::Job j = vsk::make_job(logits, dt, B, V, ld, ws);
+  if (ws_bytes < vsk::ws_layout(B, V, nslot).total) return VS_ERR_WORKSPACE_TOO_SMALL;
+  vsk::Job j = vsk::make_job(logits, dt, B, V, ld, ws, nslot);
   j.sample = 1;
   j.T = temperature;
   j.k = top_k;
@@ -323,6 +342,69 @@ vs_status vs_sample_logprobs(const void* logits, vs_dtype dt, int B, int V, int6
   return VS_OK;
 }
 
+// The library's own scratch for vs_sample_logprobs_noalloc: one array per
+// device (each device that loads the library's code holds its own copy until
+// the process ends). Host code never uses the array's name as an address: the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[VS_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The current device's scratch address (NULL if it cannot be had).
+void* scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  void* p = __atomic_load_n(&g_scratch_ptr[dev], __ATOMIC_ACQUIRE);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev];
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    __atomic_store_n(&g_scratch_ptr[dev], p, __ATOMIC_RELEASE);
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+vs_status vs_sample_logprobs(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
+                             const float* temperature, const int32_t* top_k,
+                             const float* top_p, const float* min_p,
+                             const uint64_t* seeds, uint32_t hints, int32_t* out_ids,
+                             int32_t* out_kept_count, uint32_t* out_kept_mask,
+                             int32_t* out_row_status, float* out_token_logprob, int k,
+                             int32_t* out_topk_ids, float* out_topk_logprobs, float* out_full,
+                             int64_t ld_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return sample_logprobs_impl(logits, dt, B, V, ld, temperature, top_k, top_p, min_p, seeds, hints,
+                              out_ids, out_kept_count, out_kept_mask, out_row_status,
+                              out_token_logprob, k, out_topk_ids, out_topk_logprobs, out_full,
+                              ld_out, ws, ws_bytes, vsk::ws_slots_any(V), stream);
+}
+
+vs_status vs_sample_logprobs_noalloc(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
+                                     const float* temperature, const int32_t* top_k,
+                                     const float* top_p, const float* min_p,
+                                     const uint64_t* seeds, uint32_t hints, int32_t* out_ids,
+                                     int32_t* out_kept_count, uint32_t* out_kept_mask,
+                                     int32_t* out_row_status, float* out_token_logprob, int k,
+                                     int32_t* out_topk_ids, float* out_topk_logprobs,
+                                     float* out_full, int64_t ld_out, hipStream_t stream) {
+  if (!logits || !out_ids || !sizes_ok(dt, B, V, ld)) return VS_ERR_INVALID_ARGUMENT;
+  // laid out for the segments this device's streaming pass uses, not for every device
+  const int nslot = vsk::stream_segments(B, V);
+  if (vsk::ws_layout(B, V, nslot).total > VS_NOALLOC_SCRATCH_BYTES) return VS_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = scratch_ptr();
+  if (!ws) return VS_ERR_HIP;
+  return sample_logprobs_impl(logits, dt, B, V, ld, temperature, top_k, top_p, min_p, seeds, hints,
+                              out_ids, out_kept_count, out_kept_mask, out_row_status,
+                              out_token_logprob, k, out_topk_ids, out_topk_logprobs, out_full,
+                              ld_out, ws, VS_NOALLOC_SCRATCH_BYTES, nslot, stream);
+}
+
 vs_status vs_logprobs(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
                       const int32_t* token_ids, float* out_token_logprob, int k,
                       int32_t* out_topk_ids, float* out_topk_logprobs,
@@ -344,8 +426,8 @@ vs_status vs_logprobs_ex(const void* logits, vs_dtype dt, int B, int V, int64_t 
   if (k < 0 || k > VS_LOGPROB_K_MAX || k > V) return VS_ERR_INVALID_ARGUMENT;
   if (k > 0 && (!out_topk_ids || !out_topk_logprobs)) return VS_ERR_INVALID_ARGUMENT;
   if (out_full && ld_out < V) return VS_ERR_INVALID_ARGUMENT;
-  if (ws_bytes < vsk::ws_layout(B, V).total) return VS_ERR_WORKSPACE_TOO_SMALL;
-  vsk::Job j = vsk::make_job(logits, dt, B, V, ld, ws);
+  if (ws_bytes < vsk::ws_layout(B, V, vsk::ws_slots_any(V)).total) return VS_ERR_WORKSPACE_TOO_SMALL;
+  vsk::Job j = vsk::make_job(logits, dt, B, V, ld, ws, vsk::ws_slots_any(V));
   j.lse = 1;
   j.k_lp = k;
   j.tok = token_ids;

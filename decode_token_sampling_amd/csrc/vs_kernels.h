@@ -178,7 +178,13 @@ struct WsLayout {
   int ntile, ntile3;
   size_t meta, candA, candB, kthA, kthB, desc, gpart, lpart, rlse, fhw, flist, fcnt, fcut, total;
 };
-WsLayout ws_layout(int B, int V);
+// The workspace layout for B rows of V ids with nslot segment slots per row
+// (the streaming pass uses min(nslot, its segment count) of them per row).
+WsLayout ws_layout(int B, int V, int nslot);
+// Segment slots per row that covers every device: one per kSegMin ids.
+inline int ws_slots_any(int V) { return (V + kSegMin - 1) / kSegMin; }
+// Streaming-pass segments per row on the current device.
+int stream_segments(int B, int V);
 
 hipError_t launch_select(const Job& j, hipStream_t st);
 hipError_t launch_row_light(const Job& j, hipStream_t st);

@@ -12,7 +12,9 @@
  * Conventions shared by every call:
  *  - All array arguments are DEVICE pointers unless stated otherwise; sizes and
  *    scalars are host values. The caller owns every buffer. The library keeps no
- *    pointer after a call returns, never allocates and never frees.
+ *    pointer after a call returns, and no call allocates or frees memory (the
+ *    one device array the library owns, the scratch of
+ *    vs_sample_logprobs_noalloc, exists from load to process end).
  *  - Each call checks its host-visible arguments, enqueues kernels on `stream`
  *    and returns without waiting. Outputs are valid once the stream reaches that
  *    point; inputs must stay alive until then. No call synchronises, copies to
@@ -248,6 +250,37 @@ vs_status vs_sample_logprobs(const void* logits, vs_dtype dt, int B, int V, int6
                              int32_t* out_row_status, float* out_token_logprob, int k,
                              int32_t* out_topk_ids, float* out_topk_logprobs, float* out_full,
                              int64_t ld_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * vs_sample_logprobs_noalloc — vs_sample_logprobs without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops that must not call hipMalloc, harnesses that
+ * forbid allocation). The call allocates nothing: its kernels use a scratch
+ * array that the library holds in device memory, VS_NOALLOC_SCRATCH_BYTES
+ * per device, for as long as the process runs.
+ *
+ *  Arguments, outputs and per-row errors: as vs_sample_logprobs (minus ws and
+ *  ws_bytes). The scratch is laid out for the current device's geometry; a
+ *  batch whose layout exceeds VS_NOALLOC_SCRATCH_BYTES (about 100 KB per row
+ *  plus 2 KB per row segment: B = 1024 rows of 128,256 ids do not fit, 256 rows
+ *  of 248,320 do) returns VS_ERR_WORKSPACE_TOO_SMALL and enqueues nothing: use
+ *  vs_sample_logprobs with a workspace instead.
+ *  Every call on one device shares that device's scratch, whatever the stream:
+ *  calls that may overlap in time on one device race and give wrong results;
+ *  order them on one stream (or with events). Nothing in the scratch needs
+ *  clearing between calls.
+ * Errors: as vs_sample_logprobs; VS_ERR_HIP if the scratch's device address
+ * cannot be obtained.
+ */
+#define VS_NOALLOC_SCRATCH_BYTES (64u << 20)
+vs_status vs_sample_logprobs_noalloc(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
+                                     const float* temperature, const int32_t* top_k,
+                                     const float* top_p, const float* min_p,
+                                     const uint64_t* seeds, uint32_t hints, int32_t* out_ids,
+                                     int32_t* out_kept_count, uint32_t* out_kept_mask,
+                                     int32_t* out_row_status, float* out_token_logprob, int k,
+                                     int32_t* out_topk_ids, float* out_topk_logprobs,
+                                     float* out_full, int64_t ld_out, hipStream_t stream);
 
 /*
  * vs_logprobs — log-softmax log-probabilities of the buffer given (temperature

@@ -19,7 +19,7 @@ def _declared():
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["vs_workspace_size", "vs_status_string", "vs_penalize",
                                   "vs_penalize_ex", "vs_sample", "vs_logprobs", "vs_logprobs_ex",
-                                  "vs_sample_logprobs",
+                                  "vs_sample_logprobs", "vs_sample_logprobs_noalloc",
                                   "vs_topp_decay", "vs_seed_advance", "vs_slot_remap",
                                   "vs_profile_begin", "vs_profile_end"])
 
