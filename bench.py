@@ -4,9 +4,11 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|all] [--no-cpu]
 
 A step is one pass of the whole sampling path over one batch of synthetic
-logits already resident in HBM: occurrence penalties when the workload has
-them (vs_penalize), then the draw and the log-probabilities the workload asks
-for in one call (vs_sample_logprobs, one read of the logits).
+logits already resident in HBM: the draw and the log-probabilities the
+workload asks for in one call (vs_sample_logprobs, one read of the logits),
+with the occurrence penalties applied by the same call's streaming pass when
+the workload has them (vs_penalize_sample_logprobs; the separate vs_penalize
+launch before vs_sample_logprobs is timed beside it).
 
 The headline is the 256 x 248,320 fp32 workload (temperature 1, top-k 20,
 top-p 0.95, sampled-id and top-20 log-probs): its K steps are timed exactly,
@@ -181,16 +183,22 @@ class Bench:
         self.tids = torch.empty((B, k), dtype=torch.int32, device=dev) if k else None
         self.tlps = torch.empty((B, k), dtype=torch.float32, device=dev) if k else None
 
-    def step(self, i, hints=None):
+    def step(self, i, hints=None, separate=False):
+        """One step on input copy i: with penalties, the fused call (the
+        streaming pass applies them) or, separate, vs_penalize first."""
         vs = self.vs
         x = self.xs[i % self.copies]
+        kw = dict(hints=self.hints if hints is None else hints, k=self.wl.logprob_k,
+                  token_logprob=self.want_token_lp, ws=self.ws, out_ids=self.ids, kept=self.kept,
+                  row_status=self.st, out_token_lp=self.tlp, out_topk_ids=self.tids,
+                  out_topk_lp=self.tlps, out_full=self.full)
+        if self.pen is not None and not separate:
+            vs.penalize_sample_logprobs(x, *self.pen, penalty_status=self.pst, temperature=self.T,
+                                        top_k=self.K, top_p=self.P, min_p=self.MP, seeds=self.S, **kw)
+            return
         if self.pen is not None:
             vs.penalize(x, *self.pen, row_status=self.pst)
-        vs.sample_logprobs(x, self.T, self.K, self.P, self.MP, self.S,
-                           hints=self.hints if hints is None else hints, k=self.wl.logprob_k,
-                           token_logprob=self.want_token_lp, ws=self.ws, out_ids=self.ids,
-                           kept=self.kept, row_status=self.st, out_token_lp=self.tlp,
-                           out_topk_ids=self.tids, out_topk_lp=self.tlps, out_full=self.full)
+        vs.sample_logprobs(x, self.T, self.K, self.P, self.MP, self.S, **kw)
 
     def restore(self):
         """Fresh logits in every copy (only workloads that penalise in place need it)."""
@@ -198,14 +206,17 @@ class Bench:
             for x in self.xs:
                 x.copy_(self.base)
 
-    def describe(self, hints=None):
+    def describe(self, hints=None, separate=False):
         h = self.hints if hints is None else hints
         wl = self.wl
+        outs = ", ".join(p for p in [
+            "sampled-id lp" if self.want_token_lp else "",
+            f"top-{wl.logprob_k}" if wl.logprob_k else "",
+            "full [B,V] write" if wl.full_logprobs else ""] if p)
+        if self.pen is not None and not separate:
+            return f"vs_penalize_sample_logprobs(hints={h}; {outs})"
         parts = (["vs_penalize"] if self.pen is not None else []) + [
-            f"vs_sample_logprobs(hints={h}; " + ", ".join(p for p in [
-                "sampled-id lp" if self.want_token_lp else "",
-                f"top-{wl.logprob_k}" if wl.logprob_k else "",
-                "full [B,V] write" if wl.full_logprobs else ""] if p) + ")"]
+            f"vs_sample_logprobs(hints={h}; {outs})"]
         return " + ".join(parts)
 
 
@@ -227,12 +238,12 @@ def capture(torch, dev, fn, n):
     return g
 
 
-def time_steps(torch, dev, hip, b: Bench, K, hints=None, eager=False):
+def time_steps(torch, dev, hip, b: Bench, K, hints=None, eager=False, separate=False):
     """Exactly K steps: graph replays of `copies` steps (plus one shorter graph
     for the remainder), each replay bracketed by HIP events on the stream the
     kernels run on; inputs restored between replays outside the events. Returns
     (total ms, per-step ms of each full replay)."""
-    fn = lambda i: b.step(i, hints)
+    fn = lambda i: b.step(i, hints, separate)
     stream = torch.cuda.current_stream(dev).cuda_stream
     g = b.copies
     plan = [g] * (K // g) + ([K % g] if K % g else [])
@@ -260,7 +271,7 @@ def time_steps(torch, dev, hip, b: Bench, K, hints=None, eager=False):
     return float(sum(spans)), per_step
 
 
-def stage_profile(torch, dev, hip, lib, b: Bench, n):
+def stage_profile(torch, dev, hip, lib, b: Bench, n, separate=False):
     """Per-stage durations: eager steps with every kernel stage bracketed by HIP
     events on its stream, queued behind a spin kernel so that the events time
     the GPU, not the host's enqueue rate."""
@@ -272,7 +283,7 @@ def stage_profile(torch, dev, hip, lib, b: Bench, n):
     if lib.vs_profile_begin(pev, cap) != 0:
         raise RuntimeError("vs_profile_begin failed")
     for i in range(n):
-        b.step(i)
+        b.step(i, separate=separate)
     names = (ctypes.c_char_p * (cap // 2))()
     m = lib.vs_profile_end(names, cap // 2)
     torch.cuda.synchronize()
@@ -408,6 +419,12 @@ def measure(vs, torch, dev, hip, st, wl, steps, warmup, eager, splitmix_rate):
     }
     rr = rec["read_reference"]
     rec["read_reference"]["step_vs_read"] = rr["us"] / (ms_per_step * 1e3)
+    if b.pen is not None:
+        t1, _ = time_steps(torch, dev, hip, b, steps, eager=eager, separate=True)
+        sep_stages = stage_profile(torch, dev, hip, vs.load(), b, min(steps, 32), separate=True)
+        rec["separate_penalize"] = {
+            "ms_per_step": t1 / steps, "step": b.describe(separate=True),
+            "stages_ms": {k: float(np.mean(v)) for k, v in sep_stages.items()}}
     if wl.name == HEADLINE and b.hints != 0:
         t0, _ = time_steps(torch, dev, hip, b, steps, hints=0, eager=eager)
         rec["no_hint"] = {"ms_per_step": t0 / steps, "step": b.describe(0),

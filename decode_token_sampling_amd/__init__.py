@@ -24,7 +24,7 @@ __all__ = [
     "logprobs", "sample_logprobs", "ROW_BAD_PARAM", "ROW_BAD_LOGITS", "ROW_BAD_TOKEN_ID", "ROW_TOPK_UNSUPPORTED",
     "ROW_HINT_VIOLATED", "HINT_NONE", "HINT_NO_FULLVOCAB", "HINT_ALL_GREEDY", "HINT_SMALL_TOPK", "MAX_V",
     "TOPK_MAX", "LOGPROB_K_MAX", "EXPORTED_SYMBOLS", "hints_for", "sample_logprobs_noalloc",
-    "NOALLOC_SCRATCH_BYTES",
+    "NOALLOC_SCRATCH_BYTES", "penalize_sample_logprobs",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvs.so")
@@ -46,7 +46,7 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 EXPORTED_SYMBOLS = ("vs_workspace_size", "vs_status_string", "vs_penalize", "vs_penalize_ex",
                     "vs_sample", "vs_logprobs", "vs_logprobs_ex", "vs_sample_logprobs", "vs_topp_decay",
                     "vs_seed_advance", "vs_slot_remap", "vs_profile_begin", "vs_profile_end",
-                    "vs_sample_logprobs_noalloc")
+                    "vs_sample_logprobs_noalloc", "vs_penalize_sample_logprobs")
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "workspace too small", 3: "unsupported",
            4: "HIP launch failure"}
@@ -84,12 +84,15 @@ def load() -> ctypes.CDLL:
                                        i32, P, P, P, i64, P, sz, P]
     lib.vs_sample_logprobs_noalloc.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, u32, P, P, P,
                                                P, P, i32, P, P, P, i64, P]
+    lib.vs_penalize_sample_logprobs.argtypes = [P, i32, i32, i32, i64, P, P, P, P, P, P, P, P, P,
+                                                P, P, P, P, P, u32, P, P, P, P, P, i32, P, P, P,
+                                                i64, P, sz, P]
     lib.vs_profile_begin.argtypes = [P, i32]
     lib.vs_profile_end.argtypes = [ctypes.POINTER(ctypes.c_char_p), i32]
     for f in ("vs_workspace_size", "vs_penalize", "vs_penalize_ex", "vs_topp_decay",
               "vs_seed_advance", "vs_slot_remap", "vs_sample", "vs_logprobs", "vs_logprobs_ex",
-              "vs_sample_logprobs", "vs_sample_logprobs_noalloc", "vs_profile_begin",
-              "vs_profile_end"):
+              "vs_sample_logprobs", "vs_sample_logprobs_noalloc", "vs_penalize_sample_logprobs",
+              "vs_profile_begin", "vs_profile_end"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -326,9 +329,37 @@ def sample_logprobs_noalloc(logits, temperature=None, top_k=None, top_p=None, mi
                             out_token_lp, out_topk_ids, out_topk_lp, out_full, stream)
 
 
+def penalize_sample_logprobs(logits, prompt_ids=None, prompt_off=None, output_ids=None,
+                             output_off=None, presence=None, frequency=None, repetition=None,
+                             prompt_ignore=None, penalty_status=None, temperature=None, top_k=None,
+                             top_p=None, min_p=None, seeds=None, hints=0, k=0, token_logprob=True,
+                             full=False, V=None, ws=None, out_ids=None, kept=None, mask=False,
+                             row_status=None, out_token_lp=None, out_topk_ids=None,
+                             out_topk_lp=None, out_full=None, stream=None) -> dict:
+    """Occurrence penalties in place and sample_logprobs in one call
+    (vs_penalize_sample_logprobs): the streaming pass penalises each segment's
+    history ids before reading it. Returns sample_logprobs' dict plus
+    penalty_status."""
+    B = logits.shape[0]
+    pst = penalty_status if penalty_status is not None else torch.empty(
+        B, dtype=torch.int32, device=logits.device)
+    pen = [_ptr(prompt_ids, torch.int32, name="prompt_ids"),
+           _ptr(prompt_off, torch.int32, B + 1, "prompt_off"),
+           _ptr(output_ids, torch.int32, name="output_ids"),
+           _ptr(output_off, torch.int32, B + 1, "output_off"),
+           _ptr(presence, torch.float32, B, "presence"), _ptr(frequency, torch.float32, B, "frequency"),
+           _ptr(repetition, torch.float32, B, "repetition"),
+           _ptr(prompt_ignore, torch.int32, B, "prompt_ignore"), _ptr(pst, torch.int32, B, "penalty_status")]
+    out = _sample_logprobs(False, logits, temperature, top_k, top_p, min_p, seeds, hints, k,
+                           token_logprob, full, V, ws, out_ids, kept, mask, row_status,
+                           out_token_lp, out_topk_ids, out_topk_lp, out_full, stream, pen=pen)
+    out["penalty_status"] = pst
+    return out
+
+
 def _sample_logprobs(noalloc, logits, temperature, top_k, top_p, min_p, seeds, hints, k,
                      token_logprob, full, V, ws, out_ids, kept, mask, row_status, out_token_lp,
-                     out_topk_ids, out_topk_lp, out_full, stream) -> dict:
+                     out_topk_ids, out_topk_lp, out_full, stream, pen=None) -> dict:
     B, V, ld = _logits_args(logits, V)
     dev = logits.device
     if ws is None and not noalloc:
@@ -359,7 +390,12 @@ def _sample_logprobs(noalloc, logits, temperature, top_k, top_p, min_p, seeds, h
             _ptr(st, torch.int32, B, "row_status"), _ptr(tlp, torch.float32, B, "token_lp"), int(k),
             _ptr(tids, torch.int32, name="topk_ids"), _ptr(tlps, torch.float32, name="topk_lp"),
             fo.data_ptr() if fo is not None else None, fo.stride(0) if fo is not None else 0]
-    if noalloc:
+    if pen is not None:
+        name = "vs_penalize_sample_logprobs"
+        code = load().vs_penalize_sample_logprobs(*args[:5], *pen, *args[5:],
+                                                  _ptr(ws, torch.uint8, name="ws"), ws.numel(),
+                                                  _stream(stream))
+    elif noalloc:
         name = "vs_sample_logprobs_noalloc"
         code = load().vs_sample_logprobs_noalloc(*args, _stream(stream))
     else:

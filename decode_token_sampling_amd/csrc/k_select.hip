@@ -30,6 +30,7 @@
 // then write the row's log-probabilities, reading the row a second time.
 #include "vs_device.h"
 #include "vs_kernels.h"
+#include "vs_penalty.h"
 
 namespace vsk {
 namespace {
@@ -265,8 +266,25 @@ struct List {
 };
 
 
+// The penalty step's table: 2^12 slots of id and count.
+constexpr int kPenLog2 = 12;
+
 struct SegSh {
-  uint64_t pool[2][kPoolCap];  // each list's candidates (packed), appended by all waves
+  // The arrays of the streaming loop and its closing steps share their memory
+  // with the penalty step's table, which is done with before they are first
+  // written.
+  union {
+    struct {
+      uint64_t pool[2][kPoolCap];  // each list's candidates (packed), appended by all waves
+      double q[kPoolCap];          // list A's pool: -log(u) of the entries reaching the bound
+      uint32_t rank[2][kPoolCap];  // each pool entry's rank, summed over the waves' slices
+      uint64_t stage[kSelMaxWaves][kWave];  // per-wave staging of a list rescan
+    };
+    struct {
+      uint32_t pen_keys[1 << kPenLog2];
+      uint32_t pen_counts[1 << kPenLog2];
+    };
+  };
   int next_tile;  // the segment's next unclaimed tile (claimed by whole waves)
   int next_out;   // the next tile of the full log-softmax write
   uint32_t thr[2];
@@ -283,11 +301,9 @@ struct SegSh {
   uint64_t best[2][16];
   uint64_t top[2][kSelCap];  // each list's segment candidates
   uint64_t srt[2][kWave];    // a list's 64 best, sorted (segments handed on; rescans)
-  double q[kPoolCap];        // list A's pool: -log(u) of the entries reaching the bound
   float tot_m, tot_s;        // the segment's log-sum-exp partial
   uint64_t tot_b[2];         // the segment's argmax per argmax list
-  uint32_t rank[2][kPoolCap];  // each pool entry's rank, summed over the waves' slices
-  uint64_t stage[kSelMaxWaves][kWave];  // per-wave staging of a list rescan
+  PenSh pen;                 // the penalty step's scalars
 };
 
 
@@ -802,6 +818,23 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
   const float Tl = kScaled ? lse_T(j, row) : 1.0f;
   const int t_begin = seg * j.tps;
   const int t_end = min(t_begin + j.tps, j.ntile);
+
+  if (j.pen) {
+    // Occurrence penalties of the ids of this segment, in place, before the
+    // segment is read (every id lies in one segment, so each is penalised
+    // once; the first segment also reports ids outside [0, V)). The barrier
+    // orders the writes before the reads below, and before the table's
+    // memory is reused.
+    const PenRow pr = pen_row(row, j.pen_pids, j.pen_poff, j.pen_oids, j.pen_ooff, j.pen_pres,
+                              j.pen_freq, j.pen_rep, j.pen_ign);
+    E* rw = const_cast<E*>(static_cast<const E*>(j.logits)) + static_cast<int64_t>(row) * j.ld;
+    const bool bad_id = penalize_range<E, kPenLog2>(
+        rw, pr, j.V, t_begin * kSelTile, min(t_end * kSelTile, j.V), seg == 0, sh.pen_keys,
+        sh.pen_counts, sh.pen, NT);
+    if (seg == 0 && threadIdx.x == 0 && j.out_pen_status)
+      j.out_pen_status[row] = (pr.bad ? VS_ROW_BAD_PARAM : 0) | (bad_id ? VS_ROW_BAD_TOKEN_ID : 0);
+    __syncthreads();
+  }
 
   if (threadIdx.x == 0) {
     sh.next_tile = t_begin + W;  // the first W tiles go to the waves in order

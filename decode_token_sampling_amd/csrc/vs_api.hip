@@ -275,9 +275,18 @@ vs_status vs_sample(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
 
 namespace {
 
-// vs_sample_logprobs on a workspace laid out with nslot segment slots per row
-// (ws may be NULL only to check the arguments: then nothing is enqueued).
-vs_status sample_logprobs_impl(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
+// The occurrence penalties a fused call applies in its streaming pass.
+struct PenArgs {
+  const int32_t *prompt_ids, *prompt_off, *output_ids, *output_off;
+  const float *presence, *frequency, *repetition;
+  const int32_t* prompt_ignore_len;
+  int32_t* out_status;
+};
+
+// vs_sample_logprobs on a workspace laid out with nslot segment slots per
+// row; with pen, the streaming pass first applies those penalties in place.
+vs_status sample_logprobs_impl(const PenArgs* pen, const void* logits, vs_dtype dt, int B, int V,
+                               int64_t ld,
                                const float* temperature, const int32_t* top_k,
                                const float* top_p, const float* min_p,
                                const uint64_t* seeds, uint32_t hints, int32_t* out_ids,
@@ -293,7 +302,22 @@ vs_status sample_logprobs_impl(const void* logits, vs_dtype dt, int B, int V, in
   if (k > 0 && (!out_topk_ids || !out_topk_logprobs)) return VS_ERR_INVALID_ARGUMENT;
   if (out_full && ld_out < V) return VS_ERR_INVALID_ARGUMENT;
   if (ws_bytes < vsk::ws_layout(B, V, nslot).total) return VS_ERR_WORKSPACE_TOO_SMALL;
+  if (pen && ((pen->prompt_ids == nullptr) != (pen->prompt_off == nullptr) ||
+              (pen->output_ids == nullptr) != (pen->output_off == nullptr)))
+    return VS_ERR_INVALID_ARGUMENT;
   vsk::Job j = vsk::make_job(logits, dt, B, V, ld, ws, nslot);
+  if (pen) {
+    j.pen = 1;
+    j.pen_pids = pen->prompt_ids;
+    j.pen_poff = pen->prompt_off;
+    j.pen_oids = pen->output_ids;
+    j.pen_ooff = pen->output_off;
+    j.pen_pres = pen->presence;
+    j.pen_freq = pen->frequency;
+    j.pen_rep = pen->repetition;
+    j.pen_ign = pen->prompt_ignore_len;
+    j.out_pen_status = pen->out_status;
+  }
   j.sample = 1;
   j.T = temperature;
   j.k = top_k;
@@ -379,8 +403,8 @@ vs_status vs_sample_logprobs(const void* logits, vs_dtype dt, int B, int V, int6
                              int32_t* out_row_status, float* out_token_logprob, int k,
                              int32_t* out_topk_ids, float* out_topk_logprobs, float* out_full,
                              int64_t ld_out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  return sample_logprobs_impl(logits, dt, B, V, ld, temperature, top_k, top_p, min_p, seeds, hints,
-                              out_ids, out_kept_count, out_kept_mask, out_row_status,
+  return sample_logprobs_impl(nullptr, logits, dt, B, V, ld, temperature, top_k, top_p, min_p,
+                              seeds, hints, out_ids, out_kept_count, out_kept_mask, out_row_status,
                               out_token_logprob, k, out_topk_ids, out_topk_logprobs, out_full,
                               ld_out, ws, ws_bytes, vsk::ws_slots_any(V), stream);
 }
@@ -399,10 +423,31 @@ vs_status vs_sample_logprobs_noalloc(const void* logits, vs_dtype dt, int B, int
   if (vsk::ws_layout(B, V, nslot).total > VS_NOALLOC_SCRATCH_BYTES) return VS_ERR_WORKSPACE_TOO_SMALL;
   void* ws = scratch_ptr();
   if (!ws) return VS_ERR_HIP;
-  return sample_logprobs_impl(logits, dt, B, V, ld, temperature, top_k, top_p, min_p, seeds, hints,
-                              out_ids, out_kept_count, out_kept_mask, out_row_status,
+  return sample_logprobs_impl(nullptr, logits, dt, B, V, ld, temperature, top_k, top_p, min_p,
+                              seeds, hints, out_ids, out_kept_count, out_kept_mask, out_row_status,
                               out_token_logprob, k, out_topk_ids, out_topk_logprobs, out_full,
                               ld_out, ws, VS_NOALLOC_SCRATCH_BYTES, nslot, stream);
+}
+
+vs_status vs_penalize_sample_logprobs(void* logits, vs_dtype dt, int B, int V, int64_t ld,
+                                      const int32_t* prompt_ids, const int32_t* prompt_off,
+                                      const int32_t* output_ids, const int32_t* output_off,
+                                      const float* presence, const float* frequency,
+                                      const float* repetition, const int32_t* prompt_ignore_len,
+                                      int32_t* out_penalty_status, const float* temperature,
+                                      const int32_t* top_k, const float* top_p,
+                                      const float* min_p, const uint64_t* seeds, uint32_t hints,
+                                      int32_t* out_ids, int32_t* out_kept_count,
+                                      uint32_t* out_kept_mask, int32_t* out_row_status,
+                                      float* out_token_logprob, int k, int32_t* out_topk_ids,
+                                      float* out_topk_logprobs, float* out_full, int64_t ld_out,
+                                      void* ws, size_t ws_bytes, hipStream_t stream) {
+  const PenArgs pen{prompt_ids, prompt_off, output_ids, output_off, presence,
+                    frequency,  repetition, prompt_ignore_len, out_penalty_status};
+  return sample_logprobs_impl(&pen, logits, dt, B, V, ld, temperature, top_k, top_p, min_p, seeds,
+                              hints, out_ids, out_kept_count, out_kept_mask, out_row_status,
+                              out_token_logprob, k, out_topk_ids, out_topk_logprobs, out_full,
+                              ld_out, ws, ws_bytes, vsk::ws_slots_any(V), stream);
 }
 
 vs_status vs_logprobs(const void* logits, vs_dtype dt, int B, int V, int64_t ld,

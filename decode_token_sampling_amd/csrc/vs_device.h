@@ -581,32 +581,22 @@ __device__ __forceinline__ T wave_merge_top_desc(T a, T b) {
   return v;
 }
 
-// Truncation and the draw over the n <= 64 sorted candidates L (packed, key of
-// s = x / T) with one wave, no block barrier; call from every lane of one wave.
-// min-p keeps e = E(s - m) >= min_p; top-p keeps the shortest prefix whose
-// fixed-point mass reaches p times the kept mass; the draw is the Gumbel-max
-// argmax of e / -log(u) over the kept set, ties to the lowest id. Lane i holds
-// the i-th candidate P (the list in registers); q, when given, holds -log(u)
-// of the candidates (the same values this function would compute). Returns
-// the status (VS_ROW_BAD_LOGITS for an empty list, VS_ROW_BAD_PARAM when s =
-// +inf). Called by a whole wave, every lane active.
-__device__ inline int wave_draw_lanes(uint64_t P, int n, const RowCfg& c, int row,
-                                      int32_t* id_out, int32_t* kept_out, uint32_t* mask_row,
-                                      const double* q) {
+// The cut and the draw over the n <= 64 sorted candidates (lane i holds the
+// i-th, P, packed with the key of s = x / T), given each candidate's relative
+// weight e = E(s - m) (m the largest s) and Gumbel score sc = e / -log(u):
+// min-p keeps e >= min_p; top-p keeps the shortest prefix whose fixed-point
+// mass reaches p times the kept mass; the draw is the largest score over the
+// kept set, ties to the lowest id. Returns the status (VS_ROW_BAD_LOGITS for
+// an empty list, VS_ROW_BAD_PARAM when s = +inf). Called by a whole wave,
+// every lane active; lanes from n on are ignored.
+__device__ inline int wave_cut_draw(uint64_t P, int n, float e, double sc, const RowCfg& c,
+                                    int32_t* id_out, int32_t* kept_out, uint32_t* mask_row) {
   const int i = lane();
   if (n <= 0) return VS_ROW_BAD_LOGITS;  // no candidate: never read an id from it
-  const uint64_t top = readlane_u64(P, 0);
-  if (pkey(top) == kKeyPosInf) return VS_ROW_BAD_PARAM;
-  const float m = key2f(pkey(top));
+  if (pkey(readlane_u64(P, 0)) == kKeyPosInf) return VS_ROW_BAD_PARAM;
   const bool has = i < n;
-  if (!has) P = 0ull;
-  const float e = has ? pinned_exp(key2f(pkey(P)) - m) : 0.0f;
   const bool in_s = has && (e >= c.mp);
   const int id = has ? pid(P) : 0x7fffffff;
-  // every candidate's score, computed before the cut is known so that the two
-  // overlap; nonnegative, so its bits order as integers
-  double sc = 0.0;
-  if (has) sc = q ? static_cast<double>(e) / q[i] : gumbel_score(e, row_stream(c.seed, row), id);
   bool kept = in_s;
   if (c.p < 1.0f) {
     // fixed-point masses (< 2^31 + 1) scanned as 16-bit halves, whose sums
@@ -621,6 +611,7 @@ __device__ inline int wave_draw_lanes(uint64_t P, int n, const RowCfg& c, int ro
     const int cut = hit ? __ffsll(static_cast<unsigned long long>(hit)) - 1 : kWave;
     kept = in_s && i <= cut;
   }
+  // scores are nonnegative, so their bits order as integers
   const uint64_t sb = kept ? static_cast<uint64_t>(__double_as_longlong(sc)) : 0ull;
   const uint64_t best = wave_max_u64_dpp(sb);
   const int win = wave_min_dpp((kept && sb == best) ? id : 0x7fffffff);
@@ -628,6 +619,26 @@ __device__ inline int wave_draw_lanes(uint64_t P, int n, const RowCfg& c, int ro
   *id_out = win;
   *kept_out = __popcll(__ballot(kept));
   return 0;
+}
+
+// Truncation and the draw over the n <= 64 sorted candidates P (lane i the
+// i-th) with one wave, no block barrier: each lane forms its candidate's
+// weight and score (q, when given, holds -log(u) of the candidates by lane,
+// the same values this function would compute), then wave_cut_draw. Called by
+// a whole wave, every lane active.
+__device__ inline int wave_draw_lanes(uint64_t P, int n, const RowCfg& c, int row,
+                                      int32_t* id_out, int32_t* kept_out, uint32_t* mask_row,
+                                      const double* q) {
+  const int i = lane();
+  if (n <= 0) return VS_ROW_BAD_LOGITS;
+  const float m = key2f(pkey(readlane_u64(P, 0)));
+  const bool has = i < n;
+  const float e = has ? pinned_exp(key2f(pkey(P)) - m) : 0.0f;
+  // every candidate's score, computed before the cut is known so that the two
+  // overlap
+  double sc = 0.0;
+  if (has) sc = q ? static_cast<double>(e) / q[i] : gumbel_score(e, row_stream(c.seed, row), pid(P));
+  return wave_cut_draw(has ? P : 0ull, n, e, sc, c, id_out, kept_out, mask_row);
 }
 // The same with the sorted candidates in memory (LDS).
 __device__ inline int wave_draw(const uint64_t* L, int n, const RowCfg& c, int row,

@@ -107,6 +107,18 @@ struct Job {
   int64_t ld_out;
   int32_t* out_lp_status;  // vs_logprobs status
   const float* lpT;        // [B] temperature of the log-probs (vs_logprobs_ex), or NULL
+  // occurrence penalties applied by the streaming pass before it reads its
+  // segment (vs_penalize_sample_logprobs); the logits are then written in place
+  int pen;
+  const int32_t* pen_pids;
+  const int32_t* pen_poff;
+  const int32_t* pen_oids;
+  const int32_t* pen_ooff;
+  const float* pen_pres;
+  const float* pen_freq;
+  const float* pen_rep;
+  const int32_t* pen_ign;
+  int32_t* out_pen_status;
   // full-vocabulary top-p (per row): mass histogram, the cut bucket's ids
   uint64_t* fhw;       // [B][kFullBuckets] masses
   uint64_t* flist;     // [B][kFullListCap] packed (key, id) of the cut bucket

@@ -252,6 +252,38 @@ vs_status vs_sample_logprobs(const void* logits, vs_dtype dt, int B, int V, int6
                              int64_t ld_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * vs_penalize_sample_logprobs — vs_penalize_ex followed by vs_sample_logprobs
+ * in one call: the streaming pass that reads each row segment first applies
+ * the occurrence penalties (TensorRT-LLM "Sampling", occurrence-penalty and
+ * prompt_ignore_length bullets; the same arithmetic, rounding and row checks
+ * as vs_penalize_ex) to the segment's history ids, in place, then reads the
+ * segment. The result equals the two calls in sequence, without the separate
+ * penalty launch and its second pass over each history.
+ *
+ *  logits      [B, ld] fp32 or bf16, modified in place: on return it holds the
+ *              penalised logits, as after vs_penalize_ex (later passes of the
+ *              same call, for full-vocabulary rows, read them from there).
+ *  prompt_ids .. prompt_ignore_len: as vs_penalize_ex (NULL pairs: no history;
+ *              NULL parameters: 0, 0, 1; NULL ignore lengths: 0).
+ *  out_penalty_status [B] int32 or NULL: the penalty step's status per row, as
+ *              vs_penalize_ex's out_row_status.
+ *  every other argument, and the errors: as vs_sample_logprobs.
+ */
+vs_status vs_penalize_sample_logprobs(void* logits, vs_dtype dt, int B, int V, int64_t ld,
+                                      const int32_t* prompt_ids, const int32_t* prompt_off,
+                                      const int32_t* output_ids, const int32_t* output_off,
+                                      const float* presence, const float* frequency,
+                                      const float* repetition, const int32_t* prompt_ignore_len,
+                                      int32_t* out_penalty_status, const float* temperature,
+                                      const int32_t* top_k, const float* top_p,
+                                      const float* min_p, const uint64_t* seeds, uint32_t hints,
+                                      int32_t* out_ids, int32_t* out_kept_count,
+                                      uint32_t* out_kept_mask, int32_t* out_row_status,
+                                      float* out_token_logprob, int k, int32_t* out_topk_ids,
+                                      float* out_topk_logprobs, float* out_full, int64_t ld_out,
+                                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * vs_sample_logprobs_noalloc — vs_sample_logprobs without a workspace
  * argument, for callers that cannot allocate device memory (code under HIP
  * graph capture, serving loops that must not call hipMalloc, harnesses that

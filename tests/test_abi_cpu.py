@@ -20,6 +20,7 @@ def test_header_declares_the_boundary():
     assert _declared() == sorted(["vs_workspace_size", "vs_status_string", "vs_penalize",
                                   "vs_penalize_ex", "vs_sample", "vs_logprobs", "vs_logprobs_ex",
                                   "vs_sample_logprobs", "vs_sample_logprobs_noalloc",
+                                  "vs_penalize_sample_logprobs",
                                   "vs_topp_decay", "vs_seed_advance", "vs_slot_remap",
                                   "vs_profile_begin", "vs_profile_end"])
 
@@ -66,6 +67,20 @@ def test_host_checks_without_gpu():
                            dummy, 1 << 30, None) == 1        # k > 64
     assert lib.vs_sample(dummy, 0, 4, 10, 10, *([None] * 5), 8, dummy, None, None, None,
                          dummy, 1 << 30, None) == 1          # unknown hint bit
+
+
+def test_fused_penalty_host_checks_without_gpu():
+    import decode_token_sampling_amd as vs
+    lib = vs.load()
+    d = ctypes.c_void_p(16)  # never dereferenced: the checks fail first
+    # a prompt id array without its offsets
+    assert lib.vs_penalize_sample_logprobs(d, 0, 4, 10, 10, d, None, None, None, None, None, None,
+                                           None, None, *([None] * 5), 0, d, None, None, None, None,
+                                           0, None, None, None, 0, d, 1 << 30, None) == 1
+    # workspace too small
+    assert lib.vs_penalize_sample_logprobs(d, 0, 4, 10, 10, *([None] * 9), *([None] * 5), 0, d,
+                                           None, None, None, None, 0, None, None, None, 0, d, 8,
+                                           None) == 2
 
 
 def test_binding_refuses_host_tensors():

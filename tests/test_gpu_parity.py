@@ -307,6 +307,106 @@ def test_penalize_long_history_many_classes():
     assert np.array_equal(from_device(xd, V), xo)
 
 
+# ---------------------------------------------------------------- penalties fused into the draw
+def _histories(rng, B, V, with_bad=True):
+    pl = rng.integers(0, 1500, B)
+    ol = rng.integers(0, 300, B)
+    pl[min(3, B - 1)] = 0
+    pids, poff = synth._csr([synth.zipf_ids(rng, int(n), V) for n in pl])
+    # output ids: Zipf plus uniform ids, so that every segment of a row has some
+    oids, ooff = synth._csr([np.concatenate([synth.zipf_ids(rng, int(n) // 2, V),
+                                             rng.integers(0, V, int(n) - int(n) // 2).astype(np.int32)])
+                             for n in ol])
+    oids = oids.copy()
+    if with_bad and len(oids) > 9:
+        oids[2], oids[9] = -3, V          # bad ids: skipped and reported
+    ign = np.array([rng.integers(-5, n + 50) if n else 0 for n in pl], np.int32)
+    pres = rng.uniform(-0.5, 1.0, B).astype(np.float32)
+    freq = rng.uniform(-0.2, 1.0, B).astype(np.float32)
+    rep = rng.uniform(0.7, 1.5, B).astype(np.float32)
+    if B > 5:
+        rep[5] = 0.0                      # a bad parameter: that row is left unpenalised
+    return pids, poff, oids, ooff, pres, freq, rep, ign
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,V", [(24, 40000), (7, 70001), (320, 9000)])
+def test_fused_penalties_equal_separate_calls_and_oracle(B, V, dtype):
+    """vs_penalize_sample_logprobs against vs_penalize_ex then
+    vs_sample_logprobs on a copy, and against the oracle's penalties then draw:
+    penalised logits, penalty status, ids, kept counts and row status bit-exact;
+    log-probs within 1e-5. Rows take one segment each (320 rows: the streaming
+    pass finishes them) or several (the row and full-vocabulary kernels read
+    the penalised logits the streaming pass wrote)."""
+    import decode_token_sampling_amd as vs
+    rng = np.random.default_rng(B + V)
+    x = _row_shapes(60 + V, B, V, dtype)
+    pids, poff, oids, ooff, pres, freq, rep, ign = _histories(rng, B, V)
+    w = random_params(np.random.default_rng(V - B), B, V)
+    hist = [dev(pids, np.int32), dev(poff, np.int32), dev(oids, np.int32), dev(ooff, np.int32),
+            dev(pres, np.float32), dev(freq, np.float32), dev(rep, np.float32)]
+    args = [dev(w["temperature"], np.float32), dev(w["top_k"], np.int32), dev(w["top_p"], np.float32),
+            dev(w["min_p"], np.float32), dev(np.asarray(w["seeds"], np.uint64).view(np.int64), np.int64)]
+    xa, xb = to_device(x), to_device(x)
+    f = vs.penalize_sample_logprobs(xa, *hist, prompt_ignore=dev(ign, np.int32), temperature=args[0],
+                                    top_k=args[1], top_p=args[2], min_p=args[3], seeds=args[4],
+                                    k=5, V=V)
+    pst = vs.penalize(xb, *hist, prompt_ignore=dev(ign, np.int32), V=V)
+    s2 = vs.sample_logprobs(xb, *args, k=5, V=V)
+    torch.cuda.synchronize()
+    assert torch.equal(xa, xb) if dtype == "f32" else torch.equal(xa.view(torch.int16), xb.view(torch.int16))
+    assert torch.equal(f["penalty_status"], pst)
+    for key in ("ids", "kept", "status", "topk_ids"):
+        assert torch.equal(f[key], s2[key]), key
+    for key in ("token_lp", "topk_lp"):
+        a, b = f[key].cpu().numpy(), s2[key].cpu().numpy()
+        assert np.array_equal(np.isnan(a), np.isnan(b))
+        ok = ~np.isnan(b)
+        assert np.abs(a[ok] - b[ok]).max() <= LOGPROB_ATOL
+    xo = x.copy()
+    so = oracle.penalize(xo, V, pids, poff, oids, ooff, pres, freq, rep, prompt_ignore=ign)
+    assert np.array_equal(f["penalty_status"].cpu().numpy(), so)
+    assert np.array_equal(from_device(xa, V).view(np.uint8), xo.view(np.uint8))
+    g = dict(ids=f["ids"].cpu().numpy(), kept=f["kept"].cpu().numpy(), status=f["status"].cpu().numpy())
+    compare_sample(g, oracle_sample(xo, V, w, mask=False))
+    _check_fused_logprobs(xo, V, f, 5)
+
+
+@pytest.mark.parametrize("B", [9, 300])
+def test_fused_penalties_move_the_argmax(B):
+    """Greedy rows whose largest logit (at a segment's first, middle or last id,
+    or the row's last) is in the history with a large presence penalty: the
+    draw must see the penalised value that the same pass wrote, so the argmax
+    moves to the runner-up, as the oracle's penalties-then-draw says."""
+    import decode_token_sampling_amd as vs
+    V = 50000
+    rng = np.random.default_rng(B)
+    x = synth.random_rows(70 + B, B, V, kind="normal")
+    spots = [0, 2047, 2048, 4096 * 3 + 5, V // 2, V - 1]
+    lists = []
+    for r in range(B):
+        top = spots[r % len(spots)]
+        x[r, top] = 50.0
+        lists.append(np.array([top, int(rng.integers(0, V))], np.int32))
+    oids, ooff = synth._csr(lists)
+    pres = np.full(B, 100.0, np.float32)
+    T = np.zeros(B, np.float32)
+    w = dict(temperature=T, top_k=np.zeros(B, np.int32), top_p=np.ones(B, np.float32),
+             min_p=np.zeros(B, np.float32), seeds=np.arange(B, dtype=np.uint64))
+    xd = to_device(x)
+    f = vs.penalize_sample_logprobs(xd, output_ids=dev(oids, np.int32), output_off=dev(ooff, np.int32),
+                                    presence=dev(pres, np.float32), temperature=dev(T, np.float32),
+                                    k=1, V=V)
+    torch.cuda.synchronize()
+    xo = x.copy()
+    oracle.penalize(xo, V, None, None, oids, ooff, pres, None, None)
+    o = oracle_sample(xo, V, w, mask=False)
+    ids = f["ids"].cpu().numpy()
+    assert np.array_equal(ids, o["ids"])
+    assert not np.any(ids == np.array([spots[r % len(spots)] for r in range(B)]))
+    assert np.array_equal(from_device(xd, V), xo)
+
+
 # ---------------------------------------------------------------- log-probs
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("V", [1, 5, 64, 4097, 33333])

@@ -1,9 +1,10 @@
 """GPU parity on the five benchmark workloads at full size, against the oracle.
 
-Each workload runs exactly the call sequence bench.py times (penalties in
-place when the workload has them, then one vs_sample_logprobs call with the
-hint its parameters support, the log-prob outputs the workload asks for and no
-kept mask), and every row of every output is compared: penalised logits and
+Each workload runs the call bench.py times (one vs_sample_logprobs call with
+the hint its parameters support, the log-prob outputs the workload asks for
+and no kept mask; for the penalised workloads vs_penalize_sample_logprobs,
+and vs_penalize then vs_sample_logprobs as the separate path bench.py times
+beside it), and every row of every output is compared: penalised logits and
 row status bit-exact, ids and kept counts bit-exact, sampled-id and top-k
 log-probs within 1e-5, the full log-softmax within 1e-5 on every fourth row
 and normalised on every row. The same logits then go through the path that
@@ -85,7 +86,8 @@ def _check_lp(got, want):
 
 @pytest.mark.parametrize("name", WORKLOADS)
 def test_workload_benched_call(name):
-    """The call bench.py times, every row of every output against the oracle."""
+    """The call bench.py times (for penalised workloads, its separate-launch
+    variant), every row of every output against the oracle."""
     import decode_token_sampling_amd as vs
     wl, x, pst, o, lp, full_rows, full = _oracle(name)
     xd = _penalised_device(wl, x, pst)
@@ -138,3 +140,31 @@ def test_workload_separate_calls(name):
     _check_lp(out["topk_lp"], lp["topk_lp"])
     if wl.full_logprobs:
         _check_lp(out["full"][torch.from_numpy(full_rows).cuda()], full)
+
+
+@pytest.mark.parametrize("name", ["w32x151936_bf16", "w64x262144_bf16"])
+def test_workload_fused_penalties(name):
+    """The penalised workloads through vs_penalize_sample_logprobs (the
+    penalties applied by the streaming pass, the call bench.py times for
+    them): penalised logits, penalty status, ids, kept counts and sampled-id
+    log-probs of every row against the oracle."""
+    import decode_token_sampling_amd as vs
+    wl, x, pst, o, lp, full_rows, full = _oracle(name)
+    xd = to_device(wl.logits)
+    w = params_from(wl)
+    hints = vs.hints_for(wl.temperature, wl.top_k, wl.top_p, wl.min_p, wl.V)
+    out = vs.penalize_sample_logprobs(
+        xd, dev(wl.prompt_ids, np.int32), dev(wl.prompt_off, np.int32), dev(wl.output_ids, np.int32),
+        dev(wl.output_off, np.int32), dev(wl.presence, np.float32), dev(wl.frequency, np.float32),
+        dev(wl.repetition, np.float32), temperature=dev(w["temperature"], np.float32),
+        top_k=dev(w["top_k"], np.int32), top_p=dev(w["top_p"], np.float32),
+        min_p=dev(w["min_p"], np.float32),
+        seeds=dev(np.asarray(w["seeds"], np.uint64).view(np.int64), np.int64), hints=hints,
+        k=wl.logprob_k)
+    torch.cuda.synchronize()
+    assert np.array_equal(out["penalty_status"].cpu().numpy(), pst)
+    assert np.array_equal(from_device(xd, wl.V).view(np.uint8), x.view(np.uint8))
+    g = dict(ids=out["ids"].cpu().numpy(), kept=out["kept"].cpu().numpy(),
+             status=out["status"].cpu().numpy())
+    assert compare_sample(g, o, check_mask=False) == 0
+    _check_lp(out["token_lp"], lp["token_lp"])
