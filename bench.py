@@ -425,6 +425,12 @@ def measure(vs, torch, dev, hip, st, wl, steps, warmup, eager, splitmix_rate):
         rec["separate_penalize"] = {
             "ms_per_step": t1 / steps, "step": b.describe(separate=True),
             "stages_ms": {k: float(np.mean(v)) for k, v in sep_stages.items()}}
+    full_topp = (~((wl.temperature == 0) | (wl.top_k == 1) | (wl.top_p == 0) | (wl.min_p == 1)) &
+                 ((wl.top_k == 0) | (wl.top_k >= wl.V)) & (wl.top_p < 1)).any()
+    if full_topp:  # the other method for full-vocabulary top-p rows, timed beside
+        hr = b.hints | vs.OPT_TOPP_REJECTION
+        tr, _ = time_steps(torch, dev, hip, b, steps, hints=hr, eager=eager)
+        rec["topp_rejection"] = {"ms_per_step": tr / steps, "step": b.describe(hr)}
     if wl.name == HEADLINE and b.hints != 0:
         t0, _ = time_steps(torch, dev, hip, b, steps, hints=0, eager=eager)
         rec["no_hint"] = {"ms_per_step": t0 / steps, "step": b.describe(0),

@@ -103,9 +103,66 @@ struct SegReader {
 template <bool kDiv>
 __device__ __forceinline__ float scaled_by(float x, float T) { return kDiv ? x / T : x; }
 
-template <typename E>
+// The random words b below which an id cannot beat the score bound lim:
+// with u = ((b >> 12) + 1/2) 2^-52, every b < skip_below(lim) has
+// 1 - u >= lim (1 + 2^-45) + 2^-52, so (1 - u)(1 - 2^-50) rounded stays
+// >= lim and the id scores below the bound (0: no b, while lim >= 1).
+__device__ __forceinline__ uint64_t cand_skip_below(double lim) {
+  if (!(lim < 1.0)) return 0ull;
+  // (1 - lim (1 + 2^-45)) 2^52 - 2, whose rounding errors stay below 1.5
+  const double v = (1.0 - lim * (1.0 + 0x1p-45)) * 0x1p52 - 2.0;
+  if (!(v > 0.0)) return 0ull;
+  return static_cast<uint64_t>(v) << 12;  // floor(v) < 2^52
+}
+
+// A thread's kCandM best Gumbel candidates, best first in the order (score
+// desc, id asc); empty slots score -1.
+struct CandList {
+  double s[kCandM];
+  int32_t id[kCandM];
+  uint32_t key[kCandM];
+  __device__ __forceinline__ void clear() {
+#pragma unroll
+    for (int i = 0; i < kCandM; ++i) {
+      s[i] = -1.0;
+      id[i] = 0x7fffffff;
+      key[i] = 0u;
+    }
+  }
+  __device__ __forceinline__ static bool before(double sa, int32_t ia, double sb, int32_t ib) {
+    return sa > sb || (sa == sb && ia < ib);
+  }
+  // inserts (sc, i, k) in order when it beats the last entry
+  __device__ __forceinline__ void insert(double sc, int32_t i, uint32_t k) {
+    if (!before(sc, i, s[kCandM - 1], id[kCandM - 1])) return;
+    s[kCandM - 1] = sc;
+    id[kCandM - 1] = i;
+    key[kCandM - 1] = k;
+#pragma unroll
+    for (int p = kCandM - 1; p > 0; --p) {
+      if (before(s[p], id[p], s[p - 1], id[p - 1])) {
+        const double ts = s[p];
+        s[p] = s[p - 1];
+        s[p - 1] = ts;
+        const int32_t ti = id[p];
+        id[p] = id[p - 1];
+        id[p - 1] = ti;
+        const uint32_t tk = key[p];
+        key[p] = key[p - 1];
+        key[p - 1] = tk;
+      }
+    }
+  }
+};
+
+// kReject: the rejection draw's candidates are kept too (a separate instance,
+// so that the histogram alone keeps its own code).
+template <typename E, bool kReject>
 __global__ __launch_bounds__(kThreads) void k_full_hist(Job j) {
   __shared__ uint64_t hw[kFullBuckets];
+  __shared__ double sd[kThreads / kWave];
+  __shared__ int si[kThreads / kWave];
+  __shared__ uint64_t s_bound;  // bits of the best known lower bound on the segment's kCandM-th score
   int row, seg;
   if (!xcd_row_tile(blockIdx.x, j.B, j.fseg, &row, &seg)) return;  // uniform per block
   RowCfg c;
@@ -117,18 +174,59 @@ __global__ __launch_bounds__(kThreads) void k_full_hist(Job j) {
   SegReader<E, 4> rd;
   rd.start(rowp, lo, hi, j.aligned != 0);
   for (int i = threadIdx.x; i < kFullBuckets; i += kThreads) hw[i] = 0ull;
+  if (threadIdx.x == 0) s_bound = 0ull;
   __syncthreads();
   const FullTerms ft{m, c.mp};
+  constexpr bool reject = kReject;
+  // The rejection draw's candidates: every member id's Gumbel score e / -log u
+  // (e and u exactly as the Gumbel pass forms them) into this thread's best
+  // kCandM. An id is skipped when it provably scores below a lower bound on
+  // the segment's kCandM-th best score (the largest kCandM-th best any thread
+  // has; shared through LDS, where a stale value is only a looser bound): 
+  // -log u > 1 - u for u < 1, so 1 - u >= e / bound means e / -log u < bound;
+  // e <= 1 gives a first test on the random word alone (an integer compare).
+  const uint64_t rs = row_stream(c.seed, row);
+  CandList cl;
+  cl.clear();
+  double lim = __builtin_inf();  // (1 + 2^-40) / bound
+  uint64_t skip = 0ull;
+  const auto refresh = [&]() {
+    const uint64_t sb = __hip_atomic_load(&s_bound, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const double bd = __longlong_as_double(static_cast<long long>(sb));
+    if (bd > 0.0 && (1.0 + 0x1p-40) / bd < lim) {
+      lim = (1.0 + 0x1p-40) / bd;
+      skip = cand_skip_below(lim);
+    }
+  };
+  const auto candidate = [&](int id, float e, uint32_t key) {
+    const uint64_t b = random_bits(rs, id);
+    if (b < skip) return;  // e <= 1: below the bound
+    const double u = uniform_of_bits(b);
+    const double one_u = (1.0 - u) * (1.0 - 0x1p-50);  // rounded down past any rounding error
+    if (one_u >= lim * static_cast<double>(e)) return;  // below the bound
+    const double sc = static_cast<double>(e) / -log(u);  // as the Gumbel pass scores it
+    cl.insert(sc, id, key);
+    if (cl.s[kCandM - 1] > 0.0) {  // this thread's own kCandM-th best bounds the segment's
+      const uint64_t sb = static_cast<uint64_t>(__double_as_longlong(cl.s[kCandM - 1]));
+      atomicMax(reinterpret_cast<unsigned long long*>(&s_bound), static_cast<unsigned long long>(sb));
+      refresh();
+    }
+  };
   // one LDS atomic per member id (non-members, e.g. below min-p, skip it:
   // adding 0 at one shared address would serialize the wave's lanes)
   auto pass = [&](auto div) {
-    rd.visit([&](int, const float* x, int n) {
+    rd.visit([&](int id0, const float* x, int n) {
+      if constexpr (reject) refresh();
 #pragma unroll
       for (int q = 0; q < SegReader<E, 4>::EPV; ++q) {
         uint64_t w;
         int b;
-        if (ft.mass(scaled_by<decltype(div)::value>(x[q], c.T), &w, &b) && q < n)
+        float e;
+        const float sv = scaled_by<decltype(div)::value>(x[q], c.T);
+        if (ft.mass_e(sv, &w, &b, &e) && q < n) {
           atomicAdd(reinterpret_cast<unsigned long long*>(&hw[b]), static_cast<unsigned long long>(w));
+          if constexpr (reject) candidate(id0 + q, e, f2key(sv));
+        }
       }
     });
   };
@@ -141,6 +239,28 @@ __global__ __launch_bounds__(kThreads) void k_full_hist(Job j) {
   for (int b = threadIdx.x; b < kFullBuckets; b += kThreads) {
     const uint64_t v = hw[b];
     if (v) atomicAdd(reinterpret_cast<unsigned long long*>(&ghw[b]), static_cast<unsigned long long>(v));
+  }
+  if constexpr (reject) {
+    // the segment's kCandM best, one block argmax a round, the owner popping
+    // its head
+    GCand* out = j.fcand + (static_cast<size_t>(row) * j.ntile3 + seg) * kCandM;
+    for (int r = 0; r < kCandM; ++r) {
+      const double bs = block_max(cl.s[0], sd);
+      const int bi = block_min(cl.s[0] == bs ? cl.id[0] : 0x7fffffff, si);
+      const bool mine = cl.s[0] == bs && cl.id[0] == bi && bs >= 0.0;
+      if (mine) {
+        out[r] = GCand{bs, bi, cl.key[0]};
+#pragma unroll
+        for (int p = 0; p + 1 < kCandM; ++p) {
+          cl.s[p] = cl.s[p + 1];
+          cl.id[p] = cl.id[p + 1];
+          cl.key[p] = cl.key[p + 1];
+        }
+        cl.s[kCandM - 1] = -1.0;
+        cl.id[kCandM - 1] = 0x7fffffff;
+      }
+      if (threadIdx.x == 0 && bs < 0.0) out[r] = GCand{-1.0, 0x7fffffff, 0u};
+    }
   }
 }
 
@@ -288,10 +408,14 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
 
 hipError_t launch_full_prep(const Job& j, hipStream_t st) {
   const int grid = xcd_grid(j.B, j.fseg);
-  if (j.dt == VS_F32)
-    hipLaunchKernelGGL(k_full_hist<float>, dim3(grid), dim3(kThreads), 0, st, j);
+  if (j.dt == VS_F32 && j.topp_reject)
+    hipLaunchKernelGGL((k_full_hist<float, true>), dim3(grid), dim3(kThreads), 0, st, j);
+  else if (j.dt == VS_F32)
+    hipLaunchKernelGGL((k_full_hist<float, false>), dim3(grid), dim3(kThreads), 0, st, j);
+  else if (j.topp_reject)
+    hipLaunchKernelGGL((k_full_hist<uint16_t, true>), dim3(grid), dim3(kThreads), 0, st, j);
   else
-    hipLaunchKernelGGL(k_full_hist<uint16_t>, dim3(grid), dim3(kThreads), 0, st, j);
+    hipLaunchKernelGGL((k_full_hist<uint16_t, false>), dim3(grid), dim3(kThreads), 0, st, j);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (j.dt == VS_F32)

@@ -910,6 +910,86 @@ __device__ bool block_cut_from_list(const FullCut& fc, int n, uint64_t lo, uint6
   return true;
 }
 
+constexpr int kRejectThreads = 1024;
+static_assert(2 * kRejectThreads >= (VS_MAX_V / kFullSegMin) * kCandM, "two candidates per thread");
+
+// The rejection draw of a full-vocabulary top-p row whose cut (tau, id_cut,
+// kept) is in *d: of the row's kCandM best Gumbel candidates (the union of its
+// histogram segments' best kCandM holds them), taken in the order (score
+// desc, id asc), the first that lies inside the cut is the Gumbel-max draw
+// over the kept set: every id that scores higher is one of the candidates
+// taken before it, all outside the cut. The row's outputs are then written
+// and the row is done; when none of the kCandM lies inside the cut, the row is
+// left to the Gumbel pass over its kept set. One workgroup per row, after the
+// cut kernel (rows that are not full-vocabulary top-p rows return at once).
+template <typename E>
+__global__ __launch_bounds__(kRejectThreads) void k_topp_reject(Job j) {
+  __shared__ double rd[kRejectThreads / kWave];
+  __shared__ int32_t ri[kRejectThreads / kWave];
+  __shared__ uint32_t s_key;
+  const int row = blockIdx.x;
+  RowDesc* d = j.desc + row;
+  if (d->mode != kRowFullTopP) return;  // uniform over the block
+  const uint32_t tau = d->tau;
+  const int32_t idc = d->id_cut;
+  const int32_t kept = d->kept;
+  const GCand* cand = j.fcand + static_cast<size_t>(row) * j.ntile3 * kCandM;
+  const int n = j.fseg * kCandM;
+  // this thread's candidates: slots t, t + blockDim.x (n <= 2 blockDim.x:
+  // at most 2048 for 2^21 ids of 4096-id segments; fewer segments than
+  // compute units otherwise)
+  const int t = static_cast<int>(threadIdx.x);
+  const int t2 = t + static_cast<int>(blockDim.x);
+  double as = -1.0, bsc = -1.0;
+  int32_t ai = 0x7fffffff, bi2 = 0x7fffffff;
+  uint32_t ak = 0u, bk = 0u;
+  if (t < n) {
+    const GCand g = cand[t];
+    as = g.score;
+    ai = g.id;
+    ak = g.key;
+  }
+  if (t2 < n) {
+    const GCand g = cand[t2];
+    bsc = g.score;
+    bi2 = g.id;
+    bk = g.key;
+  }
+  for (int r = 0; r < kCandM; ++r) {
+    // this thread's best remaining candidate
+    const bool first = as > bsc || (as == bsc && ai < bi2);
+    const double hs = first ? as : bsc;
+    const int32_t hi = first ? ai : bi2;
+    const uint32_t hk = first ? ak : bk;
+    const double bs = block_max(hs, rd);
+    if (bs < 0.0) return;  // uniform: no candidate left (the Gumbel pass draws)
+    const int bi = block_min(hs == bs ? hi : 0x7fffffff, ri);
+    const bool mine = hs == bs && hi == bi;
+    if (mine) s_key = hk;
+    __syncthreads();
+    const uint32_t key = s_key;
+    __syncthreads();
+    if (key > tau || (key == tau && bi <= idc)) {  // uniform: inside the cut
+      if (threadIdx.x == 0) {
+        j.out_ids[row] = bi;
+        if (j.out_kept) j.out_kept[row] = kept;
+        if (j.tok_sampled) {
+          const float2 ml = j.rlse[row];
+          j.out_tok_lp[row] = (logit_at<E>(j, row, bi) - ml.x) - ml.y;
+        }
+        d->mode = kRowDone;
+      }
+      return;
+    }
+    if (mine) {  // taken: outside the cut
+      if (first)
+        as = -1.0;
+      else
+        bsc = -1.0;
+    }
+  }
+}
+
 template <typename E>
 __global__ __launch_bounds__(kFullThreads) void k_row_full(Job j) {
   __shared__ FullSh sh;
@@ -981,6 +1061,12 @@ hipError_t launch_row_full(const Job& j, hipStream_t st) {
     hipLaunchKernelGGL(k_row_full<float>, dim3(j.B), dim3(kFullThreads), 0, st, j);
   else
     hipLaunchKernelGGL(k_row_full<uint16_t>, dim3(j.B), dim3(kFullThreads), 0, st, j);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !j.topp_reject) return e;
+  if (j.dt == VS_F32)
+    hipLaunchKernelGGL(k_topp_reject<float>, dim3(j.B), dim3(kRejectThreads), 0, st, j);
+  else
+    hipLaunchKernelGGL(k_topp_reject<uint16_t>, dim3(j.B), dim3(kRejectThreads), 0, st, j);
   return hipGetLastError();
 }
 

@@ -59,6 +59,8 @@ WsLayout ws_layout(int B, int V, int nslot) {
   off = align_up(off + static_cast<size_t>(B) * sizeof(uint32_t));
   L.fcut = off;
   off = align_up(off + static_cast<size_t>(B) * sizeof(FullCut));
+  L.fcand = off;  // a histogram segment is at least one Gumbel tile long
+  off = align_up(off + static_cast<size_t>(B) * L.ntile3 * kCandM * sizeof(GCand));
   L.total = off;
   return L;
 }
@@ -115,6 +117,7 @@ Job make_job(const void* logits, vs_dtype dt, int B, int V, int64_t ld, void* ws
   j.flist = reinterpret_cast<uint64_t*>(w + L.flist);
   j.fcnt = reinterpret_cast<uint32_t*>(w + L.fcnt);
   j.fcut = reinterpret_cast<FullCut*>(w + L.fcut);
+  j.fcand = reinterpret_cast<GCand*>(w + L.fcand);
   // Gumbel pass of full-vocabulary rows: up to 8 tiles per workgroup (the
   // pruning bound tightens along them) while the grid keeps about 1024
   // workgroups (four waves per SIMD to hide the loads' latency).
@@ -296,7 +299,8 @@ vs_status sample_logprobs_impl(const PenArgs* pen, const void* logits, vs_dtype 
                                int64_t ld_out, void* ws, size_t ws_bytes, int nslot,
                                hipStream_t stream) {
   if (!logits || !out_ids || !ws || !sizes_ok(dt, B, V, ld)) return VS_ERR_INVALID_ARGUMENT;
-  if (hints & ~(VS_HINT_NO_FULLVOCAB | VS_HINT_ALL_GREEDY | VS_HINT_SMALL_TOPK))
+  if (hints & ~(VS_HINT_NO_FULLVOCAB | VS_HINT_ALL_GREEDY | VS_HINT_SMALL_TOPK |
+                VS_OPT_TOPP_REJECTION))
     return VS_ERR_INVALID_ARGUMENT;
   if (k < 0 || k > VS_LOGPROB_K_MAX || k > V) return VS_ERR_INVALID_ARGUMENT;
   if (k > 0 && (!out_topk_ids || !out_topk_logprobs)) return VS_ERR_INVALID_ARGUMENT;
@@ -319,6 +323,9 @@ vs_status sample_logprobs_impl(const PenArgs* pen, const void* logits, vs_dtype 
     j.out_pen_status = pen->out_status;
   }
   j.sample = 1;
+  // full-vocabulary top-p rows draw by rejection when the caller chooses it
+  // and asks for no kept mask (the Gumbel pass over the kept set writes that)
+  j.topp_reject = ((hints & VS_OPT_TOPP_REJECTION) && !out_kept_mask) ? 1 : 0;
   j.T = temperature;
   j.k = top_k;
   j.p = top_p;

@@ -23,6 +23,7 @@ constexpr int kFullBuckets = 4096;
 constexpr float kFullPerUnit = 128.0f;
 constexpr int kFullListCap = 8192;
 constexpr int kFullSegMin = 4096;  // ids per segment of the histogram and gather passes, at least
+static_assert(kFullSegMin >= kGumTile, "a histogram segment spans at least one Gumbel tile");
 
 // Segment meta word (a segment is the run of tiles of one row that one
 // streaming-pass workgroup reads).
@@ -62,8 +63,14 @@ struct FullCut {
 struct FullTerms {
   float m, mp;
   __device__ __forceinline__ bool mass(float s, uint64_t* w, int* bucket) const {
+    float e;
+    return mass_e(s, w, bucket, &e);
+  }
+  // the same, with e = E(s - m) itself
+  __device__ __forceinline__ bool mass_e(float s, uint64_t* w, int* bucket, float* e_out) const {
     const float t = s - m;
     const float e = pinned_exp(t);
+    *e_out = e;
     if (!(e >= mp)) return false;
     const uint64_t W = mass_of(e);
     if (W == 0) return false;
@@ -75,6 +82,17 @@ struct FullTerms {
     const int b = static_cast<int>(-t * kFullPerUnit);
     return b < kFullBuckets - 1 ? b : kFullBuckets - 1;
   }
+};
+
+// The rejection draw of full-vocabulary top-p rows: each histogram workgroup
+// keeps the kCandM best Gumbel scores of its segment's candidates (every id of
+// positive mass that passes min-p), and once the cut is known the first of
+// the row's kCandM best that lies inside it is the draw.
+constexpr int kCandM = 4;
+struct GCand {
+  double score;  // e / -log(u); negative: no candidate
+  int32_t id;
+  uint32_t key;  // ordered key of s = x / T
 };
 
 struct Job {
@@ -124,6 +142,8 @@ struct Job {
   uint64_t* flist;     // [B][kFullListCap] packed (key, id) of the cut bucket
   uint32_t* fcnt;      // [B] entries appended to flist (may exceed the capacity)
   FullCut* fcut;       // [B] the cut bucket and the mass needed inside it
+  GCand* fcand;        // [B][ntile3][kCandM]: each histogram segment's best candidates
+  int topp_reject;     // full-vocabulary top-p rows draw by rejection (no kept mask asked for)
   int fseg;            // segments per row of the histogram and gather passes
   int fseg_len;        // ids per segment (a multiple of 8)
   int full_in_select;      // the streaming pass writes out_full itself (it finishes every row)
@@ -188,7 +208,8 @@ __device__ __forceinline__ float lse_scaled(float x, float T) { return T == 1.0f
 
 struct WsLayout {
   int ntile, ntile3;
-  size_t meta, candA, candB, kthA, kthB, desc, gpart, lpart, rlse, fhw, flist, fcnt, fcut, total;
+  size_t meta, candA, candB, kthA, kthB, desc, gpart, lpart, rlse, fhw, flist, fcnt, fcut, fcand,
+      total;
 };
 // The workspace layout for B rows of V ids with nslot segment slots per row
 // (the streaming pass uses min(nslot, its segment count) of them per row).

@@ -70,6 +70,16 @@ typedef enum vs_status {
 #define VS_HINT_ALL_GREEDY 2u     /* every row is greedy */
 #define VS_HINT_SMALL_TOPK 4u     /* every row is greedy or has 1 < top_k <= 64 (and
                                      top_k < V): no full-vocabulary row, no larger top-k */
+/* Not a promise but a choice of method, passed in the same word: full-vocabulary
+ * top-p rows draw by rejection. The histogram pass of the top-p cut also keeps
+ * each segment's best Gumbel candidates over all ids that pass min-p; once the
+ * cut is known, the first of the row's best candidates (score order) that lies
+ * inside it is the draw (every higher score belongs to a candidate outside it),
+ * with no pass over the kept set; a row whose best candidates all lie outside
+ * falls back to that pass. Results are identical; it is off by default because
+ * it measured slower on the benchmark workloads. Ignored when a kept mask is
+ * asked for. */
+#define VS_OPT_TOPP_REJECTION 256u
 
 #define VS_MAX_V (1 << 21)        /* largest vocabulary */
 #define VS_TOPK_MAX 1024          /* largest top_k below V */

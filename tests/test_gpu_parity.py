@@ -63,6 +63,28 @@ def test_sample_grid(V, dtype, seed):
     assert compare_sample(g, o) <= 1
 
 
+@pytest.mark.parametrize("seed", range(2))
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [100, 4097, 32000, 70001, 151936, 262144])
+def test_topp_rejection_draw(V, dtype, seed):
+    """The rejection draw of full-vocabulary top-p rows (VS_OPT_TOPP_REJECTION,
+    no kept mask): ids, kept counts and status equal the oracle's and the
+    default path's (the Gumbel pass over the kept set), on rows of every mode;
+    the top-p rows cover tight and loose cuts (p from 0.05 to 0.999) with
+    min-p, ties, flat rows and masked ids."""
+    import decode_token_sampling_amd as vs
+    B = 27
+    x = _row_shapes(3100 + V + 31 * seed, B, V, dtype)
+    w = random_params(np.random.default_rng(V + 7 * seed), B, V,
+                      kinds=["topp", "topp_minp", "topp", "greedy", "kfast", "none", "minp"])
+    xd = to_device(x)
+    a = gpu_sample(xd, V, w, hints=vs.OPT_TOPP_REJECTION, mask=False)
+    b = gpu_sample(xd, V, w, hints=0, mask=False)
+    for key in ("ids", "kept", "status"):
+        assert np.array_equal(a[key], b[key]), key
+    assert compare_sample(a, oracle_sample(x, V, w, mask=False)) <= 1
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_sample_padded_and_unaligned_rows(dtype):
     V = 5000
