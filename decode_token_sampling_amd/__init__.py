@@ -28,7 +28,10 @@ __all__ = [
     "NOALLOC_SCRATCH_BYTES", "penalize_sample_logprobs",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvs.so")
+# the in-tree build; VS_LIBRARY names another build of the same library (a
+# host-sanitised one, say)
+LIB_PATH = os.environ.get("VS_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                        "libvs.so")
 
 ROW_BAD_PARAM = 1
 ROW_BAD_LOGITS = 2

@@ -57,6 +57,37 @@ def _link(objs, lib: str) -> None:
     os.replace(tmp, lib)
 
 
+# Host code under AddressSanitizer and UndefinedBehaviorSanitizer (the device
+# code is built as usual; the flags apply to the host pass only). Load the
+# result with clang's ASan runtime preloaded.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_host_sanitized(out_dir: str) -> str:
+    """libvs.so with sanitised host code, written to ``out_dir`` (the in-tree
+    library is left alone)."""
+    os.makedirs(out_dir, exist_ok=True)
+
+    def one(src):
+        obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+        flags = [f for f in FLAGS if f != "-O3"] + ["-O1", "-g", *HOST_SANITIZE]
+        r = subprocess.run(["hipcc", *flags, "-c", os.path.join(CSRC, src), "-o", obj],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(one, SOURCES))
+    lib = os.path.join(out_dir, "libvs.so")
+    r = subprocess.run(["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC",
+                        *HOST_SANITIZE[:4], *objs, "-o", lib], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    return lib
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = SOURCES + SELFTEST_SOURCES

@@ -33,7 +33,7 @@ __global__ __launch_bounds__(kThreads) void k_penalize(
 
 }  // namespace
 
-hipError_t launch_penalize(void* logits, vs_dtype dt, int B, int V, int64_t ld,
+hipError_t launch_penalize(void* logits, int dt, int B, int V, int64_t ld,
                            const int32_t* prompt_ids, const int32_t* prompt_off,
                            const int32_t* output_ids, const int32_t* output_off,
                            const float* presence, const float* frequency,

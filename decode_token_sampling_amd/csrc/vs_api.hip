@@ -1,6 +1,7 @@
 // C ABI of libvs.so: argument checks, workspace layout, kernel sequence.
 #include <stdint.h>
 
+#include <cstring>
 #include <mutex>
 
 #include "vs_device.h"
@@ -77,7 +78,7 @@ int stream_segments(int B, int V) {
 
 // nslot: the workspace's segment slots per row (ws_slots_any(V) for a
 // caller's workspace, the device's segment count for the library's scratch).
-Job make_job(const void* logits, vs_dtype dt, int B, int V, int64_t ld, void* ws, int nslot) {
+Job make_job(const void* logits, int dt, int B, int V, int64_t ld, void* ws, int nslot) {
   const WsLayout L = ws_layout(B, V, nslot);
   char* w = static_cast<char*>(ws);
   Job j{};
@@ -172,7 +173,18 @@ int full_vec(const float* out_full, int64_t ld_out) {
   return (out_full && reinterpret_cast<uintptr_t>(out_full) % 16 == 0 && ld_out % 4 == 0) ? 1 : 0;
 }
 
-bool sizes_ok(vs_dtype dt, int B, int V, int64_t ld) {
+// The integer a caller passed in an enum parameter, read without loading a
+// value of the enum type (a C caller may pass any int there; loading one
+// outside the enumerators' range as the enum would be undefined in C++).
+template <typename Enum>
+int raw(const Enum* p) {
+  static_assert(sizeof(Enum) == sizeof(int), "the C enums are passed as int");
+  int v;
+  std::memcpy(&v, p, sizeof v);
+  return v;
+}
+
+bool sizes_ok(int dt, int B, int V, int64_t ld) {
   return (dt == VS_F32 || dt == VS_BF16) && B > 0 && V > 0 && V <= VS_MAX_V && ld >= V;
 }
 
@@ -189,13 +201,13 @@ void widen_for_full_write(vsk::Job& j) {
 extern "C" {
 
 vs_status vs_workspace_size(int B, int V, vs_dtype dt, size_t* bytes) {
-  if (!bytes || !sizes_ok(dt, B, V, V)) return VS_ERR_INVALID_ARGUMENT;
+  if (!bytes || !sizes_ok(raw(&dt), B, V, V)) return VS_ERR_INVALID_ARGUMENT;
   *bytes = vsk::ws_layout(B, V, vsk::ws_slots_any(V)).total;
   return VS_OK;
 }
 
 const char* vs_status_string(vs_status s) {
-  switch (s) {
+  switch (raw(&s)) {
     case VS_OK: return "ok";
     case VS_ERR_INVALID_ARGUMENT: return "invalid argument";
     case VS_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
@@ -205,12 +217,15 @@ const char* vs_status_string(vs_status s) {
   return "unknown status";
 }
 
-vs_status vs_penalize_ex(void* logits, vs_dtype dt, int B, int V, int64_t ld,
-                         const int32_t* prompt_ids, const int32_t* prompt_off,
-                         const int32_t* output_ids, const int32_t* output_off,
-                         const float* presence, const float* frequency,
-                         const float* repetition, const int32_t* prompt_ignore_len,
-                         int32_t* out_row_status, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+vs_status penalize_impl(void* logits, int dt, int B, int V, int64_t ld,
+                        const int32_t* prompt_ids, const int32_t* prompt_off,
+                        const int32_t* output_ids, const int32_t* output_off,
+                        const float* presence, const float* frequency, const float* repetition,
+                        const int32_t* prompt_ignore_len, int32_t* out_row_status,
+                        hipStream_t stream) {
   if (!logits || !sizes_ok(dt, B, V, ld)) return VS_ERR_INVALID_ARGUMENT;
   if ((prompt_ids == nullptr) != (prompt_off == nullptr)) return VS_ERR_INVALID_ARGUMENT;
   if ((output_ids == nullptr) != (output_off == nullptr)) return VS_ERR_INVALID_ARGUMENT;
@@ -222,14 +237,28 @@ vs_status vs_penalize_ex(void* logits, vs_dtype dt, int B, int V, int64_t ld,
   return e == hipSuccess ? VS_OK : VS_ERR_HIP;
 }
 
+}  // namespace
+
+extern "C" {
+
+vs_status vs_penalize_ex(void* logits, vs_dtype dt, int B, int V, int64_t ld,
+                         const int32_t* prompt_ids, const int32_t* prompt_off,
+                         const int32_t* output_ids, const int32_t* output_off,
+                         const float* presence, const float* frequency,
+                         const float* repetition, const int32_t* prompt_ignore_len,
+                         int32_t* out_row_status, hipStream_t stream) {
+  return penalize_impl(logits, raw(&dt), B, V, ld, prompt_ids, prompt_off, output_ids, output_off,
+                       presence, frequency, repetition, prompt_ignore_len, out_row_status, stream);
+}
+
 vs_status vs_penalize(void* logits, vs_dtype dt, int B, int V, int64_t ld,
                       const int32_t* prompt_ids, const int32_t* prompt_off,
                       const int32_t* output_ids, const int32_t* output_off,
                       const float* presence, const float* frequency,
                       const float* repetition, int32_t* out_row_status,
                       hipStream_t stream) {
-  return vs_penalize_ex(logits, dt, B, V, ld, prompt_ids, prompt_off, output_ids, output_off,
-                        presence, frequency, repetition, nullptr, out_row_status, stream);
+  return penalize_impl(logits, raw(&dt), B, V, ld, prompt_ids, prompt_off, output_ids, output_off,
+                       presence, frequency, repetition, nullptr, out_row_status, stream);
 }
 
 vs_status vs_topp_decay(int B, float* top_p, const float* top_p_init, const float* decay,
@@ -262,17 +291,6 @@ vs_status vs_seed_advance(int B, uint64_t* seeds, const int32_t* sampled_ids, hi
   return e == hipSuccess ? VS_OK : VS_ERR_HIP;
 }
 
-vs_status vs_sample(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
-                    const float* temperature, const int32_t* top_k,
-                    const float* top_p, const float* min_p,
-                    const uint64_t* seeds, uint32_t hints, int32_t* out_ids,
-                    int32_t* out_kept_count, uint32_t* out_kept_mask,
-                    int32_t* out_row_status, void* ws, size_t ws_bytes,
-                    hipStream_t stream) {
-  return vs_sample_logprobs(logits, dt, B, V, ld, temperature, top_k, top_p, min_p, seeds, hints,
-                            out_ids, out_kept_count, out_kept_mask, out_row_status, nullptr, 0,
-                            nullptr, nullptr, nullptr, 0, ws, ws_bytes, stream);
-}
 
 }  // extern "C"
 
@@ -288,7 +306,7 @@ struct PenArgs {
 
 // vs_sample_logprobs on a workspace laid out with nslot segment slots per
 // row; with pen, the streaming pass first applies those penalties in place.
-vs_status sample_logprobs_impl(const PenArgs* pen, const void* logits, vs_dtype dt, int B, int V,
+vs_status sample_logprobs_impl(const PenArgs* pen, const void* logits, int dt, int B, int V,
                                int64_t ld,
                                const float* temperature, const int32_t* top_k,
                                const float* top_p, const float* min_p,
@@ -373,106 +391,11 @@ vs_status sample_logprobs_impl(const PenArgs* pen, const void* logits, vs_dtype 
   return VS_OK;
 }
 
-// The library's own scratch for vs_sample_logprobs_noalloc: one array per
-// device (each device that loads the library's code holds its own copy until
-// the process ends). Host code never uses the array's name as an address: the
-// device address comes from hipGetSymbolAddress, once per device.
-static __device__ __align__(256) unsigned char scratch[VS_NOALLOC_SCRATCH_BYTES];
-
-constexpr int kMaxScratchDevices = 64;
-std::mutex g_scratch_mu;
-void* g_scratch_ptr[kMaxScratchDevices] = {};
-
-// The current device's scratch address (NULL if it cannot be had).
-void* scratch_ptr() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
-  void* p = __atomic_load_n(&g_scratch_ptr[dev], __ATOMIC_ACQUIRE);
-  if (p) return p;
-  std::lock_guard<std::mutex> lock(g_scratch_mu);
-  p = g_scratch_ptr[dev];
-  if (!p) {
-    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
-    __atomic_store_n(&g_scratch_ptr[dev], p, __ATOMIC_RELEASE);
-  }
-  return p;
-}
-
-}  // namespace
-
-extern "C" {
-
-vs_status vs_sample_logprobs(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
-                             const float* temperature, const int32_t* top_k,
-                             const float* top_p, const float* min_p,
-                             const uint64_t* seeds, uint32_t hints, int32_t* out_ids,
-                             int32_t* out_kept_count, uint32_t* out_kept_mask,
-                             int32_t* out_row_status, float* out_token_logprob, int k,
-                             int32_t* out_topk_ids, float* out_topk_logprobs, float* out_full,
-                             int64_t ld_out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  return sample_logprobs_impl(nullptr, logits, dt, B, V, ld, temperature, top_k, top_p, min_p,
-                              seeds, hints, out_ids, out_kept_count, out_kept_mask, out_row_status,
-                              out_token_logprob, k, out_topk_ids, out_topk_logprobs, out_full,
-                              ld_out, ws, ws_bytes, vsk::ws_slots_any(V), stream);
-}
-
-vs_status vs_sample_logprobs_noalloc(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
-                                     const float* temperature, const int32_t* top_k,
-                                     const float* top_p, const float* min_p,
-                                     const uint64_t* seeds, uint32_t hints, int32_t* out_ids,
-                                     int32_t* out_kept_count, uint32_t* out_kept_mask,
-                                     int32_t* out_row_status, float* out_token_logprob, int k,
-                                     int32_t* out_topk_ids, float* out_topk_logprobs,
-                                     float* out_full, int64_t ld_out, hipStream_t stream) {
-  if (!logits || !out_ids || !sizes_ok(dt, B, V, ld)) return VS_ERR_INVALID_ARGUMENT;
-  // laid out for the segments this device's streaming pass uses, not for every device
-  const int nslot = vsk::stream_segments(B, V);
-  if (vsk::ws_layout(B, V, nslot).total > VS_NOALLOC_SCRATCH_BYTES) return VS_ERR_WORKSPACE_TOO_SMALL;
-  void* ws = scratch_ptr();
-  if (!ws) return VS_ERR_HIP;
-  return sample_logprobs_impl(nullptr, logits, dt, B, V, ld, temperature, top_k, top_p, min_p,
-                              seeds, hints, out_ids, out_kept_count, out_kept_mask, out_row_status,
-                              out_token_logprob, k, out_topk_ids, out_topk_logprobs, out_full,
-                              ld_out, ws, VS_NOALLOC_SCRATCH_BYTES, nslot, stream);
-}
-
-vs_status vs_penalize_sample_logprobs(void* logits, vs_dtype dt, int B, int V, int64_t ld,
-                                      const int32_t* prompt_ids, const int32_t* prompt_off,
-                                      const int32_t* output_ids, const int32_t* output_off,
-                                      const float* presence, const float* frequency,
-                                      const float* repetition, const int32_t* prompt_ignore_len,
-                                      int32_t* out_penalty_status, const float* temperature,
-                                      const int32_t* top_k, const float* top_p,
-                                      const float* min_p, const uint64_t* seeds, uint32_t hints,
-                                      int32_t* out_ids, int32_t* out_kept_count,
-                                      uint32_t* out_kept_mask, int32_t* out_row_status,
-                                      float* out_token_logprob, int k, int32_t* out_topk_ids,
-                                      float* out_topk_logprobs, float* out_full, int64_t ld_out,
-                                      void* ws, size_t ws_bytes, hipStream_t stream) {
-  const PenArgs pen{prompt_ids, prompt_off, output_ids, output_off, presence,
-                    frequency,  repetition, prompt_ignore_len, out_penalty_status};
-  return sample_logprobs_impl(&pen, logits, dt, B, V, ld, temperature, top_k, top_p, min_p, seeds,
-                              hints, out_ids, out_kept_count, out_kept_mask, out_row_status,
-                              out_token_logprob, k, out_topk_ids, out_topk_logprobs, out_full,
-                              ld_out, ws, ws_bytes, vsk::ws_slots_any(V), stream);
-}
-
-vs_status vs_logprobs(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
-                      const int32_t* token_ids, float* out_token_logprob, int k,
-                      int32_t* out_topk_ids, float* out_topk_logprobs,
-                      float* out_full, int64_t ld_out, int32_t* out_row_status,
-                      void* ws, size_t ws_bytes, hipStream_t stream) {
-  return vs_logprobs_ex(logits, dt, B, V, ld, nullptr, token_ids, out_token_logprob, k,
-                        out_topk_ids, out_topk_logprobs, out_full, ld_out, out_row_status, ws,
-                        ws_bytes, stream);
-}
-
-vs_status vs_logprobs_ex(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
-                         const float* temperature, const int32_t* token_ids,
-                         float* out_token_logprob, int k, int32_t* out_topk_ids,
-                         float* out_topk_logprobs, float* out_full, int64_t ld_out,
-                         int32_t* out_row_status, void* ws, size_t ws_bytes,
-                         hipStream_t stream) {
+vs_status logprobs_impl(const void* logits, int dt, int B, int V, int64_t ld,
+                        const float* temperature, const int32_t* token_ids,
+                        float* out_token_logprob, int k, int32_t* out_topk_ids,
+                        float* out_topk_logprobs, float* out_full, int64_t ld_out,
+                        int32_t* out_row_status, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!logits || !ws || !sizes_ok(dt, B, V, ld)) return VS_ERR_INVALID_ARGUMENT;
   if ((token_ids == nullptr) != (out_token_logprob == nullptr)) return VS_ERR_INVALID_ARGUMENT;
   if (k < 0 || k > VS_LOGPROB_K_MAX || k > V) return VS_ERR_INVALID_ARGUMENT;
@@ -505,6 +428,124 @@ vs_status vs_logprobs_ex(const void* logits, vs_dtype dt, int B, int V, int64_t 
       return VS_ERR_HIP;
   }
   return VS_OK;
+}
+
+// The library's own scratch for vs_sample_logprobs_noalloc: one array per
+// device (each device that loads the library's code holds its own copy until
+// the process ends). Host code never uses the array's name as an address: the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[VS_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The current device's scratch address (NULL if it cannot be had).
+void* scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  void* p = __atomic_load_n(&g_scratch_ptr[dev], __ATOMIC_ACQUIRE);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev];
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    __atomic_store_n(&g_scratch_ptr[dev], p, __ATOMIC_RELEASE);
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+vs_status vs_sample(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
+                    const float* temperature, const int32_t* top_k,
+                    const float* top_p, const float* min_p,
+                    const uint64_t* seeds, uint32_t hints, int32_t* out_ids,
+                    int32_t* out_kept_count, uint32_t* out_kept_mask,
+                    int32_t* out_row_status, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  return sample_logprobs_impl(nullptr, logits, raw(&dt), B, V, ld, temperature, top_k, top_p,
+                              min_p, seeds, hints, out_ids, out_kept_count, out_kept_mask,
+                              out_row_status, nullptr, 0, nullptr, nullptr, nullptr, 0, ws,
+                              ws_bytes, vsk::ws_slots_any(V), stream);
+}
+
+vs_status vs_sample_logprobs(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
+                             const float* temperature, const int32_t* top_k,
+                             const float* top_p, const float* min_p,
+                             const uint64_t* seeds, uint32_t hints, int32_t* out_ids,
+                             int32_t* out_kept_count, uint32_t* out_kept_mask,
+                             int32_t* out_row_status, float* out_token_logprob, int k,
+                             int32_t* out_topk_ids, float* out_topk_logprobs, float* out_full,
+                             int64_t ld_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return sample_logprobs_impl(nullptr, logits, raw(&dt), B, V, ld, temperature, top_k, top_p, min_p,
+                              seeds, hints, out_ids, out_kept_count, out_kept_mask, out_row_status,
+                              out_token_logprob, k, out_topk_ids, out_topk_logprobs, out_full,
+                              ld_out, ws, ws_bytes, vsk::ws_slots_any(V), stream);
+}
+
+vs_status vs_sample_logprobs_noalloc(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
+                                     const float* temperature, const int32_t* top_k,
+                                     const float* top_p, const float* min_p,
+                                     const uint64_t* seeds, uint32_t hints, int32_t* out_ids,
+                                     int32_t* out_kept_count, uint32_t* out_kept_mask,
+                                     int32_t* out_row_status, float* out_token_logprob, int k,
+                                     int32_t* out_topk_ids, float* out_topk_logprobs,
+                                     float* out_full, int64_t ld_out, hipStream_t stream) {
+  if (!logits || !out_ids || !sizes_ok(raw(&dt), B, V, ld)) return VS_ERR_INVALID_ARGUMENT;
+  // laid out for the segments this device's streaming pass uses, not for every device
+  const int nslot = vsk::stream_segments(B, V);
+  if (vsk::ws_layout(B, V, nslot).total > VS_NOALLOC_SCRATCH_BYTES) return VS_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = scratch_ptr();
+  if (!ws) return VS_ERR_HIP;
+  return sample_logprobs_impl(nullptr, logits, raw(&dt), B, V, ld, temperature, top_k, top_p, min_p,
+                              seeds, hints, out_ids, out_kept_count, out_kept_mask, out_row_status,
+                              out_token_logprob, k, out_topk_ids, out_topk_logprobs, out_full,
+                              ld_out, ws, VS_NOALLOC_SCRATCH_BYTES, nslot, stream);
+}
+
+vs_status vs_penalize_sample_logprobs(void* logits, vs_dtype dt, int B, int V, int64_t ld,
+                                      const int32_t* prompt_ids, const int32_t* prompt_off,
+                                      const int32_t* output_ids, const int32_t* output_off,
+                                      const float* presence, const float* frequency,
+                                      const float* repetition, const int32_t* prompt_ignore_len,
+                                      int32_t* out_penalty_status, const float* temperature,
+                                      const int32_t* top_k, const float* top_p,
+                                      const float* min_p, const uint64_t* seeds, uint32_t hints,
+                                      int32_t* out_ids, int32_t* out_kept_count,
+                                      uint32_t* out_kept_mask, int32_t* out_row_status,
+                                      float* out_token_logprob, int k, int32_t* out_topk_ids,
+                                      float* out_topk_logprobs, float* out_full, int64_t ld_out,
+                                      void* ws, size_t ws_bytes, hipStream_t stream) {
+  const PenArgs pen{prompt_ids, prompt_off, output_ids, output_off, presence,
+                    frequency,  repetition, prompt_ignore_len, out_penalty_status};
+  return sample_logprobs_impl(&pen, logits, raw(&dt), B, V, ld, temperature, top_k, top_p, min_p, seeds,
+                              hints, out_ids, out_kept_count, out_kept_mask, out_row_status,
+                              out_token_logprob, k, out_topk_ids, out_topk_logprobs, out_full,
+                              ld_out, ws, ws_bytes, vsk::ws_slots_any(V), stream);
+}
+
+vs_status vs_logprobs(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
+                      const int32_t* token_ids, float* out_token_logprob, int k,
+                      int32_t* out_topk_ids, float* out_topk_logprobs,
+                      float* out_full, int64_t ld_out, int32_t* out_row_status,
+                      void* ws, size_t ws_bytes, hipStream_t stream) {
+  return logprobs_impl(logits, raw(&dt), B, V, ld, nullptr, token_ids, out_token_logprob, k,
+                       out_topk_ids, out_topk_logprobs, out_full, ld_out, out_row_status, ws,
+                       ws_bytes, stream);
+}
+
+vs_status vs_logprobs_ex(const void* logits, vs_dtype dt, int B, int V, int64_t ld,
+                         const float* temperature, const int32_t* token_ids,
+                         float* out_token_logprob, int k, int32_t* out_topk_ids,
+                         float* out_topk_logprobs, float* out_full, int64_t ld_out,
+                         int32_t* out_row_status, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  return logprobs_impl(logits, raw(&dt), B, V, ld, temperature, token_ids, out_token_logprob, k,
+                       out_topk_ids, out_topk_logprobs, out_full, ld_out, out_row_status, ws,
+                       ws_bytes, stream);
 }
 
 vs_status vs_profile_begin(hipEvent_t* events, int capacity) {

@@ -231,7 +231,7 @@ hipError_t launch_topp_decay(int B, float* top_p, const float* top_p_init, const
 hipError_t launch_seed_advance(int B, uint64_t* seeds, const int32_t* sampled, hipStream_t st);
 hipError_t launch_slot_remap(int B, int B_src, const int32_t* remap, const void* src, void* dst,
                              int elem_bytes, int32_t* out_status, hipStream_t st);
-hipError_t launch_penalize(void* logits, vs_dtype dt, int B, int V, int64_t ld,
+hipError_t launch_penalize(void* logits, int dt, int B, int V, int64_t ld,
                            const int32_t* prompt_ids, const int32_t* prompt_off,
                            const int32_t* output_ids, const int32_t* output_off,
                            const float* presence, const float* frequency,

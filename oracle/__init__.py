@@ -26,17 +26,24 @@ ROW_BAD_TOKEN_ID = 4
 ROW_TOPK_UNSUPPORTED = 8
 
 
-def build(force: bool = True) -> str:
-    """Compile liboracle.so with g++ (no fast-math, no FP contraction)."""
-    if force or not os.path.exists(LIB_PATH):
+def build(force: bool = True, path: str | None = None, sanitize: bool = False) -> str:
+    """Compile liboracle.so with g++ (no fast-math, no FP contraction).
+
+    ``path``: where to write it (default: the library this module loads).
+    ``sanitize``: build with AddressSanitizer and UndefinedBehaviorSanitizer,
+    every report fatal (load it with gcc's libasan and libubsan preloaded)."""
+    path = path or LIB_PATH
+    if force or not os.path.exists(path):
+        san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+               "-g"] if sanitize else []
         cmd = [
             "g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fno-fast-math",
-            "-fPIC", "-shared", "-Wall", "-Wextra",
-            os.path.join(_HERE, "oracle.cpp"), "-o", LIB_PATH + ".tmp",
+            "-fPIC", "-shared", "-Wall", "-Wextra", *san,
+            os.path.join(_HERE, "oracle.cpp"), "-o", path + ".tmp",
         ]
         subprocess.run(cmd, check=True)
-        os.replace(LIB_PATH + ".tmp", LIB_PATH)
-    return LIB_PATH
+        os.replace(path + ".tmp", path)
+    return path
 
 
 def _configure(lib):
