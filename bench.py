@@ -50,12 +50,14 @@ ALL_WORKLOADS = ["w256x248320_f32", "w4x32000_f32", "w32x151936_bf16", "w1024x12
                  "w64x262144_bf16"]
 # Integer-multiply issue of the whole chip: 256 compute units x 4 SIMDs x 16
 # lanes per clock at quarter rate for 32-bit multiplies, 2.4 GHz.
-MUL32_PEAK = 256 * 4 * 16 * 2.4e9 / 4
-# One SplitMix64 word: two 64-bit products by constants, 3 quarter-rate
-# 32-bit multiply instructions each (v_mad_u64_u32 for the low halves, two
-# v_mul_lo_u32 for the cross terms).
-MUL32_PER_WORD = 6
-SPLITMIX_PEAK_WORDS = MUL32_PEAK / MUL32_PER_WORD
+# The vector ALUs' issue ceiling: 256 CUs x 4 SIMDs x 16 lanes per cycle x
+# 2.4 GHz (every VALU instruction at the non-packed fp32 rate, 32-bit integer
+# multiplies included), and one SplitMix64 word as the compiler builds it for
+# gfx950: 19 VALU instructions per lane (two 64-bit products by constants as
+# 2 v_mad_u64_u32 + 4 v_mul_lo_u32, and 13 adds, shifts and xors).
+VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+SPLITMIX_OPS_PER_WORD = 19
+SPLITMIX_PEAK_WORDS = VALU_LANE_OPS / SPLITMIX_OPS_PER_WORD
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {"select": "k_select.hip", "lse_select": "k_select.hip", "row": "k_row.hip",
                   "full_prep": "k_full.hip",
@@ -352,11 +354,25 @@ def full_vocab_words(wl, kept):
     return int(kept[full].astype(np.int64).sum())
 
 
+def topp_method(wl, hints):
+    """The method the library takes for full-vocabulary top-p rows without a
+    kept mask (the rule its header states)."""
+    import decode_token_sampling_amd as vs
+    if hints & vs.OPT_TOPP_REJECTION:
+        return "rejection"
+    if hints & vs.OPT_TOPP_GATHER_DRAW:
+        return "gather_draw"
+    if hints & vs.OPT_TOPP_KEPT_PASS:
+        return "kept_pass"
+    return "gather_draw" if wl.B * wl.V >= 1 << 23 else "kept_pass"
+
+
 def rooflines(wl, b: Bench, stage_avg, ms_per_step, kept, splitmix_rate):
     """The roofline of each kernel stage that ran: HBM-bound passes against
-    8 TB/s from their algorithmic bytes, the Gumbel pass against the chip's
-    integer-multiply rate from its random words."""
+    8 TB/s from their algorithmic bytes, the pass that forms the draw's random
+    words against the vector ALUs' issue ceiling for them."""
     out = {}
+    gather = topp_method(wl, b.hints) == "gather_draw"
     one_launch = set(stage_avg) == {"select"}
     for stage, ms in stage_avg.items():
         if stage == "select":
@@ -374,6 +390,17 @@ def rooflines(wl, b: Bench, stage_avg, ms_per_step, kept, splitmix_rate):
                           "unit": "GB/s", "frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                           "algorithmic_bytes_per_launch": by, "launch_ms": ms,
                           "traffic": load_traffic(wl.name, stage)}
+            if stage == "full_prep" and gather:  # the gather pass also forms the draw's words
+                words = full_vocab_words(wl, kept)
+                rate = words / (ms * 1e-3)
+                out[stage]["draw_words"] = {
+                    "bound": "alu", "achieved": rate / 1e12, "peak": SPLITMIX_PEAK_WORDS / 1e12,
+                    "unit": "T SplitMix64 words/s", "frac": rate / SPLITMIX_PEAK_WORDS,
+                    "words_per_launch": words,
+                    "measured_splitmix_stream_Twords": splitmix_rate / 1e12}
+        elif stage == "gumbel" and gather:  # finishing the rows: the list's kept ids
+            out[stage] = {"bound": "latency", "launch_ms": ms,
+                          "note": "the kept set's words were formed by the gather pass"}
         elif stage == "gumbel":
             words = full_vocab_words(wl, kept)
             rate = words / (ms * 1e-3)
@@ -427,10 +454,14 @@ def measure(vs, torch, dev, hip, st, wl, steps, warmup, eager, splitmix_rate):
             "stages_ms": {k: float(np.mean(v)) for k, v in sep_stages.items()}}
     full_topp = (~((wl.temperature == 0) | (wl.top_k == 1) | (wl.top_p == 0) | (wl.min_p == 1)) &
                  ((wl.top_k == 0) | (wl.top_k >= wl.V)) & (wl.top_p < 1)).any()
-    if full_topp:  # the other method for full-vocabulary top-p rows, timed beside
-        hr = b.hints | vs.OPT_TOPP_REJECTION
-        tr, _ = time_steps(torch, dev, hip, b, steps, hints=hr, eager=eager)
-        rec["topp_rejection"] = {"ms_per_step": tr / steps, "step": b.describe(hr)}
+    if full_topp:  # each method for full-vocabulary top-p rows, timed beside the default
+        rec["topp_methods"] = {}
+        for name, bit in (("rejection", vs.OPT_TOPP_REJECTION),
+                          ("gather_draw", vs.OPT_TOPP_GATHER_DRAW),
+                          ("kept_pass", vs.OPT_TOPP_KEPT_PASS)):
+            hr = b.hints | bit
+            tr, _ = time_steps(torch, dev, hip, b, steps, hints=hr, eager=eager)
+            rec["topp_methods"][name] = {"ms_per_step": tr / steps, "step": b.describe(hr)}
     if wl.name == HEADLINE and b.hints != 0:
         t0, _ = time_steps(torch, dev, hip, b, steps, hints=0, eager=eager)
         rec["no_hint"] = {"ms_per_step": t0 / steps, "step": b.describe(0),

@@ -17,6 +17,15 @@
 //    ids above are counted from their bucket alone, with no exponential.
 // The cut kernel then sorts the list and finds the exact cut; a bucket larger
 // than the list goes to its one-workgroup path.
+//
+// The gather pass also draws over the ids above the cut bucket, which are
+// all kept whatever the cut inside the bucket turns out to be: each
+// workgroup's best Gumbel score e / -log u over them (e and u exactly as the
+// Gumbel pass forms them, the same provable skips) goes to the row's
+// per-segment records, and the cut kernel, which scores the kept ids of the
+// list itself, takes the best of both as the draw. The row is then finished
+// without the Gumbel pass over its kept set (unless kept masks are asked for,
+// or the rejection draw is, or the list did not hold the whole bucket).
 #include <type_traits>
 
 #include "vs_device.h"
@@ -264,14 +273,16 @@ __global__ __launch_bounds__(kThreads) void k_full_hist(Job j) {
   }
 }
 
-template <typename E>
+template <typename E, bool kDraw>
 __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
   __shared__ uint64_t sw[kThreads / kWave];
   __shared__ uint32_t sc[kThreads / kWave];
+  __shared__ double sd[kThreads / kWave];
   __shared__ int s_bucket;
   __shared__ uint64_t s_above_w;
   __shared__ uint64_t sbuf[kGatherBuf];
   __shared__ uint32_t s_n, s_lim, s_base;
+  __shared__ uint64_t s_best;  // bits of the best score any thread has found
   int row, seg;
   if (!xcd_row_tile(blockIdx.x, j.B, j.fseg, &row, &seg)) return;  // uniform per block
   RowCfg c;
@@ -280,7 +291,10 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
   const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
   const int lo = seg * j.fseg_len;
   const int hi = min(j.V, lo + j.fseg_len);
-  SegReader<E, 4> rd;
+  // vectors in flight per thread (fewer with the draw, whose random words
+  // need the registers)
+  constexpr int kGU = kDraw ? 2 : 4;
+  SegReader<E, kGU> rd;
   rd.start(rowp, lo, hi, j.aligned != 0);
   const uint64_t* ghw = j.fhw + static_cast<size_t>(row) * kFullBuckets;
 
@@ -303,6 +317,7 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
     s_bucket = -1;
     s_n = 0u;
     s_lim = 0xffffffffu;
+    s_best = 0ull;
   }
   __syncthreads();
 #pragma unroll
@@ -334,18 +349,101 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
   uint64_t* lst = j.flist + static_cast<size_t>(row) * kFullListCap;
   uint32_t* cnt = j.fcnt + row;
   uint32_t n_above = 0, n_hit = 0;
-  constexpr int EPV = SegReader<E, 4>::EPV;
+  constexpr int EPV = SegReader<E, kGU>::EPV;
+
+  // The draw over the ids above the cut bucket (kDraw). A thread skips the
+  // logarithm and the division for an id that provably scores below the best
+  // score known in the workgroup (shared through LDS, where a stale value is
+  // only a looser bound): -log u > 1 - u for u < 1, so 1 - u >= e / best
+  // means e / -log u < best; an upper bound on e gives that test on the
+  // random word alone (an integer compare).
+  const uint64_t rs = row_stream(c.seed, row);
+  double best = -1.0;
+  int best_id = 0x7fffffff;
+  double lim = __builtin_inf();  // (1 + 2^-40) / (the best score known here)
+  float lim_up = __builtin_inff();  // a float at or above lim
+  const auto refresh = [&]() {
+    const uint64_t sb = __hip_atomic_load(&s_best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const double bd = __longlong_as_double(static_cast<long long>(sb));
+    if (bd > 0.0 && (1.0 + 0x1p-40) / bd < lim) {
+      lim = (1.0 + 0x1p-40) / bd;
+      lim_up = up_of(lim);
+    }
+  };
+  // the score of an above id whose random word b passed the integer test,
+  // unless a finer test shows it cannot beat the bound
+  const auto score = [&](int id, float sv, uint64_t b) {
+    const double u = uniform_of_bits(b);
+    const double one_u = (1.0 - u) * (1.0 - 0x1p-50);  // rounded down past any rounding error
+    if (one_u >= lim) return;                          // e <= 1: below the bound
+    const float e = pinned_exp(sv - m);
+    if (one_u >= lim * static_cast<double>(e)) return;  // below the bound
+    const double g = static_cast<double>(e) / -log(u);  // as the Gumbel pass scores it
+    if (g > best || (g == best && id < best_id)) {
+      best = g;
+      best_id = id;
+      atomicMax(reinterpret_cast<unsigned long long*>(&s_best),
+                static_cast<unsigned long long>(__double_as_longlong(g)));
+      refresh();
+    }
+  };
+  const auto above = [&](float sv) {
+    const float t = sv - m;
+    return t == t && FullTerms::bucket_of(t) < bstar;
+  };
+  if constexpr (kDraw) {
+    // one id per thread first (the first of its first vector, when above),
+    // so that the workgroup starts from the best of up to 1024 scores
+    if (static_cast<int>(threadIdx.x) < rd.nvec) {  // its first vector is in flight
+      float x[EPV];
+      unpack16(rd.raw[0], x, rowp);
+      const int id = lo + static_cast<int>(threadIdx.x) * EPV;
+      const float sv = c.T == 1.0f ? x[0] : x[0] / c.T;
+      if (above(sv)) score(id, sv, random_bits(rs, id));
+    }
+    __syncthreads();
+    refresh();
+  }
+
   auto pass = [&](auto div) {
     rd.visit([&](int id0, const float* x, int n) {
       float sv[EPV];
       uint32_t hm = 0;  // ids in the cut bucket (the bucket alone, no exponential)
+      uint32_t am = 0;  // ids above it
 #pragma unroll
       for (int q = 0; q < EPV; ++q) {
         sv[q] = scaled_by<decltype(div)::value>(x[q], c.T);
         const float t = sv[q] - m;
         const int b = (t == t && q < n) ? FullTerms::bucket_of(t) : kFullBuckets;
-        n_above += b < bstar ? 1u : 0u;
+        am |= b < bstar ? 1u << q : 0u;
         hm |= b == bstar ? 1u << q : 0u;
+      }
+      n_above += __popc(am);
+      if constexpr (kDraw) {
+        if (__ballot(am != 0u)) {  // uniform
+          refresh();
+          // the integer test for this vector, on the high halves of the
+          // random words, from an upper bound on its ids' e (the hardware
+          // exponential at the largest s, 2^-16 above any rounding of it;
+          // at most 1: every id here is at or below the maximum)
+          float vmax = sv[0];
+#pragma unroll
+          for (int q = 1; q < EPV; ++q) vmax = fmaxf(vmax, sv[q]);
+          const float veub = fminf(__builtin_amdgcn_exp2f((vmax - m) * 1.44269504088896340736f) *
+                                   (1.0f + 0x1p-16f), 1.0f);
+          const uint32_t vskip = skip_hi(lim_up, veub);
+          uint32_t need = 0;
+#pragma unroll
+          for (int q = 0; q < EPV; ++q)
+            need |= ((am >> q) & 1u) && random_hi(rs, id0 + q) >= vskip ? 1u << q : 0u;
+          // rare once a bound is known: each such id's value is read again
+          // (a cache hit) and its word formed again, so that one copy of the
+          // scoring code serves every position of the vector
+          for (uint32_t nb = need; nb != 0u; nb &= nb - 1u) {
+            const int id = id0 + __builtin_ctz(nb);
+            score(id, scaled_by<decltype(div)::value>(to_f32(rowp[id]), c.T), random_bits(rs, id));
+          }
+        }
       }
       if (__ballot(hm != 0u)) {  // uniform; few vectors hold cut-bucket ids
 #pragma unroll
@@ -385,6 +483,14 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
     pass(std::false_type{});
   else
     pass(std::true_type{});
+  if constexpr (kDraw) {
+    // the segment's best over its above ids (score desc, id asc) into the
+    // row's per-segment record (score -1: none)
+    const double bb = block_max(best, sd);
+    const int bid = block_min(best == bb ? best_id : 0x7fffffff, reinterpret_cast<int*>(sc));
+    if (threadIdx.x == 0)
+      j.gpart[static_cast<size_t>(row) * j.ntile3 + seg] = GPart{bb >= 0.0 ? bb : -1.0, bid, 0};
+  }
   // this workgroup's counts into the row's record (block_sum's barriers also
   // complete the LDS appends)
   n_above = block_sum(n_above, sc);
@@ -418,10 +524,14 @@ hipError_t launch_full_prep(const Job& j, hipStream_t st) {
     hipLaunchKernelGGL((k_full_hist<uint16_t, false>), dim3(grid), dim3(kThreads), 0, st, j);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (j.dt == VS_F32)
-    hipLaunchKernelGGL(k_full_gather<float>, dim3(grid), dim3(kThreads), 0, st, j);
+  if (j.dt == VS_F32 && j.fdraw)
+    hipLaunchKernelGGL((k_full_gather<float, true>), dim3(grid), dim3(kThreads), 0, st, j);
+  else if (j.dt == VS_F32)
+    hipLaunchKernelGGL((k_full_gather<float, false>), dim3(grid), dim3(kThreads), 0, st, j);
+  else if (j.fdraw)
+    hipLaunchKernelGGL((k_full_gather<uint16_t, true>), dim3(grid), dim3(kThreads), 0, st, j);
   else
-    hipLaunchKernelGGL(k_full_gather<uint16_t>, dim3(grid), dim3(kThreads), 0, st, j);
+    hipLaunchKernelGGL((k_full_gather<uint16_t, false>), dim3(grid), dim3(kThreads), 0, st, j);
   return hipGetLastError();
 }
 

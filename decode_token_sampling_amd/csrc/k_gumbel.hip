@@ -80,6 +80,7 @@ __global__ __launch_bounds__(kThreads) void k_gumbel_partial(Job j) {
   // until a score is known); skip: the random words that reach it for any e
   double lim = __builtin_inf();
   uint64_t skip = 0ull;
+  float lim_up = __builtin_inff();  // a float at or above lim
   int kept = 0;
 
   // the 16-byte vectors of a tile this thread reads, when the tile is whole
@@ -112,6 +113,7 @@ __global__ __launch_bounds__(kThreads) void k_gumbel_partial(Job j) {
       best_id = id;
       lim = fmin(lim, (1.0 + 0x1p-40) / best);
       skip = skip_below(lim);
+      lim_up = up_of(lim);
     }
   };
 
@@ -158,6 +160,7 @@ __global__ __launch_bounds__(kThreads) void k_gumbel_partial(Job j) {
     if (sbest > 0.0 && (1.0 + 0x1p-40) / sbest < lim) {
       lim = (1.0 + 0x1p-40) / sbest;
       skip = skip_below(lim);
+      lim_up = up_of(lim);
     }
   };
 
@@ -218,18 +221,24 @@ __global__ __launch_bounds__(kThreads) void k_gumbel_partial(Job j) {
         // EPV divides 32: the vector's ids share one mask word
         if (mask_row && km) atomicOr(&mask_row[j0 >> 5], km << (j0 & 31));
         if (__ballot(km != 0u)) {  // uniform: some lane keeps an id here
-          // every kept id's random word, then the integer bound test
-          uint64_t bw[EPV];
+          // the integer test for this vector, on the high halves of the
+          // random words, from an upper bound on its ids' e (the
+          // hardware-exponential bound of score at the vector's largest s,
+          // at most 1; tighter than e <= 1 wherever that is small)
+          float vmax = v[0];
+#pragma unroll
+          for (int c = 1; c < EPV; ++c) vmax = fmaxf(vmax, v[c]);
+          const float veub =
+              fminf(__builtin_amdgcn_exp2f((vmax - d.m) * kLog2E) * (1.0f + 0x1p-16f), 1.0f);
+          const uint32_t vskip = skip_hi(lim_up, veub);
           uint32_t need = 0;
 #pragma unroll
-          for (int c = 0; c < EPV; ++c) {
-            bw[c] = random_bits(rs, j0 + c);
-            need |= ((km >> c) & 1u) && bw[c] >= skip ? 1u << c : 0u;
-          }
-          if (__ballot(need != 0u)) {  // rare once a bound is known
+          for (int c = 0; c < EPV; ++c)
+            need |= ((km >> c) & 1u) && random_hi(rs, j0 + c) >= vskip ? 1u << c : 0u;
+          if (__ballot(need != 0u)) {  // rare once a bound is known (the words are formed again)
 #pragma unroll
             for (int c = 0; c < EPV; ++c)
-              if ((need >> c) & 1u) score(j0 + c, v[c], e[c], bw[c]);
+              if ((need >> c) & 1u) score(j0 + c, v[c], e[c], random_bits(rs, j0 + c));
           }
         }
       }
@@ -258,17 +267,72 @@ __global__ __launch_bounds__(kThreads) void k_gumbel_final(Job j) {
   __shared__ double sd[kThreads / kWave];
   __shared__ int si[kThreads / kWave];
   const int row = blockIdx.x;
-  if (!full_row(j.desc[row].mode)) return;
   const GPart* g = j.gpart + static_cast<size_t>(row) * j.ntile3;
+  const uint64_t* lst = j.flist + static_cast<size_t>(row) * kFullListCap;
+  // Every load the row may need is issued at once, before its mode is
+  // known: the descriptor, this thread's first record, the list's length and
+  // this thread's first list entries (all inside the row's slices).
+  constexpr int U = 4;  // list entries in flight per thread
+  static_assert(U * kThreads <= kFullListCap, "the first entries lie inside the list");
+  const RowDesc d = j.desc[row];
+  const int t0 = static_cast<int>(threadIdx.x);
+  const GPart p0 = t0 < j.ntile3 ? g[t0] : GPart{-1.0, 0x7fffffff, 0};
+  uint64_t v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) v[u] = lst[t0 + u * kThreads];
+  const uint32_t cnt = j.fcnt[row];
+  const bool listed = d.mode == kRowFullListed;
+  if (!full_row(d.mode) && !listed) return;  // uniform over the block
   double best = -1.0;
   int best_id = 0x7fffffff;
   int kept = 0;
-  for (int t = threadIdx.x; t < j.ntile3; t += blockDim.x) {
-    const GPart p = g[t];
-    kept += p.kept;
-    if (p.kept && (p.score > best || (p.score == best && p.id < best_id))) {
-      best = p.score;
-      best_id = p.id;
+  if (listed) {
+    // The gather pass's bests over the ids above the cut bucket (one record
+    // per segment), then the kept entries of the list: those at or above the
+    // cut entry in the packed order. An entry is skipped when it provably
+    // scores below the best so far (the integer test of the Gumbel pass, with
+    // e <= 1), else scored exactly as the Gumbel pass scores it.
+    for (int t = t0; t < j.fseg; t += blockDim.x) {
+      const GPart p = t == t0 ? p0 : g[t];
+      if (p.score >= 0.0 && (p.score > best || (p.score == best && p.id < best_id))) {
+        best = p.score;
+        best_id = p.id;
+      }
+    }
+    const uint64_t rs = row_stream(j.seeds ? j.seeds[row] : 0ull, row);
+    const double b0 = block_max(best, sd);
+    const double lim = b0 > 0.0 ? (1.0 + 0x1p-40) / b0 : __builtin_inf();
+    const uint64_t skip = skip_below(lim);
+    const uint64_t cutv = pack(d.tau, d.id_cut);
+    const int n = static_cast<int>(min(cnt, static_cast<uint32_t>(kFullListCap)));
+    for (int i0 = threadIdx.x; i0 < n; i0 += U * kThreads) {
+      if (i0 != static_cast<int>(threadIdx.x)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = i0 + u * kThreads < n ? lst[i0 + u * kThreads] : 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        // below the cut, or past the list (taken as 0, below every entry)
+        if (i0 + u * kThreads >= n || v[u] < cutv) continue;
+        const int id = pid(v[u]);
+        const uint64_t b = random_bits(rs, id);
+        if (b < skip) continue;  // e <= 1: below the bound
+        const double sc = gumbel_score(pinned_exp(key2f(pkey(v[u])) - d.m), rs, id);
+        if (sc > best || (sc == best && id < best_id)) {
+          best = sc;
+          best_id = id;
+        }
+      }
+    }
+    kept = threadIdx.x == 0 ? d.kept : 0;
+  } else {
+    for (int t = t0; t < j.ntile3; t += blockDim.x) {
+      const GPart p = t == t0 ? p0 : g[t];
+      kept += p.kept;
+      if (p.kept && (p.score > best || (p.score == best && p.id < best_id))) {
+        best = p.score;
+        best_id = p.id;
+      }
     }
   }
   const double bb = block_max(best, sd);

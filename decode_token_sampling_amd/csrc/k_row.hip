@@ -792,7 +792,7 @@ __device__ void full_topp_cut(const E* __restrict__ rowp, int V, bool aligned, c
 // masses fall short of the remainder (not expected: the list holds the whole
 // bucket). The result is the same in every thread.
 __device__ bool sort_cut_from_list(const FullCut& fc, int n, uint64_t v, uint32_t w, uint32_t* mw,
-                                   FullSh& sh, RowDesc* d) {
+                                   FullSh& sh, RowDesc* d, uint32_t mode) {
   const int t = static_cast<int>(threadIdx.x);
   // only the first P entries (P the power of two >= n) need sorting: every
   // entry past them is padding, and so is every sorted entry past n
@@ -828,7 +828,7 @@ __device__ bool sort_cut_from_list(const FullCut& fc, int n, uint64_t v, uint32_
   const int rank = block_sum(cum < fc.rem ? 1 : 0, sh.ri);  // the running mass is nondecreasing
   if (rank >= n) return false;  // uniform: the list's masses fall short of the remainder
   if (t == rank) {
-    d->mode = kRowFullTopP;
+    d->mode = mode;
     d->tau = pkey(v);
     d->id_cut = pid(v);
     d->kept = static_cast<int32_t>(fc.above_c) + rank + 1;
@@ -840,7 +840,7 @@ __device__ bool sort_cut_from_list(const FullCut& fc, int n, uint64_t v, uint32_
 // counting spread over every wave, at the price of a few barriers a round).
 // Called by every thread; the result is the same in every thread.
 __device__ bool block_cut_from_list(const FullCut& fc, int n, uint64_t lo, uint64_t hi,
-                                    const uint32_t* mw, FullSh& sh, RowDesc* d) {
+                                    const uint32_t* mw, FullSh& sh, RowDesc* d, uint32_t mode) {
   uint64_t rem = fc.rem;
   int rank = 0;
   uint64_t cutv = hi;
@@ -902,7 +902,7 @@ __device__ bool block_cut_from_list(const FullCut& fc, int n, uint64_t lo, uint6
     }
   }
   if (threadIdx.x == 0) {
-    d->mode = kRowFullTopP;
+    d->mode = mode;
     d->tau = pkey(cutv);
     d->id_cut = pid(cutv);
     d->kept = static_cast<int32_t>(fc.above_c) + rank + 1;
@@ -1008,6 +1008,9 @@ __global__ __launch_bounds__(kFullThreads) void k_row_full(Job j) {
                         got <= static_cast<uint32_t>(FullSh::kBufCap);  // uniform
     if (listed) {
       __shared__ uint32_t mw[kFullListCap];
+      // the draw then comes from the list and the gather pass's bests when
+      // the gather pass drew over the ids above the bucket
+      const uint32_t mode = j.fdraw ? kRowFullListed : kRowFullTopP;
       const int n = static_cast<int>(got);
       const uint64_t* lst = j.flist + static_cast<size_t>(row) * kFullListCap;
       const FullTerms ft{m, c.mp};
@@ -1020,7 +1023,7 @@ __global__ __launch_bounds__(kFullThreads) void k_row_full(Job j) {
           int b;
           w = ft.mass(key2f(pkey(v)), &wt, &b) ? static_cast<uint32_t>(wt) : 0u;
         }
-        if (sort_cut_from_list(fc, n, v, w, mw, sh, d)) return;  // uniform
+        if (sort_cut_from_list(fc, n, v, w, mw, sh, d, mode)) return;  // uniform
       } else {
         uint64_t lo = ~0ull, hi = 0ull;
         for (int i = threadIdx.x; i < n; i += blockDim.x) {
@@ -1035,7 +1038,7 @@ __global__ __launch_bounds__(kFullThreads) void k_row_full(Job j) {
         }
         lo = block_min(lo, sh.r64);  // (its barriers also publish buf and mw)
         hi = block_max(hi, sh.r64);
-        if (block_cut_from_list(fc, n, lo, hi, mw, sh, d)) return;  // uniform
+        if (block_cut_from_list(fc, n, lo, hi, mw, sh, d, mode)) return;  // uniform
       }
       __syncthreads();  // else (a list short of the remainder) the full path
     }

@@ -318,7 +318,7 @@ vs_status sample_logprobs_impl(const PenArgs* pen, const void* logits, int dt, i
                                hipStream_t stream) {
   if (!logits || !out_ids || !ws || !sizes_ok(dt, B, V, ld)) return VS_ERR_INVALID_ARGUMENT;
   if (hints & ~(VS_HINT_NO_FULLVOCAB | VS_HINT_ALL_GREEDY | VS_HINT_SMALL_TOPK |
-                VS_OPT_TOPP_REJECTION))
+                VS_OPT_TOPP_REJECTION | VS_OPT_TOPP_GATHER_DRAW | VS_OPT_TOPP_KEPT_PASS))
     return VS_ERR_INVALID_ARGUMENT;
   if (k < 0 || k > VS_LOGPROB_K_MAX || k > V) return VS_ERR_INVALID_ARGUMENT;
   if (k > 0 && (!out_topk_ids || !out_topk_logprobs)) return VS_ERR_INVALID_ARGUMENT;
@@ -344,6 +344,14 @@ vs_status sample_logprobs_impl(const PenArgs* pen, const void* logits, int dt, i
   // full-vocabulary top-p rows draw by rejection when the caller chooses it
   // and asks for no kept mask (the Gumbel pass over the kept set writes that)
   j.topp_reject = ((hints & VS_OPT_TOPP_REJECTION) && !out_kept_mask) ? 1 : 0;
+  // otherwise, without a kept mask, the gather pass and the last Gumbel
+  // kernel draw them (the Gumbel pass over the kept set only for rows whose
+  // cut bucket did not fit the list) when chosen, or by default for large
+  // batches
+  const bool gather_draw =
+      (hints & VS_OPT_TOPP_GATHER_DRAW) ||
+      (!(hints & VS_OPT_TOPP_KEPT_PASS) && static_cast<int64_t>(B) * V >= (int64_t{1} << 23));
+  j.fdraw = (!j.topp_reject && !out_kept_mask && gather_draw) ? 1 : 0;
   j.T = temperature;
   j.k = top_k;
   j.p = top_p;

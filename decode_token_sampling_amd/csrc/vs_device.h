@@ -174,6 +174,33 @@ __device__ __forceinline__ double uniform_of_bits(uint64_t b) {
 __device__ __forceinline__ double uniform_of(uint64_t row_state, int id) {
   return uniform_of_bits(random_bits(row_state, id));
 }
+// The high half of an id's random word (the compiler leaves out what only
+// the low half needs).
+__device__ __forceinline__ uint32_t random_hi(uint64_t row_state, int id) {
+  return static_cast<uint32_t>(random_bits(row_state, id) >> 32);
+}
+// The Gumbel draw's skip test on the high half of a random word. A kept id
+// with e <= eub and random word b cannot beat a best score S when
+// 1 - u >= (1 + 2^-40) e / S (-log u > 1 - u; the margin covers the
+// rounding of the scores); the integer form of that test takes the words
+// below (1 - L) 2^64 (up to a few units of 2^12), L = lim * eub with
+// lim = (1 + 2^-40) / S. skip_hi returns a bound H on the high half such that
+// b >> 32 < H implies that test, evaluated in fp32: lim_up is a float at or
+// above lim (up_of), the product is raised past its rounding, and 1 - L,
+// scaled by 2^32, is lowered by 256 units past the rounding of the
+// subtraction (NaN and L >= 1 give 0: nothing skipped).
+__device__ __forceinline__ float up_of(double lim) {
+  // float(lim) is within 2^-24 of lim; 2^-21 above it stays above lim after
+  // the product's own rounding (and is infinite past the float range)
+  return static_cast<float>(lim) * (1.0f + 0x1p-21f);
+}
+__device__ __forceinline__ uint32_t skip_hi(float lim_up, float eub) {
+  const float L = lim_up * eub;                  // >= lim * eub (1 + 2^-23)
+  const float t = (1.0f - L) * 4294967296.0f;    // within 2^7 of (1 - L) 2^32
+  const uint32_t h = t >= 4294967040.0f ? 4294967040u : (t > 256.0f ? static_cast<uint32_t>(t) : 256u);
+  return h - 256u;
+}
+
 // Gumbel-max score prob / q with q = -log(u) (exponential noise), in double.
 __device__ __forceinline__ double gumbel_score(float e, uint64_t row_state, int id) {
   const double q = -log(uniform_of(row_state, id));

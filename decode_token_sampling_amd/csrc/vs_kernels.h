@@ -42,6 +42,9 @@ enum : uint32_t {
   kRowFullMinP = 2,   // full vocabulary, min-p only
   kRowFullTopP = 3,   // full vocabulary, top-p cut given by (tau, id_cut)
   kRowFull = 4,       // full vocabulary, the cut still to be found (heavy kernel)
+  kRowFullListed = 5, // top-p cut (tau, id_cut) found in the row's list, whose kept entries
+                      // and the gather pass's bests over the ids above the list's bucket
+                      // hold the draw (no Gumbel pass over the kept set)
 };
 
 // The top-p cut of a full-vocabulary row, found from its mass histogram.
@@ -144,6 +147,7 @@ struct Job {
   FullCut* fcut;       // [B] the cut bucket and the mass needed inside it
   GCand* fcand;        // [B][ntile3][kCandM]: each histogram segment's best candidates
   int topp_reject;     // full-vocabulary top-p rows draw by rejection (no kept mask asked for)
+  int fdraw;           // else the gather pass and the cut kernel draw them (no kept mask asked for)
   int fseg;            // segments per row of the histogram and gather passes
   int fseg_len;        // ids per segment (a multiple of 8)
   int full_in_select;      // the streaming pass writes out_full itself (it finishes every row)

@@ -70,16 +70,26 @@ typedef enum vs_status {
 #define VS_HINT_ALL_GREEDY 2u     /* every row is greedy */
 #define VS_HINT_SMALL_TOPK 4u     /* every row is greedy or has 1 < top_k <= 64 (and
                                      top_k < V): no full-vocabulary row, no larger top-k */
-/* Not a promise but a choice of method, passed in the same word: full-vocabulary
- * top-p rows draw by rejection. The histogram pass of the top-p cut also keeps
- * each segment's best Gumbel candidates over all ids that pass min-p; once the
- * cut is known, the first of the row's best candidates (score order) that lies
- * inside it is the draw (every higher score belongs to a candidate outside it),
- * with no pass over the kept set; a row whose best candidates all lie outside
- * falls back to that pass. Results are identical; it is off by default because
- * it measured slower on the benchmark workloads. Ignored when a kept mask is
- * asked for. */
+/* Not promises but a choice of method for full-vocabulary top-p rows, passed in
+ * the same word; every method gives identical results, and all are ignored
+ * when a kept mask is asked for (the Gumbel pass over the kept set writes it).
+ *  VS_OPT_TOPP_REJECTION: draw by rejection. The histogram pass of the top-p
+ *    cut also keeps each segment's best Gumbel candidates over all ids that
+ *    pass min-p; once the cut is known, the first of the row's best candidates
+ *    (score order) that lies inside it is the draw (every higher score belongs
+ *    to a candidate outside it), with no pass over the kept set; a row whose
+ *    best candidates all lie outside falls back to that pass.
+ *  VS_OPT_TOPP_GATHER_DRAW: the pass that gathers the ids of the cut's bucket
+ *    also draws over the ids above that bucket (all kept, wherever the cut
+ *    falls inside it), and the draw's last step scores the kept ids of the
+ *    bucket; no pass over the kept set (unless the bucket overflowed its list).
+ *  VS_OPT_TOPP_KEPT_PASS: the Gumbel pass over the kept set after the cut.
+ * Without one of them (or with more than one: the first listed wins), the
+ * gather draw is taken when B * V >= 2^23 and the kept-set pass otherwise,
+ * the faster of the two on the measured workloads on each side. */
 #define VS_OPT_TOPP_REJECTION 256u
+#define VS_OPT_TOPP_GATHER_DRAW 512u
+#define VS_OPT_TOPP_KEPT_PASS 1024u
 
 #define VS_MAX_V (1 << 21)        /* largest vocabulary */
 #define VS_TOPK_MAX 1024          /* largest top_k below V */

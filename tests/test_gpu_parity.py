@@ -66,23 +66,28 @@ def test_sample_grid(V, dtype, seed):
 @pytest.mark.parametrize("seed", range(2))
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("V", [100, 4097, 32000, 70001, 151936, 262144])
-def test_topp_rejection_draw(V, dtype, seed):
-    """The rejection draw of full-vocabulary top-p rows (VS_OPT_TOPP_REJECTION,
-    no kept mask): ids, kept counts and status equal the oracle's and the
-    default path's (the Gumbel pass over the kept set), on rows of every mode;
-    the top-p rows cover tight and loose cuts (p from 0.05 to 0.999) with
-    min-p, ties, flat rows and masked ids."""
+def test_topp_draw_methods(V, dtype, seed):
+    """The three methods for full-vocabulary top-p rows without a kept mask
+    (rejection; the gather pass's draw over the ids above the cut bucket plus
+    the bucket's kept ids; the Gumbel pass over the kept set): ids, kept
+    counts and status equal the oracle's and each other's, on rows of every
+    mode; the top-p rows cover tight and loose cuts (p from 0.05 to 0.999)
+    with min-p, ties, flat rows and masked ids."""
     import decode_token_sampling_amd as vs
     B = 27
     x = _row_shapes(3100 + V + 31 * seed, B, V, dtype)
     w = random_params(np.random.default_rng(V + 7 * seed), B, V,
                       kinds=["topp", "topp_minp", "topp", "greedy", "kfast", "none", "minp"])
     xd = to_device(x)
-    a = gpu_sample(xd, V, w, hints=vs.OPT_TOPP_REJECTION, mask=False)
-    b = gpu_sample(xd, V, w, hints=0, mask=False)
-    for key in ("ids", "kept", "status"):
-        assert np.array_equal(a[key], b[key]), key
-    assert compare_sample(a, oracle_sample(x, V, w, mask=False)) <= 1
+    o = oracle_sample(x, V, w, mask=False)
+    res = {}
+    for name, h in (("rejection", vs.OPT_TOPP_REJECTION), ("gather", vs.OPT_TOPP_GATHER_DRAW),
+                    ("kept_pass", vs.OPT_TOPP_KEPT_PASS), ("default", 0)):
+        res[name] = gpu_sample(xd, V, w, hints=h, mask=False)
+        assert compare_sample(res[name], o) <= 1, name
+    for name in ("rejection", "gather", "default"):
+        for key in ("ids", "kept", "status"):
+            assert np.array_equal(res[name][key], res["kept_pass"][key]), (name, key)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -180,7 +185,19 @@ def test_sample_constant_rows_fallback_inside_bucket():
     w = dict(temperature=np.ones(B, np.float32), top_k=np.zeros(B, np.int32),
              top_p=np.array([0.37, 0.8, 0.5, 0.999], np.float32), min_p=np.zeros(B, np.float32),
              seeds=np.arange(B, dtype=np.uint64))
-    compare_sample(gpu_sample(to_device(x), V, w), oracle_sample(x, V, w))
+    xd = to_device(x)
+    compare_sample(gpu_sample(xd, V, w), oracle_sample(x, V, w))
+    _every_draw_method(xd, x, V, w)
+
+
+def _every_draw_method(xd, x, V, w):
+    """Without a kept mask, each method for full-vocabulary top-p rows against
+    the oracle (a cut bucket beyond the list: the gather draw falls back to
+    the Gumbel pass over the kept set)."""
+    import decode_token_sampling_amd as vs
+    o = oracle_sample(x, V, w, mask=False)
+    for h in (vs.OPT_TOPP_REJECTION, vs.OPT_TOPP_GATHER_DRAW, vs.OPT_TOPP_KEPT_PASS):
+        compare_sample(gpu_sample(xd, V, w, hints=h, mask=False), o)
 
 
 def test_full_topp_gather_overflows_lds_but_fits_list():
@@ -196,7 +213,9 @@ def test_full_topp_gather_overflows_lds_but_fits_list():
     w = dict(temperature=np.ones(B, np.float32), top_k=np.zeros(B, np.int32),
              top_p=np.array([0.5, 0.7, 0.3], np.float32), min_p=np.zeros(B, np.float32),
              seeds=np.arange(B, dtype=np.uint64))
-    compare_sample(gpu_sample(to_device(x), V, w), oracle_sample(x, V, w))
+    xd = to_device(x)
+    compare_sample(gpu_sample(xd, V, w), oracle_sample(x, V, w))
+    _every_draw_method(xd, x, V, w)
 
 
 # ---------------------------------------------------------------- penalties

@@ -170,19 +170,23 @@ def test_workload_fused_penalties(name):
     _check_lp(out["token_lp"], lp["token_lp"])
 
 
+@pytest.mark.parametrize("method", ["rejection", "gather", "kept_pass"])
 @pytest.mark.parametrize("name", ["w4x32000_f32", "w32x151936_bf16", "w64x262144_bf16"])
-def test_workload_topp_rejection(name):
-    """The workloads with full-vocabulary top-p rows through the rejection draw
-    (VS_OPT_TOPP_REJECTION): ids, kept counts and sampled-id log-probs of every
-    row against the oracle."""
+def test_workload_topp_methods(name, method):
+    """The workloads with full-vocabulary top-p rows through each method for
+    them (VS_OPT_TOPP_REJECTION, VS_OPT_TOPP_GATHER_DRAW, VS_OPT_TOPP_KEPT_PASS;
+    the benchmarked call takes the default): ids, kept counts and sampled-id
+    log-probs of every row against the oracle."""
     import decode_token_sampling_amd as vs
     wl, x, pst, o, lp, full_rows, full = _oracle(name)
     xd = _penalised_device(wl, x, pst)
     w = params_from(wl)
+    h = {"rejection": vs.OPT_TOPP_REJECTION, "gather": vs.OPT_TOPP_GATHER_DRAW,
+         "kept_pass": vs.OPT_TOPP_KEPT_PASS}[method]
     out = vs.sample_logprobs(xd, dev(w["temperature"], np.float32), dev(w["top_k"], np.int32),
                              dev(w["top_p"], np.float32), dev(w["min_p"], np.float32),
                              dev(np.asarray(w["seeds"], np.uint64).view(np.int64), np.int64),
-                             hints=vs.OPT_TOPP_REJECTION, k=wl.logprob_k)
+                             hints=h, k=wl.logprob_k)
     torch.cuda.synchronize()
     g = dict(ids=out["ids"].cpu().numpy(), kept=out["kept"].cpu().numpy(),
              status=out["status"].cpu().numpy())
