@@ -185,7 +185,6 @@ __global__ __launch_bounds__(kThreads) void k_full_hist(Job j) {
   for (int i = threadIdx.x; i < kFullBuckets; i += kThreads) hw[i] = 0ull;
   if (threadIdx.x == 0) s_bound = 0ull;
   __syncthreads();
-  const FullTerms ft{m, c.mp};
   constexpr bool reject = kReject;
   // The rejection draw's candidates: every member id's Gumbel score e / -log u
   // (e and u exactly as the Gumbel pass forms them) into this thread's best
@@ -225,16 +224,37 @@ __global__ __launch_bounds__(kThreads) void k_full_hist(Job j) {
   // adding 0 at one shared address would serialize the wave's lanes)
   auto pass = [&](auto div) {
     rd.visit([&](int id0, const float* x, int n) {
-      if constexpr (reject) refresh();
+      constexpr int EPV = SegReader<E, 4>::EPV;
+      if constexpr (reject) {
+        refresh();
+        const FullTerms ft{m, c.mp};
 #pragma unroll
-      for (int q = 0; q < SegReader<E, 4>::EPV; ++q) {
-        uint64_t w;
-        int b;
-        float e;
-        const float sv = scaled_by<decltype(div)::value>(x[q], c.T);
-        if (ft.mass_e(sv, &w, &b, &e) && q < n) {
-          atomicAdd(reinterpret_cast<unsigned long long*>(&hw[b]), static_cast<unsigned long long>(w));
-          if constexpr (reject) candidate(id0 + q, e, f2key(sv));
+        for (int q = 0; q < EPV; ++q) {
+          uint64_t w;
+          int b;
+          float e;
+          const float sv = scaled_by<decltype(div)::value>(x[q], c.T);
+          if (ft.mass_e(sv, &w, &b, &e) && q < n) {
+            atomicAdd(reinterpret_cast<unsigned long long*>(&hw[b]), static_cast<unsigned long long>(w));
+            candidate(id0 + q, e, f2key(sv));
+          }
+        }
+      } else {
+        // the vector's exponentials first, evaluated together (their
+        // dependent chains interleave), then its masses into the histogram:
+        // the terms of FullTerms::mass_e
+        float t[EPV], e[EPV];
+#pragma unroll
+        for (int q = 0; q < EPV; ++q) t[q] = scaled_by<decltype(div)::value>(x[q], c.T) - m;
+        constexpr int G = EPV < 4 ? EPV : 4;
+#pragma unroll
+        for (int g0 = 0; g0 < EPV; g0 += G) pinned_exp_n<G>(t + g0, e + g0);
+#pragma unroll
+        for (int q = 0; q < EPV; ++q) {
+          const uint64_t w = mass_of(e[q]);
+          if (q < n && e[q] >= c.mp && w != 0)
+            atomicAdd(reinterpret_cast<unsigned long long*>(&hw[FullTerms::bucket_of(t[q])]),
+                      static_cast<unsigned long long>(w));
         }
       }
     });

@@ -9,10 +9,23 @@
 
 namespace {
 
+// Each thread takes four consecutive inputs through the four-value form of E
+// (as the histogram pass evaluates it) and each one alone through the
+// one-value form; it writes the four-value result where both agree bit for
+// bit and NaN where they do not (no E value is NaN), so that comparing the
+// output with the oracle checks both forms.
 __global__ __launch_bounds__(256) void k_exp_bits(uint32_t lo_bits, uint32_t n, float* __restrict__ out) {
-  const uint32_t i = blockIdx.x * 256u + threadIdx.x;
-  if (i >= n) return;
-  out[i] = vsk::pinned_exp(__uint_as_float(lo_bits + i));
+  const uint32_t i0 = (blockIdx.x * 256u + threadIdx.x) * 4u;
+  if (i0 >= n) return;
+  float t[4], e4[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) t[u] = __uint_as_float(lo_bits + i0 + static_cast<uint32_t>(u));
+  vsk::pinned_exp_n<4>(t, e4);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float e1 = vsk::pinned_exp(t[u]);
+    if (i0 + u < n) out[i0 + u] = __float_as_uint(e1) == __float_as_uint(e4[u]) ? e4[u] : __builtin_nanf("");
+  }
 }
 
 }  // namespace
@@ -21,7 +34,7 @@ __global__ __launch_bounds__(256) void k_exp_bits(uint32_t lo_bits, uint32_t n, 
 // memory. Returns a hipError_t code (0 on success).
 extern "C" int vs_selftest_exp(uint32_t lo_bits, uint32_t n, float* out, hipStream_t stream) {
   if (!out || n == 0) return static_cast<int>(hipErrorInvalidValue);
-  const uint32_t blocks = (n + 255u) / 256u;
+  const uint32_t blocks = (n + 1023u) / 1024u;  // four inputs per thread
   hipLaunchKernelGGL(k_exp_bits, dim3(blocks), dim3(256), 0, stream, lo_bits, n, out);
   return static_cast<int>(hipGetLastError());
 }

@@ -120,31 +120,46 @@ __device__ __forceinline__ double fnma_k(double n, double k, double c) {
   asm("v_fma_f64 %0, -%1, %2, %3" : "=v"(d) : "v"(n), "s"(k), "v"(c));
   return d;
 }
+// pinned_exp of N values at once, the same operations on each, issued in
+// turn across the N values (the constant-operand FMAs are inline asm, which
+// the compiler keeps in source order: written value by value, the N
+// dependent chains would run one after the other).
+template <int N>
+__device__ __forceinline__ void pinned_exp_n(const float* tf, float* out) {
+  // the Taylor coefficients of exp after the leading 1/13!, highest first
+  constexpr double kC[13] = {1.0 / 479001600.0, 1.0 / 39916800.0, 1.0 / 3628800.0,
+                             1.0 / 362880.0,    1.0 / 40320.0,    1.0 / 5040.0,
+                             1.0 / 720.0,       1.0 / 120.0,      1.0 / 24.0,
+                             1.0 / 6.0,         0.5,              1.0,
+                             1.0};
+  double r[N], p[N], n[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const double t = static_cast<double>(fminf(fmaxf(tf[i], -87.5f), 128.0f));
+    n[i] = rint(t * 1.4426950408889634);
+    r[i] = fnma_k(n[i], 0x1.62e42fefa3800p-1, t);
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) r[i] = fnma_k(n[i], 0x1.ef35793c76730p-45, r[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) p[i] = fma_k(1.0 / 6227020800.0, r[i], kC[0]);
+#pragma unroll
+  for (int k = 1; k < 13; ++k) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) p[i] = fma_k(p[i], r[i], kC[k]);
+  }
+  // n is an integer in [-127, 185]; p * 2^n is exact in double (and above
+  // the fp32 range from t = 88.73 on, where the conversion gives +inf)
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float y = static_cast<float>(ldexp(p[i], static_cast<int>(n[i])));
+    out[i] = tf[i] >= -87.0f ? y : 0.0f;  // below -87 (and NaN): 0
+  }
+}
 __device__ __forceinline__ float pinned_exp(float tf) {
-  if (!(tf >= -87.0f)) return 0.0f;
-  const double t = static_cast<double>(tf);
-  const double n = rint(t * 1.4426950408889634);   // 1/ln2
-  const double hi = 0x1.62e42fefa3800p-1;           // ln2, low 11 bits cleared
-  const double lo = 0x1.ef35793c76730p-45;          // ln2 - hi
-  double r = fnma_k(n, hi, t);
-  r = fnma_k(n, lo, r);
-  double p = 1.0 / 6227020800.0;                    // 1/13!
-  p = fma_k(p, r, 1.0 / 479001600.0);
-  p = fma_k(p, r, 1.0 / 39916800.0);
-  p = fma_k(p, r, 1.0 / 3628800.0);
-  p = fma_k(p, r, 1.0 / 362880.0);
-  p = fma_k(p, r, 1.0 / 40320.0);
-  p = fma_k(p, r, 1.0 / 5040.0);
-  p = fma_k(p, r, 1.0 / 720.0);
-  p = fma_k(p, r, 1.0 / 120.0);
-  p = fma_k(p, r, 1.0 / 24.0);
-  p = fma_k(p, r, 1.0 / 6.0);
-  p = fma_k(p, r, 0.5);
-  p = fma_k(p, r, 1.0);
-  p = fma_k(p, r, 1.0);
-  // n is an integer in [-126, 128] for every t that gets here and is not
-  // above the fp32 overflow threshold; p * 2^n is exact in double
-  return static_cast<float>(ldexp(p, static_cast<int>(n)));
+  float e;
+  pinned_exp_n<1>(&tf, &e);
+  return e;
 }
 
 // Fixed-point top-p mass of a relative weight e in [0,1]: floor(e * 2^31).

@@ -54,3 +54,26 @@ def test_device_exp_matches_oracle_everywhere(selftest):
         lo += n
     assert checked == total
     assert bad == 0, f"{bad} inputs disagree"
+
+
+def test_device_exp_outside_the_method_range(selftest):
+    """Inputs the method never produces, still defined the same on both
+    sides: below -87 (0), NaN (0), -inf (0), +0 and positive t up to past
+    the fp32 overflow (+inf), +inf itself."""
+    stream = torch.cuda.current_stream().cuda_stream
+    ranges = [
+        (NEG_87 + 1, 1 << 22),                # just below -87
+        (0xC3000000, 1 << 20),                # -128 and below
+        (0xFF800000, 1),                      # -inf
+        (0xFFC00000, 1 << 10),                # negative NaNs
+        (0x7FC00000, 1 << 10),                # positive NaNs
+        (0x00000000, 1 << 22),                # +0 and the smallest positives
+        (0x42B00000, 1 << 20),                # 88 up to past the overflow threshold
+        (0x7F800000, 1),                      # +inf
+    ]
+    out = torch.empty(1 << 22, dtype=torch.float32, device="cuda")
+    for lo, n in ranges:
+        assert selftest.vs_selftest_exp(lo, n, out.data_ptr(), stream) == 0
+        got = out[:n].cpu().numpy()
+        bad, first = oracle.exp_compare(lo, got)
+        assert bad == 0, (hex(lo), first, got[first])
