@@ -22,7 +22,8 @@ import torch
 __all__ = [
     "LIB_PATH", "VsError", "load", "workspace_size", "workspace", "penalize", "sample",
     "logprobs", "sample_logprobs", "ROW_BAD_PARAM", "ROW_BAD_LOGITS", "ROW_BAD_TOKEN_ID", "ROW_TOPK_UNSUPPORTED",
-    "ROW_HINT_VIOLATED", "HINT_NONE", "HINT_NO_FULLVOCAB", "HINT_ALL_GREEDY", "HINT_SMALL_TOPK",
+    "ROW_HINT_VIOLATED", "HINT_NONE", "HINT_NO_FULLVOCAB", "HINT_ALL_GREEDY", "HINT_NO_GREEDY",
+    "HINT_SMALL_TOPK",
     "OPT_TOPP_REJECTION", "OPT_TOPP_GATHER_DRAW", "OPT_TOPP_KEPT_PASS", "MAX_V",
     "TOPK_MAX", "LOGPROB_K_MAX", "EXPORTED_SYMBOLS", "hints_for", "sample_logprobs_noalloc",
     "NOALLOC_SCRATCH_BYTES", "penalize_sample_logprobs",
@@ -41,7 +42,8 @@ ROW_HINT_VIOLATED = 16
 HINT_NONE = 0
 HINT_NO_FULLVOCAB = 1
 HINT_ALL_GREEDY = 2
-HINT_SMALL_TOPK = 4
+HINT_NO_GREEDY = 4
+HINT_SMALL_TOPK = 8
 OPT_TOPP_REJECTION = 256
 OPT_TOPP_GATHER_DRAW = 512
 OPT_TOPP_KEPT_PASS = 1024

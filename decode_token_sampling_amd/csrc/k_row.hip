@@ -539,6 +539,7 @@ __global__ __launch_bounds__(kLightThreads) void k_row_light(Job j) {
     if (pl.kA == 1 && top == 0ull) status |= VS_ROW_BAD_LOGITS;  // no argmax was found
     if (status == 0) {
       if ((j.hints & VS_HINT_ALL_GREEDY) && c.mode != kModeGreedy) status = VS_ROW_HINT_VIOLATED;
+      if ((j.hints & VS_HINT_NO_GREEDY) && c.mode == kModeGreedy) status = VS_ROW_HINT_VIOLATED;
       if ((j.hints & VS_HINT_NO_FULLVOCAB) && c.mode == kModeFull) status = VS_ROW_HINT_VIOLATED;
       if ((j.hints & VS_HINT_SMALL_TOPK) && c.mode != kModeGreedy && c.mode != kModeKFast)
         status = VS_ROW_HINT_VIOLATED;

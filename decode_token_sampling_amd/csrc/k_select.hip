@@ -718,6 +718,7 @@ __device__ __forceinline__ void finish_row(const Job& j, int row, const Plan& pl
     if (pl.kA == 1 && bA == 0ull) status |= VS_ROW_BAD_LOGITS;
     if (status == 0) {
       if ((j.hints & VS_HINT_ALL_GREEDY) && c.mode != kModeGreedy) status = VS_ROW_HINT_VIOLATED;
+      if ((j.hints & VS_HINT_NO_GREEDY) && c.mode == kModeGreedy) status = VS_ROW_HINT_VIOLATED;
       if ((j.hints & VS_HINT_SMALL_TOPK) && c.mode != kModeGreedy && c.mode != kModeKFast)
         status = VS_ROW_HINT_VIOLATED;
     }

@@ -317,7 +317,7 @@ vs_status sample_logprobs_impl(const PenArgs* pen, const void* logits, int dt, i
                                int64_t ld_out, void* ws, size_t ws_bytes, int nslot,
                                hipStream_t stream) {
   if (!logits || !out_ids || !ws || !sizes_ok(dt, B, V, ld)) return VS_ERR_INVALID_ARGUMENT;
-  if (hints & ~(VS_HINT_NO_FULLVOCAB | VS_HINT_ALL_GREEDY | VS_HINT_SMALL_TOPK |
+  if (hints & ~(VS_HINT_NO_FULLVOCAB | VS_HINT_ALL_GREEDY | VS_HINT_NO_GREEDY | VS_HINT_SMALL_TOPK |
                 VS_OPT_TOPP_REJECTION | VS_OPT_TOPP_GATHER_DRAW | VS_OPT_TOPP_KEPT_PASS))
     return VS_ERR_INVALID_ARGUMENT;
   if (k < 0 || k > VS_LOGPROB_K_MAX || k > V) return VS_ERR_INVALID_ARGUMENT;

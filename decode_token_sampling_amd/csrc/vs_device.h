@@ -239,7 +239,10 @@ __device__ __forceinline__ RowCfg load_cfg(int r, int V, const float* temperatur
                                            const int32_t* top_k, const float* top_p,
                                            const float* min_p, const uint64_t* seeds) {
   RowCfg c;
-  c.T = temperature ? temperature[r] : 1.0f;
+  // arrays left out take neutral values; temperature, top_k and top_p all
+  // left out make every row greedy (TensorRT-LLM "Sampling": none of the
+  // three set means greedy), as T = 0
+  c.T = temperature ? temperature[r] : ((!top_k && !top_p) ? 0.0f : 1.0f);
   const int k = top_k ? top_k[r] : 0;
   c.p = top_p ? top_p[r] : 1.0f;
   c.mp = min_p ? min_p[r] : 0.0f;

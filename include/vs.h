@@ -15,6 +15,11 @@
  *    pointer after a call returns, and no call allocates or frees memory (the
  *    one device array the library owns, the scratch of
  *    vs_sample_logprobs_noalloc, exists from load to process end).
+ *  - Mutable state kept by the library: cached device properties (compute-unit
+ *    count per device), the per-device address of that scratch, and the
+ *    profiling record of vs_profile_begin/_end, which is thread-local (one per
+ *    calling host thread, empty unless that thread turned it on) and so never
+ *    shared between callers.
  *  - Each call checks its host-visible arguments, enqueues kernels on `stream`
  *    and returns without waiting. Outputs are valid once the stream reaches that
  *    point; inputs must stay alive until then. No call synchronises, copies to
@@ -67,8 +72,12 @@ typedef enum vs_status {
 #define VS_HINT_NONE 0u
 #define VS_HINT_NO_FULLVOCAB 1u   /* no row samples over the full vocabulary: every row is
                                      greedy or has 0 < top_k < V */
+#define VS_HINT_NO_FULLVOCAB_TRUNCATION VS_HINT_NO_FULLVOCAB
 #define VS_HINT_ALL_GREEDY 2u     /* every row is greedy */
-#define VS_HINT_SMALL_TOPK 4u     /* every row is greedy or has 1 < top_k <= 64 (and
+#define VS_HINT_NO_GREEDY 4u      /* no row is greedy. Checked, but it lets nothing be
+                                     skipped here: a greedy row costs no kernel of its own
+                                     (its argmax comes with the streaming pass's lists) */
+#define VS_HINT_SMALL_TOPK 8u     /* every row is greedy or has 1 < top_k <= 64 (and
                                      top_k < V): no full-vocabulary row, no larger top-k */
 /* Not promises but a choice of method for full-vocabulary top-p rows, passed in
  * the same word; every method gives identical results, and all are ignored
@@ -232,6 +241,8 @@ vs_status vs_slot_remap(int B, int B_src, const int32_t* slot_remap, const void*
  *  logits       [B, ld] fp32 or bf16 (read only)
  *  temperature  [B] fp32 or NULL (all 1)       top_k [B] int32 or NULL (all 0)
  *  top_p        [B] fp32 or NULL (all 1)       min_p [B] fp32 or NULL (all 0)
+ *               with temperature, top_k and top_p all NULL every row is greedy
+ *               (the page: none of the three set means greedy sampling)
  *  seeds        [B] uint64 or NULL (all 0): the caller's per-row seed, advanced by
  *               the caller once per sampled token
  *  hints        VS_HINT_* promises (0 = none)
@@ -380,8 +391,9 @@ vs_status vs_logprobs_ex(const void* logits, vs_dtype dt, int B, int V, int64_t 
  * hipEventRecord(events[2i]) and hipEventRecord(events[2i+1]) on that call's
  * stream, i = 0, 1, ... in enqueue order, until `capacity` events are used.
  * `events` is a host array of events the caller created (hipEventCreate) and
- * owns. Stage names: "select", "row", "row_full", "gumbel", "lse_select",
- * "lse_row", "lse_full", "penalize". vs_profile_end stops recording on this thread,
+ * owns. Stage names: "select", "row", "full_prep", "row_full", "gumbel",
+ * "lse_select", "lse_row", "lse_full", "penalize", "topp_decay",
+ * "seed_advance", "slot_remap". vs_profile_end stops recording on this thread,
  * copies up to max_names stage-name pointers (static strings) to `names` (may
  * be NULL) and returns the number of stages recorded.
  */

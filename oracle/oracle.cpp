@@ -383,10 +383,16 @@ int oracle_sample_row(const void* logits, int dtype, int B, int V, int64_t ld,
                       int32_t* out_kept_count, uint8_t* out_kept_mask,
                       double* out_top2, int32_t* row_status) {
   if (r < 0 || r >= B) return 1;
+  // A parameter array left out (NULL) gives every row its neutral value
+  // (T = 1, top_k = 0, top_p = 1, min_p = 0, seed 0); with temperature, top_k
+  // and top_p all left out the rows are greedy (TensorRT-LLM "Sampling", LLM
+  // API sampling behavior: none of the three set means greedy), here T = 0.
+  const bool unset = !temperature && !top_k && !top_p;
+  const float T = temperature ? temperature[r] : (unset ? 0.0f : 1.0f);
   int32_t kept = 0;
   const int status = sample_one_row(
-      logits, dtype, V, ld, r, temperature[r], top_k[r], top_p[r],
-      min_p ? min_p[r] : 0.0f, seeds[r], &out_ids[r], &kept,
+      logits, dtype, V, ld, r, T, top_k ? top_k[r] : 0, top_p ? top_p[r] : 1.0f,
+      min_p ? min_p[r] : 0.0f, seeds ? seeds[r] : 0ull, &out_ids[r], &kept,
       out_kept_mask ? out_kept_mask + static_cast<int64_t>(r) * V : nullptr,
       out_top2 ? out_top2 + 2 * r : nullptr);
   if (out_kept_count) out_kept_count[r] = kept;

@@ -88,3 +88,20 @@ def test_binding_refuses_host_tensors():
     import decode_token_sampling_amd as vs
     with pytest.raises(ValueError):
         vs.sample(torch.zeros(2, 10))
+
+
+def test_binding_constants_match_the_header():
+    """Every VS_HINT_*, VS_OPT_*, VS_ROW_* and size constant the binding
+    exports has the header's value (the binding has no other source)."""
+    import decode_token_sampling_amd as vs
+    with open(os.path.join(ROOT, "include", "vs.h")) as f:
+        text = f.read()
+    defs = {m[0]: int(m[1]) << int(m[2] or 0)
+            for m in re.findall(r"^#define VS_(\w+)\s+\(?(\d+)u?(?:\s*<<\s*(\d+))?", text, re.M)}
+    checked = 0
+    for name, value in defs.items():
+        if hasattr(vs, name):
+            assert getattr(vs, name) == value, name
+            checked += 1
+    assert checked >= 12, checked
+    assert defs["HINT_SMALL_TOPK"] == 8 and defs["HINT_NO_GREEDY"] == 4

@@ -12,7 +12,7 @@ import torch
 import oracle
 import synth
 from parity import (LOGPROB_ATOL, compare_sample, dev, from_device, gpu_sample, host_pad,
-                    oracle_sample, params_from, random_params, to_device)
+                    mask_bits, oracle_sample, params_from, random_params, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -117,6 +117,29 @@ def test_sample_seeds_change_draw_and_repeat():
     compare_sample(c, oracle_sample(x, V, w2))
 
 
+@pytest.mark.parametrize("given", ["none", "temperature", "top_k", "top_p", "min_p"])
+def test_sample_unset_parameters(given):
+    """Parameter arrays left out (NULL): neutral values, and greedy rows when
+    temperature, top_k and top_p are all left out; ids, kept counts and kept
+    sets against the oracle given the same NULLs."""
+    import decode_token_sampling_amd as vs
+    V, B = 5000, 12
+    x = synth.random_rows(21, B, V, kind="normal")
+    vals = dict(temperature=np.full(B, 0.8, np.float32), top_k=np.full(B, 40, np.int32),
+                top_p=np.full(B, 0.7, np.float32), min_p=np.full(B, 0.02, np.float32))
+    w = {k: (v if k == given else None) for k, v in vals.items()}
+    xd = to_device(x)
+    out = vs.sample(xd, **{k: (None if v is None else dev(v, v.dtype)) for k, v in w.items()},
+                    mask=True, V=V)
+    torch.cuda.synchronize()
+    g = dict(ids=out["ids"].cpu().numpy(), kept=out["kept"].cpu().numpy(),
+             status=out["status"].cpu().numpy(), mask=mask_bits(out["mask"], V))
+    o = oracle.sample(x, V, w["temperature"], w["top_k"], w["top_p"], w["min_p"], None, want_mask=True)
+    compare_sample(g, o)
+    if given in ("none", "min_p"):
+        assert (g["kept"] == 1).all() and np.array_equal(g["ids"], np.argmax(x, axis=1))
+
+
 def test_sample_invalid_rows():
     V, B = 300, 9
     x = synth.random_rows(4, B, V)
@@ -160,6 +183,9 @@ def test_sample_hints():
     greedy = np.arange(B) % 4 == 0
     assert (g["status"][~greedy] == vs.ROW_HINT_VIOLATED).all()
     compare_sample(g, o, rows=np.nonzero(greedy)[0])
+    g = gpu_sample(to_device(x), V, w, hints=vs.HINT_NO_GREEDY)
+    assert (g["status"][greedy] == vs.ROW_HINT_VIOLATED).all() and (g["ids"][greedy] == -1).all()
+    compare_sample(g, o, rows=np.nonzero(~greedy)[0])
 
 
 def test_sample_heavy_ties_take_exact_path():
@@ -597,7 +623,6 @@ def test_sample_logprobs_fused(V, dtype, k):
                              dev(np.asarray(w["seeds"], np.uint64).view(np.int64), np.int64),
                              k=k, mask=True, V=V)
     torch.cuda.synchronize()
-    from parity import mask_bits
     g = dict(ids=out["ids"].cpu().numpy(), kept=out["kept"].cpu().numpy(),
              status=out["status"].cpu().numpy(), mask=mask_bits(out["mask"], V))
     compare_sample(g, oracle_sample(x, V, w))

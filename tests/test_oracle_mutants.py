@@ -50,6 +50,7 @@ MUTANTS = {
                                        "const float s = (T == 1.0f) ? x : x * T;"),
     "top2_second_not_demoted": ("      g2 = g1;\n      g1 = score;", "      g1 = score;"),
     "top2_second_from_best_only": ("    } else if (score > g2) {", "    } else if (score > g1) {"),
+    "unset_parameters_not_greedy": ("(unset ? 0.0f : 1.0f)", "1.0f"),
     "logprob_ties_to_highest_id": ("        if (z[a] != z[b]) return z[a] > z[b];\n        return a < b;",
                                    "        if (z[a] != z[b]) return z[a] > z[b];\n        return a > b;"),
 }

@@ -333,6 +333,25 @@ def test_greedy_triggers(orc):
         assert out["ids"][0] == 1 and out["kept"][0] == 1 and out["status"][0] == 0
 
 
+def test_unset_parameters(orc):
+    """Arrays left out take neutral values (T 1, top_k 0, top_p 1, min_p 0,
+    seed 0); temperature, top_k and top_p all left out make the row greedy
+    (TensorRT-LLM "Sampling", LLM API sampling behavior: none of the three
+    set means greedy)."""
+    x = np.array([[1.0, 3.0, 3.0, 2.0, -1.0]], np.float32)
+    out = orc.sample(x, 5, None, None, None, None, None, want_mask=True)
+    assert out["ids"][0] == 1 and out["kept"][0] == 1 and out["status"][0] == 0
+    assert out["mask"][0].tolist() == [0, 1, 0, 0, 0]
+    # one of the three given: the others neutral, untruncated (every id kept)
+    out = orc.sample(x, 5, np.ones(1, np.float32), None, None, None, None, want_mask=True)
+    assert out["kept"][0] == 5 and out["mask"][0].all()
+    out = orc.sample(x, 5, None, np.array([2], np.int32), None, None, None, want_mask=True)
+    assert out["kept"][0] == 2 and out["mask"][0].tolist() == [0, 1, 1, 0, 0]
+    explicit = orc.sample(x, 5, np.ones(1, np.float32), np.array([2], np.int32),
+                          np.ones(1, np.float32), np.zeros(1, np.float32), np.zeros(1, np.uint64))
+    assert out["ids"][0] == explicit["ids"][0]  # seed 0 when left out
+
+
 def _brute_rank(s):
     """rank_j = #{i : s_i > s_j or (s_i == s_j and i < j)} by pairwise counting."""
     n = len(s)
