@@ -65,7 +65,7 @@ def test_host_checks_without_gpu():
                          dummy, 8, None) == 2                # workspace too small
     assert lib.vs_logprobs(dummy, 0, 4, 10, 10, None, None, 65, dummy, dummy, None, 0, None,
                            dummy, 1 << 30, None) == 1        # k > 64
-    assert lib.vs_sample(dummy, 0, 4, 10, 10, *([None] * 5), 8, dummy, None, None, None,
+    assert lib.vs_sample(dummy, 0, 4, 10, 10, *([None] * 5), 16, dummy, None, None, None,
                          dummy, 1 << 30, None) == 1          # unknown hint bit
 
 
