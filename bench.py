@@ -48,8 +48,6 @@ HBM_PEAK_GBPS = 8000.0
 HEADLINE = "w256x248320_f32"
 ALL_WORKLOADS = ["w256x248320_f32", "w4x32000_f32", "w32x151936_bf16", "w1024x128256_f32",
                  "w64x262144_bf16"]
-# Integer-multiply issue of the whole chip: 256 compute units x 4 SIMDs x 16
-# lanes per clock at quarter rate for 32-bit multiplies, 2.4 GHz.
 # The vector ALUs' issue ceiling: 256 CUs x 4 SIMDs x 16 lanes per cycle x
 # 2.4 GHz (every VALU instruction at the non-packed fp32 rate, 32-bit integer
 # multiplies included), and one SplitMix64 word as the compiler builds it for
@@ -566,6 +564,9 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time eager launches, not HIP graphs")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of pinned one-thread oracle work on the headline")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first copy this many MiB device to device three times (HIP's copy "
+                         "kernel), the known-size reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): every row of the "
@@ -582,6 +583,15 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     hip = HipEvents()
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        a.fill_(1)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     names = ALL_WORKLOADS if args.workload == "all" else [args.workload]
     splitmix_rate = splitmix_reference(torch, dev, hip, st)
 
