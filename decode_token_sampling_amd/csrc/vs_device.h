@@ -343,9 +343,10 @@ constexpr int kDppXor1 = 0xB1;    // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;    // quad_perm [2,3,0,1]
 constexpr int kDppRor4 = 0x124;   // row_ror:4
 constexpr int kDppRor8 = 0x128;   // row_ror:8
+// (every lane is written, so no old value is set up first)
 template <int kCtrl>
 __device__ __forceinline__ int dpp_i32(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xF, 0xF, false);
+  return __builtin_amdgcn_mov_dpp(v, kCtrl, 0xF, 0xF, false);
 }
 template <int kCtrl>
 __device__ __forceinline__ float dpp_f32(float v) {
@@ -452,22 +453,25 @@ __device__ __forceinline__ uint32_t wave_scan_incl_u32(uint32_t v) {
 template <int J>
 __device__ __forceinline__ uint32_t lane_xor_u32(uint32_t x) {
   const int v = static_cast<int>(x);
+  // (the moves below write every lane, so no old value is set up first; for
+  // J = 4 the second move writes the lanes the first one leaves)
   if constexpr (J == 1) {
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));
   } else if constexpr (J == 2) {
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));
   } else if constexpr (J == 4) {
-    const int t = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0x5, false);  // row_shl:4, banks 0, 2
+    const int t = __builtin_amdgcn_mov_dpp(v, 0x104, 0xF, 0x5, false);  // row_shl:4, banks 0, 2
     return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(t, v, 0x114, 0xF, 0xA, false));  // row_shr:4
   } else if constexpr (J == 8) {
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false));  // row_ror:8
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false));  // row_ror:8
   } else if constexpr (J == 16) {
     const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    return (lane() & 16) ? a[0] : a[1];
+    // lanes with bit 4 set, as a wave mask (no per-lane test)
+    return __builtin_amdgcn_inverse_ballot_w64(0xFFFF0000FFFF0000ull) ? a[0] : a[1];
   } else {
     static_assert(J == 32, "lane_xor_u32: J in {1, 2, 4, 8, 16, 32}");
     const auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    return (lane() & 32) ? a[0] : a[1];
+    return __builtin_amdgcn_inverse_ballot_w64(0xFFFFFFFF00000000ull) ? a[0] : a[1];
   }
 }
 template <int J>
@@ -476,14 +480,26 @@ __device__ __forceinline__ uint64_t lane_xor_u64(uint64_t x) {
   const uint32_t hi = lane_xor_u32<J>(static_cast<uint32_t>(x >> 32));
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
+// The lanes that keep the larger value of their pair in a bitonic step (block
+// size K, partner distance J), as a wave mask fixed at compile time.
+template <int K, int J, bool kDesc>
+__host__ __device__ constexpr uint64_t keep_max_lanes() {
+  uint64_t m = 0;
+  for (int i = 0; i < 64; ++i)
+    if ((((i & K) == 0) == ((i & J) == 0)) == kDesc) m |= 1ull << i;
+  return m;
+}
 // One compare-exchange step of a bitonic network over the 64 lanes (block
-// size K, partner distance J); kDesc: the finished sequence is descending.
+// size K, partner distance J); kDesc: the finished sequence is descending. A
+// lane takes its partner's value when the partner's is larger and the lane
+// keeps the larger one, or not larger and it keeps the smaller (equal values
+// are the same either way): one compare, the lane pattern as a scalar mask.
 template <int K, int J, bool kDesc>
 __device__ __forceinline__ uint64_t bitonic_step(uint64_t v) {
-  const int l = lane();
   const uint64_t o = lane_xor_u64<J>(v);
-  const bool keep_max = (((l & K) == 0) == ((l & J) == 0)) == kDesc;
-  return keep_max ? (o > v ? o : v) : (o < v ? o : v);
+  constexpr uint64_t kKeepMax = keep_max_lanes<K, J, kDesc>();
+  const bool keep_max = __builtin_amdgcn_inverse_ballot_w64(kKeepMax);
+  return (o > v) == keep_max ? o : v;
 }
 // Sorts one u64 per lane across the wave in registers (lane 0 first).
 template <bool kDesc>
