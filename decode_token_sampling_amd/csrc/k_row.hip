@@ -237,6 +237,30 @@ __device__ __forceinline__ void sort_desc(uint64_t* a, int n) {
   block_sort_desc(a, np);
 }
 
+// The min(n, 64) largest of n <= 64 x (waves) values in shared memory, sorted
+// descending into a[0..), by the block's waves with no block-wide network:
+// each wave sorts one 64-entry chunk in registers (wave 0 descending, the
+// others ascending), and wave 0 merges the others' chunks into its 64 best.
+// Entries of a past the result are left unspecified.
+__device__ void top64_sorted(uint64_t* a, int n) {
+  const int w = static_cast<int>(threadIdx.x) / kWave;
+  const int l = lane();
+  const int nw = static_cast<int>(blockDim.x) / kWave;
+  uint64_t v = 0ull;
+  if (w * kWave < n) {  // uniform per wave
+    v = (w * kWave + l < n) ? a[w * kWave + l] : 0ull;
+    v = (w == 0) ? wave_sort_u64<true>(v) : wave_sort_u64<false>(v);
+  }
+  __syncthreads();  // every chunk is read
+  if (w > 0 && w * kWave < n) a[w * kWave + l] = v;
+  __syncthreads();
+  if (w == 0) {
+    for (int q = 1; q < nw && q * kWave < n; ++q) v = wave_merge_top_u64(v, a[q * kWave + l]);
+    a[l] = v;
+  }
+  __syncthreads();
+}
+
 // Exact k-th largest of n distinct packed values in shared memory: MSB-first
 // radix select with 8-bit digits. Stops early once the remaining rank equals
 // the size of the chosen bucket (the whole bucket is then selected and the
@@ -375,7 +399,8 @@ __device__ int union_topk(const uint32_t* __restrict__ mrow, const uint64_t* __r
     __syncthreads();
     n = k;
   }
-  sort_desc(sh.buf, n);
+  // n <= 256 here (k <= 64): the k best sorted, without a block sort
+  top64_sorted(sh.buf, n);
   return n < k ? n : k;
 }
 
