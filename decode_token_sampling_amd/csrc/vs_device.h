@@ -294,29 +294,91 @@ struct LsePart {  // log-sum-exp partial of one tile: max and sum of exp(x - max
 // ---------------------------------------------------------------- wave primitives
 __device__ __forceinline__ int lane() { return static_cast<int>(__lane_id()); }
 
+// The value of lane (this lane XOR J) for J = 1, 2, 4, 8, 16, 32, every lane
+// active: DPP quad permutations for 1 and 2, row shifts into alternate banks
+// for 4, a row rotation by 8, and the gfx950 row-pair and half-wave swaps for
+// 16 and 32 (a copy of the value in both operands, so each lane finds its
+// partner in one of the two results).
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t x) {
+  const int v = static_cast<int>(x);
+  // (the moves below write every lane, so no old value is set up first; for
+  // J = 4 the second move writes the lanes the first one leaves)
+  if constexpr (J == 1) {
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));
+  } else if constexpr (J == 2) {
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));
+  } else if constexpr (J == 4) {
+    const int t = __builtin_amdgcn_mov_dpp(v, 0x104, 0xF, 0x5, false);  // row_shl:4, banks 0, 2
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(t, v, 0x114, 0xF, 0xA, false));  // row_shr:4
+  } else if constexpr (J == 8) {
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false));  // row_ror:8
+  } else if constexpr (J == 16) {
+    const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    // lanes with bit 4 set, as a wave mask (no per-lane test)
+    return __builtin_amdgcn_inverse_ballot_w64(0xFFFF0000FFFF0000ull) ? a[0] : a[1];
+  } else {
+    static_assert(J == 32, "lane_xor_u32: J in {1, 2, 4, 8, 16, 32}");
+    const auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return __builtin_amdgcn_inverse_ballot_w64(0xFFFFFFFF00000000ull) ? a[0] : a[1];
+  }
+}
+template <int J>
+__device__ __forceinline__ uint64_t lane_xor_u64(uint64_t x) {
+  const uint32_t lo = lane_xor_u32<J>(static_cast<uint32_t>(x));
+  const uint32_t hi = lane_xor_u32<J>(static_cast<uint32_t>(x >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+// The value of lane (this lane XOR J) for a 32- or 64-bit value of any type.
+template <int J, typename T>
+__device__ __forceinline__ T lane_xor(T v) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "lane_xor: 32- or 64-bit values");
+  if constexpr (sizeof(T) == 4) {
+    const uint32_t u = lane_xor_u32<J>(__builtin_bit_cast(uint32_t, v));
+    return __builtin_bit_cast(T, u);
+  } else {
+    const uint64_t u = lane_xor_u64<J>(__builtin_bit_cast(uint64_t, v));
+    return __builtin_bit_cast(T, u);
+  }
+}
+
+
+// lane_xor for a partner distance known only at run time (uniform over the
+// wave: a scalar branch picks the exchange).
+template <typename T>
+__device__ __forceinline__ T lane_xor_rt(T v, int j) {
+  switch (j) {
+    case 1: return lane_xor<1>(v);
+    case 2: return lane_xor<2>(v);
+    case 4: return lane_xor<4>(v);
+    case 8: return lane_xor<8>(v);
+    case 16: return lane_xor<16>(v);
+    default: return lane_xor<32>(v);
+  }
+}
+// Butterfly reductions over the wave (every lane gets the result), the
+// exchanges by DPP and gfx950 lane swaps rather than through LDS.
+template <typename T, typename F>
+__device__ __forceinline__ T wave_reduce(T v, F op) {
+  v = op(v, lane_xor<32>(v));
+  v = op(v, lane_xor<16>(v));
+  v = op(v, lane_xor<8>(v));
+  v = op(v, lane_xor<4>(v));
+  v = op(v, lane_xor<2>(v));
+  v = op(v, lane_xor<1>(v));
+  return v;
+}
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    T w = __shfl_xor(v, o);
-    v = (w > v) ? w : v;
-  }
-  return v;
+  return wave_reduce(v, [](T a, T b) { return (b > a) ? b : a; });
 }
 template <typename T>
 __device__ __forceinline__ T wave_min(T v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    T w = __shfl_xor(v, o);
-    v = (w < v) ? w : v;
-  }
-  return v;
+  return wave_reduce(v, [](T a, T b) { return (b < a) ? b : a; });
 }
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return wave_reduce(v, [](T a, T b) { return a + b; });
 }
 // Number of set bits of a ballot below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t ballot) {
@@ -445,41 +507,6 @@ __device__ __forceinline__ uint32_t wave_scan_incl_u32(uint32_t v) {
   return static_cast<uint32_t>(x);
 }
 
-// The value of lane (this lane XOR J) for J = 1, 2, 4, 8, 16, 32, every lane
-// active: DPP quad permutations for 1 and 2, row shifts into alternate banks
-// for 4, a row rotation by 8, and the gfx950 row-pair and half-wave swaps for
-// 16 and 32 (a copy of the value in both operands, so each lane finds its
-// partner in one of the two results).
-template <int J>
-__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t x) {
-  const int v = static_cast<int>(x);
-  // (the moves below write every lane, so no old value is set up first; for
-  // J = 4 the second move writes the lanes the first one leaves)
-  if constexpr (J == 1) {
-    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));
-  } else if constexpr (J == 2) {
-    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));
-  } else if constexpr (J == 4) {
-    const int t = __builtin_amdgcn_mov_dpp(v, 0x104, 0xF, 0x5, false);  // row_shl:4, banks 0, 2
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(t, v, 0x114, 0xF, 0xA, false));  // row_shr:4
-  } else if constexpr (J == 8) {
-    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false));  // row_ror:8
-  } else if constexpr (J == 16) {
-    const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    // lanes with bit 4 set, as a wave mask (no per-lane test)
-    return __builtin_amdgcn_inverse_ballot_w64(0xFFFF0000FFFF0000ull) ? a[0] : a[1];
-  } else {
-    static_assert(J == 32, "lane_xor_u32: J in {1, 2, 4, 8, 16, 32}");
-    const auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    return __builtin_amdgcn_inverse_ballot_w64(0xFFFFFFFF00000000ull) ? a[0] : a[1];
-  }
-}
-template <int J>
-__device__ __forceinline__ uint64_t lane_xor_u64(uint64_t x) {
-  const uint32_t lo = lane_xor_u32<J>(static_cast<uint32_t>(x));
-  const uint32_t hi = lane_xor_u32<J>(static_cast<uint32_t>(x >> 32));
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
 // The lanes that keep the larger value of their pair in a bitonic step (block
 // size K, partner distance J), as a wave mask fixed at compile time.
 template <int K, int J, bool kDesc>
@@ -620,7 +647,7 @@ __device__ __forceinline__ T wave_sort_desc(T v) {
   for (int k = 2; k <= kWave; k <<= 1) {
 #pragma unroll
     for (int j = k >> 1; j > 0; j >>= 1) {
-      const T o = __shfl_xor(v, j);
+      const T o = lane_xor_rt(v, j);
       const bool keep_max = (((l & k) == 0) == ((l & j) == 0));
       v = keep_max ? (o > v ? o : v) : (o < v ? o : v);
     }
@@ -636,7 +663,7 @@ __device__ __forceinline__ T wave_merge_top_desc(T a, T b) {
   T v = (a > br) ? a : br;
 #pragma unroll
   for (int j = kWave >> 1; j > 0; j >>= 1) {
-    const T o = __shfl_xor(v, j);
+    const T o = lane_xor_rt(v, j);
     v = ((l & j) == 0) ? (o > v ? o : v) : (o < v ? o : v);
   }
   return v;
