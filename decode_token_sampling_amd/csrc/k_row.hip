@@ -26,6 +26,10 @@ namespace {
 constexpr int kLightThreads = 256;
 constexpr int kFullThreads = 1024;
 constexpr int kSortCutMax = kFullThreads;  // longest gathered list cut by the sort (one entry per thread)
+// Longest candidate union whose k best come from per-wave chunk sorts alone
+// (four chunks per wave of the row kernel); longer ones are cut to the k-th
+// largest first.
+constexpr int kTopChunkMax = 1024;
 constexpr int kBuckets = kFullBuckets;
 constexpr int kMaxSegs = (VS_MAX_V + kSegMin - 1) / kSegMin;
 
@@ -237,25 +241,31 @@ __device__ __forceinline__ void sort_desc(uint64_t* a, int n) {
   block_sort_desc(a, np);
 }
 
-// The min(n, 64) largest of n <= 64 x (waves) values in shared memory, sorted
-// descending into a[0..), by the block's waves with no block-wide network:
-// each wave sorts one 64-entry chunk in registers (wave 0 descending, the
-// others ascending), and wave 0 merges the others' chunks into its 64 best.
-// Entries of a past the result are left unspecified.
+// The min(n, 64) largest of n values in shared memory, sorted descending into
+// a[0..), by the block's waves with no block-wide network: wave w sorts the
+// 64-entry chunks w, w + (waves), ... in registers and keeps the 64 best of
+// them (a chunk sorted ascending merged into the best so far, descending);
+// the other waves leave their best in a, reversed, and wave 0 merges them
+// into its own. Entries of a past the result are left unspecified.
 __device__ void top64_sorted(uint64_t* a, int n) {
   const int w = static_cast<int>(threadIdx.x) / kWave;
   const int l = lane();
   const int nw = static_cast<int>(blockDim.x) / kWave;
+  const int nchunk = (n + kWave - 1) / kWave;
   uint64_t v = 0ull;
-  if (w * kWave < n) {  // uniform per wave
+  if (w < nchunk) {  // uniform per wave
     v = (w * kWave + l < n) ? a[w * kWave + l] : 0ull;
-    v = (w == 0) ? wave_sort_u64<true>(v) : wave_sort_u64<false>(v);
+    v = wave_sort_u64<true>(v);
+    for (int c = w + nw; c < nchunk; c += nw) {
+      const uint64_t b = (c * kWave + l < n) ? a[c * kWave + l] : 0ull;
+      v = wave_merge_top_u64(v, wave_sort_u64<false>(b));
+    }
   }
   __syncthreads();  // every chunk is read
-  if (w > 0 && w * kWave < n) a[w * kWave + l] = v;
+  if (w > 0 && w < nchunk) a[w * kWave + (kWave - 1 - l)] = v;  // ascending
   __syncthreads();
   if (w == 0) {
-    for (int q = 1; q < nw && q * kWave < n; ++q) v = wave_merge_top_u64(v, a[q * kWave + l]);
+    for (int q = 1; q < nw && q < nchunk; ++q) v = wave_merge_top_u64(v, a[q * kWave + l]);
     a[l] = v;
   }
   __syncthreads();
@@ -385,7 +395,7 @@ __device__ int union_topk(const uint32_t* __restrict__ mrow, const uint64_t* __r
   int n = sh.n;
   __syncthreads();
   if (n > Sh::kBufCap) return -1;
-  if (n > 256 && n > k) {
+  if (n > kTopChunkMax && n > k) {
     const uint64_t thr = block_kth_largest(sh.buf, n, k, sh);
     uint64_t* tmp = sh.hw;  // at least 2048 slots
     if (threadIdx.x == 0) sh.n = 0;
@@ -399,7 +409,7 @@ __device__ int union_topk(const uint32_t* __restrict__ mrow, const uint64_t* __r
     __syncthreads();
     n = k;
   }
-  // n <= 256 here (k <= 64): the k best sorted, without a block sort
+  // n <= kTopChunkMax here (k <= 64): the k best sorted, without a block sort
   top64_sorted(sh.buf, n);
   return n < k ? n : k;
 }
@@ -810,45 +820,48 @@ __device__ void full_topp_cut(const E* __restrict__ rowp, int V, bool aligned, c
 // passes: the first entry, in the order (key desc, id asc), at which the mass
 // inside the bucket reaches the remainder. For a list of at most one entry
 // per thread: a bitonic sort of the packed values (whose descending order is
-// that order), exchanges within a wave through lane shuffles and across
-// waves through LDS, then a prefix sum of the masses in sorted order; the
-// cut is the first entry whose running mass reaches the remainder. Called by
-// every thread with its entry (v = 0, w = 0 past the list: below every
-// packed value, which holds ~id in its low half); returns false when the
-// masses fall short of the remainder (not expected: the list holds the whole
-// bucket). The result is the same in every thread.
-__device__ bool sort_cut_from_list(const FullCut& fc, int n, uint64_t v, uint32_t w, uint32_t* mw,
-                                   FullSh& sh, RowDesc* d, uint32_t mode) {
+// that order), then a prefix sum of the masses in sorted order; the cut is
+// the first entry whose running mass reaches the remainder. The sort runs
+// each wave's 64 entries through an in-register network (runs of 64,
+// descending in even waves and ascending in odd ones), then merges runs of
+// 128, 256, ...: partner distances of 64 and more through LDS (two buffers
+// in turn, so one barrier per step), the last six steps inside the wave.
+// Masses are formed after the sort, from the keys. Called by every thread
+// with its entry (v = 0 past the list: below every packed value, which holds
+// ~id in its low half); xa and xb are two LDS buffers of blockDim entries.
+// Returns false when the masses fall short of the remainder (not expected:
+// the list holds the whole bucket). The result is the same in every thread.
+__device__ bool sort_cut_from_list(const FullCut& fc, int n, uint64_t v, const FullTerms& ft,
+                                   uint64_t* xa, uint64_t* xb, FullSh& sh, RowDesc* d,
+                                   uint32_t mode) {
   const int t = static_cast<int>(threadIdx.x);
+  const int wv = t / kWave;  // uniform per wave
   // only the first P entries (P the power of two >= n) need sorting: every
   // entry past them is padding, and so is every sorted entry past n
   const int P = n <= 1 ? 1 : 1 << (32 - __clz(n - 1));
-  for (int k = 2; k <= P; k <<= 1) {
-    for (int jj = k >> 1; jj > 0; jj >>= 1) {
-      uint64_t ov;
-      uint32_t ow;
-      if (jj >= kWave) {  // uniform
-        __syncthreads();  // every read of the previous exchange is done
-        sh.buf[t] = v;
-        mw[t] = w;
-        __syncthreads();
-        ov = sh.buf[t ^ jj];
-        ow = mw[t ^ jj];
-      } else {
-        ov = __shfl_xor(v, jj);
-        ow = __shfl_xor(w, jj);
-      }
-      // runs of k entries alternate descending / ascending; the lower
-      // index of each pair keeps the larger entry of a descending run
-      const bool desc = (t & k) == 0;
-      const bool lower = (t & jj) == 0;
-      if (lower == desc ? ov > v : ov < v) {
-        v = ov;
-        w = ow;
-      }
+  if (wv * kWave < P) v = (wv & 1) ? wave_sort_u64<false>(v) : wave_sort_u64<true>(v);
+  int step = 0;
+  for (int k = 2 * kWave; k <= P; k <<= 1) {
+    // runs of k entries alternate descending / ascending; the lower index of
+    // each pair keeps the larger entry of a descending run
+    const bool desc = (t & k) == 0;  // uniform per wave
+    for (int jj = k >> 1; jj >= kWave; jj >>= 1) {
+      uint64_t* x = (step++ & 1) ? xb : xa;
+      x[t] = v;
+      __syncthreads();  // (the other buffer's reads, a step ago, are done too)
+      const uint64_t o = x[t ^ jj];
+      const bool lower = (t & jj) == 0;  // uniform per wave
+      if (lower == desc ? o > v : o < v) v = o;
     }
+    v = desc ? wave_merge_steps<true>(v) : wave_merge_steps<false>(v);
   }
   // thread t holds the entry of rank t
+  uint32_t w = 0u;
+  if (v != 0ull) {
+    uint64_t wt;
+    int b;
+    w = ft.mass(key2f(pkey(v)), &wt, &b) ? static_cast<uint32_t>(wt) : 0u;
+  }
   uint64_t total;
   const uint64_t cum = block_scan_incl(static_cast<uint64_t>(w), sh.r64, &total);
   const int rank = block_sum(cum < fc.rem ? 1 : 0, sh.ri);  // the running mass is nondecreasing
@@ -1033,7 +1046,7 @@ __global__ __launch_bounds__(kFullThreads) void k_row_full(Job j) {
     const bool listed = fc.bucket >= 0 && got == fc.count && got > 0u &&
                         got <= static_cast<uint32_t>(FullSh::kBufCap);  // uniform
     if (listed) {
-      __shared__ uint32_t mw[kFullListCap];
+      __shared__ __align__(16) uint32_t mw[kFullListCap];
       // the draw then comes from the list and the gather pass's bests when
       // the gather pass drew over the ids above the bucket
       const uint32_t mode = j.fdraw ? kRowFullListed : kRowFullTopP;
@@ -1041,15 +1054,9 @@ __global__ __launch_bounds__(kFullThreads) void k_row_full(Job j) {
       const uint64_t* lst = j.flist + static_cast<size_t>(row) * kFullListCap;
       const FullTerms ft{m, c.mp};
       if (n <= kSortCutMax) {  // uniform
-        uint64_t v = 0ull;
-        uint32_t w = 0u;
-        if (static_cast<int>(threadIdx.x) < n) {
-          v = lst[threadIdx.x];
-          uint64_t wt;
-          int b;
-          w = ft.mass(key2f(pkey(v)), &wt, &b) ? static_cast<uint32_t>(wt) : 0u;
-        }
-        if (sort_cut_from_list(fc, n, v, w, mw, sh, d, mode)) return;  // uniform
+        const uint64_t v = static_cast<int>(threadIdx.x) < n ? lst[threadIdx.x] : 0ull;
+        if (sort_cut_from_list(fc, n, v, ft, sh.buf, reinterpret_cast<uint64_t*>(mw), sh, d, mode))
+          return;  // uniform
       } else {
         uint64_t lo = ~0ull, hi = 0ull;
         for (int i = threadIdx.x; i < n; i += blockDim.x) {

@@ -528,6 +528,19 @@ __device__ __forceinline__ uint64_t bitonic_step(uint64_t v) {
   const bool keep_max = __builtin_amdgcn_inverse_ballot_w64(kKeepMax);
   return (o > v) == keep_max ? o : v;
 }
+// The last six steps of a bitonic merge whose runs are longer than the wave:
+// a bitonic sequence over the 64 lanes comes out sorted (descending with
+// kDesc, else ascending).
+template <bool kDesc>
+__device__ __forceinline__ uint64_t wave_merge_steps(uint64_t v) {
+  v = bitonic_step<64, 32, kDesc>(v);
+  v = bitonic_step<64, 16, kDesc>(v);
+  v = bitonic_step<64, 8, kDesc>(v);
+  v = bitonic_step<64, 4, kDesc>(v);
+  v = bitonic_step<64, 2, kDesc>(v);
+  v = bitonic_step<64, 1, kDesc>(v);
+  return v;
+}
 // Sorts one u64 per lane across the wave in registers (lane 0 first).
 template <bool kDesc>
 __device__ __forceinline__ uint64_t wave_sort_u64(uint64_t v) {
@@ -558,14 +571,7 @@ __device__ __forceinline__ uint64_t wave_sort_u64(uint64_t v) {
 // descending: the lane-wise maxima form a bitonic sequence holding them,
 // which the last six steps sort.
 __device__ __forceinline__ uint64_t wave_merge_top_u64(uint64_t a_desc, uint64_t b_asc) {
-  uint64_t v = a_desc > b_asc ? a_desc : b_asc;
-  v = bitonic_step<64, 32, true>(v);
-  v = bitonic_step<64, 16, true>(v);
-  v = bitonic_step<64, 8, true>(v);
-  v = bitonic_step<64, 4, true>(v);
-  v = bitonic_step<64, 2, true>(v);
-  v = bitonic_step<64, 1, true>(v);
-  return v;
+  return wave_merge_steps<true>(a_desc > b_asc ? a_desc : b_asc);
 }
 
 // k-th largest (1-based, 1 <= k <= 64) of one uint32 per lane, every lane of
