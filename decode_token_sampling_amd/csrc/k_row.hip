@@ -26,6 +26,7 @@ namespace {
 constexpr int kLightThreads = 256;
 constexpr int kFullThreads = 1024;
 constexpr int kSortCutMax = kFullThreads;  // longest gathered list cut by the sort (one entry per thread)
+static_assert(kFullThreads <= kFullListCap, "every thread of the cut kernel has a list slot");
 // Longest candidate union whose k best come from per-wave chunk sorts alone
 // (four chunks per wave of the row kernel); longer ones are cut to the k-th
 // largest first.
@@ -50,7 +51,16 @@ struct RowSh {
   int32_t b32[4];
   int32_t toff[kMaxSegs + 1];  // per-segment offsets of a candidate union
 };
-using LightSh = RowSh<4096, 2048>;
+// Candidate slots of rows short enough to be loaded whole at the row kernel's
+// entry (segments x kSelCap), and the segments those rows may have.
+constexpr int kStageMax = 1024;
+constexpr int kStageSegs = kStageMax / kSelCap;
+struct LightSh : RowSh<4096, 2048> {
+  uint64_t stage[2][kStageMax];  // lists A and B, every slot of every segment
+  uint32_t segm[kStageSegs];     // each segment's meta word
+  uint32_t segk[2][kStageSegs];  // each segment's exact k-th key, per list
+  LsePart segl[kStageSegs];      // each segment's log-sum-exp partial
+};
 using FullSh = RowSh<kFullListCap, kBuckets>;
 
 __device__ __forceinline__ float scaled(float x, float T) { return (T == 1.0f) ? x : x / T; }
@@ -247,7 +257,7 @@ __device__ __forceinline__ void sort_desc(uint64_t* a, int n) {
 // them (a chunk sorted ascending merged into the best so far, descending);
 // the other waves leave their best in a, reversed, and wave 0 merges them
 // into its own. Entries of a past the result are left unspecified.
-__device__ void top64_sorted(uint64_t* a, int n) {
+__device__ __forceinline__ void top64_sorted(uint64_t* a, int n) {
   const int w = static_cast<int>(threadIdx.x) / kWave;
   const int l = lane();
   const int nw = static_cast<int>(blockDim.x) / kWave;
@@ -323,15 +333,50 @@ __device__ uint64_t block_kth_largest(const uint64_t* a, int n, int k, Sh& sh) {
   return prefix;
 }
 
+// union_topk for a row whose segments' words and candidate slots were loaded
+// into LDS at the kernel's entry (stage: every slot of every segment, valid
+// below each segment's count; segm and segk: the meta words and k-th keys):
+// the same entries are gathered, with no global load. Every thread reads the
+// few segments' words itself, so the early return is uniform.
+template <class Sh>
+__device__ int union_topk_staged(const uint64_t* stage, const uint32_t* segm, const uint32_t* segk,
+                                 int ntile, int shift, uint32_t ovf_flag, int k, Sh& sh) {
+  uint32_t ovf = 0u, lp = 0u;
+  for (int s = 0; s < ntile; ++s) {
+    ovf |= segm[s] & ovf_flag;
+    lp = segk[s] > lp ? segk[s] : lp;
+  }
+  if (ovf) return -1;
+  const uint64_t pstar = static_cast<uint64_t>(lp) << 32;
+  if (threadIdx.x == 0) sh.n = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < ntile * kSelCap; i += blockDim.x) {
+    const int c = static_cast<int>((segm[i / kSelCap] >> shift) & 0xffu);
+    const uint64_t v = stage[i];
+    if ((i % kSelCap) < c && v >= pstar && v != 0ull) {
+      const int pos = atomicAdd(&sh.n, 1);
+      if (pos < Sh::kBufCap) sh.buf[pos] = v;
+    }
+  }
+  __syncthreads();
+  const int n = sh.n;
+  __syncthreads();
+  if (n > Sh::kBufCap) return -1;
+  // n <= ntile * kSelCap <= kTopChunkMax: the k best sorted, without a block sort
+  top64_sorted(sh.buf, n);
+  return n < k ? n : k;
+}
+
 // The exact top k (order: key desc, id asc) of the union of one candidate list
 // over the row's tiles, sorted into sh.buf[0..min(k, total)). Returns the
 // count, or -1 when a tile overflowed or the union does not fit. Only entries
 // whose key reaches P* = the largest per-tile exact k-th key are gathered: that
 // tile alone holds k values >= P*, so no entry below it is in the row's top k.
 template <class Sh>
-__device__ int union_topk(const uint32_t* __restrict__ mrow, const uint64_t* __restrict__ crow,
-                          const uint32_t* __restrict__ kth_row, int ntile, int shift,
-                          uint32_t ovf_flag, int k, Sh& sh) {
+__device__ __forceinline__ int union_topk(const uint32_t* __restrict__ mrow,
+                                          const uint64_t* __restrict__ crow,
+                                          const uint32_t* __restrict__ kth_row, int ntile,
+                                          int shift, uint32_t ovf_flag, int k, Sh& sh) {
   // tile counts -> offsets (each thread owns consecutive tiles), and P*
   const int G = (ntile + blockDim.x - 1) / blockDim.x;
   int lc = 0, ovf = 0;
@@ -513,50 +558,117 @@ __global__ __launch_bounds__(kLightThreads) void k_row_light(Job j) {
   __shared__ LightSh sh;
   const int row = blockIdx.x;
   if (j.nseg == 1 && (j.meta[row] & kMetaFinal)) return;  // finished by the streaming pass
-  const Plan pl = plan_row(j, row);
-  const RowCfg& c = pl.c;
   const int ntile = j.nseg;  // candidate lists and partials come per segment
   const uint32_t* mrow = j.meta + static_cast<size_t>(row) * ntile;
   const uint64_t* crowA = j.candA + static_cast<size_t>(row) * ntile * kSelCap;
   const uint64_t* crowB = j.candB + static_cast<size_t>(row) * ntile * kSelCap;
   const uint32_t* kthA = j.kthA + static_cast<size_t>(row) * ntile;
   const uint32_t* kthB = j.kthB + static_cast<size_t>(row) * ntile;
+  const LsePart* lrow = j.lpart + static_cast<size_t>(row) * ntile;
   const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
   const bool aligned = j.aligned;
   const float nanv = __builtin_nanf("");
 
-  // flags over the tiles, and the row argmax when list A holds argmaxes
-  if (threadIdx.x == 0) sh.flags = 0u;
-  __syncthreads();
-  uint32_t fl = 0;
-  uint64_t top = 0;
-  for (int t = threadIdx.x; t < ntile; t += blockDim.x) {
-    const uint32_t m = mrow[t];
-    fl |= m;
-    if (pl.kA == 1 && (m & kMetaCountA)) {
-      const uint64_t v = crowA[static_cast<size_t>(t) * kSelCap];
-      top = v > top ? v : top;
+  // A row of few segments has every per-segment word and every candidate slot
+  // loaded here, before its parameters are known: the loads are independent,
+  // so their latencies overlap instead of following one another, and the
+  // steps below read LDS (stale slots past a segment's count included: they
+  // are never used).
+  const bool staged = ntile <= kStageSegs;  // uniform
+  const int t0 = static_cast<int>(threadIdx.x);
+  constexpr int kStagePer = kStageMax / kLightThreads;
+  uint64_t sa[kStagePer], sb[kStagePer];
+  uint32_t m0 = 0u, kA0 = 0u, kB0 = 0u;
+  LsePart lp0{-kInf, 0.0f};
+  if (staged) {
+    const bool lists_b = j.lse && j.k_lp > 0;
+#pragma unroll
+    for (int r = 0; r < kStagePer; ++r) {
+      const int i = t0 + r * kLightThreads;
+      sa[r] = i < ntile * kSelCap ? crowA[i] : 0ull;
+      sb[r] = (lists_b && i < ntile * kSelCap) ? crowB[i] : 0ull;
+    }
+    if (t0 < ntile) {
+      m0 = mrow[t0];
+      kA0 = kthA[t0];
+      kB0 = kthB[t0];
+      if (j.lse) lp0 = lrow[t0];
     }
   }
-  if (fl) atomicOr(&sh.flags, fl & (kMetaBadLogits | kMetaHasFinite));
-  top = block_max(top, sh.r64);  // also orders the atomicOr above
-  const bool bad_logits = (sh.flags & kMetaBadLogits) || !(sh.flags & kMetaHasFinite);
+  const Plan pl = plan_row(j, row);
+  const RowCfg& c = pl.c;
+  if (staged) {
+#pragma unroll
+    for (int r = 0; r < kStagePer; ++r) {
+      sh.stage[0][t0 + r * kLightThreads] = sa[r];
+      sh.stage[1][t0 + r * kLightThreads] = sb[r];
+    }
+    if (t0 < ntile) {
+      sh.segm[t0] = m0;
+      sh.segk[0][t0] = kA0;
+      sh.segk[1][t0] = kB0;
+      sh.segl[t0] = lp0;
+    }
+  }
 
-  // log-sum-exp from the tile partials
+  // flags over the tiles, the row argmax when list A holds argmaxes, and the
+  // log-sum-exp from the tile partials: a staged row's few segments are
+  // combined by every thread from LDS (in segment order, no block
+  // reductions), a longer row's by the block
+  uint32_t fl = 0;
+  uint64_t top = 0;
   float M = -kInf, logS = nanv;
-  if (j.lse) {
-    const LsePart* lrow = j.lpart + static_cast<size_t>(row) * ntile;
-    float lm = -kInf;
-    for (int t = threadIdx.x; t < ntile; t += blockDim.x) lm = fmaxf(lm, lrow[t].m);
-    M = block_max(lm, sh.rf);
-    float ls = 0.0f;
-    if (M > -kInf) {
-      for (int t = threadIdx.x; t < ntile; t += blockDim.x) {
-        const LsePart pt = lrow[t];
-        if (pt.m > -kInf) ls += pt.s * __expf(pt.m - M);
+  if (staged) {
+    __syncthreads();  // the staged words are visible
+    for (int t = 0; t < ntile; ++t) {
+      const uint32_t mt = sh.segm[t];
+      fl |= mt;
+      if (pl.kA == 1 && (mt & kMetaCountA)) {
+        const uint64_t v = sh.stage[0][t * kSelCap];
+        top = v > top ? v : top;
       }
     }
-    logS = logf(block_sum(ls, sh.rf));
+    if (j.lse) {
+      for (int t = 0; t < ntile; ++t) M = fmaxf(M, sh.segl[t].m);
+      float ls = 0.0f;
+      if (M > -kInf) {
+        for (int t = 0; t < ntile; ++t) {
+          const LsePart pt = sh.segl[t];
+          if (pt.m > -kInf) ls += pt.s * __expf(pt.m - M);
+        }
+      }
+      logS = logf(ls);
+    }
+  } else {
+    if (threadIdx.x == 0) sh.flags = 0u;
+    __syncthreads();
+    for (int t = threadIdx.x; t < ntile; t += blockDim.x) {
+      const uint32_t m = mrow[t];
+      fl |= m;
+      if (pl.kA == 1 && (m & kMetaCountA)) {
+        const uint64_t v = crowA[static_cast<size_t>(t) * kSelCap];
+        top = v > top ? v : top;
+      }
+    }
+    if (fl) atomicOr(&sh.flags, fl & (kMetaBadLogits | kMetaHasFinite));
+    top = block_max(top, sh.r64);  // also orders the atomicOr above
+    fl = sh.flags;
+    if (j.lse) {
+      float lm = -kInf;
+      for (int t = threadIdx.x; t < ntile; t += blockDim.x) lm = fmaxf(lm, lrow[t].m);
+      M = block_max(lm, sh.rf);
+      float ls = 0.0f;
+      if (M > -kInf) {
+        for (int t = threadIdx.x; t < ntile; t += blockDim.x) {
+          const LsePart pt = lrow[t];
+          if (pt.m > -kInf) ls += pt.s * __expf(pt.m - M);
+        }
+      }
+      logS = logf(block_sum(ls, sh.rf));
+    }
+  }
+  const bool bad_logits = (fl & kMetaBadLogits) || !(fl & kMetaHasFinite);
+  if (j.lse) {
     if (threadIdx.x == 0)
       j.rlse[row] = bad_logits ? make_float2(nanv, nanv) : make_float2(M, logS);
   }
@@ -587,7 +699,10 @@ __global__ __launch_bounds__(kLightThreads) void k_row_light(Job j) {
         kept = 1;
         if (mask_row && threadIdx.x == 0) atomicOr(&mask_row[id >> 5], 1u << (id & 31));
       } else if (c.mode == kModeKFast || c.mode == kModeKSlow) {
-        int n = (pl.kA > 1) ? union_topk(mrow, crowA, kthA, ntile, 0, kMetaOverflowA, c.k, sh) : -1;
+        int n = -1;
+        if (pl.kA > 1)
+          n = staged ? union_topk_staged(sh.stage[0], sh.segm, sh.segk[0], ntile, 0, kMetaOverflowA, c.k, sh)
+                     : union_topk(mrow, crowA, kthA, ntile, 0, kMetaOverflowA, c.k, sh);
         if (n < 0) n = slow_topk(rowp, j.V, aligned, c.T, c.k, sh);
         if (c.T == 1.0f) sorted_shared = n;
         if (n <= kWave) {
@@ -674,9 +789,15 @@ __global__ __launch_bounds__(kLightThreads) void k_row_light(Job j) {
       } else if (pl.shared && sorted_shared >= k) {
         n = sorted_shared;
       } else {
-        n = pl.shared
-                ? union_topk(mrow, crowA, kthA, ntile, 0, kMetaOverflowA, k, sh)
-                : union_topk(mrow, crowB, kthB, ntile, kMetaCountBShift, kMetaOverflowB, k, sh);
+        if (staged)
+          n = pl.shared ? union_topk_staged(sh.stage[0], sh.segm, sh.segk[0], ntile, 0, kMetaOverflowA,
+                                            k, sh)
+                        : union_topk_staged(sh.stage[1], sh.segm, sh.segk[1], ntile,
+                                            kMetaCountBShift, kMetaOverflowB, k, sh);
+        else
+          n = pl.shared
+                  ? union_topk(mrow, crowA, kthA, ntile, 0, kMetaOverflowA, k, sh)
+                  : union_topk(mrow, crowB, kthB, ntile, kMetaCountBShift, kMetaOverflowB, k, sh);
         if (n < 0) n = slow_topk(rowp, j.V, aligned, lse_T(j, row), k, sh);
       }
       for (int i = threadIdx.x; i < k; i += blockDim.x) {
@@ -836,6 +957,32 @@ __device__ bool sort_cut_from_list(const FullCut& fc, int n, uint64_t v, const F
                                    uint32_t mode) {
   const int t = static_cast<int>(threadIdx.x);
   const int wv = t / kWave;  // uniform per wave
+  if (n <= kWave) {  // uniform: one wave sorts, scans and cuts; one barrier shares the outcome
+    if (wv == 0) {
+      v = wave_sort_u64<true>(v);
+      uint32_t w = 0u;
+      if (v != 0ull) {
+        uint64_t wt;
+        int b;
+        w = ft.mass(key2f(pkey(v)), &wt, &b) ? static_cast<uint32_t>(wt) : 0u;
+      }
+      // masses (at most 2^31) scanned as 16-bit halves, whose sums over 64
+      // lanes fit in 32 bits
+      const uint32_t lo = wave_scan_incl_u32(w & 0xffffu);
+      const uint32_t hi = wave_scan_incl_u32(w >> 16);
+      const uint64_t cum = (static_cast<uint64_t>(hi) << 16) + lo;
+      const int rank = __popcll(__ballot(cum < fc.rem));  // the running mass is nondecreasing
+      if (rank < n && lane() == rank) {
+        d->mode = mode;
+        d->tau = pkey(v);
+        d->id_cut = pid(v);
+        d->kept = static_cast<int32_t>(fc.above_c) + rank + 1;
+      }
+      if (lane() == 0) sh.b32[3] = rank < n ? 1 : 0;
+    }
+    __syncthreads();
+    return sh.b32[3] != 0;
+  }
   // only the first P entries (P the power of two >= n) need sorting: every
   // entry past them is padding, and so is every sorted entry past n
   const int P = n <= 1 ? 1 : 1 << (32 - __clz(n - 1));
@@ -1034,15 +1181,21 @@ __global__ __launch_bounds__(kFullThreads) void k_row_full(Job j) {
   __shared__ FullSh sh;
   const int row = blockIdx.x;
   RowDesc* d = j.desc + row;
-  if (d->mode != kRowFull) return;  // uniform over the block
-  const RowCfg c = load_cfg(row, j.V, j.T, j.k, j.p, j.mp, j.seeds);
+  // every load the row may need is issued before any is used (the cut record
+  // and this thread's list slot are read whatever the row's mode, and used
+  // only for rows with a cut): their latencies overlap
+  const uint32_t mode0 = d->mode;
   const float m = d->m;
+  const FullCut fc = j.fcut[row];
+  const uint32_t got = j.fcnt[row];
+  const uint64_t* lst = j.flist + static_cast<size_t>(row) * kFullListCap;
+  const uint64_t v0 = lst[threadIdx.x];  // (kFullThreads <= kFullListCap)
+  const RowCfg c = load_cfg(row, j.V, j.T, j.k, j.p, j.mp, j.seeds);
+  if (mode0 != kRowFull) return;  // uniform over the block
   if (c.p < 1.0f) {
     // the gathered list, when it holds the whole cut bucket: a short list
     // (one entry per thread) sorted and cut by the whole workgroup, a longer
     // one loaded with its masses into LDS for the workgroup's radix select
-    const FullCut fc = j.fcut[row];
-    const uint32_t got = j.fcnt[row];
     const bool listed = fc.bucket >= 0 && got == fc.count && got > 0u &&
                         got <= static_cast<uint32_t>(FullSh::kBufCap);  // uniform
     if (listed) {
@@ -1051,10 +1204,9 @@ __global__ __launch_bounds__(kFullThreads) void k_row_full(Job j) {
       // the gather pass drew over the ids above the bucket
       const uint32_t mode = j.fdraw ? kRowFullListed : kRowFullTopP;
       const int n = static_cast<int>(got);
-      const uint64_t* lst = j.flist + static_cast<size_t>(row) * kFullListCap;
       const FullTerms ft{m, c.mp};
       if (n <= kSortCutMax) {  // uniform
-        const uint64_t v = static_cast<int>(threadIdx.x) < n ? lst[threadIdx.x] : 0ull;
+        const uint64_t v = static_cast<int>(threadIdx.x) < n ? v0 : 0ull;
         if (sort_cut_from_list(fc, n, v, ft, sh.buf, reinterpret_cast<uint64_t*>(mw), sh, d, mode))
           return;  // uniform
       } else {
