@@ -1022,70 +1022,130 @@ __device__ bool sort_cut_from_list(const FullCut& fc, int n, uint64_t v, const F
   return true;
 }
 
-// The same select over the whole workgroup, for long lists (each round's
-// counting spread over every wave, at the price of a few barriers a round).
-// Called by every thread; the result is the same in every thread.
+// The same select over the whole workgroup, for long lists: a radix select on
+// the packed values, with 10-bit digits taken just below the highest bit in
+// which the remaining entries still differ (bits they all share are skipped:
+// the bitwise AND and OR of the chosen digit's entries give the next such
+// bit). Each round is one counting pass over the list by every wave and one
+// scan of the digits' masses by wave 0. Called by every thread; the result is
+// the same in every thread. lo and hi: the list's smallest and largest entry.
 __device__ bool block_cut_from_list(const FullCut& fc, int n, uint64_t lo, uint64_t hi,
                                     const uint32_t* mw, FullSh& sh, RowDesc* d, uint32_t mode) {
+  constexpr int kDig = 10;
+  constexpr int kBins = 1 << kDig;
+  constexpr int kPerLane = kBins / kWave;
+  static_assert(3 * kBins <= FullSh::kBinCap && kBins <= FullSh::kBinCap, "digit tables");
+  uint64_t* bw = sh.hw;               // each digit's mass
+  uint64_t* band = sh.hw + kBins;     // the AND of its entries
+  uint64_t* bor = sh.hw + 2 * kBins;  // their OR
+  uint32_t* bc = sh.hc;               // their count
   uint64_t rem = fc.rem;
   int rank = 0;
   uint64_t cutv = hi;
-  if (lo != hi) {
-    int shift = ((63 - __clzll(lo ^ hi)) / 8) * 8;
-    uint64_t pmask = (shift + 8 >= 64) ? 0ull : (~0ull << (shift + 8));
-    uint64_t prefix = hi & pmask;
-    for (;;) {  // every condition below is uniform over the block
-      for (int i = threadIdx.x; i < 256; i += blockDim.x) {
-        sh.hw[i] = 0ull;
-        sh.hc[i] = 0u;
+  uint64_t diff = lo ^ hi;  // the bits in which the remaining entries differ
+  uint64_t same = hi;       // (their common bits, above the highest of those)
+  const int t = static_cast<int>(threadIdx.x);
+  while (diff != 0ull) {  // uniform
+    const int hb = 63 - __clzll(diff);
+    const int shift = hb >= kDig - 1 ? hb - (kDig - 1) : 0;
+    const uint64_t pmask = hb >= 63 ? 0ull : (~0ull << (hb + 1));
+    const uint64_t prefix = same & pmask;
+    for (int i = t; i < kBins; i += blockDim.x) {
+      bw[i] = 0ull;
+      band[i] = ~0ull;
+      bor[i] = 0ull;
+      bc[i] = 0u;
+    }
+    if (t == 0) sh.b32[0] = -1;
+    __syncthreads();
+    // (whole waves per step: when every counted entry of a wave falls in one
+    // digit, as when the entries share their key, the wave combines them and
+    // one lane updates the digit, instead of 64 atomics on one address)
+#pragma unroll 1
+    for (int i0 = 0; i0 < n; i0 += blockDim.x) {
+      const int i = i0 + t;
+      const uint64_t v = i < n ? sh.buf[i] : 0ull;
+      const bool in = i < n && (v & pmask) == prefix;
+      const int dg = static_cast<int>((v >> shift) & (kBins - 1));
+      const uint64_t vb = __ballot(in);
+      if (vb == 0ull) continue;  // uniform per wave
+      const int first = __ffsll(static_cast<unsigned long long>(vb)) - 1;
+      const int d0 = __builtin_amdgcn_readlane(dg, first);
+      const uint64_t w = in ? static_cast<uint64_t>(mw[i]) : 0ull;
+      if (__ballot(in && dg != d0) == 0ull) {  // uniform per wave
+        const uint64_t ws = wave_sum(w);
+        const uint64_t wa = wave_reduce(in ? v : ~0ull, [](uint64_t a, uint64_t b) { return a & b; });
+        const uint64_t wo = wave_reduce(in ? v : 0ull, [](uint64_t a, uint64_t b) { return a | b; });
+        if (lane() == first) {
+          atomicAdd(reinterpret_cast<unsigned long long*>(&bw[d0]), static_cast<unsigned long long>(ws));
+          atomicAdd(&bc[d0], static_cast<uint32_t>(__popcll(vb)));
+          atomicAnd(reinterpret_cast<unsigned long long*>(&band[d0]), static_cast<unsigned long long>(wa));
+          atomicOr(reinterpret_cast<unsigned long long*>(&bor[d0]), static_cast<unsigned long long>(wo));
+        }
+      } else if (in) {
+        atomicAdd(reinterpret_cast<unsigned long long*>(&bw[dg]), static_cast<unsigned long long>(w));
+        atomicAdd(&bc[dg], 1u);
+        atomicAnd(reinterpret_cast<unsigned long long*>(&band[dg]), static_cast<unsigned long long>(v));
+        atomicOr(reinterpret_cast<unsigned long long*>(&bor[dg]), static_cast<unsigned long long>(v));
       }
-      if (threadIdx.x == 0) sh.b32[0] = -1;
-      __syncthreads();
-      for (int i = threadIdx.x; i < n; i += blockDim.x) {
-        const uint64_t v = sh.buf[i];
-        if ((v & pmask) == prefix) {
-          const int dg = static_cast<int>((v >> shift) & 255u);
-          atomicAdd(reinterpret_cast<unsigned long long*>(&sh.hw[dg]),
-                    static_cast<unsigned long long>(mw[i]));
-          atomicAdd(&sh.hc[dg], 1u);
+    }
+    __syncthreads();
+    if (t < kWave) {
+      // lane l scans the digits kBins - 1 - (kPerLane l + q), q = 0.., largest
+      // first; an exclusive scan over the lanes gives each lane's start
+      const int l = t;
+      uint64_t lw = 0ull;
+      uint32_t lc = 0u;
+#pragma unroll 4
+      for (int q = 0; q < kPerLane; ++q) {
+        const int dg = kBins - 1 - (l * kPerLane + q);
+        lw += bw[dg];
+        lc += bc[dg];
+      }
+      uint64_t sw = lw;
+      uint32_t scn = lc;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const uint64_t yw = __shfl_up(sw, o);
+        const uint32_t yc = __shfl_up(scn, o);
+        if (l >= o) {
+          sw += yw;
+          scn += yc;
         }
       }
-      __syncthreads();
-      // thread t < 256 holds digit 255 - t (largest digits first)
-      const int t = static_cast<int>(threadIdx.x);
-      const uint64_t w = t < 256 ? sh.hw[255 - t] : 0ull;
-      const int cn = t < 256 ? static_cast<int>(sh.hc[255 - t]) : 0;
-      uint64_t tw;
-      int tc;
-      const uint64_t wb = block_scan_incl(w, sh.r64, &tw) - w;
-      const int cb = block_scan_incl(cn, sh.ri, &tc) - cn;
-      if (t < 256 && cn > 0 && wb < rem && rem <= wb + w) {
-        sh.b32[0] = 255 - t;
-        sh.b32[1] = cb;
-        sh.b32[2] = cn;
-        sh.b64[0] = wb;
+      uint64_t wb = sw - lw;
+      uint32_t cb = scn - lc;
+#pragma unroll 4
+      for (int q = 0; q < kPerLane; ++q) {
+        const int dg = kBins - 1 - (l * kPerLane + q);
+        const uint64_t w = bw[dg];
+        const uint32_t cn = bc[dg];
+        if (cn > 0u && wb < rem && rem <= wb + w) {  // one digit of one lane
+          sh.b32[0] = dg;
+          sh.b32[1] = static_cast<int32_t>(cb);
+          sh.b32[2] = static_cast<int32_t>(cn);
+          sh.b64[0] = wb;
+          sh.b64[1] = band[dg];
+          sh.b64[2] = bor[dg];
+        }
+        wb += w;
+        cb += cn;
       }
-      __syncthreads();
-      const int dg = sh.b32[0];
-      const int above = sh.b32[1], cnt = sh.b32[2];
-      const uint64_t wabove = sh.b64[0];
-      __syncthreads();
-      if (dg < 0) return false;  // the list's masses fall short of the remainder
-      rem -= wabove;
-      rank += above;
-      prefix |= static_cast<uint64_t>(dg) << shift;
-      pmask |= 0xffull << shift;
-      if (cnt == 1) {
-        for (int i = threadIdx.x; i < n; i += blockDim.x)
-          if ((sh.buf[i] & pmask) == prefix) sh.b64[1] = sh.buf[i];
-        __syncthreads();
-        cutv = sh.b64[1];
-        __syncthreads();
-        break;
-      }
-      if (shift == 0) return false;  // distinct entries: unreachable
-      shift -= 8;
     }
+    __syncthreads();
+    const int dg = sh.b32[0];
+    const int above = sh.b32[1], cnt = sh.b32[2];
+    const uint64_t wabove = sh.b64[0], dand = sh.b64[1], dor = sh.b64[2];
+    __syncthreads();  // every thread has read the round's result
+    if (dg < 0) return false;  // the list's masses fall short of the remainder
+    rem -= wabove;
+    rank += above;
+    if (cnt == 1) {
+      cutv = dand;
+      break;
+    }
+    diff = dand ^ dor;  // nonzero: the entries are distinct
+    same = dand;
   }
   if (threadIdx.x == 0) {
     d->mode = mode;
@@ -1212,7 +1272,7 @@ __global__ __launch_bounds__(kFullThreads) void k_row_full(Job j) {
       } else {
         uint64_t lo = ~0ull, hi = 0ull;
         for (int i = threadIdx.x; i < n; i += blockDim.x) {
-          const uint64_t v = lst[i];
+          const uint64_t v = static_cast<int>(threadIdx.x) == i ? v0 : lst[i];
           uint64_t w;
           int b;
           if (!ft.mass(key2f(pkey(v)), &w, &b)) w = 0;
