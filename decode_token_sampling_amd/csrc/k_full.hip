@@ -369,6 +369,18 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
   uint64_t* lst = j.flist + static_cast<size_t>(row) * kFullListCap;
   uint32_t* cnt = j.fcnt + row;
   uint32_t n_above = 0, n_hit = 0;
+  // Every id of the cut bucket is a member (e >= min_p and a positive mass)
+  // when the bucket's lowest t already is: t > -(b* + 1) / kFullPerUnit up to
+  // the rounding of the bucket's product, and E is nondecreasing, so E at a t
+  // just below that bound is a lower bound on each id's e. Then no id needs
+  // its own exponential; else (a bucket at the min-p or zero-mass edge, or
+  // the last bucket, which holds every smaller t) each id is tested.
+  bool bucket_in = false;
+  if (bstar < kFullBuckets - 1) {
+    const float t_lo = -static_cast<float>(bstar + 1) / kFullPerUnit * (1.0f + 0x1p-20f);
+    const float e_lo = pinned_exp(t_lo);
+    bucket_in = e_lo >= c.mp && mass_of(e_lo) != 0ull;
+  }
   constexpr int EPV = SegReader<E, kGU>::EPV;
 
   // The draw over the ids above the cut bucket (kDraw). A thread skips the
@@ -392,7 +404,8 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
   };
   // the score of an above id whose random word b passed the integer test,
   // unless a finer test shows it cannot beat the bound
-  const auto score = [&](int id, float sv, uint64_t b) {
+  // (share: a new best of the thread is offered to the workgroup's bound)
+  const auto score = [&](int id, float sv, uint64_t b, bool share) {
     const double u = uniform_of_bits(b);
     const double one_u = (1.0 - u) * (1.0 - 0x1p-50);  // rounded down past any rounding error
     if (one_u >= lim) return;                          // e <= 1: below the bound
@@ -402,9 +415,11 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
     if (g > best || (g == best && id < best_id)) {
       best = g;
       best_id = id;
-      atomicMax(reinterpret_cast<unsigned long long*>(&s_best),
-                static_cast<unsigned long long>(__double_as_longlong(g)));
-      refresh();
+      if (share) {
+        atomicMax(reinterpret_cast<unsigned long long*>(&s_best),
+                  static_cast<unsigned long long>(__double_as_longlong(g)));
+        refresh();
+      }
     }
   };
   const auto above = [&](float sv) {
@@ -413,13 +428,22 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
   };
   if constexpr (kDraw) {
     // one id per thread first (the first of its first vector, when above),
-    // so that the workgroup starts from the best of up to 1024 scores
+    // so that the workgroup starts from the best of up to 1024 scores, taken
+    // by a block maximum (not by 1024 atomics on one LDS word)
     if (static_cast<int>(threadIdx.x) < rd.nvec) {  // its first vector is in flight
       float x[EPV];
       unpack16(rd.raw[0], x, rowp);
       const int id = lo + static_cast<int>(threadIdx.x) * EPV;
       const float sv = c.T == 1.0f ? x[0] : x[0] / c.T;
-      if (above(sv)) score(id, sv, random_bits(rs, id));
+      if (above(sv)) score(id, sv, random_bits(rs, id), false);
+    }
+    const double wb = wave_max(best);
+    if (lane() == 0) sd[threadIdx.x / kWave] = wb;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      double bb = sd[0];
+      for (int i = 1; i < kThreads / kWave; ++i) bb = sd[i] > bb ? sd[i] : bb;
+      if (bb > 0.0) s_best = static_cast<uint64_t>(__double_as_longlong(bb));
     }
     __syncthreads();
     refresh();
@@ -461,38 +485,59 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
           // scoring code serves every position of the vector
           for (uint32_t nb = need; nb != 0u; nb &= nb - 1u) {
             const int id = id0 + __builtin_ctz(nb);
-            score(id, scaled_by<decltype(div)::value>(to_f32(rowp[id]), c.T), random_bits(rs, id));
+            score(id, scaled_by<decltype(div)::value>(to_f32(rowp[id]), c.T), random_bits(rs, id), true);
           }
         }
       }
       if (__ballot(hm != 0u)) {  // uniform; few vectors hold cut-bucket ids
+        uint32_t hits = hm;
+        if (!bucket_in) {  // uniform
 #pragma unroll
-        for (int q = 0; q < EPV; ++q) {
-          bool hit = (hm >> q) & 1u;
-          if (hit) {
-            uint64_t wt;
-            int bb;
-            hit = ft.mass(sv[q], &wt, &bb);  // the histogram's membership (e >= min_p, mass > 0)
+          for (int q = 0; q < EPV; ++q) {
+            if ((hits >> q) & 1u) {
+              uint64_t wt;
+              int bb;
+              // the histogram's membership (e >= min_p, mass > 0)
+              if (!ft.mass(sv[q], &wt, &bb)) hits &= ~(1u << q);
+            }
           }
-          n_hit += hit ? 1u : 0u;
-          const uint64_t bal = __ballot(hit);
-          if (bal) {
-            const int first = __ffsll(static_cast<unsigned long long>(bal)) - 1;
-            const uint32_t nb = static_cast<uint32_t>(__popcll(bal));
-            uint32_t at = 0;
-            if (lane() == first) at = atomicAdd(&s_n, nb);
-            at = __builtin_amdgcn_readlane(at, first);
-            if (at + nb <= static_cast<uint32_t>(kGatherBuf)) {  // uniform
-              if (hit) sbuf[at + lanes_below(bal)] = pack(f2key(sv[q]), id0 + q);
-            } else {
-              uint32_t base = 0;
-              if (lane() == first) {
-                atomicMin(&s_lim, at);
-                base = atomicAdd(cnt, nb);
+        }
+        // one reservation for the wave's hits of this vector (lanes past the
+        // segment's end may be inactive here: the counts go through ballots,
+        // one per bit of a lane's count, and the first active lane reserves)
+        const uint32_t nh = static_cast<uint32_t>(__popc(hits));
+        n_hit += nh;
+        uint32_t before = 0u, tot = 0u;
+#pragma unroll
+        for (int bit = 0; bit < 4; ++bit) {  // nh <= EPV <= 8
+          const uint64_t bb = __ballot((nh >> bit) & 1u);
+          before += static_cast<uint32_t>(lanes_below(bb)) << bit;
+          tot += static_cast<uint32_t>(__popcll(bb)) << bit;
+        }
+        if (tot) {  // uniform
+          const int lead = __ffsll(static_cast<unsigned long long>(__ballot(true))) - 1;
+          uint32_t at = 0;
+          if (lane() == lead) at = atomicAdd(&s_n, tot);
+          at = __builtin_amdgcn_readlane(at, lead);
+          uint32_t pos = before;
+          if (at + tot <= static_cast<uint32_t>(kGatherBuf)) {  // uniform
+            pos += at;
+#pragma unroll
+            for (int q = 0; q < EPV; ++q)
+              if ((hits >> q) & 1u) sbuf[pos++] = pack(f2key(sv[q]), id0 + q);
+          } else {
+            uint32_t base = 0;
+            if (lane() == lead) {
+              atomicMin(&s_lim, at);
+              base = atomicAdd(cnt, tot);
+            }
+            pos += __builtin_amdgcn_readlane(base, lead);
+#pragma unroll
+            for (int q = 0; q < EPV; ++q) {
+              if ((hits >> q) & 1u) {
+                if (pos < static_cast<uint32_t>(kFullListCap)) lst[pos] = pack(f2key(sv[q]), id0 + q);
+                ++pos;
               }
-              base = __builtin_amdgcn_readlane(base, first);
-              const uint32_t pos = base + static_cast<uint32_t>(lanes_below(bal));
-              if (hit && pos < static_cast<uint32_t>(kFullListCap)) lst[pos] = pack(f2key(sv[q]), id0 + q);
             }
           }
         }

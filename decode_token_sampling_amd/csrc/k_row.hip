@@ -1060,10 +1060,13 @@ __device__ bool block_cut_from_list(const FullCut& fc, int n, uint64_t lo, uint6
     __syncthreads();
     // (whole waves per step: when every counted entry of a wave falls in one
     // digit, as when the entries share their key, the wave combines them and
-    // one lane updates the digit, instead of 64 atomics on one address)
+    // one lane updates the digit, instead of 64 atomics on one address; the
+    // lanes of a wave take entries 67 apart, a permutation of each 1024, so
+    // that neighbouring entries, often neighbouring ids, spread over waves)
+    static_assert(kFullThreads == 1024, "the entry permutation covers 1024 threads");
 #pragma unroll 1
-    for (int i0 = 0; i0 < n; i0 += blockDim.x) {
-      const int i = i0 + t;
+    for (int i0 = 0; i0 < n; i0 += kFullThreads) {
+      const int i = i0 + ((t * 67) & (kFullThreads - 1));
       const uint64_t v = i < n ? sh.buf[i] : 0ull;
       const bool in = i < n && (v & pmask) == prefix;
       const int dg = static_cast<int>((v >> shift) & (kBins - 1));
