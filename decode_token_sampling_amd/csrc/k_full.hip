@@ -422,10 +422,15 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
       }
     }
   };
-  const auto above = [&](float sv) {
-    const float t = sv - m;
-    return t == t && FullTerms::bucket_of(t) < bstar;
-  };
+  // The bucket of t is floor(-t kFullPerUnit) (a power of two: the product is
+  // exact), capped at the last bucket, so bucket < b* is t > -b* / kFullPerUnit
+  // and bucket == b* is -(b* + 1) / kFullPerUnit < t <= -b* / kFullPerUnit
+  // (the lower end open for the last bucket; a NaN t fails both): two compares
+  // against exact bounds instead of the bucket's arithmetic.
+  const float t_above = -static_cast<float>(bstar) / kFullPerUnit;
+  const float t_floor =
+      bstar < kFullBuckets - 1 ? -static_cast<float>(bstar + 1) / kFullPerUnit : -kInf;
+  const auto above = [&](float sv) { return sv - m > t_above; };
   if constexpr (kDraw) {
     // one id per thread first (the first of its first vector, when above),
     // so that the workgroup starts from the best of up to 1024 scores, taken
@@ -458,9 +463,11 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
       for (int q = 0; q < EPV; ++q) {
         sv[q] = scaled_by<decltype(div)::value>(x[q], c.T);
         const float t = sv[q] - m;
-        const int b = (t == t && q < n) ? FullTerms::bucket_of(t) : kFullBuckets;
-        am |= b < bstar ? 1u << q : 0u;
-        hm |= b == bstar ? 1u << q : 0u;
+        // (positions past n hold -inf: in no bucket by these bounds either,
+        // except the last, whose ids the membership test below drops)
+        const bool in = q < n;
+        am |= (in && t > t_above) ? 1u << q : 0u;
+        hm |= (in && t <= t_above && t > t_floor) ? 1u << q : 0u;
       }
       n_above += __popc(am);
       if constexpr (kDraw) {
