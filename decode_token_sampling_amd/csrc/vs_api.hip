@@ -350,7 +350,7 @@ vs_status sample_logprobs_impl(const PenArgs* pen, const void* logits, int dt, i
   // batches
   const bool gather_draw =
       (hints & VS_OPT_TOPP_GATHER_DRAW) ||
-      (!(hints & VS_OPT_TOPP_KEPT_PASS) && static_cast<int64_t>(B) * V >= (int64_t{1} << 23));
+      (!(hints & VS_OPT_TOPP_KEPT_PASS) && static_cast<int64_t>(B) * V >= (int64_t{1} << 22));
   j.fdraw = (!j.topp_reject && !out_kept_mask && gather_draw) ? 1 : 0;
   j.T = temperature;
   j.k = top_k;

@@ -94,7 +94,7 @@ typedef enum vs_status {
  *    bucket; no pass over the kept set (unless the bucket overflowed its list).
  *  VS_OPT_TOPP_KEPT_PASS: the Gumbel pass over the kept set after the cut.
  * Without one of them (or with more than one: the first listed wins), the
- * gather draw is taken when B * V >= 2^23 and the kept-set pass otherwise,
+ * gather draw is taken when B * V >= 2^22 and the kept-set pass otherwise,
  * the faster of the two on the measured workloads on each side. */
 #define VS_OPT_TOPP_REJECTION 256u
 #define VS_OPT_TOPP_GATHER_DRAW 512u
