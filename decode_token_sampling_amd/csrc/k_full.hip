@@ -54,23 +54,42 @@ __device__ __forceinline__ bool topp_row(const Job& j, int row, RowCfg* c, float
 // the workgroup does its set-up; visit() then calls f(id0, x, n) for every
 // vector (x[c] the value of id id0 + c, c < n; the rest -inf), all lanes of
 // a wave together in the vector loop, with the next U vectors' loads issued
-// before the current ones are used.
+// before the current ones are used. Two ways to hand out the vectors:
+// statically (thread t takes t, t + kThreads, ...), or, for segments of at
+// least kDynChunks chunks per wave when the caller asks for it, in chunks of
+// U vectors per lane that each wave claims from an LDS counter as it starts
+// the previous one (wave w starts with chunk w; a wave that runs ahead takes
+// more chunks, so the waves end together). The counter is set by start() and
+// published by a barrier of the caller's before visit().
 template <typename E, int U>
 struct SegReader {
   static constexpr int EPV = Epv<E>::n;
+  static constexpr int kChunk = kWave * U;  // vectors per claimed chunk
+  static constexpr int kDynChunks = 4;      // chunks per wave, at least, for the claimed hand-out
   const E* rowp;
   int lo, hi, nvec;
+  bool dyn;   // claimed chunks (uniform over the block)
+  int p;      // this thread's first vector of the current step
+  int* next;  // the next unclaimed chunk (LDS)
   uint4 raw[U];
 
-  __device__ __forceinline__ void start(const E* __restrict__ r, int l, int h, bool aligned) {
+  __device__ __forceinline__ int stride() const { return dyn ? kWave : kThreads; }
+
+  __device__ __forceinline__ void start(const E* __restrict__ r, int l, int h, bool aligned,
+                                        int* counter = nullptr) {
     rowp = r;
     lo = l;
     hi = h;
     nvec = aligned ? (h - l) / EPV : 0;
+    next = counter;
+    dyn = counter && nvec >= kDynChunks * (kThreads / kWave) * kChunk;
+    const int w = static_cast<int>(threadIdx.x) / kWave;
+    p = dyn ? w * kChunk + lane() : static_cast<int>(threadIdx.x);
+    if (dyn && threadIdx.x == 0) *counter = kThreads / kWave;
     const E* base = rowp + lo;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int i = static_cast<int>(threadIdx.x) + u * kThreads;
+      const int i = p + u * stride();
       if (i < nvec) raw[u] = load16(base + i * EPV);
     }
   }
@@ -78,16 +97,26 @@ struct SegReader {
   template <typename F>
   __device__ __forceinline__ void visit(F&& f) {
     const E* base = rowp + lo;
-    for (int i0 = static_cast<int>(threadIdx.x); i0 < nvec; i0 += U * kThreads) {
+    const int sd = stride();
+    // (claimed: the condition is uniform per wave, p's chunk being the wave's)
+    while (dyn ? (p - lane()) < nvec : p < nvec) {
+      int pn;
+      if (dyn) {
+        int c2 = 0;
+        if (lane() == 0) c2 = atomicAdd(next, 1);
+        pn = __builtin_amdgcn_readfirstlane(c2) * kChunk + lane();
+      } else {
+        pn = p + U * kThreads;
+      }
       uint4 nxt[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int i = i0 + (U + u) * kThreads;
+        const int i = pn + u * sd;
         if (i < nvec) nxt[u] = load16(base + i * EPV);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * kThreads;
+        const int i = p + u * sd;
         if (i < nvec) {
           float x[EPV];
           unpack16(raw[u], x, rowp);
@@ -96,6 +125,7 @@ struct SegReader {
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) raw[u] = nxt[u];
+      p = pn;
     }
     for (int q = lo + nvec * EPV + static_cast<int>(threadIdx.x); q < hi; q += kThreads) {
       float x[EPV];
@@ -303,6 +333,7 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
   __shared__ uint64_t sbuf[kGatherBuf];
   __shared__ uint32_t s_n, s_lim, s_base;
   __shared__ uint64_t s_best;  // bits of the best score any thread has found
+  __shared__ int s_chunk;      // the reader's next chunk, when claimed
   int row, seg;
   if (!xcd_row_tile(blockIdx.x, j.B, j.fseg, &row, &seg)) return;  // uniform per block
   RowCfg c;
@@ -315,7 +346,7 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
   // need the registers)
   constexpr int kGU = kDraw ? 2 : 4;
   SegReader<E, kGU> rd;
-  rd.start(rowp, lo, hi, j.aligned != 0);
+  rd.start(rowp, lo, hi, j.aligned != 0, &s_chunk);
   const uint64_t* ghw = j.fhw + static_cast<size_t>(row) * kFullBuckets;
 
   // The cut bucket: thread t holds buckets [4 t, 4 t + 4); an exclusive scan
@@ -435,10 +466,10 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
     // one id per thread first (the first of its first vector, when above),
     // so that the workgroup starts from the best of up to 1024 scores, taken
     // by a block maximum (not by 1024 atomics on one LDS word)
-    if (static_cast<int>(threadIdx.x) < rd.nvec) {  // its first vector is in flight
+    if (rd.p < rd.nvec) {  // its first vector is in flight
       float x[EPV];
       unpack16(rd.raw[0], x, rowp);
-      const int id = lo + static_cast<int>(threadIdx.x) * EPV;
+      const int id = lo + rd.p * EPV;
       const float sv = c.T == 1.0f ? x[0] : x[0] / c.T;
       if (above(sv)) score(id, sv, random_bits(rs, id), false);
     }
