@@ -83,6 +83,55 @@ __device__ __forceinline__ bool penalize_range(E* rowp, const PenRow& pr, int V,
                                                PenSh& ps, int NT) {
   constexpr uint32_t kEmpty = 0xffffffffu;
   const int L = pr.len();  // an upper bound on the range's distinct ids
+  const int n = L;
+  // The table in use: the smallest power of two of at least twice the
+  // history, between 2^10 and 2^kMaxLog2 slots (clearing and scanning it is
+  // most of the work for short histories).
+  int lgs = 10 < kMaxLog2 ? 10 : kMaxLog2;
+  while ((1 << lgs) < 2 * n && lgs < kMaxLog2) ++lgs;
+  const int S = 1 << lgs;
+  if (2 * n <= S) {  // uniform
+    // One class: the table holds every distinct id with half its slots to
+    // spare, so no probe sequence can fail. Clear, count, apply, with two
+    // barriers.
+    for (int i = threadIdx.x; i < S; i += NT) {
+      keys[i] = kEmpty;
+      counts[i] = 0u;
+    }
+    if (threadIdx.x == 0) ps.badid = 0;
+    __syncthreads();  // the table and the flag are clear
+    for (int i = threadIdx.x; i < L; i += NT) {
+      const int32_t id = pr.id(i);
+      if (check_bad && (id < 0 || id >= V)) ps.badid = 1;
+      if (pr.bad || id < lo || id >= hi) continue;
+      const uint32_t u = static_cast<uint32_t>(id);
+      uint32_t slot = (u * 0x2545F491u) >> (32 - lgs);
+      while (true) {
+        const uint32_t prev = atomicCAS(&keys[slot], kEmpty, u);
+        if (prev == kEmpty || prev == u) {
+          if (i >= pr.nign) atomicAdd(&counts[slot], 1u);
+          break;
+        }
+        slot = (slot + 1) & static_cast<uint32_t>(S - 1);
+      }
+    }
+    __syncthreads();  // every id is counted, the flag final
+    for (int i = threadIdx.x; i < S; i += NT) {
+      const uint32_t id = keys[i];
+      if (id == kEmpty) continue;
+      const uint32_t c = counts[i];
+      E* p = rowp + id;
+      const float x = to_f32(*p);
+      float y = (x >= 0.0f) ? x / pr.rep : x * pr.rep;
+      if (c > 0u) {
+        y = y - pr.pres;
+        const float fc = pr.freq * static_cast<float>(c);
+        y = y - fc;
+      }
+      store_penalised<E>(p, y);
+    }
+    return ps.badid != 0;
+  }
   if (threadIdx.x == 0) {
     ps.badid = 0;
     ps.top = 0;
@@ -94,13 +143,6 @@ __device__ __forceinline__ bool penalize_range(E* rowp, const PenRow& pr, int V,
       if (id < 0 || id >= V) ps.badid = 1;
     }
   }
-  const int n = L;
-  // The table in use: the smallest power of two of at least twice the
-  // history, between 2^10 and 2^kMaxLog2 slots (clearing and scanning it is
-  // most of the work for short histories).
-  int lgs = 10 < kMaxLog2 ? 10 : kMaxLog2;
-  while ((1 << lgs) < 2 * n && lgs < kMaxLog2) ++lgs;
-  const int S = 1 << lgs;
   if (threadIdx.x == 0 && !pr.bad && n > 0) {
     // start with enough classes for about half a table of ids each; push every
     // class of that level (in reverse so class 0 pops first); at most 32
