@@ -39,12 +39,20 @@ constexpr int kPer = kFullBuckets / kThreads;  // buckets per thread (4)
 constexpr int kGatherBuf = 2048;  // ids a gather workgroup collects in LDS before one global append
 
 // A full-vocabulary row whose top-p cut is still to be found.
-__device__ __forceinline__ bool topp_row(const Job& j, int row, RowCfg* c, float* m) {
-  const RowDesc d = j.desc[row];
-  if (d.mode != kRowFull) return false;
-  *c = load_cfg(row, j.V, j.T, j.k, j.p, j.mp, j.seeds);
-  *m = d.m;
-  return c->p < 1.0f;
+// d: the row's descriptor, which the row kernel wrote when it ran before this
+// pass (j.full_chain unset); else the row's route is found here.
+__device__ __forceinline__ bool topp_row(const Job& j, int row, const RowDesc& d,
+                                         const RoutePre& rp, RowCfg* c, float* m) {
+  if (!j.full_chain) {  // uniform
+    if (d.mode != kRowFull) return false;
+    *c = load_cfg(row, j.V, j.T, j.k, j.p, j.mp, j.seeds);
+    *m = d.m;
+    return c->p < 1.0f;
+  }
+  const RowRoute r = route_row(j, row, rp);
+  *c = r.c;
+  *m = r.m;
+  return r.full && r.c.p < 1.0f;
 }
 
 // Reads the ids [lo, hi) of a row with the whole block: 16-byte loads when
@@ -204,14 +212,18 @@ __global__ __launch_bounds__(kThreads) void k_full_hist(Job j) {
   __shared__ uint64_t s_bound;  // bits of the best known lower bound on the segment's kCandM-th score
   int row, seg;
   if (!xcd_row_tile(blockIdx.x, j.B, j.fseg, &row, &seg)) return;  // uniform per block
-  RowCfg c;
-  float m;
-  if (!topp_row(j, row, &c, &m)) return;  // uniform per block
   const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
   const int lo = seg * j.fseg_len;
   const int hi = min(j.V, lo + j.fseg_len);
+  // the route's loads, then the segment's first ones, before the row's route
+  // is known (wasted, and harmless, for a row this pass does not take)
+  const RowDesc dsc = j.desc[row];  // (the row kernel's, when it ran first)
+  const RoutePre rp = route_preload(j, row);
   SegReader<E, 4> rd;
   rd.start(rowp, lo, hi, j.aligned != 0);
+  RowCfg c;
+  float m;
+  if (!topp_row(j, row, dsc, rp, &c, &m)) return;  // uniform per block
   for (int i = threadIdx.x; i < kFullBuckets; i += kThreads) hw[i] = 0ull;
   if (threadIdx.x == 0) s_bound = 0ull;
   __syncthreads();
@@ -336,17 +348,19 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
   __shared__ int s_chunk;      // the reader's next chunk, when claimed
   int row, seg;
   if (!xcd_row_tile(blockIdx.x, j.B, j.fseg, &row, &seg)) return;  // uniform per block
-  RowCfg c;
-  float m;
-  if (!topp_row(j, row, &c, &m)) return;  // uniform per block
   const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
   const int lo = seg * j.fseg_len;
   const int hi = min(j.V, lo + j.fseg_len);
   // vectors in flight per thread (fewer with the draw, whose random words
-  // need the registers)
+  // need the registers); the first before the row's route is known
   constexpr int kGU = kDraw ? 2 : 4;
+  const RowDesc dsc = j.desc[row];  // (the row kernel's, when it ran first)
+  const RoutePre rp = route_preload(j, row);
   SegReader<E, kGU> rd;
   rd.start(rowp, lo, hi, j.aligned != 0, &s_chunk);
+  RowCfg c;
+  float m;
+  if (!topp_row(j, row, dsc, rp, &c, &m)) return;  // uniform per block
   const uint64_t* ghw = j.fhw + static_cast<size_t>(row) * kFullBuckets;
 
   // The cut bucket: thread t holds buckets [4 t, 4 t + 4); an exclusive scan

@@ -17,6 +17,11 @@
 // monotone in s), the bucket where the cumulative mass reaches top_p * total,
 // then the exact cut inside that bucket (gathered and sorted in LDS, or by a
 // mass-weighted radix select when the bucket holds more than 8192 ids).
+// When a call runs the full-vocabulary passes over 16 rows or more, the light
+// kernel is not launched: k_row_full does its work at entry (same code, same
+// results), the streaming pass clears the histogram counters, and every row is
+// routed to the full-vocabulary path from its tiles' flags and maxima alone
+// (route_row), so no row descriptor has to exist before the histogram pass.
 #include "vs_device.h"
 #include "vs_kernels.h"
 
@@ -339,8 +344,9 @@ __device__ uint64_t block_kth_largest(const uint64_t* a, int n, int k, Sh& sh) {
 // the same entries are gathered, with no global load. Every thread reads the
 // few segments' words itself, so the early return is uniform.
 template <class Sh>
-__device__ int union_topk_staged(const uint64_t* stage, const uint32_t* segm, const uint32_t* segk,
-                                 int ntile, int shift, uint32_t ovf_flag, int k, Sh& sh) {
+__device__ __forceinline__ int union_topk_staged(const uint64_t* stage, const uint32_t* segm,
+                                                 const uint32_t* segk, int ntile, int shift,
+                                                 uint32_t ovf_flag, int k, Sh& sh) {
   uint32_t ovf = 0u, lp = 0u;
   for (int s = 0; s < ntile; ++s) {
     ovf |= segm[s] & ovf_flag;
@@ -553,10 +559,52 @@ __device__ __forceinline__ float logit_at(const Job& j, int row, int id) {
   return to_f32(static_cast<const E*>(j.logits)[static_cast<int64_t>(row) * j.ld + id]);
 }
 
-template <typename E>
-__global__ __launch_bounds__(kLightThreads) void k_row_light(Job j) {
-  __shared__ LightSh sh;
-  const int row = blockIdx.x;
+// The loads the row kernel's work begins with (light_row), issued apart so
+// that a caller can start them before it knows the row's route. A row of few
+// segments has every per-segment word and every candidate slot loaded, before
+// its parameters are known: the loads are independent, so their latencies
+// overlap instead of following one another, and the steps that follow read
+// LDS (stale slots past a segment's count included: they are never used).
+// kPer: candidate slots per thread (kStageMax / the block size).
+template <int kPer>
+struct LightLoads {
+  uint64_t sa[kPer], sb[kPer];
+  uint32_t m0, kA0, kB0;
+  LsePart lp0;
+};
+template <int kPer>
+__device__ __forceinline__ void light_load(const Job& j, int row, LightLoads<kPer>& L) {
+  const int ntile = j.nseg;
+  const int t0 = static_cast<int>(threadIdx.x);
+  L.m0 = L.kA0 = L.kB0 = 0u;
+  L.lp0 = LsePart{-kInf, 0.0f};
+  if (ntile <= kStageSegs) {  // uniform
+    const size_t s0 = static_cast<size_t>(row) * ntile;
+    const uint64_t* crowA = j.candA + s0 * kSelCap;
+    const uint64_t* crowB = j.candB + s0 * kSelCap;
+    const bool lists_b = j.lse && j.k_lp > 0;
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int i = t0 + r * static_cast<int>(blockDim.x);
+      L.sa[r] = i < ntile * kSelCap ? crowA[i] : 0ull;
+      L.sb[r] = (lists_b && i < ntile * kSelCap) ? crowB[i] : 0ull;
+    }
+    if (t0 < ntile) {
+      L.m0 = j.meta[s0 + t0];
+      L.kA0 = j.kthA[s0 + t0];
+      L.kB0 = j.kthB[s0 + t0];
+      if (j.lse) L.lp0 = j.lpart[s0 + t0];
+    }
+  }
+}
+
+// The row kernel's work for one row (a block of kStageMax / kPer threads,
+// the loads of light_load in L): the row's draw, status, log-sum-exp and
+// log-probs from the streaming pass's per-segment words, for every row the
+// streaming pass did not finish and the full-vocabulary passes do not take.
+template <typename E, int kPer>
+__device__ __forceinline__ void light_row(const Job& j, int row, LightSh& sh,
+                                          const LightLoads<kPer>& L) {
   if (j.nseg == 1 && (j.meta[row] & kMetaFinal)) return;  // finished by the streaming pass
   const int ntile = j.nseg;  // candidate lists and partials come per segment
   const uint32_t* mrow = j.meta + static_cast<size_t>(row) * ntile;
@@ -568,45 +616,26 @@ __global__ __launch_bounds__(kLightThreads) void k_row_light(Job j) {
   const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
   const bool aligned = j.aligned;
   const float nanv = __builtin_nanf("");
-
-  // A row of few segments has every per-segment word and every candidate slot
-  // loaded here, before its parameters are known: the loads are independent,
-  // so their latencies overlap instead of following one another, and the
-  // steps below read LDS (stale slots past a segment's count included: they
-  // are never used).
   const bool staged = ntile <= kStageSegs;  // uniform
   const int t0 = static_cast<int>(threadIdx.x);
-  constexpr int kStagePer = kStageMax / kLightThreads;
-  uint64_t sa[kStagePer], sb[kStagePer];
-  uint32_t m0 = 0u, kA0 = 0u, kB0 = 0u;
-  LsePart lp0{-kInf, 0.0f};
-  if (staged) {
-    const bool lists_b = j.lse && j.k_lp > 0;
-#pragma unroll
-    for (int r = 0; r < kStagePer; ++r) {
-      const int i = t0 + r * kLightThreads;
-      sa[r] = i < ntile * kSelCap ? crowA[i] : 0ull;
-      sb[r] = (lists_b && i < ntile * kSelCap) ? crowB[i] : 0ull;
-    }
-    if (t0 < ntile) {
-      m0 = mrow[t0];
-      kA0 = kthA[t0];
-      kB0 = kthB[t0];
-      if (j.lse) lp0 = lrow[t0];
-    }
-  }
+  const int NT = static_cast<int>(blockDim.x);
+  const uint32_t m0 = L.m0;
+  const LsePart lp0 = L.lp0;
   const Plan pl = plan_row(j, row);
   const RowCfg& c = pl.c;
   if (staged) {
 #pragma unroll
-    for (int r = 0; r < kStagePer; ++r) {
-      sh.stage[0][t0 + r * kLightThreads] = sa[r];
-      sh.stage[1][t0 + r * kLightThreads] = sb[r];
+    for (int r = 0; r < kPer; ++r) {
+      const int i = t0 + r * NT;
+      if (i < kStageMax) {
+        sh.stage[0][i] = L.sa[r];
+        sh.stage[1][i] = L.sb[r];
+      }
     }
     if (t0 < ntile) {
       sh.segm[t0] = m0;
-      sh.segk[0][t0] = kA0;
-      sh.segk[1][t0] = kB0;
+      sh.segk[0][t0] = L.kA0;
+      sh.segk[1][t0] = L.kB0;
       sh.segl[t0] = lp0;
     }
   }
@@ -729,7 +758,11 @@ __global__ __launch_bounds__(kLightThreads) void k_row_light(Job j) {
         } else {
           next = kRowFull;
           if (threadIdx.x == 0) j.desc[row].m = m;
-          if (c.p < 1.0f) {  // the histogram and gather passes accumulate from zero
+          // the histogram and gather passes accumulate from zero (cleared
+          // here when they run after this kernel; with the cut kernel doing
+          // this work they have run already, after the streaming pass
+          // cleared their counters)
+          if (c.p < 1.0f && !j.full_chain) {
             uint64_t* hw = j.fhw + static_cast<size_t>(row) * kFullBuckets;
             for (int i = threadIdx.x; i < kFullBuckets; i += blockDim.x) hw[i] = 0ull;
             if (threadIdx.x == 0) {
@@ -829,9 +862,18 @@ __global__ __launch_bounds__(kLightThreads) void k_row_light(Job j) {
 }
 
 template <typename E>
-__device__ void full_topp_cut(const E* __restrict__ rowp, int V, bool aligned, const RowCfg& c,
-                              float m, FullSh& sh, RowDesc* d) {
-  const FullTerms ft{m, c.mp};
+__global__ __launch_bounds__(kLightThreads) void k_row_light(Job j) {
+  __shared__ LightSh sh;
+  const int row = static_cast<int>(blockIdx.x);
+  LightLoads<kStageMax / kLightThreads> L;
+  light_load(j, row, L);
+  light_row<E>(j, row, sh, L);
+}
+
+template <typename E>
+__device__ void full_topp_cut(const E* __restrict__ rowp, int V, bool aligned, float T, float p,
+                              float mp, float m, FullSh& sh, RowDesc* d) {
+  const FullTerms ft{m, mp};
   for (int i = threadIdx.x; i < kBuckets; i += blockDim.x) {
     sh.hw[i] = 0;
     sh.hc[i] = 0;
@@ -840,7 +882,7 @@ __device__ void full_topp_cut(const E* __restrict__ rowp, int V, bool aligned, c
   row_visit(rowp, V, aligned, [&](int, float x) {
     uint64_t w;
     int b;
-    if (ft.mass(scaled(x, c.T), &w, &b)) {
+    if (ft.mass(scaled(x, T), &w, &b)) {
       atomicAdd(reinterpret_cast<unsigned long long*>(&sh.hw[b]), static_cast<unsigned long long>(w));
       atomicAdd(&sh.hc[b], 1u);
     }
@@ -851,7 +893,7 @@ __device__ void full_topp_cut(const E* __restrict__ rowp, int V, bool aligned, c
   const uint64_t total = block_sum(lt, sh.r64);
   // The kept prefix is the shortest whose mass reaches thr; masses are
   // integers, so "cum >= thr" is "cum >= ceil(thr)".
-  const double thr = static_cast<double>(c.p) * static_cast<double>(total);
+  const double thr = static_cast<double>(p) * static_cast<double>(total);
   const uint64_t target = ceil(thr) >= 1.0 ? static_cast<uint64_t>(ceil(thr)) : 1ull;
   // Bucket 0 holds the largest s; hist_find_desc scans from the highest index
   // down, so present the buckets in reverse.
@@ -883,7 +925,7 @@ __device__ void full_topp_cut(const E* __restrict__ rowp, int V, bool aligned, c
     if (threadIdx.x == 0) sh.n = 0;
     __syncthreads();
     row_visit(rowp, V, aligned, [&](int jj, float x) {
-      const float s = scaled(x, c.T);
+      const float s = scaled(x, T);
       uint64_t w;
       int b;
       if (ft.mass(s, &w, &b) && b == bstar) {
@@ -923,10 +965,10 @@ __device__ void full_topp_cut(const E* __restrict__ rowp, int V, bool aligned, c
     kept = static_cast<int32_t>(ac) + cc + 1;
   } else {
     uint64_t wa, ca, wt;
-    radix_select(rowp, V, aligned, c.T, rem, in_bucket, sh, &tau, &wa, &ca, &wt);
+    radix_select(rowp, V, aligned, T, rem, in_bucket, sh, &tau, &wa, &ca, &wt);
     const uint64_t r2 = rem - wa;
     const uint64_t need = wt ? (r2 + wt - 1) / wt : 1;
-    idc = tie_cut(rowp, V, c.T, tau, need, in_bucket, sh);
+    idc = tie_cut(rowp, V, T, tau, need, in_bucket, sh);
     kept = static_cast<int32_t>(ac + ca + need);
   }
   if (threadIdx.x == 0) {
@@ -952,9 +994,10 @@ __device__ void full_topp_cut(const E* __restrict__ rowp, int V, bool aligned, c
 // ~id in its low half); xa and xb are two LDS buffers of blockDim entries.
 // Returns false when the masses fall short of the remainder (not expected:
 // the list holds the whole bucket). The result is the same in every thread.
-__device__ bool sort_cut_from_list(const FullCut& fc, int n, uint64_t v, const FullTerms& ft,
-                                   uint64_t* xa, uint64_t* xb, FullSh& sh, RowDesc* d,
-                                   uint32_t mode) {
+__device__ __forceinline__ bool sort_cut_from_list(const FullCut& fc, int n, uint64_t v,
+                                                   const FullTerms& ft, uint64_t* xa,
+                                                   uint64_t* xb, FullSh& sh, RowDesc* d,
+                                                   uint32_t mode) {
   const int t = static_cast<int>(threadIdx.x);
   const int wv = t / kWave;  // uniform per wave
   if (n <= kWave) {  // uniform: one wave sorts, scans and cuts; one barrier shares the outcome
@@ -1029,8 +1072,9 @@ __device__ bool sort_cut_from_list(const FullCut& fc, int n, uint64_t v, const F
 // bit). Each round is one counting pass over the list by every wave and one
 // scan of the digits' masses by wave 0. Called by every thread; the result is
 // the same in every thread. lo and hi: the list's smallest and largest entry.
-__device__ bool block_cut_from_list(const FullCut& fc, int n, uint64_t lo, uint64_t hi,
-                                    const uint32_t* mw, FullSh& sh, RowDesc* d, uint32_t mode) {
+__device__ __forceinline__ bool block_cut_from_list(const FullCut& fc, int n, uint64_t lo,
+                                                    uint64_t hi, const uint32_t* mw, FullSh& sh,
+                                                    RowDesc* d, uint32_t mode) {
   constexpr int kDig = 10;
   constexpr int kBins = 1 << kDig;
   constexpr int kPerLane = kBins / kWave;
@@ -1239,22 +1283,106 @@ __global__ __launch_bounds__(kRejectThreads) void k_topp_reject(Job j) {
   }
 }
 
+// What the row kernel writes for a row it routes to the full-vocabulary path
+// (when it has no top-k log-probs to write): the descriptor's m, status 0,
+// the row's (max, log sum) from the segment partials (combined as the row
+// kernel combines them: in segment order for a few segments, whose partials
+// wave 0's lanes hold from light_load), an empty kept-mask row.
+template <int kPer>
+__device__ __forceinline__ void full_row_writes(const Job& j, int row, float m, FullSh& sh,
+                                                const LightLoads<kPer>& L) {
+  if (threadIdx.x == 0) {
+    j.desc[row].m = m;
+    if (j.out_status) j.out_status[row] = 0;
+  }
+  if (j.lse) {  // uniform
+    const int ntile = j.nseg;
+    float M = -kInf, ls = 0.0f;
+    if (ntile <= kStageSegs) {  // uniform
+      if (threadIdx.x < kWave) {
+        for (int t = 0; t < ntile; ++t) M = fmaxf(M, __shfl(L.lp0.m, t));
+        for (int t = 0; t < ntile; ++t) {
+          const float pm = __shfl(L.lp0.m, t), ps = __shfl(L.lp0.s, t);
+          if (M > -kInf && pm > -kInf) ls += ps * __expf(pm - M);
+        }
+        if (threadIdx.x == 0) j.rlse[row] = make_float2(M, logf(ls));
+      }
+    } else {
+      const LsePart* lrow = j.lpart + static_cast<size_t>(row) * ntile;
+      float lm = -kInf;
+      for (int t = threadIdx.x; t < ntile; t += blockDim.x) lm = fmaxf(lm, lrow[t].m);
+      M = block_max(lm, sh.rf);
+      if (M > -kInf) {
+        for (int t = threadIdx.x; t < ntile; t += blockDim.x) {
+          const LsePart pt = lrow[t];
+          if (pt.m > -kInf) ls += pt.s * __expf(pt.m - M);
+        }
+      }
+      ls = block_sum(ls, sh.rf);
+      if (threadIdx.x == 0) j.rlse[row] = make_float2(M, logf(ls));
+    }
+  }
+  if (j.out_mask) {  // uniform
+    const int mwords = (j.V + 31) / 32;
+    uint32_t* mask_row = j.out_mask + static_cast<size_t>(row) * mwords;
+    for (int i = threadIdx.x; i < mwords; i += blockDim.x) mask_row[i] = 0u;
+  }
+}
+
+// The cut kernel, after the full-vocabulary passes: a full-vocabulary row
+// (route_row, the histogram and gather passes' own decision) gets its cut,
+// which sets the draw's mode for the Gumbel kernels. When the row kernel is
+// not launched before the passes (j.full_chain), this kernel also does its
+// work: a full-vocabulary row's status, log-sum-exp and kept-mask row before
+// the cut, and every other row the streaming pass did not finish gets the
+// row kernel's work (light_row), in parallel with the cuts.
+union RowFullSh {
+  FullSh full;
+  LightSh light;
+};
+
 template <typename E>
 __global__ __launch_bounds__(kFullThreads) void k_row_full(Job j) {
-  __shared__ FullSh sh;
+  __shared__ RowFullSh sm;
+  FullSh& sh = sm.full;
   const int row = blockIdx.x;
   RowDesc* d = j.desc + row;
   // every load the row may need is issued before any is used (the cut record
-  // and this thread's list slot are read whatever the row's mode, and used
+  // and this thread's list slot are read whatever the row's route, and used
   // only for rows with a cut): their latencies overlap
-  const uint32_t mode0 = d->mode;
-  const float m = d->m;
+  const RowDesc dsc = *d;  // (the row kernel's, when it ran before the passes)
+  const RoutePre rp = route_preload(j, row);
   const FullCut fc = j.fcut[row];
   const uint32_t got = j.fcnt[row];
   const uint64_t* lst = j.flist + static_cast<size_t>(row) * kFullListCap;
   const uint64_t v0 = lst[threadIdx.x];  // (kFullThreads <= kFullListCap)
-  const RowCfg c = load_cfg(row, j.V, j.T, j.k, j.p, j.mp, j.seeds);
-  if (mode0 != kRowFull) return;  // uniform over the block
+  // and the row kernel's first loads, for the rows that take its work
+  LightLoads<kStageMax / kFullThreads> L;
+  if (j.full_chain) light_load(j, row, L);
+  RowRoute rt;
+  if (j.full_chain) {  // uniform
+    rt = route_row(j, row, rp);
+  } else {  // the row kernel routed the row and wrote its m
+    rt.c = load_cfg(row, j.V, j.T, j.k, j.p, j.mp, j.seeds);
+    rt.m = dsc.m;
+    rt.full = dsc.mode == kRowFull;
+  }
+  if (!rt.full) {  // uniform over the block
+    if (j.full_chain) light_row<E>(j, row, sm.light, L);
+    return;
+  }
+  const RowCfg& c = rt.c;
+  const float m = rt.m;
+  // (without j.full_chain the row kernel ran before the passes and did the
+  // row's writes)
+  if (j.full_chain && j.lse && j.k_lp > 0) {  // uniform
+    // the row kernel's writes for the row, its top-k log-probs included (the
+    // same route: the row kernel sends it to the full-vocabulary path)
+    light_row<E>(j, row, sm.light, L);
+    __syncthreads();  // (the cut reuses the LDS)
+  } else if (j.full_chain) {  // uniform
+    full_row_writes(j, row, m, sh, L);
+  }
   if (c.p < 1.0f) {
     // the gathered list, when it holds the whole cut bucket: a short list
     // (one entry per thread) sorted and cut by the whole workgroup, a longer
@@ -1291,7 +1419,7 @@ __global__ __launch_bounds__(kFullThreads) void k_row_full(Job j) {
       __syncthreads();  // else (a list short of the remainder) the full path
     }
     const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
-    full_topp_cut(rowp, j.V, j.aligned, c, m, sh, d);
+    full_topp_cut(rowp, j.V, j.aligned, c.T, c.p, c.mp, m, sh, d);
   } else if (threadIdx.x == 0) {
     d->mode = (c.mp > 0.0f) ? kRowFullMinP : kRowFullNone;
   }

@@ -820,6 +820,22 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
   const int t_begin = seg * j.tps;
   const int t_end = min(t_begin + j.tps, j.ntile);
 
+  if (j.full_chain && pl.c.mode == kModeFull && pl.c.p < 1.0f) {
+    // A full-vocabulary top-p row's histogram, list counter and cut counts
+    // start at zero for the histogram and gather passes: this segment's share
+    // of the buckets, and the counters with the first segment (the passes
+    // route the row themselves; clearing a row they do not take is harmless).
+    uint64_t* hw = j.fhw + static_cast<size_t>(row) * kFullBuckets;
+    const int per = (kFullBuckets + j.nseg - 1) / j.nseg;
+    const int b1 = min(kFullBuckets, (seg + 1) * per);
+    for (int i = seg * per + static_cast<int>(threadIdx.x); i < b1; i += NT) hw[i] = 0ull;
+    if (seg == 0 && threadIdx.x == 0) {
+      j.fcnt[row] = 0u;
+      j.fcut[row].count = 0u;
+      j.fcut[row].above_c = 0ull;
+    }
+  }
+
   if (j.pen) {
     // Occurrence penalties of the ids of this segment, in place, before the
     // segment is read (every id lies in one segment, so each is penalised

@@ -151,6 +151,8 @@ struct Job {
   int fseg;            // segments per row of the histogram and gather passes
   int fseg_len;        // ids per segment (a multiple of 8)
   int full_in_select;      // the streaming pass writes out_full itself (it finishes every row)
+  int full_chain;          // the full-vocabulary passes run: the streaming pass clears their
+                           // counters and the cut kernel does the row kernel's work
   int full_vec;            // out_full rows take 16-byte stores
   // workspace; streaming-pass geometry
   int ntile;  // tiles per row
@@ -197,6 +199,66 @@ __device__ __forceinline__ Plan plan_row(const Job& j, int row) {
     pl.TA = 1.0f;
   }
   return pl;
+}
+
+// The route of a sampling row that the streaming pass did not finish: a
+// full-vocabulary row (mode kModeFull) whose checks pass goes through the
+// histogram, gather and cut passes with m = its largest s = x / T; any other
+// row is the row kernel's. The checks are the row kernel's for such a row:
+// no NaN or +inf logit and some finite one, an argmax found, no hint that
+// rules the row out, and a finite m. The histogram and gather passes and the
+// cut kernel each decide it with this one function from the same inputs (the
+// row's parameters and the streaming pass's per-segment words). Called with
+// every lane of the wave active (the segments' words are combined across it).
+struct RowRoute {
+  RowCfg c;
+  float m;    // the largest s of a full-vocabulary row
+  bool full;  // a full-vocabulary row whose checks pass
+};
+// The first 64 segments' words for route_row, one per lane: loads a caller
+// issues ahead of its other loads, so that they return first.
+struct RoutePre {
+  uint32_t mt;  // the segment's meta word
+  uint64_t v;   // its list-A slot 0 (the segment argmax when it found one)
+};
+__device__ __forceinline__ RoutePre route_preload(const Job& j, int row) {
+  RoutePre p{0u, 0ull};
+  const int ntile = j.nseg;
+  const size_t s0 = static_cast<size_t>(row) * ntile;
+  const int t = lane();
+  if (t < ntile) {  // (the slot is read whether or not the segment found one)
+    p.mt = j.meta[s0 + t];
+    p.v = j.candA[(s0 + t) * kSelCap];
+  }
+  return p;
+}
+__device__ __forceinline__ RowRoute route_row(const Job& j, int row, const RoutePre& p) {
+  RowRoute r;
+  r.c = load_cfg(row, j.V, j.T, j.k, j.p, j.mp, j.seeds);
+  r.m = 0.0f;
+  r.full = false;
+  if (r.c.mode != kModeFull) return r;  // uniform
+  const int ntile = j.nseg;
+  const size_t s0 = static_cast<size_t>(row) * ntile;
+  uint32_t fl = p.mt;
+  uint64_t top = (p.mt & kMetaCountA) ? p.v : 0ull;  // the row argmax: the best segment argmax
+  for (int t = lane() + kWave; t < ntile; t += kWave) {
+    const uint32_t mt = j.meta[s0 + t];
+    const uint64_t v = j.candA[(s0 + t) * kSelCap];
+    fl |= mt;
+    if (mt & kMetaCountA) top = v > top ? v : top;
+  }
+  fl = wave_reduce(fl, [](uint32_t a, uint32_t b) { return a | b; });
+  top = wave_max(top);
+  const bool bad_logits = (fl & kMetaBadLogits) || !(fl & kMetaHasFinite);
+  if (r.c.status || bad_logits || top == 0ull) return r;
+  if (j.hints & (VS_HINT_ALL_GREEDY | VS_HINT_NO_FULLVOCAB | VS_HINT_SMALL_TOPK)) return r;
+  const float x = key2f(pkey(top));
+  const float m = (r.c.T == 1.0f) ? x : x / r.c.T;
+  if (m == kInf) return r;  // x / T overflowed
+  r.m = m;
+  r.full = true;
+  return r;
 }
 
 // The temperature the log-probs of a row are taken at: vs_logprobs_ex's per-row
