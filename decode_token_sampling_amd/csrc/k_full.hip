@@ -38,21 +38,25 @@ constexpr int kThreads = 1024;
 constexpr int kPer = kFullBuckets / kThreads;  // buckets per thread (4)
 constexpr int kGatherBuf = 2048;  // ids a gather workgroup collects in LDS before one global append
 
-// A full-vocabulary row whose top-p cut is still to be found.
-// d: the row's descriptor, which the row kernel wrote when it ran before this
-// pass (j.full_chain unset); else the row's route is found here.
-__device__ __forceinline__ bool topp_row(const Job& j, int row, const RowDesc& d,
-                                         const RoutePre& rp, RowCfg* c, float* m) {
+// The rows the passes take: kPassTopP, a full-vocabulary top-p row (the
+// histogram, its cut bucket, the gather); kPassWhole, a full-vocabulary row
+// without the cut (top_p >= 1), which only the drawing gather pass takes, to
+// draw over all of its members; kPassNone, any other. Without j.full_chain the
+// row kernel ran first and its descriptor routes the row; with it, route_row.
+enum : int { kPassNone = 0, kPassTopP = 1, kPassWhole = 2 };
+__device__ __forceinline__ int pass_row(const Job& j, int row, const RowDesc& d,
+                                        const RoutePre& rp, RowCfg* c, float* m) {
   if (!j.full_chain) {  // uniform
-    if (d.mode != kRowFull) return false;
+    if (d.mode != kRowFull) return kPassNone;
     *c = load_cfg(row, j.V, j.T, j.k, j.p, j.mp, j.seeds);
     *m = d.m;
-    return c->p < 1.0f;
+  } else {
+    const RowRoute r = route_row(j, row, rp);
+    *c = r.c;
+    *m = r.m;
+    if (!r.full) return kPassNone;
   }
-  const RowRoute r = route_row(j, row, rp);
-  *c = r.c;
-  *m = r.m;
-  return r.full && r.c.p < 1.0f;
+  return c->p < 1.0f ? kPassTopP : kPassWhole;
 }
 
 // Reads the ids [lo, hi) of a row with the whole block: 16-byte loads when
@@ -150,18 +154,6 @@ struct SegReader {
 template <bool kDiv>
 __device__ __forceinline__ float scaled_by(float x, float T) { return kDiv ? x / T : x; }
 
-// The random words b below which an id cannot beat the score bound lim:
-// with u = ((b >> 12) + 1/2) 2^-52, every b < skip_below(lim) has
-// 1 - u >= lim (1 + 2^-45) + 2^-52, so (1 - u)(1 - 2^-50) rounded stays
-// >= lim and the id scores below the bound (0: no b, while lim >= 1).
-__device__ __forceinline__ uint64_t cand_skip_below(double lim) {
-  if (!(lim < 1.0)) return 0ull;
-  // (1 - lim (1 + 2^-45)) 2^52 - 2, whose rounding errors stay below 1.5
-  const double v = (1.0 - lim * (1.0 + 0x1p-45)) * 0x1p52 - 2.0;
-  if (!(v > 0.0)) return 0ull;
-  return static_cast<uint64_t>(v) << 12;  // floor(v) < 2^52
-}
-
 // A thread's kCandM best Gumbel candidates, best first in the order (score
 // desc, id asc); empty slots score -1.
 struct CandList {
@@ -223,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void k_full_hist(Job j) {
   rd.start(rowp, lo, hi, j.aligned != 0);
   RowCfg c;
   float m;
-  if (!topp_row(j, row, dsc, rp, &c, &m)) return;  // uniform per block
+  if (pass_row(j, row, dsc, rp, &c, &m) != kPassTopP) return;  // uniform per block
   for (int i = threadIdx.x; i < kFullBuckets; i += kThreads) hw[i] = 0ull;
   if (threadIdx.x == 0) s_bound = 0ull;
   __syncthreads();
@@ -245,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void k_full_hist(Job j) {
     const double bd = __longlong_as_double(static_cast<long long>(sb));
     if (bd > 0.0 && (1.0 + 0x1p-40) / bd < lim) {
       lim = (1.0 + 0x1p-40) / bd;
-      skip = cand_skip_below(lim);
+      skip = skip_below(lim);
     }
   };
   const auto candidate = [&](int id, float e, uint32_t key) {
@@ -346,6 +338,7 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
   __shared__ uint32_t s_n, s_lim, s_base;
   __shared__ uint64_t s_best;  // bits of the best score any thread has found
   __shared__ int s_chunk;      // the reader's next chunk, when claimed
+  __shared__ float s_win;      // the segment's best id's s (kDraw)
   int row, seg;
   if (!xcd_row_tile(blockIdx.x, j.B, j.fseg, &row, &seg)) return;  // uniform per block
   const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
@@ -360,24 +353,30 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
   rd.start(rowp, lo, hi, j.aligned != 0, &s_chunk);
   RowCfg c;
   float m;
-  if (!topp_row(j, row, dsc, rp, &c, &m)) return;  // uniform per block
+  const int kind = pass_row(j, row, dsc, rp, &c, &m);
+  if (kind == kPassNone || (!kDraw && kind == kPassWhole)) return;  // uniform per block
+  // a row without the cut: every member is drawn over (kDraw), nothing gathered
+  const bool whole = kDraw && kind == kPassWhole;
   const uint64_t* ghw = j.fhw + static_cast<size_t>(row) * kFullBuckets;
 
   // The cut bucket: thread t holds buckets [4 t, 4 t + 4); an exclusive scan
   // over the threads gives the mass of the buckets before.
   uint64_t w[kPer];
-  uint64_t lw = 0;
+  uint64_t cw = 0, target = 0;
+  if (!whole) {  // uniform
+    uint64_t lw = 0;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    w[i] = ghw[threadIdx.x * kPer + i];
-    lw += w[i];
+    for (int i = 0; i < kPer; ++i) {
+      w[i] = ghw[threadIdx.x * kPer + i];
+      lw += w[i];
+    }
+    uint64_t total_w;
+    cw = block_scan_incl(lw, sw, &total_w) - lw;
+    // the kept prefix is the shortest whose mass reaches p * total; masses
+    // are integers, so "cum >= thr" is "cum >= ceil(thr)" (at least one id)
+    const double thr = static_cast<double>(c.p) * static_cast<double>(total_w);
+    target = ceil(thr) >= 1.0 ? static_cast<uint64_t>(ceil(thr)) : 1ull;
   }
-  uint64_t total_w;
-  uint64_t cw = block_scan_incl(lw, sw, &total_w) - lw;
-  // the kept prefix is the shortest whose mass reaches p * total; masses are
-  // integers, so "cum >= thr" is "cum >= ceil(thr)" (at least one id)
-  const double thr = static_cast<double>(c.p) * static_cast<double>(total_w);
-  const uint64_t target = ceil(thr) >= 1.0 ? static_cast<uint64_t>(ceil(thr)) : 1ull;
   if (threadIdx.x == 0) {
     s_bucket = -1;
     s_n = 0u;
@@ -385,26 +384,29 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
     s_best = 0ull;
   }
   __syncthreads();
+  int bstar = kFullBuckets - 1;  // (whole rows: unused)
+  if (!whole) {  // uniform
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int b = threadIdx.x * kPer + i;
-    if (cw < target && target <= cw + w[i]) {
-      s_bucket = b;
-      s_above_w = cw;
+    for (int i = 0; i < kPer; ++i) {
+      const int b = threadIdx.x * kPer + i;
+      if (cw < target && target <= cw + w[i]) {
+        s_bucket = b;
+        s_above_w = cw;
+      }
+      cw += w[i];
     }
-    cw += w[i];
-  }
-  __syncthreads();
-  const int bstar = s_bucket;
-  if (bstar < 0) {  // uniform; unreachable (the row maximum has mass 2^31)
-    // no stale record from an earlier call may stand: the cut kernel then
-    // takes its one-workgroup path
-    if (seg == 0 && threadIdx.x == 0) j.fcut[row].bucket = -1;
-    return;
-  }
-  if (seg == 0 && threadIdx.x == 0) {
-    j.fcut[row].bucket = bstar;
-    j.fcut[row].rem = target - s_above_w;
+    __syncthreads();
+    bstar = s_bucket;
+    if (bstar < 0) {  // uniform; unreachable (the row maximum has mass 2^31)
+      // no stale record from an earlier call may stand: the cut kernel then
+      // takes its one-workgroup path
+      if (seg == 0 && threadIdx.x == 0) j.fcut[row].bucket = -1;
+      return;
+    }
+    if (seg == 0 && threadIdx.x == 0) {
+      j.fcut[row].bucket = bstar;
+      j.fcut[row].rem = target - s_above_w;
+    }
   }
 
   // The ids of that bucket: collected in LDS (one LDS atomic add per wave),
@@ -421,7 +423,7 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
   // its own exponential; else (a bucket at the min-p or zero-mass edge, or
   // the last bucket, which holds every smaller t) each id is tested.
   bool bucket_in = false;
-  if (bstar < kFullBuckets - 1) {
+  if (!whole && bstar < kFullBuckets - 1) {
     const float t_lo = -static_cast<float>(bstar + 1) / kFullPerUnit * (1.0f + 0x1p-20f);
     const float e_lo = pinned_exp(t_lo);
     bucket_in = e_lo >= c.mp && mass_of(e_lo) != 0ull;
@@ -437,6 +439,7 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
   const uint64_t rs = row_stream(c.seed, row);
   double best = -1.0;
   int best_id = 0x7fffffff;
+  float best_s = 0.0f;
   double lim = __builtin_inf();  // (1 + 2^-40) / (the best score known here)
   float lim_up = __builtin_inff();  // a float at or above lim
   const auto refresh = [&]() {
@@ -460,6 +463,7 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
     if (g > best || (g == best && id < best_id)) {
       best = g;
       best_id = id;
+      best_s = sv;
       if (share) {
         atomicMax(reinterpret_cast<unsigned long long*>(&s_best),
                   static_cast<unsigned long long>(__double_as_longlong(g)));
@@ -476,6 +480,9 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
   const float t_floor =
       bstar < kFullBuckets - 1 ? -static_cast<float>(bstar + 1) / kFullPerUnit : -kInf;
   const auto above = [&](float sv) { return sv - m > t_above; };
+  // a member of a row without the cut: every id, or e >= min_p when it is set
+  const bool minp = c.mp > 0.0f;
+  const auto member = [&](float sv) { return !minp || pinned_exp(sv - m) >= c.mp; };
   if constexpr (kDraw) {
     // one id per thread first (the first of its first vector, when above),
     // so that the workgroup starts from the best of up to 1024 scores, taken
@@ -485,7 +492,7 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
       unpack16(rd.raw[0], x, rowp);
       const int id = lo + rd.p * EPV;
       const float sv = c.T == 1.0f ? x[0] : x[0] / c.T;
-      if (above(sv)) score(id, sv, random_bits(rs, id), false);
+      if (whole ? member(sv) : above(sv)) score(id, sv, random_bits(rs, id), false);
     }
     const double wb = wave_max(best);
     if (lane() == 0) sd[threadIdx.x / kWave] = wb;
@@ -503,16 +510,23 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
     rd.visit([&](int id0, const float* x, int n) {
       float sv[EPV];
       uint32_t hm = 0;  // ids in the cut bucket (the bucket alone, no exponential)
-      uint32_t am = 0;  // ids above it
+      uint32_t am = 0;  // ids above it (a whole row's members)
 #pragma unroll
-      for (int q = 0; q < EPV; ++q) {
-        sv[q] = scaled_by<decltype(div)::value>(x[q], c.T);
-        const float t = sv[q] - m;
-        // (positions past n hold -inf: in no bucket by these bounds either,
-        // except the last, whose ids the membership test below drops)
-        const bool in = q < n;
-        am |= (in && t > t_above) ? 1u << q : 0u;
-        hm |= (in && t <= t_above && t > t_floor) ? 1u << q : 0u;
+      for (int q = 0; q < EPV; ++q) sv[q] = scaled_by<decltype(div)::value>(x[q], c.T);
+      if (whole) {  // uniform
+#pragma unroll
+        for (int q = 0; q < EPV; ++q) am |= (q < n && member(sv[q])) ? 1u << q : 0u;
+      } else {
+#pragma unroll
+        for (int q = 0; q < EPV; ++q) {
+          const float t = sv[q] - m;
+          // (positions past n hold -inf: in no bucket by these bounds
+          // either, except the last, whose ids the membership test below
+          // drops)
+          const bool in = q < n;
+          am |= (in && t > t_above) ? 1u << q : 0u;
+          hm |= (in && t <= t_above && t > t_floor) ? 1u << q : 0u;
+        }
       }
       n_above += __popc(am);
       if constexpr (kDraw) {
@@ -600,13 +614,12 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
     pass(std::false_type{});
   else
     pass(std::true_type{});
+  double bb = -1.0;
+  int bid = 0x7fffffff;
   if constexpr (kDraw) {
-    // the segment's best over its above ids (score desc, id asc) into the
-    // row's per-segment record (score -1: none)
-    const double bb = block_max(best, sd);
-    const int bid = block_min(best == bb ? best_id : 0x7fffffff, reinterpret_cast<int*>(sc));
-    if (threadIdx.x == 0)
-      j.gpart[static_cast<size_t>(row) * j.ntile3 + seg] = GPart{bb >= 0.0 ? bb : -1.0, bid, 0};
+    bb = block_max(best, sd);
+    bid = block_min(best == bb ? best_id : 0x7fffffff, reinterpret_cast<int*>(sc));
+    if (bb >= 0.0 && best == bb && best_id == bid) s_win = best_s;  // one thread (ids are distinct)
   }
   // this workgroup's counts into the row's record (block_sum's barriers also
   // complete the LDS appends)
@@ -616,9 +629,17 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
   // first one that did not fit (s_lim), or all of s_n
   const uint32_t n = min(s_n, s_lim);
   if (threadIdx.x == 0) {
+    // the segment's best over its above ids (a whole row's members), score
+    // desc, id asc, into the row's per-segment record (score -1: none),
+    // with a whole row's member count
+    if constexpr (kDraw)
+      j.gpart[static_cast<size_t>(row) * j.ntile3 + seg] =
+          GPart{bb >= 0.0 ? bb : -1.0, bid, whole ? static_cast<int32_t>(n_above) : 0,
+                bb >= 0.0 ? s_win : 0.0f};
     s_base = n ? atomicAdd(cnt, n) : 0u;
-    if (n_above) atomicAdd(reinterpret_cast<unsigned long long*>(&j.fcut[row].above_c),
-                           static_cast<unsigned long long>(n_above));
+    if (n_above && !whole)
+      atomicAdd(reinterpret_cast<unsigned long long*>(&j.fcut[row].above_c),
+                static_cast<unsigned long long>(n_above));
     if (n_hit) atomicAdd(&j.fcut[row].count, n_hit);
   }
   __syncthreads();

@@ -39,18 +39,6 @@ __device__ __forceinline__ bool full_row(uint32_t mode) {
   return mode == kRowFullNone || mode == kRowFullMinP || mode == kRowFullTopP;
 }
 
-// The random words b below which an id cannot beat the score bound lim:
-// with u = ((b >> 12) + 1/2) 2^-52, every b < skip_below(lim) has
-// 1 - u >= lim (1 + 2^-45) + 2^-52, so (1 - u)(1 - 2^-50) rounded stays
-// >= lim and the id scores below the best (0: no b, while lim >= 1).
-__device__ __forceinline__ uint64_t skip_below(double lim) {
-  if (!(lim < 1.0)) return 0ull;
-  // (1 - lim (1 + 2^-45)) 2^52 - 2, whose rounding errors stay below 1.5
-  const double v = (1.0 - lim * (1.0 + 0x1p-45)) * 0x1p52 - 2.0;
-  if (!(v > 0.0)) return 0ull;
-  return static_cast<uint64_t>(v) << 12;  // floor(v) < 2^52
-}
-
 template <typename E>
 __global__ __launch_bounds__(kThreads) void k_gumbel_partial(Job j) {
   __shared__ double sd[kThreads / kWave];
@@ -268,71 +256,20 @@ __global__ __launch_bounds__(kThreads) void k_gumbel_final(Job j) {
   __shared__ int si[kThreads / kWave];
   const int row = blockIdx.x;
   const GPart* g = j.gpart + static_cast<size_t>(row) * j.ntile3;
-  const uint64_t* lst = j.flist + static_cast<size_t>(row) * kFullListCap;
-  // Every load the row may need is issued at once, before its mode is
-  // known: the descriptor, this thread's first record, the list's length and
-  // this thread's first list entries (all inside the row's slices).
-  constexpr int U = 4;  // list entries in flight per thread
-  static_assert(U * kThreads <= kFullListCap, "the first entries lie inside the list");
+  // the descriptor and this thread's first record, loaded together
   const RowDesc d = j.desc[row];
   const int t0 = static_cast<int>(threadIdx.x);
   const GPart p0 = t0 < j.ntile3 ? g[t0] : GPart{-1.0, 0x7fffffff, 0};
-  uint64_t v[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) v[u] = lst[t0 + u * kThreads];
-  const uint32_t cnt = j.fcnt[row];
-  const bool listed = d.mode == kRowFullListed;
-  if (!full_row(d.mode) && !listed) return;  // uniform over the block
+  if (!full_row(d.mode)) return;  // uniform over the block
   double best = -1.0;
   int best_id = 0x7fffffff;
   int kept = 0;
-  if (listed) {
-    // The gather pass's bests over the ids above the cut bucket (one record
-    // per segment), then the kept entries of the list: those at or above the
-    // cut entry in the packed order. An entry is skipped when it provably
-    // scores below the best so far (the integer test of the Gumbel pass, with
-    // e <= 1), else scored exactly as the Gumbel pass scores it.
-    for (int t = t0; t < j.fseg; t += blockDim.x) {
-      const GPart p = t == t0 ? p0 : g[t];
-      if (p.score >= 0.0 && (p.score > best || (p.score == best && p.id < best_id))) {
-        best = p.score;
-        best_id = p.id;
-      }
-    }
-    const uint64_t rs = row_stream(j.seeds ? j.seeds[row] : 0ull, row);
-    const double b0 = block_max(best, sd);
-    const double lim = b0 > 0.0 ? (1.0 + 0x1p-40) / b0 : __builtin_inf();
-    const uint64_t skip = skip_below(lim);
-    const uint64_t cutv = pack(d.tau, d.id_cut);
-    const int n = static_cast<int>(min(cnt, static_cast<uint32_t>(kFullListCap)));
-    for (int i0 = threadIdx.x; i0 < n; i0 += U * kThreads) {
-      if (i0 != static_cast<int>(threadIdx.x)) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = i0 + u * kThreads < n ? lst[i0 + u * kThreads] : 0ull;
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        // below the cut, or past the list (taken as 0, below every entry)
-        if (i0 + u * kThreads >= n || v[u] < cutv) continue;
-        const int id = pid(v[u]);
-        const uint64_t b = random_bits(rs, id);
-        if (b < skip) continue;  // e <= 1: below the bound
-        const double sc = gumbel_score(pinned_exp(key2f(pkey(v[u])) - d.m), rs, id);
-        if (sc > best || (sc == best && id < best_id)) {
-          best = sc;
-          best_id = id;
-        }
-      }
-    }
-    kept = threadIdx.x == 0 ? d.kept : 0;
-  } else {
-    for (int t = t0; t < j.ntile3; t += blockDim.x) {
-      const GPart p = t == t0 ? p0 : g[t];
-      kept += p.kept;
-      if (p.kept && (p.score > best || (p.score == best && p.id < best_id))) {
-        best = p.score;
-        best_id = p.id;
-      }
+  for (int t = t0; t < j.ntile3; t += blockDim.x) {
+    const GPart p = t == t0 ? p0 : g[t];
+    kept += p.kept;
+    if (p.kept && (p.score > best || (p.score == best && p.id < best_id))) {
+      best = p.score;
+      best_id = p.id;
     }
   }
   const double bb = block_max(best, sd);

@@ -47,6 +47,7 @@ struct RowSh {
   uint64_t hw[kBins];
   uint32_t hc[kBins];
   uint64_t r64[16];
+  uint64_t r64b[16];
   double rd[16];
   int32_t ri[16];
   float rf[16];
@@ -55,7 +56,24 @@ struct RowSh {
   uint64_t b64[4];
   int32_t b32[4];
   int32_t toff[kMaxSegs + 1];  // per-segment offsets of a candidate union
+  int32_t rk[16];              // per-wave kept counts of a draw
+  int32_t cr32[2][4];          // a long-list cut's round results (alternating)
+  uint64_t cr64[2][4];
+  uint64_t cut_v;              // a top-p cut as written to the descriptor:
+  int32_t cut_kept;            //   pack(tau, id_cut) and the kept count
 };
+// A top-p cut into the row's descriptor, and into LDS for the workgroup's
+// own draw (published by the caller's next barrier).
+template <class Sh>
+__device__ __forceinline__ void set_cut(RowDesc* d, Sh& sh, uint32_t mode, uint32_t tau,
+                                        int32_t id_cut, int32_t kept) {
+  d->mode = mode;
+  d->tau = tau;
+  d->id_cut = id_cut;
+  d->kept = kept;
+  sh.cut_v = pack(tau, id_cut);
+  sh.cut_kept = kept;
+}
 // Candidate slots of rows short enough to be loaded whole at the row kernel's
 // entry (segments x kSelCap), and the segments those rows may have.
 constexpr int kStageMax = 1024;
@@ -972,10 +990,7 @@ __device__ void full_topp_cut(const E* __restrict__ rowp, int V, bool aligned, f
     kept = static_cast<int32_t>(ac + ca + need);
   }
   if (threadIdx.x == 0) {
-    d->mode = kRowFullTopP;
-    d->tau = tau;
-    d->id_cut = idc;
-    d->kept = kept;
+    set_cut(d, sh, kRowFullTopP, tau, idc, kept);
   }
 }
 
@@ -1016,10 +1031,7 @@ __device__ __forceinline__ bool sort_cut_from_list(const FullCut& fc, int n, uin
       const uint64_t cum = (static_cast<uint64_t>(hi) << 16) + lo;
       const int rank = __popcll(__ballot(cum < fc.rem));  // the running mass is nondecreasing
       if (rank < n && lane() == rank) {
-        d->mode = mode;
-        d->tau = pkey(v);
-        d->id_cut = pid(v);
-        d->kept = static_cast<int32_t>(fc.above_c) + rank + 1;
+        set_cut(d, sh, mode, pkey(v), pid(v), static_cast<int32_t>(fc.above_c) + rank + 1);
       }
       if (lane() == 0) sh.b32[3] = rank < n ? 1 : 0;
     }
@@ -1057,10 +1069,7 @@ __device__ __forceinline__ bool sort_cut_from_list(const FullCut& fc, int n, uin
   const int rank = block_sum(cum < fc.rem ? 1 : 0, sh.ri);  // the running mass is nondecreasing
   if (rank >= n) return false;  // uniform: the list's masses fall short of the remainder
   if (t == rank) {
-    d->mode = mode;
-    d->tau = pkey(v);
-    d->id_cut = pid(v);
-    d->kept = static_cast<int32_t>(fc.above_c) + rank + 1;
+    set_cut(d, sh, mode, pkey(v), pid(v), static_cast<int32_t>(fc.above_c) + rank + 1);
   }
   return true;
 }
@@ -1070,38 +1079,42 @@ __device__ __forceinline__ bool sort_cut_from_list(const FullCut& fc, int n, uin
 // which the remaining entries still differ (bits they all share are skipped:
 // the bitwise AND and OR of the chosen digit's entries give the next such
 // bit). Each round is one counting pass over the list by every wave and one
-// scan of the digits' masses by wave 0. Called by every thread; the result is
-// the same in every thread. lo and hi: the list's smallest and largest entry.
+// scan of the digits' masses and counts over the workgroup (a digit per
+// thread, largest first: in-wave DPP scans, then the waves' totals), with
+// three barriers a round; each thread clears its own digit for the next
+// round once it has read it, and the round's result alternates between two
+// LDS records. Called by every thread; the result is the same in every
+// thread. lo and hi: the list's smallest and largest entry.
 __device__ __forceinline__ bool block_cut_from_list(const FullCut& fc, int n, uint64_t lo,
                                                     uint64_t hi, const uint32_t* mw, FullSh& sh,
                                                     RowDesc* d, uint32_t mode) {
   constexpr int kDig = 10;
   constexpr int kBins = 1 << kDig;
-  constexpr int kPerLane = kBins / kWave;
   static_assert(3 * kBins <= FullSh::kBinCap && kBins <= FullSh::kBinCap, "digit tables");
   uint64_t* bw = sh.hw;               // each digit's mass
   uint64_t* band = sh.hw + kBins;     // the AND of its entries
   uint64_t* bor = sh.hw + 2 * kBins;  // their OR
   uint32_t* bc = sh.hc;               // their count
+  static_assert(kBins == kFullThreads, "one digit per thread");
   uint64_t rem = fc.rem;
   int rank = 0;
   uint64_t cutv = hi;
   uint64_t diff = lo ^ hi;  // the bits in which the remaining entries differ
   uint64_t same = hi;       // (their common bits, above the highest of those)
   const int t = static_cast<int>(threadIdx.x);
+  const int wv = t / kWave, ln = lane();
+  const int dgt = kBins - 1 - t;  // this thread's digit
+  bw[dgt] = 0ull;
+  band[dgt] = ~0ull;
+  bor[dgt] = 0ull;
+  bc[dgt] = 0u;
+  __syncthreads();
+  int par = 0;  // the round's result record
   while (diff != 0ull) {  // uniform
     const int hb = 63 - __clzll(diff);
     const int shift = hb >= kDig - 1 ? hb - (kDig - 1) : 0;
     const uint64_t pmask = hb >= 63 ? 0ull : (~0ull << (hb + 1));
     const uint64_t prefix = same & pmask;
-    for (int i = t; i < kBins; i += blockDim.x) {
-      bw[i] = 0ull;
-      band[i] = ~0ull;
-      bor[i] = 0ull;
-      bc[i] = 0u;
-    }
-    if (t == 0) sh.b32[0] = -1;
-    __syncthreads();
     // (whole waves per step: when every counted entry of a wave falls in one
     // digit, as when the entries share their key, the wave combines them and
     // one lane updates the digit, instead of 64 atomics on one address; the
@@ -1137,53 +1150,43 @@ __device__ __forceinline__ bool block_cut_from_list(const FullCut& fc, int n, ui
       }
     }
     __syncthreads();
-    if (t < kWave) {
-      // lane l scans the digits kBins - 1 - (kPerLane l + q), q = 0.., largest
-      // first; an exclusive scan over the lanes gives each lane's start
-      const int l = t;
-      uint64_t lw = 0ull;
-      uint32_t lc = 0u;
-#pragma unroll 4
-      for (int q = 0; q < kPerLane; ++q) {
-        const int dg = kBins - 1 - (l * kPerLane + q);
-        lw += bw[dg];
-        lc += bc[dg];
-      }
-      uint64_t sw = lw;
-      uint32_t scn = lc;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const uint64_t yw = __shfl_up(sw, o);
-        const uint32_t yc = __shfl_up(scn, o);
-        if (l >= o) {
-          sw += yw;
-          scn += yc;
-        }
-      }
-      uint64_t wb = sw - lw;
-      uint32_t cb = scn - lc;
-#pragma unroll 4
-      for (int q = 0; q < kPerLane; ++q) {
-        const int dg = kBins - 1 - (l * kPerLane + q);
-        const uint64_t w = bw[dg];
-        const uint32_t cn = bc[dg];
-        if (cn > 0u && wb < rem && rem <= wb + w) {  // one digit of one lane
-          sh.b32[0] = dg;
-          sh.b32[1] = static_cast<int32_t>(cb);
-          sh.b32[2] = static_cast<int32_t>(cn);
-          sh.b64[0] = wb;
-          sh.b64[1] = band[dg];
-          sh.b64[2] = bor[dg];
-        }
-        wb += w;
-        cb += cn;
-      }
+    // the masses (at most 2^31 an entry, 2^13 entries: below 2^44 a digit)
+    // scanned as 22-bit halves and the counts, each below 2^32 over a wave
+    const uint64_t w = bw[dgt];
+    const uint32_t cn = bc[dgt];
+    const uint32_t s_lo = wave_scan_incl_u32(static_cast<uint32_t>(w & 0x3fffffull));
+    const uint32_t s_hi = wave_scan_incl_u32(static_cast<uint32_t>(w >> 22));
+    const uint32_t s_cn = wave_scan_incl_u32(cn);
+    const uint64_t w_in = (static_cast<uint64_t>(s_hi) << 22) + s_lo;
+    if (ln == kWave - 1) {
+      sh.r64[wv] = w_in;
+      sh.ri[wv] = static_cast<int32_t>(s_cn);
     }
+    if (t == 0) sh.cr32[par][0] = -1;
     __syncthreads();
-    const int dg = sh.b32[0];
-    const int above = sh.b32[1], cnt = sh.b32[2];
-    const uint64_t wabove = sh.b64[0], dand = sh.b64[1], dor = sh.b64[2];
-    __syncthreads();  // every thread has read the round's result
+    uint64_t wb = w_in - w;
+    uint32_t cb = s_cn - cn;
+    for (int q = 0; q < wv; ++q) {
+      wb += sh.r64[q];
+      cb += static_cast<uint32_t>(sh.ri[q]);
+    }
+    if (cn > 0u && wb < rem && rem <= wb + w) {  // one digit of one thread
+      sh.cr32[par][0] = dgt;
+      sh.cr32[par][1] = static_cast<int32_t>(cb);
+      sh.cr32[par][2] = static_cast<int32_t>(cn);
+      sh.cr64[par][0] = wb;
+      sh.cr64[par][1] = band[dgt];
+      sh.cr64[par][2] = bor[dgt];
+    }
+    bw[dgt] = 0ull;  // (read: cleared for the next round)
+    band[dgt] = ~0ull;
+    bor[dgt] = 0ull;
+    bc[dgt] = 0u;
+    __syncthreads();
+    const int dg = sh.cr32[par][0];
+    const int above = sh.cr32[par][1], cnt = sh.cr32[par][2];
+    const uint64_t wabove = sh.cr64[par][0], dand = sh.cr64[par][1], dor = sh.cr64[par][2];
+    par ^= 1;
     if (dg < 0) return false;  // the list's masses fall short of the remainder
     rem -= wabove;
     rank += above;
@@ -1195,10 +1198,7 @@ __device__ __forceinline__ bool block_cut_from_list(const FullCut& fc, int n, ui
     same = dand;
   }
   if (threadIdx.x == 0) {
-    d->mode = mode;
-    d->tau = pkey(cutv);
-    d->id_cut = pid(cutv);
-    d->kept = static_cast<int32_t>(fc.above_c) + rank + 1;
+    set_cut(d, sh, mode, pkey(cutv), pid(cutv), static_cast<int32_t>(fc.above_c) + rank + 1);
   }
   return true;
 }
@@ -1329,9 +1329,134 @@ __device__ __forceinline__ void full_row_writes(const Job& j, int row, float m, 
   }
 }
 
+// The draw of a full-vocabulary row in a call whose gather pass drew (no kept
+// mask asked for), finished here, after the cut. The gather pass left one
+// record per segment: for a top-p row the best (score desc, id asc) over its
+// ids above the cut bucket, for a row without the cut (top_p >= 1) the best
+// over all of its members and their count (kFinWhole). A top-p row cut from
+// its list adds the list's kept entries, those at or above the cut entry
+// (kFinListed: nlist entries, entry t in thread t's v0 for a list of at most
+// one entry per thread, all of them in sh.buf otherwise); a top-p row cut from
+// the row itself draws over its whole kept set in one pass over the row
+// (kFinRow; rare: the cut bucket did not fit the list). Each id's score, the
+// skip test and the tie order are those of the Gumbel pass over the kept set
+// (an id is skipped only when it provably scores below a best already found),
+// so the draw is the same. Then the row's outputs: the sampled id, the kept
+// count and, in the fused call, the sampled id's log-probability (from ml,
+// thread 0's (max, log-sum-exp) of the row, and the sampled id's logit, which
+// at T = 1 is its s). Every wave reads the records (g0: lane l's record l,
+// loaded by the caller ahead of the cut), so each holds their best without a
+// barrier; the cut comes from LDS (set_cut, published by the caller's
+// barrier).
+enum : int { kFinWhole = 0, kFinListed = 1, kFinRow = 2 };
+template <typename E>
+__device__ __forceinline__ void finish_full_draw(const Job& j, int row, float T, uint64_t seed,
+                                                  float m, int how, int nlist, uint64_t v0,
+                                                  const GPart& g0, float2 ml, FullSh& sh) {
+  constexpr int kNT = kFullThreads, kNW = kFullThreads / kWave;
+  const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
+  const uint64_t rs = row_stream(seed, row);
+  const int t0 = static_cast<int>(threadIdx.x);
+  const int ln = lane(), wv = t0 / kWave;
+  double best = -1.0;
+  int best_id = 0x7fffffff;
+  float best_s = 0.0f;
+  int kept = 0;
+  const auto take = [&](double sc, int id, float sv) {
+    if (sc > best || (sc == best && id < best_id)) {
+      best = sc;
+      best_id = id;
+      best_s = sv;
+    }
+  };
+  if (how != kFinRow) {  // uniform
+    const GPart* g = j.gpart + static_cast<size_t>(row) * j.ntile3;
+    for (int t = ln; t < j.fseg; t += kWave) {
+      const GPart p = t == ln ? g0 : g[t];
+      if (wv == 0) kept += p.kept;  // (counted once)
+      if (p.score >= 0.0) take(p.score, p.id, p.s);
+    }
+  }
+  if (how != kFinWhole) {  // uniform
+    const uint64_t cutv = sh.cut_v;
+    kept = t0 == 0 ? sh.cut_kept : 0;
+    // every thread's bound starts from the records' best
+    const double b0 = how == kFinListed ? wave_max(best) : -1.0;
+    double lim = b0 > 0.0 ? (1.0 + 0x1p-40) / b0 : __builtin_inf();
+    uint64_t skip = skip_below(lim);
+    const auto score = [&](float sv, int id) {
+      const uint64_t b = random_bits(rs, id);
+      if (b < skip) return;  // e <= 1: below the bound
+      const double sc = gumbel_score(pinned_exp(sv - m), rs, id);
+      if (sc > best || (sc == best && id < best_id)) {
+        best = sc;
+        best_id = id;
+        best_s = sv;
+        lim = fmin(lim, (1.0 + 0x1p-40) / best);
+        skip = skip_below(lim);
+      }
+    };
+    if (how == kFinListed) {  // uniform
+      for (int i = t0; i < nlist; i += kNT) {
+        const uint64_t v = i == t0 ? v0 : sh.buf[i];
+        if (v >= cutv) score(key2f(pkey(v)), pid(v));  // at or above the cut entry
+      }
+    } else {
+      // key > tau, or key == tau and id <= id_cut
+      for (int id = t0; id < j.V; id += kNT) {
+        const float x = to_f32(rowp[id]);
+        const float sv = T == 1.0f ? x : x / T;
+        if (pack(f2key(sv), id) >= cutv) score(sv, id);
+      }
+    }
+  }
+  // the block's best and kept count with one barrier: each wave's through
+  // slots of its own, read by thread 0
+  {
+    const double wb = wave_max(best);
+    const int wi = wave_min(best == wb ? best_id : 0x7fffffff);
+    const int wk = wave_sum(kept);
+    const uint64_t own = __ballot(best == wb && best_id == wi);  // the lane holding it
+    const float ws = own ? __shfl(best_s, __ffsll(static_cast<unsigned long long>(own)) - 1) : 0.0f;
+    if (ln == 0) {
+      sh.rd[wv] = wb;
+      sh.ri[wv] = wi;
+      sh.rk[wv] = wk;
+      sh.rf[wv] = ws;
+    }
+  }
+  __syncthreads();
+  if (wv != 0) return;  // uniform per wave: wave 0 combines the waves' slots
+  const bool slot = ln < kNW;
+  const double sd = slot ? sh.rd[ln] : -1.0;
+  const int si = slot ? sh.ri[ln] : 0x7fffffff;
+  const double bb = wave_max(sd);
+  const int bid = wave_min(sd == bb ? si : 0x7fffffff);
+  const int bk = wave_sum(slot ? sh.rk[ln] : 0);
+  const uint64_t own = __ballot(slot && sd == bb && si == bid);
+  const float bs = own ? __shfl(slot ? sh.rf[ln] : 0.0f, __ffsll(static_cast<unsigned long long>(own)) - 1) : 0.0f;
+  if (ln == 0) {
+    if (bid < 0 || bid >= j.V) {  // unreachable: the row maximum is always kept
+      j.out_ids[row] = -1;
+      if (j.out_kept) j.out_kept[row] = 0;
+      if (j.out_status) j.out_status[row] = VS_ROW_BAD_LOGITS;
+      if (j.tok_sampled) j.out_tok_lp[row] = __builtin_nanf("");
+      return;
+    }
+    j.out_ids[row] = bid;
+    if (j.out_kept) j.out_kept[row] = bk;
+    if (j.tok_sampled) {
+      const float x = T == 1.0f ? bs : to_f32(rowp[bid]);
+      j.out_tok_lp[row] = (x - ml.x) - ml.y;
+    }
+  }
+}
+
 // The cut kernel, after the full-vocabulary passes: a full-vocabulary row
 // (route_row, the histogram and gather passes' own decision) gets its cut,
-// which sets the draw's mode for the Gumbel kernels. When the row kernel is
+// which sets the draw's mode for the Gumbel kernels; in a call whose gather
+// pass drew (j.fdraw) this kernel then finishes the draw of every such row
+// itself (finish_full_draw) and the Gumbel kernels do not run. When the row kernel is
 // not launched before the passes (j.full_chain), this kernel also does its
 // work: a full-vocabulary row's status, log-sum-exp and kept-mask row before
 // the cut, and every other row the streaming pass did not finish gets the
@@ -1373,6 +1498,11 @@ __global__ __launch_bounds__(kFullThreads) void k_row_full(Job j) {
   }
   const RowCfg& c = rt.c;
   const float m = rt.m;
+  // the gather pass's record of segment l for lane l of every wave, for the
+  // draw at the end (in flight during the cut)
+  GPart g0{-1.0, 0x7fffffff, 0};
+  if (j.fdraw && lane() < j.fseg)  // (j.fdraw uniform)
+    g0 = j.gpart[static_cast<size_t>(row) * j.ntile3 + lane()];
   // (without j.full_chain the row kernel ran before the passes and did the
   // row's writes)
   if (j.full_chain && j.lse && j.k_lp > 0) {  // uniform
@@ -1383,12 +1513,17 @@ __global__ __launch_bounds__(kFullThreads) void k_row_full(Job j) {
   } else if (j.full_chain) {  // uniform
     full_row_writes(j, row, m, sh, L);
   }
+  // the row's (max, log-sum-exp) for the sampled id's log-prob (thread 0
+  // wrote it, here or in the row kernel; in flight during the cut)
+  float2 ml = make_float2(0.0f, 0.0f);
+  if (j.fdraw && j.tok_sampled && threadIdx.x == 0) ml = j.rlse[row];
   if (c.p < 1.0f) {
     // the gathered list, when it holds the whole cut bucket: a short list
     // (one entry per thread) sorted and cut by the whole workgroup, a longer
     // one loaded with its masses into LDS for the workgroup's radix select
     const bool listed = fc.bucket >= 0 && got == fc.count && got > 0u &&
                         got <= static_cast<uint32_t>(FullSh::kBufCap);  // uniform
+    int fin = kFinRow;  // the draw's source once the cut is known (j.fdraw)
     if (listed) {
       __shared__ __align__(16) uint32_t mw[kFullListCap];
       // the draw then comes from the list and the gather pass's bests when
@@ -1399,29 +1534,61 @@ __global__ __launch_bounds__(kFullThreads) void k_row_full(Job j) {
       if (n <= kSortCutMax) {  // uniform
         const uint64_t v = static_cast<int>(threadIdx.x) < n ? v0 : 0ull;
         if (sort_cut_from_list(fc, n, v, ft, sh.buf, reinterpret_cast<uint64_t*>(mw), sh, d, mode))
-          return;  // uniform
+          fin = kFinListed;  // uniform
       } else {
+        // (kLB entries per thread in flight at once; the list's least and
+        // largest entries through per-wave slots and one barrier, which
+        // also publishes buf and mw)
+        constexpr int kLB = 4;
+        const int t = static_cast<int>(threadIdx.x);
         uint64_t lo = ~0ull, hi = 0ull;
-        for (int i = threadIdx.x; i < n; i += blockDim.x) {
-          const uint64_t v = static_cast<int>(threadIdx.x) == i ? v0 : lst[i];
-          uint64_t w;
-          int b;
-          if (!ft.mass(key2f(pkey(v)), &w, &b)) w = 0;
-          sh.buf[i] = v;
-          mw[i] = static_cast<uint32_t>(w);
-          lo = v < lo ? v : lo;
-          hi = v > hi ? v : hi;
+        for (int i0 = 0; i0 < n; i0 += kLB * kFullThreads) {
+          uint64_t vb[kLB];
+#pragma unroll
+          for (int k = 0; k < kLB; ++k) {
+            const int i = i0 + k * kFullThreads + t;
+            vb[k] = (i0 == 0 && k == 0) ? v0 : (i < n ? lst[i] : 0ull);
+          }
+#pragma unroll
+          for (int k = 0; k < kLB; ++k) {
+            const int i = i0 + k * kFullThreads + t;
+            if (i < n) {
+              uint64_t w;
+              int b;
+              if (!ft.mass(key2f(pkey(vb[k])), &w, &b)) w = 0;
+              sh.buf[i] = vb[k];
+              mw[i] = static_cast<uint32_t>(w);
+              lo = vb[k] < lo ? vb[k] : lo;
+              hi = vb[k] > hi ? vb[k] : hi;
+            }
+          }
         }
-        lo = block_min(lo, sh.r64);  // (its barriers also publish buf and mw)
-        hi = block_max(hi, sh.r64);
-        if (block_cut_from_list(fc, n, lo, hi, mw, sh, d, mode)) return;  // uniform
+        lo = wave_min(lo);
+        hi = wave_max(hi);
+        if (lane() == 0) {
+          sh.r64[t / kWave] = lo;
+          sh.r64b[t / kWave] = hi;
+        }
+        __syncthreads();
+        for (int w = 0; w < kFullThreads / kWave; ++w) {
+          lo = sh.r64[w] < lo ? sh.r64[w] : lo;
+          hi = sh.r64b[w] > hi ? sh.r64b[w] : hi;
+        }
+        if (block_cut_from_list(fc, n, lo, hi, mw, sh, d, mode)) fin = kFinListed;  // uniform
       }
-      __syncthreads();  // else (a list short of the remainder) the full path
+      __syncthreads();  // (else, a list short of the remainder, the full path)
     }
-    const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
-    full_topp_cut(rowp, j.V, j.aligned, c.T, c.p, c.mp, m, sh, d);
-  } else if (threadIdx.x == 0) {
-    d->mode = (c.mp > 0.0f) ? kRowFullMinP : kRowFullNone;
+    if (fin == kFinRow) {  // uniform
+      const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
+      full_topp_cut(rowp, j.V, j.aligned, c.T, c.p, c.mp, m, sh, d);
+      __syncthreads();  // (the cut's record)
+    }
+    if (j.fdraw)  // uniform
+      finish_full_draw<E>(j, row, c.T, c.seed, m, fin, static_cast<int>(got), v0, g0, ml, sh);
+  } else {
+    if (threadIdx.x == 0) d->mode = (c.mp > 0.0f) ? kRowFullMinP : kRowFullNone;
+    if (j.fdraw)  // uniform
+      finish_full_draw<E>(j, row, c.T, c.seed, m, kFinWhole, 0, 0ull, g0, ml, sh);
   }
 }
 

@@ -400,7 +400,10 @@ vs_status sample_logprobs_impl(const PenArgs* pen, const void* logits, int dt, i
       return VS_ERR_HIP;
     if (stage("row_full", stream, [&] { return vsk::launch_row_full(j, stream); }) != hipSuccess)
       return VS_ERR_HIP;
-    if (stage("gumbel", stream, [&] { return vsk::launch_gumbel(j, stream); }) != hipSuccess)
+    // (when the gather pass drew, the cut kernel finished every
+    // full-vocabulary row: no Gumbel pass over the kept sets)
+    if (!j.fdraw &&
+        stage("gumbel", stream, [&] { return vsk::launch_gumbel(j, stream); }) != hipSuccess)
       return VS_ERR_HIP;
   }
   if (out_full && !j.full_in_select) {

@@ -216,6 +216,18 @@ __device__ __forceinline__ uint32_t skip_hi(float lim_up, float eub) {
   return h - 256u;
 }
 
+// The random words b below which an id cannot beat the score bound lim:
+// with u = ((b >> 12) + 1/2) 2^-52, every b < skip_below(lim) has
+// 1 - u >= lim (1 + 2^-45) + 2^-52, so (1 - u)(1 - 2^-50) rounded stays
+// >= lim and the id scores below the bound (0: no b, while lim >= 1).
+__device__ __forceinline__ uint64_t skip_below(double lim) {
+  if (!(lim < 1.0)) return 0ull;
+  // (1 - lim (1 + 2^-45)) 2^52 - 2, whose rounding errors stay below 1.5
+  const double v = (1.0 - lim * (1.0 + 0x1p-45)) * 0x1p52 - 2.0;
+  if (!(v > 0.0)) return 0ull;
+  return static_cast<uint64_t>(v) << 12;  // floor(v) < 2^52
+}
+
 // Gumbel-max score prob / q with q = -log(u) (exponential noise), in double.
 __device__ __forceinline__ double gumbel_score(float e, uint64_t row_state, int id) {
   const double q = -log(uniform_of(row_state, id));
@@ -284,6 +296,7 @@ struct GPart {  // Gumbel partial result of one tile
   double score;
   int32_t id;
   int32_t kept;
+  float s;  // the best id's s = x / T, where the gather pass drew (else 0)
 };
 
 struct LsePart {  // log-sum-exp partial of one tile: max and sum of exp(x - max)

@@ -42,10 +42,13 @@ enum : uint32_t {
   kRowFullMinP = 2,   // full vocabulary, min-p only
   kRowFullTopP = 3,   // full vocabulary, top-p cut given by (tau, id_cut)
   kRowFull = 4,       // full vocabulary, the cut still to be found (heavy kernel)
-  kRowFullListed = 5, // top-p cut (tau, id_cut) found in the row's list, whose kept entries
-                      // and the gather pass's bests over the ids above the list's bucket
-                      // hold the draw (no Gumbel pass over the kept set)
+  kRowFullListed = 5, // top-p cut (tau, id_cut) found in the row's list; the cut kernel drew
+                      // from the list's kept entries and the gather pass's bests over the
+                      // ids above the list's bucket (no Gumbel pass over the kept set)
 };
+// In a call whose gather pass draws (j.fdraw), the cut kernel finishes every
+// full-vocabulary row, whatever its state above, and the Gumbel pass over the
+// kept sets does not run.
 
 // The top-p cut of a full-vocabulary row, found from its mass histogram.
 // bucket and rem come from the first segment's gather workgroup; count and
