@@ -362,7 +362,7 @@ def topp_method(wl, hints):
         return "gather_draw"
     if hints & vs.OPT_TOPP_KEPT_PASS:
         return "kept_pass"
-    return "gather_draw" if wl.B * wl.V >= 1 << 22 else "kept_pass"
+    return "gather_draw"
 
 
 def rooflines(wl, b: Bench, stage_avg, ms_per_step, kept, splitmix_rate):

@@ -90,12 +90,13 @@ typedef enum vs_status {
  *    best candidates all lie outside falls back to that pass.
  *  VS_OPT_TOPP_GATHER_DRAW: the pass that gathers the ids of the cut's bucket
  *    also draws over the ids above that bucket (all kept, wherever the cut
- *    falls inside it), and the draw's last step scores the kept ids of the
- *    bucket; no pass over the kept set (unless the bucket overflowed its list).
+ *    falls inside it), and the kernel that finds the cut scores the kept ids
+ *    of the bucket and finishes the row (a bucket that overflowed its list:
+ *    one pass over the row's kept set in that kernel); no pass over the kept
+ *    sets, and rows without the cut (top_p = 1) drawn in the gather pass too.
  *  VS_OPT_TOPP_KEPT_PASS: the Gumbel pass over the kept set after the cut.
  * Without one of them (or with more than one: the first listed wins), the
- * gather draw is taken when B * V >= 2^22 and the kept-set pass otherwise,
- * the faster of the two on the measured workloads on each side. */
+ * gather draw is taken, the fastest of the three on every measured workload. */
 #define VS_OPT_TOPP_REJECTION 256u
 #define VS_OPT_TOPP_GATHER_DRAW 512u
 #define VS_OPT_TOPP_KEPT_PASS 1024u
