@@ -330,7 +330,6 @@ __global__ __launch_bounds__(kThreads) void k_full_hist(Job j) {
 template <typename E, bool kDraw>
 __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
   __shared__ uint64_t sw[kThreads / kWave];
-  __shared__ uint32_t sc[kThreads / kWave];
   __shared__ double sd[kThreads / kWave];
   __shared__ int s_bucket;
   __shared__ uint64_t s_above_w;
@@ -338,7 +337,9 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
   __shared__ uint32_t s_n, s_lim, s_base;
   __shared__ uint64_t s_best;  // bits of the best score any thread has found
   __shared__ int s_chunk;      // the reader's next chunk, when claimed
-  __shared__ float s_win;      // the segment's best id's s (kDraw)
+  __shared__ int s_wi[kThreads / kWave];  // per-wave bests' ids, their s and counts
+  __shared__ float s_ws[kThreads / kWave];
+  __shared__ uint32_t s_wa[kThreads / kWave], s_wh[kThreads / kWave];
   int row, seg;
   if (!xcd_row_tile(blockIdx.x, j.B, j.fseg, &row, &seg)) return;  // uniform per block
   const E* rowp = static_cast<const E*>(j.logits) + static_cast<int64_t>(row) * j.ld;
@@ -614,33 +615,58 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
     pass(std::false_type{});
   else
     pass(std::true_type{});
-  double bb = -1.0;
-  int bid = 0x7fffffff;
-  if constexpr (kDraw) {
-    bb = block_max(best, sd);
-    bid = block_min(best == bb ? best_id : 0x7fffffff, reinterpret_cast<int*>(sc));
-    if (bb >= 0.0 && best == bb && best_id == bid) s_win = best_s;  // one thread (ids are distinct)
+  // The workgroup's draw record and counts with one barrier: each wave's
+  // best (score desc, id asc, with its s) and counts through slots of its
+  // own (the barrier also completes the LDS appends), combined by wave 0.
+  {
+    const int wv = static_cast<int>(threadIdx.x) / kWave;
+    double wb = -1.0;
+    int wi = 0x7fffffff;
+    float ws = 0.0f;
+    if constexpr (kDraw) {
+      wb = wave_max(best);
+      wi = wave_min(best == wb ? best_id : 0x7fffffff);
+      const uint64_t own = __ballot(best == wb && best_id == wi);  // (ids are distinct)
+      ws = own ? __shfl(best_s, __ffsll(static_cast<unsigned long long>(own)) - 1) : 0.0f;
+    }
+    const uint32_t wa = wave_sum(n_above), wh = wave_sum(n_hit);
+    if (lane() == 0) {
+      sd[wv] = wb;
+      s_wi[wv] = wi;
+      s_ws[wv] = ws;
+      s_wa[wv] = wa;
+      s_wh[wv] = wh;
+    }
   }
-  // this workgroup's counts into the row's record (block_sum's barriers also
-  // complete the LDS appends)
-  n_above = block_sum(n_above, sc);
-  n_hit = block_sum(n_hit, sc);
+  __syncthreads();
   // reservations are contiguous, so the buffer holds everything below the
   // first one that did not fit (s_lim), or all of s_n
   const uint32_t n = min(s_n, s_lim);
-  if (threadIdx.x == 0) {
-    // the segment's best over its above ids (a whole row's members), score
-    // desc, id asc, into the row's per-segment record (score -1: none),
-    // with a whole row's member count
-    if constexpr (kDraw)
-      j.gpart[static_cast<size_t>(row) * j.ntile3 + seg] =
-          GPart{bb >= 0.0 ? bb : -1.0, bid, whole ? static_cast<int32_t>(n_above) : 0,
-                bb >= 0.0 ? s_win : 0.0f};
-    s_base = n ? atomicAdd(cnt, n) : 0u;
-    if (n_above && !whole)
-      atomicAdd(reinterpret_cast<unsigned long long*>(&j.fcut[row].above_c),
-                static_cast<unsigned long long>(n_above));
-    if (n_hit) atomicAdd(&j.fcut[row].count, n_hit);
+  if (threadIdx.x < kWave) {  // wave 0
+    const int l = lane();
+    const bool slot = l < kThreads / kWave;
+    const double sb = slot ? sd[l] : -1.0;
+    const int si = slot ? s_wi[l] : 0x7fffffff;
+    const double bb = wave_max(sb);
+    const int bid = wave_min(sb == bb ? si : 0x7fffffff);
+    const uint64_t own = __ballot(slot && sb == bb && si == bid);
+    const float bs = own ? __shfl(slot ? s_ws[l] : 0.0f, __ffsll(static_cast<unsigned long long>(own)) - 1)
+                         : 0.0f;
+    const uint32_t ta = wave_sum(slot ? s_wa[l] : 0u), th = wave_sum(slot ? s_wh[l] : 0u);
+    if (l == 0) {
+      // the segment's best over its above ids (a whole row's members), score
+      // desc, id asc, into the row's per-segment record (score -1: none),
+      // with a whole row's member count
+      if constexpr (kDraw)
+        j.gpart[static_cast<size_t>(row) * j.ntile3 + seg] =
+            GPart{bb >= 0.0 ? bb : -1.0, bid, whole ? static_cast<int32_t>(ta) : 0,
+                  bb >= 0.0 ? bs : 0.0f};
+      s_base = n ? atomicAdd(cnt, n) : 0u;
+      if (ta && !whole)
+        atomicAdd(reinterpret_cast<unsigned long long*>(&j.fcut[row].above_c),
+                  static_cast<unsigned long long>(ta));
+      if (th) atomicAdd(&j.fcut[row].count, th);
+    }
   }
   __syncthreads();
   const uint32_t base = s_base;
