@@ -90,6 +90,67 @@ __device__ __forceinline__ bool penalize_range(E* rowp, const PenRow& pr, int V,
   int lgs = 10 < kMaxLog2 ? 10 : kMaxLog2;
   while ((1 << lgs) < 2 * n && lgs < kMaxLog2) ++lgs;
   const int S = 1 << lgs;
+  constexpr int kOwnMax = 4;  // history entries a thread holds at once
+  if (2 * n <= S && L <= kOwnMax * NT) {  // uniform
+    // One class, as below, with the history in registers: each thread's
+    // entries are loaded before the table is cleared, and the thread whose
+    // insert claims an id's slot (one per distinct id) loads that id's logit
+    // at once, so that both loads overlap the table's work; after the barrier
+    // that completes the counts, each owner applies its ids' penalties.
+    int32_t hid[kOwnMax];
+#pragma unroll
+    for (int r = 0; r < kOwnMax; ++r) {
+      const int i = static_cast<int>(threadIdx.x) + r * NT;
+      hid[r] = i < L ? pr.id(i) : 0;
+    }
+    for (int i = threadIdx.x; i < S; i += NT) {
+      keys[i] = kEmpty;
+      counts[i] = 0u;
+    }
+    if (threadIdx.x == 0) ps.badid = 0;
+    __syncthreads();  // the table and the flag are clear
+    uint32_t own[kOwnMax];
+    float ox[kOwnMax];
+#pragma unroll
+    for (int r = 0; r < kOwnMax; ++r) {
+      own[r] = kEmpty;
+      ox[r] = 0.0f;
+      const int i = static_cast<int>(threadIdx.x) + r * NT;
+      const int32_t id = hid[r];
+      if (i >= L) continue;
+      if (check_bad && (id < 0 || id >= V)) ps.badid = 1;
+      if (pr.bad || id < lo || id >= hi) continue;
+      const uint32_t u = static_cast<uint32_t>(id);
+      uint32_t slot = (u * 0x2545F491u) >> (32 - lgs);
+      while (true) {
+        const uint32_t prev = atomicCAS(&keys[slot], kEmpty, u);
+        if (prev == kEmpty || prev == u) {
+          if (prev == kEmpty) {  // this thread owns the id
+            own[r] = slot;
+            ox[r] = to_f32(rowp[id]);
+          }
+          if (i >= pr.nign) atomicAdd(&counts[slot], 1u);
+          break;
+        }
+        slot = (slot + 1) & static_cast<uint32_t>(S - 1);
+      }
+    }
+    __syncthreads();  // every id is counted, the flag final
+#pragma unroll
+    for (int r = 0; r < kOwnMax; ++r) {
+      if (own[r] == kEmpty) continue;
+      const uint32_t c = counts[own[r]];
+      const float x = ox[r];
+      float y = (x >= 0.0f) ? x / pr.rep : x * pr.rep;
+      if (c > 0u) {
+        y = y - pr.pres;
+        const float fc = pr.freq * static_cast<float>(c);
+        y = y - fc;
+      }
+      store_penalised<E>(rowp + hid[r], y);
+    }
+    return ps.badid != 0;
+  }
   if (2 * n <= S) {  // uniform
     // One class: the table holds every distinct id with half its slots to
     // spare, so no probe sequence can fail. Clear, count, apply, with two
