@@ -362,21 +362,19 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
 
   // The cut bucket: thread t holds buckets [4 t, 4 t + 4); an exclusive scan
   // over the threads gives the mass of the buckets before.
+  // (an in-wave DPP scan, then the waves' totals through LDS: one barrier,
+  // which also publishes the shared state cleared here)
   uint64_t w[kPer];
-  uint64_t cw = 0, target = 0;
+  uint64_t cw = 0, lw = 0, inc = 0;
+  const int wv = static_cast<int>(threadIdx.x) / kWave;
   if (!whole) {  // uniform
-    uint64_t lw = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       w[i] = ghw[threadIdx.x * kPer + i];
       lw += w[i];
     }
-    uint64_t total_w;
-    cw = block_scan_incl(lw, sw, &total_w) - lw;
-    // the kept prefix is the shortest whose mass reaches p * total; masses
-    // are integers, so "cum >= thr" is "cum >= ceil(thr)" (at least one id)
-    const double thr = static_cast<double>(c.p) * static_cast<double>(total_w);
-    target = ceil(thr) >= 1.0 ? static_cast<uint64_t>(ceil(thr)) : 1ull;
+    inc = wave_scan_incl_u64(lw);
+    if (lane() == kWave - 1) sw[wv] = inc;
   }
   if (threadIdx.x == 0) {
     s_bucket = -1;
@@ -387,6 +385,17 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
   __syncthreads();
   int bstar = kFullBuckets - 1;  // (whole rows: unused)
   if (!whole) {  // uniform
+    uint64_t before = 0, total_w = 0;
+    for (int q = 0; q < kThreads / kWave; ++q) {
+      const uint64_t t = sw[q];
+      before += q < wv ? t : 0ull;
+      total_w += t;
+    }
+    cw = before + inc - lw;
+    // the kept prefix is the shortest whose mass reaches p * total; masses
+    // are integers, so "cum >= thr" is "cum >= ceil(thr)" (at least one id)
+    const double thr = static_cast<double>(c.p) * static_cast<double>(total_w);
+    const uint64_t target = ceil(thr) >= 1.0 ? static_cast<uint64_t>(ceil(thr)) : 1ull;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int b = threadIdx.x * kPer + i;

@@ -10,6 +10,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 #include "../../include/vs.h"
@@ -520,6 +521,30 @@ __device__ __forceinline__ uint32_t wave_scan_incl_u32(uint32_t v) {
   return static_cast<uint32_t>(x);
 }
 
+// The same inclusive prefix sum for a u64 (sums below 2^64): each step moves
+// both halves with the same DPP control (masked lanes read 0) and adds with
+// carry.
+template <int kCtrl, int kRowMask, int kBankMask>
+__device__ __forceinline__ uint64_t dpp_mv_u64(uint64_t x) {
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(x)), kCtrl,
+                                             kRowMask, kBankMask, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(x >> 32)),
+                                             kCtrl, kRowMask, kBankMask, false);
+  return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+__device__ __forceinline__ uint64_t wave_scan_incl_u64(uint64_t v) {
+  const uint64_t x0 = v;
+  uint64_t x = x0;
+  x += dpp_mv_u64<0x111, 0xF, 0xF>(x0);  // row_shr:1..3 of the inputs
+  x += dpp_mv_u64<0x112, 0xF, 0xF>(x0);
+  x += dpp_mv_u64<0x113, 0xF, 0xF>(x0);
+  x += dpp_mv_u64<0x114, 0xF, 0xE>(x);   // row_shr:4, banks 1-3
+  x += dpp_mv_u64<0x118, 0xF, 0xC>(x);   // row_shr:8, banks 2-3
+  x += dpp_mv_u64<0x142, 0xA, 0xF>(x);   // row_bcast:15 into rows 1 and 3
+  x += dpp_mv_u64<0x143, 0xC, 0xF>(x);   // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
 // The lanes that keep the larger value of their pair in a bitonic step (block
 // size K, partner distance J), as a wave mask fixed at compile time.
 template <int K, int J, bool kDesc>
@@ -799,10 +824,16 @@ __device__ __forceinline__ T block_sum(T v, T* scratch) {
 template <typename T>
 __device__ __forceinline__ T block_scan_incl(T v, T* scratch, T* total) {
   const int l = lane();
+  if constexpr (std::is_same<T, uint64_t>::value) {  // in-wave: DPP row shifts and broadcasts
+    v = wave_scan_incl_u64(v);
+  } else if constexpr (std::is_integral<T>::value && sizeof(T) == 4) {
+    v = static_cast<T>(wave_scan_incl_u32(static_cast<uint32_t>(v)));
+  } else {
 #pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const T w = __shfl_up(v, o);
-    if (l >= o) v += w;
+    for (int o = 1; o < kWave; o <<= 1) {
+      const T w = __shfl_up(v, o);
+      if (l >= o) v += w;
+    }
   }
   const int w = threadIdx.x / kWave, nw = blockDim.x / kWave;
   __syncthreads();
