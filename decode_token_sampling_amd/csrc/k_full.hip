@@ -41,21 +41,14 @@ constexpr int kGatherBuf = 2048;  // ids a gather workgroup collects in LDS befo
 // The rows the passes take: kPassTopP, a full-vocabulary top-p row (the
 // histogram, its cut bucket, the gather); kPassWhole, a full-vocabulary row
 // without the cut (top_p >= 1), which only the drawing gather pass takes, to
-// draw over all of its members; kPassNone, any other. Without j.full_chain the
-// row kernel ran first and its descriptor routes the row; with it, route_row.
+// draw over all of its members; kPassNone, any other (route_row decides).
 enum : int { kPassNone = 0, kPassTopP = 1, kPassWhole = 2 };
-__device__ __forceinline__ int pass_row(const Job& j, int row, const RowDesc& d,
-                                        const RoutePre& rp, RowCfg* c, float* m) {
-  if (!j.full_chain) {  // uniform
-    if (d.mode != kRowFull) return kPassNone;
-    *c = load_cfg(row, j.V, j.T, j.k, j.p, j.mp, j.seeds);
-    *m = d.m;
-  } else {
-    const RowRoute r = route_row(j, row, rp);
-    *c = r.c;
-    *m = r.m;
-    if (!r.full) return kPassNone;
-  }
+__device__ __forceinline__ int pass_row(const Job& j, int row, const RoutePre& rp, RowCfg* c,
+                                        float* m) {
+  const RowRoute r = route_row(j, row, rp);
+  *c = r.c;
+  *m = r.m;
+  if (!r.full) return kPassNone;
   return c->p < 1.0f ? kPassTopP : kPassWhole;
 }
 
@@ -209,13 +202,12 @@ __global__ __launch_bounds__(kThreads) void k_full_hist(Job j) {
   const int hi = min(j.V, lo + j.fseg_len);
   // the route's loads, then the segment's first ones, before the row's route
   // is known (wasted, and harmless, for a row this pass does not take)
-  const RowDesc dsc = j.desc[row];  // (the row kernel's, when it ran first)
   const RoutePre rp = route_preload(j, row);
   SegReader<E, 4> rd;
   rd.start(rowp, lo, hi, j.aligned != 0);
   RowCfg c;
   float m;
-  if (pass_row(j, row, dsc, rp, &c, &m) != kPassTopP) return;  // uniform per block
+  if (pass_row(j, row, rp, &c, &m) != kPassTopP) return;  // uniform per block
   for (int i = threadIdx.x; i < kFullBuckets; i += kThreads) hw[i] = 0ull;
   if (threadIdx.x == 0) s_bound = 0ull;
   __syncthreads();
@@ -348,13 +340,12 @@ __global__ __launch_bounds__(kThreads) void k_full_gather(Job j) {
   // vectors in flight per thread (fewer with the draw, whose random words
   // need the registers); the first before the row's route is known
   constexpr int kGU = kDraw ? 2 : 4;
-  const RowDesc dsc = j.desc[row];  // (the row kernel's, when it ran first)
   const RoutePre rp = route_preload(j, row);
   SegReader<E, kGU> rd;
   rd.start(rowp, lo, hi, j.aligned != 0, &s_chunk);
   RowCfg c;
   float m;
-  const int kind = pass_row(j, row, dsc, rp, &c, &m);
+  const int kind = pass_row(j, row, rp, &c, &m);
   if (kind == kPassNone || (!kDraw && kind == kPassWhole)) return;  // uniform per block
   // a row without the cut: every member is drawn over (kDraw), nothing gathered
   const bool whole = kDraw && kind == kPassWhole;

@@ -17,11 +17,11 @@
 // monotone in s), the bucket where the cumulative mass reaches top_p * total,
 // then the exact cut inside that bucket (gathered and sorted in LDS, or by a
 // mass-weighted radix select when the bucket holds more than 8192 ids).
-// When a call runs the full-vocabulary passes over 16 rows or more, the light
-// kernel is not launched: k_row_full does its work at entry (same code, same
-// results), the streaming pass clears the histogram counters, and every row is
-// routed to the full-vocabulary path from its tiles' flags and maxima alone
-// (route_row), so no row descriptor has to exist before the histogram pass.
+// When a call runs the full-vocabulary passes, the light kernel is not
+// launched: k_row_full does its work at entry (same code, same results), the
+// streaming pass clears the histogram counters, and every row is routed to the
+// full-vocabulary path from its tiles' flags and maxima alone (route_row), so
+// no row descriptor has to exist before the histogram pass.
 #include "vs_device.h"
 #include "vs_kernels.h"
 
@@ -774,21 +774,10 @@ __device__ __forceinline__ void light_row(const Job& j, int row, LightSh& sh,
         if (m == kInf) {
           status = VS_ROW_BAD_PARAM;
         } else {
+          // (the passes ran already: this is the cut kernel's entry, and
+          // the streaming pass cleared their counters)
           next = kRowFull;
           if (threadIdx.x == 0) j.desc[row].m = m;
-          // the histogram and gather passes accumulate from zero (cleared
-          // here when they run after this kernel; with the cut kernel doing
-          // this work they have run already, after the streaming pass
-          // cleared their counters)
-          if (c.p < 1.0f && !j.full_chain) {
-            uint64_t* hw = j.fhw + static_cast<size_t>(row) * kFullBuckets;
-            for (int i = threadIdx.x; i < kFullBuckets; i += blockDim.x) hw[i] = 0ull;
-            if (threadIdx.x == 0) {
-              j.fcnt[row] = 0u;
-              j.fcut[row].count = 0u;
-              j.fcut[row].above_c = 0ull;
-            }
-          }
         }
       }
     }
@@ -1456,11 +1445,11 @@ __device__ __forceinline__ void finish_full_draw(const Job& j, int row, float T,
 // (route_row, the histogram and gather passes' own decision) gets its cut,
 // which sets the draw's mode for the Gumbel kernels; in a call whose gather
 // pass drew (j.fdraw) this kernel then finishes the draw of every such row
-// itself (finish_full_draw) and the Gumbel kernels do not run. When the row kernel is
-// not launched before the passes (j.full_chain), this kernel also does its
-// work: a full-vocabulary row's status, log-sum-exp and kept-mask row before
-// the cut, and every other row the streaming pass did not finish gets the
-// row kernel's work (light_row), in parallel with the cuts.
+// itself (finish_full_draw) and the Gumbel kernels do not run. The row kernel
+// is not launched in a call that runs these passes: this kernel does its work,
+// a full-vocabulary row's status, log-sum-exp and kept-mask row before the
+// cut, and every other row the streaming pass did not finish gets the row
+// kernel's work (light_row), in parallel with the cuts.
 union RowFullSh {
   FullSh full;
   LightSh light;
@@ -1475,7 +1464,6 @@ __global__ __launch_bounds__(kFullThreads) void k_row_full(Job j) {
   // every load the row may need is issued before any is used (the cut record
   // and this thread's list slot are read whatever the row's route, and used
   // only for rows with a cut): their latencies overlap
-  const RowDesc dsc = *d;  // (the row kernel's, when it ran before the passes)
   const RoutePre rp = route_preload(j, row);
   const FullCut fc = j.fcut[row];
   const uint32_t got = j.fcnt[row];
@@ -1483,17 +1471,10 @@ __global__ __launch_bounds__(kFullThreads) void k_row_full(Job j) {
   const uint64_t v0 = lst[threadIdx.x];  // (kFullThreads <= kFullListCap)
   // and the row kernel's first loads, for the rows that take its work
   LightLoads<kStageMax / kFullThreads> L;
-  if (j.full_chain) light_load(j, row, L);
-  RowRoute rt;
-  if (j.full_chain) {  // uniform
-    rt = route_row(j, row, rp);
-  } else {  // the row kernel routed the row and wrote its m
-    rt.c = load_cfg(row, j.V, j.T, j.k, j.p, j.mp, j.seeds);
-    rt.m = dsc.m;
-    rt.full = dsc.mode == kRowFull;
-  }
+  light_load(j, row, L);
+  const RowRoute rt = route_row(j, row, rp);
   if (!rt.full) {  // uniform over the block
-    if (j.full_chain) light_row<E>(j, row, sm.light, L);
+    light_row<E>(j, row, sm.light, L);
     return;
   }
   const RowCfg& c = rt.c;
@@ -1503,18 +1484,16 @@ __global__ __launch_bounds__(kFullThreads) void k_row_full(Job j) {
   GPart g0{-1.0, 0x7fffffff, 0};
   if (j.fdraw && lane() < j.fseg)  // (j.fdraw uniform)
     g0 = j.gpart[static_cast<size_t>(row) * j.ntile3 + lane()];
-  // (without j.full_chain the row kernel ran before the passes and did the
-  // row's writes)
-  if (j.full_chain && j.lse && j.k_lp > 0) {  // uniform
+  if (j.lse && j.k_lp > 0) {  // uniform
     // the row kernel's writes for the row, its top-k log-probs included (the
     // same route: the row kernel sends it to the full-vocabulary path)
     light_row<E>(j, row, sm.light, L);
     __syncthreads();  // (the cut reuses the LDS)
-  } else if (j.full_chain) {  // uniform
+  } else {
     full_row_writes(j, row, m, sh, L);
   }
   // the row's (max, log-sum-exp) for the sampled id's log-prob (thread 0
-  // wrote it, here or in the row kernel; in flight during the cut)
+  // wrote it above; in flight during the cut)
   float2 ml = make_float2(0.0f, 0.0f);
   if (j.fdraw && j.tok_sampled && threadIdx.x == 0) ml = j.rlse[row];
   if (c.p < 1.0f) {

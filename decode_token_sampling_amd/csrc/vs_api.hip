@@ -378,16 +378,14 @@ vs_status sample_logprobs_impl(const PenArgs* pen, const void* logits, int dt, i
   widen_for_full_write(j);
   j.full_vec = full_vec(out_full, ld_out);
   // Unless a hint rules out full-vocabulary rows, their passes run (each
-  // returns at once for rows it does not take). From kMergeRows rows on, the
-  // row kernel's work moves into the cut kernel after them, which saves a
-  // launch and its wait on the path: the streaming pass clears the passes'
-  // counters, and every pass routes the rows itself (measured: w32x151936
-  // 91.6 -> 84.3 us, w64x262144 111.3 -> 107.2 us; on w4x32000 the row
-  // kernel's 256-thread workgroups finish its rows sooner than the cut
-  // kernel's 1024-thread ones, 54.8 against 56.7 us).
-  constexpr int kMergeRows = 16;
+  // returns at once for rows it does not take), and the row kernel's work
+  // then moves into the cut kernel after them, which saves a launch and its
+  // wait on the path: the streaming pass clears the passes' counters, and
+  // every pass routes the rows itself (measured: w32x151936 91.6 -> 84.3 us,
+  // w64x262144 111.3 -> 107.2 us; w4x32000 43.4 -> 40.8 us once the cut
+  // kernel also finished the draw).
   const bool full_passes = !(hints & (VS_HINT_NO_FULLVOCAB | VS_HINT_ALL_GREEDY | VS_HINT_SMALL_TOPK));
-  j.full_chain = (full_passes && B >= kMergeRows) ? 1 : 0;
+  j.full_chain = full_passes ? 1 : 0;
   if (stage("select", stream, [&] { return vsk::launch_select(j, stream); }) != hipSuccess)
     return VS_ERR_HIP;
   if (!select_finishes && !j.full_chain &&

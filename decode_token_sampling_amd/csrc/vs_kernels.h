@@ -155,7 +155,8 @@ struct Job {
   int fseg_len;        // ids per segment (a multiple of 8)
   int full_in_select;      // the streaming pass writes out_full itself (it finishes every row)
   int full_chain;          // the full-vocabulary passes run: the streaming pass clears their
-                           // counters and the cut kernel does the row kernel's work
+                           // counters and the cut kernel does the row kernel's work (the
+                           // row kernel is not launched)
   int full_vec;            // out_full rows take 16-byte stores
   // workspace; streaming-pass geometry
   int ntile;  // tiles per row
