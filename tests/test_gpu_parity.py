@@ -629,6 +629,41 @@ def test_sample_logprobs_fused(V, dtype, k):
     _check_fused_logprobs(x, V, out, k)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("k", [0, 5])
+def test_gather_draw_finish_with_logprobs(dtype, k):
+    """The default draw of full-vocabulary rows (the gather pass draws, the cut
+    kernel finishes each row) with the sampled ids' log-probs and no kept mask,
+    on every way the cut kernel finishes a row: a cut from the gathered list,
+    a cut bucket beyond the list (a row of one value: the one-pass draw over
+    the kept set), rows without the cut (top_p = 1) with and without min-p; at
+    T = 1 (where the sampled id's logit is its s) and T != 1; a batch below
+    and one above 16 rows. Ids, kept counts, status and log-probs against the
+    oracle."""
+    import decode_token_sampling_amd as vs
+    V = 40000
+    for B in (6, 20):
+        x = _row_shapes(4000 + B + 13 * k, B, V, dtype)
+        one = synth.f32_to_bf16_bits(np.array([np.float32(0.5)]))[0] if dtype == "bf16" else np.float32(0.5)
+        x[1] = one                                   # one value: the bucket holds every id
+        x[B - 2] = one
+        rows = np.arange(B)
+        T = np.where(rows % 2 == 0, 1.0, 0.7).astype(np.float32)
+        p = np.array([0.9, 0.6, 1.0, 0.99, 1.0, 0.3], np.float32)[rows % 6]
+        mp = np.where(rows % 3 == 2, 0.05, 0.0).astype(np.float32)
+        w = dict(temperature=T, top_k=np.zeros(B, np.int32), top_p=p, min_p=mp,
+                 seeds=(900 + rows).astype(np.uint64))
+        out = vs.sample_logprobs(to_device(x), dev(T, np.float32), dev(w["top_k"], np.int32),
+                                 dev(p, np.float32), dev(mp, np.float32),
+                                 dev(np.asarray(w["seeds"], np.uint64).view(np.int64), np.int64),
+                                 k=k, mask=False, V=V)
+        torch.cuda.synchronize()
+        g = dict(ids=out["ids"].cpu().numpy(), kept=out["kept"].cpu().numpy(),
+                 status=out["status"].cpu().numpy())
+        assert compare_sample(g, oracle_sample(x, V, w, mask=False), check_mask=False) == 0
+        _check_fused_logprobs(x, V, out, k)
+
+
 def test_fused_equals_separate_calls():
     import decode_token_sampling_amd as vs
     V, B = 50000, 24
