@@ -1028,38 +1028,61 @@ __device__ __forceinline__ bool sort_cut_from_list(const FullCut& fc, int n, uin
     return sh.b32[3] != 0;
   }
   // only the first P entries (P the power of two >= n) need sorting: every
-  // entry past them is padding, and so is every sorted entry past n
+  // entry past them is padding, and so is every sorted entry past n. Each
+  // wave sorts its 64 in registers (descending); then runs of L merge
+  // pairwise into 2L through two LDS buffers in turn, one barrier a level: an
+  // entry's place in the merged run is its index in its own run plus the
+  // entries of the partner run that come before it (a binary search; on
+  // equal values, padding, those of the left run first).
   const int P = n <= 1 ? 1 : 1 << (32 - __clz(n - 1));
-  if (wv * kWave < P) v = (wv & 1) ? wave_sort_u64<false>(v) : wave_sort_u64<true>(v);
-  int step = 0;
-  for (int k = 2 * kWave; k <= P; k <<= 1) {
-    // runs of k entries alternate descending / ascending; the lower index of
-    // each pair keeps the larger entry of a descending run
-    const bool desc = (t & k) == 0;  // uniform per wave
-    for (int jj = k >> 1; jj >= kWave; jj >>= 1) {
-      uint64_t* x = (step++ & 1) ? xb : xa;
-      x[t] = v;
-      __syncthreads();  // (the other buffer's reads, a step ago, are done too)
-      const uint64_t o = x[t ^ jj];
-      const bool lower = (t & jj) == 0;  // uniform per wave
-      if (lower == desc ? o > v : o < v) v = o;
+  if (wv * kWave < P) v = wave_sort_u64<true>(v);
+  uint64_t* src = xa;
+  uint64_t* dst = xb;
+  if (t < P) src[t] = v;
+  __syncthreads();
+  for (int L = kWave; L < P; L <<= 1) {  // uniform
+    if (t < P) {
+      const int run = t / L, i = t - run * L;
+      const uint64_t* pr = src + (run ^ 1) * L;
+      const bool left = (run & 1) == 0;
+      int lo = 0, hi = L;  // the partner entries before v: larger, or equal from the left run
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        const uint64_t o = pr[mid];
+        if (o > v || (!left && o == v)) lo = mid + 1;
+        else hi = mid;
+      }
+      dst[(run & ~1) * L + i + lo] = v;
     }
-    v = desc ? wave_merge_steps<true>(v) : wave_merge_steps<false>(v);
+    __syncthreads();
+    uint64_t* tmp = src;
+    src = dst;
+    dst = tmp;
+    if (t < P) v = src[t];
   }
-  // thread t holds the entry of rank t
+  // thread t holds the entry of rank t; the running mass (in-wave DPP scans
+  // of 16-bit halves, then the waves' totals: one barrier) first reaches the
+  // remainder at the cut, whose rank is its thread's index
   uint32_t w = 0u;
   if (v != 0ull) {
     uint64_t wt;
     int b;
     w = ft.mass(key2f(pkey(v)), &wt, &b) ? static_cast<uint32_t>(wt) : 0u;
   }
-  uint64_t total;
-  const uint64_t cum = block_scan_incl(static_cast<uint64_t>(w), sh.r64, &total);
-  const int rank = block_sum(cum < fc.rem ? 1 : 0, sh.ri);  // the running mass is nondecreasing
-  if (rank >= n) return false;  // uniform: the list's masses fall short of the remainder
-  if (t == rank) {
-    set_cut(d, sh, mode, pkey(v), pid(v), static_cast<int32_t>(fc.above_c) + rank + 1);
+  const uint32_t slo = wave_scan_incl_u32(w & 0xffffu);
+  const uint32_t shi = wave_scan_incl_u32(w >> 16);
+  const uint64_t in_w = (static_cast<uint64_t>(shi) << 16) + slo;
+  if (lane() == kWave - 1) sh.r64[wv] = in_w;
+  __syncthreads();
+  uint64_t cum = in_w, total = 0ull;
+  for (int q = 0; q < kFullThreads / kWave; ++q) {
+    const uint64_t tq = sh.r64[q];
+    cum += q < wv ? tq : 0ull;
+    total += tq;
   }
+  if (total < fc.rem) return false;  // uniform: the list's masses fall short of the remainder
+  if (cum >= fc.rem && cum - w < fc.rem)  // (one thread: the running mass is nondecreasing)
+    set_cut(d, sh, mode, pkey(v), pid(v), static_cast<int32_t>(fc.above_c) + t + 1);
   return true;
 }
 
