@@ -1230,9 +1230,293 @@ __global__ __launch_bounds__(1024) void k_select(Job j) {
   }
 }
 
+// The greedy call with the full log-softmax written, one read of the logits:
+// one 1024-thread workgroup per row keeps the whole row on chip, 23 of each
+// thread's 16-byte vectors in registers and 9 in LDS (rows of 94,209 to
+// 131,072 fp32 values: the register part is then always whole), so the write
+// reads nothing again (the streaming pass re-reads each row for it, mostly
+// from beyond L2). Vector g = r * 1024 + t is thread t's r-th. Each thread
+// forms its own maximum and sum of exponentials (the streaming pass's shifted
+// base-2 form; a NaN or +inf value leaves a NaN sum), and each wave bounds the
+// top-k: the k-th largest of its threads' maxima, and the ceil(k/16)-th (k
+// values reach the larger of the first's maximum over the waves and the
+// second's minimum). One barrier combines them; the log-softmax
+// (x - M) - log S is written from the resident values, the values at or above
+// the bound are gathered in LDS and the threads whose maximum is M find the
+// argmax (lowest id among equal values); after a second barrier one wave keeps
+// the k best of the gathered values by sorts and merges 64 at a time (with
+// more than kResPool of them, k rounds of a block maximum over the row read
+// again, below the last one taken). The outputs and their edge cases are the
+// streaming pass's for greedy rows.
+constexpr int kResT = 1024;
+constexpr int kResW = kResT / kWave;
+constexpr int kResReg = 23;  // 16-byte vectors a thread keeps in registers
+constexpr int kResLds = 9;   // and in LDS
+constexpr int kResFirst = 14;  // register vectors loaded with the LDS part's
+constexpr int kResPool = 1024;
+constexpr int kResMinV = kResReg * 4 * kResT + 1;          // 94,209 values
+constexpr int kResMaxV = (kResReg + kResLds) * 4 * kResT;  // 131,072 values
+struct ResSh {
+  f32x4 lv[kResLds * kResT];  // 144 KB
+  uint64_t pool[kResPool];
+  uint64_t wx[kResW];
+  float wm[kResW], ws[kResW];
+  uint32_t wta[kResW], wtb[kResW];
+  int pool_n, amin;
+};
+__device__ __forceinline__ f32x4 res_load(const float* p) {
+  const uint4 u = load16(p);
+  f32x4 x;
+  x.x = __uint_as_float(u.x);
+  x.y = __uint_as_float(u.y);
+  x.z = __uint_as_float(u.z);
+  x.w = __uint_as_float(u.w);
+  return x;
+}
+__device__ __forceinline__ float res_max4(const f32x4& x) {
+  return fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w));
+}
+// sum over the vector of 2^(x log2 e - c), or exp(x - c) in huge mode
+template <bool kHuge>
+__device__ __forceinline__ float res_exp4(const f32x4& x, float c) {
+  if (kHuge) return (__expf(x.x - c) + __expf(x.y - c)) + (__expf(x.z - c) + __expf(x.w - c));
+  return (__builtin_amdgcn_exp2f(fmaf(x.x, kL2E, -c)) + __builtin_amdgcn_exp2f(fmaf(x.y, kL2E, -c))) +
+         (__builtin_amdgcn_exp2f(fmaf(x.z, kL2E, -c)) + __builtin_amdgcn_exp2f(fmaf(x.w, kL2E, -c)));
+}
+
+__global__ __launch_bounds__(kResT) void k_select_resident(Job j) {
+  __shared__ ResSh sh;
+  const int row = blockIdx.x;
+  const int t = static_cast<int>(threadIdx.x), ln = lane();
+  const int wv = __builtin_amdgcn_readfirstlane(t / kWave);
+  const float* rowp = static_cast<const float*>(j.logits) + static_cast<int64_t>(row) * j.ld;
+  const int nvec = j.V / 4;
+  const float nanv = __builtin_nanf("");
+  const int kl = j.k_lp;
+  // the LDS part's loads first (their registers are free again once stored)
+  f32x4 tmp[kResLds];
+  // (vectors past the row load its last one and read as -inf when used: a
+  // value written over a load in flight would wait for it)
+#pragma unroll
+  for (int r = 0; r < kResLds; ++r) tmp[r] = res_load(rowp + 4 * min((kResReg + r) * kResT + t, nvec - 1));
+  f32x4 rv[kResReg];
+#pragma unroll
+  for (int r = 0; r < kResFirst; ++r) rv[r] = res_load(rowp + 4 * (r * kResT + t));
+  // this thread's maximum m and sum s of 2^(x log2 e - c), c = fl(m log2 e),
+  // taken vector by vector as the loads land (a larger maximum rescales s by
+  // 2^(c_old - c_new)); a NaN value, or m = +inf, leaves s NaN
+  float m = -kInf, cs = -kInf, s = 0.0f;
+  const auto acc = [&](const f32x4& x) __attribute__((always_inline)) {
+    const float mn = fmaxf(m, res_max4(x));
+    const float cn = mn * kL2E;
+    const bool fin = mn > -kInf;
+    s *= fin ? __builtin_amdgcn_exp2f(cs - cn) : 1.0f;
+    s += res_exp4<false>(x, fin ? cn : 0.0f);
+    m = mn;
+    cs = cn;
+  };
+#pragma unroll
+  for (int r = 0; r < kResLds; ++r) {
+    f32x4 x = tmp[r];
+    if ((kResReg + r) * kResT + t >= nvec) x.x = x.y = x.z = x.w = -kInf;
+    acc(x);
+    sh.lv[r * kResT + t] = x;  // (each thread reads back its own)
+  }
+  // (the values above are taken and stored here, before the remaining loads,
+  // so their registers are free for them)
+  asm volatile("" : "+v"(m), "+v"(s), "+v"(cs) : : "memory");
+#pragma unroll
+  for (int r = kResFirst; r < kResReg; ++r) rv[r] = res_load(rowp + 4 * (r * kResT + t));
+  if (t == 0) {
+    sh.pool_n = 0;
+    sh.amin = 0x7fffffff;
+  }
+#pragma unroll
+  for (int r = 0; r < kResReg; ++r) {
+    acc(rv[r]);
+    // (each vector's terms as it lands, not after the last one)
+    asm volatile("" : "+v"(m), "+v"(s), "+v"(cs));
+  }
+  // s relative to m; with a maximum of 2^120 or more in the wave (m log2 e
+  // near overflow) the sum again as exp(x - m)
+  if (__ballot(fabsf(m) >= 0x1p120f && fabsf(m) < kInf) != 0ull) {
+    const float cu = m > -kInf ? m : 0.0f;
+    float s2[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int r = 0; r < kResReg; ++r) s2[r & 1] += res_exp4<true>(rv[r], cu);
+#pragma unroll 3
+    for (int r = 0; r < kResLds; ++r) s2[r & 1] += res_exp4<true>(sh.lv[r * kResT + t], cu);
+    s = s2[0] + s2[1];
+  } else if (m > -kInf) {
+    s *= __builtin_amdgcn_exp2f(-fmaf(m, kL2E, -cs));
+  }
+  {
+    const float wm = wave_max(m);
+    const float ws = wave_sum((m > -kInf) ? s * __expf(m - wm) : s);
+    uint32_t ta = 0u, tb = 0u;
+    if (kl > 0) {
+      const uint32_t key = f2key(m);
+      ta = wave_kth_largest(key, kl);
+      tb = wave_kth_largest(key, (kl + kResW - 1) / kResW);
+    }
+    if (ln == 0) {
+      sh.wm[wv] = wm;
+      sh.ws[wv] = ws;
+      sh.wta[wv] = ta;
+      sh.wtb[wv] = tb;
+    }
+  }
+  __syncthreads();
+  const float wmi = ln < kResW ? sh.wm[ln] : -kInf;
+  const float M = wave_max(wmi);
+  const float wsi = ln < kResW ? sh.ws[ln] : 0.0f;
+  const float S = wave_sum((wmi > -kInf) ? wsi * __expf(wmi - M) : wsi);
+  const uint32_t tau = kl > 0 ? max(wave_max(ln < kResW ? sh.wta[ln] : 0u),
+                                    wave_min(ln < kResW ? sh.wtb[ln] : 0xffffffffu))
+                              : 0u;
+  const bool rowbad = __builtin_isnan(S) || !(M > -kInf) || !(M < kInf);
+  const float Mo = rowbad ? nanv : M;
+  const float logS = rowbad ? nanv : logf(S);
+  // the argmax: the lowest id holding M, from the threads whose maximum it is
+  if (!rowbad && m == M) {
+    int aid = 0x7fffffff;
+#pragma unroll 1
+    for (int r = kResLds - 1; r >= 0; --r) {
+      const f32x4 x = sh.lv[r * kResT + t];
+      const int id = 4 * ((kResReg + r) * kResT + t);
+      aid = x.w == M ? id + 3 : aid;
+      aid = x.z == M ? id + 2 : aid;
+      aid = x.y == M ? id + 1 : aid;
+      aid = x.x == M ? id : aid;
+    }
+#pragma unroll
+    for (int r = kResReg - 1; r >= 0; --r) {
+      const int id = 4 * (r * kResT + t);
+      aid = rv[r].w == M ? id + 3 : aid;
+      aid = rv[r].z == M ? id + 2 : aid;
+      aid = rv[r].y == M ? id + 1 : aid;
+      aid = rv[r].x == M ? id : aid;
+    }
+    atomicMin(&sh.amin, aid);
+  }
+  // the candidates for the top-k log-probs
+  const bool gather = kl > 0 && !rowbad;
+  const float tauf = key2f(tau);
+  const auto take = [&](const f32x4& x, int g) __attribute__((always_inline)) {
+    // (four compares: a maximum here would be the first pass's, kept live)
+    if (((x.x >= tauf) | (x.y >= tauf) | (x.z >= tauf) | (x.w >= tauf)) && g < nvec) {
+      const float e[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (e[q] >= tauf) {
+          const int at = atomicAdd(&sh.pool_n, 1);
+          if (at < kResPool) sh.pool[at] = pack(f2key(e[q]), 4 * g + q);
+        }
+      }
+    }
+  };
+  // the log-softmax from the resident values
+  float* orow = j.out_full + static_cast<int64_t>(row) * j.ld_out;
+#pragma unroll
+  for (int r = 0; r < kResReg; ++r) {
+    const int g = r * kResT + t;
+    if (gather) take(rv[r], g);
+    f32x4 o;
+    o.x = (rv[r].x - Mo) - logS;
+    o.y = (rv[r].y - Mo) - logS;
+    o.z = (rv[r].z - Mo) - logS;
+    o.w = (rv[r].w - Mo) - logS;
+    __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(orow + 4 * g));
+  }
+#pragma unroll 3
+  for (int r = 0; r < kResLds; ++r) {
+    const int g = (kResReg + r) * kResT + t;
+    const f32x4 x = sh.lv[r * kResT + t];
+    if (gather) take(x, g);
+    if (g < nvec) {
+      f32x4 o;
+      o.x = (x.x - Mo) - logS;
+      o.y = (x.y - Mo) - logS;
+      o.z = (x.z - Mo) - logS;
+      o.w = (x.w - Mo) - logS;
+      __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(orow + 4 * g));
+    }
+  }
+  __syncthreads();
+  // the row's outputs (a greedy row's, as the streaming pass writes them)
+  // (by wave 1: wave 0 keeps the top-k meanwhile)
+  if (t == kWave) {
+    const RowCfg c = load_cfg(row, j.V, j.T, j.k, j.p, j.mp, j.seeds);
+    int status = c.status | (rowbad ? VS_ROW_BAD_LOGITS : 0);
+    if (status == 0) {
+      if ((j.hints & VS_HINT_ALL_GREEDY) && c.mode != kModeGreedy) status = VS_ROW_HINT_VIOLATED;
+      if ((j.hints & VS_HINT_NO_GREEDY) && c.mode == kModeGreedy) status = VS_ROW_HINT_VIOLATED;
+      if ((j.hints & VS_HINT_SMALL_TOPK) && c.mode != kModeGreedy && c.mode != kModeKFast)
+        status = VS_ROW_HINT_VIOLATED;
+    }
+    const int32_t id = status ? -1 : sh.amin;
+    j.rlse[row] = rowbad ? make_float2(nanv, nanv) : make_float2(M, logS);
+    j.desc[row].mode = kRowDone;
+    j.out_ids[row] = id;
+    if (j.out_kept) j.out_kept[row] = status ? 0 : 1;
+    if (j.out_status) j.out_status[row] = status;
+    if (j.tok_sampled) j.out_tok_lp[row] = (id < 0 || rowbad) ? nanv : (M - M) - logS;
+  }
+  if (kl == 0) return;
+  if (rowbad) {
+    if (t < kl) {
+      j.out_lp_ids[static_cast<size_t>(row) * kl + t] = -1;
+      j.out_lp[static_cast<size_t>(row) * kl + t] = nanv;
+    }
+    return;
+  }
+  const int np = sh.pool_n;
+  if (np <= kResPool) {  // uniform
+    if (wv != 0) return;
+    uint64_t top = 0ull;  // the 64 best so far, descending
+    for (int c0 = 0; c0 < np; c0 += kWave) {
+      uint64_t v = c0 + ln < np ? sh.pool[c0 + ln] : 0ull;
+      v = wave_sort_u64<false>(v);
+      top = wave_merge_top_u64(top, v);
+    }
+    if (ln < kl) {
+      j.out_lp_ids[static_cast<size_t>(row) * kl + ln] = top ? pid(top) : -1;
+      j.out_lp[static_cast<size_t>(row) * kl + ln] = top ? (key2f(pkey(top)) - M) - logS : nanv;
+    }
+    return;
+  }
+  // rare (many equal values): one block maximum a rank, below the last
+  uint64_t last = ~0ull;
+  for (int q = 0; q < kl; ++q) {
+    uint64_t b = 0ull;
+    for (int i = t; i < j.V; i += kResT) {
+      const uint64_t pk = pack(f2key(rowp[i]), i);
+      b = (pk < last && pk > b) ? pk : b;
+    }
+    const uint64_t wb = wave_max(b);
+    if (ln == 0) sh.wx[wv] = wb;
+    __syncthreads();
+    b = wave_max(ln < kResW ? sh.wx[ln] : 0ull);
+    __syncthreads();  // (the slots are written again next rank)
+    if (t == 0) {
+      j.out_lp_ids[static_cast<size_t>(row) * kl + q] = b ? pid(b) : -1;
+      j.out_lp[static_cast<size_t>(row) * kl + q] = b ? (key2f(pkey(b)) - M) - logS : nanv;
+    }
+    last = b;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_select(const Job& j, hipStream_t st) {
+  // greedy rows with the full log-softmax written, small enough to keep on
+  // chip: one read (k_select_resident)
+  if (j.full_in_select && j.sample && (j.hints & VS_HINT_ALL_GREEDY) && j.dt == VS_F32 &&
+      j.V % 4 == 0 && j.V >= kResMinV && j.V <= kResMaxV && j.aligned && j.full_vec && !j.pen && !j.out_mask &&
+      j.k_lp <= kWave && !j.lpT) {
+    hipLaunchKernelGGL(k_select_resident, dim3(j.B), dim3(kResT), 0, st, j);
+    return hipGetLastError();
+  }
   const int grid = xcd_grid(j.B, j.nseg);
   const dim3 block(kWave * j.nwave);
   const size_t lds = 0;

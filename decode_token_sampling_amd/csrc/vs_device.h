@@ -248,18 +248,33 @@ struct RowCfg {
   uint64_t seed;
 };
 
-__device__ __forceinline__ RowCfg load_cfg(int r, int V, const float* temperature,
-                                           const int32_t* top_k, const float* top_p,
-                                           const float* min_p, const uint64_t* seeds) {
+// A row's parameters as the caller's arrays give them: arrays left out take
+// neutral values; temperature, top_k and top_p all left out make every row
+// greedy (TensorRT-LLM "Sampling": none of the three set means greedy), as T = 0.
+struct RowParams {
+  float T, p, mp;
+  int k;
+  uint64_t seed;
+};
+__device__ __forceinline__ RowParams load_params(int r, const float* temperature,
+                                                 const int32_t* top_k, const float* top_p,
+                                                 const float* min_p, const uint64_t* seeds) {
+  RowParams a;
+  a.T = temperature ? temperature[r] : ((!top_k && !top_p) ? 0.0f : 1.0f);
+  a.k = top_k ? top_k[r] : 0;
+  a.p = top_p ? top_p[r] : 1.0f;
+  a.mp = min_p ? min_p[r] : 0.0f;
+  a.seed = seeds ? seeds[r] : 0ull;
+  return a;
+}
+// The row's mode and status from its parameters.
+__device__ __forceinline__ RowCfg cfg_of(const RowParams& a, int V) {
   RowCfg c;
-  // arrays left out take neutral values; temperature, top_k and top_p all
-  // left out make every row greedy (TensorRT-LLM "Sampling": none of the
-  // three set means greedy), as T = 0
-  c.T = temperature ? temperature[r] : ((!top_k && !top_p) ? 0.0f : 1.0f);
-  const int k = top_k ? top_k[r] : 0;
-  c.p = top_p ? top_p[r] : 1.0f;
-  c.mp = min_p ? min_p[r] : 0.0f;
-  c.seed = seeds ? seeds[r] : 0ull;
+  c.T = a.T;
+  const int k = a.k;
+  c.p = a.p;
+  c.mp = a.mp;
+  c.seed = a.seed;
   c.mode = kModeInvalid;
   c.status = 0;
   c.k = k;
@@ -280,6 +295,11 @@ __device__ __forceinline__ RowCfg load_cfg(int r, int V, const float* temperatur
   }
   c.mode = (c.k == 0) ? kModeFull : (c.k <= kFastK ? kModeKFast : kModeKSlow);
   return c;
+}
+__device__ __forceinline__ RowCfg load_cfg(int r, int V, const float* temperature,
+                                           const int32_t* top_k, const float* top_p,
+                                           const float* min_p, const uint64_t* seeds) {
+  return cfg_of(load_params(r, temperature, top_k, top_p, min_p, seeds), V);
 }
 
 // ---------------------------------------------------------------- workspace records

@@ -904,3 +904,72 @@ def test_sample_hint_small_topk(B):
     assert (g["status"][bad] == vs.ROW_HINT_VIOLATED).all() and (g["ids"][bad] == -1).all()
     assert (g["kept"][bad] == 0).all()
     compare_sample(g, o, rows=np.nonzero(~bad)[0])
+
+
+# ---------------------------------------------------------------- greedy rows kept on chip
+# Greedy batches with the full log-softmax, fp32 rows of 94,209 to 131,072
+# values and one row per workgroup: one kernel keeps each row in registers and
+# LDS and writes every output from there.
+@pytest.mark.parametrize("V", [94212, 128256, 131072])
+@pytest.mark.parametrize("k", [0, 1, 20, 64])
+def test_resident_greedy_full(V, k):
+    """Edge rows first: a constant row (ties everywhere: the top-k from the row
+    read again), a NaN, a +inf, all -inf, ten finite values among -inf (the
+    top-k runs into -inf), huge values (one maximum near the fp32 limit: exact
+    differences), a maximum held twice, -0 and +0 as the maximum, the maximum in
+    the last vector (the LDS part); then random rows. Ids, kept counts and
+    status against the oracle; log-probs, top-k and the full log-softmax against
+    the oracle on the edge rows and a few random ones, and on every row against
+    the same call with a kept mask (the row kernels' path)."""
+    import decode_token_sampling_amd as vs
+    B = 256
+    rng = np.random.default_rng(V + 7 * k)
+    x = (np.float32(4.0) * rng.standard_normal((B, V), dtype=np.float32))
+    x[0] = np.float32(0.5)
+    x[1, 77] = np.nan
+    x[2, V // 2] = np.inf
+    x[3] = -np.inf
+    x[4] = -np.inf
+    x[4, rng.choice(V, 10, replace=False)] = rng.standard_normal(10).astype(np.float32)
+    x[5] = np.float32(2e38) - np.float32(2.0 ** 110) * rng.integers(0, 1000, V).astype(np.float32)
+    x[5, 12345] = np.float32(3e38)
+    x[6, 100] = x[6, 5000] = np.float32(50.0)
+    x[7] = -np.abs(x[7]) - np.float32(1.0)
+    x[7, 300] = np.float32(0.0)
+    x[7, 200] = np.float32(-0.0)
+    x[8, V - 1] = np.float32(60.0)
+    T = np.zeros(B, np.float32)
+    top_k = np.zeros(B, np.int32)
+    T[9], top_k[9] = 1.0, 1                      # greedy by top_k = 1
+    w = dict(temperature=T, top_k=top_k, top_p=np.ones(B, np.float32),
+             min_p=np.zeros(B, np.float32), seeds=np.arange(B, dtype=np.uint64))
+    args = [dev(T, np.float32), dev(top_k, np.int32), dev(w["top_p"], np.float32),
+            dev(w["min_p"], np.float32), dev(w["seeds"].view(np.int64), np.int64)]
+    xd = to_device(x)
+    f = vs.sample_logprobs(xd, *args, hints=vs.HINT_ALL_GREEDY, k=k, full=True, V=V)
+    r = vs.sample_logprobs(xd, *args, k=k, full=True, mask=True, V=V)
+    torch.cuda.synchronize()
+    g = dict(ids=f["ids"].cpu().numpy(), kept=f["kept"].cpu().numpy(),
+             status=f["status"].cpu().numpy())
+    assert compare_sample(g, oracle_sample(x, V, w, mask=False), check_mask=False) == 0
+    assert g["ids"][0] == 0 and g["ids"][6] == 100 and g["ids"][7] == 200 and g["ids"][8] == V - 1
+    assert torch.equal(f["ids"], r["ids"]) and torch.equal(f["status"], r["status"])
+    ff, rf = f["full"], r["full"]
+    assert torch.equal(torch.isnan(ff), torch.isnan(rf))
+    assert torch.equal(torch.isinf(ff), torch.isinf(rf))
+    fin = torch.isfinite(ff)
+    assert (ff[fin] - rf[fin]).abs().max().item() <= LOGPROB_ATOL
+    if k:
+        assert torch.equal(f["topk_ids"], r["topk_ids"])
+    rows = np.array(list(range(10)) + [10, 100, B - 1])
+    xs = np.ascontiguousarray(x[rows])
+    ids = g["ids"][rows]
+    out = {key: (f[key][torch.from_numpy(rows).cuda()] if f.get(key) is not None else None)
+           for key in ("ids", "token_lp", "topk_ids", "topk_lp")}
+    _check_fused_logprobs(xs, V, out, k)
+    o = oracle.logprobs(xs, V, ids, k=k, full=True)
+    got = ff[torch.from_numpy(rows).cuda()].cpu().numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(o["full"]))
+    finf = np.isfinite(o["full"])
+    assert np.array_equal(np.isfinite(got), finf)
+    assert np.abs(got[finf] - o["full"][finf]).max() <= LOGPROB_ATOL
